@@ -1,0 +1,185 @@
+/* swa.h -- C ABI of libswa.so: windowed+sink GQA attention and compressed-KV
+ * attention on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *   [NW] "How the 256-Token Sliding Window Works with Tools as KV Sinks in
+ *        Needle" (instagit.com)
+ *   [NS] "256-token滑动窗口+KV sink：Needle 2工具钉住机制源码分析" (cf-1.com)
+ *   [CA] "Compressed attention and the copy probe" (octlm.ramaa.tech)
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers to contiguous row-major arrays owned
+ *     by the caller, unless the comment says HOST.  The library never
+ *     allocates, frees or synchronises; it keeps no state between calls and is
+ *     safe to call from several threads.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns at once.
+ *   - The return value is a status code.  Arguments are validated on the host
+ *     before any HIP call; a non-OK status leaves outputs untouched and sets a
+ *     thread-local message readable with swa_last_error().
+ *   - Device pointers must be 16-byte aligned.
+ *   - Empty problems (B == 0, T == 0, N == 0) return SWA_OK and launch nothing.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWA_OK 0
+#define SWA_ERR_INVALID 1     /* bad shape, argument, NULL or misaligned pointer */
+#define SWA_ERR_UNSUPPORTED 2 /* valid request this library does not implement  */
+#define SWA_ERR_HIP 3         /* a HIP launch or runtime error (message has the HIP text) */
+
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+
+/* Text of the last non-OK status on the calling thread ("" if none). */
+const char* swa_last_error(void);
+/* Library version, major*100 + minor. */
+int swa_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Prefill attention.                                                        */
+/*                                                                           */
+/* Plain mode (compress_block == 0) computes, for every (b, query head h,     */
+/* row t), softmax attention over the keys s that the packing mask of         */
+/* [NW §"KV Sinks for Tools: Pinning Critical Context"] keeps:                */
+/*   vis(t, s) = seg[t] > 0 && seg[s] == seg[t] && s <= t                     */
+/*               && (window == 0 || t - s < window || prefix[s] != 0)         */
+/* i.e. packing & causal & (recent | sink).  Sinks never leave the window but */
+/* stay inside their own segment (the code composes the terms that way).      */
+/* GQA: query head h reads kv head h / (Hq / Hkv).                            */
+/*                                                                           */
+/* Compressed mode (compress_block = b >= 1) follows [CA §"Two kinds of       */
+/* columns, pooled blocks and exact recent keys"]: the columns are            */
+/* [pooled blocks j < T/b, exact keys s < T]; pooled block j is visible to    */
+/* row t iff (j + 1) * b <= t - window + 1 and exact key s iff s <= t and     */
+/* t - s < window.  One softmax runs over both column sets.  pooled_k must   */
+/* already be rotated (kv_pool_compress_rope does that); seg_ids and prefix   */
+/* must be NULL and window >= 1.                                             */
+/*                                                                           */
+/* RoPE: with rope_len > 0, q and the exact k are rotated inside the kernel   */
+/* at their row index t with the tables from swa_rope_table (rotate-half      */
+/* pairing (i, i + D/2)); rope_len must be >= T.  rope_len == 0 means q and k */
+/* are used as given.                                                        */
+/*                                                                           */
+/* Rows with no visible key (segment 0 padding) get out = 0 and lse = -inf.  */
+/* Accumulation is fp32 for both dtypes; bf16 runs the MFMA kernel, f32 runs */
+/* an fp32 vector kernel.                                                    */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int B, Hq, Hkv, T, D; /* q, out: [B,Hq,T,D]; k, v: [B,Hkv,T,D]; Hq % Hkv == 0; D in {32, 64} */
+    int window;           /* >= 0; 0 = no window                                         */
+    int compress_block;   /* 0 = plain; b >= 1 = compressed columns (pooled_k/v [B,Hkv,T/b,D]) */
+    int rope_len;         /* rows of rope_cos/rope_sin; 0 = no in-kernel RoPE              */
+    float scale;          /* softmax scale; 0 selects 1/sqrt(D)                           */
+    int dtype;            /* swa_dtype of q, k, v, pooled_k, pooled_v and out             */
+} swa_prefill_params;
+
+int swa_attn_prefill(const swa_prefill_params* p,
+                     const void* q, const void* k, const void* v,
+                     const void* pooled_k, const void* pooled_v, /* NULL unless compress_block > 0 */
+                     const int32_t* seg_ids,                     /* [B,T] or NULL (all segment 1)  */
+                     const uint8_t* prefix,                      /* [B,T] sink flags or NULL       */
+                     const float* rope_cos, const float* rope_sin, /* [rope_len, D/2] or NULL      */
+                     void* out,                                  /* [B,Hq,T,D], dtype of q         */
+                     float* lse,                                 /* [B,Hq,T] natural-log LSE or NULL */
+                     void* stream);
+
+/* Visibility as the prefill kernels see it: the same tile enumeration, the  */
+/* same tile classification (skip / full / per-element) and the same element */
+/* predicate, written out.  mask_out [B,T,Tk] u8 (Tk = T, or T/b + T in       */
+/* compressed mode) may be NULL; count_out [B,T] i32 receives the number of   */
+/* visible columns per row.  Used to check masks bit-exactly.                */
+int swa_debug_visibility(const swa_prefill_params* p, const int32_t* seg_ids, const uint8_t* prefix,
+                         uint8_t* mask_out, int32_t* count_out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* RoPE tables and block pooling.                                            */
+/* ------------------------------------------------------------------------ */
+/* cos_out/sin_out [rope_len, D/2] fp32: angle = pos * theta^(-2i/D),         */
+/* evaluated in fp64 on the device and rounded once to fp32.  D even.         */
+int swa_rope_table(double theta, int rope_len, int D, float* cos_out, float* sin_out, void* stream);
+
+/* [CA §"Pool before rotating, not after"]: pooled_k[j] and pooled_v[j] are   */
+/* the means of rows j*b .. j*b+b-1 of k_pre (the key BEFORE RoPE) and v;     */
+/* rows past (T/b)*b are dropped.  With rope tables given, pooled_k[j] alone  */
+/* is then rotated once at position min(j*b + b/2, rope_len - 1).  Sums are   */
+/* fp32; the result is rounded once to dtype.                                */
+/*   k_pre, v [B,H,T,D]; pooled_k, pooled_v [B,H,T/block,D]; block >= 1.     */
+int kv_pool_compress_rope(int B, int H, int T, int D, int block, int dtype,
+                          const void* k_pre, const void* v,
+                          const float* rope_cos, const float* rope_sin, int rope_len, /* NULL/0 = no RoPE */
+                          void* pooled_k, void* pooled_v, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Int8 KV cache and decode.                                                 */
+/*                                                                           */
+/* The cache stores one int8 per K/V element plus one fp32 scale per 32       */
+/* channels, the layout the budget formula of [NW §"Effective KV Window:      */
+/* Bounding the Cache Size"] prices.  Quantization is symmetric:              */
+/* s = max|x| / 127 over the 32-channel group (IEEE fp32 division), code =    */
+/* clamp(rint(x / s), -127, 127) with round-half-even; an all-zero group gets */
+/* s = 0 and zero codes.  Dequantized value = code * s.                      */
+/* ------------------------------------------------------------------------ */
+/* x [N,D] bf16 -> xq [N,D] i8, xs [N,D/32] f32.  D % 32 == 0.               */
+int swa_kv_quantize(long long N, int D, const void* x_bf16, int8_t* xq, float* xs, void* stream);
+
+typedef struct {
+    int B, Hq, Hkv, D; /* D in {32, 64}; Hq % Hkv == 0                         */
+    int W;             /* ring capacity = window length, >= 1                   */
+    int S;             /* sink cache capacity, >= 0                             */
+    float scale;       /* 0 selects 1/sqrt(D)                                   */
+    int num_splits;    /* 0 = automatic; >1 splits each row set across workgroups */
+} swa_decode_params;
+
+/* Workspace bytes swa_attn_decode needs for these parameters (0 when the    */
+/* chosen split count is 1).                                                 */
+size_t swa_decode_workspace_size(const swa_decode_params* p);
+
+/* One decode step with the mask of [NS §"256-token 滑动窗口：源码走读"]:     */
+/* the new token at position pos[b] sees the sink rows [0, sink_len[b]) and  */
+/* the ring positions [max(sink_len[b], pos[b] - W + 1), pos[b]], stored at   */
+/* slot position % W.  There is no packing term in decode.  When k_new and   */
+/* v_new are given they are first quantized into slot pos[b] % W of the ring. */
+/* Preconditions the device cannot check cheaply: sink_len[b] <= pos[b] (else */
+/* the ring counts as empty) and sink_len[b] <= S.                           */
+int swa_attn_decode(const swa_decode_params* p,
+                    const void* q,                        /* [B,Hq,D] bf16, already rotated   */
+                    const void* k_new, const void* v_new, /* [B,Hkv,D] bf16, or both NULL      */
+                    int8_t* ring_k, int8_t* ring_v,       /* [B,Hkv,W,D]                       */
+                    float* ring_ks, float* ring_vs,       /* [B,Hkv,W,D/32]                    */
+                    const int8_t* sink_k, const int8_t* sink_v, /* [B,Hkv,S,D] (NULL if S==0)  */
+                    const float* sink_ks, const float* sink_vs, /* [B,Hkv,S,D/32]              */
+                    const int32_t* pos,                   /* [B]                               */
+                    const int32_t* sink_len,              /* [B] or NULL (= S)                 */
+                    void* out,                            /* [B,Hq,D] bf16                     */
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Window sizing (HOST functions, no device work).                           */
+/* [NW §"Effective KV Window: Bounding the Cache Size"], [NS §"256 这个窗口宽  */
+/* 度从哪来：内存预算计算器"]: per_pos = L*(2*kv + 2*(kv/32)*4)               */
+/* + sites*(d_model + 32*4) bytes with kv = num_kv_heads * head_dim and       */
+/* head_dim = (attn_dim ? attn_dim : d_model) / num_heads; the budget window  */
+/* is (11.5 MiB / per_pos) rounded down to a multiple of 32, clamped to       */
+/* [160, max_seq_len] (the lower bound wins).  The effective window is        */
+/* min(budget window, kv_window) when kv_window != 0.  Returns -1 on invalid  */
+/* arguments (non-positive sizes).                                           */
+/* ------------------------------------------------------------------------ */
+long long swa_kv_budget_window(long long d_model, long long attn_dim, long long num_heads,
+                               long long num_kv_heads, long long num_layers, long long sites,
+                               long long max_seq_len);
+long long swa_effective_kv_window(long long d_model, long long attn_dim, long long num_heads,
+                                  long long num_kv_heads, long long num_layers, long long sites,
+                                  long long max_seq_len, long long kv_window);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */
