@@ -1,0 +1,314 @@
+"""Benchmark of the hot path on one MI355X.
+
+One step = one pass of every hot-path row over one batch of synthetic input:
+  * needle-shaped windowed+sink GQA prefill, bf16 (B8, 8q/2kv heads, D64,
+    T2048, window 256, per-row sink prefix of 64..384 tool tokens, RoPE);
+  * compressed-column prefill, bf16 (B4, 8/8 heads, D64, T4096, window 256,
+    block 4): pooling + midpoint RoPE, then attention over [pooled, exact];
+  * one decode step over 12 layers of int8 ring (256) + sink (256) caches
+    (B256, 16q/4kv heads, D64, positions up to 32768).
+Each part is captured in a HIP graph and replayed, input copies rotate so that
+the working set exceeds the 256 MB Infinity Cache, and HIP events on the
+launch stream time the region.  `value` is the prefill throughput in TFLOP/s
+counted on visible (query, key) pairs only: 4 * D * Hq * sum(n_vis).
+
+The JSON line also carries the decode HBM rate, the other prefill workloads
+(packed multi-segment rows, compressed block 16), a `roofline` object for the
+dominant kernel and a `cpu_baseline` object (the CPU oracle on a bounded
+sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 600 << 20          # > 2 x the 256 MB MALL
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=20, help="iterations per timed graph when timing one kernel")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16")
+    return ap.parse_args()
+
+
+class Part:
+    """One workload: device inputs (several rotating copies), a launch function and its work counts."""
+
+    def __init__(self, name, launch, ncopies, flops=0.0, bytes_=0.0, kernel=None):
+        self.name, self.launch, self.ncopies = name, launch, ncopies
+        self.flops, self.bytes, self.kernel = flops, bytes_, kernel
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    from compressed_kv_attention_amd import swa, workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    parts_wanted = args.parts.split(",")
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def copies(n, *tensors):
+        return [tuple(t.clone() for t in tensors) for _ in range(n)]
+
+    parts = {}
+
+    # ---- needle-shaped prefill -------------------------------------------------
+    def make_prefill(name, w, step_bytes_extra=0):
+        q, k, v = bf16(w["q_bits"]), bf16(w["k_bits"]), bf16(w["v_bits"])
+        seg = torch.from_numpy(w["seg_ids"]).to(dev) if w["seg_ids"] is not None else None
+        pre = torch.from_numpy(w["prefix"]).to(dev) if w["prefix"] is not None else None
+        rope = swa.rope_table(w["rope_theta"], w["T"], w["D"]) if w["rope_theta"] else None
+        per_copy = (q.numel() * 2 + k.numel() * 4) * 2
+        n = max(2, min(16, ROTATE_BYTES // per_copy + 1))
+        bufs = [(q.clone(), k.clone(), v.clone(), torch.empty_like(q)) for _ in range(n)]
+        _, count = swa.debug_visibility(w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["window"], torch.bfloat16,
+                                        seg, pre, want_mask=False)
+        nvis = int(count.to(torch.int64).sum().item())
+        flops = 4.0 * w["D"] * w["Hq"] * nvis
+        bytes_ = q.numel() * 2 * 2 + k.numel() * 2 * 2
+
+        def launch(i):
+            qq, kk, vv, oo = bufs[i % n]
+            swa.prefill(qq, kk, vv, seg, pre, w["window"], rope=rope, out=oo)
+        p = Part(name, launch, n, flops, bytes_, kernel="prefill_bf16_kernel")
+        p.extra = dict(B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], T=w["T"], D=w["D"], window=w["window"],
+                       visible_pairs_per_head=nvis)
+        p.w = w
+        p.count = count.cpu().numpy()
+        return p
+
+    def make_compressed(name, block):
+        w = workloads.compressed(block=block, dtype="bf16")
+        q, k, v = bf16(w["q_bits"]), bf16(w["k_bits"]), bf16(w["v_bits"])
+        rope = swa.rope_table(w["rope_theta"], w["T"], w["D"])
+        per_copy = q.numel() * 2 * 4
+        n = max(2, min(16, ROTATE_BYTES // per_copy + 1))
+        bufs = []
+        for _ in range(n):
+            kk, vv = k.clone(), v.clone()
+            pk, pv = swa.pool_compress_rope(kk, vv, block, rope)
+            bufs.append((q.clone(), kk, vv, torch.empty_like(q), pk, pv))
+        _, count = swa.debug_visibility(w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["window"], torch.bfloat16,
+                                        compress_block=block, want_mask=False)
+        nvis = int(count.to(torch.int64).sum().item())
+        flops = 4.0 * w["D"] * w["Hq"] * nvis
+        nb = w["T"] // block
+        bytes_ = q.numel() * 2 * 2 + k.numel() * 2 * 2 + 2 * (w["B"] * w["Hkv"] * nb * w["D"] * 2) * 2
+
+        # pooled_k/pooled_v of the step are produced inside the step (pool then attend)
+        def launch_step(i):
+            qq, kk, vv, oo, pk, pv = bufs[i % n]
+            swa.pool_compress_rope(kk, vv, block, rope, out=(pk, pv))
+            swa.prefill(qq, kk, vv, window=w["window"], rope=rope, pooled_k=pk, pooled_v=pv, compress_block=block,
+                        out=oo)
+        p = Part(name, launch_step, n, flops, bytes_, kernel="prefill_bf16_kernel")
+        p.extra = dict(B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], T=w["T"], D=w["D"], window=w["window"], block=block,
+                       visible_pairs_per_head=nvis)
+        p.w = w
+        return p
+
+    def make_decode(name, layers=12):
+        B, Hq, Hkv, D, W, S = 256, 16, 4, 64, 256, 256
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        caches = []
+        for _ in range(layers):
+            c = {}
+            for nm, rows in (("ring_k", W), ("ring_v", W), ("sink_k", S), ("sink_v", S)):
+                x = torch.randn((B, Hkv, rows, D), generator=g, device=dev).to(torch.bfloat16)
+                c[nm], c[nm + "s"] = swa.kv_quantize(x)
+            c["q"] = torch.randn((B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+            c["k_new"] = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+            c["v_new"] = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+            c["out"] = torch.empty_like(c["q"])
+            caches.append(c)
+        rng = np.random.default_rng(5)
+        pos = torch.from_numpy(rng.integers(512, 32768, size=B).astype(np.int32)).to(dev)
+        sink_len = torch.full((B,), S, dtype=torch.int32, device=dev)
+        cache_bytes = 2 * (B * Hkv * (W + S) * D) + 2 * (B * Hkv * (W + S) * (D // 32) * 4)
+        io_bytes = 2 * B * Hq * D * 2 + 2 * B * Hkv * D * 2 + 2 * B * Hkv * (D + (D // 32) * 4)
+        per_layer = cache_bytes + io_bytes
+
+        def launch(i):
+            for c in caches:
+                swa.decode(c["q"], c["ring_k"], c["ring_v"], c["ring_ks"], c["ring_vs"], c["sink_k"], c["sink_v"],
+                           c["sink_ks"], c["sink_vs"], pos, sink_len, c["k_new"], c["v_new"], out=c["out"])
+        p = Part(name, launch, 1, 0.0, per_layer * layers, kernel="decode_kernel")
+        p.extra = dict(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, layers=layers, bytes_per_layer=per_layer)
+        p.tokens = B
+        p.launches = layers
+        return p
+
+    t_setup = time.time()
+    if "needle" in parts_wanted:
+        parts["needle"] = make_prefill("needle", workloads.needle())
+    if "compressed4" in parts_wanted:
+        parts["compressed4"] = make_compressed("compressed4", 4)
+    if "decode" in parts_wanted:
+        parts["decode"] = make_decode("decode")
+    if "packed" in parts_wanted:
+        parts["packed"] = make_prefill("packed", workloads.packed())
+    if "compressed16" in parts_wanted:
+        parts["compressed16"] = make_compressed("compressed16", 16)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s")
+
+    stream = torch.cuda.Stream(device=dev)
+
+    def capture(fn, iters, offset=0):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            fn(offset)  # warm the code path on the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(iters):
+                    fn(offset + i)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(replays):
+                g.replay()
+            e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1)
+
+    # ---- per-part timing (one graph of `reps` iterations each) -----------------
+    results = {}
+    for name, p in parts.items():
+        reps = max(p.ncopies, args.reps)
+        g = capture(p.launch, reps)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = time_graph(g, max(1, args.steps // 4)) / (max(1, args.steps // 4) * reps)
+        r = dict(ms=ms)
+        if p.flops:
+            r["tflops"] = p.flops / (ms * 1e-3) / 1e12
+            r["frac_mfma_peak"] = r["tflops"] / MFMA_BF16_PEAK_TFLOPS
+        if p.bytes:
+            r["gbs"] = p.bytes / (ms * 1e-3) / 1e9
+            r["frac_hbm_peak"] = r["gbs"] / HBM_PEAK_GBS
+        if hasattr(p, "tokens"):
+            r["tokens_per_s"] = p.tokens / (ms * 1e-3)
+            r["ms_per_launch"] = ms / p.launches
+        r.update(p.extra)
+        results[name] = r
+        log(f"{name}: {json.dumps(r)}")
+        del g
+
+    # ---- the step: needle + compressed4 + decode, K timed steps ----------------
+    step_names = [n for n in ("needle", "compressed4", "decode") if n in parts]
+
+    def step(i):
+        for n in step_names:
+            parts[n].launch(i)
+    ncopy = max([parts[n].ncopies for n in step_names] + [1])
+    step_graph = capture(step, ncopy)
+    for _ in range(args.warmup):
+        step_graph.replay()
+    torch.cuda.synchronize()
+    replays = max(1, args.steps // ncopy)
+    steps_timed = replays * ncopy
+    ms_total = time_graph(step_graph, replays)
+    ms_per_step = ms_total / steps_timed
+
+    head = results.get("needle", {})
+    dec = results.get("decode", {})
+    out = {
+        "metric": "prefill TFLOP/s (unmasked) + decode GB/s, % of MI355X roofline",
+        "value": round(head.get("tflops", 0.0), 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps_timed,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "needle-shaped windowed+sink GQA prefill, B8 8q/2kv D64 T2048 window 256, "
+                               "sink prefix 64..384, RoPE; step also runs compressed b=4 (B4 8/8 T4096) and a "
+                               "12-layer int8 decode step (B256 16q/4kv ring 256 + 256 sinks)",
+                   "global_batch": 8, "seq_len": 2048, "parallelism": "none (1 GPU)"},
+        "decode": {"value": round(dec.get("gbs", 0.0), 1), "unit": "GB/s",
+                   "frac_hbm_peak": round(dec.get("frac_hbm_peak", 0.0), 4),
+                   "tokens_per_s": round(dec.get("tokens_per_s", 0.0), 1)},
+        "parts": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                  for k, v in results.items()},
+        "roofline": {"bound": "mfma", "achieved": round(head.get("tflops", 0.0), 3),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(head.get("frac_mfma_peak", 0.0), 5), "traffic": None,
+                     "kernel": "prefill_bf16_kernel (needle workload)"},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec.get("gbs", 0.0), 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(dec.get("frac_hbm_peak", 0.0), 5), "traffic": None,
+                            "kernel": "decode_kernel"},
+    }
+
+    # ---- CPU baseline: the oracle on a bounded sample of the needle workload ----
+    if not args.no_cpu_baseline and "needle" in parts:
+        out["cpu_baseline"] = cpu_baseline(parts["needle"], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(part, seconds):
+    """Time the CPU oracle on sampled rows of the needle workload (visible-pair TFLOP/s)."""
+    import oracle
+    w = part.w
+    B, Hq, T, D = w["B"], w["Hq"], w["T"], w["D"]
+    rng = np.random.default_rng(0)
+    n = 256
+    elapsed = 0.0
+    while True:
+        rows = rng.integers(0, B * Hq * T, size=n).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.prefill(w["q"], w["k"], w["v"], w["seg_ids"], w["prefix"], w["window"], theta=w["rope_theta"],
+                       rows=rows)
+        elapsed = time.perf_counter() - t0
+        if elapsed > seconds / 4 or n >= B * Hq * T:
+            break
+        n = min(B * Hq * T, int(n * max(2.0, seconds / max(elapsed, 1e-3) * 0.9)))
+    # visible pairs of the sampled rows, from the per-row counts of the visibility kernel
+    nvis = part.count[rows // (Hq * T), rows % T]
+    flops = 4.0 * D * float(nvis.astype(np.float64).sum())
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} random (b, head, row) query rows of the needle workload, incl. RoPE of all keys; "
+                      f"{elapsed:.1f} s", "seconds": round(elapsed, 2)}
+
+
+if __name__ == "__main__":
+    main()

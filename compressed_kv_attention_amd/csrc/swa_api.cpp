@@ -1,0 +1,294 @@
+// swa_api.cpp -- the C ABI of libswa.so (declared in include/swa.h).
+//
+// Every entry point validates its arguments on the host before any HIP call,
+// then enqueues kernels on the caller's stream.  Nothing here allocates,
+// frees or synchronises, and no state survives a call except the
+// thread-local text of the last error.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/swa.h"
+#include "swa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return SWA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                                  \
+    do {                                                    \
+        if (!(cond)) return fail(SWA_ERR_INVALID, __VA_ARGS__); \
+    } while (0)
+
+#define REQUIRE_PTR(p)                                                          \
+    do {                                                                        \
+        if ((p) == nullptr) return fail(SWA_ERR_INVALID, "%s must not be NULL", #p); \
+        if (!aligned16(p)) return fail(SWA_ERR_INVALID, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+#define OPTIONAL_PTR(p)                                                            \
+    do {                                                                           \
+        if ((p) != nullptr && !aligned16(p))                                       \
+            return fail(SWA_ERR_INVALID, "%s is not 16-byte aligned", #p);         \
+    } while (0)
+
+// Shared validation of prefill parameters; fills the kernel argument block.
+int check_prefill(const swa_prefill_params* p, const int32_t* seg_ids, const uint8_t* prefix, swa::PrefillArgs& a) {
+    REQUIRE(p != nullptr, "params must not be NULL");
+    REQUIRE(p->B >= 0 && p->T >= 0, "B and T must be >= 0 (B=%d, T=%d)", p->B, p->T);
+    REQUIRE(p->Hq > 0 && p->Hkv > 0, "Hq and Hkv must be > 0 (Hq=%d, Hkv=%d)", p->Hq, p->Hkv);
+    REQUIRE(p->Hq % p->Hkv == 0, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+    REQUIRE(p->window >= 0, "window must be >= 0 (got %d)", p->window);
+    REQUIRE(p->compress_block >= 0, "compress_block must be >= 0 (got %d)", p->compress_block);
+    REQUIRE(p->rope_len >= 0, "rope_len must be >= 0 (got %d)", p->rope_len);
+    REQUIRE(p->scale >= 0.f && std::isfinite(p->scale), "scale must be finite and >= 0");
+    REQUIRE(p->dtype == SWA_F32 || p->dtype == SWA_BF16, "dtype must be SWA_F32 or SWA_BF16 (got %d)", p->dtype);
+    if (p->D != 32 && p->D != 64) return fail(SWA_ERR_UNSUPPORTED, "head dim D=%d is not built (32 or 64)", p->D);
+    if (p->T > swa::kMaxT) return fail(SWA_ERR_UNSUPPORTED, "T=%d exceeds the supported %d", p->T, swa::kMaxT);
+    if (p->compress_block > 0) {
+        REQUIRE(p->window >= 1, "compressed mode needs window >= 1 (got %d)", p->window);
+        if (seg_ids != nullptr || prefix != nullptr)
+            return fail(SWA_ERR_UNSUPPORTED, "compressed mode takes no seg_ids or prefix");
+    }
+    if (p->rope_len > 0) REQUIRE(p->rope_len >= p->T, "rope_len (%d) must be >= T (%d)", p->rope_len, p->T);
+    OPTIONAL_PTR(seg_ids);
+    OPTIONAL_PTR(prefix);
+    a = swa::PrefillArgs{};
+    a.B = p->B;
+    a.Hq = p->Hq;
+    a.Hkv = p->Hkv;
+    a.T = p->T;
+    a.D = p->D;
+    a.window = p->window;
+    a.block = p->compress_block;
+    a.nblk = p->compress_block > 0 ? p->T / p->compress_block : 0;
+    a.rope_len = p->rope_len;
+    a.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->D);
+    a.seg = seg_ids;
+    a.prefix = prefix;
+    const swa::MfmaGeom g = swa::mfma_geometry(p->Hq / p->Hkv);
+    a.hpw = g.hpw;
+    a.rbs = g.rbs;
+    return SWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* swa_last_error(void) { return g_last_error.c_str(); }
+
+int swa_version(void) { return 100; }
+
+int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, const void* v, const void* pooled_k,
+                     const void* pooled_v, const int32_t* seg_ids, const uint8_t* prefix, const float* rope_cos,
+                     const float* rope_sin, void* out, float* lse, void* stream) {
+    swa::PrefillArgs a;
+    int rc = check_prefill(p, seg_ids, prefix, a);
+    if (rc != SWA_OK) return rc;
+    if (p->B == 0 || p->T == 0) return ok();
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(lse);
+    if (p->compress_block > 0 && a.nblk > 0) {
+        REQUIRE_PTR(pooled_k);
+        REQUIRE_PTR(pooled_v);
+    }
+    if (p->rope_len > 0) {
+        REQUIRE_PTR(rope_cos);
+        REQUIRE_PTR(rope_sin);
+    }
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.pk = pooled_k;
+    a.pv = pooled_v;
+    a.rope_cos = p->rope_len > 0 ? rope_cos : nullptr;
+    a.rope_sin = p->rope_len > 0 ? rope_sin : nullptr;
+    a.out = out;
+    a.lse = lse;
+    const hipStream_t s = (hipStream_t)stream;
+    const hipError_t e = p->dtype == SWA_BF16 ? swa::launch_prefill_bf16(a, s) : swa::launch_prefill_f32(a, s);
+    return hip_status(e, "swa_attn_prefill launch");
+}
+
+int swa_debug_visibility(const swa_prefill_params* p, const int32_t* seg_ids, const uint8_t* prefix,
+                         uint8_t* mask_out, int32_t* count_out, void* stream) {
+    swa::PrefillArgs a;
+    int rc = check_prefill(p, seg_ids, prefix, a);
+    if (rc != SWA_OK) return rc;
+    if (p->T > swa::kDebugMaxT)
+        return fail(SWA_ERR_UNSUPPORTED, "swa_debug_visibility supports T <= %d (got %d)", swa::kDebugMaxT, p->T);
+    if (p->B == 0 || p->T == 0) return ok();
+    REQUIRE_PTR(count_out);
+    const hipError_t e = swa::launch_debug_visibility(a, p->dtype == SWA_BF16, mask_out, count_out, (hipStream_t)stream);
+    return hip_status(e, "swa_debug_visibility launch");
+}
+
+int swa_rope_table(double theta, int rope_len, int D, float* cos_out, float* sin_out, void* stream) {
+    REQUIRE(theta > 0.0 && std::isfinite(theta), "theta must be finite and > 0");
+    REQUIRE(rope_len >= 0, "rope_len must be >= 0 (got %d)", rope_len);
+    REQUIRE(D > 0 && D % 2 == 0, "D must be positive and even (got %d)", D);
+    if (rope_len == 0) return ok();
+    REQUIRE_PTR(cos_out);
+    REQUIRE_PTR(sin_out);
+    return hip_status(swa::launch_rope_table(theta, rope_len, D, cos_out, sin_out, (hipStream_t)stream),
+                      "swa_rope_table launch");
+}
+
+int kv_pool_compress_rope(int B, int H, int T, int D, int block, int dtype, const void* k_pre, const void* v,
+                          const float* rope_cos, const float* rope_sin, int rope_len, void* pooled_k, void* pooled_v,
+                          void* stream) {
+    REQUIRE(B >= 0 && H > 0 && T >= 0, "bad shape (B=%d, H=%d, T=%d)", B, H, T);
+    REQUIRE(block >= 1, "block must be >= 1 (got %d)", block);
+    REQUIRE(dtype == SWA_F32 || dtype == SWA_BF16, "dtype must be SWA_F32 or SWA_BF16 (got %d)", dtype);
+    REQUIRE(D > 0 && D % 2 == 0, "D must be positive and even (got %d)", D);
+    REQUIRE(rope_len >= 0, "rope_len must be >= 0 (got %d)", rope_len);
+    if (B == 0 || T / block == 0) return ok();
+    REQUIRE_PTR(k_pre);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(pooled_k);
+    REQUIRE_PTR(pooled_v);
+    const bool rope = rope_cos != nullptr || rope_sin != nullptr || rope_len > 0;
+    if (rope) {
+        REQUIRE_PTR(rope_cos);
+        REQUIRE_PTR(rope_sin);
+        REQUIRE(rope_len >= 1, "rope_len must be >= 1 with RoPE tables");
+    }
+    return hip_status(swa::launch_pool_rope(B, H, T, D, block, dtype, k_pre, v, rope ? rope_cos : nullptr,
+                                            rope ? rope_sin : nullptr, rope_len, pooled_k, pooled_v,
+                                            (hipStream_t)stream),
+                      "kv_pool_compress_rope launch");
+}
+
+int swa_kv_quantize(long long N, int D, const void* x_bf16, int8_t* xq, float* xs, void* stream) {
+    REQUIRE(N >= 0, "N must be >= 0");
+    REQUIRE(D > 0 && D % 32 == 0, "D must be a positive multiple of 32 (got %d)", D);
+    if (N == 0) return ok();
+    REQUIRE_PTR(x_bf16);
+    REQUIRE_PTR(xq);
+    REQUIRE_PTR(xs);
+    return hip_status(swa::launch_kv_quantize(N, D, x_bf16, xq, xs, (hipStream_t)stream), "swa_kv_quantize launch");
+}
+
+size_t swa_decode_workspace_size(const swa_decode_params* p) {
+    (void)p;
+    return 0;
+}
+
+int swa_attn_decode(const swa_decode_params* p, const void* q, const void* k_new, const void* v_new, int8_t* ring_k,
+                    int8_t* ring_v, float* ring_ks, float* ring_vs, const int8_t* sink_k, const int8_t* sink_v,
+                    const float* sink_ks, const float* sink_vs, const int32_t* pos, const int32_t* sink_len,
+                    void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    REQUIRE(p != nullptr, "params must not be NULL");
+    REQUIRE(p->B >= 0, "B must be >= 0");
+    REQUIRE(p->Hq > 0 && p->Hkv > 0 && p->Hq % p->Hkv == 0, "Hq (%d) must be a positive multiple of Hkv (%d)", p->Hq,
+            p->Hkv);
+    REQUIRE(p->W >= 1, "W must be >= 1 (got %d)", p->W);
+    REQUIRE(p->S >= 0, "S must be >= 0 (got %d)", p->S);
+    REQUIRE(p->scale >= 0.f && std::isfinite(p->scale), "scale must be finite and >= 0");
+    REQUIRE(p->num_splits >= 0, "num_splits must be >= 0");
+    if (p->D != 32 && p->D != 64) return fail(SWA_ERR_UNSUPPORTED, "head dim D=%d is not built (32 or 64)", p->D);
+    const int G = p->Hq / p->Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(SWA_ERR_UNSUPPORTED, "GQA group size %d is not built (1, 2, 4 or 8)", G);
+    if (p->num_splits > 1) return fail(SWA_ERR_UNSUPPORTED, "num_splits > 1 is not built");
+    REQUIRE((k_new == nullptr) == (v_new == nullptr), "k_new and v_new must both be given or both be NULL");
+    if (p->B == 0) return ok();
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(ring_k);
+    REQUIRE_PTR(ring_v);
+    REQUIRE_PTR(ring_ks);
+    REQUIRE_PTR(ring_vs);
+    REQUIRE_PTR(pos);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(k_new);
+    OPTIONAL_PTR(v_new);
+    OPTIONAL_PTR(sink_len);
+    if (p->S > 0) {
+        REQUIRE_PTR(sink_k);
+        REQUIRE_PTR(sink_v);
+        REQUIRE_PTR(sink_ks);
+        REQUIRE_PTR(sink_vs);
+    }
+    swa::DecodeArgs a{};
+    a.q = q;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.ring_k = ring_k;
+    a.ring_v = ring_v;
+    a.ring_ks = ring_ks;
+    a.ring_vs = ring_vs;
+    a.sink_k = p->S > 0 ? sink_k : nullptr;
+    a.sink_v = p->S > 0 ? sink_v : nullptr;
+    a.sink_ks = p->S > 0 ? sink_ks : nullptr;
+    a.sink_vs = p->S > 0 ? sink_vs : nullptr;
+    a.pos = pos;
+    a.sink_len = sink_len;
+    a.out = out;
+    a.B = p->B;
+    a.Hq = p->Hq;
+    a.Hkv = p->Hkv;
+    a.D = p->D;
+    a.W = p->W;
+    a.S = p->S;
+    a.num_splits = 1;
+    a.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->D);
+    return hip_status(swa::launch_decode(a, (hipStream_t)stream), "swa_attn_decode launch");
+}
+
+long long swa_kv_budget_window(long long d_model, long long attn_dim, long long num_heads, long long num_kv_heads,
+                               long long num_layers, long long sites, long long max_seq_len) {
+    if (d_model <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_layers <= 0 || sites < 0 || max_seq_len <= 0 ||
+        attn_dim < 0)
+        return -1;
+    const long long budget = 11LL * 1024 * 1024 + 512LL * 1024;  // bytes for the whole KV cache
+    const long long group = 32;                                  // channels per fp32 scale
+    const long long floor_window = 160;
+    const long long head_dim = (attn_dim > 0 ? attn_dim : d_model) / num_heads;
+    const long long kv = num_kv_heads * head_dim;
+    const long long per_pos = num_layers * (2 * kv + 2 * (kv / group) * 4) + sites * (d_model + group * 4);
+    if (per_pos <= 0) return -1;
+    long long w = (budget / per_pos) / group * group;
+    if (w > max_seq_len) w = max_seq_len;
+    if (w < floor_window) w = floor_window;
+    return w;
+}
+
+long long swa_effective_kv_window(long long d_model, long long attn_dim, long long num_heads, long long num_kv_heads,
+                                  long long num_layers, long long sites, long long max_seq_len, long long kv_window) {
+    const long long w = swa_kv_budget_window(d_model, attn_dim, num_heads, num_kv_heads, num_layers, sites, max_seq_len);
+    if (w < 0 || kv_window < 0) return -1;
+    return kv_window != 0 && kv_window < w ? kv_window : w;
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// swa_internal.h -- kernel argument blocks and launchers behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "swa_common.h"
+
+namespace swa {
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* pk;  // pooled keys (compressed mode)
+    const void* pv;
+    const int32_t* seg;
+    const uint8_t* prefix;
+    const float* rope_cos;
+    const float* rope_sin;
+    void* out;
+    float* lse;
+    int B, Hq, Hkv, T, D;
+    int window;
+    int block;  // compress block, 0 = plain
+    int nblk;   // T / block
+    int rope_len;
+    float scale;
+    // workgroup geometry of the MFMA kernel: heads per workgroup and 32-row
+    // blocks per workgroup (hpw * rbs waves)
+    int hpw, rbs;
+};
+
+// Geometry the bf16 MFMA kernel uses for a given GQA group size.
+struct MfmaGeom {
+    int hpw, rbs;
+};
+inline MfmaGeom mfma_geometry(int G) {
+    MfmaGeom g;
+    g.hpw = G >= 4 ? 4 : G;
+    while (G % g.hpw) --g.hpw;
+    g.rbs = 4 / g.hpw;
+    if (g.rbs < 1) g.rbs = 1;
+    return g;
+}
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_debug_visibility(const PrefillArgs& a, bool mfma_geometry, uint8_t* mask, int32_t* count,
+                                   hipStream_t s);
+hipError_t launch_rope_table(double theta, int rope_len, int D, float* c, float* sn, hipStream_t s);
+hipError_t launch_pool_rope(int B, int H, int T, int D, int block, int dtype, const void* k_pre,
+                            const void* v, const float* c, const float* sn, int rope_len, void* pk,
+                            void* pv, hipStream_t s);
+hipError_t launch_kv_quantize(long long N, int D, const void* x, int8_t* xq, float* xs, hipStream_t s);
+
+struct DecodeArgs {
+    const void* q;
+    const void* k_new;
+    const void* v_new;
+    int8_t* ring_k;
+    int8_t* ring_v;
+    float* ring_ks;
+    float* ring_vs;
+    const int8_t* sink_k;
+    const int8_t* sink_v;
+    const float* sink_ks;
+    const float* sink_vs;
+    const int32_t* pos;
+    const int32_t* sink_len;
+    void* out;
+    float* partial;  // workspace for split-K partials (num_splits > 1)
+    int B, Hq, Hkv, D, W, S;
+    int num_splits;
+    float scale;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace swa

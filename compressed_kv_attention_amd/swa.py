@@ -1,0 +1,232 @@
+"""Thin ctypes binding over libswa.so (include/swa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libswa.so.  torch supplies device memory and the stream (the
+current torch stream of the tensors' device).  There is no CPU fallback: if
+the library is missing, or a call returns a non-OK status, a RuntimeError is
+raised with the library's message.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # must be imported before libswa.so is loaded: the two share torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libswa.so")
+
+SWA_OK, SWA_ERR_INVALID, SWA_ERR_UNSUPPORTED, SWA_ERR_HIP = 0, 1, 2, 3
+SWA_F32, SWA_BF16 = 0, 1
+
+EXPORTS = ("swa_last_error", "swa_version", "swa_attn_prefill", "swa_debug_visibility", "swa_rope_table",
+           "kv_pool_compress_rope", "swa_kv_quantize", "swa_decode_workspace_size", "swa_attn_decode",
+           "swa_kv_budget_window", "swa_effective_kv_window")
+
+
+class PrefillParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("T", ctypes.c_int),
+                ("D", ctypes.c_int), ("window", ctypes.c_int), ("compress_block", ctypes.c_int),
+                ("rope_len", ctypes.c_int), ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("D", ctypes.c_int),
+                ("W", ctypes.c_int), ("S", ctypes.c_int), ("scale", ctypes.c_float), ("num_splits", ctypes.c_int)]
+
+
+class SwaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libswa status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libswa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m compressed_kv_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, LL, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_size_t
+    L.swa_last_error.restype = ctypes.c_char_p
+    L.swa_last_error.argtypes = []
+    L.swa_version.restype = I
+    L.swa_attn_prefill.argtypes = [ctypes.POINTER(PrefillParams)] + [P] * 12
+    L.swa_attn_prefill.restype = I
+    L.swa_debug_visibility.argtypes = [ctypes.POINTER(PrefillParams), P, P, P, P, P]
+    L.swa_debug_visibility.restype = I
+    L.swa_rope_table.argtypes = [ctypes.c_double, I, I, P, P, P]
+    L.swa_rope_table.restype = I
+    L.kv_pool_compress_rope.argtypes = [I, I, I, I, I, I, P, P, P, P, I, P, P, P]
+    L.kv_pool_compress_rope.restype = I
+    L.swa_kv_quantize.argtypes = [LL, I, P, P, P, P]
+    L.swa_kv_quantize.restype = I
+    L.swa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams)]
+    L.swa_decode_workspace_size.restype = Z
+    L.swa_attn_decode.argtypes = [ctypes.POINTER(DecodeParams)] + [P] * 14 + [P, Z, P]
+    L.swa_attn_decode.restype = I
+    L.swa_kv_budget_window.argtypes = [LL] * 7
+    L.swa_kv_budget_window.restype = LL
+    L.swa_effective_kv_window.argtypes = [LL] * 8
+    L.swa_effective_kv_window.restype = LL
+    _lib = L
+    return L
+
+
+def _check(rc):
+    if rc != SWA_OK:
+        raise SwaError(rc, lib().swa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _swa_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return SWA_BF16
+    if t.dtype == torch.float32:
+        return SWA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def rope_table(theta: float, rope_len: int, D: int, device="cuda"):
+    """cos/sin tables [rope_len, D/2] fp32 (angle pos * theta^(-2i/D), fp64 on device)."""
+    c = torch.empty((rope_len, D // 2), dtype=torch.float32, device=device)
+    s = torch.empty_like(c)
+    _check(lib().swa_rope_table(float(theta), int(rope_len), int(D), _ptr(c), _ptr(s), _stream(c)))
+    return c, s
+
+
+def prefill_params(q, k, window, compress_block=0, rope_len=0, scale=0.0):
+    B, Hq, T, D = q.shape
+    return PrefillParams(B, Hq, k.shape[1], T, D, int(window), int(compress_block), int(rope_len), float(scale),
+                         _swa_dtype(q))
+
+
+def prefill(q, k, v, seg_ids=None, prefix=None, window=0, rope=None, pooled_k=None, pooled_v=None,
+            compress_block=0, scale=0.0, return_lse=False, out=None):
+    """Windowed+sink (or compressed) prefill attention.  q [B,Hq,T,D], k/v [B,Hkv,T,D]."""
+    _dev(q, "q")
+    _dev(k, "k", q.dtype)
+    _dev(v, "v", q.dtype)
+    _dev(seg_ids, "seg_ids", torch.int32)
+    _dev(prefix, "prefix", torch.uint8)
+    _dev(pooled_k, "pooled_k", q.dtype)
+    _dev(pooled_v, "pooled_v", q.dtype)
+    cos, sin = rope if rope is not None else (None, None)
+    _dev(cos, "rope_cos", torch.float32)
+    _dev(sin, "rope_sin", torch.float32)
+    rope_len = cos.shape[0] if cos is not None else 0
+    p = prefill_params(q, k, window, compress_block, rope_len, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib().swa_attn_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(pooled_k), _ptr(pooled_v),
+                                  _ptr(seg_ids), _ptr(prefix), _ptr(cos), _ptr(sin), _ptr(out), _ptr(lse),
+                                  _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def debug_visibility(B, Hq, Hkv, T, D, window, dtype=torch.bfloat16, seg_ids=None, prefix=None, compress_block=0,
+                     want_mask=True, device="cuda"):
+    """Mask [B,T,Tk] (uint8) and visible counts [B,T] exactly as the prefill kernel for `dtype` applies them."""
+    p = PrefillParams(B, Hq, Hkv, T, D, int(window), int(compress_block), 0, 0.0,
+                      SWA_BF16 if dtype == torch.bfloat16 else SWA_F32)
+    _dev(seg_ids, "seg_ids", torch.int32)
+    _dev(prefix, "prefix", torch.uint8)
+    Tk = T + (T // compress_block if compress_block else 0)
+    mask = torch.empty((B, T, Tk), dtype=torch.uint8, device=device) if want_mask else None
+    count = torch.empty((B, T), dtype=torch.int32, device=device)
+    _check(lib().swa_debug_visibility(ctypes.byref(p), _ptr(seg_ids), _ptr(prefix), _ptr(mask), _ptr(count),
+                                      _stream(count)))
+    return mask, count
+
+
+def pool_compress_rope(k_pre, v, block, rope=None, out=None):
+    """Mean-pool b-row blocks of k_pre and v ([B,H,T,D]); rotate pooled keys at block midpoints.
+
+    out: optional (pooled_k, pooled_v) tensors [B,H,T//block,D] to write into."""
+    _dev(k_pre, "k_pre")
+    _dev(v, "v", k_pre.dtype)
+    B, H, T, D = k_pre.shape
+    cos, sin = rope if rope is not None else (None, None)
+    rope_len = cos.shape[0] if cos is not None else 0
+    if out is None:
+        pk = torch.empty((B, H, T // block, D), dtype=k_pre.dtype, device=k_pre.device)
+        pv = torch.empty_like(pk)
+    else:
+        pk, pv = _dev(out[0], "pooled_k", k_pre.dtype), _dev(out[1], "pooled_v", k_pre.dtype)
+        if tuple(pk.shape) != (B, H, T // block, D) or tuple(pv.shape) != (B, H, T // block, D):
+            raise ValueError("pooled outputs must be [B, H, T // block, D]")
+    _check(lib().kv_pool_compress_rope(B, H, T, D, int(block), _swa_dtype(k_pre), _ptr(k_pre), _ptr(v), _ptr(cos),
+                                       _ptr(sin), int(rope_len), _ptr(pk), _ptr(pv), _stream(k_pre)))
+    return pk, pv
+
+
+def kv_quantize(x):
+    """bf16 [..., D] -> (int8 codes [..., D], fp32 scales [..., D/32])."""
+    _dev(x, "x", torch.bfloat16)
+    D = x.shape[-1]
+    N = x.numel() // D
+    xq = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    xs = torch.empty(x.shape[:-1] + (D // 32,), dtype=torch.float32, device=x.device)
+    _check(lib().swa_kv_quantize(N, D, _ptr(x), _ptr(xq), _ptr(xs), _stream(x)))
+    return xq, xs
+
+
+def decode(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos, sink_len=None, k_new=None,
+           v_new=None, scale=0.0, num_splits=0, out=None):
+    """One decode step; appends k_new/v_new into the ring (in place) first.  Returns out [B,Hq,D] bf16."""
+    _dev(q, "q", torch.bfloat16)
+    for name, t, dt in (("ring_k", ring_k, torch.int8), ("ring_v", ring_v, torch.int8),
+                        ("ring_ks", ring_ks, torch.float32), ("ring_vs", ring_vs, torch.float32),
+                        ("sink_k", sink_k, torch.int8), ("sink_v", sink_v, torch.int8),
+                        ("sink_ks", sink_ks, torch.float32), ("sink_vs", sink_vs, torch.float32),
+                        ("pos", pos, torch.int32), ("sink_len", sink_len, torch.int32),
+                        ("k_new", k_new, torch.bfloat16), ("v_new", v_new, torch.bfloat16)):
+        _dev(t, name, dt)
+    B, Hq, D = q.shape
+    Hkv, W = ring_k.shape[1], ring_k.shape[2]
+    S = sink_k.shape[2] if sink_k is not None else 0
+    p = DecodeParams(B, Hq, Hkv, D, W, S, float(scale), int(num_splits))
+    ws_bytes = lib().swa_decode_workspace_size(ctypes.byref(p))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().swa_attn_decode(ctypes.byref(p), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(ring_k), _ptr(ring_v),
+                                 _ptr(ring_ks), _ptr(ring_vs), _ptr(sink_k), _ptr(sink_v), _ptr(sink_ks),
+                                 _ptr(sink_vs), _ptr(pos), _ptr(sink_len), _ptr(out), _ptr(ws), ws_bytes,
+                                 _stream(q)))
+    return out
+
+
+def kv_budget_window(d_model, num_heads, num_kv_heads, num_layers, max_seq_len, sites=2, attn_dim=0):
+    return int(lib().swa_kv_budget_window(d_model, attn_dim, num_heads, num_kv_heads, num_layers, sites,
+                                          max_seq_len))
+
+
+def effective_kv_window(d_model, num_heads, num_kv_heads, num_layers, max_seq_len, kv_window, sites=2, attn_dim=0):
+    return int(lib().swa_effective_kv_window(d_model, attn_dim, num_heads, num_kv_heads, num_layers, sites,
+                                             max_seq_len, kv_window or 0))

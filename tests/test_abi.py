@@ -1,0 +1,142 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/swa.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_kv_attention_amd import swa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(swa.LIB_PATH), reason="libswa.so not built")
+
+FAKE = 0x10000  # an aligned address that validation must reject before it is ever dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("swa_attn_prefill", "swa_attn_decode", "kv_pool_compress_rope", "swa_last_error"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = swa.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(swa.EXPORTS) <= set(declared_functions())
+    assert L.swa_version() >= 100
+
+
+def _p(**kw):
+    d = dict(B=1, Hq=4, Hkv=2, T=64, D=64, window=16, compress_block=0, rope_len=0, scale=0.0, dtype=swa.SWA_BF16)
+    d.update(kw)
+    return swa.PrefillParams(**d)
+
+
+def _prefill(p, ptrs=None, seg=None, prefix=None, pk=None, pv=None, cos=None, sin=None, lse=None):
+    L = swa.lib()
+    q = k = v = out = ptrs
+    rc = L.swa_attn_prefill(ctypes.byref(p), q, k, v, pk, pv, seg, prefix, cos, sin, out, lse, None)
+    return rc, L.swa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(Hq=3, Hkv=2), swa.SWA_ERR_INVALID, "multiple of Hkv"),
+    (dict(window=-1), swa.SWA_ERR_INVALID, "window"),
+    (dict(D=48), swa.SWA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=7), swa.SWA_ERR_INVALID, "dtype"),
+    (dict(compress_block=-2), swa.SWA_ERR_INVALID, "compress_block"),
+    (dict(compress_block=4, window=0), swa.SWA_ERR_INVALID, "window >= 1"),
+    (dict(rope_len=10), swa.SWA_ERR_INVALID, "rope_len"),
+    (dict(T=200000), swa.SWA_ERR_UNSUPPORTED, "exceeds"),
+    (dict(scale=float("inf")), swa.SWA_ERR_INVALID, "scale"),
+])
+def test_prefill_rejects_bad_params(kw, code, text):
+    rc, msg = _prefill(_p(**kw), ptrs=FAKE)
+    assert rc == code and text in msg, (rc, msg)
+
+
+def test_prefill_rejects_null_and_misaligned_pointers():
+    rc, msg = _prefill(_p(), ptrs=None)
+    assert rc == swa.SWA_ERR_INVALID and "must not be NULL" in msg
+    rc, msg = _prefill(_p(), ptrs=FAKE + 2)
+    assert rc == swa.SWA_ERR_INVALID and "aligned" in msg
+    rc, msg = _prefill(_p(compress_block=4), ptrs=FAKE)           # pooled tensors missing
+    assert rc == swa.SWA_ERR_INVALID and "pooled_k" in msg
+    rc, msg = _prefill(_p(compress_block=4), ptrs=FAKE, seg=FAKE)
+    assert rc == swa.SWA_ERR_UNSUPPORTED and "seg_ids" in msg
+    rc, msg = _prefill(_p(rope_len=64), ptrs=FAKE)                # tables missing
+    assert rc == swa.SWA_ERR_INVALID and "rope_cos" in msg
+
+
+def test_empty_problems_are_ok_without_pointers():
+    assert _prefill(_p(B=0))[0] == swa.SWA_OK
+    assert _prefill(_p(T=0))[0] == swa.SWA_OK
+    L = swa.lib()
+    assert L.swa_kv_quantize(0, 64, None, None, None, None) == swa.SWA_OK
+    assert L.kv_pool_compress_rope(0, 1, 16, 64, 4, swa.SWA_BF16, None, None, None, None, 0, None, None, None) == 0
+    assert L.kv_pool_compress_rope(1, 1, 3, 64, 4, swa.SWA_BF16, None, None, None, None, 0, None, None, None) == 0
+    dp = swa.DecodeParams(0, 4, 2, 64, 8, 4, 0.0, 0)
+    assert L.swa_attn_decode(ctypes.byref(dp), *([None] * 14), None, 0, None) == swa.SWA_OK
+
+
+def test_debug_visibility_limits():
+    L = swa.lib()
+    p = _p(T=20000)
+    assert L.swa_debug_visibility(ctypes.byref(p), None, None, None, FAKE, None) == swa.SWA_ERR_UNSUPPORTED
+    p = _p()
+    assert L.swa_debug_visibility(ctypes.byref(p), None, None, None, None, None) == swa.SWA_ERR_INVALID
+    assert "count_out" in L.swa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(W=0), swa.SWA_ERR_INVALID, "W must be"),
+    (dict(S=-1), swa.SWA_ERR_INVALID, "S must be"),
+    (dict(D=128), swa.SWA_ERR_UNSUPPORTED, "head dim"),
+    (dict(Hq=12, Hkv=4), swa.SWA_ERR_UNSUPPORTED, "group size"),
+    (dict(Hq=5, Hkv=2), swa.SWA_ERR_INVALID, "multiple"),
+])
+def test_decode_rejects_bad_params(kw, code, text):
+    d = dict(B=2, Hq=4, Hkv=2, D=64, W=8, S=4, scale=0.0, num_splits=0)
+    d.update(kw)
+    dp = swa.DecodeParams(**d)
+    L = swa.lib()
+    rc = L.swa_attn_decode(ctypes.byref(dp), *([FAKE] * 14), None, 0, None)
+    assert rc == code and text in L.swa_last_error().decode()
+
+
+def test_decode_rejects_half_given_new_token():
+    dp = swa.DecodeParams(2, 4, 2, 64, 8, 4, 0.0, 0)
+    L = swa.lib()
+    args = [FAKE] * 14
+    args[2] = None                                             # v_new missing, k_new given
+    assert L.swa_attn_decode(ctypes.byref(dp), *args, None, 0, None) == swa.SWA_ERR_INVALID
+    assert "k_new and v_new" in L.swa_last_error().decode()
+
+
+def test_rope_and_quantize_validation():
+    L = swa.lib()
+    assert L.swa_rope_table(0.0, 4, 64, FAKE, FAKE, None) == swa.SWA_ERR_INVALID
+    assert L.swa_rope_table(1e4, 4, 63, FAKE, FAKE, None) == swa.SWA_ERR_INVALID
+    assert L.swa_kv_quantize(4, 48, FAKE, FAKE, FAKE, None) == swa.SWA_ERR_INVALID
+    assert L.kv_pool_compress_rope(1, 1, 16, 64, 0, 1, FAKE, FAKE, None, None, 0, FAKE, FAKE, None) == 1
+
+
+def test_budget_window_host_functions_match_golden_cases():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "budget_window.txt")) if l.strip() and not l.startswith("#")]
+    for r in rows:
+        d, ad, nh, nkv, L_, sites, msl, kvw, per_pos, bw, eff = (int(x) for x in r)
+        assert swa.kv_budget_window(d, nh, nkv, L_, msl, sites, ad) == bw, r
+        assert swa.effective_kv_window(d, nh, nkv, L_, msl, kvw, sites, ad) == eff, r
+    assert swa.kv_budget_window(0, 16, 4, 12, 100) == -1

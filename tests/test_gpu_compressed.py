@@ -1,0 +1,100 @@
+"""GPU parity of the compressed-KV path (block pooling + midpoint RoPE, then one
+softmax over [pooled blocks, exact keys]) against the CPU oracle.
+
+Source: [CA] "Compressed attention and the copy probe", sections "Two kinds of
+columns, pooled blocks and exact recent keys" and "Pool before rotating, not
+after".
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_kv_attention_amd import swa, workloads
+from gpu_util import assert_close, assert_lse_close, dev_input, sample_rows, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def run_compressed(w, q_override=None):
+    q = dev_input(w, "q") if q_override is None else q_override
+    k, v = dev_input(w, "k"), dev_input(w, "v")
+    rope = swa.rope_table(w["rope_theta"], w["T"], w["D"]) if w["rope_theta"] else None
+    pk, pv = swa.pool_compress_rope(k, v, w["compress_block"], rope)
+    out, lse = swa.prefill(q, k, v, window=w["window"], rope=rope, pooled_k=pk, pooled_v=pv,
+                           compress_block=w["compress_block"], return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse, pk, pv
+
+
+def oracle_compressed(w, rows=None):
+    return oracle.compressed_prefill(w["q"], w["k"], w["v"], w["window"], w["compress_block"],
+                                     theta=w["rope_theta"], rope_len=w["T"], rows=rows)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("block,rope_len_short", [(1, False), (3, False), (4, False), (16, False), (4, True)])
+def test_pool_kernel(dtype, block, rope_len_short):
+    w = workloads.prefill_case(2, 3, 3, 101, 64, 8, dtype, seed=block)
+    k, v = dev_input(w, "k"), dev_input(w, "v")
+    rl = 20 if rope_len_short else w["T"]
+    rope = swa.rope_table(10000.0, rl, 64)
+    pk, pv = swa.pool_compress_rope(k, v, block, rope)
+    torch.cuda.synchronize()
+    rk, rv = oracle.pool_rope(w["k"], w["v"], block, theta=10000.0, rope_len=rl)
+    # each pooled value is rounded once to the storage dtype
+    # (fp32 sums and rotation with fp32 tables, then one rounding to the storage dtype)
+    rtol = 1e-6 if dtype == "f32" else 2.0 ** -8
+    atol = 1e-6
+    for name, got, ref in (("pooled_k", pk, rk), ("pooled_v", pv, rv)):
+        g = to_np(got)
+        excess = np.abs(g - ref) - (rtol * np.abs(ref) + atol)
+        say(f"  {name} b={block}: max abs err {np.abs(g - ref).max():.2e}")
+        assert excess.max() <= 0
+
+
+CASES = []
+for dtype in ("f32", "bf16"):
+    for i, (B, H, Hkv, T, W, b) in enumerate([(1, 1, 1, 64, 8, 4), (2, 2, 2, 150, 16, 3), (1, 4, 2, 300, 32, 16),
+                                              (1, 2, 2, 257, 64, 1), (2, 2, 1, 129, 5, 7), (1, 1, 1, 100, 200, 4)]):
+        CASES.append(pytest.param(dtype, B, H, Hkv, T, W, b, i, id=f"{dtype}-{i}"))
+
+
+@pytest.mark.parametrize("dtype,B,H,Hkv,T,W,b,seed", CASES)
+def test_compressed_random_small(dtype, B, H, Hkv, T, W, b, seed):
+    w = workloads.prefill_case(B, H, Hkv, T, 64, W, dtype, seed=300 + seed, rope_theta=10000.0, compress_block=b)
+    say(f"case {dtype} B{B} {H}/{Hkv} T{T} W{W} b{b}")
+    out, lse, _, _ = run_compressed(w)
+    ref, ref_lse = oracle_compressed(w)
+    assert_close(to_np(out), ref, dtype, "out")
+    assert_lse_close(to_np(lse), ref_lse, dtype, "out")
+
+
+@pytest.mark.parametrize("T,W,b", [(200, 16, 4), (333, 64, 16), (129, 8, 3)])
+def test_compressed_visibility_bit_exact(T, W, b):
+    for dt in (torch.bfloat16, torch.float32):
+        mask, count = swa.debug_visibility(1, 4, 4, T, 64, W, dt, compress_block=b)
+        torch.cuda.synchronize()
+        ref = oracle.compressed_mask(T, W, b)
+        np.testing.assert_array_equal(mask.cpu().numpy()[0], ref)
+        np.testing.assert_array_equal(count.cpu().numpy()[0], ref.sum(axis=1))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("block", [4, 16])
+def test_compressed_full_size(dtype, block):
+    w = workloads.compressed(block=block, dtype=dtype)
+    B, H, T = w["B"], w["Hq"], w["T"]
+    say(f"compressed {dtype} b={block}: B{B} H{H} T{T} W{w['window']}")
+    out, lse, _, _ = run_compressed(w)
+    rng = np.random.default_rng(block)
+    extra = [0, 255, 256, 258, 259, 260, 261, 511, 512, 1000, 2047, 4000, T - 1]
+    rows = sample_rows(rng, B, H, T, 1500, extra)
+    ref, ref_lse = oracle_compressed(w, rows)
+    assert_close(to_np(out).reshape(-1, w["D"])[rows], ref, dtype, f"b={block}")
+    assert_lse_close(lse.cpu().numpy().reshape(-1)[rows], ref_lse, dtype, f"b={block}")
+    # the last row reads the pooled blocks that cleared the window plus W exact keys
+    q0 = torch.zeros_like(dev_input(w, "q"))
+    _, lse0, _, _ = run_compressed(w, q_override=q0)
+    n_last = np.rint(np.exp(lse0[0, 0, T - 1].item()))
+    assert n_last == (T - w["window"] + 1) // block + w["window"]

@@ -1,0 +1,114 @@
+"""GPU parity of the int8 quantizer and the ring + sink decode step.
+
+Source: [NS] "256-token滑动窗口+KV sink：Needle 2工具钉住机制源码分析", section
+"256-token 滑动窗口：源码走读" (decode keeps recent | sink, no packing term);
+cache layout priced by [NW] "How the 256-Token Sliding Window Works with Tools
+as KV Sinks in Needle", section "Effective KV Window: Bounding the Cache Size".
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_kv_attention_amd import swa, workloads
+from gpu_util import assert_close, bf16_dev, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def test_quantizer_bit_exact():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((4096, 64)) * rng.uniform(1e-3, 30, (4096, 1))).astype(np.float32)
+    x[3, :32] = 0.0
+    x[7, 32:] = 0.0
+    x[11, 0] = 127.0
+    x[11, 1:33] = np.arange(-16, 16) + 0.5          # ties with scale 1 (rows mix groups)
+    bits, vals = workloads.bf16_round(x)
+    q, s = swa.kv_quantize(bf16_dev(bits))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize(vals)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def make_caches(w):
+    """Quantize the caches on the GPU (for the kernel) and in the oracle (for the
+    reference), and check the two agree bit for bit."""
+    dev, ref = {}, {}
+    for name in ("ring_k", "ring_v", "sink_k", "sink_v"):
+        q, s = swa.kv_quantize(bf16_dev(w[name + "_bits"]))
+        dev[name], dev[name[:-2] + ("_ks" if name.endswith("k") else "_vs")] = q, s
+        shp = w[name].shape
+        rq, rs = oracle.quantize(w[name].reshape(-1, shp[-1]))
+        ref[name] = rq.reshape(shp)
+        ref[name[:-2] + ("_ks" if name.endswith("k") else "_vs")] = rs.reshape(shp[:-1] + (shp[-1] // 32,))
+    torch.cuda.synchronize()
+    for k in ref:
+        np.testing.assert_array_equal(dev[k].cpu().numpy(), ref[k])
+    return dev, ref
+
+
+def run_decode(w, dev, append=True):
+    out = swa.decode(bf16_dev(w["q_bits"]), dev["ring_k"], dev["ring_v"], dev["ring_ks"], dev["ring_vs"],
+                     dev["sink_k"], dev["sink_v"], dev["sink_ks"], dev["sink_vs"],
+                     torch.from_numpy(w["pos"]).cuda(), torch.from_numpy(w["sink_len"]).cuda(),
+                     bf16_dev(w["k_new_bits"]) if append else None, bf16_dev(w["v_new_bits"]) if append else None)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_decode(w, ref, append=True):
+    return oracle.decode(w["q"], ref["ring_k"], ref["ring_v"], ref["ring_ks"], ref["ring_vs"], ref["sink_k"],
+                         ref["sink_v"], ref["sink_ks"], ref["sink_vs"], w["pos"], w["sink_len"],
+                         w["k_new"] if append else None, w["v_new"] if append else None)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,W,S,pos,sink_len", [
+    (4, 4, 2, 64, 8, 5, [5, 7, 12, 33], [5, 3, 5, 0]),            # partial ring, full, wrapped
+    (3, 8, 1, 64, 16, 4, [4, 19, 100], [4, 4, 1]),                # G = 8
+    (2, 2, 2, 32, 6, 3, [3, 50], [3, 2]),                         # D = 32, G = 1
+    (5, 16, 4, 64, 256, 256, [256, 300, 511, 512, 20000], [256, 256, 100, 0, 256]),
+    (2, 4, 2, 64, 1, 0, [0, 9], [0, 0]),                          # W = 1, no sinks
+    (3, 4, 2, 64, 37, 11, [11, 47, 48], [11, 11, 11]),            # odd sizes
+])
+def test_decode_small(B, Hq, Hkv, D, W, S, pos, sink_len):
+    w = workloads.decode_case(seed=B * 100 + W, B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, sink_len=sink_len)
+    w["pos"] = np.asarray(pos, np.int32)
+    say(f"decode B{B} {Hq}/{Hkv} D{D} W{W} S{S} pos {pos} sink_len {sink_len}")
+    dev, ref = make_caches(w)
+    out = run_decode(w, dev)
+    r_out, _, rk, rv, rks, rvs = oracle_decode(w, ref)
+    assert_close(to_np(out), r_out, "bf16", "decode")
+    for name, r in (("ring_k", rk), ("ring_v", rv), ("ring_ks", rks), ("ring_vs", rvs)):
+        np.testing.assert_array_equal(dev[name].cpu().numpy(), r)
+
+
+def test_decode_without_append_and_q0_counts():
+    B, Hq, Hkv, D, W, S = 3, 4, 2, 64, 16, 8
+    w = workloads.decode_case(seed=77, B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, sink_len=[8, 2, 0])
+    w["pos"] = np.array([8, 30, 5], np.int32)
+    dev, ref = make_caches(w)
+    out = run_decode(w, dev, append=False)
+    r_out, *_ = oracle_decode(w, ref, append=False)
+    assert_close(to_np(out), r_out, "bf16", "no-append")
+    # q = 0: uniform weights -> output is the mean of the visible dequantized values
+    w0 = dict(w)
+    w0["q_bits"] = np.zeros_like(w["q_bits"])
+    w0["q"] = np.zeros_like(w["q"])
+    out0 = run_decode(w0, dev, append=False)
+    r0, lse0, *_ = oracle_decode(w0, ref, append=False)
+    n = np.rint(np.exp(lse0)).astype(int)
+    for b, (p, sl) in enumerate(zip(w["pos"], w["sink_len"])):
+        assert np.all(n[b] == sl + min(W, p - sl + 1))
+    assert_close(to_np(out0), r0, "bf16", "q0")
+
+
+def test_decode_full_size_one_layer():
+    w = workloads.decode_case(seed=5)
+    say(f"decode full: B{w['B']} {w['Hq']}/{w['Hkv']} D{w['D']} W{w['W']} S{w['S']}")
+    dev, ref = make_caches(w)
+    out = run_decode(w, dev)
+    r_out, _, rk, rv, rks, rvs = oracle_decode(w, ref)
+    assert_close(to_np(out), r_out, "bf16", "decode full")
+    np.testing.assert_array_equal(dev["ring_k"].cpu().numpy(), rk)
+    np.testing.assert_array_equal(dev["ring_vs"].cpu().numpy(), rvs)
