@@ -75,7 +75,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int b = blockIdx.x / a.Hkv;
     const int hkv = blockIdx.x % a.Hkv;
     const int W = a.W, S = a.S;
-    const int pos = a.pos[b];
+    const int pos_in = a.pos[b];
+    const int pos = pos_in < 0 ? -1 : pos_in;  // a negative position appends nothing and sees only sinks
     int sl = a.sink_len ? a.sink_len[b] : S;
     sl = sl < 0 ? 0 : (sl > S ? S : sl);
     const size_t bh = (size_t)b * a.Hkv + hkv;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const float* svs = a.sink_vs ? a.sink_vs + bh * S * GROUPS : nullptr;
 
     // 1. append the new token into slot pos % W (waves 0 and 1: K and V)
-    if (a.k_new && wave < 2) {
+    if (a.k_new && wave < 2 && pos >= 0) {
         const uint16_t* src = (const uint16_t*)(wave == 0 ? a.k_new : a.v_new) + bh * D;
         const int slot = pos % W;
         if (lane < D) {

@@ -247,6 +247,11 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
                 const bf16x8 ka = *(const bf16x8*)&sm.ks[st * SUB + lq][16 * c + 8 * h];
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], s, 0, 0, 0);
             }
+            // Scores leave the accumulator into plain registers; the mask is applied
+            // with selects (no divergent writes into the MFMA result vector).
+            float sv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sv[j] = s[j];
             if (cls == TILE_PARTIAL) {
                 const int pooled_n = (kind == COL_POOLED && row_ok)
                                          ? pooled_visible_count(my_q, a.window, a.block, a.nblk)
@@ -256,16 +261,21 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
                     const int kidx = st * SUB + 8 * (j >> 2) + 4 * h + (j & 3);
                     const int gk = tile * BN + kidx;
                     bool vis;
-                    if (!row_ok) vis = false;
-                    else if (kind == COL_POOLED) vis = gk < pooled_n;
-                    else if (plain) vis = visible_plain(seg_q, sm.kseg[kidx], sm.ksink[kidx] != 0, my_q, gk, a.window);
-                    else vis = visible_exact_window(my_q, gk, a.window);
-                    if (!vis) s[j] = kNegInf;
+                    if (kind == COL_POOLED) {
+                        vis = gk < pooled_n;
+                    } else if (plain) {
+                        const int seg_k = sm.kseg[kidx];
+                        const bool sink_k = sm.ksink[kidx] != 0;
+                        vis = visible_plain(seg_q, seg_k, sink_k, my_q, gk, a.window);
+                    } else {
+                        vis = visible_exact_window(my_q, gk, a.window);
+                    }
+                    sv[j] = (vis & row_ok) ? sv[j] : kNegInf;
                 }
             }
-            float mx = s[0];
+            float mx = sv[0];
 #pragma unroll
-            for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
+            for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sv[j]);
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             const float m_new = fmaxf(m_run, mx);
             const float base = (m_new == kNegInf) ? 0.f : m_new * c_log2;
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
             float psum = 0.f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                p[j] = __builtin_amdgcn_exp2f(s[j] * c_log2 - base);
+                p[j] = __builtin_amdgcn_exp2f(sv[j] * c_log2 - base);
                 psum += p[j];
             }
             l_run = l_run * corr + psum;

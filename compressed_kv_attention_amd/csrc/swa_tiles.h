@@ -20,15 +20,16 @@ enum : int { TILE_SKIP = 0, TILE_FULL = 1, TILE_PARTIAL = 2 };
 enum : int { COL_EXACT = 0, COL_POOLED = 1 };
 
 // Element predicate of plain mode.
+// (Evaluated without short-circuit branches.)
 __device__ __forceinline__ bool visible_plain(int seg_q, int seg_k, bool sink_k, int q, int k, int window) {
-    bool keep = (seg_q > 0) && (seg_k == seg_q) && (k <= q);
-    if (window != 0) keep = keep && (((q - k) < window) || sink_k);
-    return keep;
+    const bool keep = (seg_q > 0) & (seg_k == seg_q) & (k <= q);
+    const bool in_window = (window == 0) | ((q - k) < window) | sink_k;
+    return keep & in_window;
 }
 
 // Exact-key predicate of compressed mode: causal window, no segments, no sinks.
 __device__ __forceinline__ bool visible_exact_window(int q, int t, int window) {
-    return t <= q && (q - t) < window;
+    return (t <= q) & ((q - t) < window);
 }
 
 // Number of pooled blocks visible to row q: blocks j with (j+1)*b <= q-W+1,
