@@ -90,6 +90,7 @@ def main():
         per_copy = (q.numel() * 2 + k.numel() * 4) * 2
         n = max(2, min(16, ROTATE_BYTES // per_copy + 1))
         bufs = [(q.clone(), k.clone(), v.clone(), torch.empty_like(q)) for _ in range(n)]
+        ws = swa.prefill_workspace(q, k, w["window"], rope)
         _, count = swa.debug_visibility(w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["window"], torch.bfloat16,
                                         seg, pre, want_mask=False)
         nvis = int(count.to(torch.int64).sum().item())
@@ -98,7 +99,7 @@ def main():
 
         def launch(i):
             qq, kk, vv, oo = bufs[i % n]
-            swa.prefill(qq, kk, vv, seg, pre, w["window"], rope=rope, out=oo)
+            swa.prefill(qq, kk, vv, seg, pre, w["window"], rope=rope, out=oo, workspace=ws)
         p = Part(name, launch, n, flops, bytes_, kernel="prefill_bf16_kernel")
         p.extra = dict(B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], T=w["T"], D=w["D"], window=w["window"],
                        visible_pairs_per_head=nvis)
@@ -117,6 +118,7 @@ def main():
             kk, vv = k.clone(), v.clone()
             pk, pv = swa.pool_compress_rope(kk, vv, block, rope)
             bufs.append((q.clone(), kk, vv, torch.empty_like(q), pk, pv))
+        ws = swa.prefill_workspace(q, k, w["window"], rope, block)
         _, count = swa.debug_visibility(w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["window"], torch.bfloat16,
                                         compress_block=block, want_mask=False)
         nvis = int(count.to(torch.int64).sum().item())
@@ -129,7 +131,7 @@ def main():
             qq, kk, vv, oo, pk, pv = bufs[i % n]
             swa.pool_compress_rope(kk, vv, block, rope, out=(pk, pv))
             swa.prefill(qq, kk, vv, window=w["window"], rope=rope, pooled_k=pk, pooled_v=pv, compress_block=block,
-                        out=oo)
+                        out=oo, workspace=ws)
         p = Part(name, launch_step, n, flops, bytes_, kernel="prefill_bf16_kernel")
         p.extra = dict(B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], T=w["T"], D=w["D"], window=w["window"], block=block,
                        visible_pairs_per_head=nvis)

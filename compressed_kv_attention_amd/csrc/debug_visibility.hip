@@ -13,7 +13,7 @@ namespace swa {
 namespace {
 
 constexpr int kDbgMaxT = kDebugMaxT;
-constexpr int kDbgMaxRows = 128;
+constexpr int kDbgMaxRows = 256;
 constexpr int kDbgSub = 32;
 constexpr int kDbgSubTiles = kDbgMaxT / kDbgSub;  // per column kind
 
@@ -24,10 +24,11 @@ struct DbgGeom {
 __global__ __launch_bounds__(256) void debug_vis_kernel(PrefillArgs a, DbgGeom g, uint8_t* mask, int32_t* count) {
     __shared__ uint32_t enum_bits[2][kDbgMaxT / 32 / 32 + 1];
     __shared__ uint32_t sink_bits[kDbgMaxT / 32 / 32 + 1];
-    __shared__ int row_sum[kDbgMaxRows / 32][4];
+    __shared__ int row_sum[kDbgMaxRows / 32][4];  // row groups of 32 (MFMA) or 64 (f32)
     __shared__ int key_sum[kDbgSubTiles][4];
     __shared__ int cnt[kDbgMaxRows];
     __shared__ int dup;
+    __shared__ int red[2];
 
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int T = a.T, b = blockIdx.z;
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void debug_vis_kernel(PrefillArgs a, DbgGeom g
     if (tid == 0) dup = 0;
 
     const TilePlan plan = plan_tiles(q0, q1, a.window, a.block, a.nblk, a.prefix != nullptr, g.BN);
-    if (plan.sink_keys > 0) scan_sink_tiles(pre, plan.sink_keys, g.BN, sink_bits, tid, nthreads);
+    plan_sink_tiles(plan, seg, pre, T, q0, q1, g.BN, red, sink_bits, tid, nthreads);
     __syncthreads();
     if (tid == 0) {
         TileIter it;
@@ -74,22 +75,24 @@ __global__ __launch_bounds__(256) void debug_vis_kernel(PrefillArgs a, DbgGeom g
         row_sum[gi][2] = smin;
         row_sum[gi][3] = smax;
     }
-    // exact-column sub-tile summaries
+    // exact-column sub-tile summaries (same meaning as the kernels' ballots)
     const int nsub = (T + kDbgSub - 1) / kDbgSub;
     for (int si = tid; si < nsub; si += nthreads) {
-        int smin = 0x7fffffff, smax = (int)0x80000000, any = 0, all = 1;
-        for (int k = si * kDbgSub; k < min(si * kDbgSub + kDbgSub, T); ++k) {
-            const int s = plain ? (seg ? seg[k] : 1) : 0;
-            const int sk = (plain && pre) ? (pre[k] != 0) : 0;
-            smin = min(smin, s);
-            smax = max(smax, s);
+        const int k_lo = si * kDbgSub, k_hi = min(si * kDbgSub + kDbgSub, T);
+        const int s_first = plain ? (seg ? max(seg[k_lo], 0) : 1) : 0;
+        bool uniform = true, any = false, all = true;
+        for (int k = k_lo; k < k_hi; ++k) {
+            const int s = plain ? (seg ? max(seg[k], 0) : 1) : 0;
+            const bool sk = plain && pre && pre[k] != 0;
+            uniform &= s == s_first;
             any |= sk;
             all &= sk;
         }
-        key_sum[si][0] = smin;
-        key_sum[si][1] = smax;
-        key_sum[si][2] = any;
-        key_sum[si][3] = all;
+        const KeySum ks = make_key_sum(uniform, s_first, any, all);
+        key_sum[si][0] = ks.smin;
+        key_sum[si][1] = ks.smax;
+        key_sum[si][2] = ks.any_sink;
+        key_sum[si][3] = ks.all_sink;
     }
     __syncthreads();
 
@@ -122,14 +125,17 @@ __global__ __launch_bounds__(256) void debug_vis_kernel(PrefillArgs a, DbgGeom g
                 ks.all_sink = key_sum[si][3];
                 cls = classify_exact(rs, ks, k0, kDbgSub, T, a.window, plain);
             }
+            const int seg_q = plain ? (seg ? seg[q] : 1) : 1;
+            const bool row_vis = seg_q > 0;
+            const unsigned wlim = window_limit(a.window);
             if (cls == TILE_FULL) {
                 vis = true;
+            } else if (cls == TILE_PARTIAL_POS) {
+                vis = row_vis && visible_pos(q - key, wlim);
             } else if (cls == TILE_PARTIAL) {
                 if (pooled) vis = key < pooled_visible_count(q, a.window, a.block, a.nblk);
-                else if (plain)
-                    vis = visible_plain(seg ? seg[q] : 1, seg ? seg[key] : 1, pre ? pre[key] != 0 : false, q, key,
-                                        a.window);
-                else vis = visible_exact_window(q, key, a.window);
+                else vis = row_vis && visible_full(q - key, wlim, pack_key_info(seg ? seg[key] : 1, pre && pre[key] != 0),
+                                                   seg_q);
             }
         }
         if (mask) mask[((size_t)b * T + q) * Tk + col] = vis ? 1 : 0;

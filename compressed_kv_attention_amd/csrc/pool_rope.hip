@@ -1,4 +1,5 @@
-// pool_rope.hip -- RoPE tables and block pooling of the compressed variant.
+// pool_rope.hip -- the pre-passes of a prefill: RoPE tables, key rotation,
+// block pooling of the compressed variant and the packed per-key mask info.
 //
 // [CA] "Compressed attention and the copy probe", section "Pool before
 // rotating, not after": keys are mean-pooled over blocks of b rows BEFORE
@@ -8,6 +9,7 @@
 // (i, i + D/2) with angle pos * theta^(-2i/D).
 #include "swa_common.h"
 #include "swa_internal.h"
+#include "swa_tiles.h"
 
 namespace swa {
 namespace {
@@ -78,7 +80,96 @@ __global__ void pool_rope_kernel(long long N, int T, int D, int block, int nblk,
     store_elem<BF16>(pv, out_base + i + half, v2);
 }
 
+// Rotate every row t of x [N, T, D] at position t (rotate-half pairs
+// (i, i + D/2)); one thread per 8 channel pairs, 16-byte loads and stores.
+// Used to rotate the keys of a prefill once instead of once per query block
+// that reads them.
+__global__ void rope_rows_bf16_kernel(long long rows, int T, int D, const uint16_t* x, const float* cs,
+                                      const float* sn, uint16_t* y) {
+    const int half = D / 2;
+    const int chunks = half / 8;
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * chunks) return;
+    const long long row = idx / chunks;
+    const int i0 = (int)(idx % chunks) * 8;
+    const int t = (int)(row % T);
+    const size_t base = (size_t)row * D;
+    const uint4 w1 = *(const uint4*)(x + base + i0);
+    const uint4 w2 = *(const uint4*)(x + base + half + i0);
+    const float4 c0 = *(const float4*)(cs + (size_t)t * half + i0);
+    const float4 c1 = *(const float4*)(cs + (size_t)t * half + i0 + 4);
+    const float4 s0 = *(const float4*)(sn + (size_t)t * half + i0);
+    const float4 s1 = *(const float4*)(sn + (size_t)t * half + i0 + 4);
+    const uint32_t a[4] = {w1.x, w1.y, w1.z, w1.w};
+    const uint32_t bb[4] = {w2.x, w2.y, w2.z, w2.w};
+    const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    uint32_t o1[4], o2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x1l = __uint_as_float(a[i] << 16), x1h = __uint_as_float(a[i] & 0xffff0000u);
+        const float x2l = __uint_as_float(bb[i] << 16), x2h = __uint_as_float(bb[i] & 0xffff0000u);
+        const float cl = c[2 * i], ch = c[2 * i + 1], sl = s[2 * i], sh = s[2 * i + 1];
+        o1[i] = f32_to_bf16_bits(x1l * cl - x2l * sl) | (f32_to_bf16_bits(x1h * ch - x2h * sh) << 16);
+        o2[i] = f32_to_bf16_bits(x2l * cl + x1l * sl) | (f32_to_bf16_bits(x2h * ch + x1h * sh) << 16);
+    }
+    *(uint4*)(y + base + i0) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+    *(uint4*)(y + base + half + i0) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+}
+
+__global__ void rope_rows_f32_kernel(long long rows, int T, int D, const float* x, const float* cs, const float* sn,
+                                     float* y) {
+    const int half = D / 2;
+    const int chunks = half / 4;
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * chunks) return;
+    const long long row = idx / chunks;
+    const int i0 = (int)(idx % chunks) * 4;
+    const int t = (int)(row % T);
+    const size_t base = (size_t)row * D;
+    const float4 a = *(const float4*)(x + base + i0);
+    const float4 bb = *(const float4*)(x + base + half + i0);
+    const float4 c = *(const float4*)(cs + (size_t)t * half + i0);
+    const float4 s = *(const float4*)(sn + (size_t)t * half + i0);
+    *(float4*)(y + base + i0) = make_float4(a.x * c.x - bb.x * s.x, a.y * c.y - bb.y * s.y, a.z * c.z - bb.z * s.z,
+                                            a.w * c.w - bb.w * s.w);
+    *(float4*)(y + base + half + i0) = make_float4(bb.x * c.x + a.x * s.x, bb.y * c.y + a.y * s.y,
+                                                   bb.z * c.z + a.z * s.z, bb.w * c.w + a.w * s.w);
+}
+
+// Packed key info of every key of a plain prefill: segment id (negative ids
+// count as 0, padding) with the sink flag in bit 31, one int32 per key, so the
+// attention kernel stages it with 4-byte copies.  [NW section "KV Sinks for
+// Tools: Pinning Critical Context"]: the packing and sink terms of the mask.
+__global__ void key_info_kernel(long long n, const int32_t* seg, const uint8_t* prefix, int32_t* info) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    info[i] = pack_key_info(seg ? seg[i] : 1, prefix ? prefix[i] != 0 : false);
+}
+
 }  // namespace
+
+hipError_t launch_key_info(long long n, const int32_t* seg, const uint8_t* prefix, int32_t* info, hipStream_t s) {
+    const int threads = 256;
+    hipLaunchKernelGGL(key_info_kernel, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s, n, seg,
+                       prefix, info);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_rows(long long rows, int T, int D, int dtype, const void* x, const float* cs,
+                            const float* sn, void* y, hipStream_t s) {
+    const int threads = 256;
+    if (dtype == 1) {
+        const long long n = rows * (D / 16);
+        hipLaunchKernelGGL(rope_rows_bf16_kernel, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s,
+                           rows, T, D, (const uint16_t*)x, cs, sn, (uint16_t*)y);
+    } else {
+        const long long n = rows * (D / 8);
+        hipLaunchKernelGGL(rope_rows_f32_kernel, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s,
+                           rows, T, D, (const float*)x, cs, sn, (float*)y);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_rope_table(double theta, int rope_len, int D, float* c, float* sn, hipStream_t s) {
     const long long n = (long long)rope_len * (D / 2);

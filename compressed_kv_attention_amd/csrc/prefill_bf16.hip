@@ -7,16 +7,27 @@
 // (sections "Two kinds of columns, pooled blocks and exact recent keys" and
 // "Pool before rotating, not after").
 //
-// Work decomposition.  A workgroup owns one (batch, kv head) pair and
-// 32 * rbs query rows for hpw query heads of that kv head's GQA group; each
-// of its hpw * rbs waves owns 32 rows of one head.  The heads of a group share
-// every K/V tile the workgroup stages in LDS.
+// Work decomposition.  A workgroup of 8 waves owns one (batch, kv head) pair
+// and 32 * rbs query rows for hpw query heads of that kv head's GQA group
+// (hpw * rbs = 8); each wave owns 32 rows of one head.  The heads of a group
+// share every K/V tile staged in LDS.  Workgroups are numbered so that each XCD
+// (and its L2) gets a contiguous run of query blocks of the same (batch, kv
+// head), which read overlapping key tiles.
 //
-// Per key tile of 64 keys (K row-major, V transposed in LDS), each wave works
-// on two 32-key sub-tiles:
+// Staging.  Key tiles of 64 keys go from global memory straight into LDS
+// (global_load_lds, 16 bytes per lane, no registers), three buffers deep: while
+// tile t is computed, tiles t+1 and t+2 are in flight.  K and V are stored
+// row-major with an XOR swizzle of their 16-byte chunks chosen so that the MFMA
+// operand reads hit distinct banks; V is read column-wise with
+// ds_read_b64_tr_b16.  With RoPE, q is rotated here as it is loaded; the keys
+// arrive already rotated (the library rotates them once, in a pre-pass).
+//
+// Per tile each wave works on two 32-key sub-tiles:
 //   S^T = K Q^T      4 x v_mfma_f32_32x32x16_bf16 (keys are the M rows)
 //   online softmax   per query = per lane column, so the running max, sum
-//                    and rescale are lane-local (one xor-32 exchange for max)
+//                    and rescale are lane-local (one xor-32 exchange for max);
+//                    the output is rescaled only when a row max grows by more
+//                    than 2^8 (the stale max is used consistently otherwise)
 //   O^T += V^T P^T   2 x 2 MFMAs; P^T comes straight from the S^T registers
 // Sub-tiles the mask hides completely are skipped, sub-tiles it shows
 // completely skip the element predicate (swa_tiles.h).
@@ -24,22 +35,185 @@
 #include "swa_internal.h"
 #include "swa_tiles.h"
 
+// Optional phase-time accounting for profiling builds; no code in normal builds.
+#ifndef SWA_TRACE_DECL
+#define SWA_TRACE_DECL
+#define SWA_TRACE(slot)
+#endif
+
 namespace swa {
 namespace {
 
 constexpr int BN = 64;   // keys per LDS tile
 constexpr int SUB = 32;  // keys per MFMA sub-tile
+constexpr int NBUF = 3;  // LDS tile buffers
 constexpr int kSinkWords = (kMaxT / BN + 31) / 32;
+constexpr float kRescaleLog2 = 8.0f;  // rescale when the max grows by > 2^8
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS access inside the main loop goes through these helpers.  While tiles
+// are in flight through global_load_lds, the compiler would otherwise wait
+// for every outstanding load before any LDS access (it cannot tell the three
+// buffers apart); here each wait is explicit.  After issuing reads, call
+// lds_wait() and then lds_tie() on every result before using it.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// LDS byte offset of a pointer into __shared__ memory (device pass only; the
+// host pass never runs device functions).
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(uint32_t, (__attribute__((address_space(3))) const char*)p);
+#else
+    (void)p;
+    return 0u;
+#endif
+}
+__device__ __forceinline__ u32x4 ds_read128(uint32_t addr) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ uint32_t ds_read32(uint32_t addr) {
+    uint32_t r;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ uint32_t ds_read_u8(uint32_t addr) {
+    uint32_t r;
+    asm volatile("ds_read_u8 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ void ds_write32(uint32_t addr, uint32_t v) {
+    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v));
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"); }
+template <typename X>
+__device__ __forceinline__ void lds_tie(X& x) {
+    asm volatile("" : "+v"(x));
+}
+
+// s_waitcnt with vmcnt <= n (n < 16), lgkmcnt = 0, expcnt untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 16, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N));
+}
+__device__ __forceinline__ void barrier_raw() { asm volatile("s_barrier"); }
+__device__ __forceinline__ void wait_vm_upto(int n) {  // n = loads that may stay in flight
+    switch (n) {
+        case 0: wait_vm_lgkm0<0>(); break;
+        case 1: wait_vm_lgkm0<1>(); break;
+        case 2: wait_vm_lgkm0<2>(); break;
+        case 3: wait_vm_lgkm0<3>(); break;
+        default: wait_vm_lgkm0<4>(); break;
+    }
+}
 
 template <int D>
 struct SmemBf16 {
-    uint16_t ks[BN][D + 8];  // K tile, row-major, padded rows
-    uint16_t vt[D][BN + 8];  // V tile, transposed (key-contiguous per channel)
-    int kseg[BN];
-    uint8_t ksink[BN];
-    int ksum[BN / SUB][4];  // per sub-tile: seg min, seg max, any sink, all sink
+    uint16_t k[NBUF][BN * D];  // K tiles, row-major, 16-byte chunks swizzled
+    uint16_t v[NBUF][BN * D];  // V tiles, row-major, 16-byte chunks swizzled
+    int kinfo[NBUF][BN];       // packed segment | sink << 31 of the tile's keys
+    int ksum[NBUF][BN / SUB][4];  // per sub-tile: seg min, seg max, any sink, all sink
     uint32_t sink_bits[kSinkWords];
+    int red[2];
 };
+
+// Swizzled position (in 16-byte chunks) of chunk c of key row k.  K: rows that
+// share LDS banks get different chunk orders, so the 32 rows one MFMA operand
+// read touches are conflict free.  V: the four rows one transpose read covers
+// per half-wave fall into different bank halves.
+template <int D>
+__device__ __forceinline__ int k_chunk(int k, int c) {
+    constexpr int CPR = D / 8;  // chunks per row
+    return k * CPR + (c ^ ((k * CPR / 16) % CPR));
+}
+template <int D>
+__device__ __forceinline__ int v_chunk(int k, int c) {
+    constexpr int CPR = D / 8;
+    return k * CPR + (D == 64 ? (c ^ (((k >> 1) & 1) * 4)) : c);
+}
+
+// Issue the global->LDS loads of one tile into buffer `buf`: wave w moves
+// 1 KB of K and 1 KB of V (64 lanes x 16 bytes) per instruction; wave 0 also
+// moves the keys' segment ids and sink flags.  Rows past the last key load a
+// clamped row (finite data, masked later).
+template <int D>
+__device__ __forceinline__ int issue_tile(const PrefillArgs& a, SmemBf16<D>& sm, int buf, int kind, int tile, int b,
+                                          int hkv, int wave, int lane) {
+    int issued = 0;
+    constexpr int CPR = D / 8;
+    constexpr int ROWS_PER_LOAD = 64 / CPR;  // key rows per wave instruction
+    const bool pooled = kind == COL_POOLED;
+    const int nkeys = pooled ? a.nblk : a.T;
+    const size_t head_off = ((size_t)b * a.Hkv + hkv) * (size_t)nkeys * D;
+    const uint16_t* kg = (const uint16_t*)(pooled ? a.pk : a.k) + head_off;
+    const uint16_t* vg = (const uint16_t*)(pooled ? a.pv : a.v) + head_off;
+    const int k0 = tile * BN;
+    for (int ld = wave; ld < BN / ROWS_PER_LOAD; ld += kMfmaWaves) {
+        const int kr = ld * ROWS_PER_LOAD + lane / CPR;  // key row in the tile
+        const int pc = lane % CPR;                        // physical chunk
+        const int gk = min(k0 + kr, nkeys - 1);
+        // the lane writes LDS chunk (ld * 64 + lane); pick the logical chunk stored there
+        const int ck = pc ^ ((kr * CPR / 16) % CPR);
+        const int cv = D == 64 ? (pc ^ (((kr >> 1) & 1) * 4)) : pc;
+        __builtin_amdgcn_global_load_lds(kg + (size_t)gk * D + 8 * ck, (lds_void*)&sm.k[buf][ld * 64 * 8], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vg + (size_t)gk * D + 8 * cv, (lds_void*)&sm.v[buf][ld * 64 * 8], 16, 0, 0);
+        issued += 2;
+    }
+    if (wave == 0 && !pooled && a.kinfo) {
+        const int gk = min(k0 + lane, a.T - 1);
+        __builtin_amdgcn_global_load_lds(a.kinfo + (size_t)b * a.T + gk, (lds_void*)&sm.kinfo[buf][0], 4, 0, 0);
+        ++issued;
+    }
+    return issued;
+}
+
+// Wave 0, after its loads of the tile have landed: packed key info and the
+// per-sub-tile summaries (ballots only).
+template <int D>
+__device__ __forceinline__ void summarize_tile(const PrefillArgs& a, SmemBf16<D>& sm, int buf, int kind, int tile,
+                                               int lane) {
+    const bool pooled = kind == COL_POOLED;
+    const int nkeys = pooled ? a.nblk : a.T;
+    const bool valid = tile * BN + lane < nkeys;
+    int info = 0;
+    if (!pooled) {
+        uint32_t ki = (uint32_t)pack_key_info(1, false);
+        if (a.kinfo) {
+            ki = ds_read32(lds_off(&sm.kinfo[buf][lane]));
+            lds_wait();
+            lds_tie(ki);
+        }
+        if (valid) info = (int)ki;
+    }
+    ds_write32(lds_off(&sm.kinfo[buf][lane]), (uint32_t)info);
+    const int s = info & 0x7fffffff;
+    const bool sk = info < 0;
+    const int half = lane >> 5;
+    const int s_first = half ? __builtin_amdgcn_readlane(s, 32) : __builtin_amdgcn_readlane(s, 0);
+    const uint64_t eq_b = __ballot(!valid || s == s_first);
+    const uint64_t any_b = __ballot(valid && sk);
+    const uint64_t all_b = __ballot(!valid || sk);
+    if ((lane & 31) == 0) {
+        const uint32_t eq_h = (uint32_t)(eq_b >> (32 * half));
+        const uint32_t any_h = (uint32_t)(any_b >> (32 * half));
+        const uint32_t all_h = (uint32_t)(all_b >> (32 * half));
+        const KeySum ks = make_key_sum(eq_h == 0xffffffffu, s_first, any_h != 0u, all_h == 0xffffffffu);
+        const uint32_t base = lds_off(&sm.ksum[buf][half][0]);
+        ds_write32(base, (uint32_t)ks.smin);
+        ds_write32(base + 4, (uint32_t)ks.smax);
+        ds_write32(base + 8, (uint32_t)ks.any_sink);
+        ds_write32(base + 12, (uint32_t)ks.all_sink);
+    }
+}
 
 __device__ __forceinline__ void unpack8(const uint4& x, float* f) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -49,25 +223,31 @@ __device__ __forceinline__ void unpack8(const uint4& x, float* f) {
         f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
 }
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
 __device__ __forceinline__ uint4 pack8(const float* f) {
     uint4 r;
-    r.x = pack_bf16x2(f[0], f[1]);
-    r.y = pack_bf16x2(f[2], f[3]);
-    r.z = pack_bf16x2(f[4], f[5]);
-    r.w = pack_bf16x2(f[6], f[7]);
+    r.x = cvt_pk_bf16(f[0], f[1]);
+    r.y = cvt_pk_bf16(f[2], f[3]);
+    r.z = cvt_pk_bf16(f[4], f[5]);
+    r.w = cvt_pk_bf16(f[6], f[7]);
     return r;
 }
 
 // Rotate-half RoPE of 8 channel pairs: x1 holds channels d..d+7 (< D/2), x2
-// holds d+D/2..d+D/2+7; cs/sn point at the table entries of channels d..d+7.
-__device__ __forceinline__ void rotate8(uint4& x1, uint4& x2, const float* cs, const float* sn) {
-    float a[8], bb[8], c[8], s[8];
+// holds d+D/2..d+D/2+7; c/s hold the table entries of channels d..d+7.
+__device__ __forceinline__ void rotate8(uint4& x1, uint4& x2, const float4& c0, const float4& c1, const float4& s0,
+                                        const float4& s1) {
+    float a[8], bb[8];
     unpack8(x1, a);
     unpack8(x2, bb);
-    *(float4*)&c[0] = *(const float4*)cs;
-    *(float4*)&c[4] = *(const float4*)(cs + 4);
-    *(float4*)&s[0] = *(const float4*)sn;
-    *(float4*)&s[4] = *(const float4*)(sn + 4);
+    const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
     float y1[8], y2[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -78,241 +258,323 @@ __device__ __forceinline__ void rotate8(uint4& x1, uint4& x2, const float* cs, c
     x2 = pack8(y2);
 }
 
-template <int D, bool ROPE>
-__device__ __forceinline__ void stage_tile(const PrefillArgs& a, SmemBf16<D>& sm, int kind, int tile, int b,
-                                           int hkv, int tid, int nthreads) {
-    const bool pooled = kind == COL_POOLED;
-    const int nkeys = pooled ? a.nblk : a.T;
-    const size_t head_off = ((size_t)b * a.Hkv + hkv) * (size_t)nkeys * D;
-    const uint16_t* kg = (const uint16_t*)(pooled ? a.pk : a.k) + head_off;
-    const uint16_t* vg = (const uint16_t*)(pooled ? a.pv : a.v) + head_off;
-    const int k0 = tile * BN;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
 
-    // K: element e -> key e / P, chunk pair (p, p + P) of 8 channels each.
-    constexpr int P = D / 16;
-    for (int e = tid; e < BN * P; e += nthreads) {
-        const int key = e / P, p = e % P, gk = k0 + key;
-        uint4 x1 = make_uint4(0, 0, 0, 0), x2 = make_uint4(0, 0, 0, 0);
-        if (gk < nkeys) {
-            x1 = *(const uint4*)(kg + (size_t)gk * D + 8 * p);
-            x2 = *(const uint4*)(kg + (size_t)gk * D + 8 * p + D / 2);
-            if (ROPE && !pooled)
-                rotate8(x1, x2, a.rope_cos + (size_t)gk * (D / 2) + 8 * p,
-                        a.rope_sin + (size_t)gk * (D / 2) + 8 * p);
-        }
-        *(uint4*)&sm.ks[key][8 * p] = x1;
-        *(uint4*)&sm.ks[key][8 * p + D / 2] = x2;
-    }
-
-    // V, transposed: element e -> key pair kp, channel chunk dc.
-    constexpr int DC = D / 8;
-    for (int e = tid; e < (BN / 2) * DC; e += nthreads) {
-        const int kp = e % (BN / 2), dc = e / (BN / 2);
-        const int g0 = k0 + 2 * kp;
-        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-        if (g0 < nkeys) v0 = *(const uint4*)(vg + (size_t)g0 * D + 8 * dc);
-        if (g0 + 1 < nkeys) v1 = *(const uint4*)(vg + (size_t)(g0 + 1) * D + 8 * dc);
-        const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
-        const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *(uint32_t*)&sm.vt[8 * dc + 2 * i][2 * kp] = (w0[i] & 0xffffu) | (w1[i] << 16);
-            *(uint32_t*)&sm.vt[8 * dc + 2 * i + 1][2 * kp] = (w0[i] >> 16) | (w1[i] & 0xffff0000u);
-        }
-    }
-
-    // Key segment / sink flags and per-sub-tile summaries (wave 0; BN == 64).
-    if (tid < BN) {
-        const int gk = k0 + tid;
-        const bool valid = gk < nkeys;
-        int s = 0, sk = 0;
-        if (!pooled && valid) {
-            s = a.seg ? a.seg[(size_t)b * a.T + gk] : 1;
-            sk = a.prefix ? (a.prefix[(size_t)b * a.T + gk] != 0) : 0;
-        }
-        sm.kseg[tid] = s;
-        sm.ksink[tid] = (uint8_t)sk;
-        int smin = valid ? s : 0x7fffffff;
-        int smax = valid ? s : (int)0x80000000;
-        int any = (valid && sk) ? 1 : 0;
-        int all = (!valid || sk) ? 1 : 0;
-        smin = wave_imin_xor(smin, 1, 16);
-        smax = wave_imax_xor(smax, 1, 16);
-        any = wave_imax_xor(any, 1, 16);
-        all = wave_imin_xor(all, 1, 16);
-        if ((tid & 31) == 0) {
-            sm.ksum[tid >> 5][0] = smin;
-            sm.ksum[tid >> 5][1] = smax;
-            sm.ksum[tid >> 5][2] = any;
-            sm.ksum[tid >> 5][3] = all;
-        }
-    }
+// V^T operand of O^T += V^T P^T for keys [kb, kb + 16) of a tile
+// sub-tile and channels [32n, 32n + 32): lane (channel d = l % 32, half h)
+// needs the 8 keys 16m + 4h + {0..3} and 16m + 8 + 4h + {0..3} of channel d.
+// Two transpose reads: within each 16-lane group, source lane j = 4r + a
+// points at key K_r, channels base + 4a .. +3; output lane 4a' + b' then holds
+// channel base + lane%16 of keys K_0..K_3.
+template <int D>
+__device__ __forceinline__ void issue_vt(uint32_t vbase, int kb, int n, int lane, u32x2& lo, u32x2& hi) {
+    const int g = lane >> 4;          // 16-lane group
+    const int h = g >> 1;             // keys half
+    const int j = lane & 15;
+    const int r = j >> 2, a4 = j & 3;
+    const int ch = 32 * n + 16 * (g & 1) + 4 * a4;  // first channel this source lane points at
+    const int c = ch >> 3, half = (ch >> 2) & 1;
+    const int k_lo = kb + 4 * h + r;
+    const int k_hi = kb + 8 + 4 * h + r;
+    lo = ds_read_tr16(vbase + (uint32_t)(v_chunk<D>(k_lo, c) * 16 + 8 * half));
+    hi = ds_read_tr16(vbase + (uint32_t)(v_chunk<D>(k_hi, c) * 16 + 8 * half));
 }
 
-template <int D, bool ROPE>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
+template <int D, bool ROPE, bool COMPRESSED>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_bf16_kernel(PrefillArgs a) {
     static_assert(D == 32 || D == 64, "head dim");
     __shared__ __align__(16) SmemBf16<D> sm;
+    SWA_TRACE_DECL
     const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
+    constexpr int nthreads = 64 * kMfmaWaves;  // the launch always uses this block size
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int lq = lane & 31;
 
     const int T = a.T;
     const int G = a.Hq / a.Hkv;
     const int groups = G / a.hpw;
-    const int b = blockIdx.z;
-    const int hkv = blockIdx.y / groups;
-    const int hsub = blockIdx.y % groups;
     const int wg_rows = 32 * a.rbs;
-    const int q0 = blockIdx.x * wg_rows;
+    const int nqb = (T + wg_rows - 1) / wg_rows;
+    // XCD-aware numbering: dispatch sends workgroup i to XCD i % 8; give each
+    // XCD a contiguous range of logical blocks (query block fastest).
+    const int nblocks = gridDim.x;
+    int lb = blockIdx.x;
+    if ((nblocks & 7) == 0) lb = (blockIdx.x & 7) * (nblocks >> 3) + (blockIdx.x >> 3);
+    const int qb = lb % nqb;
+    const int hg = (lb / nqb) % (a.Hkv * groups);
+    const int b = lb / (nqb * a.Hkv * groups);
+    const int hkv = hg / groups;
+    const int hsub = hg % groups;
+    const int q0 = qb * wg_rows;
     const int q1 = min(q0 + wg_rows - 1, T - 1);
     const int my_h = hkv * G + hsub * a.hpw + (wave % a.hpw);
     const int r0 = q0 + 32 * (wave / a.hpw);
-    const bool wave_active = r0 < T;
+    const bool wave_active = wave < a.hpw * a.rbs && r0 < T;
     const int my_q = r0 + lq;
     const bool row_ok = my_q < T;
-    const bool plain = a.block == 0;
+    constexpr bool plain = !COMPRESSED;
 
-    // Q^T operand: lane holds row my_q, channels 16c + 8h .. +7 for each c.
-    bf16x8 qf[D / 16];
+    // Tile plan.  The band comes first in the walk, so the first tiles' loads
+    // start before the sink scan; every global load of the prologue is issued
+    // before any of them is waited for.
+    const TilePlan plan = plan_tiles(q0, q1, a.window, a.block, a.nblk, a.prefix != nullptr, BN);
+    TileIter it;
+    it.init(plan, sm.sink_bits, BN);
+    int kc = 0, tc = 0;  // tile being computed
+    int kn = 0, tn = 0;  // next tile (in flight)
+    const bool have0 = it.next(kc, tc);
+    if (have0) issue_tile<D>(a, sm, 0, kc, tc, b, hkv, wave, lane);
+
+    uint4 raw[D / 16];
     {
-        uint4 raw[D / 16];
         const uint16_t* qrow = (const uint16_t*)a.q + (((size_t)b * a.Hq + my_h) * T + (row_ok ? my_q : 0)) * D;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
             raw[c] = row_ok ? *(const uint4*)(qrow + 16 * c + 8 * h) : make_uint4(0, 0, 0, 0);
-        if (ROPE && row_ok) {
-#pragma unroll
-            for (int c = 0; c < D / 32; ++c) {
-                const int d0 = 16 * c + 8 * h;
-                rotate8(raw[c], raw[c + D / 32], a.rope_cos + (size_t)my_q * (D / 2) + d0,
-                        a.rope_sin + (size_t)my_q * (D / 2) + d0);
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
     }
-
-    // Rows of this wave: segment ids and their range.
+    float4 rc[D / 32][2], rsn[D / 32][2];
+    if (ROPE && row_ok) {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+            const int d0 = 16 * c + 8 * h;
+            const float* cs = a.rope_cos + (size_t)my_q * (D / 2) + d0;
+            const float* sn = a.rope_sin + (size_t)my_q * (D / 2) + d0;
+            rc[c][0] = *(const float4*)cs;
+            rc[c][1] = *(const float4*)(cs + 4);
+            rsn[c][0] = *(const float4*)sn;
+            rsn[c][1] = *(const float4*)(sn + 4);
+        }
+    }
     int seg_q = 0;
     if (row_ok) seg_q = a.seg ? a.seg[(size_t)b * T + my_q] : 1;
+    const int32_t* seg_row = a.seg ? a.seg + (size_t)b * T : nullptr;
+    const uint8_t* pre_row = a.prefix ? a.prefix + (size_t)b * T : nullptr;
+    const bool aligned16 = (T & 15) == 0;
+    SinkChunk chunk0;
+    const bool scan = plan.sink_keys > 0;
+    if (scan && 16 * tid < plan.sink_keys) sink_chunk_load(pre_row, seg_row, 16 * tid, aligned16, chunk0);
+
+    // Q^T operand: lane holds row my_q, channels 16c + 8h .. +7 for each c.
+    bf16x8 qf[D / 16];
+    if (ROPE && row_ok) {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) rotate8(raw[c], raw[c + D / 32], rc[c][0], rc[c][1], rsn[c][0], rsn[c][1]);
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
+
+    // Rows of this wave: segment ids and their range.
+    const bool row_vis = row_ok && (!plain || seg_q > 0);  // padding rows see nothing
+    const unsigned wlim = window_limit(a.window);
     RowSum rs;
     rs.r0 = r0;
     rs.r1 = min(r0 + 31, T - 1);
-    rs.smin = wave_imin_xor(row_ok ? seg_q : 0x7fffffff, 1, 16);
-    rs.smax = wave_imax_xor(row_ok ? seg_q : (int)0x80000000, 1, 16);
+    rs.smin = __builtin_amdgcn_readfirstlane(wave_imin_xor(row_ok ? seg_q : 0x7fffffff, 1, 16));
+    rs.smax = __builtin_amdgcn_readfirstlane(wave_imax_xor(row_ok ? seg_q : (int)0x80000000, 1, 16));
+    const int pooled_n = (COMPRESSED && row_ok) ? pooled_visible_count(my_q, a.window, a.block, a.nblk) : 0;
 
-    const TilePlan plan = plan_tiles(q0, q1, a.window, a.block, a.nblk, a.prefix != nullptr, BN);
-    if (plan.sink_keys > 0)
-        scan_sink_tiles(a.prefix + (size_t)b * T, plan.sink_keys, BN, sm.sink_bits, tid, nthreads);
-    TileIter it;
-    it.init(plan, sm.sink_bits, BN);
+    // Sink tiles before the band (only sinks of this workgroup's segments).
+    if (scan) {
+        int lo = 1, hi = 1;
+        if (seg_row) row_segment_range_from_lanes(seg_q, row_ok && wave_active, sm.red, tid, lo, hi);
+        scan_sink_tiles(pre_row, seg_row, plan.sink_keys, BN, lo, hi, aligned16, sm.sink_bits, tid, nthreads,
+                        16 * tid < plan.sink_keys ? &chunk0 : nullptr);
+    }
+    const bool have1 = have0 && it.next(kn, tn);
+    int n_new = 0;  // loads of the newest tile this wave has in flight
+    if (have1) n_new = issue_tile<D>(a, sm, 1, kn, tn, b, hkv, wave, lane);
 
     const float c_log2 = a.scale * kLog2e;
-    float m_run = kNegInf;
+    float m_run = kNegInf;  // reference max (raw score units) used for p
     float l_run = 0.f;
     f32x16 o[D / 32];
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) o[n] = f32x16{};
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 
-    int kind = 0, tile = 0;
-    while (it.next(kind, tile)) {
-        __syncthreads();
-        stage_tile<D, ROPE>(a, sm, kind, tile, b, hkv, tid, nthreads);
-        __syncthreads();
-        if (!wave_active) continue;
-        const int nkeys = kind == COL_POOLED ? a.nblk : T;
-#pragma unroll
-        for (int st = 0; st < BN / SUB; ++st) {
-            const int k0 = tile * BN + st * SUB;
-            int cls;
-            if (kind == COL_POOLED) {
-                cls = classify_pooled(rs, k0, SUB, a.window, a.block, a.nblk);
-            } else {
-                KeySum ks;
-                ks.smin = sm.ksum[st][0];
-                ks.smax = sm.ksum[st][1];
-                ks.any_sink = sm.ksum[st][2];
-                ks.all_sink = sm.ksum[st][3];
-                cls = classify_exact(rs, ks, k0, SUB, nkeys, a.window, plain);
-            }
-            if (cls == TILE_SKIP) continue;
+    // tile 0 must have landed; tile 1 may still be in flight
+    wait_vm_upto(n_new);
+    if (wave == 0 && have0) summarize_tile<D>(a, sm, 0, kc, tc, lane);
+    wait_vm_upto(n_new);
+    barrier_raw();
+    SWA_TRACE(0);
 
-            f32x16 s = f32x16{};
+    const uint32_t k_lds = lds_off(&sm.k[0][0]), v_lds = lds_off(&sm.v[0][0]);
+    const uint32_t info_lds = lds_off(&sm.kinfo[0][0]), sum_lds = lds_off(&sm.ksum[0][0][0]);
+    constexpr uint32_t kTileBytes = BN * D * 2;
+    int cur = 0;
+    bool have = have0, have_next = have1;
+    while (have) {
+        const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
+        const int nxt2 = nxt == NBUF - 1 ? 0 : nxt + 1;
+        bool have_next2 = false;
+        int k2 = 0, t2 = 0;
+        n_new = 0;
+        if (have_next) {
+            have_next2 = it.next(k2, t2);
+            if (have_next2) n_new = issue_tile<D>(a, sm, nxt2, k2, t2, b, hkv, wave, lane);
+        }
+        SWA_TRACE(1);
+
+        if (wave_active) {
+            const bool pooled = COMPRESSED && kc == COL_POOLED;
+            const int nkeys = pooled ? a.nblk : T;
+            const uint32_t kbuf = k_lds + cur * kTileBytes, vbuf = v_lds + cur * kTileBytes;
+            // sub-tile summaries, moved to scalar registers at once
+            KeySum ksub[BN / SUB];
+            if (!pooled) {
+                u32x4 kv[BN / SUB];
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 ka = *(const bf16x8*)&sm.ks[st * SUB + lq][16 * c + 8 * h];
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], s, 0, 0, 0);
-            }
-            // Scores leave the accumulator into plain registers; the mask is applied
-            // with selects (no divergent writes into the MFMA result vector).
-            float sv[16];
+                for (int st = 0; st < BN / SUB; ++st) kv[st] = ds_read128(sum_lds + (cur * (BN / SUB) + st) * 16);
+                lds_wait();
 #pragma unroll
-            for (int j = 0; j < 16; ++j) sv[j] = s[j];
-            if (cls == TILE_PARTIAL) {
-                const int pooled_n = (kind == COL_POOLED && row_ok)
-                                         ? pooled_visible_count(my_q, a.window, a.block, a.nblk)
-                                         : 0;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int kidx = st * SUB + 8 * (j >> 2) + 4 * h + (j & 3);
-                    const int gk = tile * BN + kidx;
-                    bool vis;
-                    if (kind == COL_POOLED) {
-                        vis = gk < pooled_n;
-                    } else if (plain) {
-                        const int seg_k = sm.kseg[kidx];
-                        const bool sink_k = sm.ksink[kidx] != 0;
-                        vis = visible_plain(seg_q, seg_k, sink_k, my_q, gk, a.window);
-                    } else {
-                        vis = visible_exact_window(my_q, gk, a.window);
-                    }
-                    sv[j] = (vis & row_ok) ? sv[j] : kNegInf;
+                for (int st = 0; st < BN / SUB; ++st) {
+                    lds_tie(kv[st]);
+                    ksub[st].smin = __builtin_amdgcn_readfirstlane((int)kv[st][0]);
+                    ksub[st].smax = __builtin_amdgcn_readfirstlane((int)kv[st][1]);
+                    ksub[st].any_sink = __builtin_amdgcn_readfirstlane((int)kv[st][2]);
+                    ksub[st].all_sink = __builtin_amdgcn_readfirstlane((int)kv[st][3]);
                 }
             }
-            float mx = sv[0];
 #pragma unroll
-            for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sv[j]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx);
-            const float base = (m_new == kNegInf) ? 0.f : m_new * c_log2;
-            const float corr = __builtin_amdgcn_exp2f(m_run * c_log2 - base);
-            m_run = m_new;
-            float p[16];
-            float psum = 0.f;
+            for (int st = 0; st < BN / SUB; ++st) {
+                const int k0 = tc * BN + st * SUB;
+                int cls;
+                if (pooled) {
+                    cls = classify_pooled(rs, k0, SUB, a.window, a.block, a.nblk);
+                } else {
+                    cls = classify_exact(rs, ksub[st], k0, SUB, nkeys, a.window, plain);
+                }
+                cls = __builtin_amdgcn_readfirstlane(cls);
+                if (cls == TILE_SKIP) continue;
+
+                u32x4 kr[D / 16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                p[j] = __builtin_amdgcn_exp2f(sv[j] * c_log2 - base);
-                psum += p[j];
-            }
-            l_run = l_run * corr + psum;
+                for (int c = 0; c < D / 16; ++c) kr[c] = ds_read128(kbuf + k_chunk<D>(st * SUB + lq, 2 * c + h) * 16);
+                lds_wait();
+                f32x16 s = f32x16{};
 #pragma unroll
-            for (int n = 0; n < D / 32; ++n) o[n] *= corr;
+                for (int c = 0; c < D / 16; ++c) {
+                    lds_tie(kr[c]);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], s, 0, 0, 0);
+                }
+                // Scores leave the accumulator into plain registers; the mask is
+                // applied with selects (no divergent writes into the MFMA result).
+                // Element j holds key k0 + off(j) + 4h with off(j) = 8(j/4) + j%4.
+                float sv[16];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                uint4 pw;
-                pw.x = pack_bf16x2(p[8 * m + 0], p[8 * m + 1]);
-                pw.y = pack_bf16x2(p[8 * m + 2], p[8 * m + 3]);
-                pw.z = pack_bf16x2(p[8 * m + 4], p[8 * m + 5]);
-                pw.w = pack_bf16x2(p[8 * m + 6], p[8 * m + 7]);
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+                for (int j = 0; j < 16; ++j) sv[j] = s[j];
+                if (cls != TILE_FULL) {
+                    const int kb = k0 + 4 * h;  // key of element 0
+                    if (pooled) {
+                        const int lim = row_vis ? pooled_n - kb : -1;
 #pragma unroll
-                for (int n = 0; n < D / 32; ++n) {
-                    const uint16_t* vrow = &sm.vt[32 * n + lq][st * SUB + 16 * m + 4 * h];
-                    uint4 vw;
-                    const uint2 lo = *(const uint2*)vrow;
-                    const uint2 hi = *(const uint2*)(vrow + 8);
-                    vw.x = lo.x;
-                    vw.y = lo.y;
-                    vw.z = hi.x;
-                    vw.w = hi.y;
-                    o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pb, o[n], 0, 0, 0);
+                        for (int j = 0; j < 16; ++j) sv[j] = (8 * (j >> 2) + (j & 3)) < lim ? sv[j] : kNegInf;
+                    } else if (cls == TILE_PARTIAL_POS) {
+                        const int d0 = row_vis ? my_q - kb : -0x40000000;  // q - key of element 0
+#pragma unroll
+                        for (int j = 0; j < 16; ++j)
+                            sv[j] = visible_pos(d0 - (8 * (j >> 2) + (j & 3)), wlim) ? sv[j] : kNegInf;
+                    } else {
+                        const int d0 = my_q - kb;
+                        u32x4 inf[4];
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4)
+                            inf[g4] = ds_read128(info_lds + cur * BN * 4 + (st * SUB + 8 * g4 + 4 * h) * 4);
+                        lds_wait();
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            lds_tie(inf[g4]);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const bool vis =
+                                    row_vis & visible_full(d0 - (8 * g4 + r), wlim, (int)inf[g4][r], seg_q);
+                                sv[4 * g4 + r] = vis ? sv[4 * g4 + r] : kNegInf;
+                            }
+                        }
+                    }
+                } else if (!row_vis) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) sv[j] = kNegInf;
+                }
+                float mx = sv[0];
+#pragma unroll
+                for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, sv[j]);
+                {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false,
+                                                                     false);
+                    mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                }
+                // Rescale only when some row of the wave outgrows its reference
+                // max by more than 2^8 (the first visible tile always does).
+                const bool grow = (mx - m_run) * c_log2 > kRescaleLog2;
+                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                    const float m_new = __builtin_fmaxf(m_run, mx);
+                    const float corr = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
+                    m_run = m_new;
+                    l_run *= corr;
+#pragma unroll
+                    for (int n = 0; n < D / 32; ++n) o[n] *= corr;
+                }
+                // V^T operands of the first 16 keys, in flight while the weights are made
+                u32x2 vlo[D / 32], vhi[D / 32];
+#pragma unroll
+                for (int n = 0; n < D / 32; ++n) issue_vt<D>(vbuf, st * SUB, n, lane, vlo[n], vhi[n]);
+                const float base = (m_run == kNegInf) ? 0.f : m_run * c_log2;
+                uint32_t pw[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    pw[i] = cvt_pk_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c_log2, -base)),
+                                        __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c_log2, -base)));
+                // row sum of exactly the bf16 weights the PV product uses
+                float psum = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]), ones2, psum, false);
+                l_run += psum;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    lds_wait();
+                    u32x4 vw[D / 32];
+#pragma unroll
+                    for (int n = 0; n < D / 32; ++n) {
+                        lds_tie(vlo[n]);
+                        lds_tie(vhi[n]);
+                        vw[n] = u32x4{vlo[n][0], vlo[n][1], vhi[n][0], vhi[n][1]};
+                    }
+                    if (m == 0) {  // the next 16 keys load during this product
+#pragma unroll
+                        for (int n = 0; n < D / 32; ++n) issue_vt<D>(vbuf, st * SUB + 16, n, lane, vlo[n], vhi[n]);
+                    }
+                    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * m], pw[4 * m + 1], pw[4 * m + 2],
+                                                                            pw[4 * m + 3]));
+#pragma unroll
+                    for (int n = 0; n < D / 32; ++n)
+                        o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw[n]), pb, o[n], 0,
+                                                                       0, 0);
                 }
             }
         }
+        SWA_TRACE(2);
+
+        // tile `nxt` must have landed before the barrier; the newest tile may fly on
+        wait_vm_upto(n_new);
+        if (wave == 0 && have_next) summarize_tile<D>(a, sm, nxt, kn, tn, lane);
+        SWA_TRACE(3);
+        wait_vm_upto(n_new);
+        barrier_raw();
+        SWA_TRACE(4);
+        cur = nxt;
+        kc = kn;
+        tc = tn;
+        kn = k2;
+        tn = t2;
+        have = have_next;
+        have_next = have_next2;
     }
 
     if (!wave_active) return;
@@ -326,14 +588,15 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int d = 32 * n + 8 * i + 4 * h;
                 uint2 w;
-                w.x = pack_bf16x2(o[n][4 * i] * inv, o[n][4 * i + 1] * inv);
-                w.y = pack_bf16x2(o[n][4 * i + 2] * inv, o[n][4 * i + 3] * inv);
+                w.x = cvt_pk_bf16(o[n][4 * i] * inv, o[n][4 * i + 1] * inv);
+                w.y = cvt_pk_bf16(o[n][4 * i + 2] * inv, o[n][4 * i + 3] * inv);
                 *(uint2*)(orow + d) = w;
             }
         }
         if (a.lse && h == 0)
             a.lse[((size_t)b * a.Hq + my_h) * T + my_q] = l_tot > 0.f ? m_run * a.scale + __logf(l_tot) : kNegInf;
     }
+    SWA_TRACE(5);
 }
 
 }  // namespace
@@ -341,16 +604,31 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
     const int G = a.Hq / a.Hkv;
     const int wg_rows = 32 * a.rbs;
-    dim3 grid((a.T + wg_rows - 1) / wg_rows, a.Hkv * (G / a.hpw), a.B);
-    dim3 block(64 * a.hpw * a.rbs);
+    const long long nblocks = (long long)((a.T + wg_rows - 1) / wg_rows) * a.Hkv * (G / a.hpw) * a.B;
+    if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)nblocks);
+    dim3 block(64 * kMfmaWaves);
     const bool rope = a.rope_len > 0;
+    const bool comp = a.block > 0;
+#define SWA_LAUNCH(DD, RR, CC) hipLaunchKernelGGL((prefill_bf16_kernel<DD, RR, CC>), grid, block, 0, s, a)
     if (a.D == 64) {
-        if (rope) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a);
+        if (comp) {
+            if (rope) SWA_LAUNCH(64, true, true);
+            else SWA_LAUNCH(64, false, true);
+        } else {
+            if (rope) SWA_LAUNCH(64, true, false);
+            else SWA_LAUNCH(64, false, false);
+        }
     } else {
-        if (rope) hipLaunchKernelGGL((prefill_bf16_kernel<32, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<32, false>), grid, block, 0, s, a);
+        if (comp) {
+            if (rope) SWA_LAUNCH(32, true, true);
+            else SWA_LAUNCH(32, false, true);
+        } else {
+            if (rope) SWA_LAUNCH(32, true, false);
+            else SWA_LAUNCH(32, false, false);
+        }
     }
+#undef SWA_LAUNCH
     return hipGetLastError();
 }
 

@@ -3,8 +3,8 @@
 // Same mask, same tile enumeration and same column layout as the bf16 MFMA
 // kernel (see swa_tiles.h for the sources), with true fp32 inputs, products
 // and accumulation.  One wave per workgroup, one query row per lane; K/V
-// tiles of 32 keys are staged in LDS in fp32 (K rotated at its position when
-// RoPE is on) and shared by the 64 rows.  Used for fp32 inputs, where the
+// tiles of 32 keys are staged in LDS in fp32 and shared by the 64 rows.  With
+// RoPE, q is rotated here as it is loaded; the keys arrive already rotated.  Used for fp32 inputs, where the
 // tolerance is far tighter than bf16 MFMA inputs allow.
 #include "swa_common.h"
 #include "swa_internal.h"
@@ -21,8 +21,7 @@ template <int D>
 struct SmemF32 {
     float ks[BNF][D + 1];
     float vs[BNF][D + 1];
-    int kseg[BNF];
-    uint8_t ksink[BNF];
+    int kinfo[BNF];
     int ksum[4];
     uint32_t sink_bits[kSinkWordsF];
 };
@@ -60,6 +59,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     }
     int seg_q = 0;
     if (row_ok) seg_q = a.seg ? a.seg[(size_t)b * T + my_q] : 1;
+    const bool row_vis = row_ok && (!plain || seg_q > 0);  // padding rows see nothing
+    const unsigned wlim = window_limit(a.window);
     RowSum rs;
     rs.r0 = q0;
     rs.r1 = q1;
@@ -67,7 +68,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     rs.smax = wave_imax_xor(row_ok ? seg_q : (int)0x80000000, 1, 32);
 
     const TilePlan plan = plan_tiles(q0, q1, a.window, a.block, a.nblk, a.prefix != nullptr, BNF);
-    if (plan.sink_keys > 0) scan_sink_tiles(a.prefix + (size_t)b * T, plan.sink_keys, BNF, sm.sink_bits, lane, 64);
+    plan_sink_tiles(plan, a.seg ? a.seg + (size_t)b * T : nullptr, a.prefix ? a.prefix + (size_t)b * T : nullptr, T,
+                    q0, q1, BNF, sm.ksum, sm.sink_bits, lane, 64);
     TileIter it;
     it.init(plan, sm.sink_bits, BNF);
 
@@ -92,47 +94,43 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
             if (gk < nkeys) {
                 kv = kg[(size_t)gk * D + d];
                 vv = vg[(size_t)gk * D + d];
-                if (ROPE && !pooled) {
-                    const int i = d < D / 2 ? d : d - D / 2;
-                    const float c = a.rope_cos[(size_t)gk * (D / 2) + i];
-                    const float s = a.rope_sin[(size_t)gk * (D / 2) + i];
-                    const float partner = kg[(size_t)gk * D + (d < D / 2 ? d + D / 2 : d - D / 2)];
-                    kv = d < D / 2 ? kv * c - partner * s : kv * c + partner * s;
-                }
             }
             sm.ks[key][d] = kv;
             sm.vs[key][d] = vv;
         }
         if (lane < BNF) {
             const int gk = k0 + lane;
-            const bool valid = gk < nkeys;
-            int s = 0, sk = 0;
-            if (!pooled && valid) {
-                s = a.seg ? a.seg[(size_t)b * T + gk] : 1;
-                sk = a.prefix ? (a.prefix[(size_t)b * T + gk] != 0) : 0;
+            int info = 0;
+            if (!pooled && gk < nkeys) {
+                const int s = a.seg ? a.seg[(size_t)b * T + gk] : 1;
+                const bool sk = a.prefix ? (a.prefix[(size_t)b * T + gk] != 0) : false;
+                info = pack_key_info(s, sk);
             }
-            sm.kseg[lane] = s;
-            sm.ksink[lane] = (uint8_t)sk;
+            sm.kinfo[lane] = info;
         }
         {
             // summary over the 32 keys (lanes 32..63 mirror lanes 0..31)
             const int kl = lane & 31;
             const int gk = k0 + kl;
             const bool valid = gk < nkeys;
-            int s = 0, sk = 0;
+            int info = 0;
             if (!pooled && valid) {
-                s = a.seg ? a.seg[(size_t)b * T + gk] : 1;
-                sk = a.prefix ? (a.prefix[(size_t)b * T + gk] != 0) : 0;
+                const int s = a.seg ? a.seg[(size_t)b * T + gk] : 1;
+                const bool sk = a.prefix ? (a.prefix[(size_t)b * T + gk] != 0) : false;
+                info = pack_key_info(s, sk);
             }
-            const int smin = wave_imin_xor(valid ? s : 0x7fffffff, 1, 16);
-            const int smax = wave_imax_xor(valid ? s : (int)0x80000000, 1, 16);
-            const int any = wave_imax_xor((valid && sk) ? 1 : 0, 1, 16);
-            const int all = wave_imin_xor((!valid || sk) ? 1 : 0, 1, 16);
+            const int sgv = info & 0x7fffffff;
+            const int s_first = __builtin_amdgcn_readlane(sgv, 0);
+            const uint64_t eq_b = __ballot(!valid || sgv == s_first);
+            const uint64_t any_b = __ballot(valid && info < 0);
+            const uint64_t all_b = __ballot(!valid || info < 0);
             if (lane == 0) {
-                sm.ksum[0] = smin;
-                sm.ksum[1] = smax;
-                sm.ksum[2] = any;
-                sm.ksum[3] = all;
+                const KeySum ks = make_key_sum((uint32_t)eq_b == 0xffffffffu, s_first, (uint32_t)any_b != 0u,
+                                               (uint32_t)all_b == 0xffffffffu);
+                sm.ksum[0] = ks.smin;
+                sm.ksum[1] = ks.smax;
+                sm.ksum[2] = ks.any_sink;
+                sm.ksum[3] = ks.all_sink;
             }
         }
         __syncthreads();
@@ -153,12 +151,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 #pragma unroll 1
         for (int j = 0; j < BNF; ++j) {
             const int gk = k0 + j;
-            bool vis = row_ok;
-            if (vis && cls == TILE_PARTIAL) {
-                if (pooled) vis = gk < pooled_n;
-                else if (plain) vis = visible_plain(seg_q, sm.kseg[j], sm.ksink[j] != 0, my_q, gk, a.window);
-                else vis = visible_exact_window(my_q, gk, a.window);
-            }
+            bool vis = row_vis;
+            if (cls == TILE_PARTIAL_POS) vis &= visible_pos(my_q - gk, wlim);
+            else if (cls == TILE_PARTIAL) vis &= pooled ? (gk < pooled_n) : visible_full(my_q - gk, wlim, sm.kinfo[j], seg_q);
             if (!vis) continue;
             float dot = 0.f;
 #pragma unroll

@@ -91,10 +91,24 @@ int check_prefill(const swa_prefill_params* p, const int32_t* seg_ids, const uin
     a.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->D);
     a.seg = seg_ids;
     a.prefix = prefix;
+    a.kinfo = nullptr;
     const swa::MfmaGeom g = swa::mfma_geometry(p->Hq / p->Hkv);
     a.hpw = g.hpw;
     a.rbs = g.rbs;
     return SWA_OK;
+}
+
+// Workspace layout of a prefill: [packed key info, bf16 plain mode only]
+// [rotated keys, with RoPE only]; each part starts 256-byte aligned.
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t key_info_bytes(const swa_prefill_params* p) {
+    if (p->dtype != SWA_BF16 || p->compress_block != 0) return 0;
+    return round256((size_t)p->B * p->T * sizeof(int32_t));
+}
+size_t rotated_key_bytes(const swa_prefill_params* p) {
+    if (p->rope_len <= 0) return 0;
+    const size_t elem = p->dtype == SWA_BF16 ? 2 : 4;
+    return round256((size_t)p->B * p->Hkv * p->T * p->D * elem);
 }
 
 }  // namespace
@@ -105,9 +119,15 @@ const char* swa_last_error(void) { return g_last_error.c_str(); }
 
 int swa_version(void) { return 100; }
 
+size_t swa_prefill_workspace_size(const swa_prefill_params* p) {
+    if (p == nullptr || p->B <= 0 || p->T <= 0 || p->Hkv <= 0 || p->D <= 0) return 0;
+    return key_info_bytes(p) + rotated_key_bytes(p);
+}
+
 int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, const void* v, const void* pooled_k,
                      const void* pooled_v, const int32_t* seg_ids, const uint8_t* prefix, const float* rope_cos,
-                     const float* rope_sin, void* out, float* lse, void* stream) {
+                     const float* rope_sin, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
     swa::PrefillArgs a;
     int rc = check_prefill(p, seg_ids, prefix, a);
     if (rc != SWA_OK) return rc;
@@ -125,6 +145,12 @@ int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, 
         REQUIRE_PTR(rope_cos);
         REQUIRE_PTR(rope_sin);
     }
+    const size_t ws_need = swa_prefill_workspace_size(p);
+    if (ws_need > 0) {
+        REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 255u) == 0,
+                "workspace must be a 256-byte aligned buffer of swa_prefill_workspace_size() bytes");
+        REQUIRE(workspace_bytes >= ws_need, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, ws_need);
+    }
     a.q = q;
     a.k = k;
     a.v = v;
@@ -134,7 +160,23 @@ int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, 
     a.rope_sin = p->rope_len > 0 ? rope_sin : nullptr;
     a.out = out;
     a.lse = lse;
+    a.kinfo = nullptr;
     const hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    const size_t info_bytes = key_info_bytes(p);
+    if (info_bytes > 0 && (a.seg || a.prefix)) {  // pack segment ids and sink flags once
+        int32_t* info = (int32_t*)ws;
+        const hipError_t e = swa::launch_key_info((long long)p->B * p->T, a.seg, a.prefix, info, s);
+        if (e != hipSuccess) return hip_status(e, "swa_attn_prefill key info launch");
+        a.kinfo = info;
+    }
+    if (p->rope_len > 0) {  // rotate the exact keys once, into the workspace
+        void* kr = ws + info_bytes;
+        const hipError_t e = swa::launch_rope_rows((long long)p->B * p->Hkv * p->T, p->T, p->D, p->dtype, k, rope_cos,
+                                                   rope_sin, kr, s);
+        if (e != hipSuccess) return hip_status(e, "swa_attn_prefill key rotation launch");
+        a.k = kr;
+    }
     const hipError_t e = p->dtype == SWA_BF16 ? swa::launch_prefill_bf16(a, s) : swa::launch_prefill_f32(a, s);
     return hip_status(e, "swa_attn_prefill launch");
 }

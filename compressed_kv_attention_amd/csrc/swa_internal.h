@@ -16,6 +16,7 @@ struct PrefillArgs {
     const void* pv;
     const int32_t* seg;
     const uint8_t* prefix;
+    const int32_t* kinfo;  // [B,T] packed key info (segment | sink << 31), or NULL
     const float* rope_cos;
     const float* rope_sin;
     void* out;
@@ -31,7 +32,10 @@ struct PrefillArgs {
     int hpw, rbs;
 };
 
-// Geometry the bf16 MFMA kernel uses for a given GQA group size.
+// Geometry the bf16 MFMA kernel uses for a given GQA group size: 8 waves per
+// workgroup, hpw heads (the largest divisor of G that is at most 4) times rbs
+// 32-row blocks (hpw * rbs <= 8 compute waves; the rest only stage tiles).
+constexpr int kMfmaWaves = 8;
 struct MfmaGeom {
     int hpw, rbs;
 };
@@ -39,8 +43,7 @@ inline MfmaGeom mfma_geometry(int G) {
     MfmaGeom g;
     g.hpw = G >= 4 ? 4 : G;
     while (G % g.hpw) --g.hpw;
-    g.rbs = 4 / g.hpw;
-    if (g.rbs < 1) g.rbs = 1;
+    g.rbs = kMfmaWaves / g.hpw;
     return g;
 }
 
@@ -52,6 +55,9 @@ hipError_t launch_rope_table(double theta, int rope_len, int D, float* c, float*
 hipError_t launch_pool_rope(int B, int H, int T, int D, int block, int dtype, const void* k_pre,
                             const void* v, const float* c, const float* sn, int rope_len, void* pk,
                             void* pv, hipStream_t s);
+hipError_t launch_key_info(long long n, const int32_t* seg, const uint8_t* prefix, int32_t* info, hipStream_t s);
+hipError_t launch_rope_rows(long long rows, int T, int D, int dtype, const void* x, const float* cs,
+                            const float* sn, void* y, hipStream_t s);
 hipError_t launch_kv_quantize(long long N, int D, const void* x, int8_t* xq, float* xs, hipStream_t s);
 
 struct DecodeArgs {

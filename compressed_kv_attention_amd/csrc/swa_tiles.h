@@ -16,20 +16,41 @@
 
 namespace swa {
 
-enum : int { TILE_SKIP = 0, TILE_FULL = 1, TILE_PARTIAL = 2 };
+// Sub-tile classes.  PARTIAL_POS: only the causal/window test can fail (one
+// segment shared by every row and key, no sink that matters), so the element
+// predicate is the single unsigned compare (unsigned)(q - k) < wlim.
+// PARTIAL: the full packing & causal & (recent | sink) predicate per element.
+enum : int { TILE_SKIP = 0, TILE_FULL = 1, TILE_PARTIAL_POS = 2, TILE_PARTIAL = 3 };
 enum : int { COL_EXACT = 0, COL_POOLED = 1 };
 
-// Element predicate of plain mode.
-// (Evaluated without short-circuit branches.)
+// Window limit as an unsigned bound on d = q - k: visible positions are
+// 0 <= d < window, or 0 <= d when no window is set.
+__device__ __forceinline__ unsigned window_limit(int window) { return window != 0 ? (unsigned)window : 0x7fffffffu; }
+
+// Packed key info: segment id (negative ids count as padding, 0) | sink << 31.
+__device__ __forceinline__ int pack_key_info(int seg, bool sink) { return (seg < 0 ? 0 : seg) | ((int)sink << 31); }
+
+// Positional predicate: causal and inside the window.
+__device__ __forceinline__ bool visible_pos(int d, unsigned wlim) { return (unsigned)d < wlim; }
+
+// Full plain-mode predicate for a row of segment seg_q > 0 (rows of segment
+// <= 0 see nothing and are excluded by the caller): same segment, and
+// (causal and recent) or (causal and sink).  [NW §"KV Sinks for Tools"]
+__device__ __forceinline__ bool visible_full(int d, unsigned wlim, int info, int seg_q) {
+    const bool same_seg = ((info ^ seg_q) & 0x7fffffff) == 0;
+    return same_seg & (((unsigned)d < wlim) | ((info < 0) & (d >= 0)));
+}
+
+// Element predicate of plain mode in terms of ids (used by the debug path):
+// packing & causal & (recent | sink).
 __device__ __forceinline__ bool visible_plain(int seg_q, int seg_k, bool sink_k, int q, int k, int window) {
-    const bool keep = (seg_q > 0) & (seg_k == seg_q) & (k <= q);
-    const bool in_window = (window == 0) | ((q - k) < window) | sink_k;
-    return keep & in_window;
+    if (seg_q <= 0) return false;
+    return visible_full(q - k, window_limit(window), pack_key_info(seg_k, sink_k), seg_q);
 }
 
 // Exact-key predicate of compressed mode: causal window, no segments, no sinks.
 __device__ __forceinline__ bool visible_exact_window(int q, int t, int window) {
-    return (t <= q) & ((q - t) < window);
+    return visible_pos(q - t, window_limit(window));
 }
 
 // Number of pooled blocks visible to row q: blocks j with (j+1)*b <= q-W+1,
@@ -45,10 +66,20 @@ __device__ __forceinline__ int pooled_visible_count(int q, int window, int block
 struct RowSum {
     int r0, r1, smin, smax;
 };
-// Summary of the valid keys k0..k1 (< nkeys) of one key sub-tile.
+// Summary of the valid keys of one key sub-tile.  When the valid keys do not
+// all share one segment the range is widened to [0, INT_MAX] (never SKIP or
+// FULL by segment; the element predicate decides).
 struct KeySum {
     int smin, smax, any_sink, all_sink;
 };
+__device__ __forceinline__ KeySum make_key_sum(bool uniform, int seg, bool any_sink, bool all_sink) {
+    KeySum k;
+    k.smin = uniform ? seg : 0;
+    k.smax = uniform ? seg : 0x7fffffff;
+    k.any_sink = any_sink;
+    k.all_sink = all_sink;
+    return k;
+}
 
 // Classify a (row group, key sub-tile [k0, k0 + sub)) pair of plain mode, or
 // of the exact columns of compressed mode (plain == false: no segments, no
@@ -64,10 +95,10 @@ __device__ __forceinline__ int classify_exact(const RowSum& r, const KeySum& ks,
     const bool causal_full = k_last <= r.r0;
     // window (and sinks in plain mode)
     bool win_full = true;
+    const bool sinks_matter = plain && window != 0 && ks.any_sink;
     if (window != 0) {
-        const bool any_sink = plain && ks.any_sink;
         const bool all_sink = plain && ks.all_sink;
-        if (r.r0 - k_last >= window && !any_sink) return TILE_SKIP;
+        if (r.r0 - k_last >= window && !sinks_matter) return TILE_SKIP;
         win_full = (r.r1 - k0 < window) || all_sink;
     }
     // packing
@@ -77,10 +108,12 @@ __device__ __forceinline__ int classify_exact(const RowSum& r, const KeySum& ks,
         if (r.smax <= 0 || ks.smax < rlo || ks.smin > r.smax) return TILE_SKIP;
         seg_full = (r.smin == r.smax) && (ks.smin == ks.smax) && (ks.smin == r.smin) && (r.smin > 0);
     }
-    return (causal_full && win_full && seg_full && complete) ? TILE_FULL : TILE_PARTIAL;
+    if (causal_full && win_full && seg_full && complete) return TILE_FULL;
+    return (seg_full && !sinks_matter) ? TILE_PARTIAL_POS : TILE_PARTIAL;
 }
 
-// Classify pooled columns [j0, j0 + sub) for rows r0..r1.
+// Classify pooled columns [j0, j0 + sub) for rows r0..r1.  Partial pooled
+// sub-tiles use the per-row count of visible blocks.
 __device__ __forceinline__ int classify_pooled(const RowSum& r, int j0, int sub, int window, int block,
                                                int nblk) {
     if (j0 >= nblk || r.r1 < r.r0) return TILE_SKIP;
@@ -116,27 +149,146 @@ __device__ __forceinline__ TilePlan plan_tiles(int q0, int q1, int window, int b
     return p;
 }
 
-// Block-wide scan of the sink flags over keys [0, n_keys): bit t of `bits`
-// is set when key tile t (of BN keys) holds at least one sink.  `bits` is in
-// LDS with ceil(n_keys / BN / 32) words.  Ends with a barrier.
-__device__ __forceinline__ void scan_sink_tiles(const uint8_t* prefix_row, int n_keys, int BN,
-                                                uint32_t* bits, int tid, int nthreads) {
+// Block-wide segment range [lo, hi] of rows q0..q1 (lo >= 1; hi < lo when
+// every row is padding).  red is 2 ints of LDS scratch.  Ends with a barrier.
+__device__ __forceinline__ void row_segment_range(const int32_t* seg_row, int q0, int q1, int* red, int tid,
+                                                  int nthreads, int& lo, int& hi) {
+    if (!seg_row) {
+        lo = hi = 1;
+        return;
+    }
+    int smn = 0x7fffffff, smx = 0;
+    for (int r = q0 + tid; r <= q1; r += nthreads) {
+        const int s = seg_row[r];
+        smn = min(smn, s);
+        smx = max(smx, s);
+    }
+    for (int o = 1; o < 64; o <<= 1) {
+        smn = min(smn, __shfl_xor(smn, o, 64));
+        smx = max(smx, __shfl_xor(smx, o, 64));
+    }
+    if (tid == 0) {
+        red[0] = 0x7fffffff;
+        red[1] = 0;
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) {
+        atomicMin(&red[0], smn);
+        atomicMax(&red[1], smx);
+    }
+    __syncthreads();
+    lo = max(1, red[0]);
+    hi = red[1];
+    __syncthreads();
+}
+
+// One thread's 16-key chunk of the sink scan: raw flags and segment ids,
+// loaded first and evaluated once the rows' segment range is known.
+struct SinkChunk {
+    uint4 pre;    // 16 sink flags (bytes)
+    int4 seg[4];  // 16 segment ids (only when seg_row != NULL)
+};
+
+__device__ __forceinline__ void sink_chunk_load(const uint8_t* prefix_row, const int32_t* seg_row, int i0,
+                                                bool aligned16, SinkChunk& c) {
+    if (aligned16) {
+        c.pre = *(const uint4*)(prefix_row + i0);
+        if (seg_row) {
+            for (int g = 0; g < 4; ++g) c.seg[g] = *(const int4*)(seg_row + i0 + 4 * g);
+        }
+    } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int j = 0; j < 16; ++j) w[j >> 2] |= (uint32_t)prefix_row[i0 + j] << (8 * (j & 3));
+        c.pre = make_uint4(w[0], w[1], w[2], w[3]);
+        if (seg_row) {
+            for (int g = 0; g < 4; ++g)
+                c.seg[g] = make_int4(seg_row[i0 + 4 * g], seg_row[i0 + 4 * g + 1], seg_row[i0 + 4 * g + 2],
+                                     seg_row[i0 + 4 * g + 3]);
+        }
+    }
+}
+
+// True when some key of the chunk is a sink whose segment lies in [lo, hi].
+__device__ __forceinline__ bool sink_chunk_hit(const SinkChunk& c, bool has_seg, int lo, int hi) {
+    const uint32_t pws[4] = {c.pre.x, c.pre.y, c.pre.z, c.pre.w};
+    bool f = false;
+    for (int g = 0; g < 4; ++g) {
+        const int ss[4] = {c.seg[g].x, c.seg[g].y, c.seg[g].z, c.seg[g].w};
+        for (int j = 0; j < 4; ++j) {
+            const int s = has_seg ? ss[j] : 1;
+            f |= (((pws[g] >> (8 * j)) & 0xffu) != 0u) & (s >= lo) & (s <= hi);
+        }
+    }
+    return f;
+}
+
+// Block-wide scan over keys [0, n_keys) (n_keys a multiple of 16): bit t of
+// `bits` (LDS, ceil(n_keys / BN / 32) words) is set when key tile t of BN
+// keys holds a sink whose segment lies in [lo, hi] -- the only sinks rows of
+// those segments can see.  `first` (optional) is this thread's chunk at keys
+// [16 * tid, 16 * tid + 16), loaded in advance.  Ends with a barrier.
+__device__ __forceinline__ void scan_sink_tiles(const uint8_t* prefix_row, const int32_t* seg_row, int n_keys,
+                                                int BN, int lo, int hi, bool aligned16, uint32_t* bits, int tid,
+                                                int nthreads, const SinkChunk* first = nullptr) {
     const int ntiles = (n_keys + BN - 1) / BN;
     const int nwords = (ntiles + 31) / 32;
     for (int w = tid; w < nwords; w += nthreads) bits[w] = 0u;
     __syncthreads();
-    for (int i = tid; i < n_keys; i += nthreads) {
-        if (prefix_row[i]) {
-            const int t = i / BN;
-            atomicOr(&bits[t >> 5], 1u << (t & 31));
+    if (hi >= lo) {
+        for (int i0 = 16 * tid; i0 < n_keys; i0 += 16 * nthreads) {
+            SinkChunk c;
+            if (first != nullptr && i0 == 16 * tid) c = *first;
+            else sink_chunk_load(prefix_row, seg_row, i0, aligned16, c);
+            if (sink_chunk_hit(c, seg_row != nullptr, lo, hi)) {
+                const int t = i0 / BN;
+                atomicOr(&bits[t >> 5], 1u << (t & 31));
+            }
         }
     }
     __syncthreads();
 }
 
-// Walks a TilePlan.  Every thread of a workgroup walks the same sequence.
+// Block-wide segment range [lo, hi] from per-lane row segments (rows past
+// the end pass has_row = false).  red is 2 ints of LDS scratch.  Ends with a
+// barrier.
+__device__ __forceinline__ void row_segment_range_from_lanes(int seg, bool has_row, int* red, int tid, int& lo,
+                                                             int& hi) {
+    int smn = has_row ? seg : 0x7fffffff, smx = has_row ? seg : 0;
+    for (int o = 1; o < 64; o <<= 1) {
+        smn = min(smn, __shfl_xor(smn, o, 64));
+        smx = max(smx, __shfl_xor(smx, o, 64));
+    }
+    if (tid == 0) {
+        red[0] = 0x7fffffff;
+        red[1] = 0;
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) {
+        atomicMin(&red[0], smn);
+        atomicMax(&red[1], smx);
+    }
+    __syncthreads();
+    lo = max(1, red[0]);
+    hi = red[1];
+    __syncthreads();
+}
+
+// Sink tiles of a workgroup with rows [q0, q1]: row segment range, then scan.
+__device__ __forceinline__ void plan_sink_tiles(const TilePlan& plan, const int32_t* seg_row,
+                                                const uint8_t* prefix_row, int T, int q0, int q1, int BN, int* red,
+                                                uint32_t* bits, int tid, int nthreads) {
+    if (plan.sink_keys <= 0) return;
+    int lo, hi;
+    row_segment_range(seg_row, q0, q1, red, tid, nthreads, lo, hi);
+    scan_sink_tiles(prefix_row, seg_row, plan.sink_keys, BN, lo, hi, (T & 15) == 0, bits, tid, nthreads);
+}
+
+// Walks a TilePlan: the window band first (its first tile is known before any
+// sink scan, so its loads can start at once), then the pooled tiles or the
+// sink tiles.  Every thread of a workgroup walks the same sequence; the order
+// does not change the result (one softmax over all visited keys).
 struct TileIter {
-    int phase;  // 0 pooled, 1 sinks, 2 band, 3 done
+    int phase;  // 0 band, 1 pooled, 2 sinks, 3 done
     int idx;
     int word;
     uint32_t bits;
@@ -150,42 +302,39 @@ struct TileIter {
         const int ntiles = (p.sink_keys + BN - 1) / BN;
         sink_words = (ntiles + 31) / 32;
         phase = 0;
-        idx = 0;
+        idx = p.band_lo;
         word = -1;
         bits = 0u;
     }
 
     __device__ __forceinline__ bool next(int& kind, int& tile) {
         if (phase == 0) {
-            if (idx < plan.n_pooled) {
-                kind = COL_POOLED;
-                tile = idx++;
-                return true;
-            }
-            phase = 1;
-        }
-        if (phase == 1) {
-            while (bits == 0u) {
-                if (++word >= sink_words) break;
-                bits = sink_bits[word];
-            }
-            if (bits != 0u) {
-                const int b = __builtin_ctz(bits);
-                bits &= bits - 1u;
-                kind = COL_EXACT;
-                tile = word * 32 + b;
-                return true;
-            }
-            phase = 2;
-            idx = plan.band_lo;
-        }
-        if (phase == 2) {
             if (idx <= plan.band_hi) {
                 kind = COL_EXACT;
                 tile = idx++;
                 return true;
             }
-            phase = 3;
+            phase = plan.n_pooled > 0 ? 1 : 2;
+            idx = 0;
+        }
+        if (phase == 1) {
+            if (idx < plan.n_pooled) {
+                kind = COL_POOLED;
+                tile = idx++;
+                return true;
+            }
+            return false;
+        }
+        if (phase == 2) {
+            while (bits == 0u) {
+                if (++word >= sink_words) return false;
+                bits = sink_bits[word];
+            }
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            kind = COL_EXACT;
+            tile = word * 32 + b;
+            return true;
         }
         return false;
     }

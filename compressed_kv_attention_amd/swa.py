@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libswa.so")
 SWA_OK, SWA_ERR_INVALID, SWA_ERR_UNSUPPORTED, SWA_ERR_HIP = 0, 1, 2, 3
 SWA_F32, SWA_BF16 = 0, 1
 
-EXPORTS = ("swa_last_error", "swa_version", "swa_attn_prefill", "swa_debug_visibility", "swa_rope_table",
+EXPORTS = ("swa_last_error", "swa_version", "swa_prefill_workspace_size", "swa_attn_prefill", "swa_debug_visibility", "swa_rope_table",
            "kv_pool_compress_rope", "swa_kv_quantize", "swa_decode_workspace_size", "swa_attn_decode",
            "swa_kv_budget_window", "swa_effective_kv_window")
 
@@ -56,7 +56,9 @@ def lib():
     L.swa_last_error.restype = ctypes.c_char_p
     L.swa_last_error.argtypes = []
     L.swa_version.restype = I
-    L.swa_attn_prefill.argtypes = [ctypes.POINTER(PrefillParams)] + [P] * 12
+    L.swa_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
+    L.swa_prefill_workspace_size.restype = Z
+    L.swa_attn_prefill.argtypes = [ctypes.POINTER(PrefillParams)] + [P] * 11 + [P, Z, P]
     L.swa_attn_prefill.restype = I
     L.swa_debug_visibility.argtypes = [ctypes.POINTER(PrefillParams), P, P, P, P, P]
     L.swa_debug_visibility.restype = I
@@ -125,9 +127,19 @@ def prefill_params(q, k, window, compress_block=0, rope_len=0, scale=0.0):
                          _swa_dtype(q))
 
 
+def prefill_workspace(q, k, window=0, rope=None, compress_block=0):
+    """Allocate the workspace a prefill call with these arguments needs (None if none)."""
+    rope_len = rope[0].shape[0] if rope is not None else 0
+    p = prefill_params(q, k, window, compress_block, rope_len)
+    n = lib().swa_prefill_workspace_size(ctypes.byref(p))
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
 def prefill(q, k, v, seg_ids=None, prefix=None, window=0, rope=None, pooled_k=None, pooled_v=None,
-            compress_block=0, scale=0.0, return_lse=False, out=None):
-    """Windowed+sink (or compressed) prefill attention.  q [B,Hq,T,D], k/v [B,Hkv,T,D]."""
+            compress_block=0, scale=0.0, return_lse=False, out=None, workspace=None):
+    """Windowed+sink (or compressed) prefill attention.  q [B,Hq,T,D], k/v [B,Hkv,T,D].
+
+    workspace: optional preallocated buffer (see prefill_workspace); allocated here if needed."""
     _dev(q, "q")
     _dev(k, "k", q.dtype)
     _dev(v, "v", q.dtype)
@@ -143,9 +155,13 @@ def prefill(q, k, v, seg_ids=None, prefix=None, window=0, rope=None, pooled_k=No
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    ws_bytes = lib().swa_prefill_workspace_size(ctypes.byref(p))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().swa_attn_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(pooled_k), _ptr(pooled_v),
                                   _ptr(seg_ids), _ptr(prefix), _ptr(cos), _ptr(sin), _ptr(out), _ptr(lse),
-                                  _stream(q)))
+                                  _ptr(workspace), ws_len, _stream(q)))
     return (out, lse) if return_lse else out
 
 

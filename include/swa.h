@@ -62,14 +62,21 @@ int swa_version(void);
 /* already be rotated (kv_pool_compress_rope does that); seg_ids and prefix   */
 /* must be NULL and window >= 1.                                             */
 /*                                                                           */
-/* RoPE: with rope_len > 0, q and the exact k are rotated inside the kernel   */
-/* at their row index t with the tables from swa_rope_table (rotate-half      */
-/* pairing (i, i + D/2)); rope_len must be >= T.  rope_len == 0 means q and k */
-/* are used as given.                                                        */
+/* RoPE: with rope_len > 0, q and the exact k are rotated at their row index */
+/* t with the tables from swa_rope_table (rotate-half pairing (i, i + D/2)):  */
+/* q inside the attention kernel, k by a pre-pass into the workspace.         */
+/* rope_len must be >= T.  rope_len == 0 means q and k are used as given.     */
 /*                                                                           */
 /* Rows with no visible key (segment 0 padding) get out = 0 and lse = -inf.  */
 /* Accumulation is fp32 for both dtypes; bf16 runs the MFMA kernel, f32 runs */
 /* an fp32 vector kernel.                                                    */
+/*                                                                           */
+/* Workspace (swa_prefill_workspace_size bytes, 256-byte aligned; required */
+/* whenever that size is > 0): pre-passes write into it (a) for bf16 plain   */
+/* mode, seg_ids and prefix packed to one int32 per key, B*T*4 bytes, and     */
+/* (b) with RoPE, the rotated keys, B*Hkv*T*D*sizeof(dtype) bytes; each part  */
+/* is rounded up to 256 bytes.  Its contents are scratch between calls; two  */
+/* calls that overlap in time need two workspaces.                           */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     int B, Hq, Hkv, T, D; /* q, out: [B,Hq,T,D]; k, v: [B,Hkv,T,D]; Hq % Hkv == 0; D in {32, 64} */
@@ -80,6 +87,9 @@ typedef struct {
     int dtype;            /* swa_dtype of q, k, v, pooled_k, pooled_v and out             */
 } swa_prefill_params;
 
+/* Bytes of workspace swa_attn_prefill needs for these parameters.          */
+size_t swa_prefill_workspace_size(const swa_prefill_params* p);
+
 int swa_attn_prefill(const swa_prefill_params* p,
                      const void* q, const void* k, const void* v,
                      const void* pooled_k, const void* pooled_v, /* NULL unless compress_block > 0 */
@@ -88,6 +98,7 @@ int swa_attn_prefill(const swa_prefill_params* p,
                      const float* rope_cos, const float* rope_sin, /* [rope_len, D/2] or NULL      */
                      void* out,                                  /* [B,Hq,T,D], dtype of q         */
                      float* lse,                                 /* [B,Hq,T] natural-log LSE or NULL */
+                     void* workspace, size_t workspace_bytes,    /* see swa_prefill_workspace_size */
                      void* stream);
 
 /* Visibility as the prefill kernels see it: the same tile enumeration, the  */

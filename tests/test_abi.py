@@ -44,10 +44,11 @@ def _p(**kw):
     return swa.PrefillParams(**d)
 
 
-def _prefill(p, ptrs=None, seg=None, prefix=None, pk=None, pv=None, cos=None, sin=None, lse=None):
+def _prefill(p, ptrs=None, seg=None, prefix=None, pk=None, pv=None, cos=None, sin=None, lse=None, ws=None,
+             ws_bytes=0):
     L = swa.lib()
     q = k = v = out = ptrs
-    rc = L.swa_attn_prefill(ctypes.byref(p), q, k, v, pk, pv, seg, prefix, cos, sin, out, lse, None)
+    rc = L.swa_attn_prefill(ctypes.byref(p), q, k, v, pk, pv, seg, prefix, cos, sin, out, lse, ws, ws_bytes, None)
     return rc, L.swa_last_error().decode()
 
 
@@ -78,6 +79,20 @@ def test_prefill_rejects_null_and_misaligned_pointers():
     assert rc == swa.SWA_ERR_UNSUPPORTED and "seg_ids" in msg
     rc, msg = _prefill(_p(rope_len=64), ptrs=FAKE)                # tables missing
     assert rc == swa.SWA_ERR_INVALID and "rope_cos" in msg
+    rc, msg = _prefill(_p(rope_len=64), ptrs=FAKE, cos=FAKE, sin=FAKE)   # workspace missing
+    assert rc == swa.SWA_ERR_INVALID and "workspace" in msg
+    size = lambda p: swa.lib().swa_prefill_workspace_size(ctypes.byref(p))
+    need = size(_p(rope_len=64))
+    assert need == 256 + 1 * 2 * 64 * 64 * 2          # packed key info (B*T int32, 256-rounded) + rotated keys
+    rc, msg = _prefill(_p(rope_len=64), ptrs=FAKE, cos=FAKE, sin=FAKE, ws=FAKE, ws_bytes=need - 1)
+    assert rc == swa.SWA_ERR_INVALID and "too small" in msg
+    assert size(_p()) == 256                                   # bf16 plain: key info only
+    assert size(_p(T=65)) == 512
+    assert size(_p(dtype=swa.SWA_F32)) == 0                    # the fp32 kernel reads seg/prefix itself
+    assert size(_p(compress_block=4)) == 0                     # no segments in compressed mode
+    assert size(_p(compress_block=4, rope_len=64)) == 1 * 2 * 64 * 64 * 2
+    rc, msg = _prefill(_p(), ptrs=FAKE)                        # bf16 plain without workspace
+    assert rc == swa.SWA_ERR_INVALID and "workspace" in msg
 
 
 def test_empty_problems_are_ok_without_pointers():
