@@ -49,7 +49,53 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch kernels directly instead of replaying HIP graphs (for counter collection)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times) and exit; its HBM counters "
+                         "give the scale factor of FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
+
+
+def kernel_source_hash(name):
+    """sha256 (first 16 hex digits) of the HIP source a kernel is built from; a counter summary taken on
+    other source no longer describes the kernel."""
+    import hashlib
+    src = os.path.join(ROOT, "compressed_kv_attention_amd", "csrc", name)
+    with open(src, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, source):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != kernel_source_hash(source):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib):
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    x = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
 
 
 class Part:
@@ -65,6 +111,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
     import torch
 
     from compressed_kv_attention_amd import swa, workloads
@@ -186,7 +235,22 @@ def main():
 
     stream = torch.cuda.Stream(device=dev)
 
+    class Eager:
+        """Stands in for a captured graph: replay() launches the same work directly."""
+
+        def __init__(self, fn, iters, offset=0):
+            self.fn, self.iters, self.offset = fn, iters, offset
+
+        def replay(self):
+            for i in range(self.iters):
+                self.fn(self.offset + i)
+
     def capture(fn, iters, offset=0):
+        if args.eager:
+            with torch.cuda.stream(stream):
+                fn(offset)
+            torch.cuda.synchronize()
+            return Eager(fn, iters, offset)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
             fn(offset)  # warm the code path on the capture stream
@@ -198,6 +262,7 @@ def main():
         return g
 
     def time_graph(g, replays):
+        # HIP events recorded on the stream the kernels run on
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
             e0.record(stream)
@@ -207,14 +272,18 @@ def main():
         e1.synchronize()
         return e0.elapsed_time(e1)
 
+    def warm(g, n):
+        with torch.cuda.stream(stream):
+            for _ in range(n):
+                g.replay()
+        torch.cuda.synchronize()
+
     # ---- per-part timing (one graph of `reps` iterations each) -----------------
     results = {}
     for name, p in parts.items():
         reps = max(p.ncopies, args.reps)
         g = capture(p.launch, reps)
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
+        warm(g, args.warmup)
         ms = time_graph(g, max(1, args.steps // 4)) / (max(1, args.steps // 4) * reps)
         r = dict(ms=ms)
         if p.flops:
@@ -239,9 +308,7 @@ def main():
             parts[n].launch(i)
     ncopy = max([parts[n].ncopies for n in step_names] + [1])
     step_graph = capture(step, ncopy)
-    for _ in range(args.warmup):
-        step_graph.replay()
-    torch.cuda.synchronize()
+    warm(step_graph, args.warmup)
     replays = max(1, args.steps // ncopy)
     steps_timed = replays * ncopy
     ms_total = time_graph(step_graph, replays)
@@ -271,13 +338,18 @@ def main():
                    "tokens_per_s": round(dec.get("tokens_per_s", 0.0), 1)},
         "parts": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                   for k, v in results.items()},
-        "roofline": {"bound": "mfma", "achieved": round(head.get("tflops", 0.0), 3),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(head.get("frac_mfma_peak", 0.0), 5), "traffic": None,
-                     "kernel": "prefill_bf16_kernel (needle workload)"},
-        "roofline_decode": {"bound": "hbm", "achieved": round(dec.get("gbs", 0.0), 1), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(dec.get("frac_hbm_peak", 0.0), 5), "traffic": None,
-                            "kernel": "decode_kernel"},
+        # The dominant kernel of the step by GPU time is the decode kernel (12 launches per step); one
+        # swa_attn_decode call is exactly one launch of it.  achieved = algorithmic bytes per launch / the
+        # HIP-event average launch duration.
+        "roofline": roofline_decode(dec),
+        # The prefill call on the needle workload: key-info pre-pass + key rotation pre-pass + attention
+        # kernel; the time is that of the whole call.
+        "roofline_prefill": {"bound": "mfma", "achieved": round(head.get("tflops", 0.0), 3),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(head.get("frac_mfma_peak", 0.0), 5),
+                             "hbm_ceiling_tflops": round(hbm_ceiling(head), 1), "traffic": None,
+                             "kernel": "prefill_bf16_kernel + key_info_kernel + rope_rows_bf16_kernel "
+                                       "(one swa_attn_prefill call, needle workload)"},
     }
 
     # ---- CPU baseline: the oracle on a bounded sample of the needle workload ----
@@ -286,30 +358,46 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def hbm_ceiling(r):
+    """MFMA-equivalent ceiling the HBM roof puts on a prefill: 8 TB/s x (visible-pair FLOPs / compulsory
+    bytes)."""
+    if not r.get("gbs"):
+        return 0.0
+    ai = r["tflops"] * 1e12 / (r["gbs"] * 1e9)
+    return HBM_PEAK_GBS * 1e9 * ai / 1e12
+
+
+def roofline_decode(dec):
+    if not dec:
+        return None
+    per_launch = dec["bytes_per_layer"]
+    traffic = measured_traffic("decode_kernel", "decode.hip")
+    return {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dec["gbs"] / HBM_PEAK_GBS, 5), "traffic": traffic,
+            "kernel": "decode_kernel", "bytes_per_launch": per_launch,
+            "ms_per_launch": round(dec["ms_per_launch"], 5)}
+
+
 def cpu_baseline(part, seconds):
-    """Time the CPU oracle on sampled rows of the needle workload (visible-pair TFLOP/s)."""
+    """Time the CPU oracle on the needle workload (visible-pair TFLOP/s).  The oracle evaluates whole
+    passes over every (b, head, row) of the workload, repeated until about `seconds` have elapsed."""
     import oracle
     w = part.w
     B, Hq, T, D = w["B"], w["Hq"], w["T"], w["D"]
-    rng = np.random.default_rng(0)
-    n = 256
-    elapsed = 0.0
-    while True:
-        rows = rng.integers(0, B * Hq * T, size=n).astype(np.int64)
-        t0 = time.perf_counter()
+    rows = np.arange(B * Hq * T, dtype=np.int64)
+    passes, elapsed = 0, 0.0
+    t0 = time.perf_counter()
+    while passes == 0 or elapsed < seconds:
         oracle.prefill(w["q"], w["k"], w["v"], w["seg_ids"], w["prefix"], w["window"], theta=w["rope_theta"],
                        rows=rows)
+        passes += 1
         elapsed = time.perf_counter() - t0
-        if elapsed > seconds / 4 or n >= B * Hq * T:
-            break
-        n = min(B * Hq * T, int(n * max(2.0, seconds / max(elapsed, 1e-3) * 0.9)))
-    # visible pairs of the sampled rows, from the per-row counts of the visibility kernel
-    nvis = part.count[rows // (Hq * T), rows % T]
-    flops = 4.0 * D * float(nvis.astype(np.float64).sum())
+    nvis = float(part.count.astype(np.float64).sum())
+    flops = 4.0 * D * Hq * nvis * passes
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} random (b, head, row) query rows of the needle workload, incl. RoPE of all keys; "
-                      f"{elapsed:.1f} s", "seconds": round(elapsed, 2)}
+            "sample": f"{passes} full passes of the oracle over the needle workload ({B * Hq * T} query rows, "
+                      f"RoPE of all keys included); {elapsed:.1f} s", "seconds": round(elapsed, 2)}
 
 
 if __name__ == "__main__":
