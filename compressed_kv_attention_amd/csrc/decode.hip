@@ -70,26 +70,43 @@ __device__ __forceinline__ float quad_xor2(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
-// One workgroup per (batch row, kv head), 4 waves.  Each lane owns 16
-// channels of one cache row (LPR lanes per row); rows of the sink cache and of
-// the valid ring positions are dealt to the waves in chunks of NR row-steps.
-// Per chunk: scores with v_dot2_f32_f16 on f16 codes, a wave-wide running max
-// per head (so lanes later merge by plain sums), exp2, then O += P V with
-// v_dot2_f32_f16 over pairs of rows.  Waves merge in LDS.
-template <int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+// One workgroup per (batch row, kv head, GW of the G query heads), 4 waves;
+// the G/GW workgroups of a kv head are numbered consecutively on one XCD so
+// they share its L2.  Each lane owns 16 channels of one cache row (LPR lanes
+// per row); rows (sinks, then the valid ring positions) are dealt to the waves
+// in chunks of NR row-steps.  Per chunk: scores with v_dot2_f32_f16 on f16
+// codes, a running max per row group that is raised lazily (only when a score
+// exceeds it by 2^8), exp2, then O += P V with v_dot2_f32_f16 over pairs of
+// rows.  Lanes and waves merge their partial (max, sum, output) in LDS.
+//
+// The appended token is quantized by every workgroup into LDS and attended
+// from there (the ring slot it is written to is never read back in the same
+// call), so the workgroups of a kv head need no ordering between them.
+template <int D, int GW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a) {
     constexpr int LPR = D / 16;    // lanes per row
     constexpr int RPS = 64 / LPR;  // rows per wave-step
     constexpr int NR = 4;          // row-steps per chunk (even)
     constexpr int NW = 4;          // waves
     constexpr int GROUPS = D / 32;
-    __shared__ float red_m[NW][G];
-    __shared__ float red_l[NW][G];
-    __shared__ float red_acc[NW][G][D];
+    constexpr float kGrow = 8.0f;  // lazy rescale threshold (log2 units)
+    __shared__ float part_m[NW][64][GW];
+    __shared__ float part_l[NW][64][GW];
+    __shared__ float part_acc[NW][64][GW][17];  // 16 channels, padded
+    __shared__ __align__(16) int8_t new_codes[2][D];  // appended K and V codes
+    __shared__ float new_scale[2][GROUPS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.x / a.Hkv;
-    const int hkv = blockIdx.x % a.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = a.Hq / a.Hkv;
+    const int nsub = G / GW;
+    const int nblocks = gridDim.x;
+    int lb = blockIdx.x;
+    if ((nblocks & 7) == 0) lb = (blockIdx.x & 7) * (nblocks >> 3) + (blockIdx.x >> 3);
+    const int hs = lb % nsub;
+    const int b = (lb / nsub) / a.Hkv;
+    const int hkv = (lb / nsub) % a.Hkv;
+    const int h0 = hkv * G + hs * GW;  // first query head of this workgroup
     const int W = a.W, S = a.S;
     const int pos_in = a.pos[b];
     const int pos = pos_in < 0 ? -1 : pos_in;  // a negative position appends nothing and sees only sinks
@@ -104,37 +121,44 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int8_t* sv = a.sink_v ? a.sink_v + bh * S * D : nullptr;
     const float* sks = a.sink_ks ? a.sink_ks + bh * S * GROUPS : nullptr;
     const float* svs = a.sink_vs ? a.sink_vs + bh * S * GROUPS : nullptr;
+    const bool append = a.k_new != nullptr && pos >= 0;
+    const int c4 = lane % LPR;     // channel chunk: channels 16*c4 .. 16*c4+15
+    const int rsub = lane / LPR;   // row within a wave-step
 
-    // 1. append the new token into slot pos % W (waves 0 and 1: K and V)
-    if (a.k_new && wave < 2 && pos >= 0) {
+    // 1. quantize the new token (wave 0: K, wave 1: V) into LDS; the first
+    // workgroup of the kv head also writes it into ring slot pos % W
+    if (append && wave < 2) {
         const uint16_t* src = (const uint16_t*)(wave == 0 ? a.k_new : a.v_new) + bh * D;
-        const int slot = pos % W;
-        if (lane < D) {
-            float s;
-            const int code = quantize_lane(bf16_bits_to_f32(src[lane]), s);
-            int8_t* dst = (wave == 0 ? rk : rv) + (size_t)slot * D;
-            float* dsts = (wave == 0 ? rks : rvs) + (size_t)slot * GROUPS;
-            dst[lane] = (int8_t)code;
-            if ((lane & 31) == 0) dsts[lane / 32] = s;
+        const bool in = lane < D;
+        float sc;
+        const int code = quantize_lane(in ? bf16_bits_to_f32(src[in ? lane : 0]) : 0.f, sc);
+        if (in) {
+            new_codes[wave][lane] = (int8_t)code;
+            if ((lane & 31) == 0) new_scale[wave][lane / 32] = sc;
+            if (hs == 0) {
+                const int slot = pos % W;
+                ((wave == 0 ? rk : rv) + (size_t)slot * D)[lane] = (int8_t)code;
+                if ((lane & 31) == 0) (wave == 0 ? rks : rvs)[(size_t)slot * GROUPS + lane / 32] = sc;
+            }
         }
     }
-    __threadfence_block();
     __syncthreads();
 
-    // 2. attend
+    // 2. attend: sink rows [0, sl), ring positions [first, pos]
     const int first = max(sl, pos - W + 1);
     const int n_ring = pos >= first ? pos - first + 1 : 0;
     const int n_rows = sl + n_ring;
-    const int c4 = lane % LPR;     // channel chunk: channels 16*c4 .. 16*c4+15
-    const int rsub = lane / LPR;   // row within a wave-step
+    const int r_new = (append && n_ring > 0) ? n_rows - 1 : 0x7fffffff;  // row held in registers
+    const int first_slot = first >= 0 ? first % W : 0;
     const float c_log2 = a.scale * kLog2e;
 
-    // q of the G heads as f16 pairs of this lane's channels, and their sums
-    uint32_t qp[G][8];
-    float qsum[G];
+    // q of the GW heads as f16 pairs of this lane's channels; their sums times
+    // the code offset start each dot product
+    uint32_t qp[GW][8];
+    float qbias[GW];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.Hq + hkv * G + g) * D + 16 * c4;
+    for (int g = 0; g < GW; ++g) {
+        const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.Hq + h0 + g) * D + 16 * c4;
         const uint4 w0 = *(const uint4*)qrow;
         const uint4 w1 = *(const uint4*)(qrow + 8);
         const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -145,13 +169,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             qp[g][i] = __builtin_bit_cast(uint32_t, h2);
             acc += (float)h2[0] + (float)h2[1];
         }
-        qsum[g] = acc * kBias;
+        qbias[g] = -acc * kBias;
     }
 
-    float m_w[G], l_run[G], wsum[G], acc[G][16];
+    float m_ref[GW], l_run[GW], wsum[GW], acc[GW][16];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m_w[g] = kNegInf;
+    for (int g = 0; g < GW; ++g) {
+        m_ref[g] = kNegInf;
         l_run[g] = 0.f;
         wsum[g] = 0.f;
 #pragma unroll
@@ -166,12 +190,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int t = 0; t < NR; ++t) {
             const int r = base + t * RPS + rsub;
             ok[t] = r < n_rows;
-            const int8_t* kp = rk;
-            const int8_t* vp = rv;
-            const float* ksp = rks;
-            const float* vsp = rvs;
-            int row = 0;
-            if (ok[t]) {
+            kc[t] = vc[t] = make_uint4(0, 0, 0, 0);
+            ksc[t] = vsc[t] = 0.f;
+            if (r == r_new) {  // the appended token
+                kc[t] = *(const uint4*)&new_codes[0][16 * c4];
+                vc[t] = *(const uint4*)&new_codes[1][16 * c4];
+                ksc[t] = new_scale[0][c4 / 2];
+                vsc[t] = new_scale[1][c4 / 2];
+            } else if (ok[t]) {
+                const int8_t* kp = rk;
+                const int8_t* vp = rv;
+                const float* ksp = rks;
+                const float* vsp = rvs;
+                int row;
                 if (r < sl) {
                     kp = sk;
                     vp = sv;
@@ -179,16 +210,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                     vsp = svs;
                     row = r;
                 } else {
-                    row = (first + (r - sl)) % W;
+                    row = first_slot + (r - sl);
+                    row = row >= W ? row - W : row;
                 }
+                kc[t] = *(const uint4*)(kp + (size_t)row * D + 16 * c4);
+                vc[t] = *(const uint4*)(vp + (size_t)row * D + 16 * c4);
+                ksc[t] = ksp[(size_t)row * GROUPS + c4 / 2];
+                vsc[t] = vsp[(size_t)row * GROUPS + c4 / 2];
             }
-            kc[t] = ok[t] ? *(const uint4*)(kp + (size_t)row * D + 16 * c4) : make_uint4(0, 0, 0, 0);
-            vc[t] = ok[t] ? *(const uint4*)(vp + (size_t)row * D + 16 * c4) : make_uint4(0, 0, 0, 0);
-            ksc[t] = ok[t] ? ksp[(size_t)row * GROUPS + c4 / 2] : 0.f;
-            vsc[t] = ok[t] ? vsp[(size_t)row * GROUPS + c4 / 2] : 0.f;
         }
-        // scores (log2 units)
-        float sc[NR][G];
+        // scores (log2 units); every lane of a row ends with the row's score
+        float sc[NR][GW];
 #pragma unroll
         for (int t = 0; t < NR; ++t) {
             const uint32_t kw[4] = {kc[t].x ^ 0x80808080u, kc[t].y ^ 0x80808080u, kc[t].z ^ 0x80808080u,
@@ -199,28 +231,36 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                 kh[2 * i] = __builtin_amdgcn_perm(kMagic, kw[i], kSelLo);
                 kh[2 * i + 1] = __builtin_amdgcn_perm(kMagic, kw[i], kSelHi);
             }
+            const float ks = ksc[t] * c_log2;
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float d = 0.f;
+            for (int g = 0; g < GW; ++g) {
+                float d = qbias[g];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) d = fdot2(qp[g][i], kh[i], d);
-                d = (d - qsum[g]) * ksc[t];
+                d *= ks;
                 d += quad_xor1(d);
                 if (LPR == 4) d += quad_xor2(d);
-                sc[t][g] = ok[t] ? d * c_log2 : kNegInf;
+                sc[t][g] = ok[t] ? d : kNegInf;
             }
         }
-        // wave-wide running max per head; rescale when it grows
+        // raise the reference max of a row group only when a score outgrows it
+        // by more than 2^8 (the first valid row always does)
+        float cmax[GW];
+        bool grow = false;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float mx = sc[0][g];
+        for (int g = 0; g < GW; ++g) {
+            cmax[g] = sc[0][g];
 #pragma unroll
-            for (int t = 1; t < NR; ++t) mx = fmaxf(mx, sc[t][g]);
+            for (int t = 1; t < NR; ++t) cmax[g] = fmaxf(cmax[g], sc[t][g]);
+            grow |= cmax[g] > m_ref[g] + kGrow;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-            for (int o = LPR; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-            if (mx > m_w[g]) {  // wave-uniform
-                const float corr = m_w[g] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_w[g] - mx);
-                m_w[g] = mx;
+            for (int g = 0; g < GW; ++g) {
+                const bool up = cmax[g] > m_ref[g] + kGrow;
+                const float corr =
+                    up ? (m_ref[g] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_ref[g] - cmax[g])) : 1.f;
+                m_ref[g] = up ? cmax[g] : m_ref[g];
                 l_run[g] *= corr;
                 wsum[g] *= corr;
 #pragma unroll
@@ -245,76 +285,64 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                 vh[4 * i + 3] = __builtin_amdgcn_perm(kMagic, p1, kSelHi);
             }
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float p0 = __builtin_amdgcn_exp2f(sc[t][g] - m_w[g]);
-                const float p1 = __builtin_amdgcn_exp2f(sc[t + 1][g] - m_w[g]);
+            for (int g = 0; g < GW; ++g) {
+                const float p0 = ok[t] ? __builtin_amdgcn_exp2f(sc[t][g] - m_ref[g]) : 0.f;
+                const float p1 = ok[t + 1] ? __builtin_amdgcn_exp2f(sc[t + 1][g] - m_ref[g]) : 0.f;
                 l_run[g] += p0 + p1;
                 const half2_t w2 = cvt_pk_f16(p0 * vsc[t], p1 * vsc[t + 1]);
-                wsum[g] += (float)w2[0] + (float)w2[1];
                 const uint32_t wp = __builtin_bit_cast(uint32_t, w2);
+                wsum[g] = fdot2(wp, 0x3c003c00u, wsum[g]);  // exact sum of the two f16 weights
 #pragma unroll
                 for (int c = 0; c < 16; ++c) acc[g][c] = fdot2(vh[c], wp, acc[g][c]);
             }
         }
     }
 
-    // lanes holding the same channels (different rows) share the running max:
-    // plain sums over the row bits of the lane index
+    // 3. merge: every lane leaves (max, sum, 16 outputs) per head in LDS; the
+    // rows of a lane quad carry identical max and sum
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < GW; ++g) {
         const float bias = kBias * wsum[g];
+        part_m[wave][lane][g] = m_ref[g];
+        part_l[wave][lane][g] = l_run[g];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc[g][c] -= bias;
-#pragma unroll
-        for (int o = LPR; o < 64; o <<= 1) {
-            l_run[g] += __shfl_xor(l_run[g], o, 64);
-#pragma unroll
-            for (int c = 0; c < 16; ++c) acc[g][c] += __shfl_xor(acc[g][c], o, 64);
-        }
-    }
-    if (rsub == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (c4 == 0) {
-                red_m[wave][g] = m_w[g];
-                red_l[wave][g] = l_run[g];
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) red_acc[wave][g][16 * c4 + i] = acc[g][i];
-        }
+        for (int i = 0; i < 16; ++i) part_acc[wave][lane][g][i] = acc[g][i] - bias;
     }
     __syncthreads();
-    // final merge across waves (log2 units): thread -> (g, d)
-    for (int e = tid; e < G * D; e += blockDim.x) {
+    // thread -> (head g, channel d): combine the NW * RPS partials of its channel chunk
+    for (int e = tid; e < GW * D; e += 64 * NW) {
         const int g = e / D, d = e % D;
+        const int cc = d / 16, i = d % 16;
         float m = kNegInf;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) m = fmaxf(m, red_m[w][g]);
+        for (int w = 0; w < NW; ++w)
+            for (int r = 0; r < RPS; ++r) m = fmaxf(m, part_m[w][r * LPR + cc][g]);
         float l = 0.f, o = 0.f;
         if (m != kNegInf) {
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float f = red_m[w][g] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(red_m[w][g] - m);
-                l += red_l[w][g] * f;
-                o += red_acc[w][g][d] * f;
-            }
+            for (int w = 0; w < NW; ++w)
+                for (int r = 0; r < RPS; ++r) {
+                    const int ln = r * LPR + cc;
+                    const float mm = part_m[w][ln][g];
+                    const float f = mm == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mm - m);
+                    l += part_l[w][ln][g] * f;
+                    o += part_acc[w][ln][g][i] * f;
+                }
         }
         const float val = l > 0.f ? o / l : 0.f;
-        ((uint16_t*)a.out)[((size_t)b * a.Hq + hkv * G + g) * D + d] = (uint16_t)f32_to_bf16_bits(val);
+        ((uint16_t*)a.out)[((size_t)b * a.Hq + h0 + g) * D + d] = (uint16_t)f32_to_bf16_bits(val);
     }
 }
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     const int G = a.Hq / a.Hkv;
-    const dim3 grid(a.B * a.Hkv), block(256);
-    switch (G) {
-        case 1: hipLaunchKernelGGL((decode_kernel<D, 1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<D, 4>), grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((decode_kernel<D, 8>), grid, block, 0, s, a); break;
-        default: return hipErrorInvalidValue;
-    }
+    const int gw = G >= 2 ? 2 : 1;
+    const long long nblocks = (long long)a.B * a.Hkv * (G / gw);
+    if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)nblocks), block(256);
+    if (gw == 2)
+        hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, 1>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
