@@ -11,6 +11,12 @@
 #include "swa_common.h"
 #include "swa_internal.h"
 
+// Optional phase-time accounting for profiling builds; no code in normal builds.
+#ifndef SWA_TRACE_DECL
+#define SWA_TRACE_DECL
+#define SWA_TRACE(slot)
+#endif
+
 namespace swa {
 namespace {
 
@@ -74,11 +80,14 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // DPP quad permutations: xor 2 within a quad, and a broadcast of quad lane r.
-__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
-__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+// (Every lane of a quad permutation has a source, so the "old" operand is
+// never used; passing the source itself avoids materialising one.)
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false); }
 template <int R>
 __device__ __forceinline__ float quad_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), R * 0x55, 0xF, 0xF, false));
+    const int x = __float_as_int(v);
+    return __int_as_float(__builtin_amdgcn_update_dpp(x, x, R * 0x55, 0xF, 0xF, false));
 }
 
 // Four int8 codes -> four f16 values 1152 + code (see kMagic).
@@ -87,6 +96,91 @@ __device__ __forceinline__ half4_t codes_to_h4(uint32_t w) {
     const uint32_t lo = __builtin_amdgcn_perm(kMagic, u, kSelLo);
     const uint32_t hi = __builtin_amdgcn_perm(kMagic, u, kSelHi);
     return __builtin_bit_cast(half4_t, make_uint2(lo, hi));
+}
+
+// Inline-asm LDS access.  Cache rows reach LDS by DMA (global_load_lds),
+// which the compiler tracks only as outstanding vector loads, so an LDS read
+// it emitted itself would first wait for every DMA in flight; these reads and
+// the explicit waits keep the next chunk's DMA in flight during this chunk.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(uint32_t, (__attribute__((address_space(3))) const char*)p);
+#else
+    (void)p;
+    return 0u;
+#endif
+}
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
+    u32x4_t r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ u32x2_t lds_read_b64(uint32_t addr) {
+    u32x2_t r;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ uint32_t lds_read_b32(uint32_t addr) {
+    uint32_t r;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)"); }
+template <class X>
+__device__ __forceinline__ void lds_tie(X& x) {
+    asm volatile("" : "+v"(x));
+}
+template <int N>
+__device__ __forceinline__ void vm_wait_upto() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
+}
+
+// A global load the compiler does not track (waited for with vm_wait_upto).
+__device__ __forceinline__ u32x4_t gload_b128_untracked(const void* p) {
+    u32x4_t r;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+
+__device__ __forceinline__ uint32_t gload_u16_untracked(const void* p) {
+    uint32_t r;
+    asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One wave's LDS copy of a chunk of 64 cache rows: K and V codes (row-major,
+// 16-byte pieces of row r stored XOR-swizzled by (r >> 1) so that one row per
+// lane reads without bank conflicts) and the group scales.
+template <int D>
+struct DecBuf {
+    int8_t k[64 * D];
+    int8_t v[64 * D];
+    float ks[64 * (D / 32)];
+    float vs[64 * (D / 32)];
+};
+
+template <int D, int NW, int NBUF>
+struct DecSmem {
+    // chunks in flight, per wave; after its walk a wave leaves its per-head
+    // outputs (before normalisation, [4][D] floats) in its own first buffer
+    DecBuf<D> buf[NW][NBUF];
+    float part_m[NW][4], part_l[NW][4], part_ws[NW][4][D / 32];
+    static_assert(sizeof(DecBuf<D>) >= 4 * D * sizeof(float), "partials fit a chunk buffer");
+    __device__ float* part_o(int w) { return (float*)&buf[w][0]; }
+};
+
+template <int N>
+__device__ __forceinline__ void vm_wait_chunks(int n) {  // wait until at most n * N loads are outstanding
+    switch (n) {
+        case 0: vm_wait_upto<0>(); break;
+        case 1: vm_wait_upto<N>(); break;
+        case 2: vm_wait_upto<2 * N>(); break;
+        default: vm_wait_upto<3 * N>(); break;
+    }
 }
 
 // v_mfma_f32_4x4x4f16 runs 16 independent 4x4x4 blocks; block b is lanes
@@ -100,19 +194,33 @@ __device__ __forceinline__ half4_t codes_to_h4(uint32_t w) {
 //           byte transpose inside the quad)  ->  C(4b+c, r) = partial output
 //           of head r at channel 4i+c over the quad's keys.
 // So every softmax quantity of lane 4b+c belongs to head c and keys 4b..4b+3.
+//
+// A workgroup of NW waves serves one (batch row, kv head, up to 4 query
+// heads); the waves take the chunks of the walk in turn and merge at the end.
+// Rows reach LDS by DMA in coalesced 16-rows-per-instruction pieces with NBUF
+// chunks in flight per wave, and each lane then reads its own row.  The walk
+// is cut into chunks of 64 rows that lie wholly in the sink cache or wholly
+// in the ring (one base pointer per chunk).
+//
+// The appended token is quantized in registers while the first chunks load
+// (the first wave of the kv head also stores it into ring slot pos % W,
+// which the walk over positions [first, pos - 1] never reads); it joins the
+// final merge as one more exact softmax partial, so the walk needs no
+// per-lane special case.
 template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeArgs a) {
     constexpr int NI = D / 4;       // 4-channel instructions per row
     constexpr int GROUPS = D / 32;  // scale groups per row
-    constexpr int NW = 2;           // waves
+    constexpr int NW = 2;           // waves per workgroup
+    constexpr int NBUF = 2;         // chunks in flight per wave
     constexpr int CH = 64;          // rows per chunk (one per lane)
+    constexpr int CPR = D / 16;     // 16-byte pieces per row
+    constexpr int RPI = 64 / CPR;   // rows per DMA instruction
+    constexpr int NKI = CH / RPI;   // DMA instructions per chunk for K (and for V)
+    constexpr int NDMA = 2 * NKI + 2 * GROUPS;  // DMA instructions per chunk
     constexpr float kGrow = 8.0f;   // lazy rescale threshold (log2 units)
-    __shared__ float part_acc[NW][64][NI * 4 + 1];
-    __shared__ float part_ws[NW][64][GROUPS];
-    __shared__ float part_l[NW][64];
-    __shared__ float part_m[NW][4];
-    __shared__ __align__(16) int8_t new_codes[2][D];  // appended K and V codes
-    __shared__ float new_scale[2][GROUPS];
+    __shared__ __align__(16) DecSmem<D, NW, NBUF> sm;
+    SWA_TRACE_DECL
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -122,8 +230,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int hs = blockIdx.x % nsub;
     const int b = (blockIdx.x / nsub) / a.Hkv;
     const int hkv = (blockIdx.x / nsub) % a.Hkv;
-    const int h0 = hkv * G + hs * 4;            // first query head of this workgroup
-    const int nh = min(4, G - hs * 4);          // heads served (padding heads have q = 0)
+    const int h0 = hkv * G + hs * 4;    // first query head of this wave
+    const int nh = min(4, G - hs * 4);  // heads served (padding heads have q = 0)
     const int W = a.W, S = a.S;
     const int pos_in = a.pos[b];
     const int pos = pos_in < 0 ? -1 : pos_in;  // a negative position appends nothing and sees only sinks
@@ -141,97 +249,151 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     const bool append = a.k_new != nullptr && pos >= 0;
 
     // rows: sinks [0, sl), then ring positions [first, pos]; with an append
-    // the last of them (position pos) comes from LDS
+    // the last of them (position pos) is merged from LDS at the end
     const int first = max(sl, pos - W + 1);
     const int n_ring = pos >= first ? pos - first + 1 : 0;
-    const int n_rows = sl + n_ring;
-    const int r_new = (append && n_ring > 0) ? n_rows - 1 : -1;
+    const bool has_new = append && n_ring > 0;
+    const int n_ring_mem = n_ring - (has_new ? 1 : 0);  // ring rows read from the cache
     const int first_slot = first >= 0 ? first % W : 0;
+    const int nc_s = (sl + CH - 1) / CH;
+    const int n_chunks = nc_s + (n_ring_mem + CH - 1) / CH;
     const float c_log2 = a.scale * kLog2e;
+    // Waves start their walks at different chunks (the softmax does not care
+    // about the order), so the first requests of all waves do not land on the
+    // same offsets of equally sized cache regions at once.  Step ci of the
+    // walk reads chunk (ci + rot) mod n_chunks; steps past the end read
+    // nothing useful.
+    const int rot = n_chunks > 0 ? (int)(blockIdx.x % (unsigned)n_chunks) : 0;
+    auto chunk_of = [&](int ci) { return ci < n_chunks ? (ci + rot) % n_chunks : ci; };
+    // this wave's steps: kk -> walk step wave + NW * kk
+    const int n_steps = n_chunks > wave ? (n_chunks - wave + NW - 1) / NW : 0;
+    auto rows_of = [&](int cj) { return cj < nc_s ? min(CH, sl - cj * CH) : min(CH, n_ring_mem - (cj - nc_s) * CH); };
+    auto chunk_rows = [&](int ci) { return rows_of(chunk_of(ci)); };
 
-    // Row r of the walk -> cache row; rows past the end read row 0 of the
-    // ring (valid memory) and are masked, so every chunk issues the same loads.
-    uint4 kr[NI / 4], vr[NI / 4];
-    float2 ksc, vsc;
-    auto row_of = [&](int base, bool& sink) {
-        const int r = base + lane;
-        const bool ok = r < n_rows && r != r_new;
-        sink = ok && r < sl;
-        int row = first_slot + (r - sl);
-        row = row >= W ? row - W : row;
-        return ok ? (sink ? r : row) : 0;
+    // per-head sums over the wave's lanes of head c (lane bits 2..5)
+    auto all_blocks = [](float x) {
+        x += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x124, 0xF, 0xF, false));
+        x += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x128, 0xF, 0xF, false));
+        auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+        auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
     };
-    auto load_k = [&](int base) {
-        bool sink;
-        const int row = row_of(base, sink);
-        const int8_t* kp = (sink ? sk : rk) + (size_t)row * D;
-#pragma unroll
-        for (int j = 0; j < NI / 4; ++j) kr[j] = *(const uint4*)(kp + 16 * j);
-        const float* ksp = (sink ? sks : rks) + (size_t)row * GROUPS;
-        ksc.x = ksp[0];
-        ksc.y = GROUPS > 1 ? ksp[GROUPS - 1] : 0.f;
-    };
-    auto load_v = [&](int base) {
-        bool sink;
-        const int row = row_of(base, sink);
-        const int8_t* vp = (sink ? sv : rv) + (size_t)row * D;
-#pragma unroll
-        for (int j = 0; j < NI / 4; ++j) vr[j] = *(const uint4*)(vp + 16 * j);
-        const float* vsp = (sink ? svs : rvs) + (size_t)row * GROUPS;
-        vsc.x = vsp[0];
-        vsc.y = GROUPS > 1 ? vsp[GROUPS - 1] : 0.f;
-    };
-    int base = wave * CH;
-    load_k(base);
-    load_v(base);
 
-    // q of head c as the B operand: 4 channels per instruction, f16
-    half4_t qb[NI];
-    float qbias[GROUPS];
+    // q of head c (padding heads read head 0 and are zeroed below) and the
+    // appended token's elements of this lane; issued before the cache rows so
+    // they arrive first
+    const bool live = c < nh;
+    u32x4_t qraw[NI / 2];
     {
-        const bool live = c < nh;
         const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.Hq + h0 + (live ? c : 0)) * D;
 #pragma unroll
-        for (int g = 0; g < GROUPS; ++g) qbias[g] = 0.f;
-#pragma unroll
-        for (int j = 0; j < NI / 2; ++j) {
-            const uint4 w = live ? *(const uint4*)(qrow + 8 * j) : make_uint4(0, 0, 0, 0);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const half2_t lo = cvt_pk_f16(__uint_as_float(ws[2 * h] << 16), __uint_as_float(ws[2 * h] & 0xffff0000u));
-                const half2_t hi =
-                    cvt_pk_f16(__uint_as_float(ws[2 * h + 1] << 16), __uint_as_float(ws[2 * h + 1] & 0xffff0000u));
-                qb[2 * j + h] = half4_t{lo[0], lo[1], hi[0], hi[1]};
-                qbias[(8 * j) / 32] += (float)lo[0] + (float)lo[1] + (float)hi[0] + (float)hi[1];
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < GROUPS; ++g) qbias[g] *= -kBias;
+        for (int j = 0; j < NI / 2; ++j) qraw[j] = gload_b128_untracked(qrow + 8 * j);
     }
+    const uint16_t* kn_src = append ? (const uint16_t*)a.k_new + bh * D : (const uint16_t*)a.q;
+    const uint16_t* vn_src = append ? (const uint16_t*)a.v_new + bh * D : (const uint16_t*)a.q;
+    uint32_t xk = gload_u16_untracked(kn_src + lane % D), xv = gload_u16_untracked(vn_src + lane % D);
 
-    // quantize the new token (wave 0: K, wave 1: V) into LDS; the first
-    // workgroup of the kv head also writes it into ring slot pos % W
-    if (append) {
-        const uint16_t* src = (const uint16_t*)(wave == 0 ? a.k_new : a.v_new) + bh * D;
-        const bool in = lane < D;
-        float sc;
-        const int code = quantize_lane(in ? bf16_bits_to_f32(src[in ? lane : 0]) : 0.f, sc);
-        if (in) {
-            new_codes[wave][lane] = (int8_t)code;
-            if ((lane & 31) == 0) new_scale[wave][lane / 32] = sc;
-            if (hs == 0) {
-                const int slot = pos % W;
-                ((wave == 0 ? rk : rv) + (size_t)slot * D)[lane] = (int8_t)code;
-                if ((lane & 31) == 0) (wave == 0 ? rks : rvs)[(size_t)slot * GROUPS + lane / 32] = sc;
-            }
+    // DMA of chunk ci into buffer bi: NKI instructions each for K and V (RPI
+    // rows of CPR pieces), GROUPS each for the two scale arrays; a chunk past
+    // the end reads row 0 of its cache and is never used
+    auto issue = [&](int ci, int bi) {
+        const int cj = chunk_of(ci);
+        const bool sink = cj < nc_s;
+        const int j0 = (sink ? cj : cj - nc_s) * CH;
+        const int valid = rows_of(cj);
+        const int8_t* kb = sink ? sk : rk;
+        const int8_t* vb = sink ? sv : rv;
+        const float* ksb = sink ? sks : rks;
+        const float* vsb = sink ? svs : rvs;
+        auto row_of = [&](int rr) {  // (selects, no branches: the wait counts stay static)
+            const int rs = j0 + rr;
+            int rg = first_slot + rs;
+            rg = rg >= W ? rg - W : rg;
+            const int row = sink ? rs : rg;
+            return rr < valid ? row : 0;
+        };
+        DecBuf<D>& B = sm.buf[wave][bi];
+#pragma unroll
+        for (int j = 0; j < NKI; ++j) {
+            const int rr = j * RPI + lane / CPR;
+            const int pc = lane % CPR;
+            const int lc = pc ^ ((rr >> 1) & (CPR - 1));  // logical piece stored at slot pc
+            const uint32_t off = (uint32_t)row_of(rr) * D + 16 * lc;
+            __builtin_amdgcn_global_load_lds(kb + off, (lds_void_t*)&B.k[j * 1024], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb + off, (lds_void_t*)&B.v[j * 1024], 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < GROUPS; ++j) {
+            const int f = 64 * j + lane;
+            const uint32_t off = (uint32_t)row_of(f / GROUPS) * GROUPS + f % GROUPS;
+            __builtin_amdgcn_global_load_lds(ksb + off, (lds_void_t*)&B.ks[64 * j], 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(vsb + off, (lds_void_t*)&B.vs[64 * j], 4, 0, 0);
+        }
+    };
+    // the first chunk now, the rest once q is ready: the first requests of
+    // all waves then reach memory ahead of everything else
+    issue(wave, 0);
+
+    // q of head c as the B operand: 4 channels per instruction, f16 (q and
+    // the new token were loaded before the NDMA DMA instructions of chunk 0)
+    vm_wait_upto<NDMA>();
+#pragma unroll
+    for (int j = 0; j < NI / 2; ++j) lds_tie(qraw[j]);
+    lds_tie(xk);
+    lds_tie(xv);
+    half4_t qb[NI];
+    float qbias[GROUPS];
+#pragma unroll
+    for (int g = 0; g < GROUPS; ++g) qbias[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NI / 2; ++j) {
+        const u32x4_t w = qraw[j];
+        const uint32_t ws[4] = {live ? w[0] : 0u, live ? w[1] : 0u, live ? w[2] : 0u, live ? w[3] : 0u};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const half2_t lo = cvt_pk_f16(__uint_as_float(ws[2 * h] << 16), __uint_as_float(ws[2 * h] & 0xffff0000u));
+            const half2_t hi =
+                cvt_pk_f16(__uint_as_float(ws[2 * h + 1] << 16), __uint_as_float(ws[2 * h + 1] & 0xffff0000u));
+            qb[2 * j + h] = half4_t{lo[0], lo[1], hi[0], hi[1]};
+            qbias[(8 * j) / 32] += (float)lo[0] + (float)lo[1] + (float)hi[0] + (float)hi[1];
         }
     }
-    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GROUPS; ++g) qbias[g] *= -kBias;
+
+    // the appended token: lane l quantizes channel l of K and V; its score on
+    // head c comes from lane 4b + c over channels 4b .. 4b+3 (the codes of
+    // the quad's lanes, whose group scale this lane shares)
+    float s_new = kNegInf;  // score of head c (log2 units), uniform per head
+    float v_new = 0.f;      // dequantized V of channel `lane`
+    int ck = 0, cv = 0;     // its codes and scales (stored into the ring at the end)
+    float sck = 0.f, scv = 0.f;
+    if (append) {
+        ck = quantize_lane(bf16_bits_to_f32((uint16_t)xk), sck);
+        cv = quantize_lane(bf16_bits_to_f32((uint16_t)xv), scv);
+        v_new = (float)cv * scv;
+        if (has_new) {
+            const float kd = (float)ck * sck;  // dequantized K of channel `lane`
+            const int bq = lane >> 2;
+            const float k4[4] = {quad_bcast<0>(kd), quad_bcast<1>(kd), quad_bcast<2>(kd), quad_bcast<3>(kd)};
+            float d = 0.f;
+            if (bq < NI) {
+                const half4_t qv = qb[bq];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d += (float)qv[e] * k4[e];
+            }
+            s_new = all_blocks(d) * c_log2;
+        }
+    }
+#pragma unroll
+    for (int k = 1; k < NBUF; ++k) issue(wave + NW * k, k);
+    SWA_TRACE(0);
 
     // lane-dependent byte selectors of the quad transpose
     const uint32_t sel1 = (c < 2) ? 0x05040100u : 0x03020706u;
     const uint32_t sel2 = (c & 1) ? 0x03070105u : 0x06020400u;
+    const uint32_t swz = (lane >> 1) & (CPR - 1);
 
     f32x4_t acc[NI];
 #pragma unroll
@@ -243,51 +405,88 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
     for (int g = 0; g < GROUPS; ++g) ws_c[g] = 0.f;
 
-    while (base < n_rows) {
-        if (r_new >= base && r_new < base + CH && lane == r_new - base) {  // the appended token
+    for (int kk = 0; kk < n_steps; ++kk) {
+        const int bi = kk % NBUF;
+        const int ci = wave + NW * kk;
+        // this chunk's DMA has landed; the younger chunks in flight are the
+        // prologue's (all issued) and those issued below (only when they exist)
+        {
+            int younger = 0;
 #pragma unroll
-            for (int j = 0; j < NI / 4; ++j) {
-                kr[j] = *(const uint4*)&new_codes[0][16 * j];
-                vr[j] = *(const uint4*)&new_codes[1][16 * j];
-            }
-            ksc = make_float2(new_scale[0][0], new_scale[0][GROUPS - 1]);
-            vsc = make_float2(new_scale[1][0], new_scale[1][GROUPS - 1]);
+            for (int k = 1; k < NBUF; ++k) younger += (kk + k < NBUF || kk + k < n_steps) ? 1 : 0;
+            vm_wait_chunks<NDMA>(younger);
         }
+        SWA_TRACE(1);
+        const DecBuf<D>& B = sm.buf[wave][bi];
+        const int nvalid = chunk_rows(ci);
+        // this lane's row: K and V pieces in logical order
+        u32x4_t kr[CPR], vr[CPR];
+        const uint32_t kbase = lds_addr(&B.k[0]) + 16 * CPR * lane;
+        const uint32_t vbase = lds_addr(&B.v[0]) + 16 * CPR * lane;
+#pragma unroll
+        for (int m = 0; m < CPR; ++m) kr[m] = lds_read_b128(kbase + 16 * (m ^ swz));
+#pragma unroll
+        for (int m = 0; m < CPR; ++m) vr[m] = lds_read_b128(vbase + 16 * (m ^ swz));
+        // the group scales of the quad's four keys (rows 4b .. 4b+3), [key][group]
+        u32x4_t ksw[GROUPS], vsw[GROUPS];
+        const uint32_t qoff = 16 * GROUPS * (lane >> 2);
+#pragma unroll
+        for (int g = 0; g < GROUPS; ++g) {
+            ksw[g] = lds_read_b128(lds_addr(&B.ks[0]) + qoff + 16 * g);
+            vsw[g] = lds_read_b128(lds_addr(&B.vs[0]) + qoff + 16 * g);
+        }
+        lds_wait_all();
+#pragma unroll
+        for (int m = 0; m < CPR; ++m) {
+            lds_tie(kr[m]);
+            lds_tie(vr[m]);
+        }
+#pragma unroll
+        for (int g = 0; g < GROUPS; ++g) {
+            lds_tie(ksw[g]);
+            lds_tie(vsw[g]);
+        }
+        SWA_TRACE(2);
+        // the buffer is free again: the chunk NBUF steps ahead starts loading
+        if (kk + NBUF < n_steps) issue(ci + NW * NBUF, bi);
+
         // scores: C_g(4b+c, r) = sum over group g of q_c * (1152 + code) - 1152 * sum q_c
+        // (the two group chains alternate so consecutive MFMAs are independent)
         f32x4_t s0 = f32x4_t{qbias[0], qbias[0], qbias[0], qbias[0]};
         f32x4_t s1 = f32x4_t{qbias[GROUPS - 1], qbias[GROUPS - 1], qbias[GROUPS - 1], qbias[GROUPS - 1]};
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const uint4 w4 = kr[i / 4];
-            const uint32_t w = (i % 4 == 0) ? w4.x : (i % 4 == 1) ? w4.y : (i % 4 == 2) ? w4.z : w4.w;
-            if (i < 8)
-                s0 = __builtin_amdgcn_mfma_f32_4x4x4f16(codes_to_h4(w), qb[i], s0, 0, 0, 0);
-            else
-                s1 = __builtin_amdgcn_mfma_f32_4x4x4f16(codes_to_h4(w), qb[i], s1, 0, 0, 0);
+        for (int i0 = 0; i0 < 8; ++i0) {
+#pragma unroll
+            for (int gi = 0; gi < GROUPS; ++gi) {
+                const int i = i0 + 8 * gi;
+                const uint32_t w = kr[i / 4][i % 4];
+                if (gi == 0)
+                    s0 = __builtin_amdgcn_mfma_f32_4x4x4f16(codes_to_h4(w), qb[i], s0, 0, 0, 0);
+                else
+                    s1 = __builtin_amdgcn_mfma_f32_4x4x4f16(codes_to_h4(w), qb[i], s1, 0, 0, 0);
+            }
         }
-        // per-key scales of the quad's keys (key 4b + r sits in quad lane r)
-        const float ks0[4] = {quad_bcast<0>(ksc.x), quad_bcast<1>(ksc.x), quad_bcast<2>(ksc.x), quad_bcast<3>(ksc.x)};
-        const float vs0[4] = {quad_bcast<0>(vsc.x), quad_bcast<1>(vsc.x), quad_bcast<2>(vsc.x), quad_bcast<3>(vsc.x)};
-        float ks1[4], vs1[4];
-        if (GROUPS > 1) {
-            ks1[0] = quad_bcast<0>(ksc.y);
-            ks1[1] = quad_bcast<1>(ksc.y);
-            ks1[2] = quad_bcast<2>(ksc.y);
-            ks1[3] = quad_bcast<3>(ksc.y);
-            vs1[0] = quad_bcast<0>(vsc.y);
-            vs1[1] = quad_bcast<1>(vsc.y);
-            vs1[2] = quad_bcast<2>(vsc.y);
-            vs1[3] = quad_bcast<3>(vsc.y);
+        // per-key scales of the quad's keys: key 4b + r, group g at word r * GROUPS + g
+        float ks0[4], vs0[4], ks1[4] = {0.f, 0.f, 0.f, 0.f}, vs1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int w0 = r * GROUPS;
+            ks0[r] = __uint_as_float(ksw[w0 / 4][w0 % 4]);
+            vs0[r] = __uint_as_float(vsw[w0 / 4][w0 % 4]);
+            if (GROUPS > 1) {
+                const int w1 = w0 + 1;
+                ks1[r] = __uint_as_float(ksw[w1 / 4][w1 % 4]);
+                vs1[r] = __uint_as_float(vsw[w1 / 4][w1 % 4]);
+            }
         }
-        load_k(base + NW * CH);  // the next chunk's K rows load while this chunk finishes
-        const int kq = base + (lane & ~3);  // walk index of the quad's key 0
+        const int kq = lane & ~3;  // chunk row of the quad's key 0
         float sc[4];
         bool grow = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float v = s0[r] * ks0[r];
             if (GROUPS > 1) v = __builtin_fmaf(s1[r], ks1[r], v);
-            sc[r] = (kq + r < n_rows) ? v * c_log2 : kNegInf;
+            sc[r] = (kq + r < nvalid) ? v * c_log2 : kNegInf;
             grow |= sc[r] > m_c + kGrow;
         }
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -317,7 +516,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            p[r] = (kq + r < n_rows) ? __builtin_amdgcn_exp2f(sc[r] - m_c) : 0.f;
+            p[r] = (kq + r < nvalid) ? __builtin_amdgcn_exp2f(sc[r] - m_c) : 0.f;
             l_c += p[r];
         }
         const half2_t a0l = cvt_pk_f16(p[0] * vs0[0], p[1] * vs0[1]);
@@ -336,54 +535,115 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         // O += P V: V codes of the quad's keys at channel 4i + c
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const uint4 w4 = vr[i / 4];
-            const uint32_t w = (i % 4 == 0) ? w4.x : (i % 4 == 1) ? w4.y : (i % 4 == 2) ? w4.z : w4.w;
+            const uint32_t w = vr[i / 4][i % 4];
             const uint32_t t = __builtin_amdgcn_perm(dpp_xor2(w), w, sel1);
             const uint32_t col = __builtin_amdgcn_perm(dpp_xor1(t), t, sel2);
             acc[i] = __builtin_amdgcn_mfma_f32_4x4x4f16(i < 8 ? pa0 : pa1, codes_to_h4(col), acc[i], 0, 0, 0);
         }
-        base += NW * CH;
-        load_v(base);
+        SWA_TRACE(3);
     }
+    // every DMA has landed (also unused prologue chunks) before LDS is reused
+    // or the wave ends
+    vm_wait_upto<0>();
 
-    // merge: lanes of one head and channel (16 quads) and the two waves
+    // sum the 16 blocks' partial outputs.  Two halving exchanges (lane bits 5
+    // and 4) leave each lane NJ = NI / 4 channel steps per head; row
+    // rotations by 4 and 8 add the four blocks of each 16-lane row.  Lane l
+    // then holds the totals of channels 4 i + c with i = j + NJ * (l >> 4).
+    constexpr int NJ = NI / 4;
+    float o1[NI / 2][4];
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+    for (int j = 0; j < NI / 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part_acc[wave][lane][4 * i + r] = acc[i][r];
+        for (int r = 0; r < 4; ++r) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[j][r]),
+                                                            __float_as_uint(acc[j + NI / 2][r]), false, false);
+            o1[j][r] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+    float o2[NJ][4];
 #pragma unroll
-    for (int g = 0; g < GROUPS; ++g) part_ws[wave][lane][g] = ws_c[g];
-    part_l[wave][lane] = l_c;
-    if (lane < 4) part_m[wave][lane] = m_c;
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(o1[j][r]), __float_as_uint(o1[j + NJ][r]),
+                                                            false, false);
+            float x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            x += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x124, 0xF, 0xF, false));
+            x += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x128, 0xF, 0xF, false));
+            o2[j][r] = x;
+        }
+    const float l_tot = all_blocks(l_c);
+    float ws_tot[GROUPS];
+#pragma unroll
+    for (int g = 0; g < GROUPS; ++g) ws_tot[g] = all_blocks(ws_c[g]);
+
+    // the first wave of the kv head stores the new token into its ring slot
+    if (append && hs == 0 && wave == 0 && lane < D) {
+        const int slot = pos % W;
+        (rk + (size_t)slot * D)[lane] = (int8_t)ck;
+        (rv + (size_t)slot * D)[lane] = (int8_t)cv;
+        if ((lane & 31) == 0) {
+            rks[(size_t)slot * GROUPS + lane / 32] = sck;
+            rvs[(size_t)slot * GROUPS + lane / 32] = scv;
+        }
+    }
+    SWA_TRACE(4);
+
+    // merge of the waves: each leaves its per-head totals in LDS; then every
+    // lane of the workgroup produces outputs (head, channel) together with the
+    // appended token
+    const int i_out = (lane >> 2) % NJ;
+    const bool writer = ((lane >> 2) & 3) < NJ;
+    {
+        const int ch = 4 * (i_out + NJ * (lane >> 4)) + c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float o = o2[0][r];
+#pragma unroll
+            for (int j = 1; j < NJ; ++j) o = i_out == j ? o2[j][r] : o;
+            if (writer) sm.part_o(wave)[r * D + ch] = o;
+        }
+        if (lane < 4) {
+            sm.part_m[wave][lane] = m_c;
+            sm.part_l[wave][lane] = l_tot;
+#pragma unroll
+            for (int g = 0; g < GROUPS; ++g) sm.part_ws[wave][lane][g] = ws_tot[g];
+        }
+    }
     __syncthreads();
-    for (int e = tid; e < 4 * D; e += 64 * NW) {
-        const int h = e / D, d = e % D;
-        if (h >= nh) continue;
-        const int i = d / 4, cc = d % 4, g = d / 32;
-        float m = kNegInf;
+    const float sn[4] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_new), 0)),
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_new), 1)),
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_new), 2)),
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_new), 3))};
+    for (int e = tid; e < 4 * D; e += 64 * NW) {  // (4 * D is a multiple of the block size)
+        const int r = e / D, d = e % D;
+        const float vn = __shfl(v_new, d, 64);    // before any lane leaves the loop body
+        if (r >= nh) continue;
+        const int g = d / 32;
+        const float sr = r == 0 ? sn[0] : r == 1 ? sn[1] : r == 2 ? sn[2] : sn[3];
+        float m = sr;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) m = fmaxf(m, part_m[w][h]);
-        float l = 0.f, o = 0.f;
+        for (int w = 0; w < NW; ++w) m = fmaxf(m, sm.part_m[w][r]);
+        float num = 0.f, den = 0.f;
         if (m != kNegInf) {
+            if (sr != kNegInf) {
+                const float fn = __builtin_amdgcn_exp2f(sr - m);
+                num = fn * vn;
+                den = fn;
+            }
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                const float mw = part_m[w][h];
+                const float mw = sm.part_m[w][r];
                 if (mw == kNegInf) continue;
-                float ow = 0.f, wsw = 0.f, lw = 0.f;
-#pragma unroll
-                for (int q4 = 0; q4 < 16; ++q4) {
-                    ow += part_acc[w][4 * q4 + cc][4 * i + h];
-                    wsw += part_ws[w][4 * q4 + h][g];
-                    lw += part_l[w][4 * q4 + h];
-                }
                 const float f = __builtin_amdgcn_exp2f(mw - m);
-                o += (ow - kBias * wsw) * f;
-                l += lw * f;
+                num += f * (sm.part_o(w)[r * D + d] - kBias * sm.part_ws[w][r][g]);
+                den += f * sm.part_l[w][r];
             }
         }
-        const float val = l > 0.f ? o / l : 0.f;
-        ((uint16_t*)a.out)[((size_t)b * a.Hq + h0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(val);
+        const float val = den > 0.f ? num / den : 0.f;
+        ((uint16_t*)a.out)[((size_t)b * a.Hq + h0 + r) * D + d] = (uint16_t)f32_to_bf16_bits(val);
     }
+    SWA_TRACE(5);
 }
 
 template <int D>
