@@ -145,11 +145,12 @@ typedef struct {
     int W;             /* ring capacity = window length, >= 1                   */
     int S;             /* sink cache capacity, >= 0                             */
     float scale;       /* 0 selects 1/sqrt(D)                                   */
-    int num_splits;    /* 0 = automatic; >1 splits each row set across workgroups */
+    int num_splits;    /* 0 or 1: one workgroup walks all rows of a (b, kv head);
+                          larger values return SWA_ERR_UNSUPPORTED              */
 } swa_decode_params;
 
-/* Workspace bytes swa_attn_decode needs for these parameters (0 when the    */
-/* chosen split count is 1).                                                 */
+/* Workspace bytes swa_attn_decode needs for these parameters (always 0:    */
+/* the decode kernel keeps its partials on chip).                            */
 size_t swa_decode_workspace_size(const swa_decode_params* p);
 
 /* One decode step with the mask of [NS §"256-token 滑动窗口：源码走读"]:     */
