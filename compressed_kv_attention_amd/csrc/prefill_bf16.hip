@@ -46,7 +46,7 @@ namespace {
 
 constexpr int BN = 64;   // keys per LDS tile
 constexpr int SUB = 32;  // keys per MFMA sub-tile
-constexpr int NBUF = 3;  // LDS tile buffers
+constexpr int NBUF = 2;  // LDS tile buffers: the tile computed and the next one
 constexpr int kSinkWords = (kMaxT / BN + 31) / 32;
 constexpr float kRescaleLog2 = 8.0f;  // rescale when the max grows by > 2^8
 
@@ -282,7 +282,7 @@ __device__ __forceinline__ void issue_vt(uint32_t vbase, int kb, int n, int lane
 }
 
 template <int D, bool ROPE, bool COMPRESSED>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_bf16_kernel(PrefillArgs a) {
     static_assert(D == 32 || D == 64, "head dim");
     __shared__ __align__(16) SmemBf16<D> sm;
     SWA_TRACE_DECL
@@ -324,7 +324,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     TileIter it;
     it.init(plan, sm.sink_bits, BN);
     int kc = 0, tc = 0;  // tile being computed
-    int kn = 0, tn = 0;  // next tile (in flight)
     const bool have0 = it.next(kc, tc);
     if (have0) issue_tile<D>(a, sm, 0, kc, tc, b, hkv, wave, lane);
 
@@ -383,10 +382,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         scan_sink_tiles(pre_row, seg_row, plan.sink_keys, BN, lo, hi, aligned16, sm.sink_bits, tid, nthreads,
                         16 * tid < plan.sink_keys ? &chunk0 : nullptr);
     }
-    const bool have1 = have0 && it.next(kn, tn);
-    int n_new = 0;  // loads of the newest tile this wave has in flight
-    if (have1) n_new = issue_tile<D>(a, sm, 1, kn, tn, b, hkv, wave, lane);
-
+    int n_new = 0;  // (no loads beyond tile 0 are in flight here)
     const float c_log2 = a.scale * kLog2e;
     float m_run = kNegInf;  // reference max (raw score units) used for p
     float l_run = 0.f;
@@ -396,10 +392,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 
-    // tile 0 must have landed; tile 1 may still be in flight
-    wait_vm_upto(n_new);
+    // tile 0 must have landed
+    wait_vm_upto(0);
     if (wave == 0 && have0) summarize_tile<D>(a, sm, 0, kc, tc, lane);
-    wait_vm_upto(n_new);
+    wait_vm_upto(0);
     barrier_raw();
     SWA_TRACE(0);
 
@@ -407,17 +403,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const uint32_t info_lds = lds_off(&sm.kinfo[0][0]), sum_lds = lds_off(&sm.ksum[0][0][0]);
     constexpr uint32_t kTileBytes = BN * D * 2;
     int cur = 0;
-    bool have = have0, have_next = have1;
+    bool have = have0;
     while (have) {
-        const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-        const int nxt2 = nxt == NBUF - 1 ? 0 : nxt + 1;
-        bool have_next2 = false;
-        int k2 = 0, t2 = 0;
+        // the next tile loads into the other buffer (free since the last barrier)
+        const int nxt = cur ^ 1;
+        int kn = 0, tn = 0;
+        const bool have_next = it.next(kn, tn);
         n_new = 0;
-        if (have_next) {
-            have_next2 = it.next(k2, t2);
-            if (have_next2) n_new = issue_tile<D>(a, sm, nxt2, k2, t2, b, hkv, wave, lane);
-        }
+        if (have_next) n_new = issue_tile<D>(a, sm, nxt, kn, tn, b, hkv, wave, lane);
         SWA_TRACE(1);
 
         if (wave_active) {
@@ -561,20 +554,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         }
         SWA_TRACE(2);
 
-        // tile `nxt` must have landed before the barrier; the newest tile may fly on
-        wait_vm_upto(n_new);
+        // tile `nxt` must have landed before the barrier
+        wait_vm_upto(0);
         if (wave == 0 && have_next) summarize_tile<D>(a, sm, nxt, kn, tn, lane);
         SWA_TRACE(3);
-        wait_vm_upto(n_new);
+        wait_vm_upto(0);
         barrier_raw();
         SWA_TRACE(4);
         cur = nxt;
         kc = kn;
         tc = tn;
-        kn = k2;
-        tn = t2;
         have = have_next;
-        have_next = have_next2;
     }
 
     if (!wave_active) return;

@@ -32,10 +32,11 @@ struct PrefillArgs {
     int hpw, rbs;
 };
 
-// Geometry the bf16 MFMA kernel uses for a given GQA group size: 8 waves per
+// Geometry the bf16 MFMA kernel uses for a given GQA group size: 4 waves per
 // workgroup, hpw heads (the largest divisor of G that is at most 4) times rbs
-// 32-row blocks (hpw * rbs <= 8 compute waves; the rest only stage tiles).
-constexpr int kMfmaWaves = 8;
+// 32-row blocks (hpw * rbs = 4).  With G >= 4 every wave of a workgroup has
+// the same rows, hence the same mask and the same amount of work.
+constexpr int kMfmaWaves = 4;
 struct MfmaGeom {
     int hpw, rbs;
 };
