@@ -326,6 +326,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     int kc = 0, tc = 0;  // tile being computed
     const bool have0 = it.next(kc, tc);
     if (have0) issue_tile<D>(a, sm, 0, kc, tc, b, hkv, wave, lane);
+    SWA_TRACE(6);
 
     uint4 raw[D / 16];
     {
@@ -365,6 +366,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
 
+    SWA_TRACE(7);
     // Rows of this wave: segment ids and their range.
     const bool row_vis = row_ok && (!plain || seg_q > 0);  // padding rows see nothing
     const unsigned wlim = window_limit(a.window);
@@ -382,6 +384,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         scan_sink_tiles(pre_row, seg_row, plan.sink_keys, BN, lo, hi, aligned16, sm.sink_bits, tid, nthreads,
                         16 * tid < plan.sink_keys ? &chunk0 : nullptr);
     }
+    SWA_TRACE(8);
     int n_new = 0;  // (no loads beyond tile 0 are in flight here)
     const float c_log2 = a.scale * kLog2e;
     float m_run = kNegInf;  // reference max (raw score units) used for p
