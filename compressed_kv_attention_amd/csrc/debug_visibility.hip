@@ -2,7 +2,8 @@
 // apply it: the workgroup walks the same TileIter over the same TilePlan, and
 // each (row group, key sub-tile) pair is classified with the same functions
 // (swa_tiles.h).  An element is visible iff its tile was enumerated and its
-// pair is FULL, or PARTIAL and the element predicate holds.  A tile that the
+// pair is FULL and the row passes the lane gate, PARTIAL_POS and the row passes
+// the gate and the positional test, or PARTIAL and the element predicate holds.  A tile that the
 // iterator yields twice (which would count its keys twice) marks the rows of
 // the workgroup with count -1.
 #include "swa_common.h"
@@ -113,29 +114,31 @@ __global__ __launch_bounds__(256) void debug_vis_kernel(PrefillArgs a, DbgGeom g
         bool vis = false;
         if (enum_bits[kind][tile >> 5] & (1u << (tile & 31))) {
             const int k0 = (key / kDbgSub) * kDbgSub;
+            const int seg_q = plain ? (seg ? seg[q] : 1) : 1;
+            const bool row_vis = seg_q > 0;
             int cls;
+            unsigned wlim = window_limit(a.window);
+            KeySum ks{0, 0, 0, 0};
             if (pooled) {
                 cls = classify_pooled(rs, k0, kDbgSub, a.window, a.block, a.nblk);
             } else {
-                KeySum ks;
                 const int si = key / kDbgSub;
                 ks.smin = key_sum[si][0];
                 ks.smax = key_sum[si][1];
                 ks.any_sink = key_sum[si][2];
                 ks.all_sink = key_sum[si][3];
-                cls = classify_exact(rs, ks, k0, kDbgSub, T, a.window, plain);
+                cls = classify_exact(rs, ks, k0, kDbgSub, T, a.window, plain, wlim);
             }
-            const int seg_q = plain ? (seg ? seg[q] : 1) : 1;
-            const bool row_vis = seg_q > 0;
-            const unsigned wlim = window_limit(a.window);
-            if (cls == TILE_FULL) {
-                vis = true;
+            if (pooled) {
+                if (cls == TILE_FULL) vis = true;
+                else if (cls != TILE_SKIP) vis = key < pooled_visible_count(q, a.window, a.block, a.nblk);
+            } else if (cls == TILE_FULL) {
+                vis = lane_gate(row_vis, plain, seg_q, ks);
             } else if (cls == TILE_PARTIAL_POS) {
-                vis = row_vis && visible_pos(q - key, wlim);
+                vis = lane_gate(row_vis, plain, seg_q, ks) && visible_pos(q - key, wlim);
             } else if (cls == TILE_PARTIAL) {
-                if (pooled) vis = key < pooled_visible_count(q, a.window, a.block, a.nblk);
-                else vis = row_vis && visible_full(q - key, wlim, pack_key_info(seg ? seg[key] : 1, pre && pre[key] != 0),
-                                                   seg_q);
+                vis = row_vis && visible_full(q - key, wlim, pack_key_info(seg ? seg[key] : 1, pre && pre[key] != 0),
+                                              seg_q);
             }
         }
         if (mask) mask[((size_t)b * T + q) * Tk + col] = vis ? 1 : 0;

@@ -1,5 +1,5 @@
 // pool_rope.hip -- the pre-passes of a prefill: RoPE tables, key rotation,
-// block pooling of the compressed variant and the packed per-key mask info.
+// block pooling of the compressed variant and the per-key mask metadata.
 //
 // [CA] "Compressed attention and the copy probe", section "Pool before
 // rotating, not after": keys are mean-pooled over blocks of b rows BEFORE
@@ -81,17 +81,33 @@ __global__ void pool_rope_kernel(long long N, int T, int D, int block, int nblk,
 }
 
 // Rotate every row t of x [N, T, D] at position t (rotate-half pairs
-// (i, i + D/2)); one thread per 8 channel pairs, 16-byte loads and stores.
-// Used to rotate the keys of a prefill once instead of once per query block
-// that reads them.
-__global__ void rope_rows_bf16_kernel(long long rows, int T, int D, const uint16_t* x, const float* cs,
-                                      const float* sn, uint16_t* y) {
+// (i, i + D/2)); one thread per 4 channel pairs.  The fp32 prefill rotates
+// its keys with this once instead of once per query block that reads them.
+__global__ void rope_rows_f32_kernel(long long rows, int T, int D, const float* x, const float* cs, const float* sn,
+                                     float* y) {
     const int half = D / 2;
-    const int chunks = half / 8;
+    const int chunks = half / 4;
     const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= rows * chunks) return;
     const long long row = idx / chunks;
-    const int i0 = (int)(idx % chunks) * 8;
+    const int i0 = (int)(idx % chunks) * 4;
+    const int t = (int)(row % T);
+    const size_t base = (size_t)row * D;
+    const float4 a = *(const float4*)(x + base + i0);
+    const float4 bb = *(const float4*)(x + base + half + i0);
+    const float4 c = *(const float4*)(cs + (size_t)t * half + i0);
+    const float4 s = *(const float4*)(sn + (size_t)t * half + i0);
+    *(float4*)(y + base + i0) = make_float4(a.x * c.x - bb.x * s.x, a.y * c.y - bb.y * s.y, a.z * c.z - bb.z * s.z,
+                                            a.w * c.w - bb.w * s.w);
+    *(float4*)(y + base + half + i0) = make_float4(bb.x * c.x + a.x * s.x, bb.y * c.y + a.y * s.y,
+                                                   bb.z * c.z + a.z * s.z, bb.w * c.w + a.w * s.w);
+}
+
+// Key rotation of one 8-pair chunk: row `row` of x [rows, D] at position
+// row % T (rotate-half pairs (i, i + D/2)), 16-byte loads and stores.
+__device__ __forceinline__ void rope_chunk_bf16(long long row, int i0, int T, int D, const uint16_t* x,
+                                                const float* cs, const float* sn, uint16_t* y) {
+    const int half = D / 2;
     const int t = (int)(row % T);
     const size_t base = (size_t)row * D;
     const uint4 w1 = *(const uint4*)(x + base + i0);
@@ -117,57 +133,72 @@ __global__ void rope_rows_bf16_kernel(long long rows, int T, int D, const uint16
     *(uint4*)(y + base + half + i0) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
 }
 
-__global__ void rope_rows_f32_kernel(long long rows, int T, int D, const float* x, const float* cs, const float* sn,
-                                     float* y) {
-    const int half = D / 2;
-    const int chunks = half / 4;
-    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= rows * chunks) return;
-    const long long row = idx / chunks;
-    const int i0 = (int)(idx % chunks) * 4;
-    const int t = (int)(row % T);
-    const size_t base = (size_t)row * D;
-    const float4 a = *(const float4*)(x + base + i0);
-    const float4 bb = *(const float4*)(x + base + half + i0);
-    const float4 c = *(const float4*)(cs + (size_t)t * half + i0);
-    const float4 s = *(const float4*)(sn + (size_t)t * half + i0);
-    *(float4*)(y + base + i0) = make_float4(a.x * c.x - bb.x * s.x, a.y * c.y - bb.y * s.y, a.z * c.z - bb.z * s.z,
-                                            a.w * c.w - bb.w * s.w);
-    *(float4*)(y + base + half + i0) = make_float4(bb.x * c.x + a.x * s.x, bb.y * c.y + a.y * s.y,
-                                                   bb.z * c.z + a.z * s.z, bb.w * c.w + a.w * s.w);
-}
-
-// Packed key info of every key of a plain prefill: segment id (negative ids
-// count as 0, padding) with the sink flag in bit 31, one int32 per key, so the
-// attention kernel stages it with 4-byte copies.  [NW section "KV Sinks for
-// Tools: Pinning Critical Context"]: the packing and sink terms of the mask.
-__global__ void key_info_kernel(long long n, const int32_t* seg, const uint8_t* prefix, int32_t* info) {
-    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    info[i] = pack_key_info(seg ? seg[i] : 1, prefix ? prefix[i] != 0 : false);
+// One launch for everything a bf16 prefill prepares before attention:
+//   blocks [0, rope_blocks): rotate the keys (one thread per 8-pair chunk);
+//   the other blocks: key metadata, one wave per key tile of 64 keys --
+//     info[b][t]     packed segment | sink << 31 of every key
+//     ksub[b][2j+h]  KeySum of keys [64j + 32h, 64j + 32h + 32) ∩ [0, T)
+//     tsink[b][j]    (min, max) segment of the tile's sink keys,
+//                    (INT_MAX, INT_MIN) when it holds none
+// [NW section "KV Sinks for Tools: Pinning Critical Context"]: the packing
+// and sink terms of the mask; the summaries let the attention kernel classify
+// sub-tiles and find the tiles holding sinks without reading every key.
+__global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs p) {
+    if ((long long)blockIdx.x < p.rope_blocks) {
+        const int chunks = p.D / 16;
+        const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+        if (idx < p.rope_rows * chunks)
+            rope_chunk_bf16(idx / chunks, (int)(idx % chunks) * 8, p.T, p.D, p.x, p.cs, p.sn, p.y);
+        return;
+    }
+    const long long gt = ((long long)blockIdx.x - p.rope_blocks) * 4 + (threadIdx.x >> 6);
+    if (gt >= (long long)p.B * p.ntile) return;
+    const int lane = threadIdx.x & 63;
+    const int b = (int)(gt / p.ntile), j = (int)(gt % p.ntile);
+    const int t = 64 * j + lane;
+    const bool valid = t < p.T;
+    int info = 0;
+    if (valid) {
+        const size_t i = (size_t)b * p.T + t;
+        info = pack_key_info(p.seg ? p.seg[i] : 1, p.prefix ? p.prefix[i] != 0 : false);
+        p.info[i] = info;
+    }
+    const int sg = info & 0x7fffffff;
+    const bool sk = info < 0;
+    const int half = lane >> 5;
+    const int s_first = half ? __builtin_amdgcn_readlane(sg, 32) : __builtin_amdgcn_readlane(sg, 0);
+    const uint64_t eq_b = __ballot(!valid || sg == s_first);
+    const uint64_t any_b = __ballot(valid && sk);
+    const uint64_t all_b = __ballot(!valid || sk);
+    const int smn = wave_imin_xor(valid && sk ? sg : 0x7fffffff, 1, 32);
+    const int smx = wave_imax_xor(valid && sk ? sg : (int)0x80000000, 1, 32);
+    if ((lane & 31) == 0) {
+        const uint32_t eq_h = (uint32_t)(eq_b >> (32 * half));
+        const uint32_t any_h = (uint32_t)(any_b >> (32 * half));
+        const uint32_t all_h = (uint32_t)(all_b >> (32 * half));
+        const KeySum ks = make_key_sum(eq_h == 0xffffffffu, s_first, any_h != 0u, all_h == 0xffffffffu);
+        *(int4*)(p.ksub + ((size_t)b * 2 * p.ntile + 2 * j + half) * 4) = make_int4(ks.smin, ks.smax, ks.any_sink,
+                                                                                      ks.all_sink);
+    }
+    if (lane == 0) *(int2*)(p.tsink + ((size_t)b * p.ntile + j) * 2) = make_int2(smn, smx);
 }
 
 }  // namespace
 
-hipError_t launch_key_info(long long n, const int32_t* seg, const uint8_t* prefix, int32_t* info, hipStream_t s) {
-    const int threads = 256;
-    hipLaunchKernelGGL(key_info_kernel, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s, n, seg,
-                       prefix, info);
+hipError_t launch_prefill_prep(const PrepArgs& p, hipStream_t s) {
+    const long long meta_blocks = p.info ? ((long long)p.B * p.ntile + 3) / 4 : 0;
+    const long long blocks = p.rope_blocks + meta_blocks;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(prefill_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_rope_rows(long long rows, int T, int D, int dtype, const void* x, const float* cs,
-                            const float* sn, void* y, hipStream_t s) {
+hipError_t launch_rope_rows_f32(long long rows, int T, int D, const float* x, const float* cs, const float* sn,
+                                float* y, hipStream_t s) {
     const int threads = 256;
-    if (dtype == 1) {
-        const long long n = rows * (D / 16);
-        hipLaunchKernelGGL(rope_rows_bf16_kernel, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s,
-                           rows, T, D, (const uint16_t*)x, cs, sn, (uint16_t*)y);
-    } else {
-        const long long n = rows * (D / 8);
-        hipLaunchKernelGGL(rope_rows_f32_kernel, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s,
-                           rows, T, D, (const float*)x, cs, sn, (float*)y);
-    }
+    const long long n = rows * (D / 8);
+    hipLaunchKernelGGL(rope_rows_f32_kernel, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s,
+                       rows, T, D, x, cs, sn, y);
     return hipGetLastError();
 }
 

@@ -75,6 +75,18 @@ __device__ __forceinline__ u32x4 ds_read128(uint32_t addr) {
     asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
     return r;
 }
+// Reads at a base register plus an immediate byte offset (a constant once
+// the surrounding loops are unrolled).
+__device__ __forceinline__ u32x4 ds_read128_at(uint32_t addr, int off) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off));
+    return r;
+}
+__device__ __forceinline__ u32x2 ds_read_tr16_at(uint32_t addr, int off) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off));
+    return r;
+}
 __device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
     u32x2 r;
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
@@ -118,18 +130,18 @@ __device__ __forceinline__ void wait_vm_upto(int n) {  // n = loads that may sta
 
 template <int D>
 struct SmemBf16 {
-    uint16_t k[NBUF][BN * D];  // K tiles, row-major, 16-byte chunks swizzled
-    uint16_t v[NBUF][BN * D];  // V tiles, row-major, 16-byte chunks swizzled
-    int kinfo[NBUF][BN];       // packed segment | sink << 31 of the tile's keys
-    int ksum[NBUF][BN / SUB][4];  // per sub-tile: seg min, seg max, any sink, all sink
+    uint16_t k[NBUF][BN * D];     // K tiles, row-major, 16-byte chunks swizzled
+    uint16_t v[NBUF][BN * D];     // V tiles, row-major, 16-byte chunks swizzled
+    int kinfo[NBUF][BN];          // packed segment | sink << 31 of the tile's keys
+    int ksum[NBUF][BN / SUB][4];  // KeySum of each sub-tile (seg min, seg max, any sink, all sink)
     uint32_t sink_bits[kSinkWords];
-    int red[2];
 };
 
 // Swizzled position (in 16-byte chunks) of chunk c of key row k.  K: rows that
 // share LDS banks get different chunk orders, so the 32 rows one MFMA operand
 // read touches are conflict free.  V: the four rows one transpose read covers
-// per half-wave fall into different bank halves.
+// per half-wave fall into different bank halves.  Both swizzles depend only on
+// the low bits of k, so rows 32 apart differ by a constant offset.
 template <int D>
 __device__ __forceinline__ int k_chunk(int k, int c) {
     constexpr int CPR = D / 8;  // chunks per row
@@ -141,14 +153,17 @@ __device__ __forceinline__ int v_chunk(int k, int c) {
     return k * CPR + (D == 64 ? (c ^ (((k >> 1) & 1) * 4)) : c);
 }
 
+// The wave that stages the sub-tile summaries (wave 0 stages the key info).
+constexpr int kMetaWave = 1 % kMfmaWaves;
+
 // Issue the global->LDS loads of one tile into buffer `buf`: wave w moves
-// 1 KB of K and 1 KB of V (64 lanes x 16 bytes) per instruction; wave 0 also
-// moves the keys' segment ids and sink flags.  Rows past the last key load a
-// clamped row (finite data, masked later).
+// 1 KB of K and 1 KB of V (64 lanes x 16 bytes) per instruction; with key
+// metadata, wave 0 also moves the keys' packed info and kMetaWave the two
+// sub-tile summaries.  Rows past the last key load a clamped row (finite
+// data, masked later).
 template <int D>
-__device__ __forceinline__ int issue_tile(const PrefillArgs& a, SmemBf16<D>& sm, int buf, int kind, int tile, int b,
-                                          int hkv, int wave, int lane) {
-    int issued = 0;
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, SmemBf16<D>& sm, int buf, int kind, int tile, int b,
+                                           int hkv, int wave, int lane) {
     constexpr int CPR = D / 8;
     constexpr int ROWS_PER_LOAD = 64 / CPR;  // key rows per wave instruction
     const bool pooled = kind == COL_POOLED;
@@ -166,52 +181,16 @@ __device__ __forceinline__ int issue_tile(const PrefillArgs& a, SmemBf16<D>& sm,
         const int cv = D == 64 ? (pc ^ (((kr >> 1) & 1) * 4)) : pc;
         __builtin_amdgcn_global_load_lds(kg + (size_t)gk * D + 8 * ck, (lds_void*)&sm.k[buf][ld * 64 * 8], 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vg + (size_t)gk * D + 8 * cv, (lds_void*)&sm.v[buf][ld * 64 * 8], 16, 0, 0);
-        issued += 2;
     }
-    if (wave == 0 && !pooled && a.kinfo) {
-        const int gk = min(k0 + lane, a.T - 1);
-        __builtin_amdgcn_global_load_lds(a.kinfo + (size_t)b * a.T + gk, (lds_void*)&sm.kinfo[buf][0], 4, 0, 0);
-        ++issued;
-    }
-    return issued;
-}
-
-// Wave 0, after its loads of the tile have landed: packed key info and the
-// per-sub-tile summaries (ballots only).
-template <int D>
-__device__ __forceinline__ void summarize_tile(const PrefillArgs& a, SmemBf16<D>& sm, int buf, int kind, int tile,
-                                               int lane) {
-    const bool pooled = kind == COL_POOLED;
-    const int nkeys = pooled ? a.nblk : a.T;
-    const bool valid = tile * BN + lane < nkeys;
-    int info = 0;
-    if (!pooled) {
-        uint32_t ki = (uint32_t)pack_key_info(1, false);
-        if (a.kinfo) {
-            ki = ds_read32(lds_off(&sm.kinfo[buf][lane]));
-            lds_wait();
-            lds_tie(ki);
+    if (!pooled && a.kinfo) {
+        if (wave == 0) {
+            const int gk = min(k0 + lane, a.T - 1);
+            __builtin_amdgcn_global_load_lds(a.kinfo + (size_t)b * a.T + gk, (lds_void*)&sm.kinfo[buf][0], 4, 0, 0);
         }
-        if (valid) info = (int)ki;
-    }
-    ds_write32(lds_off(&sm.kinfo[buf][lane]), (uint32_t)info);
-    const int s = info & 0x7fffffff;
-    const bool sk = info < 0;
-    const int half = lane >> 5;
-    const int s_first = half ? __builtin_amdgcn_readlane(s, 32) : __builtin_amdgcn_readlane(s, 0);
-    const uint64_t eq_b = __ballot(!valid || s == s_first);
-    const uint64_t any_b = __ballot(valid && sk);
-    const uint64_t all_b = __ballot(!valid || sk);
-    if ((lane & 31) == 0) {
-        const uint32_t eq_h = (uint32_t)(eq_b >> (32 * half));
-        const uint32_t any_h = (uint32_t)(any_b >> (32 * half));
-        const uint32_t all_h = (uint32_t)(all_b >> (32 * half));
-        const KeySum ks = make_key_sum(eq_h == 0xffffffffu, s_first, any_h != 0u, all_h == 0xffffffffu);
-        const uint32_t base = lds_off(&sm.ksum[buf][half][0]);
-        ds_write32(base, (uint32_t)ks.smin);
-        ds_write32(base + 4, (uint32_t)ks.smax);
-        ds_write32(base + 8, (uint32_t)ks.any_sink);
-        ds_write32(base + 12, (uint32_t)ks.all_sink);
+        if (wave == kMetaWave && lane < 2 * 4) {
+            const int32_t* src = a.ksub + ((size_t)b * 2 * a.ntile + 2 * tile) * 4 + lane;
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)&sm.ksum[buf][0][0], 4, 0, 0);
+        }
     }
 }
 
@@ -264,21 +243,36 @@ typedef __attribute__((address_space(3))) short4_t lds_short4;
 // V^T operand of O^T += V^T P^T for keys [kb, kb + 16) of a tile
 // sub-tile and channels [32n, 32n + 32): lane (channel d = l % 32, half h)
 // needs the 8 keys 16m + 4h + {0..3} and 16m + 8 + 4h + {0..3} of channel d.
-// Two transpose reads: within each 16-lane group, source lane j = 4r + a
-// points at key K_r, channels base + 4a .. +3; output lane 4a' + b' then holds
-// channel base + lane%16 of keys K_0..K_3.
+// Two transpose reads (hi = 0, 1): within each 16-lane group, source lane
+// j = 4r + a points at key K_r, channels base + 4a .. +3; output lane 4a' + b'
+// then holds channel base + lane%16 of keys K_0..K_3.  This is the lane's byte
+// offset for kb = 0; keys kb (a multiple of 16) sit kb * D * 2 bytes further.
 template <int D>
-__device__ __forceinline__ void issue_vt(uint32_t vbase, int kb, int n, int lane, u32x2& lo, u32x2& hi) {
-    const int g = lane >> 4;          // 16-lane group
-    const int h = g >> 1;             // keys half
+__device__ __forceinline__ uint32_t vt_lane_off(int n, int hi, int lane) {
+    const int g = lane >> 4;  // 16-lane group
+    const int h = g >> 1;     // keys half
     const int j = lane & 15;
     const int r = j >> 2, a4 = j & 3;
     const int ch = 32 * n + 16 * (g & 1) + 4 * a4;  // first channel this source lane points at
     const int c = ch >> 3, half = (ch >> 2) & 1;
-    const int k_lo = kb + 4 * h + r;
-    const int k_hi = kb + 8 + 4 * h + r;
-    lo = ds_read_tr16(vbase + (uint32_t)(v_chunk<D>(k_lo, c) * 16 + 8 * half));
-    hi = ds_read_tr16(vbase + (uint32_t)(v_chunk<D>(k_hi, c) * 16 + 8 * half));
+    return (uint32_t)(v_chunk<D>(8 * hi + 4 * h + r, c) * 16 + 8 * half);
+}
+// K operand of S^T = K Q^T, chunk c (channels 16c + 8h .. +7) of key lq of a
+// sub-tile at keys [0, 32); sub-tile st sits st * SUB * D * 2 bytes further.
+template <int D>
+__device__ __forceinline__ uint32_t k_lane_off(int c, int lane) {
+    return (uint32_t)(k_chunk<D>(lane & 31, 2 * c + (lane >> 5)) * 16);
+}
+
+__device__ __forceinline__ float max3f(float x, float y, float z) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+    return r;
+}
+__device__ __forceinline__ float max2f(float x, float y) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+    return r;
 }
 
 template <int D, bool ROPE, bool COMPRESSED>
@@ -317,9 +311,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const bool row_ok = my_q < T;
     constexpr bool plain = !COMPRESSED;
 
-    // Tile plan.  The band comes first in the walk, so the first tiles' loads
-    // start before the sink scan; every global load of the prologue is issued
-    // before any of them is waited for.
+    // Tile plan.  The band comes first in the walk, so the first tile's loads
+    // start at once; every global load of the prologue is issued before any of
+    // them is waited for.
     const TilePlan plan = plan_tiles(q0, q1, a.window, a.block, a.nblk, a.prefix != nullptr, BN);
     TileIter it;
     it.init(plan, sm.sink_bits, BN);
@@ -350,12 +344,19 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     }
     int seg_q = 0;
     if (row_ok) seg_q = a.seg ? a.seg[(size_t)b * T + my_q] : 1;
-    const int32_t* seg_row = a.seg ? a.seg + (size_t)b * T : nullptr;
-    const uint8_t* pre_row = a.prefix ? a.prefix + (size_t)b * T : nullptr;
-    const bool aligned16 = (T & 15) == 0;
-    SinkChunk chunk0;
-    const bool scan = plan.sink_keys > 0;
-    if (scan && 16 * tid < plan.sink_keys) sink_chunk_load(pre_row, seg_row, 16 * tid, aligned16, chunk0);
+    // Sink tiles before the band: tiles whose sinks belong to a segment of the
+    // workgroup's rows (the prep pass gives each tile's sink segment range).
+    // Every wave loads the rows' segment ids (at most 128 rows) itself.
+    const int n_sink_tiles = plan.sink_keys / BN;
+    const bool scan = n_sink_tiles > 0;
+    int rseg0 = 0x7fffffff, rseg1 = 0x7fffffff;
+    int2 tsk = make_int2(0x7fffffff, (int)0x80000000);
+    if (scan) {
+        const int32_t* seg_row = a.seg ? a.seg + (size_t)b * T : nullptr;
+        if (q0 + lane <= q1) rseg0 = seg_row ? seg_row[q0 + lane] : 1;
+        if (q0 + 64 + lane <= q1) rseg1 = seg_row ? seg_row[q0 + 64 + lane] : 1;
+        if (lane < n_sink_tiles) tsk = *(const int2*)(a.tsink + ((size_t)b * a.ntile + lane) * 2);
+    }
 
     // Q^T operand: lane holds row my_q, channels 16c + 8h .. +7 for each c.
     bf16x8 qf[D / 16];
@@ -367,7 +368,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     for (int c = 0; c < D / 16; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
 
     SWA_TRACE(7);
-    // Rows of this wave: segment ids and their range.
     const bool row_vis = row_ok && (!plain || seg_q > 0);  // padding rows see nothing
     const unsigned wlim = window_limit(a.window);
     RowSum rs;
@@ -377,15 +377,23 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     rs.smax = __builtin_amdgcn_readfirstlane(wave_imax_xor(row_ok ? seg_q : (int)0x80000000, 1, 16));
     const int pooled_n = (COMPRESSED && row_ok) ? pooled_visible_count(my_q, a.window, a.block, a.nblk) : 0;
 
-    // Sink tiles before the band (only sinks of this workgroup's segments).
     if (scan) {
-        int lo = 1, hi = 1;
-        if (seg_row) row_segment_range_from_lanes(seg_q, row_ok && wave_active, sm.red, tid, lo, hi);
-        scan_sink_tiles(pre_row, seg_row, plan.sink_keys, BN, lo, hi, aligned16, sm.sink_bits, tid, nthreads,
-                        16 * tid < plan.sink_keys ? &chunk0 : nullptr);
+        const int lo = max(1, wave_imin_xor(min(rseg0, rseg1), 1, 32));
+        const int hi = wave_imax_xor(max(rseg0 == 0x7fffffff ? (int)0x80000000 : rseg0,
+                                         rseg1 == 0x7fffffff ? (int)0x80000000 : rseg1), 1, 32);
+        for (int t0 = 0; t0 < n_sink_tiles; t0 += 64) {
+            if (t0 > 0) {
+                tsk = make_int2(0x7fffffff, (int)0x80000000);
+                if (t0 + lane < n_sink_tiles) tsk = *(const int2*)(a.tsink + ((size_t)b * a.ntile + t0 + lane) * 2);
+            }
+            const uint64_t hit = __ballot(tsk.x <= hi && tsk.y >= lo);
+            if (wave == 0 && lane == 0) {
+                sm.sink_bits[t0 / 32] = (uint32_t)hit;
+                if (t0 / 32 + 1 < kSinkWords) sm.sink_bits[t0 / 32 + 1] = (uint32_t)(hit >> 32);
+            }
+        }
     }
     SWA_TRACE(8);
-    int n_new = 0;  // (no loads beyond tile 0 are in flight here)
     const float c_log2 = a.scale * kLog2e;
     float m_run = kNegInf;  // reference max (raw score units) used for p
     float l_run = 0.f;
@@ -397,14 +405,24 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 
     // tile 0 must have landed
     wait_vm_upto(0);
-    if (wave == 0 && have0) summarize_tile<D>(a, sm, 0, kc, tc, lane);
-    wait_vm_upto(0);
     barrier_raw();
     SWA_TRACE(0);
 
-    const uint32_t k_lds = lds_off(&sm.k[0][0]), v_lds = lds_off(&sm.v[0][0]);
-    const uint32_t info_lds = lds_off(&sm.kinfo[0][0]), sum_lds = lds_off(&sm.ksum[0][0][0]);
+    // LDS addresses of the operand reads in the buffer being computed; they
+    // move by +-kTileBytes from one tile to the next.
     constexpr uint32_t kTileBytes = BN * D * 2;
+    uint32_t k_addr[D / 16], v_addr[D / 32][2];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) k_addr[c] = lds_off(&sm.k[0][0]) + k_lane_off<D>(c, lane);
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+        v_addr[n][0] = lds_off(&sm.v[0][0]) + vt_lane_off<D>(n, 0, lane);
+        v_addr[n][1] = lds_off(&sm.v[0][0]) + vt_lane_off<D>(n, 1, lane);
+    }
+    int buf_step = (int)kTileBytes;
+    const uint32_t info_lds = lds_off(&sm.kinfo[0][0]), sum_lds = lds_off(&sm.ksum[0][0][0]);
+    // summaries of exact sub-tiles without key metadata: one segment, no sinks
+    const bool have_meta = a.kinfo != nullptr;
     int cur = 0;
     bool have = have0;
     while (have) {
@@ -412,17 +430,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         const int nxt = cur ^ 1;
         int kn = 0, tn = 0;
         const bool have_next = it.next(kn, tn);
-        n_new = 0;
-        if (have_next) n_new = issue_tile<D>(a, sm, nxt, kn, tn, b, hkv, wave, lane);
+        if (have_next) issue_tile<D>(a, sm, nxt, kn, tn, b, hkv, wave, lane);
         SWA_TRACE(1);
 
         if (wave_active) {
             const bool pooled = COMPRESSED && kc == COL_POOLED;
             const int nkeys = pooled ? a.nblk : T;
-            const uint32_t kbuf = k_lds + cur * kTileBytes, vbuf = v_lds + cur * kTileBytes;
-            // sub-tile summaries, moved to scalar registers at once
             KeySum ksub[BN / SUB];
-            if (!pooled) {
+#pragma unroll
+            for (int st = 0; st < BN / SUB; ++st) ksub[st] = make_key_sum(true, 1, false, false);
+            if (!pooled && have_meta) {
                 u32x4 kv[BN / SUB];
 #pragma unroll
                 for (int st = 0; st < BN / SUB; ++st) kv[st] = ds_read128(sum_lds + (cur * (BN / SUB) + st) * 16);
@@ -440,41 +457,45 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
             for (int st = 0; st < BN / SUB; ++st) {
                 const int k0 = tc * BN + st * SUB;
                 int cls;
+                unsigned wl = wlim;
                 if (pooled) {
                     cls = classify_pooled(rs, k0, SUB, a.window, a.block, a.nblk);
                 } else {
-                    cls = classify_exact(rs, ksub[st], k0, SUB, nkeys, a.window, plain);
+                    cls = classify_exact(rs, ksub[st], k0, SUB, nkeys, a.window, plain, wl);
                 }
                 cls = __builtin_amdgcn_readfirstlane(cls);
+                wl = __builtin_amdgcn_readfirstlane(wl);
                 if (cls == TILE_SKIP) continue;
+                // Rows outside the sub-tile's segment (and padding rows) take no
+                // weight from it: their max ignores it and their exponent base
+                // is +inf, so every weight is exactly 0.
+                const bool gate =
+                    (pooled || cls == TILE_PARTIAL) ? row_vis : lane_gate(row_vis, plain, seg_q, ksub[st]);
 
                 u32x4 kr[D / 16];
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) kr[c] = ds_read128(kbuf + k_chunk<D>(st * SUB + lq, 2 * c + h) * 16);
+                for (int c = 0; c < D / 16; ++c) kr[c] = ds_read128_at(k_addr[c], st * SUB * D * 2);
                 lds_wait();
-                f32x16 s = f32x16{};
+                f32x16 sacc = f32x16{};
 #pragma unroll
                 for (int c = 0; c < D / 16; ++c) {
                     lds_tie(kr[c]);
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], s, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc, 0, 0,
+                                                                   0);
                 }
-                // Scores leave the accumulator into plain registers; the mask is
-                // applied with selects (no divergent writes into the MFMA result).
                 // Element j holds key k0 + off(j) + 4h with off(j) = 8(j/4) + j%4.
-                float sv[16];
+                // Masks are selects on the accumulator registers themselves.
+                const int kb = k0 + 4 * h;  // key of element 0
+                if (cls == TILE_PARTIAL_POS) {
+                    const int d0 = my_q - kb;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) sv[j] = s[j];
-                if (cls != TILE_FULL) {
-                    const int kb = k0 + 4 * h;  // key of element 0
+                    for (int j = 0; j < 16; ++j)
+                        sacc[j] = visible_pos(d0 - (8 * (j >> 2) + (j & 3)), wl) ? sacc[j] : kNegInf;
+                } else if (cls == TILE_PARTIAL) {
                     if (pooled) {
                         const int lim = row_vis ? pooled_n - kb : -1;
 #pragma unroll
-                        for (int j = 0; j < 16; ++j) sv[j] = (8 * (j >> 2) + (j & 3)) < lim ? sv[j] : kNegInf;
-                    } else if (cls == TILE_PARTIAL_POS) {
-                        const int d0 = row_vis ? my_q - kb : -0x40000000;  // q - key of element 0
-#pragma unroll
-                        for (int j = 0; j < 16; ++j)
-                            sv[j] = visible_pos(d0 - (8 * (j >> 2) + (j & 3)), wlim) ? sv[j] : kNegInf;
+                        for (int j = 0; j < 16; ++j) sacc[j] = (8 * (j >> 2) + (j & 3)) < lim ? sacc[j] : kNegInf;
                     } else {
                         const int d0 = my_q - kb;
                         u32x4 inf[4];
@@ -489,22 +510,24 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                             for (int r = 0; r < 4; ++r) {
                                 const bool vis =
                                     row_vis & visible_full(d0 - (8 * g4 + r), wlim, (int)inf[g4][r], seg_q);
-                                sv[4 * g4 + r] = vis ? sv[4 * g4 + r] : kNegInf;
+                                sacc[4 * g4 + r] = vis ? sacc[4 * g4 + r] : kNegInf;
                             }
                         }
                     }
-                } else if (!row_vis) {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) sv[j] = kNegInf;
                 }
-                float mx = sv[0];
+                float sv[16];
 #pragma unroll
-                for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, sv[j]);
+                for (int j = 0; j < 16; ++j) sv[j] = sacc[j];
+                float mx = max3f(sv[0], sv[1], sv[2]);
+#pragma unroll
+                for (int j = 3; j < 15; j += 2) mx = max3f(mx, sv[j], sv[j + 1]);
+                mx = max2f(mx, sv[15]);
                 {
                     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false,
                                                                      false);
-                    mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                    mx = max2f(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
                 }
+                mx = gate ? mx : kNegInf;
                 // Rescale only when some row of the wave outgrows its reference
                 // max by more than 2^8 (the first visible tile always does).
                 const bool grow = (mx - m_run) * c_log2 > kRescaleLog2;
@@ -519,8 +542,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 // V^T operands of the first 16 keys, in flight while the weights are made
                 u32x2 vlo[D / 32], vhi[D / 32];
 #pragma unroll
-                for (int n = 0; n < D / 32; ++n) issue_vt<D>(vbuf, st * SUB, n, lane, vlo[n], vhi[n]);
-                const float base = (m_run == kNegInf) ? 0.f : m_run * c_log2;
+                for (int n = 0; n < D / 32; ++n) {
+                    vlo[n] = ds_read_tr16_at(v_addr[n][0], st * SUB * D * 2);
+                    vhi[n] = ds_read_tr16_at(v_addr[n][1], st * SUB * D * 2);
+                }
+                const float base = gate ? ((m_run == kNegInf) ? 0.f : m_run * c_log2) : __builtin_inff();
                 uint32_t pw[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
@@ -544,7 +570,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                     }
                     if (m == 0) {  // the next 16 keys load during this product
 #pragma unroll
-                        for (int n = 0; n < D / 32; ++n) issue_vt<D>(vbuf, st * SUB + 16, n, lane, vlo[n], vhi[n]);
+                        for (int n = 0; n < D / 32; ++n) {
+                            vlo[n] = ds_read_tr16_at(v_addr[n][0], (st * SUB + 16) * D * 2);
+                            vhi[n] = ds_read_tr16_at(v_addr[n][1], (st * SUB + 16) * D * 2);
+                        }
                     }
                     const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * m], pw[4 * m + 1], pw[4 * m + 2],
                                                                             pw[4 * m + 3]));
@@ -559,11 +588,17 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 
         // tile `nxt` must have landed before the barrier
         wait_vm_upto(0);
-        if (wave == 0 && have_next) summarize_tile<D>(a, sm, nxt, kn, tn, lane);
         SWA_TRACE(3);
-        wait_vm_upto(0);
         barrier_raw();
         SWA_TRACE(4);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) k_addr[c] += buf_step;
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) {
+            v_addr[n][0] += buf_step;
+            v_addr[n][1] += buf_step;
+        }
+        buf_step = -buf_step;
         cur = nxt;
         kc = kn;
         tc = tn;

@@ -135,6 +135,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
         }
         __syncthreads();
         int cls;
+        unsigned wl = wlim;
+        bool gate = row_vis;
         if (pooled) {
             cls = classify_pooled(rs, k0, BNF, a.window, a.block, a.nblk);
         } else {
@@ -143,7 +145,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
             ks.smax = sm.ksum[1];
             ks.any_sink = sm.ksum[2];
             ks.all_sink = sm.ksum[3];
-            cls = classify_exact(rs, ks, k0, BNF, nkeys, a.window, plain);
+            cls = classify_exact(rs, ks, k0, BNF, nkeys, a.window, plain, wl);
+            gate = lane_gate(row_vis, plain, seg_q, ks);
         }
         if (cls == TILE_SKIP) continue;
         const int pooled_n = (pooled && row_ok) ? pooled_visible_count(my_q, a.window, a.block, a.nblk) : 0;
@@ -151,9 +154,11 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 #pragma unroll 1
         for (int j = 0; j < BNF; ++j) {
             const int gk = k0 + j;
-            bool vis = row_vis;
-            if (cls == TILE_PARTIAL_POS) vis &= visible_pos(my_q - gk, wlim);
-            else if (cls == TILE_PARTIAL) vis &= pooled ? (gk < pooled_n) : visible_full(my_q - gk, wlim, sm.kinfo[j], seg_q);
+            bool vis;
+            if (pooled) vis = row_vis && (cls == TILE_FULL || gk < pooled_n);
+            else if (cls == TILE_FULL) vis = gate;
+            else if (cls == TILE_PARTIAL_POS) vis = gate && visible_pos(my_q - gk, wl);
+            else vis = row_vis && visible_full(my_q - gk, wlim, sm.kinfo[j], seg_q);
             if (!vis) continue;
             float dot = 0.f;
 #pragma unroll

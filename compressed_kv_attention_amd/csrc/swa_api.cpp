@@ -92,18 +92,31 @@ int check_prefill(const swa_prefill_params* p, const int32_t* seg_ids, const uin
     a.seg = seg_ids;
     a.prefix = prefix;
     a.kinfo = nullptr;
+    a.ksub = nullptr;
+    a.tsink = nullptr;
+    a.ntile = (p->T + 63) / 64;
     const swa::MfmaGeom g = swa::mfma_geometry(p->Hq / p->Hkv);
     a.hpw = g.hpw;
     a.rbs = g.rbs;
     return SWA_OK;
 }
 
-// Workspace layout of a prefill: [packed key info, bf16 plain mode only]
-// [rotated keys, with RoPE only]; each part starts 256-byte aligned.
+// Workspace layout of a prefill: [key metadata, bf16 plain mode only:
+// packed key info, sub-tile summaries, tile sink ranges] [rotated keys, with
+// RoPE only]; each part starts 256-byte aligned.
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-size_t key_info_bytes(const swa_prefill_params* p) {
-    if (p->dtype != SWA_BF16 || p->compress_block != 0) return 0;
-    return round256((size_t)p->B * p->T * sizeof(int32_t));
+struct MetaLayout {
+    size_t info, ksub, tsink, total;  // byte offsets and size
+};
+MetaLayout key_meta_layout(const swa_prefill_params* p) {
+    MetaLayout m{0, 0, 0, 0};
+    if (p->dtype != SWA_BF16 || p->compress_block != 0) return m;
+    const size_t ntile = ((size_t)p->T + 63) / 64;
+    m.info = 0;
+    m.ksub = round256((size_t)p->B * p->T * sizeof(int32_t));
+    m.tsink = m.ksub + round256((size_t)p->B * 2 * ntile * 4 * sizeof(int32_t));
+    m.total = m.tsink + round256((size_t)p->B * ntile * 2 * sizeof(int32_t));
+    return m;
 }
 size_t rotated_key_bytes(const swa_prefill_params* p) {
     if (p->rope_len <= 0) return 0;
@@ -121,7 +134,7 @@ int swa_version(void) { return 100; }
 
 size_t swa_prefill_workspace_size(const swa_prefill_params* p) {
     if (p == nullptr || p->B <= 0 || p->T <= 0 || p->Hkv <= 0 || p->D <= 0) return 0;
-    return key_info_bytes(p) + rotated_key_bytes(p);
+    return key_meta_layout(p).total + rotated_key_bytes(p);
 }
 
 int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, const void* v, const void* pooled_k,
@@ -160,23 +173,42 @@ int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, 
     a.rope_sin = p->rope_len > 0 ? rope_sin : nullptr;
     a.out = out;
     a.lse = lse;
-    a.kinfo = nullptr;
     const hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
-    const size_t info_bytes = key_info_bytes(p);
-    if (info_bytes > 0 && (a.seg || a.prefix)) {  // pack segment ids and sink flags once
-        int32_t* info = (int32_t*)ws;
-        const hipError_t e = swa::launch_key_info((long long)p->B * p->T, a.seg, a.prefix, info, s);
-        if (e != hipSuccess) return hip_status(e, "swa_attn_prefill key info launch");
-        a.kinfo = info;
-    }
-    if (p->rope_len > 0) {  // rotate the exact keys once, into the workspace
-        void* kr = ws + info_bytes;
-        const hipError_t e = swa::launch_rope_rows((long long)p->B * p->Hkv * p->T, p->T, p->D, p->dtype, k, rope_cos,
-                                                   rope_sin, kr, s);
+    const MetaLayout meta = key_meta_layout(p);
+    void* kr = p->rope_len > 0 ? ws + meta.total : nullptr;  // rotated keys
+    if (p->dtype == SWA_BF16) {
+        swa::PrepArgs pa{};
+        pa.B = p->B;
+        pa.T = p->T;
+        pa.D = p->D;
+        pa.ntile = a.ntile;
+        if (kr) {  // rotate the exact keys once, into the workspace
+            pa.rope_rows = (long long)p->B * p->Hkv * p->T;
+            pa.rope_blocks = (pa.rope_rows * (p->D / 16) + 255) / 256;
+            pa.x = (const uint16_t*)k;
+            pa.cs = rope_cos;
+            pa.sn = rope_sin;
+            pa.y = (uint16_t*)kr;
+        }
+        if (meta.total > 0 && (a.seg || a.prefix)) {  // key metadata once per prefill
+            pa.seg = a.seg;
+            pa.prefix = a.prefix;
+            pa.info = (int32_t*)(ws + meta.info);
+            pa.ksub = (int32_t*)(ws + meta.ksub);
+            pa.tsink = (int32_t*)(ws + meta.tsink);
+            a.kinfo = pa.info;
+            a.ksub = pa.ksub;
+            a.tsink = pa.tsink;
+        }
+        const hipError_t e = swa::launch_prefill_prep(pa, s);
+        if (e != hipSuccess) return hip_status(e, "swa_attn_prefill prep launch");
+    } else if (kr) {
+        const hipError_t e = swa::launch_rope_rows_f32((long long)p->B * p->Hkv * p->T, p->T, p->D, (const float*)k,
+                                                       rope_cos, rope_sin, (float*)kr, s);
         if (e != hipSuccess) return hip_status(e, "swa_attn_prefill key rotation launch");
-        a.k = kr;
     }
+    if (kr) a.k = kr;
     const hipError_t e = p->dtype == SWA_BF16 ? swa::launch_prefill_bf16(a, s) : swa::launch_prefill_f32(a, s);
     return hip_status(e, "swa_attn_prefill launch");
 }

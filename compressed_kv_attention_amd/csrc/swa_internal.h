@@ -16,7 +16,12 @@ struct PrefillArgs {
     const void* pv;
     const int32_t* seg;
     const uint8_t* prefix;
-    const int32_t* kinfo;  // [B,T] packed key info (segment | sink << 31), or NULL
+    // key metadata of a bf16 plain prefill with segment ids or sink flags
+    // (all NULL otherwise), written by the prep pass:
+    const int32_t* kinfo;  // [B][T] packed key info (segment | sink << 31)
+    const int32_t* ksub;   // [B][2 * ntile][4] KeySum of each 32-key sub-tile
+    const int32_t* tsink;  // [B][ntile][2] segment range of each 64-key tile's sinks
+    int ntile;             // ceil(T / 64)
     const float* rope_cos;
     const float* rope_sin;
     void* out;
@@ -56,9 +61,25 @@ hipError_t launch_rope_table(double theta, int rope_len, int D, float* c, float*
 hipError_t launch_pool_rope(int B, int H, int T, int D, int block, int dtype, const void* k_pre,
                             const void* v, const float* c, const float* sn, int rope_len, void* pk,
                             void* pv, hipStream_t s);
-hipError_t launch_key_info(long long n, const int32_t* seg, const uint8_t* prefix, int32_t* info, hipStream_t s);
-hipError_t launch_rope_rows(long long rows, int T, int D, int dtype, const void* x, const float* cs,
-                            const float* sn, void* y, hipStream_t s);
+// Arguments of the bf16 prep pass (key rotation and key metadata in one
+// launch); either part may be empty (rope_blocks == 0, or info == NULL).
+struct PrepArgs {
+    long long rope_blocks;  // ceil(rope_rows * D / 16 / 256)
+    long long rope_rows;    // B * Hkv * T
+    int B, T, D, ntile;
+    const uint16_t* x;  // keys to rotate [rope_rows, D]
+    const float* cs;
+    const float* sn;
+    uint16_t* y;  // rotated keys
+    const int32_t* seg;
+    const uint8_t* prefix;
+    int32_t* info;  // [B][T]
+    int32_t* ksub;  // [B][2 * ntile][4]
+    int32_t* tsink; // [B][ntile][2]
+};
+hipError_t launch_prefill_prep(const PrepArgs& p, hipStream_t s);
+hipError_t launch_rope_rows_f32(long long rows, int T, int D, const float* x, const float* cs, const float* sn,
+                                float* y, hipStream_t s);
 hipError_t launch_kv_quantize(long long N, int D, const void* x, int8_t* xq, float* xs, hipStream_t s);
 
 struct DecodeArgs {

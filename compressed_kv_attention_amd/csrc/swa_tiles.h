@@ -16,9 +16,12 @@
 
 namespace swa {
 
-// Sub-tile classes.  PARTIAL_POS: only the causal/window test can fail (one
-// segment shared by every row and key, no sink that matters), so the element
-// predicate is the single unsigned compare (unsigned)(q - k) < wlim.
+// Sub-tile classes.  In FULL and PARTIAL_POS sub-tiles of plain mode every
+// valid key lies in one segment (KeySum::smin); a row sees keys of the
+// sub-tile only if it belongs to that segment, which the kernels test once
+// per row ("lane gate") instead of once per element.  FULL: a row that passes
+// the gate sees every key.  PARTIAL_POS: it sees key k iff the positional test
+// (unsigned)(q - k) < wlim holds, with the bound classify_exact returns.
 // PARTIAL: the full packing & causal & (recent | sink) predicate per element.
 enum : int { TILE_SKIP = 0, TILE_FULL = 1, TILE_PARTIAL_POS = 2, TILE_PARTIAL = 3 };
 enum : int { COL_EXACT = 0, COL_POOLED = 1 };
@@ -83,33 +86,41 @@ __device__ __forceinline__ KeySum make_key_sum(bool uniform, int seg, bool any_s
 
 // Classify a (row group, key sub-tile [k0, k0 + sub)) pair of plain mode, or
 // of the exact columns of compressed mode (plain == false: no segments, no
-// sinks).  FULL means every (row, key) pair is visible; SKIP means none is.
-// A sub-tile that runs past the last key is never FULL.
-__device__ __forceinline__ int classify_exact(const RowSum& r, const KeySum& ks, int k0, int sub,
-                                              int nkeys, int window, bool plain) {
+// sinks).  SKIP: no pair is visible.  For FULL and PARTIAL_POS, wlim_eff is
+// the bound of the positional test: the window limit, or no window when every
+// key of the sub-tile is a sink (a sink stays visible to its segment however
+// far back it lies) or when the window cannot cut any causal pair.  A sub-tile
+// that runs past the last key is never FULL.
+__device__ __forceinline__ int classify_exact(const RowSum& r, const KeySum& ks, int k0, int sub, int nkeys,
+                                              int window, bool plain, unsigned& wlim_eff) {
+    wlim_eff = window_limit(window);
     if (k0 >= nkeys || r.r1 < r.r0) return TILE_SKIP;
+    if (k0 > r.r1) return TILE_SKIP;  // every key lies after every row
     const int k_last = min(k0 + sub - 1, nkeys - 1);
     const bool complete = (k0 + sub) <= nkeys;
-    // causal
-    if (k0 > r.r1) return TILE_SKIP;
     const bool causal_full = k_last <= r.r0;
-    // window (and sinks in plain mode)
-    bool win_full = true;
-    const bool sinks_matter = plain && window != 0 && ks.any_sink;
-    if (window != 0) {
-        const bool all_sink = plain && ks.all_sink;
-        if (r.r0 - k_last >= window && !sinks_matter) return TILE_SKIP;
-        win_full = (r.r1 - k0 < window) || all_sink;
-    }
-    // packing
-    bool seg_full = true;
+    const bool sinks = plain && ks.any_sink;
+    // every pair lies at distance >= window and no key is a sink
+    if (window != 0 && r.r0 - k_last >= window && !sinks) return TILE_SKIP;
     if (plain) {
         const int rlo = max(1, r.smin);
         if (r.smax <= 0 || ks.smax < rlo || ks.smin > r.smax) return TILE_SKIP;
-        seg_full = (r.smin == r.smax) && (ks.smin == ks.smax) && (ks.smin == r.smin) && (r.smin > 0);
+        if (ks.smin != ks.smax) return TILE_PARTIAL;  // keys of several segments
     }
-    if (causal_full && win_full && seg_full && complete) return TILE_FULL;
-    return (seg_full && !sinks_matter) ? TILE_PARTIAL_POS : TILE_PARTIAL;
+    // every causal pair lies inside the window
+    const bool in_window = window == 0 || r.r1 - k0 < window;
+    if (!in_window && sinks) {
+        if (!ks.all_sink) return TILE_PARTIAL;  // sinks and non-sinks at the window edge
+        wlim_eff = 0x7fffffffu;                 // all sinks: the causal test alone
+    }
+    const bool pos_full = causal_full && complete && (in_window || wlim_eff == 0x7fffffffu);
+    return pos_full ? TILE_FULL : TILE_PARTIAL_POS;
+}
+
+// Lane gate of FULL and PARTIAL_POS sub-tiles for a row of segment seg_q that
+// is visible at all (row_vis): plain mode needs the keys' segment.
+__device__ __forceinline__ bool lane_gate(bool row_vis, bool plain, int seg_q, const KeySum& ks) {
+    return row_vis && (!plain || seg_q == ks.smin);
 }
 
 // Classify pooled columns [j0, j0 + sub) for rows r0..r1.  Partial pooled

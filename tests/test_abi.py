@@ -83,11 +83,13 @@ def test_prefill_rejects_null_and_misaligned_pointers():
     assert rc == swa.SWA_ERR_INVALID and "workspace" in msg
     size = lambda p: swa.lib().swa_prefill_workspace_size(ctypes.byref(p))
     need = size(_p(rope_len=64))
-    assert need == 256 + 1 * 2 * 64 * 64 * 2          # packed key info (B*T int32, 256-rounded) + rotated keys
+    # key metadata (B*T packed key info, 2 sub-tile summaries and 1 sink range per
+    # 64-key tile; each part 256-rounded) + rotated keys
+    assert need == 3 * 256 + 1 * 2 * 64 * 64 * 2
     rc, msg = _prefill(_p(rope_len=64), ptrs=FAKE, cos=FAKE, sin=FAKE, ws=FAKE, ws_bytes=need - 1)
     assert rc == swa.SWA_ERR_INVALID and "too small" in msg
-    assert size(_p()) == 256                                   # bf16 plain: key info only
-    assert size(_p(T=65)) == 512
+    assert size(_p()) == 3 * 256                               # bf16 plain: key metadata only
+    assert size(_p(T=65)) == 512 + 256 + 256
     assert size(_p(dtype=swa.SWA_F32)) == 0                    # the fp32 kernel reads seg/prefix itself
     assert size(_p(compress_block=4)) == 0                     # no segments in compressed mode
     assert size(_p(compress_block=4, rope_len=64)) == 1 * 2 * 64 * 64 * 2
