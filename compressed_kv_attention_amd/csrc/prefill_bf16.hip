@@ -288,24 +288,24 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const int lq = lane & 31;
 
     const int T = a.T;
-    const int G = a.Hq / a.Hkv;
-    const int groups = G / a.hpw;
+    const int G = (int)a.div_groups.d * a.hpw;  // GQA group size
     const int wg_rows = 32 * a.rbs;
-    const int nqb = (T + wg_rows - 1) / wg_rows;
     // XCD-aware numbering: dispatch sends workgroup i to XCD i % 8; give each
     // XCD a contiguous range of logical blocks (query block fastest).
     const int nblocks = gridDim.x;
     int lb = blockIdx.x;
     if ((nblocks & 7) == 0) lb = (blockIdx.x & 7) * (nblocks >> 3) + (blockIdx.x >> 3);
-    const int qb = lb % nqb;
-    const int hg = (lb / nqb) % (a.Hkv * groups);
-    const int b = lb / (nqb * a.Hkv * groups);
-    const int hkv = hg / groups;
-    const int hsub = hg % groups;
+    const int bh = (int)fdiv((uint32_t)lb, a.div_nqb);  // batch row * head groups + head group
+    const int qb = lb - bh * (int)a.div_nqb.d;
+    const int b = (int)fdiv((uint32_t)bh, a.div_hg);
+    const int hg = bh - b * (int)a.div_hg.d;
+    const int hkv = (int)fdiv((uint32_t)hg, a.div_groups);
+    const int hsub = hg - hkv * (int)a.div_groups.d;
     const int q0 = qb * wg_rows;
     const int q1 = min(q0 + wg_rows - 1, T - 1);
-    const int my_h = hkv * G + hsub * a.hpw + (wave % a.hpw);
-    const int r0 = q0 + 32 * (wave / a.hpw);
+    const int wrb = (int)fdiv((uint32_t)wave, a.div_hpw);  // row block of this wave
+    const int my_h = hkv * G + hsub * a.hpw + (wave - wrb * a.hpw);
+    const int r0 = q0 + 32 * wrb;
     const bool wave_active = wave < a.hpw * a.rbs && r0 < T;
     const int my_q = r0 + lq;
     const bool row_ok = my_q < T;
@@ -319,6 +319,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     it.init(plan, sm.sink_bits, BN);
     int kc = 0, tc = 0;  // tile being computed
     const bool have0 = it.next(kc, tc);
+    SWA_TRACE(11);
     if (have0) issue_tile<D>(a, sm, 0, kc, tc, b, hkv, wave, lane);
     SWA_TRACE(6);
 
@@ -373,14 +374,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     RowSum rs;
     rs.r0 = r0;
     rs.r1 = min(r0 + 31, T - 1);
-    rs.smin = __builtin_amdgcn_readfirstlane(wave_imin_xor(row_ok ? seg_q : 0x7fffffff, 1, 16));
-    rs.smax = __builtin_amdgcn_readfirstlane(wave_imax_xor(row_ok ? seg_q : (int)0x80000000, 1, 16));
+    rs.smin = __builtin_amdgcn_readfirstlane(wave_min_i32(row_ok ? seg_q : 0x7fffffff));
+    rs.smax = __builtin_amdgcn_readfirstlane(wave_max_i32(row_ok ? seg_q : (int)0x80000000));
     const int pooled_n = (COMPRESSED && row_ok) ? pooled_visible_count(my_q, a.window, a.block, a.nblk) : 0;
 
     if (scan) {
-        const int lo = max(1, wave_imin_xor(min(rseg0, rseg1), 1, 32));
-        const int hi = wave_imax_xor(max(rseg0 == 0x7fffffff ? (int)0x80000000 : rseg0,
-                                         rseg1 == 0x7fffffff ? (int)0x80000000 : rseg1), 1, 32);
+        const int lo = max(1, wave_min_i32(min(rseg0, rseg1)));
+        const int hi = wave_max_i32(max(rseg0 == 0x7fffffff ? (int)0x80000000 : rseg0,
+                                         rseg1 == 0x7fffffff ? (int)0x80000000 : rseg1));
         for (int t0 = 0; t0 < n_sink_tiles; t0 += 64) {
             if (t0 > 0) {
                 tsk = make_int2(0x7fffffff, (int)0x80000000);
@@ -629,11 +630,17 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_prefill_bf16(const PrefillArgs& args, hipStream_t s) {
+    PrefillArgs a = args;
     const int G = a.Hq / a.Hkv;
     const int wg_rows = 32 * a.rbs;
-    const long long nblocks = (long long)((a.T + wg_rows - 1) / wg_rows) * a.Hkv * (G / a.hpw) * a.B;
+    const int nqb = (a.T + wg_rows - 1) / wg_rows;
+    const long long nblocks = (long long)nqb * a.Hkv * (G / a.hpw) * a.B;
     if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    a.div_nqb = make_fastdiv((uint32_t)nqb);
+    a.div_hg = make_fastdiv((uint32_t)(a.Hkv * (G / a.hpw)));
+    a.div_groups = make_fastdiv((uint32_t)(G / a.hpw));
+    a.div_hpw = make_fastdiv((uint32_t)a.hpw);
     dim3 grid((unsigned)nblocks);
     dim3 block(64 * kMfmaWaves);
     const bool rope = a.rope_len > 0;

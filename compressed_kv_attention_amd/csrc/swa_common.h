@@ -44,4 +44,26 @@ __device__ __forceinline__ int wave_imax_xor(int v, int first, int last) {
     return v;
 }
 
+// Whole-wave min / max without LDS: DPP steps within each row of 16 lanes
+// (xor 1, xor 2, rotate 4, rotate 8), then the row-pair and half-wave swaps.
+// Every lane gets the result.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_i32(int x) {
+    auto op = [](int u, int v) { return MAX ? max(u, v) : min(u, v); };
+    x = op(x, dpp_i32<0xB1>(x));
+    x = op(x, dpp_i32<0x4E>(x));
+    x = op(x, dpp_i32<0x124>(x));
+    x = op(x, dpp_i32<0x128>(x));
+    const auto s16 = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = op((int)s16[0], (int)s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return op((int)s32[0], (int)s32[1]);
+}
+__device__ __forceinline__ int wave_min_i32(int x) { return wave_reduce_i32<false>(x); }
+__device__ __forceinline__ int wave_max_i32(int x) { return wave_reduce_i32<true>(x); }
+
 }  // namespace swa

@@ -8,6 +8,25 @@
 
 namespace swa {
 
+// Division by a divisor fixed at launch: q = (mulhi(n, mul) + n) >> shift with
+// shift = ceil(log2 d) and mul = floor(2^32 (2^shift - d) / d) + 1, exact for
+// every n < 2^31 (the round-up multiply-and-shift method of Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994).
+struct FastDiv {
+    uint32_t d, mul, shift;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    f.shift = 0;
+    while ((1ull << f.shift) < d) ++f.shift;
+    f.mul = (uint32_t)((((1ull << 32) * ((1ull << f.shift) - d)) / d) + 1);
+    return f;
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+    return (__umulhi(n, f.mul) + n) >> f.shift;
+}
+
 struct PrefillArgs {
     const void* q;
     const void* k;
@@ -35,6 +54,10 @@ struct PrefillArgs {
     // workgroup geometry of the MFMA kernel: heads per workgroup and 32-row
     // blocks per workgroup (hpw * rbs waves)
     int hpw, rbs;
+    // divisors of the bf16 kernel's workgroup numbering (set by its launcher):
+    // query blocks, head groups per batch row (Hkv * G / hpw), head groups per
+    // kv head (G / hpw), and hpw
+    FastDiv div_nqb, div_hg, div_groups, div_hpw;
 };
 
 // Geometry the bf16 MFMA kernel uses for a given GQA group size: 4 waves per
