@@ -48,7 +48,7 @@ constexpr int BN = 64;   // keys per LDS tile
 constexpr int SUB = 32;  // keys per MFMA sub-tile
 constexpr int NBUF = 2;  // LDS tile buffers: the tile computed and the next one
 constexpr int kSinkWords = (kMaxT / BN + 31) / 32;
-constexpr float kRescaleLog2 = 8.0f;  // rescale when the max grows by > 2^8
+constexpr float kRescaleSum = 256.0f;  // the reference max moves when a weight sum passes 2^8
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -133,7 +133,6 @@ struct SmemBf16 {
     uint16_t k[NBUF][BN * D];     // K tiles, row-major, 16-byte chunks swizzled
     uint16_t v[NBUF][BN * D];     // V tiles, row-major, 16-byte chunks swizzled
     int kinfo[NBUF][BN];          // packed segment | sink << 31 of the tile's keys
-    int ksum[NBUF][BN / SUB][4];  // KeySum of each sub-tile (seg min, seg max, any sink, all sink)
     uint32_t sink_bits[kSinkWords];
 };
 
@@ -153,44 +152,71 @@ __device__ __forceinline__ int v_chunk(int k, int c) {
     return k * CPR + (D == 64 ? (c ^ (((k >> 1) & 1) * 4)) : c);
 }
 
-// The wave that stages the sub-tile summaries (wave 0 stages the key info).
-constexpr int kMetaWave = 1 % kMfmaWaves;
+// Per-lane byte offsets, within a key tile, of the rows and chunks this
+// lane's wave moves: wave w issues loads ld = w, w + kMfmaWaves, ...; load ld
+// covers key rows [ld * ROWS, ld * ROWS + ROWS) and lane l moves 16 bytes of
+// row ld * ROWS + l / CPR.  The lane writes LDS chunk ld * 64 + l; it picks the
+// logical chunk whose swizzled position that is.
+template <int D>
+struct TileLoads {
+    static constexpr int CPR = D / 8;                       // 16-byte chunks per row
+    static constexpr int ROWS = 64 / CPR;                   // key rows per wave instruction
+    static constexpr int LOADS = BN / ROWS / kMfmaWaves;    // instructions per wave per tile
+    // Offsets of the wave's first load; load i sits i * kMfmaWaves * ROWS rows
+    // further (a multiple of 32 rows, which keeps the swizzle unchanged).
+    uint32_t koff, voff;
+    __device__ __forceinline__ void init(int wave, int lane) {
+        const int kr = wave * ROWS + lane / CPR;
+        const int pc = lane % CPR;
+        const int ck = pc ^ ((kr * CPR / 16) % CPR);
+        const int cv = D == 64 ? (pc ^ (((kr >> 1) & 1) * 4)) : pc;
+        koff = (uint32_t)(kr * D + 8 * ck) * 2;
+        voff = (uint32_t)(kr * D + 8 * cv) * 2;
+        static_assert((kMfmaWaves * ROWS) % 32 == 0 || LOADS == 1, "swizzle period");
+    }
+};
 
 // Issue the global->LDS loads of one tile into buffer `buf`: wave w moves
 // 1 KB of K and 1 KB of V (64 lanes x 16 bytes) per instruction; with key
-// metadata, wave 0 also moves the keys' packed info and kMetaWave the two
-// sub-tile summaries.  Rows past the last key load a clamped row (finite
-// data, masked later).
+// metadata, wave 0 also moves the keys' packed info.  Rows past the last key
+// load the last key's row (finite data, masked later).
 template <int D>
-__device__ __forceinline__ void issue_tile(const PrefillArgs& a, SmemBf16<D>& sm, int buf, int kind, int tile, int b,
-                                           int hkv, int wave, int lane) {
-    constexpr int CPR = D / 8;
-    constexpr int ROWS_PER_LOAD = 64 / CPR;  // key rows per wave instruction
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, SmemBf16<D>& sm, uint32_t koff, uint32_t voff, int buf,
+                                           int kind, int tile, int b, int hkv, int wave, int lane) {
+    using TL = TileLoads<D>;
+    constexpr uint32_t kStep = kMfmaWaves * TL::ROWS * D * 2;  // bytes between a wave's loads
     const bool pooled = kind == COL_POOLED;
     const int nkeys = pooled ? a.nblk : a.T;
-    const size_t head_off = ((size_t)b * a.Hkv + hkv) * (size_t)nkeys * D;
-    const uint16_t* kg = (const uint16_t*)(pooled ? a.pk : a.k) + head_off;
-    const uint16_t* vg = (const uint16_t*)(pooled ? a.pv : a.v) + head_off;
     const int k0 = tile * BN;
-    for (int ld = wave; ld < BN / ROWS_PER_LOAD; ld += kMfmaWaves) {
-        const int kr = ld * ROWS_PER_LOAD + lane / CPR;  // key row in the tile
-        const int pc = lane % CPR;                        // physical chunk
-        const int gk = min(k0 + kr, nkeys - 1);
-        // the lane writes LDS chunk (ld * 64 + lane); pick the logical chunk stored there
-        const int ck = pc ^ ((kr * CPR / 16) % CPR);
-        const int cv = D == 64 ? (pc ^ (((kr >> 1) & 1) * 4)) : pc;
-        __builtin_amdgcn_global_load_lds(kg + (size_t)gk * D + 8 * ck, (lds_void*)&sm.k[buf][ld * 64 * 8], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vg + (size_t)gk * D + 8 * cv, (lds_void*)&sm.v[buf][ld * 64 * 8], 16, 0, 0);
+    const size_t head_off = (((size_t)b * a.Hkv + hkv) * (size_t)nkeys + k0) * D;
+    // uniform base pointers (the tile's first row) plus 32-bit per-lane offsets
+    const char* kb = (const char*)((const uint16_t*)(pooled ? a.pk : a.k) + head_off);
+    const char* vb = (const char*)((const uint16_t*)(pooled ? a.pv : a.v) + head_off);
+    if (k0 + BN <= nkeys) {
+#pragma unroll
+        for (int i = 0; i < TL::LOADS; ++i) {
+            const int ld = wave + kMfmaWaves * i;
+            __builtin_amdgcn_global_load_lds(kb + koff + i * kStep, (lds_void*)&sm.k[buf][ld * 64 * 8], 16, 0,
+                                             0);
+            __builtin_amdgcn_global_load_lds(vb + voff + i * kStep, (lds_void*)&sm.v[buf][ld * 64 * 8], 16, 0,
+                                             0);
+        }
+    } else {  // the last tile: rows past the end repeat the last key
+#pragma unroll
+        for (int i = 0; i < TL::LOADS; ++i) {
+            const int ld = wave + kMfmaWaves * i;
+            const int kr = ld * TL::ROWS + lane / TL::CPR;
+            const uint32_t back = (uint32_t)(kr - min(kr, nkeys - 1 - k0)) * D * 2;
+            __builtin_amdgcn_global_load_lds(kb + (koff + i * kStep - back), (lds_void*)&sm.k[buf][ld * 64 * 8],
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb + (voff + i * kStep - back), (lds_void*)&sm.v[buf][ld * 64 * 8],
+                                             16, 0, 0);
+        }
     }
-    if (!pooled && a.kinfo) {
-        if (wave == 0) {
-            const int gk = min(k0 + lane, a.T - 1);
-            __builtin_amdgcn_global_load_lds(a.kinfo + (size_t)b * a.T + gk, (lds_void*)&sm.kinfo[buf][0], 4, 0, 0);
-        }
-        if (wave == kMetaWave && lane < 2 * 4) {
-            const int32_t* src = a.ksub + ((size_t)b * 2 * a.ntile + 2 * tile) * 4 + lane;
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)&sm.ksum[buf][0][0], 4, 0, 0);
-        }
+    if (!pooled && a.kinfo && wave == 0) {
+        const char* ib = (const char*)(a.kinfo + (size_t)b * a.T);
+        const uint32_t gk = (uint32_t)min(k0 + lane, a.T - 1);
+        __builtin_amdgcn_global_load_lds(ib + gk * 4, (lds_void*)&sm.kinfo[buf][0], 4, 0, 0);
     }
 }
 
@@ -264,15 +290,30 @@ __device__ __forceinline__ uint32_t k_lane_off(int c, int lane) {
     return (uint32_t)(k_chunk<D>(lane & 31, 2 * c + (lane >> 5)) * 16);
 }
 
-__device__ __forceinline__ float max3f(float x, float y, float z) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
-    return r;
-}
-__device__ __forceinline__ float max2f(float x, float y) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
-    return r;
+
+// The prep pass's summaries of the two sub-tiles of exact key tile `tile`,
+// through the scalar cache (uniform address, constant address space: the
+// buffer is read-only while the kernel runs).  Without key metadata every
+// key is in segment 1 and none is a sink.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load_key_sums(const PrefillArgs& a, int b, int tile, KeySum* ks) {
+    if (a.ksub == nullptr) {
+        ks[0] = ks[1] = make_key_sum(true, 1, false, false);
+        return;
+    }
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(4))) const i32x4 const_i32x4;
+    const const_i32x4* p = (const const_i32x4*)(a.ksub + ((size_t)b * 2 * a.ntile + 2 * tile) * 4);
+    const i32x4 v0 = p[0], v1 = p[1];
+    ks[0].smin = v0[0];
+    ks[0].smax = v0[1];
+    ks[0].any_sink = v0[2];
+    ks[0].all_sink = v0[3];
+    ks[1].smin = v1[0];
+    ks[1].smax = v1[1];
+    ks[1].any_sink = v1[2];
+    ks[1].all_sink = v1[3];
+#endif
 }
 
 template <int D, bool ROPE, bool COMPRESSED>
@@ -281,7 +322,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     __shared__ __align__(16) SmemBf16<D> sm;
     SWA_TRACE_DECL
     const int tid = threadIdx.x;
-    constexpr int nthreads = 64 * kMfmaWaves;  // the launch always uses this block size
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
@@ -320,7 +360,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     int kc = 0, tc = 0;  // tile being computed
     const bool have0 = it.next(kc, tc);
     SWA_TRACE(11);
-    if (have0) issue_tile<D>(a, sm, 0, kc, tc, b, hkv, wave, lane);
+    TileLoads<D> tl;
+    tl.init(wave, lane);
+    if (have0) issue_tile<D>(a, sm, tl.koff, tl.voff, 0, kc, tc, b, hkv, wave, lane);
     SWA_TRACE(6);
 
     uint4 raw[D / 16];
@@ -376,7 +418,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     rs.r1 = min(r0 + 31, T - 1);
     rs.smin = __builtin_amdgcn_readfirstlane(wave_min_i32(row_ok ? seg_q : 0x7fffffff));
     rs.smax = __builtin_amdgcn_readfirstlane(wave_max_i32(row_ok ? seg_q : (int)0x80000000));
-    const int pooled_n = (COMPRESSED && row_ok) ? pooled_visible_count(my_q, a.window, a.block, a.nblk) : 0;
 
     if (scan) {
         const int lo = max(1, wave_min_i32(min(rseg0, rseg1)));
@@ -397,6 +438,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     SWA_TRACE(8);
     const float c_log2 = a.scale * kLog2e;
     float m_run = kNegInf;  // reference max (raw score units) used for p
+    float base_vis = 0.f;   // m_run * scale * log2 e, or 0 while m_run is -inf
     float l_run = 0.f;
     f32x16 o[D / 32];
 #pragma unroll
@@ -421,9 +463,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         v_addr[n][1] = lds_off(&sm.v[0][0]) + vt_lane_off<D>(n, 1, lane);
     }
     int buf_step = (int)kTileBytes;
-    const uint32_t info_lds = lds_off(&sm.kinfo[0][0]), sum_lds = lds_off(&sm.ksum[0][0][0]);
-    // summaries of exact sub-tiles without key metadata: one segment, no sinks
-    const bool have_meta = a.kinfo != nullptr;
+    const uint32_t info_lds = lds_off(&sm.kinfo[0][0]);
+    // Fast classification of exact sub-tiles: a sub-tile starting at key k0
+    // is FULL for this wave when fpos_lo <= k0 <= fpos_hi (every pair causal
+    // and inside the window) and its keys are sink-free and all in the
+    // segment every row of the wave belongs to (fast_seg; -2 when the rows
+    // are not all in one real segment).
+    const int fpos_lo = a.window != 0 ? max(rs.r1 - a.window + 1, 0) : 0;
+    const int fpos_hi = rs.r0 - (SUB - 1);
+    const int fast_seg = !plain ? 1 : (rs.smin == rs.smax && rs.smin > 0 ? rs.smin : -2);
+    const bool fpos_any = fpos_hi >= fpos_lo;
+    KeySum ks_cur[BN / SUB];
+    if (have0 && kc == COL_EXACT) load_key_sums(a, b, tc, ks_cur);
     int cur = 0;
     bool have = have0;
     while (have) {
@@ -431,72 +482,83 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         const int nxt = cur ^ 1;
         int kn = 0, tn = 0;
         const bool have_next = it.next(kn, tn);
-        if (have_next) issue_tile<D>(a, sm, nxt, kn, tn, b, hkv, wave, lane);
+        if (have_next) issue_tile<D>(a, sm, tl.koff, tl.voff, nxt, kn, tn, b, hkv, wave, lane);
+        KeySum ks_next[BN / SUB];
+        if (have_next && kn == COL_EXACT) load_key_sums(a, b, tn, ks_next);
         SWA_TRACE(1);
 
         if (wave_active) {
             const bool pooled = COMPRESSED && kc == COL_POOLED;
             const int nkeys = pooled ? a.nblk : T;
-            KeySum ksub[BN / SUB];
-#pragma unroll
-            for (int st = 0; st < BN / SUB; ++st) ksub[st] = make_key_sum(true, 1, false, false);
-            if (!pooled && have_meta) {
-                u32x4 kv[BN / SUB];
-#pragma unroll
-                for (int st = 0; st < BN / SUB; ++st) kv[st] = ds_read128(sum_lds + (cur * (BN / SUB) + st) * 16);
-                lds_wait();
-#pragma unroll
-                for (int st = 0; st < BN / SUB; ++st) {
-                    lds_tie(kv[st]);
-                    ksub[st].smin = __builtin_amdgcn_readfirstlane((int)kv[st][0]);
-                    ksub[st].smax = __builtin_amdgcn_readfirstlane((int)kv[st][1]);
-                    ksub[st].any_sink = __builtin_amdgcn_readfirstlane((int)kv[st][2]);
-                    ksub[st].all_sink = __builtin_amdgcn_readfirstlane((int)kv[st][3]);
-                }
-            }
+            // Scores of both sub-tiles first, then their softmax and P V: the
+            // second sub-tile's S MFMAs run while the first one's weights are made.
+            f32x16 sacc_st[BN / SUB];
+            int cls_st[BN / SUB];
+            bool gate_st[BN / SUB];
 #pragma unroll
             for (int st = 0; st < BN / SUB; ++st) {
                 const int k0 = tc * BN + st * SUB;
                 int cls;
                 unsigned wl = wlim;
+                const KeySum& ks = ks_cur[st];
                 if (pooled) {
                     cls = classify_pooled(rs, k0, SUB, a.window, a.block, a.nblk);
+                } else if (fpos_any && (unsigned)(k0 - fpos_lo) <= (unsigned)(fpos_hi - fpos_lo) &&
+                           (!plain || (ks.smin == ks.smax && ks.any_sink == 0 && ks.smin == fast_seg))) {
+                    cls = TILE_FULL;
                 } else {
-                    cls = classify_exact(rs, ksub[st], k0, SUB, nkeys, a.window, plain, wl);
+                    cls = classify_exact(rs, ks, k0, SUB, nkeys, a.window, plain, wl);
                 }
                 cls = __builtin_amdgcn_readfirstlane(cls);
                 wl = __builtin_amdgcn_readfirstlane(wl);
+                cls_st[st] = cls;
                 if (cls == TILE_SKIP) continue;
                 // Rows outside the sub-tile's segment (and padding rows) take no
                 // weight from it: their max ignores it and their exponent base
                 // is +inf, so every weight is exactly 0.
-                const bool gate =
-                    (pooled || cls == TILE_PARTIAL) ? row_vis : lane_gate(row_vis, plain, seg_q, ksub[st]);
+                gate_st[st] =
+                    (pooled || cls == TILE_PARTIAL) ? row_vis : lane_gate(row_vis, plain, seg_q, ks);
 
                 u32x4 kr[D / 16];
 #pragma unroll
                 for (int c = 0; c < D / 16; ++c) kr[c] = ds_read128_at(k_addr[c], st * SUB * D * 2);
-                lds_wait();
-                f32x16 sacc = f32x16{};
-#pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    lds_tie(kr[c]);
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc, 0, 0,
-                                                                   0);
-                }
-                // Element j holds key k0 + off(j) + 4h with off(j) = 8(j/4) + j%4.
-                // Masks are selects on the accumulator registers themselves.
+                // Element j of the score block holds key k0 + off(j) + 4h with
+                // off(j) = 8(j/4) + j%4.  The mask enters as the accumulator's
+                // initial value: 0 where the pair is visible, -inf where it is not.
                 const int kb = k0 + 4 * h;  // key of element 0
-                if (cls == TILE_PARTIAL_POS) {
-                    const int d0 = my_q - kb;
+                f32x16 sacc;
+                if (cls == TILE_FULL) {
+                    lds_wait();
+                    lds_tie(kr[0]);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0], f32x16{},
+                                                                   0, 0, 0);
+                } else {
+                    f32x16 bias;
+                    if (cls == TILE_PARTIAL_POS) {
+                        // Element j is visible iff its key offset off(j) lies in
+                        // [d0 - wl + 1, d0]: a mask over offsets 0..31, then one
+                        // bit extract and one AND per element.
+                        const int d0 = my_q - kb;
+                        // (bounds past 2^20 act as no bound: |d0| stays far below it)
+                        const int lo = max(d0 + 1 - (int)min(wl, 1u << 20), 0);
+                        const int hi = min(d0, 31);
+                        uint32_t vis = 0u;
+                        if (hi >= lo) vis = (hi == 31 ? 0xffffffffu : (2u << hi) - 1u) & ~((1u << lo) - 1u);
+                        const uint32_t hid = ~vis;
 #pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        sacc[j] = visible_pos(d0 - (8 * (j >> 2) + (j & 3)), wl) ? sacc[j] : kNegInf;
-                } else if (cls == TILE_PARTIAL) {
-                    if (pooled) {
+                        for (int j = 0; j < 16; ++j)
+                            bias[j] = __uint_as_float(
+                                (uint32_t)__builtin_amdgcn_sbfe((int)hid, 8 * (j >> 2) + (j & 3), 1) & 0xff800000u);
+                    } else if (pooled) {
+                        // pooled blocks visible to this row (recomputed here, where
+                        // it is rarely needed, rather than held in a register)
+                        int plim = my_q - a.window + 1;
+                        asm volatile("" : "+v"(plim));  // keep it here, not hoisted
+                        const int pooled_n =
+                            plim < a.block ? 0 : min((int)fdiv((uint32_t)plim, a.div_block), a.nblk);
                         const int lim = row_vis ? pooled_n - kb : -1;
 #pragma unroll
-                        for (int j = 0; j < 16; ++j) sacc[j] = (8 * (j >> 2) + (j & 3)) < lim ? sacc[j] : kNegInf;
+                        for (int j = 0; j < 16; ++j) bias[j] = (8 * (j >> 2) + (j & 3)) < lim ? 0.f : kNegInf;
                     } else {
                         const int d0 = my_q - kb;
                         u32x4 inf[4];
@@ -511,35 +573,73 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                             for (int r = 0; r < 4; ++r) {
                                 const bool vis =
                                     row_vis & visible_full(d0 - (8 * g4 + r), wlim, (int)inf[g4][r], seg_q);
-                                sacc[4 * g4 + r] = vis ? sacc[4 * g4 + r] : kNegInf;
+                                bias[4 * g4 + r] = vis ? 0.f : kNegInf;
                             }
                         }
                     }
+                    lds_wait();
+                    lds_tie(kr[0]);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0], bias, 0, 0,
+                                                                   0);
                 }
+#pragma unroll
+                for (int c = 1; c < D / 16; ++c) {
+                    lds_tie(kr[c]);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc, 0, 0,
+                                                                   0);
+                }
+                sacc_st[st] = sacc;
+            }
+#pragma unroll
+            for (int st = 0; st < BN / SUB; ++st) {
+                if (cls_st[st] == TILE_SKIP) continue;
+                const bool gate = gate_st[st];
+                const f32x16 sacc = sacc_st[st];
                 float sv[16];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) sv[j] = sacc[j];
-                float mx = max3f(sv[0], sv[1], sv[2]);
+                // Max of the sub-tile's scores per row (both key halves); -inf
+                // for rows the lane gate excludes.
+                auto sub_max = [&]() {
+                    // (compiler-generated max, not inline asm: sv holds MFMA results,
+                    // and only the compiler inserts the wait a VALU read of them needs)
+                    float mx = sv[0];
 #pragma unroll
-                for (int j = 3; j < 15; j += 2) mx = max3f(mx, sv[j], sv[j + 1]);
-                mx = max2f(mx, sv[15]);
-                {
+                    for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, sv[j]);
                     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false,
                                                                      false);
-                    mx = max2f(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-                }
-                mx = gate ? mx : kNegInf;
-                // Rescale only when some row of the wave outgrows its reference
-                // max by more than 2^8 (the first visible tile always does).
-                const bool grow = (mx - m_run) * c_log2 > kRescaleLog2;
-                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                    mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                    return gate ? mx : kNegInf;
+                };
+                // Move each row's reference max up to mx (if larger), rescaling
+                // what has been accumulated against the old one.
+                auto raise_max = [&](float mx) {
                     const float m_new = __builtin_fmaxf(m_run, mx);
                     const float corr = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
                     m_run = m_new;
+                    base_vis = (m_new == kNegInf) ? 0.f : m_new * c_log2;
                     l_run *= corr;
 #pragma unroll
                     for (int n = 0; n < D / 32; ++n) o[n] *= corr;
-                }
+                };
+                // bf16 weights exp2((s - m_run) * scale * log2 e) and the sum of
+                // exactly those weights over this lane's keys; rows the gate
+                // excludes get base +inf, hence weights of exactly 0.
+                uint32_t pw[8];
+                auto weights = [&]() {
+                    const float base = gate ? base_vis : __builtin_inff();
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        pw[i] = cvt_pk_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c_log2, -base)),
+                                            __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c_log2, -base)));
+                    float ps = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]), ones2, ps, false);
+                    return ps;
+                };
+                // Rows with no reference max yet take this sub-tile's max.
+                if (__builtin_amdgcn_ballot_w64(gate && m_run == kNegInf) != 0) raise_max(sub_max());
                 // V^T operands of the first 16 keys, in flight while the weights are made
                 u32x2 vlo[D / 32], vhi[D / 32];
 #pragma unroll
@@ -547,17 +647,15 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                     vlo[n] = ds_read_tr16_at(v_addr[n][0], st * SUB * D * 2);
                     vhi[n] = ds_read_tr16_at(v_addr[n][1], st * SUB * D * 2);
                 }
-                const float base = gate ? ((m_run == kNegInf) ? 0.f : m_run * c_log2) : __builtin_inff();
-                uint32_t pw[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    pw[i] = cvt_pk_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c_log2, -base)),
-                                        __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c_log2, -base)));
-                // row sum of exactly the bf16 weights the PV product uses
-                float psum = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]), ones2, psum, false);
+                float psum = weights();
+                // The reference max is lazy: it moves only when some row's scores
+                // outgrow it by more than 2^8.  Any weight above 2^8 lifts its
+                // lane's sum above 2^8, so the sum is the test; the rare case
+                // recomputes the weights against the true max.
+                if (__builtin_amdgcn_ballot_w64(psum > kRescaleSum) != 0) {
+                    raise_max(sub_max());
+                    psum = weights();
+                }
                 l_run += psum;
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
@@ -603,6 +701,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         cur = nxt;
         kc = kn;
         tc = tn;
+#pragma unroll
+        for (int st = 0; st < BN / SUB; ++st) ks_cur[st] = ks_next[st];
         have = have_next;
     }
 
@@ -641,6 +741,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& args, hipStream_t s) {
     a.div_hg = make_fastdiv((uint32_t)(a.Hkv * (G / a.hpw)));
     a.div_groups = make_fastdiv((uint32_t)(G / a.hpw));
     a.div_hpw = make_fastdiv((uint32_t)a.hpw);
+    a.div_block = make_fastdiv((uint32_t)(a.block > 0 ? a.block : 1));
     dim3 grid((unsigned)nblocks);
     dim3 block(64 * kMfmaWaves);
     const bool rope = a.rope_len > 0;

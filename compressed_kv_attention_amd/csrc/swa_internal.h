@@ -56,8 +56,8 @@ struct PrefillArgs {
     int hpw, rbs;
     // divisors of the bf16 kernel's workgroup numbering (set by its launcher):
     // query blocks, head groups per batch row (Hkv * G / hpw), head groups per
-    // kv head (G / hpw), and hpw
-    FastDiv div_nqb, div_hg, div_groups, div_hpw;
+    // kv head (G / hpw), hpw, and the compress block
+    FastDiv div_nqb, div_hg, div_groups, div_hpw, div_block;
 };
 
 // Geometry the bf16 MFMA kernel uses for a given GQA group size: 4 waves per
