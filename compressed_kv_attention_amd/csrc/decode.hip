@@ -127,6 +127,15 @@ __device__ __forceinline__ uint32_t lds_read_b32(uint32_t addr) {
     asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
     return r;
 }
+// Transposing 8-bit read: in each group of 16 lanes, source lanes 2r and 2r+1
+// each name 8 bytes that together form row r (16 bytes) of an 8 x 16 byte
+// matrix; output lane j of the group receives column j (rows 0..7, one byte
+// each, row 0 in the lowest byte).
+__device__ __forceinline__ u32x2_t lds_read_tr8(uint32_t addr, int off) {
+    u32x2_t r;
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off));
+    return r;
+}
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)"); }
 template <class X>
 __device__ __forceinline__ void lds_tie(X& x) {
@@ -320,8 +329,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
             const int pc = lane % CPR;
             const int lc = pc ^ ((rr >> 1) & (CPR - 1));  // logical piece stored at slot pc
             const uint32_t off = (uint32_t)row_of(rr) * D + 16 * lc;
+            // (V stays row-major for D = 64: it is read with transposing reads)
+            const uint32_t voff = D == 64 ? (uint32_t)row_of(rr) * D + 16 * pc : off;
             __builtin_amdgcn_global_load_lds(kb + off, (lds_void_t*)&B.k[j * 1024], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vb + off, (lds_void_t*)&B.v[j * 1024], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb + voff, (lds_void_t*)&B.v[j * 1024], 16, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < GROUPS; ++j) {
@@ -386,8 +397,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
             s_new = all_blocks(d) * c_log2;
         }
     }
-#pragma unroll
-    for (int k = 1; k < NBUF; ++k) issue(wave + NW * k, k);
+    // (the second chunk is requested once the first has landed: fewer bytes
+    // requested up front make every wave's first chunk arrive sooner)
+    static_assert(NBUF == 2, "issue schedule");
     SWA_TRACE(0);
 
     // lane-dependent byte selectors of the quad transpose
@@ -395,9 +407,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     const uint32_t sel2 = (c & 1) ? 0x03070105u : 0x06020400u;
     const uint32_t swz = (lane >> 1) & (CPR - 1);
 
-    f32x4_t acc[NI];
+    // D = 64: lane l accumulates O of all four heads (reg r = head r) at
+    // channel l, in two halves (quads 0-7 and 8-15 of each chunk) that are
+    // added at the end.  D = 32: acc[i] holds the per-quad partials of
+    // channels 4i + c, summed over the quads at the end.
+    constexpr int NACC = D == 64 ? 2 : NI;
+    f32x4_t acc[NACC];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NACC; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // D = 64 transposing V reads: lane l of 16-lane group g names 8 bytes of
+    // row 8t + (l % 16) / 2 at channels 16g + 8 (l % 2) .. +7
+    const uint32_t vt_lane = 64 * ((lane & 15) >> 1) + 16 * (lane >> 4) + 8 * (lane & 1);
     float m_h[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // reference max per head (wave-uniform)
     float m_c = kNegInf;                                  // = m_h[c]
     float l_c = 0.f;                                      // row sum of head c (this lane's keys)
@@ -408,12 +428,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     for (int kk = 0; kk < n_steps; ++kk) {
         const int bi = kk % NBUF;
         const int ci = wave + NW * kk;
-        // this chunk's DMA has landed; the younger chunks in flight are the
-        // prologue's (all issued) and those issued below (only when they exist)
+        // this chunk's DMA has landed
         {
-            int younger = 0;
-#pragma unroll
-            for (int k = 1; k < NBUF; ++k) younger += (kk + k < NBUF || kk + k < n_steps) ? 1 : 0;
+            // issued after chunk kk: chunk kk + 1, at step kk - 1 (steps >= 1)
+            const int younger = (kk >= 1 && kk + 1 < n_steps) ? 1 : 0;
             vm_wait_chunks<NDMA>(younger);
         }
         SWA_TRACE(1);
@@ -425,8 +443,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         const uint32_t vbase = lds_addr(&B.v[0]) + 16 * CPR * lane;
 #pragma unroll
         for (int m = 0; m < CPR; ++m) kr[m] = lds_read_b128(kbase + 16 * (m ^ swz));
+        u32x2_t vt[8];  // D = 64: read t -> V codes of rows 8t .. 8t+7 at channel `lane`
+        if constexpr (D == 64) {
 #pragma unroll
-        for (int m = 0; m < CPR; ++m) vr[m] = lds_read_b128(vbase + 16 * (m ^ swz));
+            for (int t = 0; t < 8; ++t) vt[t] = lds_read_tr8(lds_addr(&B.v[0]) + vt_lane, 512 * t);
+        } else {
+#pragma unroll
+            for (int m = 0; m < CPR; ++m) vr[m] = lds_read_b128(vbase + 16 * (m ^ swz));
+        }
         // the group scales of the quad's four keys (rows 4b .. 4b+3), [key][group]
         u32x4_t ksw[GROUPS], vsw[GROUPS];
         const uint32_t qoff = 16 * GROUPS * (lane >> 2);
@@ -437,9 +461,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         }
         lds_wait_all();
 #pragma unroll
-        for (int m = 0; m < CPR; ++m) {
-            lds_tie(kr[m]);
-            lds_tie(vr[m]);
+        for (int m = 0; m < CPR; ++m) lds_tie(kr[m]);
+        if constexpr (D == 64) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) lds_tie(vt[t]);
+        } else {
+#pragma unroll
+            for (int m = 0; m < CPR; ++m) lds_tie(vr[m]);
         }
 #pragma unroll
         for (int g = 0; g < GROUPS; ++g) {
@@ -448,7 +476,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         }
         SWA_TRACE(2);
         // the buffer is free again: the chunk NBUF steps ahead starts loading
-        if (kk + NBUF < n_steps) issue(ci + NW * NBUF, bi);
+        if (kk == 0) {
+            issue(ci + NW, 1);  // (a step past the end reads row 0, never used)
+            if (2 < n_steps) issue(ci + 2 * NW, 0);
+        } else if (kk + 2 < n_steps) {
+            issue(ci + 2 * NW, bi);
+        }
 
         // scores: C_g(4b+c, r) = sum over group g of q_c * (1152 + code) - 1152 * sum q_c
         // (the two group chains alternate so consecutive MFMAs are independent)
@@ -508,7 +541,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
             for (int g = 0; g < GROUPS; ++g) ws_c[g] *= corr_c;
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
+            for (int i = 0; i < NACC; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][r] *= corr[r];
         }
@@ -532,13 +565,34 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
             ws_c[GROUPS - 1] = fdot2(__builtin_bit_cast(uint32_t, a1l), 0x3c003c00u, ws_c[GROUPS - 1]);
             ws_c[GROUPS - 1] = fdot2(__builtin_bit_cast(uint32_t, a1h), 0x3c003c00u, ws_c[GROUPS - 1]);
         }
-        // O += P V: V codes of the quad's keys at channel 4i + c
+        if constexpr (D == 64) {
+            // O += P V with blocks = channel quads: block b (lanes 4b..4b+3)
+            // computes O[head r][channel 4b + c] over one key quad whose
+            // weights every block of its half takes by broadcast (CBSZ = 3:
+            // blocks 0-7 read block ABID, blocks 8-15 block 8 + ABID).  The
+            // halves need different V group scales, so one lane exchange
+            // builds the two A operands: for quads 0-7, lanes 0-31 keep their
+            // group-0 weights and lanes 32-63 receive the group-1 weights of
+            // lanes 0-31; for quads 8-15 the other way round.
+            const u32x2_t w0 = __builtin_bit_cast(u32x2_t, pa0), w1 = __builtin_bit_cast(u32x2_t, pa1);
+            const auto e0 = __builtin_amdgcn_permlane32_swap(w0[0], w1[0], false, false);
+            const auto e1 = __builtin_amdgcn_permlane32_swap(w0[1], w1[1], false, false);
+            const half4_t a_lo = __builtin_bit_cast(half4_t, make_uint2(e0[0], e1[0]));  // quads 0-7
+            const half4_t a_hi = __builtin_bit_cast(half4_t, make_uint2(e0[1], e1[1]));  // quads 8-15
+#define SWA_PV(Q)                                                                                          \
+    acc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(a_lo, codes_to_h4(vt[(Q) / 2][(Q) % 2]), acc[0], 3, Q, 0);   \
+    acc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(a_hi, codes_to_h4(vt[4 + (Q) / 2][(Q) % 2]), acc[1], 3, Q, 0);
+            SWA_PV(0) SWA_PV(1) SWA_PV(2) SWA_PV(3) SWA_PV(4) SWA_PV(5) SWA_PV(6) SWA_PV(7)
+#undef SWA_PV
+        } else {
+            // O += P V: V codes of the quad's keys at channel 4i + c
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const uint32_t w = vr[i / 4][i % 4];
-            const uint32_t t = __builtin_amdgcn_perm(dpp_xor2(w), w, sel1);
-            const uint32_t col = __builtin_amdgcn_perm(dpp_xor1(t), t, sel2);
-            acc[i] = __builtin_amdgcn_mfma_f32_4x4x4f16(i < 8 ? pa0 : pa1, codes_to_h4(col), acc[i], 0, 0, 0);
+            for (int i = 0; i < NI; ++i) {
+                const uint32_t w = vr[i / 4][i % 4];
+                const uint32_t t = __builtin_amdgcn_perm(dpp_xor2(w), w, sel1);
+                const uint32_t col = __builtin_amdgcn_perm(dpp_xor1(t), t, sel2);
+                acc[i] = __builtin_amdgcn_mfma_f32_4x4x4f16(i < 8 ? pa0 : pa1, codes_to_h4(col), acc[i], 0, 0, 0);
+            }
         }
         SWA_TRACE(3);
     }
@@ -546,32 +600,40 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     // or the wave ends
     vm_wait_upto<0>();
 
-    // sum the 16 blocks' partial outputs.  Two halving exchanges (lane bits 5
-    // and 4) leave each lane NJ = NI / 4 channel steps per head; row
-    // rotations by 4 and 8 add the four blocks of each 16-lane row.  Lane l
-    // then holds the totals of channels 4 i + c with i = j + NJ * (l >> 4).
+    // D = 32: sum the 16 blocks' partial outputs.  Two halving exchanges
+    // (lane bits 5 and 4) leave each lane NJ = NI / 4 channel steps per head;
+    // row rotations by 4 and 8 add the four blocks of each 16-lane row.  Lane
+    // l then holds the totals of channels 4 i + c with i = j + NJ * (l >> 4).
+    // D = 64 needs no reduction: lane l already holds channel l.
     constexpr int NJ = NI / 4;
-    float o1[NI / 2][4];
-#pragma unroll
-    for (int j = 0; j < NI / 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[j][r]),
-                                                            __float_as_uint(acc[j + NI / 2][r]), false, false);
-            o1[j][r] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
     float o2[NJ][4];
+    if constexpr (D == 64) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+        for (int r = 0; r < 4; ++r) o2[0][r] = acc[0][r] + acc[1][r];
+    } else {
+        float o1[NI / 2][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(o1[j][r]), __float_as_uint(o1[j + NJ][r]),
-                                                            false, false);
-            float x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            x += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x124, 0xF, 0xF, false));
-            x += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x128, 0xF, 0xF, false));
-            o2[j][r] = x;
-        }
+        for (int j = 0; j < NI / 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[j][r]),
+                                                                __float_as_uint(acc[j + NI / 2][r]), false, false);
+                o1[j][r] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(o1[j][r]),
+                                                                __float_as_uint(o1[j + NJ][r]), false, false);
+                float x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                x += __int_as_float(
+                    __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x124, 0xF, 0xF, false));
+                x += __int_as_float(
+                    __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x128, 0xF, 0xF, false));
+                o2[j][r] = x;
+            }
+    }
     const float l_tot = all_blocks(l_c);
     float ws_tot[GROUPS];
 #pragma unroll
@@ -592,16 +654,21 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     // merge of the waves: each leaves its per-head totals in LDS; then every
     // lane of the workgroup produces outputs (head, channel) together with the
     // appended token
-    const int i_out = (lane >> 2) % NJ;
-    const bool writer = ((lane >> 2) & 3) < NJ;
     {
-        const int ch = 4 * (i_out + NJ * (lane >> 4)) + c;
+        if constexpr (D == 64) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float o = o2[0][r];
+            for (int r = 0; r < 4; ++r) sm.part_o(wave)[r * D + lane] = o2[0][r];
+        } else {
+            const int i_out = (lane >> 2) % NJ;
+            const bool writer = ((lane >> 2) & 3) < NJ;
+            const int ch = 4 * (i_out + NJ * (lane >> 4)) + c;
 #pragma unroll
-            for (int j = 1; j < NJ; ++j) o = i_out == j ? o2[j][r] : o;
-            if (writer) sm.part_o(wave)[r * D + ch] = o;
+            for (int r = 0; r < 4; ++r) {
+                float o = o2[0][r];
+#pragma unroll
+                for (int j = 1; j < NJ; ++j) o = i_out == j ? o2[j][r] : o;
+                if (writer) sm.part_o(wave)[r * D + ch] = o;
+            }
         }
         if (lane < 4) {
             sm.part_m[wave][lane] = m_c;
@@ -615,9 +682,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_new), 1)),
                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_new), 2)),
                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_new), 3))};
-    for (int e = tid; e < 4 * D; e += 64 * NW) {  // (4 * D is a multiple of the block size)
+    // (4 * D is a multiple of the block size; with D = 64 each iteration is one
+    // head per wave and lane = channel, so the head's merge factors are uniform
+    // and the lane's own v_new is the channel's)
+    for (int e = tid; e < 4 * D; e += 64 * NW) {
         const int r = e / D, d = e % D;
-        const float vn = __shfl(v_new, d, 64);    // before any lane leaves the loop body
+        const float vn = D == 64 ? v_new : __shfl(v_new, d, 64);  // before any lane leaves the loop body
         if (r >= nh) continue;
         const int g = d / 32;
         const float sr = r == 0 ? sn[0] : r == 1 ? sn[1] : r == 2 ? sn[2] : sn[3];
@@ -626,21 +696,18 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         for (int w = 0; w < NW; ++w) m = fmaxf(m, sm.part_m[w][r]);
         float num = 0.f, den = 0.f;
         if (m != kNegInf) {
-            if (sr != kNegInf) {
-                const float fn = __builtin_amdgcn_exp2f(sr - m);
-                num = fn * vn;
-                den = fn;
-            }
+            // exp2(-inf - m) is 0 for a finite m: empty parts drop out
+            const float fn = __builtin_amdgcn_exp2f(sr - m);
+            num = fn * vn;
+            den = fn;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                const float mw = sm.part_m[w][r];
-                if (mw == kNegInf) continue;
-                const float f = __builtin_amdgcn_exp2f(mw - m);
+                const float f = __builtin_amdgcn_exp2f(sm.part_m[w][r] - m);
                 num += f * (sm.part_o(w)[r * D + d] - kBias * sm.part_ws[w][r][g]);
                 den += f * sm.part_l[w][r];
             }
         }
-        const float val = den > 0.f ? num / den : 0.f;
+        const float val = den > 0.f ? num * __builtin_amdgcn_rcpf(den) : 0.f;
         ((uint16_t*)a.out)[((size_t)b * a.Hq + h0 + r) * D + d] = (uint16_t)f32_to_bf16_bits(val);
     }
     SWA_TRACE(5);
