@@ -52,16 +52,18 @@ constexpr float kRescaleSum = 256.0f;  // the reference max moves when a weight 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS access inside the main loop goes through these helpers.  While tiles
-// are in flight through global_load_lds, the compiler would otherwise wait
-// for every outstanding load before any LDS access (it cannot tell the three
-// buffers apart); here each wait is explicit.  After issuing reads, call
-// lds_wait() and then lds_tie() on every result before using it.
+// Tiles move global -> LDS by direct loads issued from inline asm, so the
+// compiler does not see them: seen, they would make it wait for every tile in
+// flight before any LDS read (it cannot tell the two buffers apart).  Each
+// wave waits for its own loads (vmcnt) before the barrier that publishes a
+// tile.  Every LDS read is an ordinary load the compiler schedules, waits for
+// and orders against the matrix instructions itself.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// LDS byte offset of a pointer into __shared__ memory (device pass only; the
-// host pass never runs device functions).
+// LDS byte offset of a pointer into __shared__ memory, and back (device pass
+// only; the host pass never runs device functions).
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     return __builtin_bit_cast(uint32_t, (__attribute__((address_space(3))) const char*)p);
@@ -70,62 +72,44 @@ __device__ __forceinline__ uint32_t lds_off(const void* p) {
     return 0u;
 #endif
 }
-__device__ __forceinline__ u32x4 ds_read128(uint32_t addr) {
-    u32x4 r;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
-    return r;
+__device__ __forceinline__ u32x4 lds_load128(uint32_t addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return *__builtin_bit_cast(__attribute__((address_space(3))) const u32x4*, addr);
+#else
+    (void)addr;
+    return u32x4{};
+#endif
 }
-// Reads at a base register plus an immediate byte offset (a constant once
-// the surrounding loops are unrolled).
-__device__ __forceinline__ u32x4 ds_read128_at(uint32_t addr, int off) {
-    u32x4 r;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off));
-    return r;
+// ds_read_b64_tr_b16: the 16-bit transpose read (lane j of each 16-lane group
+// gets element j of the four rows the group's lanes address).
+__device__ __forceinline__ u32x2 lds_load_tr16(uint32_t addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(__builtin_bit_cast(__attribute__((address_space(3))) s16x4*, addr)));
+#else
+    (void)addr;
+    return u32x2{};
+#endif
 }
-__device__ __forceinline__ u32x2 ds_read_tr16_at(uint32_t addr, int off) {
-    u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off));
-    return r;
+// Direct global -> LDS loads: lane l's 16 (or 4) bytes at base + voff land at
+// LDS byte lds + 16 l (or 4 l).  base and lds are wave-uniform.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
 }
-__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
-    u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
-    return r;
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
 }
-__device__ __forceinline__ uint32_t ds_read32(uint32_t addr) {
-    uint32_t r;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
-    return r;
-}
-__device__ __forceinline__ uint32_t ds_read_u8(uint32_t addr) {
-    uint32_t r;
-    asm volatile("ds_read_u8 %0, %1" : "=v"(r) : "v"(addr));
-    return r;
-}
-__device__ __forceinline__ void ds_write32(uint32_t addr, uint32_t v) {
-    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v));
-}
-__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"); }
-template <typename X>
-__device__ __forceinline__ void lds_tie(X& x) {
-    asm volatile("" : "+v"(x));
-}
-
-// s_waitcnt with vmcnt <= n (n < 16), lgkmcnt = 0, expcnt untouched.
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-    static_assert(N >= 0 && N < 16, "vmcnt");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N));
-}
-__device__ __forceinline__ void barrier_raw() { asm volatile("s_barrier"); }
-__device__ __forceinline__ void wait_vm_upto(int n) {  // n = loads that may stay in flight
-    switch (n) {
-        case 0: wait_vm_lgkm0<0>(); break;
-        case 1: wait_vm_lgkm0<1>(); break;
-        case 2: wait_vm_lgkm0<2>(); break;
-        case 3: wait_vm_lgkm0<3>(); break;
-        default: wait_vm_lgkm0<4>(); break;
-    }
+// Wait for all of this wave's global loads (direct-to-LDS ones included) and
+// LDS accesses, then the workgroup barrier.  The wait is the builtin, not asm,
+// so that the compiler knows every earlier load has completed and inserts no
+// wait of its own on the tiles in flight later.
+__device__ __forceinline__ void wait_all_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 template <int D>
@@ -133,6 +117,7 @@ struct SmemBf16 {
     uint16_t k[NBUF][BN * D];     // K tiles, row-major, 16-byte chunks swizzled
     uint16_t v[NBUF][BN * D];     // V tiles, row-major, 16-byte chunks swizzled
     int kinfo[NBUF][BN];          // packed segment | sink << 31 of the tile's keys
+    int ksum[NBUF][BN / SUB][4];  // KeySum of each sub-tile (from the prep pass)
     uint32_t sink_bits[kSinkWords];
 };
 
@@ -176,9 +161,13 @@ struct TileLoads {
     }
 };
 
+// The wave that stages the sub-tile summaries (wave 0 stages the key info).
+constexpr int kMetaWave = 1 % kMfmaWaves;
+
 // Issue the global->LDS loads of one tile into buffer `buf`: wave w moves
 // 1 KB of K and 1 KB of V (64 lanes x 16 bytes) per instruction; with key
-// metadata, wave 0 also moves the keys' packed info.  Rows past the last key
+// metadata, wave 0 also moves the keys' packed info and kMetaWave the two
+// sub-tile summaries.  Rows past the last key
 // load the last key's row (finite data, masked later).
 template <int D>
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, SmemBf16<D>& sm, uint32_t koff, uint32_t voff, int buf,
@@ -196,10 +185,8 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, SmemBf16<D>& sm
 #pragma unroll
         for (int i = 0; i < TL::LOADS; ++i) {
             const int ld = wave + kMfmaWaves * i;
-            __builtin_amdgcn_global_load_lds(kb + koff + i * kStep, (lds_void*)&sm.k[buf][ld * 64 * 8], 16, 0,
-                                             0);
-            __builtin_amdgcn_global_load_lds(vb + voff + i * kStep, (lds_void*)&sm.v[buf][ld * 64 * 8], 16, 0,
-                                             0);
+            dma16(kb, koff + i * kStep, lds_off(&sm.k[buf][ld * 64 * 8]));
+            dma16(vb, voff + i * kStep, lds_off(&sm.v[buf][ld * 64 * 8]));
         }
     } else {  // the last tile: rows past the end repeat the last key
 #pragma unroll
@@ -207,16 +194,20 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, SmemBf16<D>& sm
             const int ld = wave + kMfmaWaves * i;
             const int kr = ld * TL::ROWS + lane / TL::CPR;
             const uint32_t back = (uint32_t)(kr - min(kr, nkeys - 1 - k0)) * D * 2;
-            __builtin_amdgcn_global_load_lds(kb + (koff + i * kStep - back), (lds_void*)&sm.k[buf][ld * 64 * 8],
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vb + (voff + i * kStep - back), (lds_void*)&sm.v[buf][ld * 64 * 8],
-                                             16, 0, 0);
+            dma16(kb, koff + i * kStep - back, lds_off(&sm.k[buf][ld * 64 * 8]));
+            dma16(vb, voff + i * kStep - back, lds_off(&sm.v[buf][ld * 64 * 8]));
         }
     }
-    if (!pooled && a.kinfo && wave == 0) {
-        const char* ib = (const char*)(a.kinfo + (size_t)b * a.T);
-        const uint32_t gk = (uint32_t)min(k0 + lane, a.T - 1);
-        __builtin_amdgcn_global_load_lds(ib + gk * 4, (lds_void*)&sm.kinfo[buf][0], 4, 0, 0);
+    if (!pooled && a.kinfo) {
+        if (wave == 0) {
+            const char* ib = (const char*)(a.kinfo + (size_t)b * a.T);
+            const uint32_t gk = (uint32_t)min(k0 + lane, a.T - 1);
+            dma4(ib, gk * 4, lds_off(&sm.kinfo[buf][0]));
+        }
+        if (wave == kMetaWave && lane < 2 * 4) {
+            const char* sb = (const char*)(a.ksub + ((size_t)b * 2 * a.ntile + 2 * tile) * 4);
+            dma4(sb, (uint32_t)lane * 4, lds_off(&sm.ksum[buf][0][0]));
+        }
     }
 }
 
@@ -290,31 +281,6 @@ __device__ __forceinline__ uint32_t k_lane_off(int c, int lane) {
     return (uint32_t)(k_chunk<D>(lane & 31, 2 * c + (lane >> 5)) * 16);
 }
 
-
-// The prep pass's summaries of the two sub-tiles of exact key tile `tile`,
-// through the scalar cache (uniform address, constant address space: the
-// buffer is read-only while the kernel runs).  Without key metadata every
-// key is in segment 1 and none is a sink.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void load_key_sums(const PrefillArgs& a, int b, int tile, KeySum* ks) {
-    if (a.ksub == nullptr) {
-        ks[0] = ks[1] = make_key_sum(true, 1, false, false);
-        return;
-    }
-#if defined(__HIP_DEVICE_COMPILE__)
-    typedef __attribute__((address_space(4))) const i32x4 const_i32x4;
-    const const_i32x4* p = (const const_i32x4*)(a.ksub + ((size_t)b * 2 * a.ntile + 2 * tile) * 4);
-    const i32x4 v0 = p[0], v1 = p[1];
-    ks[0].smin = v0[0];
-    ks[0].smax = v0[1];
-    ks[0].any_sink = v0[2];
-    ks[0].all_sink = v0[3];
-    ks[1].smin = v1[0];
-    ks[1].smax = v1[1];
-    ks[1].any_sink = v1[2];
-    ks[1].all_sink = v1[3];
-#endif
-}
 
 template <int D, bool ROPE, bool COMPRESSED>
 __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_bf16_kernel(PrefillArgs a) {
@@ -447,8 +413,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 
     // tile 0 must have landed
-    wait_vm_upto(0);
-    barrier_raw();
+    wait_all_barrier();
     SWA_TRACE(0);
 
     // LDS addresses of the operand reads in the buffer being computed; they
@@ -473,8 +438,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const int fpos_hi = rs.r0 - (SUB - 1);
     const int fast_seg = !plain ? 1 : (rs.smin == rs.smax && rs.smin > 0 ? rs.smin : -2);
     const bool fpos_any = fpos_hi >= fpos_lo;
-    KeySum ks_cur[BN / SUB];
-    if (have0 && kc == COL_EXACT) load_key_sums(a, b, tc, ks_cur);
+    const uint32_t sum_lds = lds_off(&sm.ksum[0][0][0]);
     int cur = 0;
     bool have = have0;
     while (have) {
@@ -483,18 +447,28 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         int kn = 0, tn = 0;
         const bool have_next = it.next(kn, tn);
         if (have_next) issue_tile<D>(a, sm, tl.koff, tl.voff, nxt, kn, tn, b, hkv, wave, lane);
-        KeySum ks_next[BN / SUB];
-        if (have_next && kn == COL_EXACT) load_key_sums(a, b, tn, ks_next);
         SWA_TRACE(1);
 
         if (wave_active) {
             const bool pooled = COMPRESSED && kc == COL_POOLED;
             const int nkeys = pooled ? a.nblk : T;
-            // Scores of both sub-tiles first, then their softmax and P V: the
-            // second sub-tile's S MFMAs run while the first one's weights are made.
-            f32x16 sacc_st[BN / SUB];
             int cls_st[BN / SUB];
             bool gate_st[BN / SUB];
+            // sub-tile summaries (staged with the tile); without key metadata
+            // every key is in segment 1 and none is a sink
+            KeySum ks_cur[BN / SUB];
+#pragma unroll
+            for (int st = 0; st < BN / SUB; ++st) ks_cur[st] = make_key_sum(true, 1, false, false);
+            if (!pooled && a.ksub) {
+#pragma unroll
+                for (int st = 0; st < BN / SUB; ++st) {
+                    const u32x4 kv = lds_load128(sum_lds + (cur * (BN / SUB) + st) * 16);
+                    ks_cur[st].smin = __builtin_amdgcn_readfirstlane((int)kv[0]);
+                    ks_cur[st].smax = __builtin_amdgcn_readfirstlane((int)kv[1]);
+                    ks_cur[st].any_sink = __builtin_amdgcn_readfirstlane((int)kv[2]);
+                    ks_cur[st].all_sink = __builtin_amdgcn_readfirstlane((int)kv[3]);
+                }
+            }
 #pragma unroll
             for (int st = 0; st < BN / SUB; ++st) {
                 const int k0 = tc * BN + st * SUB;
@@ -521,15 +495,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 
                 u32x4 kr[D / 16];
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) kr[c] = ds_read128_at(k_addr[c], st * SUB * D * 2);
+                for (int c = 0; c < D / 16; ++c) kr[c] = lds_load128(k_addr[c] + st * SUB * D * 2);
                 // Element j of the score block holds key k0 + off(j) + 4h with
                 // off(j) = 8(j/4) + j%4.  The mask enters as the accumulator's
                 // initial value: 0 where the pair is visible, -inf where it is not.
                 const int kb = k0 + 4 * h;  // key of element 0
                 f32x16 sacc;
                 if (cls == TILE_FULL) {
-                    lds_wait();
-                    lds_tie(kr[0]);
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0], f32x16{},
                                                                    0, 0, 0);
                 } else {
@@ -564,11 +536,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                         u32x4 inf[4];
 #pragma unroll
                         for (int g4 = 0; g4 < 4; ++g4)
-                            inf[g4] = ds_read128(info_lds + cur * BN * 4 + (st * SUB + 8 * g4 + 4 * h) * 4);
-                        lds_wait();
+                            inf[g4] = lds_load128(info_lds + cur * BN * 4 + (st * SUB + 8 * g4 + 4 * h) * 4);
 #pragma unroll
                         for (int g4 = 0; g4 < 4; ++g4) {
-                            lds_tie(inf[g4]);
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 const bool vis =
@@ -577,24 +547,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                             }
                         }
                     }
-                    lds_wait();
-                    lds_tie(kr[0]);
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0], bias, 0, 0,
                                                                    0);
                 }
 #pragma unroll
-                for (int c = 1; c < D / 16; ++c) {
-                    lds_tie(kr[c]);
+                for (int c = 1; c < D / 16; ++c)
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc, 0, 0,
                                                                    0);
-                }
-                sacc_st[st] = sacc;
-            }
-#pragma unroll
-            for (int st = 0; st < BN / SUB; ++st) {
-                if (cls_st[st] == TILE_SKIP) continue;
                 const bool gate = gate_st[st];
-                const f32x16 sacc = sacc_st[st];
                 float sv[16];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) sv[j] = sacc[j];
@@ -640,13 +600,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 };
                 // Rows with no reference max yet take this sub-tile's max.
                 if (__builtin_amdgcn_ballot_w64(gate && m_run == kNegInf) != 0) raise_max(sub_max());
-                // V^T operands of the first 16 keys, in flight while the weights are made
-                u32x2 vlo[D / 32], vhi[D / 32];
-#pragma unroll
-                for (int n = 0; n < D / 32; ++n) {
-                    vlo[n] = ds_read_tr16_at(v_addr[n][0], st * SUB * D * 2);
-                    vhi[n] = ds_read_tr16_at(v_addr[n][1], st * SUB * D * 2);
-                }
                 float psum = weights();
                 // The reference max is lazy: it moves only when some row's scores
                 // outgrow it by more than 2^8.  Any weight above 2^8 lifts its
@@ -657,22 +610,21 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                     psum = weights();
                 }
                 l_run += psum;
+                // V^T operands of the sub-tile's 32 keys
+                u32x2 vlo[2][D / 32], vhi[2][D / 32];
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int n = 0; n < D / 32; ++n) {
+                        vlo[m][n] = lds_load_tr16(v_addr[n][0] + (st * SUB + 16 * m) * D * 2);
+                        vhi[m][n] = lds_load_tr16(v_addr[n][1] + (st * SUB + 16 * m) * D * 2);
+                    }
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
-                    lds_wait();
                     u32x4 vw[D / 32];
 #pragma unroll
                     for (int n = 0; n < D / 32; ++n) {
-                        lds_tie(vlo[n]);
-                        lds_tie(vhi[n]);
-                        vw[n] = u32x4{vlo[n][0], vlo[n][1], vhi[n][0], vhi[n][1]};
-                    }
-                    if (m == 0) {  // the next 16 keys load during this product
-#pragma unroll
-                        for (int n = 0; n < D / 32; ++n) {
-                            vlo[n] = ds_read_tr16_at(v_addr[n][0], (st * SUB + 16) * D * 2);
-                            vhi[n] = ds_read_tr16_at(v_addr[n][1], (st * SUB + 16) * D * 2);
-                        }
+                        vw[n] = u32x4{vlo[m][n][0], vlo[m][n][1], vhi[m][n][0], vhi[m][n][1]};
                     }
                     const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * m], pw[4 * m + 1], pw[4 * m + 2],
                                                                             pw[4 * m + 3]));
@@ -686,9 +638,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         SWA_TRACE(2);
 
         // tile `nxt` must have landed before the barrier
-        wait_vm_upto(0);
-        SWA_TRACE(3);
-        barrier_raw();
+        wait_all_barrier();
         SWA_TRACE(4);
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) k_addr[c] += buf_step;
@@ -701,8 +651,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         cur = nxt;
         kc = kn;
         tc = tn;
-#pragma unroll
-        for (int st = 0; st < BN / SUB; ++st) ks_cur[st] = ks_next[st];
+
         have = have_next;
     }
 
