@@ -98,68 +98,24 @@ __device__ __forceinline__ half4_t codes_to_h4(uint32_t w) {
     return __builtin_bit_cast(half4_t, make_uint2(lo, hi));
 }
 
-// Inline-asm LDS access.  Cache rows reach LDS by DMA (global_load_lds),
-// which the compiler tracks only as outstanding vector loads, so an LDS read
-// it emitted itself would first wait for every DMA in flight; these reads and
-// the explicit waits keep the next chunk's DMA in flight during this chunk.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    return __builtin_bit_cast(uint32_t, (__attribute__((address_space(3))) const char*)p);
-#else
-    (void)p;
-    return 0u;
-#endif
-}
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
-    u32x4_t r;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
-    return r;
-}
-__device__ __forceinline__ u32x2_t lds_read_b64(uint32_t addr) {
-    u32x2_t r;
-    asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(addr));
-    return r;
-}
-__device__ __forceinline__ uint32_t lds_read_b32(uint32_t addr) {
-    uint32_t r;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
-    return r;
-}
-// Transposing 8-bit read: in each group of 16 lanes, source lanes 2r and 2r+1
-// each name 8 bytes that together form row r (16 bytes) of an 8 x 16 byte
-// matrix; output lane j of the group receives column j (rows 0..7, one byte
-// each, row 0 in the lowest byte).
-__device__ __forceinline__ u32x2_t lds_read_tr8(uint32_t addr, int off) {
-    u32x2_t r;
-    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off));
-    return r;
-}
-__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)"); }
+// q and the appended token are read by global loads the compiler does not
+// track either (they are issued before a chunk's direct loads and waited for
+// with vm_wait_upto); tie() marks the point after that wait from which their
+// registers may be read.
 template <class X>
-__device__ __forceinline__ void lds_tie(X& x) {
+__device__ __forceinline__ void tie(X& x) {
     asm volatile("" : "+v"(x));
 }
-template <int N>
-__device__ __forceinline__ void vm_wait_upto() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
-}
-
-// A global load the compiler does not track (waited for with vm_wait_upto).
-__device__ __forceinline__ u32x4_t gload_b128_untracked(const void* p) {
-    u32x4_t r;
+__device__ __forceinline__ u32x4 gload_b128_untracked(const void* p) {
+    u32x4 r;
     asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
     return r;
 }
-
 __device__ __forceinline__ uint32_t gload_u16_untracked(const void* p) {
     uint32_t r;
     asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
     return r;
 }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 // One wave's LDS copy of a chunk of 64 cache rows: K and V codes (row-major,
 // 16-byte pieces of row r stored XOR-swizzled by (r >> 1) so that one row per
@@ -293,7 +249,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     // appended token's elements of this lane; issued before the cache rows so
     // they arrive first
     const bool live = c < nh;
-    u32x4_t qraw[NI / 2];
+    u32x4 qraw[NI / 2];
     {
         const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.Hq + h0 + (live ? c : 0)) * D;
 #pragma unroll
@@ -331,15 +287,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
             const uint32_t off = (uint32_t)row_of(rr) * D + 16 * lc;
             // (V stays row-major for D = 64: it is read with transposing reads)
             const uint32_t voff = D == 64 ? (uint32_t)row_of(rr) * D + 16 * pc : off;
-            __builtin_amdgcn_global_load_lds(kb + off, (lds_void_t*)&B.k[j * 1024], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vb + voff, (lds_void_t*)&B.v[j * 1024], 16, 0, 0);
+            dma16(kb, off, lds_off(&B.k[j * 1024]));
+            dma16(vb, voff, lds_off(&B.v[j * 1024]));
         }
 #pragma unroll
         for (int j = 0; j < GROUPS; ++j) {
             const int f = 64 * j + lane;
             const uint32_t off = (uint32_t)row_of(f / GROUPS) * GROUPS + f % GROUPS;
-            __builtin_amdgcn_global_load_lds(ksb + off, (lds_void_t*)&B.ks[64 * j], 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(vsb + off, (lds_void_t*)&B.vs[64 * j], 4, 0, 0);
+            dma4(ksb, off * 4, lds_off(&B.ks[64 * j]));
+            dma4(vsb, off * 4, lds_off(&B.vs[64 * j]));
         }
     };
     // the first chunk now, the rest once q is ready: the first requests of
@@ -350,16 +306,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     // the new token were loaded before the NDMA DMA instructions of chunk 0)
     vm_wait_upto<NDMA>();
 #pragma unroll
-    for (int j = 0; j < NI / 2; ++j) lds_tie(qraw[j]);
-    lds_tie(xk);
-    lds_tie(xv);
+    for (int j = 0; j < NI / 2; ++j) tie(qraw[j]);
+    tie(xk);
+    tie(xv);
     half4_t qb[NI];
     float qbias[GROUPS];
 #pragma unroll
     for (int g = 0; g < GROUPS; ++g) qbias[g] = 0.f;
 #pragma unroll
     for (int j = 0; j < NI / 2; ++j) {
-        const u32x4_t w = qraw[j];
+        const u32x4 w = qraw[j];
         const uint32_t ws[4] = {live ? w[0] : 0u, live ? w[1] : 0u, live ? w[2] : 0u, live ? w[3] : 0u};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -438,44 +394,31 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         const DecBuf<D>& B = sm.buf[wave][bi];
         const int nvalid = chunk_rows(ci);
         // this lane's row: K and V pieces in logical order
-        u32x4_t kr[CPR], vr[CPR];
-        const uint32_t kbase = lds_addr(&B.k[0]) + 16 * CPR * lane;
-        const uint32_t vbase = lds_addr(&B.v[0]) + 16 * CPR * lane;
+        u32x4 kr[CPR], vr[CPR];
+        const uint32_t kbase = lds_off(&B.k[0]) + 16 * CPR * lane;
+        const uint32_t vbase = lds_off(&B.v[0]) + 16 * CPR * lane;
 #pragma unroll
-        for (int m = 0; m < CPR; ++m) kr[m] = lds_read_b128(kbase + 16 * (m ^ swz));
-        u32x2_t vt[8];  // D = 64: read t -> V codes of rows 8t .. 8t+7 at channel `lane`
+        for (int m = 0; m < CPR; ++m) kr[m] = lds_load128(kbase + 16 * (m ^ swz));
+        u32x2 vt[8];  // D = 64: read t -> V codes of rows 8t .. 8t+7 at channel `lane`
         if constexpr (D == 64) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) vt[t] = lds_read_tr8(lds_addr(&B.v[0]) + vt_lane, 512 * t);
+            for (int t = 0; t < 8; ++t) vt[t] = lds_load_tr8(lds_off(&B.v[0]) + vt_lane + 512 * t);
         } else {
 #pragma unroll
-            for (int m = 0; m < CPR; ++m) vr[m] = lds_read_b128(vbase + 16 * (m ^ swz));
+            for (int m = 0; m < CPR; ++m) vr[m] = lds_load128(vbase + 16 * (m ^ swz));
         }
         // the group scales of the quad's four keys (rows 4b .. 4b+3), [key][group]
-        u32x4_t ksw[GROUPS], vsw[GROUPS];
+        u32x4 ksw[GROUPS], vsw[GROUPS];
         const uint32_t qoff = 16 * GROUPS * (lane >> 2);
 #pragma unroll
         for (int g = 0; g < GROUPS; ++g) {
-            ksw[g] = lds_read_b128(lds_addr(&B.ks[0]) + qoff + 16 * g);
-            vsw[g] = lds_read_b128(lds_addr(&B.vs[0]) + qoff + 16 * g);
-        }
-        lds_wait_all();
-#pragma unroll
-        for (int m = 0; m < CPR; ++m) lds_tie(kr[m]);
-        if constexpr (D == 64) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) lds_tie(vt[t]);
-        } else {
-#pragma unroll
-            for (int m = 0; m < CPR; ++m) lds_tie(vr[m]);
-        }
-#pragma unroll
-        for (int g = 0; g < GROUPS; ++g) {
-            lds_tie(ksw[g]);
-            lds_tie(vsw[g]);
+            ksw[g] = lds_load128(lds_off(&B.ks[0]) + qoff + 16 * g);
+            vsw[g] = lds_load128(lds_off(&B.vs[0]) + qoff + 16 * g);
         }
         SWA_TRACE(2);
-        // the buffer is free again: the chunk NBUF steps ahead starts loading
+        // the buffer is free again once these reads have completed: the chunk
+        // NBUF steps ahead starts loading
+        lds_reads_done();
         if (kk == 0) {
             issue(ci + NW, 1);  // (a step past the end reads row 0, never used)
             if (2 < n_steps) issue(ci + 2 * NW, 0);
@@ -574,7 +517,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
             // builds the two A operands: for quads 0-7, lanes 0-31 keep their
             // group-0 weights and lanes 32-63 receive the group-1 weights of
             // lanes 0-31; for quads 8-15 the other way round.
-            const u32x2_t w0 = __builtin_bit_cast(u32x2_t, pa0), w1 = __builtin_bit_cast(u32x2_t, pa1);
+            const u32x2 w0 = __builtin_bit_cast(u32x2, pa0), w1 = __builtin_bit_cast(u32x2, pa1);
             const auto e0 = __builtin_amdgcn_permlane32_swap(w0[0], w1[0], false, false);
             const auto e1 = __builtin_amdgcn_permlane32_swap(w0[1], w1[1], false, false);
             const half4_t a_lo = __builtin_bit_cast(half4_t, make_uint2(e0[0], e1[0]));  // quads 0-7

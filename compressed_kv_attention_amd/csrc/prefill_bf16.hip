@@ -50,57 +50,6 @@ constexpr int NBUF = 2;  // LDS tile buffers: the tile computed and the next one
 constexpr int kSinkWords = (kMaxT / BN + 31) / 32;
 constexpr float kRescaleSum = 256.0f;  // the reference max moves when a weight sum passes 2^8
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Tiles move global -> LDS by direct loads issued from inline asm, so the
-// compiler does not see them: seen, they would make it wait for every tile in
-// flight before any LDS read (it cannot tell the two buffers apart).  Each
-// wave waits for its own loads (vmcnt) before the barrier that publishes a
-// tile.  Every LDS read is an ordinary load the compiler schedules, waits for
-// and orders against the matrix instructions itself.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// LDS byte offset of a pointer into __shared__ memory, and back (device pass
-// only; the host pass never runs device functions).
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    return __builtin_bit_cast(uint32_t, (__attribute__((address_space(3))) const char*)p);
-#else
-    (void)p;
-    return 0u;
-#endif
-}
-__device__ __forceinline__ u32x4 lds_load128(uint32_t addr) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    return *__builtin_bit_cast(__attribute__((address_space(3))) const u32x4*, addr);
-#else
-    (void)addr;
-    return u32x4{};
-#endif
-}
-// ds_read_b64_tr_b16: the 16-bit transpose read (lane j of each 16-lane group
-// gets element j of the four rows the group's lanes address).
-__device__ __forceinline__ u32x2 lds_load_tr16(uint32_t addr) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    return __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(__builtin_bit_cast(__attribute__((address_space(3))) s16x4*, addr)));
-#else
-    (void)addr;
-    return u32x2{};
-#endif
-}
-// Direct global -> LDS loads: lane l's 16 (or 4) bytes at base + voff land at
-// LDS byte lds + 16 l (or 4 l).  base and lds are wave-uniform.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
-                 : "memory", "m0");
-}
 // Wait for all of this wave's global loads (direct-to-LDS ones included) and
 // LDS accesses, then the workgroup barrier.  The wait is the builtin, not asm,
 // so that the compiler knows every earlier load has completed and inserts no

@@ -66,4 +66,89 @@ __device__ __forceinline__ int wave_reduce_i32(int x) {
 __device__ __forceinline__ int wave_min_i32(int x) { return wave_reduce_i32<false>(x); }
 __device__ __forceinline__ int wave_max_i32(int x) { return wave_reduce_i32<true>(x); }
 
+// ---- LDS staging ---------------------------------------------------------
+// Cache and key tiles move global -> LDS by direct loads issued from inline
+// asm, which the compiler does not see: seen, they would make it wait for
+// every load in flight before any LDS read (it cannot tell buffers apart).
+// A wave waits for its own direct loads with an explicit vmcnt wait.  Every
+// LDS read is an ordinary load that the compiler schedules, waits for and
+// orders against the matrix instructions under its own hazard rules.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// LDS byte address of a pointer into __shared__ memory (device pass only; the
+// host pass never runs device functions).
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(uint32_t, (__attribute__((address_space(3))) const char*)p);
+#else
+    (void)p;
+    return 0u;
+#endif
+}
+__device__ __forceinline__ u32x4 lds_load128(uint32_t addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return *__builtin_bit_cast(__attribute__((address_space(3))) const u32x4*, addr);
+#else
+    (void)addr;
+    return u32x4{};
+#endif
+}
+// ds_read_b64_tr_b16: in each 16-lane group, lane j gets element j of the
+// four 16-bit rows the group's lanes address (row i from lanes 4i..4i+3).
+__device__ __forceinline__ u32x2 lds_load_tr16(uint32_t addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(__builtin_bit_cast(__attribute__((address_space(3))) s16x4*, addr)));
+#else
+    (void)addr;
+    return u32x2{};
+#endif
+}
+// ds_read_b64_tr_b8: in each 16-lane group, lanes 2r and 2r+1 each name 8
+// bytes that together form row r (16 bytes) of an 8 x 16 byte matrix; lane j
+// gets column j (rows 0..7, one byte each, row 0 in the lowest byte).
+__device__ __forceinline__ u32x2 lds_load_tr8(uint32_t addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(__builtin_bit_cast(__attribute__((address_space(3))) i32x2*, addr)));
+#else
+    (void)addr;
+    return u32x2{};
+#endif
+}
+// Direct global -> LDS loads: lane l's 16 (or 4) bytes at base + voff land at
+// LDS byte lds + 16 l (or 4 l).  base and lds must be wave-uniform.  M0 holds
+// the LDS address; the compiler reserves M0 and does not keep values in it
+// across these statements in the kernels here (none of their own code reads
+// M0, which a host test checks on the generated assembly).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// All LDS reads issued so far have completed (before a direct load may
+// overwrite what they read); the compiler sees the wait.
+__device__ __forceinline__ void lds_reads_done() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited for
+    asm volatile("" ::: "memory");
+}
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (direct loads included).  A compiler barrier for memory accesses: no LDS
+// read moves above it.
+template <int N>
+__device__ __forceinline__ void vm_wait_upto() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace swa

@@ -157,3 +157,24 @@ def test_budget_window_host_functions_match_golden_cases():
         assert swa.kv_budget_window(d, nh, nkv, L_, msl, sites, ad) == bw, r
         assert swa.effective_kv_window(d, nh, nkv, L_, msl, kvw, sites, ad) == eff, r
     assert swa.kv_budget_window(0, 16, 4, 12, 100) == -1
+
+
+def test_kernels_leave_m0_to_direct_loads():
+    """The direct global->LDS loads set M0 inside their inline asm; that is
+    only sound while no compiler-generated instruction of the kernels reads M0
+    (the compiler reserves it and would not expect the asm to change it)."""
+    import subprocess
+    import tempfile
+    from compressed_kv_attention_amd import build
+    for src in ("prefill_bf16.hip", "decode.hip"):
+        with tempfile.TemporaryDirectory() as td:
+            out = os.path.join(td, "k.s")
+            cmd = [build._hipcc()] + [f for f in build.compile_flags() if f != "-fPIC"] + [
+                "--cuda-device-only", "-S", os.path.join(build.CSRC, src), "-o", out]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            assert r.returncode == 0, r.stderr[-2000:]
+            text = open(out).read()
+        outside = re.sub(r";;#ASMSTART.*?;;#ASMEND", "", text, flags=re.S)
+        code = [l for l in outside.splitlines() if l.strip() and not l.strip().startswith((";", "."))]
+        users = [l for l in code if re.search(r"\bm0\b", l)]
+        assert not users, f"{src}: compiler-generated code uses M0: {users[:5]}"
