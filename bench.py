@@ -57,16 +57,22 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash(name):
-    """sha256 (first 16 hex digits) of the HIP source a kernel is built from; a counter summary taken on
-    other source no longer describes the kernel."""
+def kernel_source_hash(names):
+    """sha256 (first 16 hex digits) of the HIP sources a kernel is built from (concatenated in the given
+    order); a counter summary taken on other source no longer describes the kernel."""
     import hashlib
-    src = os.path.join(ROOT, "compressed_kv_attention_amd", "csrc", name)
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "compressed_kv_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, source):
+# the files the decode kernel is compiled from (its own source and the device helpers it includes)
+DECODE_SOURCES = ("decode.hip", "swa_common.h", "swa_internal.h")
+
+
+def measured_traffic(kernel, sources):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None when the
     summary is missing or was taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.txt")
@@ -77,7 +83,7 @@ def measured_traffic(kernel, source):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("source_sha256_16") != kernel_source_hash(source):
+    if fields.get("source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -371,7 +377,7 @@ def roofline_decode(dec):
     if not dec:
         return None
     per_launch = dec["bytes_per_layer"]
-    traffic = measured_traffic("decode_kernel", "decode.hip")
+    traffic = measured_traffic("decode_kernel", DECODE_SOURCES)
     return {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(dec["gbs"] / HBM_PEAK_GBS, 5), "traffic": traffic,
             "kernel": "decode_kernel", "bytes_per_launch": per_launch,
