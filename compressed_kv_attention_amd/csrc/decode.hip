@@ -353,9 +353,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
             s_new = all_blocks(d) * c_log2;
         }
     }
-    // (the second chunk is requested once the first has landed: fewer bytes
-    // requested up front make every wave's first chunk arrive sooner)
-    static_assert(NBUF == 2, "issue schedule");
+    // the other buffers' chunks (ring schedule: step kk reads buffer
+    // kk % NBUF, then refills it with step kk + NBUF)
+    for (int k = 1; k < NBUF; ++k)
+        if (k < n_steps) issue(wave + NW * k, k);
     SWA_TRACE(0);
 
     // lane-dependent byte selectors of the quad transpose
@@ -386,8 +387,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         const int ci = wave + NW * kk;
         // this chunk's DMA has landed
         {
-            // issued after chunk kk: chunk kk + 1, at step kk - 1 (steps >= 1)
-            const int younger = (kk >= 1 && kk + 1 < n_steps) ? 1 : 0;
+            // issued after chunk kk and still outstanding: steps kk + 1 .. kk + NBUF - 1
+            const int younger = min(NBUF - 1, n_steps - 1 - kk);
             vm_wait_chunks<NDMA>(younger);
         }
         SWA_TRACE(1);
@@ -419,12 +420,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         // the buffer is free again once these reads have completed: the chunk
         // NBUF steps ahead starts loading
         lds_reads_done();
-        if (kk == 0) {
-            issue(ci + NW, 1);  // (a step past the end reads row 0, never used)
-            if (2 < n_steps) issue(ci + 2 * NW, 0);
-        } else if (kk + 2 < n_steps) {
-            issue(ci + 2 * NW, bi);
-        }
+        if (kk + NBUF < n_steps) issue(ci + NBUF * NW, bi);
 
         // scores: C_g(4b+c, r) = sum over group g of q_c * (1152 + code) - 1152 * sum q_c
         // (the two group chains alternate so consecutive MFMAs are independent)
