@@ -37,6 +37,173 @@ __device__ __forceinline__ void store_elem(void* p, size_t i, float v) {
     else ((float*)p)[i] = v;
 }
 
+// Pooling with 16-byte accesses: one thread per (row group n, block j, tensor
+// K or V, piece c of CH channel pairs): channels i0 .. i0+CH-1 and their
+// rotate-half partners i0 + D/2 .. of the pooled key (rotated) or value.  The
+// same arithmetic, in the same order per element, as the element-wise kernel
+// below.
+template <bool BF16>
+__global__ __launch_bounds__(256) void pool_rope_vec_kernel(long long N, int T, int D, int block, int nblk,
+                                                            const void* k, const void* v, const float* cs,
+                                                            const float* sn, int rope_len, void* pk, void* pv) {
+    constexpr int CH = BF16 ? 8 : 4;  // elements per 16-byte piece
+    constexpr int ES = BF16 ? 2 : 4;  // bytes per element
+    const int half = D / 2;
+    const int per_row = half / CH;  // pieces per half row
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= N * nblk * 2 * per_row) return;
+    const int c = (int)(idx % per_row);
+    const long long t2 = idx / per_row;
+    const bool is_k = (t2 & 1) == 0;
+    const long long nj = t2 >> 1;
+    const int j = (int)(nj % nblk);
+    const long long n = nj / nblk;
+    const int i0 = c * CH;
+    const char* src = (const char*)(is_k ? k : v) + (((size_t)n * T + (size_t)j * block) * D + i0) * ES;
+    float x1[CH], x2[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) x1[e] = x2[e] = 0.f;
+#pragma unroll 4
+    for (int r = 0; r < block; ++r) {
+        const uint4 a = *(const uint4*)(src + (size_t)r * D * ES);
+        const uint4 b = *(const uint4*)(src + ((size_t)r * D + half) * ES);
+        const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
+        if (BF16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x1[2 * i] += __uint_as_float(ua[i] << 16);
+                x1[2 * i + 1] += __uint_as_float(ua[i] & 0xffff0000u);
+                x2[2 * i] += __uint_as_float(ub[i] << 16);
+                x2[2 * i + 1] += __uint_as_float(ub[i] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x1[i] += __uint_as_float(ua[i]);
+                x2[i] += __uint_as_float(ub[i]);
+            }
+        }
+    }
+    const float fb = (float)block;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+        x1[e] /= fb;
+        x2[e] /= fb;
+    }
+    if (is_k && cs) {
+        int mid = j * block + block / 2;
+        if (mid > rope_len - 1) mid = rope_len - 1;
+        const float* cr = cs + (size_t)mid * half + i0;
+        const float* sr = sn + (size_t)mid * half + i0;
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+            const float cc = cr[e], ss = sr[e];
+            const float y1 = x1[e] * cc - x2[e] * ss;
+            const float y2 = x2[e] * cc + x1[e] * ss;
+            x1[e] = y1;
+            x2[e] = y2;
+        }
+    }
+    char* dst = (char*)(is_k ? pk : pv) + (((size_t)n * nblk + j) * D + i0) * ES;
+    uint4 w1, w2;
+    if (BF16) {
+        w1 = make_uint4(pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]), pack_bf16x2(x1[4], x1[5]),
+                        pack_bf16x2(x1[6], x1[7]));
+        w2 = make_uint4(pack_bf16x2(x2[0], x2[1]), pack_bf16x2(x2[2], x2[3]), pack_bf16x2(x2[4], x2[5]),
+                        pack_bf16x2(x2[6], x2[7]));
+    } else {
+        w1 = make_uint4(__float_as_uint(x1[0]), __float_as_uint(x1[1]), __float_as_uint(x1[2]), __float_as_uint(x1[3]));
+        w2 = make_uint4(__float_as_uint(x2[0]), __float_as_uint(x2[1]), __float_as_uint(x2[2]), __float_as_uint(x2[3]));
+    }
+    *(uint4*)dst = w1;
+    *(uint4*)(dst + (size_t)half * ES) = w2;
+}
+
+// Pooling of one block per wave, for long blocks.  A row of K followed by its
+// row of V is PPR 16-byte pieces; lane l loads piece l % PPR of rows l / PPR,
+// l / PPR + RPL, ... of the block (RPL = 64 / PPR rows per step), sums them in
+// fp32, and the partial sums of the RPL row groups are added across lanes
+// (butterfly over lane bits log2(PPR) and up).  Lanes 0 .. PPR-1 then hold the
+// block sums; each divides by b, K pieces exchange with their rotate-half
+// partner piece (lane xor PPR/4) for the rotation, and every piece is stored
+// once.  (The sums associate differently from a sequential loop; each pooled
+// value is still one fp32 sum of b values and one rounding.)
+template <bool BF16>
+__global__ __launch_bounds__(256) void pool_rope_wave_kernel(long long N, int T, int D, int block, int nblk,
+                                                            const void* k, const void* v, const float* cs,
+                                                            const float* sn, int rope_len, void* pk, void* pv) {
+    constexpr int CH = BF16 ? 8 : 4;  // elements per 16-byte piece
+    constexpr int ES = BF16 ? 2 : 4;  // bytes per element
+    const long long wid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wid >= N * nblk) return;
+    const int lane = threadIdx.x & 63;
+    const int j = (int)(wid % nblk);
+    const long long n = wid / nblk;
+    const int kp = D * ES / 16;  // pieces per K row (and per V row)
+    const int ppr = 2 * kp;      // pieces per K+V row pair (a power of two up to 64)
+    const int rpl = 64 / ppr;    // rows per step
+    const int g = lane / ppr, p = lane % ppr;
+    const bool is_k = p < kp;
+    const char* src = (const char*)(is_k ? k : v) + ((size_t)n * T + (size_t)j * block) * D * ES +
+                      (size_t)(is_k ? p : p - kp) * 16;
+    float acc[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc[e] = 0.f;
+    for (int r = g; r < block; r += rpl) {
+        const uint4 w = *(const uint4*)(src + (size_t)r * D * ES);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+        if (BF16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += __uint_as_float(u[i] << 16);
+                acc[2 * i + 1] += __uint_as_float(u[i] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(u[i]);
+        }
+    }
+    for (int o = ppr; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < CH; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+    const float fb = (float)block;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc[e] /= fb;
+    if (cs) {
+        // the rotate-half partner piece (every lane takes part in the exchange)
+        const int hp = kp / 2;  // pieces per half row
+        float other[CH];
+#pragma unroll
+        for (int e = 0; e < CH; ++e) other[e] = __shfl_xor(acc[e], hp, 64);
+        if (is_k) {
+            int mid = j * block + block / 2;
+            if (mid > rope_len - 1) mid = rope_len - 1;
+            const bool first = p < hp;
+            const int i0 = (first ? p : p - hp) * CH;
+            const int half = D / 2;
+#pragma unroll
+            for (int e = 0; e < CH; ++e) {
+                const float c = cs[(size_t)mid * half + i0 + e];
+                const float s = sn[(size_t)mid * half + i0 + e];
+                const float k1 = first ? acc[e] : other[e], k2 = first ? other[e] : acc[e];
+                acc[e] = first ? k1 * c - k2 * s : k2 * c + k1 * s;
+            }
+        }
+    }
+    if (g == 0) {
+        uint4 w;
+        if (BF16) {
+            w = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                           pack_bf16x2(acc[6], acc[7]));
+        } else {
+            w = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                           __float_as_uint(acc[3]));
+        }
+        char* dst = (char*)(is_k ? pk : pv) + ((size_t)n * nblk + j) * D * ES + (size_t)(is_k ? p : p - kp) * 16;
+        *(uint4*)dst = w;
+    }
+}
+
 // One thread per (row group n, block j, channel pair i): channels i and i+D/2
 // of the pooled key and the pooled value.
 template <bool BF16>
@@ -170,8 +337,8 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs p) {
     const uint64_t eq_b = __ballot(!valid || sg == s_first);
     const uint64_t any_b = __ballot(valid && sk);
     const uint64_t all_b = __ballot(!valid || sk);
-    const int smn = wave_imin_xor(valid && sk ? sg : 0x7fffffff, 1, 32);
-    const int smx = wave_imax_xor(valid && sk ? sg : (int)0x80000000, 1, 32);
+    const int smn = wave_min_i32(valid && sk ? sg : 0x7fffffff);
+    const int smx = wave_max_i32(valid && sk ? sg : (int)0x80000000);
     if ((lane & 31) == 0) {
         const uint32_t eq_h = (uint32_t)(eq_b >> (32 * half));
         const uint32_t any_h = (uint32_t)(any_b >> (32 * half));
@@ -214,6 +381,33 @@ hipError_t launch_pool_rope(int B, int H, int T, int D, int block, int dtype, co
                             const float* c, const float* sn, int rope_len, void* pk, void* pv, hipStream_t s) {
     const int nblk = T / block;
     const long long N = (long long)B * H;
+    // 16-byte pieces when a half row is a whole number of them (pointers are
+    // 16-byte aligned: the entry point checks): long blocks one wave per
+    // pooled row, short ones one thread per piece
+    const int ch = dtype == 1 ? 8 : 4;
+    const int pieces = 2 * D * (dtype == 1 ? 2 : 4) / 16;  // per K+V row pair
+    if ((D / 2) % ch == 0 && block >= 8 && pieces <= 64 && (pieces & (pieces - 1)) == 0) {
+        const long long waves = N * nblk;
+        const dim3 gw((unsigned)((waves + 3) / 4));
+        if (dtype == 1)
+            hipLaunchKernelGGL((pool_rope_wave_kernel<true>), gw, dim3(256), 0, s, N, T, D, block, nblk, k_pre, v, c,
+                               sn, rope_len, pk, pv);
+        else
+            hipLaunchKernelGGL((pool_rope_wave_kernel<false>), gw, dim3(256), 0, s, N, T, D, block, nblk, k_pre, v, c,
+                               sn, rope_len, pk, pv);
+        return hipGetLastError();
+    }
+    if ((D / 2) % ch == 0) {
+        const long long nt = N * nblk * 2 * ((D / 2) / ch);
+        const dim3 gv((unsigned)((nt + 255) / 256));
+        if (dtype == 1)
+            hipLaunchKernelGGL((pool_rope_vec_kernel<true>), gv, dim3(256), 0, s, N, T, D, block, nblk, k_pre, v, c, sn,
+                               rope_len, pk, pv);
+        else
+            hipLaunchKernelGGL((pool_rope_vec_kernel<false>), gv, dim3(256), 0, s, N, T, D, block, nblk, k_pre, v, c,
+                               sn, rope_len, pk, pv);
+        return hipGetLastError();
+    }
     const long long n = N * nblk * (D / 2);
     const int threads = 256;
     const dim3 grid((unsigned)((n + threads - 1) / threads));

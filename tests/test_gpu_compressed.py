@@ -53,6 +53,22 @@ def test_pool_kernel(dtype, block, rope_len_short):
         assert excess.max() <= 0
 
 
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pool_kernel_narrow_rows(dtype):
+    """A head dim whose half is not a whole number of 16-byte pieces (D = 36)
+    takes the element-wise pooling kernel."""
+    w = workloads.prefill_case(1, 2, 2, 64, 36, 8, dtype, seed=9)
+    k, v = dev_input(w, "k"), dev_input(w, "v")
+    rope = swa.rope_table(10000.0, w["T"], 36)
+    pk, pv = swa.pool_compress_rope(k, v, 4, rope)
+    torch.cuda.synchronize()
+    rk, rv = oracle.pool_rope(w["k"], w["v"], 4, theta=10000.0, rope_len=w["T"])
+    rtol = 1e-6 if dtype == "f32" else 2.0 ** -8
+    for got, ref in ((pk, rk), (pv, rv)):
+        g = to_np(got)
+        assert (np.abs(g - ref) - (rtol * np.abs(ref) + 1e-6)).max() <= 0
+
 CASES = []
 for dtype in ("f32", "bf16"):
     for i, (B, H, Hkv, T, W, b) in enumerate([(1, 1, 1, 64, 8, 4), (2, 2, 2, 150, 16, 3), (1, 4, 2, 300, 32, 16),
