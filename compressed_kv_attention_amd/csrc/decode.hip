@@ -84,11 +84,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // never used; passing the source itself avoids materialising one.)
 __device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false); }
 __device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false); }
-template <int R>
-__device__ __forceinline__ float quad_bcast(float v) {
-    const int x = __float_as_int(v);
-    return __int_as_float(__builtin_amdgcn_update_dpp(x, x, R * 0x55, 0xF, 0xF, false));
-}
 
 // Four int8 codes -> four f16 values 1152 + code (see kMagic).
 __device__ __forceinline__ half4_t codes_to_h4(uint32_t w) {
@@ -341,16 +336,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         cv = quantize_lane(bf16_bits_to_f32((uint16_t)xv), scv);
         v_new = (float)cv * scv;
         if (has_new) {
+            // every lane forms the whole dot product of its head's q with the
+            // dequantized new key, reading channel ch's value from lane ch
             const float kd = (float)ck * sck;  // dequantized K of channel `lane`
-            const int bq = lane >> 2;
-            const float k4[4] = {quad_bcast<0>(kd), quad_bcast<1>(kd), quad_bcast<2>(kd), quad_bcast<3>(kd)};
             float d = 0.f;
-            if (bq < NI) {
-                const half4_t qv = qb[bq];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) d += (float)qv[e] * k4[e];
-            }
-            s_new = all_blocks(d) * c_log2;
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    d = __builtin_fmaf((float)qb[i][e],
+                                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kd), 4 * i + e)), d);
+            s_new = d * c_log2;
         }
     }
     // the other buffers' chunks (ring schedule: step kk reads buffer
