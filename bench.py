@@ -354,7 +354,7 @@ def main():
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(head.get("frac_mfma_peak", 0.0), 5),
                              "hbm_ceiling_tflops": round(hbm_ceiling(head), 1), "traffic": None,
-                             "kernel": "prefill_bf16_kernel + key_info_kernel + rope_rows_bf16_kernel "
+                             "kernel": "prefill_prep_kernel + prefill_bf16_kernel "
                                        "(one swa_attn_prefill call, needle workload)"},
     }
 
