@@ -159,22 +159,66 @@ def test_budget_window_host_functions_match_golden_cases():
     assert swa.kv_budget_window(0, 16, 4, 12, 100) == -1
 
 
+def _device_asm(src):
+    import subprocess
+    import tempfile
+    from compressed_kv_attention_amd import build
+    with tempfile.TemporaryDirectory() as td:
+        out = os.path.join(td, "k.s")
+        cmd = [build._hipcc()] + [f for f in build.compile_flags() if f != "-fPIC"] + [
+            "--cuda-device-only", "-S", os.path.join(build.CSRC, src), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return open(out).read()
+
+
+def _vgprs(tok):
+    out = set()
+    for m in re.finditer(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b", tok):
+        if m.group(3):
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
 def test_kernels_leave_m0_to_direct_loads():
     """The direct global->LDS loads set M0 inside their inline asm; that is
     only sound while no compiler-generated instruction of the kernels reads M0
     (the compiler reserves it and would not expect the asm to change it)."""
-    import subprocess
-    import tempfile
-    from compressed_kv_attention_amd import build
     for src in ("prefill_bf16.hip", "decode.hip"):
-        with tempfile.TemporaryDirectory() as td:
-            out = os.path.join(td, "k.s")
-            cmd = [build._hipcc()] + [f for f in build.compile_flags() if f != "-fPIC"] + [
-                "--cuda-device-only", "-S", os.path.join(build.CSRC, src), "-o", out]
-            r = subprocess.run(cmd, capture_output=True, text=True)
-            assert r.returncode == 0, r.stderr[-2000:]
-            text = open(out).read()
+        text = _device_asm(src)
         outside = re.sub(r";;#ASMSTART.*?;;#ASMEND", "", text, flags=re.S)
         code = [l for l in outside.splitlines() if l.strip() and not l.strip().startswith((";", "."))]
         users = [l for l in code if re.search(r"\bm0\b", l)]
         assert not users, f"{src}: compiler-generated code uses M0: {users[:5]}"
+
+
+def test_untracked_loads_are_left_alone_until_waited_for():
+    """q and the appended token reach the decode kernel through global loads
+    issued from inline asm, whose registers fill in later than the compiler
+    believes; no instruction may read or write those registers before a
+    vmcnt wait (checked on the generated assembly, in program order)."""
+    text = _device_asm("decode.hip")
+    pending, inasm, bad = {}, False, []
+    for i, line in enumerate(text.splitlines()):
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            inasm = True
+            continue
+        if s.startswith(";;#ASMEND"):
+            inasm = False
+            continue
+        if not s or s.startswith((";", ".")):
+            continue
+        if s.startswith("s_endpgm") or re.match(r"s_waitcnt vmcnt\(", s):
+            pending.clear()
+            continue
+        m = re.match(r"(global_load_\w+)\s+(v\[\d+:\d+\]|v\d+),", s)
+        if m and inasm and "lds" not in m.group(1):
+            for r in _vgprs(m.group(2)):
+                pending[r] = i
+            continue
+        if pending and s[0].isalpha() and _vgprs(s) & set(pending):
+            bad.append(s)
+    assert not bad, f"instructions touch untracked-load registers before their wait: {bad[:5]}"
