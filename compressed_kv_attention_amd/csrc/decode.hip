@@ -168,11 +168,11 @@ __device__ __forceinline__ void vm_wait_chunks(int n) {  // wait until at most n
 // final merge as one more exact softmax partial, so the walk needs no
 // per-lane special case.
 template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(DecodeArgs a) {
     constexpr int NI = D / 4;       // 4-channel instructions per row
     constexpr int GROUPS = D / 32;  // scale groups per row
     constexpr int NW = 2;           // waves per workgroup
-    constexpr int NBUF = 2;         // chunks in flight per wave
+    constexpr int NBUF = 1;         // chunk buffers per wave (three waves per SIMD hide the latency)
     constexpr int CH = 64;          // rows per chunk (one per lane)
     constexpr int CPR = D / 16;     // 16-byte pieces per row
     constexpr int RPI = 64 / CPR;   // rows per DMA instruction
