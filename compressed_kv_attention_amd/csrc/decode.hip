@@ -218,13 +218,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     const int nc_s = (sl + CH - 1) / CH;
     const int n_chunks = nc_s + (n_ring_mem + CH - 1) / CH;
     const float c_log2 = a.scale * kLog2e;
-    // Waves start their walks at different chunks (the softmax does not care
-    // about the order), so the first requests of all waves do not land on the
-    // same offsets of equally sized cache regions at once.  Step ci of the
-    // walk reads chunk (ci + rot) mod n_chunks; steps past the end read
-    // nothing useful.
-    const int rot = n_chunks > 0 ? (int)(blockIdx.x % (unsigned)n_chunks) : 0;
-    auto chunk_of = [&](int ci) { return ci < n_chunks ? (ci + rot) % n_chunks : ci; };
+    // Step ci of the walk reads chunk ci (sinks first, then the ring), so the
+    // two waves of a workgroup read neighbouring chunks at the same time;
+    // steps past the end read nothing useful.  (Starting the workgroups at
+    // different chunks, to spread their first requests, measured slower.)
+    auto chunk_of = [&](int ci) { return ci; };
     // this wave's steps: kk -> walk step wave + NW * kk
     const int n_steps = n_chunks > wave ? (n_chunks - wave + NW - 1) / NW : 0;
     auto rows_of = [&](int cj) { return cj < nc_s ? min(CH, sl - cj * CH) : min(CH, n_ring_mem - (cj - nc_s) * CH); };
