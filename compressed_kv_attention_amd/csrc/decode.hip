@@ -272,23 +272,31 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
             return rr < valid ? row : 0;
         };
         DecBuf<D>& B = sm.buf[wave][bi];
+        // K rows and K scales first, then V rows and V scales: each tensor's
+        // part of the chunk is requested back to back (measured faster than
+        // interleaving K and V pieces)
 #pragma unroll
-        for (int j = 0; j < NKI; ++j) {
-            const int rr = j * RPI + lane / CPR;
-            const int pc = lane % CPR;
-            const int lc = pc ^ ((rr >> 1) & (CPR - 1));  // logical piece stored at slot pc
-            const uint32_t off = (uint32_t)row_of(rr) * D + 16 * lc;
-            // (V stays row-major for D = 64: it is read with transposing reads)
-            const uint32_t voff = D == 64 ? (uint32_t)row_of(rr) * D + 16 * pc : off;
-            dma16(kb, off, lds_off(&B.k[j * 1024]));
-            dma16(vb, voff, lds_off(&B.v[j * 1024]));
-        }
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int j = 0; j < GROUPS; ++j) {
-            const int f = 64 * j + lane;
-            const uint32_t off = (uint32_t)row_of(f / GROUPS) * GROUPS + f % GROUPS;
-            dma4(ksb, off * 4, lds_off(&B.ks[64 * j]));
-            dma4(vsb, off * 4, lds_off(&B.vs[64 * j]));
+            for (int j = 0; j < NKI; ++j) {
+                const int rr = j * RPI + lane / CPR;
+                const int pc = lane % CPR;
+                if (t == 0) {
+                    const int lc = pc ^ ((rr >> 1) & (CPR - 1));  // logical piece stored at slot pc
+                    dma16(kb, (uint32_t)row_of(rr) * D + 16 * lc, lds_off(&B.k[j * 1024]));
+                } else {
+                    // (V stays row-major for D = 64: it is read with transposing reads)
+                    const int lv = D == 64 ? pc : pc ^ ((rr >> 1) & (CPR - 1));
+                    dma16(vb, (uint32_t)row_of(rr) * D + 16 * lv, lds_off(&B.v[j * 1024]));
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < GROUPS; ++j) {
+                const int f = 64 * j + lane;
+                const uint32_t off = (uint32_t)row_of(f / GROUPS) * GROUPS + f % GROUPS;
+                if (t == 0) dma4(ksb, off * 4, lds_off(&B.ks[64 * j]));
+                else dma4(vsb, off * 4, lds_off(&B.vs[64 * j]));
+            }
         }
     };
     // the first chunk now, the rest once q is ready: the first requests of
