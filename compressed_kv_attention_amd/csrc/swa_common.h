@@ -126,12 +126,22 @@ __device__ __forceinline__ u32x2 lds_load_tr8(uint32_t addr) {
 // M0, which a host test checks on the generated assembly).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// (readfirstlane makes the uniformity explicit, so the operands always get
+// scalar registers; it costs nothing on values already held in them)
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t u = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (const void*)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(base)),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(base)),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
