@@ -301,24 +301,27 @@ __device__ __forceinline__ void rope_chunk_bf16(long long row, int i0, int T, in
 }
 
 // One launch for everything a bf16 prefill prepares before attention:
-//   blocks [0, rope_blocks): rotate the keys (one thread per 8-pair chunk);
-//   the other blocks: key metadata, one wave per key tile of 64 keys --
+//   the first blocks: key metadata, one wave per key tile of 64 keys --
 //     info[b][t]     packed segment | sink << 31 of every key
 //     ksub[b][2j+h]  KeySum of keys [64j + 32h, 64j + 32h + 32) ∩ [0, T)
 //     tsink[b][j]    (min, max) segment of the tile's sink keys,
 //                    (INT_MAX, INT_MIN) when it holds none
+//   the other blocks: rotate the keys (one thread per 8-pair chunk).
 // [NW section "KV Sinks for Tools: Pinning Critical Context"]: the packing
 // and sink terms of the mask; the summaries let the attention kernel classify
 // sub-tiles and find the tiles holding sinks without reading every key.
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs p) {
-    if ((long long)blockIdx.x < p.rope_blocks) {
+    // (the metadata blocks come first: their load -> reduce -> store chain is
+    // the longer one, so they start while the rotation blocks stream)
+    const long long meta_blocks = p.info ? ((long long)p.B * p.ntile + 3) / 4 : 0;
+    if ((long long)blockIdx.x >= meta_blocks) {
         const int chunks = p.D / 16;
-        const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+        const long long idx = ((long long)blockIdx.x - meta_blocks) * 256 + threadIdx.x;
         if (idx < p.rope_rows * chunks)
             rope_chunk_bf16(idx / chunks, (int)(idx % chunks) * 8, p.T, p.D, p.x, p.cs, p.sn, p.y);
         return;
     }
-    const long long gt = ((long long)blockIdx.x - p.rope_blocks) * 4 + (threadIdx.x >> 6);
+    const long long gt = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (gt >= (long long)p.B * p.ntile) return;
     const int lane = threadIdx.x & 63;
     const int b = (int)(gt / p.ntile), j = (int)(gt % p.ntile);
