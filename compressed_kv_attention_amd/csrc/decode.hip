@@ -133,15 +133,6 @@ struct DecSmem {
     __device__ float* part_o(int w) { return (float*)&buf[w][0]; }
 };
 
-template <int N>
-__device__ __forceinline__ void vm_wait_chunks(int n) {  // wait until at most n * N loads are outstanding
-    switch (n) {
-        case 0: vm_wait_upto<0>(); break;
-        case 1: vm_wait_upto<N>(); break;
-        case 2: vm_wait_upto<2 * N>(); break;
-        default: vm_wait_upto<3 * N>(); break;
-    }
-}
 
 // v_mfma_f32_4x4x4f16 runs 16 independent 4x4x4 blocks; block b is lanes
 // 4b..4b+3 and, with c = lane % 4, computes
@@ -157,8 +148,10 @@ __device__ __forceinline__ void vm_wait_chunks(int n) {  // wait until at most n
 //
 // A workgroup of NW waves serves one (batch row, kv head, up to 4 query
 // heads); the waves take the chunks of the walk in turn and merge at the end.
-// Rows reach LDS by DMA in coalesced 16-rows-per-instruction pieces with NBUF
-// chunks in flight per wave, and each lane then reads its own row.  The walk
+// Rows reach LDS by DMA in coalesced 16-rows-per-instruction pieces into one
+// chunk buffer per wave, whose K part (rows and scales) and V part are each
+// refilled with the next chunk as soon as they have been read; each lane
+// then reads its own row.  The walk
 // is cut into chunks of 64 rows that lie wholly in the sink cache or wholly
 // in the ring (one base pointer per chunk).
 //
@@ -172,12 +165,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     constexpr int NI = D / 4;       // 4-channel instructions per row
     constexpr int GROUPS = D / 32;  // scale groups per row
     constexpr int NW = 2;           // waves per workgroup
-    constexpr int NBUF = 1;         // chunk buffers per wave (three waves per SIMD hide the latency)
+    constexpr int NBUF = 1;         // chunk buffers per wave (K and V parts refilled separately)
     constexpr int CH = 64;          // rows per chunk (one per lane)
     constexpr int CPR = D / 16;     // 16-byte pieces per row
     constexpr int RPI = 64 / CPR;   // rows per DMA instruction
     constexpr int NKI = CH / RPI;   // DMA instructions per chunk for K (and for V)
-    constexpr int NDMA = 2 * NKI + 2 * GROUPS;  // DMA instructions per chunk
+    constexpr int NDMA_PART = NKI + GROUPS;     // DMA instructions per chunk part (K or V)
+    constexpr int NDMA = 2 * NDMA_PART;         // DMA instructions per chunk
     constexpr float kGrow = 8.0f;   // lazy rescale threshold (log2 units)
     __shared__ __align__(16) DecSmem<D, NW, NBUF> sm;
     SWA_TRACE_DECL
@@ -255,7 +249,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     // DMA of chunk ci into buffer bi: NKI instructions each for K and V (RPI
     // rows of CPR pieces), GROUPS each for the two scale arrays; a chunk past
     // the end reads row 0 of its cache and is never used
-    auto issue = [&](int ci, int bi) {
+    auto issue = [&](int ci, int bi, int part) {
         const int cj = chunk_of(ci);
         const bool sink = cj < nc_s;
         const int j0 = (sink ? cj : cj - nc_s) * CH;
@@ -272,11 +266,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
             return rr < valid ? row : 0;
         };
         DecBuf<D>& B = sm.buf[wave][bi];
-        // K rows and K scales first, then V rows and V scales: each tensor's
-        // part of the chunk is requested back to back (measured faster than
-        // interleaving K and V pieces)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        // part 0: the K rows and K scales, part 1: the V rows and V scales
+        // (each tensor's part of a chunk requested back to back measured
+        // faster than interleaved K and V pieces)
+        {
+            const int t = part;
 #pragma unroll
             for (int j = 0; j < NKI; ++j) {
                 const int rr = j * RPI + lane / CPR;
@@ -301,7 +295,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     };
     // the first chunk now, the rest once q is ready: the first requests of
     // all waves then reach memory ahead of everything else
-    issue(wave, 0);
+    issue(wave, 0, 0);
+    issue(wave, 0, 1);
 
     // q of head c as the B operand: 4 channels per instruction, f16 (q and
     // the new token were loaded before the NDMA DMA instructions of chunk 0)
@@ -355,10 +350,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
             s_new = d * c_log2;
         }
     }
-    // the other buffers' chunks (ring schedule: step kk reads buffer
-    // kk % NBUF, then refills it with step kk + NBUF)
-    for (int k = 1; k < NBUF; ++k)
-        if (k < n_steps) issue(wave + NW * k, k);
     SWA_TRACE(0);
 
     // lane-dependent byte selectors of the quad transpose
@@ -387,12 +378,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     for (int kk = 0; kk < n_steps; ++kk) {
         const int bi = kk % NBUF;
         const int ci = wave + NW * kk;
-        // this chunk's DMA has landed
-        {
-            // issued after chunk kk and still outstanding: steps kk + 1 .. kk + NBUF - 1
-            const int younger = min(NBUF - 1, n_steps - 1 - kk);
-            vm_wait_chunks<NDMA>(younger);
-        }
+        // The K part of this chunk has landed once at most NDMA_PART loads are
+        // outstanding (its V part was requested after it).  The two parts are
+        // read and refilled separately, so the next chunk's K streams in while
+        // this chunk's V arrives and its scores are computed.
+        vm_wait_upto<NDMA_PART>();
         SWA_TRACE(1);
         const DecBuf<D>& B = sm.buf[wave][bi];
         const int nvalid = chunk_rows(ci);
@@ -402,27 +392,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
         const uint32_t vbase = lds_off(&B.v[0]) + 16 * CPR * lane;
 #pragma unroll
         for (int m = 0; m < CPR; ++m) kr[m] = lds_load128(kbase + 16 * (m ^ swz));
-        u32x2 vt[8];  // D = 64: read t -> V codes of rows 8t .. 8t+7 at channel `lane`
-        if constexpr (D == 64) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) vt[t] = lds_load_tr8(lds_off(&B.v[0]) + vt_lane + 512 * t);
-        } else {
-#pragma unroll
-            for (int m = 0; m < CPR; ++m) vr[m] = lds_load128(vbase + 16 * (m ^ swz));
-        }
         // the group scales of the quad's four keys (rows 4b .. 4b+3), [key][group]
         u32x4 ksw[GROUPS], vsw[GROUPS];
         const uint32_t qoff = 16 * GROUPS * (lane >> 2);
 #pragma unroll
-        for (int g = 0; g < GROUPS; ++g) {
-            ksw[g] = lds_load128(lds_off(&B.ks[0]) + qoff + 16 * g);
-            vsw[g] = lds_load128(lds_off(&B.vs[0]) + qoff + 16 * g);
-        }
+        for (int g = 0; g < GROUPS; ++g) ksw[g] = lds_load128(lds_off(&B.ks[0]) + qoff + 16 * g);
         SWA_TRACE(2);
-        // the buffer is free again once these reads have completed: the chunk
-        // NBUF steps ahead starts loading
+        // the K buffers are free again once these reads have completed
         lds_reads_done();
-        if (kk + NBUF < n_steps) issue(ci + NBUF * NW, bi);
+        const bool more = kk + 1 < n_steps;
+        if (more) issue(ci + NW, bi, 0);
 
         // scores: C_g(4b+c, r) = sum over group g of q_c * (1152 + code) - 1152 * sum q_c
         // (the two group chains alternate so consecutive MFMAs are independent)
@@ -446,12 +425,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
         for (int r = 0; r < 4; ++r) {
             const int w0 = r * GROUPS;
             ks0[r] = __uint_as_float(ksw[w0 / 4][w0 % 4]);
-            vs0[r] = __uint_as_float(vsw[w0 / 4][w0 % 4]);
-            if (GROUPS > 1) {
-                const int w1 = w0 + 1;
-                ks1[r] = __uint_as_float(ksw[w1 / 4][w1 % 4]);
-                vs1[r] = __uint_as_float(vsw[w1 / 4][w1 % 4]);
-            }
+            if (GROUPS > 1) ks1[r] = __uint_as_float(ksw[(w0 + 1) / 4][(w0 + 1) % 4]);
         }
         const int kq = lane & ~3;  // chunk row of the quad's key 0
         float sc[4];
@@ -486,13 +460,35 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][r] *= corr[r];
         }
-        // weights of head c on the quad's keys, scaled per V group, as the A operand
+        // weights of head c on the quad's keys
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             p[r] = (kq + r < nvalid) ? __builtin_amdgcn_exp2f(sc[r] - m_c) : 0.f;
             l_c += p[r];
         }
+        // the V part of this chunk: outstanding after it, at most the next K part
+        if (more) vm_wait_upto<NDMA_PART>();
+        else vm_wait_upto<0>();
+        u32x2 vt[8];  // D = 64: read t -> V codes of rows 8t .. 8t+7 at channel `lane`
+        if constexpr (D == 64) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) vt[t] = lds_load_tr8(lds_off(&B.v[0]) + vt_lane + 512 * t);
+        } else {
+#pragma unroll
+            for (int m = 0; m < CPR; ++m) vr[m] = lds_load128(vbase + 16 * (m ^ swz));
+        }
+#pragma unroll
+        for (int g = 0; g < GROUPS; ++g) vsw[g] = lds_load128(lds_off(&B.vs[0]) + qoff + 16 * g);
+        lds_reads_done();
+        if (more) issue(ci + NW, bi, 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int w0 = r * GROUPS;
+            vs0[r] = __uint_as_float(vsw[w0 / 4][w0 % 4]);
+            if (GROUPS > 1) vs1[r] = __uint_as_float(vsw[(w0 + 1) / 4][(w0 + 1) % 4]);
+        }
+        // ... scaled per V group, as the A operand of P V
         const half2_t a0l = cvt_pk_f16(p[0] * vs0[0], p[1] * vs0[1]);
         const half2_t a0h = cvt_pk_f16(p[2] * vs0[2], p[3] * vs0[3]);
         const half4_t pa0 = half4_t{a0l[0], a0l[1], a0h[0], a0h[1]};
