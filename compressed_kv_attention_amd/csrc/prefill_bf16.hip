@@ -251,7 +251,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     int lb = blockIdx.x;
     if ((nblocks & 7) == 0) lb = (blockIdx.x & 7) * (nblocks >> 3) + (blockIdx.x >> 3);
     const int bh = (int)fdiv((uint32_t)lb, a.div_nqb);  // batch row * head groups + head group
-    const int qb = lb - bh * (int)a.div_nqb.d;
+    // Query blocks run in reverse order for odd bh: the dispatcher fills an
+    // XCD's CUs one workgroup each in turn, so a CU receives blocks 32 apart
+    // in this numbering, and the reversal pairs late (costly: more keys
+    // visible) query blocks with early ones on every CU.
+    int qb = lb - bh * (int)a.div_nqb.d;
+    if (bh & 1) qb = (int)a.div_nqb.d - 1 - qb;
     const int b = (int)fdiv((uint32_t)bh, a.div_hg);
     const int hg = bh - b * (int)a.div_hg.d;
     const int hkv = (int)fdiv((uint32_t)hg, a.div_groups);
