@@ -54,8 +54,9 @@ __global__ __launch_bounds__(256) void pool_rope_vec_kernel(long long N, int T, 
     if (idx >= N * nblk * 2 * per_row) return;
     const int c = (int)(idx % per_row);
     const long long t2 = idx / per_row;
-    const bool is_k = (t2 & 1) == 0;
-    const long long nj = t2 >> 1;
+    const long long nrow = N * nblk;  // pooled rows: the first nrow * per_row threads pool K, the rest V
+    const bool is_k = t2 < nrow;
+    const long long nj = is_k ? t2 : t2 - nrow;
     const int j = (int)(nj % nblk);
     const long long n = nj / nblk;
     const int i0 = c * CH;
