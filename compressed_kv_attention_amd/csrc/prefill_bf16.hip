@@ -251,12 +251,15 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     int lb = blockIdx.x;
     if ((nblocks & 7) == 0) lb = (blockIdx.x & 7) * (nblocks >> 3) + (blockIdx.x >> 3);
     const int bh = (int)fdiv((uint32_t)lb, a.div_nqb);  // batch row * head groups + head group
-    // Query blocks run in reverse order for odd bh: the dispatcher fills an
-    // XCD's CUs one workgroup each in turn, so a CU receives blocks 32 apart
-    // in this numbering, and the reversal pairs late (costly: more keys
-    // visible) query blocks with early ones on every CU.
-    int qb = lb - bh * (int)a.div_nqb.d;
-    if (bh & 1) qb = (int)a.div_nqb.d - 1 - qb;
+    // The dispatcher fills an XCD's 32 CUs one workgroup each in turn, so a CU
+    // receives blocks 32 apart in this numbering.  Reversing the query-block
+    // order of every other run of max(32, nqb) blocks pairs late query blocks
+    // (costly: more keys visible) with early ones on every CU; the decision is
+    // taken per (batch row, head group), so the map stays one to one.
+    const int nqb = (int)a.div_nqb.d;
+    int qb = lb - bh * nqb;
+    const int run = nqb >= 32 ? bh : (bh * nqb) >> 5;  // run of the group's first block
+    if (run & 1) qb = nqb - 1 - qb;
     const int b = (int)fdiv((uint32_t)bh, a.div_hg);
     const int hg = bh - b * (int)a.div_hg.d;
     const int hkv = (int)fdiv((uint32_t)hg, a.div_groups);
