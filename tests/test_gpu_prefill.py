@@ -154,6 +154,33 @@ def test_full_size_sampled_rows(make):
     assert_lse_close(lse.cpu().numpy().reshape(-1)[rows], ref_lse, "bf16", make.__name__)
 
 
+
+def test_longest_sequence_sampled_rows():
+    """T at the kernels' limit (131072 keys: 2048 key tiles, so the sink scan
+    walks all 32 of its 64-tile words), with sinks in three places of two
+    segments: every row sees its window band plus the sinks of its own
+    segment that lie before it, up to 130 000 positions back."""
+    T, W = 131072, 256
+    seg = np.ones((1, T), np.int32)
+    seg[0, 70000:] = 2
+    prefix = np.zeros((1, T), np.uint8)
+    prefix[0, :300] = 1            # sinks of segment 1 at its start
+    prefix[0, 40000:40064] = 1     # and in its middle
+    prefix[0, 70000:70500] = 1     # sinks of segment 2 at its start
+    prefix[0, 131000:131010] = 1   # and near the end
+    w = workloads.prefill_case(1, 2, 1, T, 64, W, "bf16", seed=21, seg_ids=seg, prefix=prefix, rope_theta=10000.0)
+    say(f"longest: T{T} W{W} sinks {int(prefix.sum())}")
+    out, lse = run_prefill(w)
+    rng = np.random.default_rng(8)
+    extra = [0, 299, 300, 555, 39999, 40000, 40063, 40064, 40300, 69999, 70000, 70255, 70499, 70500, 70756,
+             100000, 130999, 131000, 131009, 131010, T - 1]
+    rows = sample_rows(rng, 1, 2, T, 400, extra)
+    ref, ref_lse = oracle_rows(w, rows)
+    got = to_np(out).reshape(-1, 64)[rows]
+    assert_close(got, ref, "bf16", "longest")
+    assert_lse_close(lse.cpu().numpy().reshape(-1)[rows], ref_lse, "bf16", "longest")
+
+
 def test_bitwise_deterministic():
     w = workloads.packed(B=4, T=1024)
     a, _ = run_prefill(w)
