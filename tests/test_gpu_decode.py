@@ -70,6 +70,8 @@ def oracle_decode(w, ref, append=True):
     (5, 16, 4, 64, 256, 256, [256, 300, 511, 512, 20000], [256, 256, 100, 0, 256]),
     (2, 4, 2, 64, 1, 0, [0, 9], [0, 0]),                          # W = 1, no sinks
     (3, 4, 2, 64, 37, 11, [11, 47, 48], [11, 11, 11]),            # odd sizes
+    (2, 8, 2, 64, 2048, 448, [700, 90000], [448, 300]),          # long walks: 39 and 37 chunks
+    (2, 4, 1, 32, 1000, 100, [1099, 5000], [100, 77]),          # D = 32, ring wrapping mid-chunk
 ])
 def test_decode_small(B, Hq, Hkv, D, W, S, pos, sink_len):
     w = workloads.decode_case(seed=B * 100 + W, B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, sink_len=sink_len)
