@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void pool_rope_vec_kernel(long long N, int T, 
         const uint4 a = *(const uint4*)(src + (size_t)r * D * ES);
         const uint4 b = *(const uint4*)(src + ((size_t)r * D + half) * ES);
         const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
-        if (BF16) {
+        if constexpr (BF16) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 x1[2 * i] += __uint_as_float(ua[i] << 16);
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void pool_rope_vec_kernel(long long N, int T, 
     }
     char* dst = (char*)(is_k ? pk : pv) + (((size_t)n * nblk + j) * D + i0) * ES;
     uint4 w1, w2;
-    if (BF16) {
+    if constexpr (BF16) {
         w1 = make_uint4(pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]), pack_bf16x2(x1[4], x1[5]),
                         pack_bf16x2(x1[6], x1[7]));
         w2 = make_uint4(pack_bf16x2(x2[0], x2[1]), pack_bf16x2(x2[2], x2[3]), pack_bf16x2(x2[4], x2[5]),
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void pool_rope_wave_kernel(long long N, int T,
     for (int r = g; r < block; r += rpl) {
         const uint4 w = *(const uint4*)(src + (size_t)r * D * ES);
         const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-        if (BF16) {
+        if constexpr (BF16) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 acc[2 * i] += __uint_as_float(u[i] << 16);
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void pool_rope_wave_kernel(long long N, int T,
     }
     if (g == 0) {
         uint4 w;
-        if (BF16) {
+        if constexpr (BF16) {
             w = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
                            pack_bf16x2(acc[6], acc[7]));
         } else {
