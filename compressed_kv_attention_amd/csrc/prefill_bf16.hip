@@ -113,23 +113,46 @@ struct TileLoads {
 // The wave that stages the sub-tile summaries (wave 0 stages the key info).
 constexpr int kMetaWave = 1 % kMfmaWaves;
 
+// Per-wave base addresses of the (batch row, kv head) a workgroup works on,
+// computed once: each tile then only adds its offset.
+struct TileBases {
+    const char* k;      // exact keys: row 0 of this head
+    const char* v;
+    const char* pk;     // pooled keys (compressed mode)
+    const char* pv;
+    const char* info;   // packed key info of this batch row (or null)
+    const char* ksub;   // sub-tile summaries of this batch row
+};
+template <int D>
+__device__ __forceinline__ TileBases tile_bases(const PrefillArgs& a, int b, int hkv) {
+    TileBases t;
+    const size_t head = (size_t)b * a.Hkv + hkv;
+    t.k = (const char*)((const uint16_t*)a.k + head * (size_t)a.T * D);
+    t.v = (const char*)((const uint16_t*)a.v + head * (size_t)a.T * D);
+    t.pk = a.pk ? (const char*)((const uint16_t*)a.pk + head * (size_t)a.nblk * D) : nullptr;
+    t.pv = a.pv ? (const char*)((const uint16_t*)a.pv + head * (size_t)a.nblk * D) : nullptr;
+    t.info = a.kinfo ? (const char*)(a.kinfo + (size_t)b * a.T) : nullptr;
+    t.ksub = a.ksub ? (const char*)(a.ksub + (size_t)b * 2 * a.ntile * 4) : nullptr;
+    return t;
+}
+
 // Issue the global->LDS loads of one tile into buffer `buf`: wave w moves
 // 1 KB of K and 1 KB of V (64 lanes x 16 bytes) per instruction; with key
 // metadata, wave 0 also moves the keys' packed info and kMetaWave the two
-// sub-tile summaries.  Rows past the last key
-// load the last key's row (finite data, masked later).
+// sub-tile summaries.  Rows past the last key load the last key's row
+// (finite data, masked later).
 template <int D>
-__device__ __forceinline__ void issue_tile(const PrefillArgs& a, SmemBf16<D>& sm, uint32_t koff, uint32_t voff, int buf,
-                                           int kind, int tile, int b, int hkv, int wave, int lane) {
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TileBases& tb, SmemBf16<D>& sm, uint32_t koff,
+                                           uint32_t voff, int buf, int kind, int tile, int wave, int lane) {
     using TL = TileLoads<D>;
     constexpr uint32_t kStep = kMfmaWaves * TL::ROWS * D * 2;  // bytes between a wave's loads
     const bool pooled = kind == COL_POOLED;
     const int nkeys = pooled ? a.nblk : a.T;
     const int k0 = tile * BN;
-    const size_t head_off = (((size_t)b * a.Hkv + hkv) * (size_t)nkeys + k0) * D;
     // uniform base pointers (the tile's first row) plus 32-bit per-lane offsets
-    const char* kb = (const char*)((const uint16_t*)(pooled ? a.pk : a.k) + head_off);
-    const char* vb = (const char*)((const uint16_t*)(pooled ? a.pv : a.v) + head_off);
+    const size_t toff = (size_t)k0 * D * 2;
+    const char* kb = (pooled ? tb.pk : tb.k) + toff;
+    const char* vb = (pooled ? tb.pv : tb.v) + toff;
     if (k0 + BN <= nkeys) {
 #pragma unroll
         for (int i = 0; i < TL::LOADS; ++i) {
@@ -147,16 +170,13 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, SmemBf16<D>& sm
             dma16(vb, voff + i * kStep - back, lds_off(&sm.v[buf][ld * 64 * 8]));
         }
     }
-    if (!pooled && a.kinfo) {
+    if (!pooled && tb.info) {
         if (wave == 0) {
-            const char* ib = (const char*)(a.kinfo + (size_t)b * a.T);
             const uint32_t gk = (uint32_t)min(k0 + lane, a.T - 1);
-            dma4(ib, gk * 4, lds_off(&sm.kinfo[buf][0]));
+            dma4(tb.info, gk * 4, lds_off(&sm.kinfo[buf][0]));
         }
-        if (wave == kMetaWave && lane < 2 * 4) {
-            const char* sb = (const char*)(a.ksub + ((size_t)b * 2 * a.ntile + 2 * tile) * 4);
-            dma4(sb, (uint32_t)lane * 4, lds_off(&sm.ksum[buf][0][0]));
-        }
+        if (wave == kMetaWave && lane < 2 * 4)
+            dma4(tb.ksub, (uint32_t)(2 * tile * 4 + lane) * 4, lds_off(&sm.ksum[buf][0][0]));
     }
 }
 
@@ -285,7 +305,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     SWA_TRACE(11);
     TileLoads<D> tl;
     tl.init(wave, lane);
-    if (have0) issue_tile<D>(a, sm, tl.koff, tl.voff, 0, kc, tc, b, hkv, wave, lane);
+    const TileBases tb = tile_bases<D>(a, b, hkv);
+    if (have0) issue_tile<D>(a, tb, sm, tl.koff, tl.voff, 0, kc, tc, wave, lane);
     SWA_TRACE(6);
 
     uint4 raw[D / 16];
@@ -403,7 +424,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         const int nxt = cur ^ 1;
         int kn = 0, tn = 0;
         const bool have_next = it.next(kn, tn);
-        if (have_next) issue_tile<D>(a, sm, tl.koff, tl.voff, nxt, kn, tn, b, hkv, wave, lane);
+        if (have_next) issue_tile<D>(a, tb, sm, tl.koff, tl.voff, nxt, kn, tn, wave, lane);
         SWA_TRACE(1);
 
         if (wave_active) {
