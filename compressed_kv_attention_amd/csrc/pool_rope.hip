@@ -37,37 +37,49 @@ __device__ __forceinline__ void store_elem(void* p, size_t i, float v) {
     else ((float*)p)[i] = v;
 }
 
-// Pooling with 16-byte accesses: one thread per (row group n, block j, tensor
-// K or V, piece c of CH channel pairs): channels i0 .. i0+CH-1 and their
-// rotate-half partners i0 + D/2 .. of the pooled key (rotated) or value.  The
-// same arithmetic, in the same order per element, as the element-wise kernel
-// below.
+// Mean of b values: the fp32 sum divided by b, or multiplied by 1/b when b is
+// a power of two (then the same value).
+__device__ __forceinline__ void scale_by_block(float* x, int n, int block, float inv_b) {
+    if (inv_b != 0.f) {
+        for (int e = 0; e < n; ++e) x[e] *= inv_b;
+    } else {
+        const float fb = (float)block;
+        for (int e = 0; e < n; ++e) x[e] /= fb;
+    }
+}
+inline float pow2_reciprocal(int block) { return (block & (block - 1)) == 0 ? 1.0f / (float)block : 0.f; }
+
+// Pooling with 16-byte accesses: one thread per (block j, tensor K or V,
+// piece c of CH channel pairs) of a row group n: channels i0 .. i0+CH-1 and
+// their rotate-half partners i0 + D/2 .. of the pooled key (rotated) or
+// value.  Grid x covers one row group's pieces (the first half pools K, the
+// second V), grid y the row groups.  The same arithmetic, in the same order
+// per element, as the element-wise kernel below.
 template <bool BF16>
-__global__ __launch_bounds__(256) void pool_rope_vec_kernel(long long N, int T, int D, int block, int nblk,
-                                                            const void* k, const void* v, const float* cs,
+__global__ __launch_bounds__(256) void pool_rope_vec_kernel(int N, int T, int D, int block, int nblk, FastDiv div_pr,
+                                                            float inv_b, const void* k, const void* v, const float* cs,
                                                             const float* sn, int rope_len, void* pk, void* pv) {
     constexpr int CH = BF16 ? 8 : 4;  // elements per 16-byte piece
     constexpr int ES = BF16 ? 2 : 4;  // bytes per element
     const int half = D / 2;
-    const int per_row = half / CH;  // pieces per half row
-    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= N * nblk * 2 * per_row) return;
-    const int c = (int)(idx % per_row);
-    const long long t2 = idx / per_row;
-    const long long nrow = N * nblk;  // pooled rows: the first nrow * per_row threads pool K, the rest V
-    const bool is_k = t2 < nrow;
-    const long long nj = is_k ? t2 : t2 - nrow;
-    const int j = (int)(nj % nblk);
-    const long long n = nj / nblk;
+    const int per_row = (int)div_pr.d;  // pieces per half row
+    const uint32_t per_tensor = (uint32_t)nblk * (uint32_t)per_row;
+    const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
+    if (idx >= 2 * per_tensor) return;
+    const bool is_k = idx < per_tensor;
+    const uint32_t r = is_k ? idx : idx - per_tensor;
+    const int j = (int)fdiv(r, div_pr);
+    const int c = (int)r - j * per_row;
     const int i0 = c * CH;
+    for (int n = blockIdx.y; n < N; n += gridDim.y) {
     const char* src = (const char*)(is_k ? k : v) + (((size_t)n * T + (size_t)j * block) * D + i0) * ES;
     float x1[CH], x2[CH];
 #pragma unroll
     for (int e = 0; e < CH; ++e) x1[e] = x2[e] = 0.f;
 #pragma unroll 4
-    for (int r = 0; r < block; ++r) {
-        const uint4 a = *(const uint4*)(src + (size_t)r * D * ES);
-        const uint4 b = *(const uint4*)(src + ((size_t)r * D + half) * ES);
+    for (int rr = 0; rr < block; ++rr) {
+        const uint4 a = *(const uint4*)(src + (size_t)rr * D * ES);
+        const uint4 b = *(const uint4*)(src + ((size_t)rr * D + half) * ES);
         const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
         if constexpr (BF16) {
 #pragma unroll
@@ -85,12 +97,8 @@ __global__ __launch_bounds__(256) void pool_rope_vec_kernel(long long N, int T, 
             }
         }
     }
-    const float fb = (float)block;
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-        x1[e] /= fb;
-        x2[e] /= fb;
-    }
+    scale_by_block(x1, CH, block, inv_b);
+    scale_by_block(x2, CH, block, inv_b);
     if (is_k && cs) {
         int mid = j * block + block / 2;
         if (mid > rope_len - 1) mid = rope_len - 1;
@@ -118,6 +126,7 @@ __global__ __launch_bounds__(256) void pool_rope_vec_kernel(long long N, int T, 
     }
     *(uint4*)dst = w1;
     *(uint4*)(dst + (size_t)half * ES) = w2;
+    }
 }
 
 // Pooling of one block per wave, for long blocks.  A row of K followed by its
@@ -129,17 +138,18 @@ __global__ __launch_bounds__(256) void pool_rope_vec_kernel(long long N, int T, 
 // partner piece (lane xor PPR/4) for the rotation, and every piece is stored
 // once.  (The sums associate differently from a sequential loop; each pooled
 // value is still one fp32 sum of b values and one rounding.)
+// Grid x covers a row group's blocks (four per workgroup), grid y the row
+// groups.
 template <bool BF16>
-__global__ __launch_bounds__(256) void pool_rope_wave_kernel(long long N, int T, int D, int block, int nblk,
+__global__ __launch_bounds__(256) void pool_rope_wave_kernel(int N, int T, int D, int block, int nblk, float inv_b,
                                                             const void* k, const void* v, const float* cs,
                                                             const float* sn, int rope_len, void* pk, void* pv) {
     constexpr int CH = BF16 ? 8 : 4;  // elements per 16-byte piece
     constexpr int ES = BF16 ? 2 : 4;  // bytes per element
-    const long long wid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid >= N * nblk) return;
+    const int j = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (j >= nblk) return;
     const int lane = threadIdx.x & 63;
-    const int j = (int)(wid % nblk);
-    const long long n = wid / nblk;
+    for (int n = blockIdx.y; n < N; n += gridDim.y) {
     const int kp = D * ES / 16;  // pieces per K row (and per V row)
     const int ppr = 2 * kp;      // pieces per K+V row pair (a power of two up to 64)
     const int rpl = 64 / ppr;    // rows per step
@@ -167,9 +177,7 @@ __global__ __launch_bounds__(256) void pool_rope_wave_kernel(long long N, int T,
     for (int o = ppr; o < 64; o <<= 1)
 #pragma unroll
         for (int e = 0; e < CH; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
-    const float fb = (float)block;
-#pragma unroll
-    for (int e = 0; e < CH; ++e) acc[e] /= fb;
+    scale_by_block(acc, CH, block, inv_b);
     if (cs) {
         // the rotate-half partner piece (every lane takes part in the exchange)
         const int hp = kp / 2;  // pieces per half row
@@ -203,13 +211,14 @@ __global__ __launch_bounds__(256) void pool_rope_wave_kernel(long long N, int T,
         char* dst = (char*)(is_k ? pk : pv) + ((size_t)n * nblk + j) * D * ES + (size_t)(is_k ? p : p - kp) * 16;
         *(uint4*)dst = w;
     }
+    }
 }
 
 // One thread per (row group n, block j, channel pair i): channels i and i+D/2
 // of the pooled key and the pooled value.
 template <bool BF16>
-__global__ void pool_rope_kernel(long long N, int T, int D, int block, int nblk, const void* k, const void* v,
-                                 const float* cs, const float* sn, int rope_len, void* pk, void* pv) {
+__global__ void pool_rope_kernel(long long N, int T, int D, int block, int nblk, float inv_b, const void* k,
+                                 const void* v, const float* cs, const float* sn, int rope_len, void* pk, void* pv) {
     const int half = D / 2;
     const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= N * nblk * half) return;
@@ -226,11 +235,12 @@ __global__ void pool_rope_kernel(long long N, int T, int D, int block, int nblk,
         v1 += load_elem<BF16>(v, o + i);
         v2 += load_elem<BF16>(v, o + i + half);
     }
-    const float fb = (float)block;
-    k1 /= fb;
-    k2 /= fb;
-    v1 /= fb;
-    v2 /= fb;
+    float kv4[4] = {k1, k2, v1, v2};
+    scale_by_block(kv4, 4, block, inv_b);
+    k1 = kv4[0];
+    k2 = kv4[1];
+    v1 = kv4[2];
+    v2 = kv4[3];
     if (cs) {
         int mid = j * block + block / 2;
         if (mid > rope_len - 1) mid = rope_len - 1;
@@ -272,11 +282,10 @@ __global__ void rope_rows_f32_kernel(long long rows, int T, int D, const float* 
 }
 
 // Key rotation of one 8-pair chunk: row `row` of x [rows, D] at position
-// row % T (rotate-half pairs (i, i + D/2)), 16-byte loads and stores.
-__device__ __forceinline__ void rope_chunk_bf16(long long row, int i0, int T, int D, const uint16_t* x,
+// t = row % T (rotate-half pairs (i, i + D/2)), 16-byte loads and stores.
+__device__ __forceinline__ void rope_chunk_bf16(long long row, int t, int i0, int D, const uint16_t* x,
                                                 const float* cs, const float* sn, uint16_t* y) {
     const int half = D / 2;
-    const int t = (int)(row % T);
     const size_t base = (size_t)row * D;
     const uint4 w1 = *(const uint4*)(x + base + i0);
     const uint4 w2 = *(const uint4*)(x + base + half + i0);
@@ -317,9 +326,20 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs p) {
     const long long meta_blocks = p.info ? ((long long)p.B * p.ntile + 3) / 4 : 0;
     if ((long long)blockIdx.x >= meta_blocks) {
         const int chunks = p.D / 16;
-        const long long idx = ((long long)blockIdx.x - meta_blocks) * 256 + threadIdx.x;
-        if (idx < p.rope_rows * chunks)
-            rope_chunk_bf16(idx / chunks, (int)(idx % chunks) * 8, p.T, p.D, p.x, p.cs, p.sn, p.y);
+        if (p.rope_rows * chunks < 0x7fffffffLL) {  // 32-bit indexing
+            const uint32_t idx = ((uint32_t)blockIdx.x - (uint32_t)meta_blocks) * 256u + threadIdx.x;
+            if (idx < (uint32_t)(p.rope_rows * chunks)) {
+                const uint32_t row = idx / (uint32_t)chunks;  // chunks is 2 or 4
+                const uint32_t t = row - fdiv(row, p.div_T) * (uint32_t)p.T;
+                rope_chunk_bf16(row, (int)t, (int)(idx - row * chunks) * 8, p.D, p.x, p.cs, p.sn, p.y);
+            }
+        } else {
+            const long long idx = ((long long)blockIdx.x - meta_blocks) * 256 + threadIdx.x;
+            if (idx < p.rope_rows * chunks) {
+                const long long row = idx / chunks;
+                rope_chunk_bf16(row, (int)(row % p.T), (int)(idx % chunks) * 8, p.D, p.x, p.cs, p.sn, p.y);
+            }
+        }
         return;
     }
     const long long gt = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -385,42 +405,45 @@ hipError_t launch_pool_rope(int B, int H, int T, int D, int block, int dtype, co
                             const float* c, const float* sn, int rope_len, void* pk, void* pv, hipStream_t s) {
     const int nblk = T / block;
     const long long N = (long long)B * H;
+    const float inv_b = pow2_reciprocal(block);
+    // row groups go on grid y (at most 65535; the kernels loop over the rest)
+    const unsigned gy = (unsigned)(N < 65535 ? N : 65535);
     // 16-byte pieces when a half row is a whole number of them (pointers are
     // 16-byte aligned: the entry point checks): long blocks one wave per
     // pooled row, short ones one thread per piece
     const int ch = dtype == 1 ? 8 : 4;
     const int pieces = 2 * D * (dtype == 1 ? 2 : 4) / 16;  // per K+V row pair
-    if ((D / 2) % ch == 0 && block >= 8 && pieces <= 64 && (pieces & (pieces - 1)) == 0) {
-        const long long waves = N * nblk;
-        const dim3 gw((unsigned)((waves + 3) / 4));
+    const long long vec_threads = 2LL * nblk * ((D / 2) / ch);  // per row group
+    if (N <= 0x7fffffff && (D / 2) % ch == 0 && block >= 8 && pieces <= 64 && (pieces & (pieces - 1)) == 0) {
+        const dim3 gw((unsigned)((nblk + 3) / 4), gy);
         if (dtype == 1)
-            hipLaunchKernelGGL((pool_rope_wave_kernel<true>), gw, dim3(256), 0, s, N, T, D, block, nblk, k_pre, v, c,
-                               sn, rope_len, pk, pv);
+            hipLaunchKernelGGL((pool_rope_wave_kernel<true>), gw, dim3(256), 0, s, (int)N, T, D, block, nblk, inv_b,
+                               k_pre, v, c, sn, rope_len, pk, pv);
         else
-            hipLaunchKernelGGL((pool_rope_wave_kernel<false>), gw, dim3(256), 0, s, N, T, D, block, nblk, k_pre, v, c,
-                               sn, rope_len, pk, pv);
+            hipLaunchKernelGGL((pool_rope_wave_kernel<false>), gw, dim3(256), 0, s, (int)N, T, D, block, nblk, inv_b,
+                               k_pre, v, c, sn, rope_len, pk, pv);
         return hipGetLastError();
     }
-    if ((D / 2) % ch == 0) {
-        const long long nt = N * nblk * 2 * ((D / 2) / ch);
-        const dim3 gv((unsigned)((nt + 255) / 256));
+    if (N <= 0x7fffffff && (D / 2) % ch == 0 && vec_threads < 0x7fffffffLL) {
+        const dim3 gv((unsigned)((vec_threads + 255) / 256), gy);
+        const FastDiv div_pr = make_fastdiv((uint32_t)((D / 2) / ch));
         if (dtype == 1)
-            hipLaunchKernelGGL((pool_rope_vec_kernel<true>), gv, dim3(256), 0, s, N, T, D, block, nblk, k_pre, v, c, sn,
-                               rope_len, pk, pv);
+            hipLaunchKernelGGL((pool_rope_vec_kernel<true>), gv, dim3(256), 0, s, (int)N, T, D, block, nblk, div_pr,
+                               inv_b, k_pre, v, c, sn, rope_len, pk, pv);
         else
-            hipLaunchKernelGGL((pool_rope_vec_kernel<false>), gv, dim3(256), 0, s, N, T, D, block, nblk, k_pre, v, c,
-                               sn, rope_len, pk, pv);
+            hipLaunchKernelGGL((pool_rope_vec_kernel<false>), gv, dim3(256), 0, s, (int)N, T, D, block, nblk, div_pr,
+                               inv_b, k_pre, v, c, sn, rope_len, pk, pv);
         return hipGetLastError();
     }
     const long long n = N * nblk * (D / 2);
     const int threads = 256;
     const dim3 grid((unsigned)((n + threads - 1) / threads));
     if (dtype == 1)
-        hipLaunchKernelGGL((pool_rope_kernel<true>), grid, dim3(threads), 0, s, N, T, D, block, nblk, k_pre, v, c, sn,
-                           rope_len, pk, pv);
+        hipLaunchKernelGGL((pool_rope_kernel<true>), grid, dim3(threads), 0, s, N, T, D, block, nblk, inv_b, k_pre, v,
+                           c, sn, rope_len, pk, pv);
     else
-        hipLaunchKernelGGL((pool_rope_kernel<false>), grid, dim3(threads), 0, s, N, T, D, block, nblk, k_pre, v, c, sn,
-                           rope_len, pk, pv);
+        hipLaunchKernelGGL((pool_rope_kernel<false>), grid, dim3(threads), 0, s, N, T, D, block, nblk, inv_b, k_pre, v,
+                           c, sn, rope_len, pk, pv);
     return hipGetLastError();
 }
 

@@ -7,20 +7,20 @@
 // (sections "Two kinds of columns, pooled blocks and exact recent keys" and
 // "Pool before rotating, not after").
 //
-// Work decomposition.  A workgroup of 8 waves owns one (batch, kv head) pair
+// Work decomposition.  A workgroup of 4 waves owns one (batch, kv head) pair
 // and 32 * rbs query rows for hpw query heads of that kv head's GQA group
-// (hpw * rbs = 8); each wave owns 32 rows of one head.  The heads of a group
+// (hpw * rbs = 4); each wave owns 32 rows of one head.  The heads of a group
 // share every K/V tile staged in LDS.  Workgroups are numbered so that each XCD
 // (and its L2) gets a contiguous run of query blocks of the same (batch, kv
 // head), which read overlapping key tiles.
 //
 // Staging.  Key tiles of 64 keys go from global memory straight into LDS
-// (global_load_lds, 16 bytes per lane, no registers), three buffers deep: while
-// tile t is computed, tiles t+1 and t+2 are in flight.  K and V are stored
-// row-major with an XOR swizzle of their 16-byte chunks chosen so that the MFMA
-// operand reads hit distinct banks; V is read column-wise with
-// ds_read_b64_tr_b16.  With RoPE, q is rotated here as it is loaded; the keys
-// arrive already rotated (the library rotates them once, in a pre-pass).
+// (global_load_lds, 16 bytes per lane, no registers), two buffers deep: while
+// tile t is computed, tile t+1 is in flight.  K and V are stored row-major
+// with an XOR swizzle of their 16-byte chunks chosen so that the MFMA operand
+// reads hit distinct banks; V is read column-wise with ds_read_b64_tr_b16.
+// With RoPE, q is rotated here as it is loaded; the keys arrive already
+// rotated (the library rotates them once, in a pre-pass).
 //
 // Per tile each wave works on two 32-key sub-tiles:
 //   S^T = K Q^T      4 x v_mfma_f32_32x32x16_bf16 (keys are the M rows)

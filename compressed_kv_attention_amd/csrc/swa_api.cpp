@@ -183,6 +183,7 @@ int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, 
         pa.T = p->T;
         pa.D = p->D;
         pa.ntile = a.ntile;
+        pa.div_T = swa::make_fastdiv((uint32_t)p->T);
         if (kr) {  // rotate the exact keys once, into the workspace
             pa.rope_rows = (long long)p->B * p->Hkv * p->T;
             pa.rope_blocks = (pa.rope_rows * (p->D / 16) + 255) / 256;

@@ -90,6 +90,7 @@ struct PrepArgs {
     long long rope_blocks;  // ceil(rope_rows * D / 16 / 256)
     long long rope_rows;    // B * Hkv * T
     int B, T, D, ntile;
+    FastDiv div_T;          // T, for rows * D / 16 < 2^31 (else 64-bit indexing)
     const uint16_t* x;  // keys to rotate [rope_rows, D]
     const float* cs;
     const float* sn;

@@ -33,7 +33,8 @@ def oracle_compressed(w, rows=None):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("block,rope_len_short", [(1, False), (3, False), (4, False), (16, False), (4, True)])
+@pytest.mark.parametrize("block,rope_len_short", [(1, False), (3, False), (4, False), (12, False), (16, False),
+                                                  (4, True)])
 def test_pool_kernel(dtype, block, rope_len_short):
     w = workloads.prefill_case(2, 3, 3, 101, 64, 8, dtype, seed=block)
     k, v = dev_input(w, "k"), dev_input(w, "v")
@@ -50,6 +51,23 @@ def test_pool_kernel(dtype, block, rope_len_short):
         g = to_np(got)
         excess = np.abs(g - ref) - (rtol * np.abs(ref) + atol)
         say(f"  {name} b={block}: max abs err {np.abs(g - ref).max():.2e}")
+        assert excess.max() <= 0
+
+
+@pytest.mark.parametrize("block", [4, 8])
+def test_pool_kernel_many_row_groups(block):
+    """More row groups (B * H = 66000) than one grid dimension holds (65535):
+    the pooling kernels loop over the rest.  Short rows keep it small."""
+    w = workloads.prefill_case(1, 66000, 66000, 16, 32, 8, "bf16", seed=40 + block)
+    k, v = dev_input(w, "k"), dev_input(w, "v")
+    rope = swa.rope_table(10000.0, w["T"], 32)
+    pk, pv = swa.pool_compress_rope(k, v, block, rope)
+    torch.cuda.synchronize()
+    rk, rv = oracle.pool_rope(w["k"], w["v"], block, theta=10000.0, rope_len=w["T"])
+    for name, got, ref in (("pooled_k", pk, rk), ("pooled_v", pv, rv)):
+        g = to_np(got)
+        excess = np.abs(g - ref) - (2.0 ** -8 * np.abs(ref) + 1e-6)
+        say(f"  {name} b={block}: max abs err {np.abs(g - ref).max():.2e} (last row group {np.abs(g - ref)[0, -1].max():.2e})")
         assert excess.max() <= 0
 
 
