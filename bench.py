@@ -70,6 +70,8 @@ def kernel_source_hash(names):
 
 # the files the decode kernel is compiled from (its own source and the device helpers it includes)
 DECODE_SOURCES = ("decode.hip", "swa_common.h", "swa_internal.h")
+# the files the kernels of a bf16 prefill call (pre-pass and attention) are compiled from
+PREFILL_SOURCES = ("prefill_bf16.hip", "pool_rope.hip", "swa_common.h", "swa_internal.h", "swa_tiles.h")
 
 
 def measured_traffic(kernel, sources):
@@ -353,7 +355,8 @@ def main():
         "roofline_prefill": {"bound": "mfma", "achieved": round(head.get("tflops", 0.0), 3),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(head.get("frac_mfma_peak", 0.0), 5),
-                             "hbm_ceiling_tflops": round(hbm_ceiling(head), 1), "traffic": None,
+                             "hbm_ceiling_tflops": round(hbm_ceiling(head), 1),
+                             "traffic": measured_traffic("prefill_needle_call", PREFILL_SOURCES),
                              "kernel": "prefill_prep_kernel + prefill_bf16_kernel "
                                        "(one swa_attn_prefill call, needle workload)"},
     }
