@@ -180,6 +180,25 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TileBases
     }
 }
 
+// RoPE table rows q0 .. q0 + 31 (clamped to the table) of cos and of sin,
+// staged by direct loads into the second V buffer as [2][32][D/2] floats
+// (exactly that buffer's 128 D bytes): when every wave of a workgroup rotates
+// the same 32 query rows, the workgroup reads their table rows once.  The
+// buffer is free until the walk's second tile is issued into it.
+template <int D>
+__device__ __forceinline__ void issue_rope_rows(const PrefillArgs& a, SmemBf16<D>& sm, int q0, int wave, int lane) {
+    constexpr int PPR = D / 8;               // 16-byte pieces per table row (D/2 floats)
+    constexpr int NI = 2 * 32 * PPR / 64;    // 1 KB instructions for both tables
+    static_assert(NI * 1024 == (int)sizeof(sm.v[1]), "table rows fill the second V buffer");
+    const uint32_t dst = lds_off(&sm.v[1][0]);
+    for (int i = wave; i < NI; i += kMfmaWaves) {
+        const int id = (i % (NI / 2)) * 64 + lane;  // piece within one table's 32 rows
+        const int row = min(q0 + id / PPR, a.rope_len - 1);
+        dma16(i < NI / 2 ? (const void*)a.rope_cos : (const void*)a.rope_sin,
+              (uint32_t)(row * (D / 2) * 4 + (id % PPR) * 16), dst + i * 1024);
+    }
+}
+
 __device__ __forceinline__ void unpack8(const uint4& x, float* f) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -307,6 +326,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     tl.init(wave, lane);
     const TileBases tb = tile_bases<D>(a, b, hkv);
     if (have0) issue_tile<D>(a, tb, sm, tl.koff, tl.voff, 0, kc, tc, wave, lane);
+    // one 32-row block per workgroup: the table rows go through LDS, once
+    const bool tab_lds = ROPE && a.rbs == 1;
+    if (tab_lds) issue_rope_rows<D>(a, sm, q0, wave, lane);
     SWA_TRACE(6);
 
     uint4 raw[D / 16];
@@ -317,7 +339,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
             raw[c] = row_ok ? *(const uint4*)(qrow + 16 * c + 8 * h) : make_uint4(0, 0, 0, 0);
     }
     float4 rc[D / 32][2], rsn[D / 32][2];
-    if (ROPE && row_ok) {
+    if (ROPE && !tab_lds && row_ok) {
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
             const int d0 = 16 * c + 8 * h;
@@ -345,14 +367,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         if (lane < n_sink_tiles) tsk = *(const int2*)(a.tsink + ((size_t)b * a.ntile + lane) * 2);
     }
 
-    // Q^T operand: lane holds row my_q, channels 16c + 8h .. +7 for each c.
-    bf16x8 qf[D / 16];
-    if (ROPE && row_ok) {
+    if (ROPE && !tab_lds && row_ok) {
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) rotate8(raw[c], raw[c + D / 32], rc[c][0], rc[c][1], rsn[c][0], rsn[c][1]);
     }
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
 
     SWA_TRACE(7);
     const bool row_vis = row_ok && (!plain || seg_q > 0);  // padding rows see nothing
@@ -390,8 +408,34 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 
-    // tile 0 must have landed
+    // tile 0 (and the staged table rows) must have landed
     wait_all_barrier();
+    if (tab_lds) {
+        const uint32_t tab = lds_off(&sm.v[1][0]);
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+            const uint32_t o = (uint32_t)(lq * (D / 2) + 16 * c + 8 * h) * 4;
+            const u32x4 c0 = lds_load128(tab + o), c1 = lds_load128(tab + o + 16);
+            const u32x4 s0 = lds_load128(tab + 64 * D + o), s1 = lds_load128(tab + 64 * D + o + 16);
+            rc[c][0] = __builtin_bit_cast(float4, c0);
+            rc[c][1] = __builtin_bit_cast(float4, c1);
+            rsn[c][0] = __builtin_bit_cast(float4, s0);
+            rsn[c][1] = __builtin_bit_cast(float4, s1);
+        }
+        if (row_ok) {
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c)
+                rotate8(raw[c], raw[c + D / 32], rc[c][0], rc[c][1], rsn[c][0], rsn[c][1]);
+        }
+        // every wave has read the rows before the walk's second tile overwrites them
+        lds_reads_done();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
+    // Q^T operand: lane holds row my_q, channels 16c + 8h .. +7 for each c.
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
     SWA_TRACE(0);
 
     // LDS addresses of the operand reads in the buffer being computed; they
