@@ -75,6 +75,11 @@ for dtype in ("f32", "bf16"):
         (1, 8, 8, 300, 64, 3, "ids", True),
         (1, 16, 2, 97, 64, 500, "one", False),
         (2, 4, 4, 160, 32, 48, "packed", True),
+        # RoPE with every GQA geometry: groups of 8 and 4 (the workgroup's waves share
+        # their rows' table entries; ragged last block), 2 (two row blocks per workgroup)
+        (2, 8, 1, 150, 32, 40, "packed", True),
+        (1, 4, 1, 99, 32, 0, "one", True),
+        (1, 4, 2, 100, 64, 20, "ids", True),
     ]):
         CASES.append(pytest.param(dtype, B, Hq, Hkv, T, D, W, kind, rope, i, id=f"{dtype}-{i}"))
 
