@@ -72,60 +72,60 @@ __global__ __launch_bounds__(256) void pool_rope_vec_kernel(int N, int T, int D,
     const int c = (int)r - j * per_row;
     const int i0 = c * CH;
     for (int n = blockIdx.y; n < N; n += gridDim.y) {
-    const char* src = (const char*)(is_k ? k : v) + (((size_t)n * T + (size_t)j * block) * D + i0) * ES;
-    float x1[CH], x2[CH];
+        const char* src = (const char*)(is_k ? k : v) + (((size_t)n * T + (size_t)j * block) * D + i0) * ES;
+        float x1[CH], x2[CH];
 #pragma unroll
-    for (int e = 0; e < CH; ++e) x1[e] = x2[e] = 0.f;
+        for (int e = 0; e < CH; ++e) x1[e] = x2[e] = 0.f;
 #pragma unroll 4
-    for (int rr = 0; rr < block; ++rr) {
-        const uint4 a = *(const uint4*)(src + (size_t)rr * D * ES);
-        const uint4 b = *(const uint4*)(src + ((size_t)rr * D + half) * ES);
-        const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
+        for (int rr = 0; rr < block; ++rr) {
+            const uint4 a = *(const uint4*)(src + (size_t)rr * D * ES);
+            const uint4 b = *(const uint4*)(src + ((size_t)rr * D + half) * ES);
+            const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
+            if constexpr (BF16) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x1[2 * i] += __uint_as_float(ua[i] << 16);
+                    x1[2 * i + 1] += __uint_as_float(ua[i] & 0xffff0000u);
+                    x2[2 * i] += __uint_as_float(ub[i] << 16);
+                    x2[2 * i + 1] += __uint_as_float(ub[i] & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x1[i] += __uint_as_float(ua[i]);
+                    x2[i] += __uint_as_float(ub[i]);
+                }
+            }
+        }
+        scale_by_block(x1, CH, block, inv_b);
+        scale_by_block(x2, CH, block, inv_b);
+        if (is_k && cs) {
+            int mid = j * block + block / 2;
+            if (mid > rope_len - 1) mid = rope_len - 1;
+            const float* cr = cs + (size_t)mid * half + i0;
+            const float* sr = sn + (size_t)mid * half + i0;
+#pragma unroll
+            for (int e = 0; e < CH; ++e) {
+                const float cc = cr[e], ss = sr[e];
+                const float y1 = x1[e] * cc - x2[e] * ss;
+                const float y2 = x2[e] * cc + x1[e] * ss;
+                x1[e] = y1;
+                x2[e] = y2;
+            }
+        }
+        char* dst = (char*)(is_k ? pk : pv) + (((size_t)n * nblk + j) * D + i0) * ES;
+        uint4 w1, w2;
         if constexpr (BF16) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x1[2 * i] += __uint_as_float(ua[i] << 16);
-                x1[2 * i + 1] += __uint_as_float(ua[i] & 0xffff0000u);
-                x2[2 * i] += __uint_as_float(ub[i] << 16);
-                x2[2 * i + 1] += __uint_as_float(ub[i] & 0xffff0000u);
-            }
+            w1 = make_uint4(pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]), pack_bf16x2(x1[4], x1[5]),
+                            pack_bf16x2(x1[6], x1[7]));
+            w2 = make_uint4(pack_bf16x2(x2[0], x2[1]), pack_bf16x2(x2[2], x2[3]), pack_bf16x2(x2[4], x2[5]),
+                            pack_bf16x2(x2[6], x2[7]));
         } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x1[i] += __uint_as_float(ua[i]);
-                x2[i] += __uint_as_float(ub[i]);
-            }
+            w1 = make_uint4(__float_as_uint(x1[0]), __float_as_uint(x1[1]), __float_as_uint(x1[2]), __float_as_uint(x1[3]));
+            w2 = make_uint4(__float_as_uint(x2[0]), __float_as_uint(x2[1]), __float_as_uint(x2[2]), __float_as_uint(x2[3]));
         }
-    }
-    scale_by_block(x1, CH, block, inv_b);
-    scale_by_block(x2, CH, block, inv_b);
-    if (is_k && cs) {
-        int mid = j * block + block / 2;
-        if (mid > rope_len - 1) mid = rope_len - 1;
-        const float* cr = cs + (size_t)mid * half + i0;
-        const float* sr = sn + (size_t)mid * half + i0;
-#pragma unroll
-        for (int e = 0; e < CH; ++e) {
-            const float cc = cr[e], ss = sr[e];
-            const float y1 = x1[e] * cc - x2[e] * ss;
-            const float y2 = x2[e] * cc + x1[e] * ss;
-            x1[e] = y1;
-            x2[e] = y2;
-        }
-    }
-    char* dst = (char*)(is_k ? pk : pv) + (((size_t)n * nblk + j) * D + i0) * ES;
-    uint4 w1, w2;
-    if constexpr (BF16) {
-        w1 = make_uint4(pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]), pack_bf16x2(x1[4], x1[5]),
-                        pack_bf16x2(x1[6], x1[7]));
-        w2 = make_uint4(pack_bf16x2(x2[0], x2[1]), pack_bf16x2(x2[2], x2[3]), pack_bf16x2(x2[4], x2[5]),
-                        pack_bf16x2(x2[6], x2[7]));
-    } else {
-        w1 = make_uint4(__float_as_uint(x1[0]), __float_as_uint(x1[1]), __float_as_uint(x1[2]), __float_as_uint(x1[3]));
-        w2 = make_uint4(__float_as_uint(x2[0]), __float_as_uint(x2[1]), __float_as_uint(x2[2]), __float_as_uint(x2[3]));
-    }
-    *(uint4*)dst = w1;
-    *(uint4*)(dst + (size_t)half * ES) = w2;
+        *(uint4*)dst = w1;
+        *(uint4*)(dst + (size_t)half * ES) = w2;
     }
 }
 
@@ -150,67 +150,67 @@ __global__ __launch_bounds__(256) void pool_rope_wave_kernel(int N, int T, int D
     if (j >= nblk) return;
     const int lane = threadIdx.x & 63;
     for (int n = blockIdx.y; n < N; n += gridDim.y) {
-    const int kp = D * ES / 16;  // pieces per K row (and per V row)
-    const int ppr = 2 * kp;      // pieces per K+V row pair (a power of two up to 64)
-    const int rpl = 64 / ppr;    // rows per step
-    const int g = lane / ppr, p = lane % ppr;
-    const bool is_k = p < kp;
-    const char* src = (const char*)(is_k ? k : v) + ((size_t)n * T + (size_t)j * block) * D * ES +
-                      (size_t)(is_k ? p : p - kp) * 16;
-    float acc[CH];
+        const int kp = D * ES / 16;  // pieces per K row (and per V row)
+        const int ppr = 2 * kp;      // pieces per K+V row pair (a power of two up to 64)
+        const int rpl = 64 / ppr;    // rows per step
+        const int g = lane / ppr, p = lane % ppr;
+        const bool is_k = p < kp;
+        const char* src = (const char*)(is_k ? k : v) + ((size_t)n * T + (size_t)j * block) * D * ES +
+                          (size_t)(is_k ? p : p - kp) * 16;
+        float acc[CH];
 #pragma unroll
-    for (int e = 0; e < CH; ++e) acc[e] = 0.f;
-    for (int r = g; r < block; r += rpl) {
-        const uint4 w = *(const uint4*)(src + (size_t)r * D * ES);
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-        if constexpr (BF16) {
+        for (int e = 0; e < CH; ++e) acc[e] = 0.f;
+        for (int r = g; r < block; r += rpl) {
+            const uint4 w = *(const uint4*)(src + (size_t)r * D * ES);
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+            if constexpr (BF16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] += __uint_as_float(u[i] << 16);
-                acc[2 * i + 1] += __uint_as_float(u[i] & 0xffff0000u);
-            }
-        } else {
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] += __uint_as_float(u[i] << 16);
+                    acc[2 * i + 1] += __uint_as_float(u[i] & 0xffff0000u);
+                }
+            } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(u[i]);
-        }
-    }
-    for (int o = ppr; o < 64; o <<= 1)
-#pragma unroll
-        for (int e = 0; e < CH; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
-    scale_by_block(acc, CH, block, inv_b);
-    if (cs) {
-        // the rotate-half partner piece (every lane takes part in the exchange)
-        const int hp = kp / 2;  // pieces per half row
-        float other[CH];
-#pragma unroll
-        for (int e = 0; e < CH; ++e) other[e] = __shfl_xor(acc[e], hp, 64);
-        if (is_k) {
-            int mid = j * block + block / 2;
-            if (mid > rope_len - 1) mid = rope_len - 1;
-            const bool first = p < hp;
-            const int i0 = (first ? p : p - hp) * CH;
-            const int half = D / 2;
-#pragma unroll
-            for (int e = 0; e < CH; ++e) {
-                const float c = cs[(size_t)mid * half + i0 + e];
-                const float s = sn[(size_t)mid * half + i0 + e];
-                const float k1 = first ? acc[e] : other[e], k2 = first ? other[e] : acc[e];
-                acc[e] = first ? k1 * c - k2 * s : k2 * c + k1 * s;
+                for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(u[i]);
             }
         }
-    }
-    if (g == 0) {
-        uint4 w;
-        if constexpr (BF16) {
-            w = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                           pack_bf16x2(acc[6], acc[7]));
-        } else {
-            w = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                           __float_as_uint(acc[3]));
+        for (int o = ppr; o < 64; o <<= 1)
+#pragma unroll
+            for (int e = 0; e < CH; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+        scale_by_block(acc, CH, block, inv_b);
+        if (cs) {
+            // the rotate-half partner piece (every lane takes part in the exchange)
+            const int hp = kp / 2;  // pieces per half row
+            float other[CH];
+#pragma unroll
+            for (int e = 0; e < CH; ++e) other[e] = __shfl_xor(acc[e], hp, 64);
+            if (is_k) {
+                int mid = j * block + block / 2;
+                if (mid > rope_len - 1) mid = rope_len - 1;
+                const bool first = p < hp;
+                const int i0 = (first ? p : p - hp) * CH;
+                const int half = D / 2;
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    const float c = cs[(size_t)mid * half + i0 + e];
+                    const float s = sn[(size_t)mid * half + i0 + e];
+                    const float k1 = first ? acc[e] : other[e], k2 = first ? other[e] : acc[e];
+                    acc[e] = first ? k1 * c - k2 * s : k2 * c + k1 * s;
+                }
+            }
         }
-        char* dst = (char*)(is_k ? pk : pv) + ((size_t)n * nblk + j) * D * ES + (size_t)(is_k ? p : p - kp) * 16;
-        *(uint4*)dst = w;
-    }
+        if (g == 0) {
+            uint4 w;
+            if constexpr (BF16) {
+                w = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                               pack_bf16x2(acc[6], acc[7]));
+            } else {
+                w = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                               __float_as_uint(acc[3]));
+            }
+            char* dst = (char*)(is_k ? pk : pv) + ((size_t)n * nblk + j) * D * ES + (size_t)(is_k ? p : p - kp) * 16;
+            *(uint4*)dst = w;
+        }
     }
 }
 
