@@ -35,7 +35,9 @@ def random_structure(rng, B, T, kind):
     if kind == "one":
         seg = np.ones((B, T), np.int32)
     elif kind == "packed":
-        seg, _ = workloads.packed_structure(rng, B, T, prefix_len=0, min_seg=1, max_seg=4, max_pad=T // 4)
+        # (at most T // 2 segments, so that very short rows can be cut)
+        seg, _ = workloads.packed_structure(rng, B, T, prefix_len=0, min_seg=1, max_seg=min(4, max(1, T // 2)),
+                                            max_pad=T // 4)
     else:  # repeated, non-contiguous ids with padding
         seg = rng.integers(0, 3, size=(B, T)).astype(np.int32)
     prefix = (rng.random((B, T)) < 0.08).astype(np.uint8)
@@ -82,6 +84,26 @@ for dtype in ("f32", "bf16"):
         (1, 4, 2, 100, 64, 20, "ids", True),
     ]):
         CASES.append(pytest.param(dtype, B, Hq, Hkv, T, D, W, kind, rope, i, id=f"{dtype}-{i}"))
+
+
+# A seeded sweep over shapes the fixed cases do not reach: every GQA group size
+# 1..8 (3, 5, 6 and 7 included: 3 and 6 leave a wave of the workgroup idle, 5
+# and 7 run one head per wave), T from 1, windows 0, 1 and up to past T.
+SWEEP = []
+_srng = np.random.default_rng(2024)
+for _i in range(32):
+    _G = int(_srng.integers(1, 9))
+    _Hkv = int(_srng.integers(1, 3))
+    _T = int(_srng.choice([1, 2, 31, 33, 63, 65]) if _i % 4 == 0 else _srng.integers(1, 400))
+    _W = int(_srng.choice([0, 1, int(_srng.integers(2, 320))]))
+    SWEEP.append(pytest.param(("f32", "bf16")[_i % 2], int(_srng.integers(1, 3)), _G * _Hkv, _Hkv, _T,
+                              (32, 64)[int(_srng.integers(0, 2))], _W, ("one", "packed", "ids")[_i % 3],
+                              bool(_srng.integers(0, 2)), 500 + _i, id=f"sweep{_i}"))
+
+
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,T,D,W,kind,rope,seed", SWEEP)
+def test_prefill_random_sweep(dtype, B, Hq, Hkv, T, D, W, kind, rope, seed):
+    test_prefill_random_small(dtype, B, Hq, Hkv, T, D, W, kind, rope, seed)
 
 
 @pytest.mark.parametrize("dtype,B,Hq,Hkv,T,D,W,kind,rope,seed", CASES)
