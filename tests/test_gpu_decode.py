@@ -85,6 +85,27 @@ def test_decode_small(B, Hq, Hkv, D, W, S, pos, sink_len):
         np.testing.assert_array_equal(dev[name].cpu().numpy(), r)
 
 
+# A seeded sweep: GQA groups 1, 2, 4, 8, both head dims, rings of 1..400 rows,
+# sink caches of 0..300 rows partly filled, positions from an empty ring (pos =
+# sink_len) to many wraps.
+DEC_SWEEP = []
+_drng = np.random.default_rng(4242)
+for _i in range(20):
+    _B = int(_drng.integers(1, 7))
+    _Hkv = int(_drng.integers(1, 3))
+    _G = int(_drng.choice([1, 2, 4, 8]))
+    _W = int(_drng.integers(1, 401))
+    _S = int(_drng.integers(0, 301))
+    _sl = [int(_drng.integers(0, _S + 1)) for _ in range(_B)]
+    _pos = [sl if _drng.random() < 0.2 else sl + int(_drng.integers(0, 4 * _W + 2)) for sl in _sl]
+    DEC_SWEEP.append(pytest.param(_B, _G * _Hkv, _Hkv, (32, 64)[_i % 2], _W, _S, _pos, _sl, id=f"sweep{_i}"))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,W,S,pos,sink_len", DEC_SWEEP)
+def test_decode_sweep(B, Hq, Hkv, D, W, S, pos, sink_len):
+    test_decode_small(B, Hq, Hkv, D, W, S, pos, sink_len)
+
+
 def test_decode_without_append_and_q0_counts():
     B, Hq, Hkv, D, W, S = 3, 4, 2, 64, 16, 8
     w = workloads.decode_case(seed=77, B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, sink_len=[8, 2, 0])
