@@ -94,9 +94,26 @@ for dtype in ("f32", "bf16"):
         CASES.append(pytest.param(dtype, B, H, Hkv, T, W, b, i, id=f"{dtype}-{i}"))
 
 
+# A seeded sweep: GQA groups 1..4, both head dims, T from 1, windows 1 to past
+# T, blocks 1..20 (vector and wave pooling kernels, remainders T mod b).
+SWEEP = []
+_crng = np.random.default_rng(777)
+for _i in range(16):
+    _Hkv = int(_crng.integers(1, 3))
+    _T = int(_crng.integers(1, 400))
+    SWEEP.append(pytest.param(("f32", "bf16")[_i % 2], int(_crng.integers(1, 3)), int(_crng.integers(1, 5)) * _Hkv,
+                              _Hkv, _T, int(_crng.integers(1, 300)), int(_crng.integers(1, 21)), 600 + _i,
+                              (32, 64)[(_i // 2) % 2], id=f"sweep{_i}"))
+
+
+@pytest.mark.parametrize("dtype,B,H,Hkv,T,W,b,seed,D", SWEEP)
+def test_compressed_sweep(dtype, B, H, Hkv, T, W, b, seed, D):
+    test_compressed_random_small(dtype, B, H, Hkv, T, W, b, seed, D)
+
+
 @pytest.mark.parametrize("dtype,B,H,Hkv,T,W,b,seed", CASES)
-def test_compressed_random_small(dtype, B, H, Hkv, T, W, b, seed):
-    w = workloads.prefill_case(B, H, Hkv, T, 64, W, dtype, seed=300 + seed, rope_theta=10000.0, compress_block=b)
+def test_compressed_random_small(dtype, B, H, Hkv, T, W, b, seed, D=64):
+    w = workloads.prefill_case(B, H, Hkv, T, D, W, dtype, seed=300 + seed, rope_theta=10000.0, compress_block=b)
     say(f"case {dtype} B{B} {H}/{Hkv} T{T} W{W} b{b}")
     out, lse, _, _ = run_compressed(w)
     ref, ref_lse = oracle_compressed(w)
