@@ -135,3 +135,16 @@ def test_decode_full_size_one_layer():
     assert_close(to_np(out), r_out, "bf16", "decode full")
     np.testing.assert_array_equal(dev["ring_k"].cpu().numpy(), rk)
     np.testing.assert_array_equal(dev["ring_vs"].cpu().numpy(), rvs)
+
+
+def test_decode_bitwise_repeatable():
+    """Thirty launches of a full-size decode layer give the same output bits:
+    the two waves' merge through LDS and the appended row follow one order.
+    (Each launch appends the same token at the same ring slot, so every launch
+    sees the same cache.)"""
+    w = workloads.decode_case(seed=9)
+    dev, _ = make_caches(w)
+    first = run_decode(w, dev).view(torch.int16).clone()
+    for i in range(30):
+        out = run_decode(w, dev).view(torch.int16)
+        assert torch.equal(out, first), f"launch {i} differs"
