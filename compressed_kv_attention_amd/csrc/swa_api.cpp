@@ -6,6 +6,7 @@
 // thread-local text of the last error.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -238,6 +239,24 @@ int swa_rope_table(double theta, int rope_len, int D, float* cos_out, float* sin
                       "swa_rope_table launch");
 }
 
+int swa_rope_table_host(double theta, int rope_len, int D, float* cos_out, float* sin_out) {
+    REQUIRE(theta > 0.0 && std::isfinite(theta), "theta must be finite and > 0");
+    REQUIRE(rope_len >= 0, "rope_len must be >= 0 (got %d)", rope_len);
+    REQUIRE(D > 0 && D % 2 == 0, "D must be positive and even (got %d)", D);
+    if (rope_len == 0) return ok();
+    REQUIRE(cos_out != nullptr && sin_out != nullptr, "cos_out and sin_out must not be NULL");
+    const int half = D / 2;
+    for (int i = 0; i < half; ++i) {
+        const double inv_freq = std::pow(theta, -2.0 * (double)i / (double)D);
+        for (int pos = 0; pos < rope_len; ++pos) {
+            const double ang = (double)pos * inv_freq;
+            cos_out[(size_t)pos * half + i] = (float)std::cos(ang);
+            sin_out[(size_t)pos * half + i] = (float)std::sin(ang);
+        }
+    }
+    return ok();
+}
+
 int kv_pool_compress_rope(int B, int H, int T, int D, int block, int dtype, const void* k_pre, const void* v,
                           const float* rope_cos, const float* rope_sin, int rope_len, void* pooled_k, void* pooled_v,
                           void* stream) {
@@ -346,17 +365,18 @@ long long swa_kv_budget_window(long long d_model, long long attn_dim, long long 
     if (d_model <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_layers <= 0 || sites < 0 || max_seq_len <= 0 ||
         attn_dim < 0)
         return -1;
-    const long long budget = 11LL * 1024 * 1024 + 512LL * 1024;  // bytes for the whole KV cache
-    const long long group = 32;                                  // channels per fp32 scale
-    const long long floor_window = 160;
-    const long long head_dim = (attn_dim > 0 ? attn_dim : d_model) / num_heads;
-    const long long kv = num_kv_heads * head_dim;
-    const long long per_pos = num_layers * (2 * kv + 2 * (kv / group) * 4) + sites * (d_model + group * 4);
-    if (per_pos <= 0) return -1;
-    long long w = (budget / per_pos) / group * group;
-    if (w > max_seq_len) w = max_seq_len;
-    if (w < floor_window) w = floor_window;
-    return w;
+    // Bytes one cached position costs: per layer, K and V each hold one int8
+    // code per channel and one fp32 scale per 32 channels; per engram site,
+    // d_model bytes and one 128-byte record.
+    constexpr long long kBudget = (23LL << 20) / 2;  // 11.5 MiB for the whole cache
+    constexpr long long kScaleGroup = 32, kScaleBytes = sizeof(float), kFloor = 160;
+    const long long channels = num_kv_heads * ((attn_dim > 0 ? attn_dim : d_model) / num_heads);
+    const long long codes_and_scales = channels + kScaleBytes * (channels / kScaleGroup);
+    const long long bytes_per_pos = num_layers * 2 * codes_and_scales + sites * (d_model + kScaleGroup * kScaleBytes);
+    if (bytes_per_pos <= 0) return -1;
+    const long long positions = kBudget / bytes_per_pos;
+    const long long window = positions - positions % kScaleGroup;  // whole groups of 32 positions
+    return std::max(kFloor, std::min(window, max_seq_len));          // the floor wins over the cap
 }
 
 long long swa_effective_kv_window(long long d_model, long long attn_dim, long long num_heads, long long num_kv_heads,

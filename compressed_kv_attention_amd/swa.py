@@ -20,6 +20,7 @@ SWA_OK, SWA_ERR_INVALID, SWA_ERR_UNSUPPORTED, SWA_ERR_HIP = 0, 1, 2, 3
 SWA_F32, SWA_BF16 = 0, 1
 
 EXPORTS = ("swa_last_error", "swa_version", "swa_prefill_workspace_size", "swa_attn_prefill", "swa_debug_visibility", "swa_rope_table",
+           "swa_rope_table_host",
            "kv_pool_compress_rope", "swa_kv_quantize", "swa_decode_workspace_size", "swa_attn_decode",
            "swa_kv_budget_window", "swa_effective_kv_window")
 
@@ -64,6 +65,8 @@ def lib():
     L.swa_debug_visibility.restype = I
     L.swa_rope_table.argtypes = [ctypes.c_double, I, I, P, P, P]
     L.swa_rope_table.restype = I
+    L.swa_rope_table_host.argtypes = [ctypes.c_double, I, I, P, P]
+    L.swa_rope_table_host.restype = I
     L.kv_pool_compress_rope.argtypes = [I, I, I, I, I, I, P, P, P, P, I, P, P, P]
     L.kv_pool_compress_rope.restype = I
     L.swa_kv_quantize.argtypes = [LL, I, P, P, P, P]
@@ -105,6 +108,20 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _shape(t, name, shape):
+    """Raise ValueError unless tensor t (if given) has exactly this shape.  The C ABI receives raw pointers and
+    cannot see shapes, so every extent the kernels index with is checked here, before any launch."""
+    if t is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _same_device(ref, *tensors):
+    for name, t in tensors:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
 def _swa_dtype(t):
     if t.dtype == torch.bfloat16:
         return SWA_BF16
@@ -118,6 +135,17 @@ def rope_table(theta: float, rope_len: int, D: int, device="cuda"):
     c = torch.empty((rope_len, D // 2), dtype=torch.float32, device=device)
     s = torch.empty_like(c)
     _check(lib().swa_rope_table(float(theta), int(rope_len), int(D), _ptr(c), _ptr(s), _stream(c)))
+    return c, s
+
+
+def rope_table_host(theta: float, rope_len: int, D: int):
+    """cos/sin tables [rope_len, D/2] as host numpy fp32 arrays, computed by the library on the host
+    (angle pos * theta^(-2i/D) in fp64, rounded once)."""
+    import numpy as np
+    c = np.empty((int(rope_len), int(D) // 2), dtype=np.float32)
+    s = np.empty_like(c)
+    _check(lib().swa_rope_table_host(float(theta), int(rope_len), int(D), c.ctypes.data_as(ctypes.c_void_p),
+                                     s.ctypes.data_as(ctypes.c_void_p)))
     return c, s
 
 
@@ -139,7 +167,28 @@ def prefill(q, k, v, seg_ids=None, prefix=None, window=0, rope=None, pooled_k=No
             compress_block=0, scale=0.0, return_lse=False, out=None, workspace=None):
     """Windowed+sink (or compressed) prefill attention.  q [B,Hq,T,D], k/v [B,Hkv,T,D].
 
-    workspace: optional preallocated buffer (see prefill_workspace); allocated here if needed."""
+    workspace: optional preallocated buffer (see prefill_workspace); allocated here if needed.
+    Shapes are checked first, then devices and dtypes; nothing is launched unless all pass."""
+    cos, sin = rope if rope is not None else (None, None)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D: [B, Hq, T, D] and [B, Hkv, T, D]")
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    _shape(k, "k", (B, Hkv, T, D))
+    _shape(v, "v", (B, Hkv, T, D))
+    _shape(seg_ids, "seg_ids", (B, T))
+    _shape(prefix, "prefix", (B, T))
+    if compress_block:
+        _shape(pooled_k, "pooled_k", (B, Hkv, T // int(compress_block), D))
+        _shape(pooled_v, "pooled_v", (B, Hkv, T // int(compress_block), D))
+    elif pooled_k is not None or pooled_v is not None:
+        raise ValueError("pooled_k / pooled_v are only used with compress_block > 0")
+    if (cos is None) != (sin is None):
+        raise ValueError("rope must be a (cos, sin) pair")
+    rope_len = cos.shape[0] if cos is not None else 0
+    _shape(cos, "rope_cos", (rope_len, D // 2))
+    _shape(sin, "rope_sin", (rope_len, D // 2))
+    _shape(out, "out", (B, Hq, T, D))
     _dev(q, "q")
     _dev(k, "k", q.dtype)
     _dev(v, "v", q.dtype)
@@ -147,10 +196,11 @@ def prefill(q, k, v, seg_ids=None, prefix=None, window=0, rope=None, pooled_k=No
     _dev(prefix, "prefix", torch.uint8)
     _dev(pooled_k, "pooled_k", q.dtype)
     _dev(pooled_v, "pooled_v", q.dtype)
-    cos, sin = rope if rope is not None else (None, None)
     _dev(cos, "rope_cos", torch.float32)
     _dev(sin, "rope_sin", torch.float32)
-    rope_len = cos.shape[0] if cos is not None else 0
+    _dev(out, "out", q.dtype)
+    _same_device(q, ("k", k), ("v", v), ("seg_ids", seg_ids), ("prefix", prefix), ("pooled_k", pooled_k),
+                 ("pooled_v", pooled_v), ("rope_cos", cos), ("rope_sin", sin), ("out", out))
     p = prefill_params(q, k, window, compress_block, rope_len, scale)
     if out is None:
         out = torch.empty_like(q)
@@ -172,6 +222,8 @@ def debug_visibility(B, Hq, Hkv, T, D, window, dtype=torch.bfloat16, seg_ids=Non
                       SWA_BF16 if dtype == torch.bfloat16 else SWA_F32)
     _dev(seg_ids, "seg_ids", torch.int32)
     _dev(prefix, "prefix", torch.uint8)
+    _shape(seg_ids, "seg_ids", (B, T))
+    _shape(prefix, "prefix", (B, T))
     Tk = T + (T // compress_block if compress_block else 0)
     mask = torch.empty((B, T, Tk), dtype=torch.uint8, device=device) if want_mask else None
     count = torch.empty((B, T), dtype=torch.int32, device=device)
@@ -184,11 +236,21 @@ def pool_compress_rope(k_pre, v, block, rope=None, out=None):
     """Mean-pool b-row blocks of k_pre and v ([B,H,T,D]); rotate pooled keys at block midpoints.
 
     out: optional (pooled_k, pooled_v) tensors [B,H,T//block,D] to write into."""
+    if k_pre.dim() != 4:
+        raise ValueError("k_pre must be 4-D: [B, H, T, D]")
+    B, H, T, D = k_pre.shape
+    _shape(v, "v", (B, H, T, D))
+    cos, sin = rope if rope is not None else (None, None)
+    if (cos is None) != (sin is None):
+        raise ValueError("rope must be a (cos, sin) pair")
+    rope_len = cos.shape[0] if cos is not None else 0
+    _shape(cos, "rope_cos", (rope_len, D // 2))
+    _shape(sin, "rope_sin", (rope_len, D // 2))
+    _dev(cos, "rope_cos", torch.float32)
+    _dev(sin, "rope_sin", torch.float32)
     _dev(k_pre, "k_pre")
     _dev(v, "v", k_pre.dtype)
-    B, H, T, D = k_pre.shape
-    cos, sin = rope if rope is not None else (None, None)
-    rope_len = cos.shape[0] if cos is not None else 0
+    _same_device(k_pre, ("v", v), ("rope_cos", cos), ("rope_sin", sin))
     if out is None:
         pk = torch.empty((B, H, T // block, D), dtype=k_pre.dtype, device=k_pre.device)
         pv = torch.empty_like(pk)
@@ -212,29 +274,81 @@ def kv_quantize(x):
     return xq, xs
 
 
-def decode(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos, sink_len=None, k_new=None,
-           v_new=None, scale=0.0, num_splits=0, out=None):
-    """One decode step; appends k_new/v_new into the ring (in place) first.  Returns out [B,Hq,D] bf16."""
+def decode_params(q, ring_k, sink_k, scale=0.0, num_splits=0):
+    B, Hq, D = q.shape
+    Hkv, W = ring_k.shape[1], ring_k.shape[2]
+    S = sink_k.shape[2] if sink_k is not None else 0
+    return DecodeParams(B, Hq, Hkv, D, W, S, float(scale), int(num_splits))
+
+
+def decode_workspace(q, ring_k, sink_k, num_splits=0):
+    """A zero-filled workspace for decode calls of this shape and split count (None when none is needed).
+    The library leaves its counter words zero after every completed call, so it can be reused."""
+    p = decode_params(q, ring_k, sink_k, 0.0, num_splits)
+    n = lib().swa_decode_workspace_size(ctypes.byref(p))
+    return torch.zeros(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def _decode_checks(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos, sink_len, k_new,
+                   v_new, out):
+    if q.dim() != 3 or ring_k.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and ring_k [B, Hkv, W, D]")
+    B, Hq, D = q.shape
+    Hkv, W = ring_k.shape[1], ring_k.shape[2]
+    if D % 32:
+        raise ValueError(f"head dim {D} must be a multiple of 32")
+    _shape(ring_k, "ring_k", (B, Hkv, W, D))
+    _shape(ring_v, "ring_v", (B, Hkv, W, D))
+    _shape(ring_ks, "ring_ks", (B, Hkv, W, D // 32))
+    _shape(ring_vs, "ring_vs", (B, Hkv, W, D // 32))
+    if (sink_k is None) != (sink_v is None) or (sink_k is None) != (sink_ks is None) or \
+            (sink_k is None) != (sink_vs is None):
+        raise ValueError("sink_k, sink_v, sink_ks and sink_vs must all be given or all be None")
+    S = sink_k.shape[2] if sink_k is not None else 0
+    _shape(sink_k, "sink_k", (B, Hkv, S, D))
+    _shape(sink_v, "sink_v", (B, Hkv, S, D))
+    _shape(sink_ks, "sink_ks", (B, Hkv, S, D // 32))
+    _shape(sink_vs, "sink_vs", (B, Hkv, S, D // 32))
+    _shape(pos, "pos", (B,))
+    _shape(sink_len, "sink_len", (B,))
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must both be given or both be None")
+    _shape(k_new, "k_new", (B, Hkv, D))
+    _shape(v_new, "v_new", (B, Hkv, D))
+    _shape(out, "out", (B, Hq, D))
     _dev(q, "q", torch.bfloat16)
     for name, t, dt in (("ring_k", ring_k, torch.int8), ("ring_v", ring_v, torch.int8),
                         ("ring_ks", ring_ks, torch.float32), ("ring_vs", ring_vs, torch.float32),
                         ("sink_k", sink_k, torch.int8), ("sink_v", sink_v, torch.int8),
                         ("sink_ks", sink_ks, torch.float32), ("sink_vs", sink_vs, torch.float32),
                         ("pos", pos, torch.int32), ("sink_len", sink_len, torch.int32),
-                        ("k_new", k_new, torch.bfloat16), ("v_new", v_new, torch.bfloat16)):
+                        ("k_new", k_new, torch.bfloat16), ("v_new", v_new, torch.bfloat16),
+                        ("out", out, torch.bfloat16)):
         _dev(t, name, dt)
-    B, Hq, D = q.shape
-    Hkv, W = ring_k.shape[1], ring_k.shape[2]
-    S = sink_k.shape[2] if sink_k is not None else 0
-    p = DecodeParams(B, Hq, Hkv, D, W, S, float(scale), int(num_splits))
+    _same_device(q, ("ring_k", ring_k), ("ring_v", ring_v), ("ring_ks", ring_ks), ("ring_vs", ring_vs),
+                 ("sink_k", sink_k), ("sink_v", sink_v), ("sink_ks", sink_ks), ("sink_vs", sink_vs), ("pos", pos),
+                 ("sink_len", sink_len), ("k_new", k_new), ("v_new", v_new), ("out", out))
+
+
+def decode(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos, sink_len=None, k_new=None,
+           v_new=None, scale=0.0, num_splits=0, out=None, workspace=None):
+    """One decode step; appends k_new/v_new into the ring (in place) first.  Returns out [B,Hq,D] bf16.
+
+    num_splits: 0 lets the library choose; k > 0 cuts every (sequence, kv head) walk into k parts.
+    workspace: optional zero-filled buffer from decode_workspace(); allocated (zeroed) here if needed."""
+    _decode_checks(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos, sink_len, k_new,
+                   v_new, out)
+    p = decode_params(q, ring_k, sink_k, scale, num_splits)
     ws_bytes = lib().swa_decode_workspace_size(ctypes.byref(p))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = workspace.numel() * workspace.element_size() if (ws_bytes and workspace is not None) else 0
     if out is None:
         out = torch.empty_like(q)
     _check(lib().swa_attn_decode(ctypes.byref(p), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(ring_k), _ptr(ring_v),
                                  _ptr(ring_ks), _ptr(ring_vs), _ptr(sink_k), _ptr(sink_v), _ptr(sink_ks),
-                                 _ptr(sink_vs), _ptr(pos), _ptr(sink_len), _ptr(out), _ptr(ws), ws_bytes,
-                                 _stream(q)))
+                                 _ptr(sink_vs), _ptr(pos), _ptr(sink_len), _ptr(out),
+                                 _ptr(workspace) if ws_len else None, ws_len, _stream(q)))
     return out
 
 

@@ -112,9 +112,19 @@ int swa_debug_visibility(const swa_prefill_params* p, const int32_t* seg_ids, co
 /* ------------------------------------------------------------------------ */
 /* RoPE tables and block pooling.                                            */
 /* ------------------------------------------------------------------------ */
-/* cos_out/sin_out [rope_len, D/2] fp32: angle = pos * theta^(-2i/D),         */
-/* evaluated in fp64 on the device and rounded once to fp32.  D even.         */
+/* [CA §"Pool before rotating, not after"]: RoPE rotates q and the exact keys */
+/* at their own position and each pooled key once, at its block midpoint;    */
+/* these are the tables every rotation here reads.  Pairing is rotate-half   */
+/* over channels (i, i + D/2) with angle = pos * theta^(-2i/D) (the pages    */
+/* do not print the pairing; this is the common convention).                 */
+/* cos_out/sin_out [rope_len, D/2] fp32, row pos, column i.  D even.          */
+/* Device variant: DEVICE pointers, angles in fp64 on the device, each value  */
+/* rounded once to fp32, enqueued on `stream`.                                */
 int swa_rope_table(double theta, int rope_len, int D, float* cos_out, float* sin_out, void* stream);
+/* Host variant: HOST pointers, angles in fp64 on the host, rounded once to   */
+/* fp32, computed before the call returns (no device work).  The two agree to */
+/* within one fp32 ulp (the two fp64 libraries may round differently).        */
+int swa_rope_table_host(double theta, int rope_len, int D, float* cos_out, float* sin_out);
 
 /* [CA §"Pool before rotating, not after"]: pooled_k[j] and pooled_v[j] are   */
 /* the means of rows j*b .. j*b+b-1 of k_pre (the key BEFORE RoPE) and v;     */

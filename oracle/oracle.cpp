@@ -293,40 +293,44 @@ void oracle_compressed_prefill(int B, int Hq, int Hkv, int T, int D, const doubl
 }
 
 // O5: budget window.  [NW §"Effective KV Window: Bounding the Cache Size"]
-// and [NS §"256 这个窗口宽度从哪来：内存预算计算器"]:
-//   head_dim = (attn_dim or d_model) // num_heads; kv = num_kv_heads * head_dim
-//   per_pos  = L * (2*kv + 2*(kv // 32)*4) + sites * (d_model + 32*4)
-//   window   = (budget // per_pos) // 32 * 32
-//   budget window = max(160, min(window, max_seq_len))
-// with budget = 11 MiB + 512 KiB.  attn_dim == 0 means "unset".
+// and [NS §"256 这个窗口宽度从哪来：内存预算计算器"], restated: the whole KV
+// cache gets a fixed budget of 11.5 MiB.  One cached position costs, in every
+// layer, one byte per K and per V channel plus one 4-byte scale per group of
+// 32 channels of each; every engram site adds d_model bytes plus 128.  The
+// channel count is num_kv_heads times the head size, the head size being
+// attn_dim (or d_model when attn_dim is unset, 0) divided by num_heads.  The
+// budget window is the largest multiple of 32 positions whose cache fits the
+// budget, capped at max_seq_len, with a floor of 160 that wins over the cap.
+// The effective window is the smaller of that and a set kv_window.
 long long oracle_kv_budget_per_pos(long long d_model, long long attn_dim, long long num_heads,
                                    long long num_kv_heads, long long num_layers, long long sites) {
-    const long long kv_group = 32;
-    const long long head_dim = (attn_dim ? attn_dim : d_model) / num_heads;
-    const long long kv = num_kv_heads * head_dim;
-    return num_layers * (2 * kv + 2 * (kv / kv_group) * 4) + sites * (d_model + kv_group * 4);
+    const long long group = 32;          // channels sharing one fp32 scale
+    const long long scale_bytes = 4;     // one fp32 scale
+    const long long head_size = (attn_dim != 0 ? attn_dim : d_model) / num_heads;
+    const long long channels = num_kv_heads * head_size;
+    const long long one_tensor = channels * 1 + (channels / group) * scale_bytes;  // int8 codes + scales
+    const long long per_layer = 2 * one_tensor;                                    // K and V
+    const long long per_site = d_model + group * scale_bytes;
+    return num_layers * per_layer + sites * per_site;
 }
 long long oracle_kv_budget_window(long long d_model, long long attn_dim, long long num_heads,
                                   long long num_kv_heads, long long num_layers, long long sites,
                                   long long max_seq_len) {
     const long long budget_bytes = 11LL * 1024 * 1024 + 512LL * 1024;
-    const long long kv_group = 32;
-    const long long window_min = 160;
     const long long per_pos =
         oracle_kv_budget_per_pos(d_model, attn_dim, num_heads, num_kv_heads, num_layers, sites);
-    long long window = (budget_bytes / per_pos) / kv_group * kv_group;
-    long long capped = window < max_seq_len ? window : max_seq_len;
-    return capped > window_min ? capped : window_min;
+    // largest multiple of 32 positions that fits: 32 * floor(budget / (32 * per_pos))
+    const long long fits = 32 * (budget_bytes / (32 * per_pos));
+    if (fits <= 160 || max_seq_len <= 160) return 160;
+    return fits < max_seq_len ? fits : max_seq_len;
 }
-// effective window: min(budget window, kv_window) when kv_window is set
-// (non-zero), else the budget window.
+// effective window: the budget window, or kv_window when one is set and smaller
 long long oracle_effective_kv_window(long long d_model, long long attn_dim, long long num_heads,
                                      long long num_kv_heads, long long num_layers, long long sites,
                                      long long max_seq_len, long long kv_window) {
     const long long budget = oracle_kv_budget_window(d_model, attn_dim, num_heads, num_kv_heads,
                                                      num_layers, sites, max_seq_len);
-    if (kv_window) return budget < kv_window ? budget : kv_window;
-    return budget;
+    return (kv_window != 0 && kv_window < budget) ? kv_window : budget;
 }
 
 // O6: int8 quantizer with one fp32 scale per 32 channels (the cache layout

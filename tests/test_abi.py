@@ -222,3 +222,109 @@ def test_untracked_loads_are_left_alone_until_waited_for():
         if pending and s[0].isalpha() and _vgprs(s) & set(pending):
             bad.append(s)
     assert not bad, f"instructions touch untracked-load registers before their wait: {bad[:5]}"
+
+
+def test_rope_table_host_matches_fp64_angles():
+    """Host table = cos/sin of pos * theta^(-2i/D) evaluated in fp64 and rounded
+    once to fp32 (within one fp32 ulp: numpy's fp64 cos/sin and the C library's
+    may round the last bit differently)."""
+    import numpy as np
+    for theta, T, D in ((10000.0, 4096, 64), (500.0, 300, 32), (1e6, 17, 36)):
+        c, s = swa.rope_table_host(theta, T, D)
+        i = np.arange(D // 2, dtype=np.float64)
+        ang = np.arange(T, dtype=np.float64)[:, None] * theta ** (-2.0 * i / D)[None, :]
+        for got, ref in ((c, np.cos(ang)), (s, np.sin(ang))):
+            ref32 = ref.astype(np.float32)
+            ulp = np.spacing(np.abs(ref32)).astype(np.float64)
+            assert np.all(np.abs(got.astype(np.float64) - ref32.astype(np.float64)) <= ulp)
+        assert np.all(c[0] == 1.0) and np.all(s[0] == 0.0)      # position 0 is the identity
+
+
+def test_rope_table_host_validation():
+    L = swa.lib()
+    assert L.swa_rope_table_host(0.0, 4, 64, FAKE, FAKE) == swa.SWA_ERR_INVALID
+    assert L.swa_rope_table_host(1e4, 4, 63, FAKE, FAKE) == swa.SWA_ERR_INVALID
+    assert L.swa_rope_table_host(1e4, -1, 64, FAKE, FAKE) == swa.SWA_ERR_INVALID
+    assert L.swa_rope_table_host(1e4, 4, 64, None, FAKE) == swa.SWA_ERR_INVALID
+    assert L.swa_rope_table_host(1e4, 0, 64, None, None) == swa.SWA_OK
+
+
+# The binding checks every tensor's full shape before any launch (the C ABI
+# sees raw pointers only); CPU tensors suffice: shape errors come first, then
+# the device check, so nothing here reaches the library's kernels.
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _prefill_kw(**over):
+    import torch
+    kw = dict(q=_t(2, 4, 64, 64), k=_t(2, 2, 64, 64), v=_t(2, 2, 64, 64),
+              seg_ids=_t(2, 64, dtype=torch.int32), prefix=_t(2, 64, dtype=torch.uint8), window=16)
+    kw.update(over)
+    return kw
+
+
+@pytest.mark.parametrize("over,what", [
+    (dict(v=_t(2, 2, 63, 64)), "v"),
+    (dict(k=_t(2, 2, 64, 32)), "k"),
+    (dict(seg_ids=_t(2, 65, dtype=__import__("torch").int32)), "seg_ids"),
+    (dict(prefix=_t(1, 64, dtype=__import__("torch").uint8)), "prefix"),
+    (dict(out=_t(2, 4, 64, 32)), "out"),
+    (dict(rope=(_t(64, 16, dtype=__import__("torch").float32), _t(64, 32, dtype=__import__("torch").float32))),
+     "rope_cos"),
+    (dict(compress_block=4, seg_ids=None, prefix=None, pooled_k=_t(2, 2, 16, 64), pooled_v=_t(2, 2, 15, 64)),
+     "pooled_v"),
+])
+def test_prefill_wrapper_rejects_bad_shapes(over, what):
+    with pytest.raises(ValueError, match=what):
+        swa.prefill(**_prefill_kw(**over))
+
+
+def test_prefill_wrapper_rejects_host_tensors_after_shapes():
+    with pytest.raises(ValueError, match="device tensor"):
+        swa.prefill(**_prefill_kw())
+
+
+def _decode_args(**over):
+    import torch
+    B, Hq, Hkv, D, W, S = 3, 8, 2, 64, 16, 8
+    a = dict(q=_t(B, Hq, D), ring_k=_t(B, Hkv, W, D, dtype=torch.int8), ring_v=_t(B, Hkv, W, D, dtype=torch.int8),
+             ring_ks=_t(B, Hkv, W, 2, dtype=torch.float32), ring_vs=_t(B, Hkv, W, 2, dtype=torch.float32),
+             sink_k=_t(B, Hkv, S, D, dtype=torch.int8), sink_v=_t(B, Hkv, S, D, dtype=torch.int8),
+             sink_ks=_t(B, Hkv, S, 2, dtype=torch.float32), sink_vs=_t(B, Hkv, S, 2, dtype=torch.float32),
+             pos=_t(B, dtype=torch.int32), sink_len=_t(B, dtype=torch.int32), k_new=_t(B, Hkv, D),
+             v_new=_t(B, Hkv, D))
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("over,what", [
+    (dict(ring_v=_t(3, 2, 15, 64, dtype=__import__("torch").int8)), "ring_v"),
+    (dict(ring_ks=_t(3, 2, 16, 1, dtype=__import__("torch").float32)), "ring_ks"),
+    (dict(sink_vs=_t(3, 2, 9, 2, dtype=__import__("torch").float32)), "sink_vs"),
+    (dict(sink_k=_t(3, 2, 8, 32, dtype=__import__("torch").int8)), "sink_k"),
+    (dict(pos=_t(4, dtype=__import__("torch").int32)), "pos"),
+    (dict(sink_len=_t(2, dtype=__import__("torch").int32)), "sink_len"),
+    (dict(k_new=_t(3, 1, 64)), "k_new"),
+    (dict(v_new=None), "k_new and v_new"),
+    (dict(sink_v=None), "sink_k, sink_v"),
+    (dict(out=_t(3, 8, 32)), "out"),
+])
+def test_decode_wrapper_rejects_bad_shapes(over, what):
+    with pytest.raises(ValueError, match=what):
+        swa.decode(**_decode_args(**over))
+
+
+def test_decode_wrapper_rejects_host_tensors_after_shapes():
+    with pytest.raises(ValueError, match="device tensor"):
+        swa.decode(**_decode_args())
+
+
+def test_pool_wrapper_rejects_bad_shapes():
+    import torch
+    with pytest.raises(ValueError, match="v must have shape"):
+        swa.pool_compress_rope(_t(1, 2, 32, 64), _t(1, 2, 31, 64), 4)
+    with pytest.raises(ValueError, match="rope_cos"):
+        swa.pool_compress_rope(_t(1, 2, 32, 64), _t(1, 2, 32, 64), 4,
+                               rope=(_t(32, 16, dtype=torch.float32), _t(32, 32, dtype=torch.float32)))
