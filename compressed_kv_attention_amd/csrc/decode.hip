@@ -53,6 +53,11 @@ typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ half2_t cvt_pk_f16(float lo, float hi) {
     return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
+// fp32 pair -> f16 pair, round to nearest even (one v_cvt_pk_f16_f32): the
+// weight operands, whose rounding errors then carry no bias.
+__device__ __forceinline__ half2_t cvt_pk_f16_rne(float lo, float hi) {
+    return half2_t{(_Float16)lo, (_Float16)hi};
+}
 
 // int8 codes -> f16 without conversion instructions: a code c is stored as the
 // byte u = c ^ 0x80 = c + 128, and the f16 with bits 0x64uu is exactly
@@ -128,7 +133,8 @@ struct DecSmem {
     // chunks in flight, per wave; after its walk a wave leaves its per-head
     // outputs (before normalisation, [4][D] floats) in its own first buffer
     DecBuf<D> buf[NW][NBUF];
-    float part_m[NW][4], part_l[NW][4], part_ws[NW][4][D / 32];
+    float part_m[NW][4], part_l[NW][4];
+    int last;  // this workgroup is the last of its unit to finish (split-K)
     static_assert(sizeof(DecBuf<D>) >= 4 * D * sizeof(float), "partials fit a chunk buffer");
     __device__ float* part_o(int w) { return (float*)&buf[w][0]; }
 };
@@ -173,6 +179,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     constexpr int NDMA_PART = NKI + GROUPS;     // DMA instructions per chunk part (K or V)
     constexpr int NDMA = 2 * NDMA_PART;         // DMA instructions per chunk
     constexpr float kGrow = 8.0f;   // lazy rescale threshold (log2 units)
+    constexpr int kNoExp = -100000; // "no V scale seen yet"
     __shared__ __align__(16) DecSmem<D, NW, NBUF> sm;
     SWA_TRACE_DECL
 
@@ -181,9 +188,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     const int c = lane & 3;  // head of this lane's softmax quantities
     const int G = a.Hq / a.Hkv;
     const int nsub = (G + 3) / 4;
-    const int hs = blockIdx.x % nsub;
-    const int b = (blockIdx.x / nsub) / a.Hkv;
-    const int hkv = (blockIdx.x / nsub) % a.Hkv;
+    // workgroup -> (unit = (batch row, kv head, group of 4 query heads), split)
+    const int splits = a.num_splits;
+    const int sp = blockIdx.x % splits;
+    const int unit = blockIdx.x / splits;
+    const int hs = unit % nsub;
+    const int b = (unit / nsub) / a.Hkv;
+    const int hkv = (unit / nsub) % a.Hkv;
     const int h0 = hkv * G + hs * 4;    // first query head of this wave
     const int nh = min(4, G - hs * 4);  // heads served (padding heads have q = 0)
     const int W = a.W, S = a.S;
@@ -203,15 +214,26 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     const bool append = a.k_new != nullptr && pos >= 0;
 
     // rows: sinks [0, sl), then ring positions [first, pos]; with an append
-    // the last of them (position pos) is merged from LDS at the end
+    // the last of them (position pos) is merged from registers at the end
     const int first = max(sl, pos - W + 1);
     const int n_ring = pos >= first ? pos - first + 1 : 0;
     const bool has_new = append && n_ring > 0;
     const int n_ring_mem = n_ring - (has_new ? 1 : 0);  // ring rows read from the cache
     const int first_slot = first >= 0 ? first % W : 0;
-    const int nc_s = (sl + CH - 1) / CH;
-    const int n_chunks = nc_s + (n_ring_mem + CH - 1) / CH;
-    const float c_log2 = a.scale * kLog2e;
+    // This split's share of the walk over the sl + n_ring_mem cached rows:
+    // rows [r0, r1), whole 16-row pieces, cut into its sink part [s0, s1) and
+    // its ring part [g0, g1) (ring rows counted from position `first`).
+    int r0 = 0, r1 = sl + n_ring_mem;
+    if (splits > 1) {
+        const int per = (((r1 + splits - 1) / splits) + 15) & ~15;
+        r0 = min(sp * per, r1);
+        r1 = min(r0 + per, r1);
+    }
+    const int s0 = min(r0, sl), s1 = min(r1, sl);
+    const int g0 = max(r0, sl) - sl, g1 = max(r1, sl) - sl;
+    const int nc_s = (s1 - s0 + CH - 1) / CH;
+    const int n_chunks = nc_s + (g1 - g0 + CH - 1) / CH;
+    const float c_log2_all = a.scale * kLog2e;
     // Step ci of the walk reads chunk ci (sinks first, then the ring), so the
     // two waves of a workgroup read neighbouring chunks at the same time;
     // steps past the end read nothing useful.  (Starting the workgroups at
@@ -219,9 +241,20 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     auto chunk_of = [&](int ci) { return ci; };
     // this wave's steps: kk -> walk step wave + NW * kk
     const int n_steps = n_chunks > wave ? (n_chunks - wave + NW - 1) / NW : 0;
-    auto rows_of = [&](int cj) { return cj < nc_s ? min(CH, sl - cj * CH) : min(CH, n_ring_mem - (cj - nc_s) * CH); };
+    auto first_row_of = [&](int cj) { return cj < nc_s ? s0 + cj * CH : g0 + (cj - nc_s) * CH; };
+    auto rows_of = [&](int cj) { return min(CH, (cj < nc_s ? s1 : g1) - first_row_of(cj)); };
     auto chunk_rows = [&](int ci) { return rows_of(chunk_of(ci)); };
 
+    // per-head maxima over the wave's lanes of head c (lane bits 2..5), made
+    // wave-uniform (every quad holds the same four rows' scales)
+    auto all_blocks_umax = [](uint32_t x) {
+        x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x124, 0xF, 0xF, false));
+        x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xF, 0xF, false));
+        const auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        x = max(s16[0], s16[1]);
+        const auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return __builtin_amdgcn_readfirstlane(max(s32[0], s32[1]));
+    };
     // per-head sums over the wave's lanes of head c (lane bits 2..5)
     auto all_blocks = [](float x) {
         x += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x124, 0xF, 0xF, false));
@@ -247,23 +280,24 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     uint32_t xk = gload_u16_untracked(kn_src + lane % D), xv = gload_u16_untracked(vn_src + lane % D);
 
     // DMA of chunk ci into buffer bi: NKI instructions each for K and V (RPI
-    // rows of CPR pieces), GROUPS each for the two scale arrays; a chunk past
-    // the end reads row 0 of its cache and is never used
+    // rows of CPR pieces), GROUPS each for the two scale arrays.  Rows past a
+    // chunk's last valid row repeat its first row; a chunk past the end reads
+    // row 0 of the ring and is never used.
     auto issue = [&](int ci, int bi, int part) {
         const int cj = chunk_of(ci);
         const bool sink = cj < nc_s;
-        const int j0 = (sink ? cj : cj - nc_s) * CH;
         const int valid = rows_of(cj);
+        const int j0 = valid > 0 ? first_row_of(cj) : 0;
         const int8_t* kb = sink ? sk : rk;
         const int8_t* vb = sink ? sv : rv;
         const float* ksb = sink ? sks : rks;
         const float* vsb = sink ? svs : rvs;
         auto row_of = [&](int rr) {  // (selects, no branches: the wait counts stay static)
-            const int rs = j0 + rr;
+            const int rs = j0 + (rr < valid ? rr : 0);
             int rg = first_slot + rs;
             rg = rg >= W ? rg - W : rg;
             const int row = sink ? rs : rg;
-            return rr < valid ? row : 0;
+            return valid > 0 ? row : 0;
         };
         DecBuf<D>& B = sm.buf[wave][bi];
         // part 0: the K rows and K scales, part 1: the V rows and V scales
@@ -305,6 +339,21 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     for (int j = 0; j < NI / 2; ++j) tie(qraw[j]);
     tie(xk);
     tie(xv);
+    // q is scaled by a power of two (per head, exact) that brings its largest
+    // magnitude into [2^13, 2^14): the f16 operand then neither overflows nor
+    // drops the low bits of small values (bf16 carries 8 significant bits, f16
+    // 11).  The factor comes out again through this lane's c_log2.
+    uint32_t qmax = 0;
+#pragma unroll
+    for (int j = 0; j < NI / 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w = live ? qraw[j][e] : 0u;
+            qmax = max(qmax, max(w & 0x7fffu, (w >> 16) & 0x7fffu));
+        }
+    const int qsh = qmax == 0 ? 0 : 140 - (int)(qmax >> 7);  // 2^(e - 127) * 2^(140 - e) = 2^13
+    const float c_log2 = __builtin_amdgcn_ldexpf(c_log2_all, -qsh);
+    auto q16 = [&](uint32_t bits) { return __builtin_amdgcn_ldexpf(__uint_as_float(bits), qsh); };
     half4_t qb[NI];
     float qbias[GROUPS];
 #pragma unroll
@@ -315,9 +364,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
         const uint32_t ws[4] = {live ? w[0] : 0u, live ? w[1] : 0u, live ? w[2] : 0u, live ? w[3] : 0u};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const half2_t lo = cvt_pk_f16(__uint_as_float(ws[2 * h] << 16), __uint_as_float(ws[2 * h] & 0xffff0000u));
-            const half2_t hi =
-                cvt_pk_f16(__uint_as_float(ws[2 * h + 1] << 16), __uint_as_float(ws[2 * h + 1] & 0xffff0000u));
+            const half2_t lo = cvt_pk_f16(q16(ws[2 * h] << 16), q16(ws[2 * h] & 0xffff0000u));
+            const half2_t hi = cvt_pk_f16(q16(ws[2 * h + 1] << 16), q16(ws[2 * h + 1] & 0xffff0000u));
             qb[2 * j + h] = half4_t{lo[0], lo[1], hi[0], hi[1]};
             qbias[(8 * j) / 32] += (float)lo[0] + (float)lo[1] + (float)hi[0] + (float)hi[1];
         }
@@ -372,8 +420,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     float m_c = kNegInf;                                  // = m_h[c]
     float l_c = 0.f;                                      // row sum of head c (this lane's keys)
     float ws_c[GROUPS];                                   // sum of f16 weights of head c per group
+    int ve[GROUPS];                                       // V-scale exponent per group (wave-uniform)
 #pragma unroll
-    for (int g = 0; g < GROUPS; ++g) ws_c[g] = 0.f;
+    for (int g = 0; g < GROUPS; ++g) {
+        ws_c[g] = 0.f;
+        ve[g] = kNoExp;
+    }
 
     for (int kk = 0; kk < n_steps; ++kk) {
         const int bi = kk % NBUF;
@@ -484,20 +536,56 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
         if (more) issue(ci + NW, bi, 1);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+            // rows past the chunk's end carry no weight; their scale words (slots
+            // that may never have been written) are not used
             const int w0 = r * GROUPS;
-            vs0[r] = __uint_as_float(vsw[w0 / 4][w0 % 4]);
-            if (GROUPS > 1) vs1[r] = __uint_as_float(vsw[(w0 + 1) / 4][(w0 + 1) % 4]);
+            const bool ok = kq + r < nvalid;
+            vs0[r] = ok ? __uint_as_float(vsw[w0 / 4][w0 % 4]) : 0.f;
+            if (GROUPS > 1) vs1[r] = ok ? __uint_as_float(vsw[(w0 + 1) / 4][(w0 + 1) % 4]) : 0.f;
+        }
+        // The weight operand p * s_v is an f16 number: it is formed relative to
+        // a power of two 2^ve[g] at least as large as every V scale of group g
+        // seen so far (p <= 2^8, so the operand stays below 2^8), and the
+        // accumulators are rescaled exactly when a chunk raises ve[g].
+        {
+            const uint32_t m0 = all_blocks_umax(max(max(__float_as_uint(vs0[0]), __float_as_uint(vs0[1])),
+                                                    max(__float_as_uint(vs0[2]), __float_as_uint(vs0[3]))));
+            const uint32_t m1 = GROUPS > 1 ? all_blocks_umax(max(max(__float_as_uint(vs1[0]), __float_as_uint(vs1[1])),
+                                                                 max(__float_as_uint(vs1[2]), __float_as_uint(vs1[3]))))
+                                           : 0u;
+            const int e0 = m0 ? (int)(m0 >> 23) - 126 : kNoExp;  // scales < 2^e (finite, non-negative)
+            const int e1 = m1 ? (int)(m1 >> 23) - 126 : kNoExp;
+            if (e0 > ve[0] || (GROUPS > 1 && e1 > ve[GROUPS - 1])) {
+                float f[GROUPS];
+                const int en[2] = {max(e0, ve[0]), max(e1, ve[GROUPS - 1])};
+#pragma unroll
+                for (int g = 0; g < GROUPS; ++g) {
+                    f[g] = ve[g] == kNoExp ? 1.f : __builtin_amdgcn_ldexpf(1.f, ve[g] - en[g]);
+                    ve[g] = en[g];
+                    ws_c[g] *= f[g];
+                }
+                const float fl = (D == 64 && lane >= 32) ? f[GROUPS - 1] : f[0];
+#pragma unroll
+                for (int i = 0; i < NACC; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][r] *= fl;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                vs0[r] = __builtin_amdgcn_ldexpf(vs0[r], -ve[0]);
+                if (GROUPS > 1) vs1[r] = __builtin_amdgcn_ldexpf(vs1[r], -ve[GROUPS - 1]);
+            }
         }
         // ... scaled per V group, as the A operand of P V
-        const half2_t a0l = cvt_pk_f16(p[0] * vs0[0], p[1] * vs0[1]);
-        const half2_t a0h = cvt_pk_f16(p[2] * vs0[2], p[3] * vs0[3]);
+        const half2_t a0l = cvt_pk_f16_rne(p[0] * vs0[0], p[1] * vs0[1]);
+        const half2_t a0h = cvt_pk_f16_rne(p[2] * vs0[2], p[3] * vs0[3]);
         const half4_t pa0 = half4_t{a0l[0], a0l[1], a0h[0], a0h[1]};
         ws_c[0] = fdot2(__builtin_bit_cast(uint32_t, a0l), 0x3c003c00u, ws_c[0]);
         ws_c[0] = fdot2(__builtin_bit_cast(uint32_t, a0h), 0x3c003c00u, ws_c[0]);
         half4_t pa1 = pa0;
         if (GROUPS > 1) {
-            const half2_t a1l = cvt_pk_f16(p[0] * vs1[0], p[1] * vs1[1]);
-            const half2_t a1h = cvt_pk_f16(p[2] * vs1[2], p[3] * vs1[3]);
+            const half2_t a1l = cvt_pk_f16_rne(p[0] * vs1[0], p[1] * vs1[1]);
+            const half2_t a1h = cvt_pk_f16_rne(p[2] * vs1[2], p[3] * vs1[3]);
             pa1 = half4_t{a1l[0], a1l[1], a1h[0], a1h[1]};
             ws_c[GROUPS - 1] = fdot2(__builtin_bit_cast(uint32_t, a1l), 0x3c003c00u, ws_c[GROUPS - 1]);
             ws_c[GROUPS - 1] = fdot2(__builtin_bit_cast(uint32_t, a1h), 0x3c003c00u, ws_c[GROUPS - 1]);
@@ -577,7 +665,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     for (int g = 0; g < GROUPS; ++g) ws_tot[g] = all_blocks(ws_c[g]);
 
     // the first wave of the kv head stores the new token into its ring slot
-    if (append && hs == 0 && wave == 0 && lane < D) {
+    if (append && hs == 0 && sp == 0 && wave == 0 && lane < D) {
         const int slot = pos % W;
         (rk + (size_t)slot * D)[lane] = (int8_t)ck;
         (rv + (size_t)slot * D)[lane] = (int8_t)cv;
@@ -588,13 +676,23 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     }
     SWA_TRACE(4);
 
-    // merge of the waves: each leaves its per-head totals in LDS; then every
-    // lane of the workgroup produces outputs (head, channel) together with the
-    // appended token
+    // Merge of the waves: each leaves its per-head partial in LDS, in final
+    // units: (acc - 1152 * sum of f16 weights) * 2^ve[g] over max m_c.
     {
-        if constexpr (D == 64) {
+        float ws_r[4][GROUPS];  // the f16 weight sums of each head r (lanes 0..3 hold heads 0..3)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.part_o(wave)[r * D + lane] = o2[0][r];
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int g = 0; g < GROUPS; ++g)
+                ws_r[r][g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws_tot[g]), r));
+        if constexpr (D == 64) {
+            const int g = lane >> 5;
+            const int e = g ? ve[GROUPS - 1] : ve[0];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sm.part_o(wave)[r * D + lane] =
+                    e == kNoExp ? 0.f
+                                : __builtin_amdgcn_ldexpf(o2[0][r] - kBias * (g ? ws_r[r][GROUPS - 1] : ws_r[r][0]), e);
         } else {
             const int i_out = (lane >> 2) % NJ;
             const bool writer = ((lane >> 2) & 3) < NJ;
@@ -604,14 +702,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
                 float o = o2[0][r];
 #pragma unroll
                 for (int j = 1; j < NJ; ++j) o = i_out == j ? o2[j][r] : o;
+                o = ve[0] == kNoExp ? 0.f : __builtin_amdgcn_ldexpf(o - kBias * ws_r[r][0], ve[0]);
                 if (writer) sm.part_o(wave)[r * D + ch] = o;
             }
         }
         if (lane < 4) {
             sm.part_m[wave][lane] = m_c;
             sm.part_l[wave][lane] = l_tot;
-#pragma unroll
-            for (int g = 0; g < GROUPS; ++g) sm.part_ws[wave][lane][g] = ws_tot[g];
         }
     }
     __syncthreads();
@@ -619,41 +716,91 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_new), 1)),
                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_new), 2)),
                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_new), 3))};
+    // One softmax partial (m, l, o) merged with the appended token -> output.
+    auto finish = [&](int r, int d, float sr, float vn, float m, float l, float o) {
+        const float mm = fmaxf(m, sr);
+        float num = 0.f, den = 0.f;
+        if (mm != kNegInf) {  // exp2(-inf - mm) is 0 for a finite mm: empty parts drop out
+            const float fn = __builtin_amdgcn_exp2f(sr - mm), fo = __builtin_amdgcn_exp2f(m - mm);
+            num = fn * vn + fo * o;
+            den = fn + fo * l;
+        }
+        const float val = den > 0.f ? num * __builtin_amdgcn_rcpf(den) : 0.f;
+        ((uint16_t*)a.out)[((size_t)b * a.Hq + h0 + r) * D + d] = (uint16_t)f32_to_bf16_bits(val);
+    };
+    // Partials of split-K, [unit][split][head] (m, l) and [unit][split][head][D] o.
+    const size_t pbase = ((size_t)unit * splits) * 4;
     // (4 * D is a multiple of the block size; with D = 64 each iteration is one
     // head per wave and lane = channel, so the head's merge factors are uniform
     // and the lane's own v_new is the channel's)
     for (int e = tid; e < 4 * D; e += 64 * NW) {
         const int r = e / D, d = e % D;
         const float vn = D == 64 ? v_new : __shfl(v_new, d, 64);  // before any lane leaves the loop body
-        if (r >= nh) continue;
-        const int g = d / 32;
-        const float sr = r == 0 ? sn[0] : r == 1 ? sn[1] : r == 2 ? sn[2] : sn[3];
-        float m = sr;
+        float m = kNegInf;
 #pragma unroll
         for (int w = 0; w < NW; ++w) m = fmaxf(m, sm.part_m[w][r]);
-        float num = 0.f, den = 0.f;
+        float o = 0.f, l = 0.f;
         if (m != kNegInf) {
-            // exp2(-inf - m) is 0 for a finite m: empty parts drop out
-            const float fn = __builtin_amdgcn_exp2f(sr - m);
-            num = fn * vn;
-            den = fn;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 const float f = __builtin_amdgcn_exp2f(sm.part_m[w][r] - m);
-                num += f * (sm.part_o(w)[r * D + d] - kBias * sm.part_ws[w][r][g]);
-                den += f * sm.part_l[w][r];
+                o += f * sm.part_o(w)[r * D + d];
+                l += f * sm.part_l[w][r];
             }
         }
-        const float val = den > 0.f ? num * __builtin_amdgcn_rcpf(den) : 0.f;
-        ((uint16_t*)a.out)[((size_t)b * a.Hq + h0 + r) * D + d] = (uint16_t)f32_to_bf16_bits(val);
+        if (splits == 1) {
+            if (r < nh) finish(r, d, r == 0 ? sn[0] : r == 1 ? sn[1] : r == 2 ? sn[2] : sn[3], vn, m, l, o);
+        } else {
+            const size_t row = pbase + (size_t)sp * 4 + r;
+            a.part_o[row * D + d] = o;
+            if (d == 0) {
+                a.part_ml[2 * row] = m;
+                a.part_ml[2 * row + 1] = l;
+            }
+        }
     }
+    if (splits == 1) return;
+
+    // Split-K combine: the last workgroup of the unit to finish merges every
+    // split's partial (in split order, so the result does not depend on which
+    // workgroup is last) and sets the unit's counter back to zero.
+    __threadfence();  // this workgroup's partials are visible device-wide ...
+    __syncthreads();
+    if (tid == 0) {   // ... before its arrival is counted
+        const int prev = __hip_atomic_fetch_add(a.counters + unit, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        sm.last = prev == splits - 1;
+    }
+    __syncthreads();
+    if (!sm.last) return;
+    __threadfence();
+    auto ld = [](const float* p) {
+        return __uint_as_float(__hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    };
+    for (int e = tid; e < 4 * D; e += 64 * NW) {
+        const int r = e / D, d = e % D;
+        const float vn = D == 64 ? v_new : __shfl(v_new, d, 64);
+        if (r >= nh) continue;
+        float m = kNegInf;
+        for (int q = 0; q < splits; ++q) m = fmaxf(m, ld(a.part_ml + 2 * (pbase + (size_t)q * 4 + r)));
+        float o = 0.f, l = 0.f;
+        if (m != kNegInf) {
+            for (int q = 0; q < splits; ++q) {
+                const size_t row = pbase + (size_t)q * 4 + r;
+                const float f = __builtin_amdgcn_exp2f(ld(a.part_ml + 2 * row) - m);
+                o += f * ld(a.part_o + row * D + d);
+                l += f * ld(a.part_ml + 2 * row + 1);
+            }
+        }
+        finish(r, d, r == 0 ? sn[0] : r == 1 ? sn[1] : r == 2 ? sn[2] : sn[3], vn, m, l, o);
+    }
+    if (tid == 0) __hip_atomic_store(a.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     SWA_TRACE(5);
 }
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     const int G = a.Hq / a.Hkv;
-    const long long nblocks = (long long)a.B * a.Hkv * ((G + 3) / 4);
+    const long long nblocks = (long long)a.B * a.Hkv * ((G + 3) / 4) * a.num_splits;
     if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_kernel<D>), dim3((unsigned)nblocks), dim3(128), 0, s, a);
     return hipGetLastError();

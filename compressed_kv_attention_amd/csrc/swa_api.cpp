@@ -292,17 +292,28 @@ int swa_kv_quantize(long long N, int D, const void* x_bf16, int8_t* xq, float* x
     return hip_status(swa::launch_kv_quantize(N, D, x_bf16, xq, xs, (hipStream_t)stream), "swa_kv_quantize launch");
 }
 
+namespace {
+// Split count a decode call runs with (0 = automatic), or -1 if invalid.
+int resolve_splits(const swa_decode_params* p) {
+    if (p->num_splits < 0 || p->num_splits > swa::kMaxDecodeSplits) return -1;
+    if (p->num_splits > 0) return p->num_splits;
+    return swa::decode_auto_splits(p->B, p->Hq, p->Hkv, p->W, p->S);
+}
+}  // namespace
+
 size_t swa_decode_workspace_size(const swa_decode_params* p) {
-    (void)p;
-    return 0;
+    if (p == nullptr || p->B <= 0 || p->Hkv <= 0 || p->Hq <= 0 || p->Hq % p->Hkv != 0 || p->D <= 0 || p->W < 1 ||
+        p->S < 0)
+        return 0;
+    const int splits = resolve_splits(p);
+    if (splits < 0) return 0;
+    return swa::decode_workspace_layout(p->B, p->Hq, p->Hkv, p->D, splits).total;
 }
 
 int swa_attn_decode(const swa_decode_params* p, const void* q, const void* k_new, const void* v_new, int8_t* ring_k,
                     int8_t* ring_v, float* ring_ks, float* ring_vs, const int8_t* sink_k, const int8_t* sink_v,
                     const float* sink_ks, const float* sink_vs, const int32_t* pos, const int32_t* sink_len,
                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     REQUIRE(p != nullptr, "params must not be NULL");
     REQUIRE(p->B >= 0, "B must be >= 0");
     REQUIRE(p->Hq > 0 && p->Hkv > 0 && p->Hq % p->Hkv == 0, "Hq (%d) must be a positive multiple of Hkv (%d)", p->Hq,
@@ -310,14 +321,20 @@ int swa_attn_decode(const swa_decode_params* p, const void* q, const void* k_new
     REQUIRE(p->W >= 1, "W must be >= 1 (got %d)", p->W);
     REQUIRE(p->S >= 0, "S must be >= 0 (got %d)", p->S);
     REQUIRE(p->scale >= 0.f && std::isfinite(p->scale), "scale must be finite and >= 0");
-    REQUIRE(p->num_splits >= 0, "num_splits must be >= 0");
+    REQUIRE(p->num_splits >= 0 && p->num_splits <= swa::kMaxDecodeSplits, "num_splits must be in [0, %d] (got %d)",
+            swa::kMaxDecodeSplits, p->num_splits);
     if (p->D != 32 && p->D != 64) return fail(SWA_ERR_UNSUPPORTED, "head dim D=%d is not built (32 or 64)", p->D);
-    const int G = p->Hq / p->Hkv;
-    if (G != 1 && G != 2 && G != 4 && G != 8)
-        return fail(SWA_ERR_UNSUPPORTED, "GQA group size %d is not built (1, 2, 4 or 8)", G);
-    if (p->num_splits > 1) return fail(SWA_ERR_UNSUPPORTED, "num_splits > 1 is not built");
     REQUIRE((k_new == nullptr) == (v_new == nullptr), "k_new and v_new must both be given or both be NULL");
     if (p->B == 0) return ok();
+    const int splits = resolve_splits(p);
+    const swa::DecodeWorkspace wl = swa::decode_workspace_layout(p->B, p->Hq, p->Hkv, p->D, splits);
+    if (wl.total > 0) {
+        REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 255u) == 0,
+                "workspace must be a 256-byte aligned buffer of swa_decode_workspace_size() bytes (%d splits)",
+                splits);
+        REQUIRE(workspace_bytes >= wl.total, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                wl.total);
+    }
     REQUIRE_PTR(q);
     REQUIRE_PTR(ring_k);
     REQUIRE_PTR(ring_v);
@@ -355,7 +372,13 @@ int swa_attn_decode(const swa_decode_params* p, const void* q, const void* k_new
     a.D = p->D;
     a.W = p->W;
     a.S = p->S;
-    a.num_splits = 1;
+    a.num_splits = splits;
+    if (wl.total > 0) {
+        char* ws = (char*)workspace;
+        a.counters = (int*)(ws + wl.counters);
+        a.part_ml = (float*)(ws + wl.part_ml);
+        a.part_o = (float*)(ws + wl.part_o);
+    }
     a.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->D);
     return hip_status(swa::launch_decode(a, (hipStream_t)stream), "swa_attn_decode launch");
 }

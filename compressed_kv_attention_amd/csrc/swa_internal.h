@@ -121,11 +121,45 @@ struct DecodeArgs {
     const int32_t* pos;
     const int32_t* sink_len;
     void* out;
-    float* partial;  // workspace for split-K partials (num_splits > 1)
+    // split-K state (num_splits > 1), in the caller's workspace: one arrival
+    // counter per (batch row, kv head, group of 4 query heads) -- zero between
+    // calls -- and each split's softmax partials: (m, l) and o[D] per head
+    int* counters;
+    float* part_ml;
+    float* part_o;
     int B, Hq, Hkv, D, W, S;
-    int num_splits;
+    int num_splits;  // >= 1 (the entry point resolves 0 = automatic)
     float scale;
 };
+// Workspace of a decode with `splits` parts: [counters][partial m, l][partial o],
+// each part 256-byte aligned; 0 bytes when splits == 1.
+struct DecodeWorkspace {
+    size_t counters, part_ml, part_o, total;
+};
+inline DecodeWorkspace decode_workspace_layout(int B, int Hq, int Hkv, int D, int splits) {
+    DecodeWorkspace w{0, 0, 0, 0};
+    if (splits <= 1 || B <= 0 || Hkv <= 0) return w;
+    auto r256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t units = (size_t)B * Hkv * ((Hq / Hkv + 3) / 4);
+    w.counters = 0;
+    w.part_ml = r256(units * sizeof(int));
+    w.part_o = w.part_ml + r256(units * splits * 4 * 2 * sizeof(float));
+    w.total = w.part_o + r256(units * splits * 4 * (size_t)D * sizeof(float));
+    return w;
+}
+// Split count the library picks for num_splits == 0: enough workgroups for
+// two per compute unit when the batch alone does not provide them, each
+// split keeping at least one 64-row chunk of the walk.
+inline int decode_auto_splits(int B, int Hq, int Hkv, int W, int S) {
+    const long long units = (long long)B * Hkv * ((Hq / Hkv + 3) / 4);
+    const long long want = 512;  // 2 x 256 compute units
+    if (units <= 0 || units >= want) return 1;
+    long long s = (want + units - 1) / units;
+    const long long max_by_rows = ((long long)S + W + 63) / 64;
+    if (s > max_by_rows) s = max_by_rows;
+    return (int)(s < 1 ? 1 : s);
+}
+constexpr int kMaxDecodeSplits = 256;
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace swa

@@ -121,7 +121,8 @@ def test_debug_visibility_limits():
     (dict(W=0), swa.SWA_ERR_INVALID, "W must be"),
     (dict(S=-1), swa.SWA_ERR_INVALID, "S must be"),
     (dict(D=128), swa.SWA_ERR_UNSUPPORTED, "head dim"),
-    (dict(Hq=12, Hkv=4), swa.SWA_ERR_UNSUPPORTED, "group size"),
+    (dict(num_splits=257), swa.SWA_ERR_INVALID, "num_splits"),
+    (dict(num_splits=-1), swa.SWA_ERR_INVALID, "num_splits"),
     (dict(Hq=5, Hkv=2), swa.SWA_ERR_INVALID, "multiple"),
 ])
 def test_decode_rejects_bad_params(kw, code, text):
@@ -131,6 +132,30 @@ def test_decode_rejects_bad_params(kw, code, text):
     L = swa.lib()
     rc = L.swa_attn_decode(ctypes.byref(dp), *([FAKE] * 14), None, 0, None)
     assert rc == code and text in L.swa_last_error().decode()
+
+
+def test_decode_workspace_sizes():
+    """Split-K workspace: one counter per (batch row, kv head, group of 4 query
+    heads), then (m, l) and o[D] per split and query head of the group, each
+    part 256-byte aligned; nothing with one split."""
+    L = swa.lib()
+    size = lambda **kw: L.swa_decode_workspace_size(ctypes.byref(swa.DecodeParams(**dict(
+        dict(B=256, Hq=16, Hkv=4, D=64, W=256, S=256, scale=0.0, num_splits=0), **kw))))
+    assert size() == 0                                   # 1024 units: the automatic choice is one split
+    assert size(num_splits=1) == 0
+    units = 1 * 4 * 1
+    r = lambda x: (x + 255) // 256 * 256
+    assert size(B=1, num_splits=8) == r(units * 4) + r(units * 8 * 4 * 2 * 4) + r(units * 8 * 4 * 64 * 4)
+    assert size(B=1, Hq=24, Hkv=4, num_splits=2) == r(8 * 4) + r(8 * 2 * 4 * 2 * 4) + r(8 * 2 * 4 * 64 * 4)
+    # automatic: at least 512 workgroups when the batch allows, one 64-row chunk per split at least
+    assert size(B=1) == r(units * 4) + r(units * 8 * 4 * 2 * 4) + r(units * 8 * 4 * 64 * 4)
+    dp = swa.DecodeParams(1, 16, 4, 64, 256, 256, 0.0, 8)
+    args = [FAKE] * 14
+    assert L.swa_attn_decode(ctypes.byref(dp), *args, None, 0, None) == swa.SWA_ERR_INVALID
+    assert "workspace" in L.swa_last_error().decode()
+    assert L.swa_attn_decode(ctypes.byref(dp), *args, FAKE, size(B=1, num_splits=8) - 1, None) == \
+        swa.SWA_ERR_INVALID
+    assert "too small" in L.swa_last_error().decode()
 
 
 def test_decode_rejects_half_given_new_token():

@@ -48,11 +48,12 @@ def make_caches(w):
     return dev, ref
 
 
-def run_decode(w, dev, append=True):
+def run_decode(w, dev, append=True, num_splits=0):
     out = swa.decode(bf16_dev(w["q_bits"]), dev["ring_k"], dev["ring_v"], dev["ring_ks"], dev["ring_vs"],
                      dev["sink_k"], dev["sink_v"], dev["sink_ks"], dev["sink_vs"],
                      torch.from_numpy(w["pos"]).cuda(), torch.from_numpy(w["sink_len"]).cuda(),
-                     bf16_dev(w["k_new_bits"]) if append else None, bf16_dev(w["v_new_bits"]) if append else None)
+                     bf16_dev(w["k_new_bits"]) if append else None, bf16_dev(w["v_new_bits"]) if append else None,
+                     num_splits=num_splits)
     torch.cuda.synchronize()
     return out
 
@@ -148,3 +149,147 @@ def test_decode_bitwise_repeatable():
     for i in range(30):
         out = run_decode(w, dev).view(torch.int16)
         assert torch.equal(out, first), f"launch {i} differs"
+
+
+def vmax_per_head(w, ref):
+    """max |dequantized V| over each (sequence, kv head)'s caches, broadcast to [B, Hq, 1]."""
+    G = w["Hq"] // w["Hkv"]
+    m = np.zeros((w["B"], w["Hkv"]))
+    for codes, scales in (("ring_v", "ring_vs"), ("sink_v", "sink_vs")):
+        c = ref[codes].astype(np.float64)
+        if c.size:
+            deq = c * np.repeat(ref[scales].astype(np.float64), 32, axis=-1)
+            m = np.maximum(m, np.abs(deq).max(axis=(2, 3)))
+    vn = np.abs(w["v_new"]).max(axis=-1)
+    return np.repeat(np.maximum(m, vn), G, axis=1)[:, :, None]
+
+
+def split_invariant(a, b, vmax, what):
+    """Outputs of two split counts agree within the rounding both carry: each
+    weight operand p * s_v is one f16 number (relative error <= 2^-11 each way),
+    so the two fp32 results differ by at most 2 * 2^-11 * max|v| before their
+    bf16 rounding (half a step each, 2^-9 relative)."""
+    a = a.float().cpu().numpy().astype(np.float64)
+    b = b.float().cpu().numpy().astype(np.float64)
+    tol = 2.0 ** -10 * vmax + 2.0 ** -8 * np.maximum(np.abs(a), np.abs(b))
+    d = np.abs(a - b)
+    say(f"  {what}: max |diff| {d.max():.3e} (max of diff / bound {float((d / tol).max()):.3f})")
+    assert np.all(d <= tol), what
+
+
+# Split-K: every (sequence, kv head) walk cut into num_splits parts, combined by
+# the last workgroup to finish.  Oracle parity for each split count, and the
+# same output whatever the count (the pin "output invariant to num_splits").
+@pytest.mark.parametrize("B,Hq,Hkv,D,W,S,pos,sink_len", [
+    (1, 16, 4, 64, 256, 256, [20000], [256]),                  # one conversation: the small-batch case
+    (3, 8, 2, 32, 100, 60, [59, 130, 4000], [60, 10, 0]),      # empty ring, partial ring, no sinks
+    (2, 12, 4, 64, 64, 200, [300, 263], [200, 150]),           # G = 3
+    (4, 40, 4, 64, 48, 16, [16, 17, 70, 5000], [16, 16, 0, 7]),  # G = 10: 3 head groups
+])
+def test_decode_split_k(B, Hq, Hkv, D, W, S, pos, sink_len):
+    w = workloads.decode_case(seed=300 + B * 7 + W, B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, sink_len=sink_len)
+    w["pos"] = np.asarray(pos, np.int32)
+    dev, ref = make_caches(w)
+    r_out, _, rk, rv, rks, rvs = oracle_decode(w, ref)
+    vmax = vmax_per_head(w, ref)
+    base = None
+    for splits in (1, 2, 3, 4, 8, 16, 33, 0):
+        say(f"decode split-K B{B} {Hq}/{Hkv} D{D} W{W} S{S} splits {splits}")
+        out = run_decode(w, dev, num_splits=splits)
+        assert_close(to_np(out), r_out, "bf16", f"splits={splits}")
+        for name, r in (("ring_k", rk), ("ring_v", rv), ("ring_ks", rks), ("ring_vs", rvs)):
+            np.testing.assert_array_equal(dev[name].cpu().numpy(), r)
+        if base is None:
+            base = out.clone()
+        else:
+            split_invariant(out, base, vmax, f"splits={splits} vs 1")
+
+
+def test_decode_split_k_full_size_and_repeatable():
+    """The full decode layer (B256, 16/4 heads, ring 256 + 256 sinks) with 2 and
+    4 splits (2048 and 4096 workgroups) against the oracle and against one
+    split; ten launches of 4 splits give the same bits (the combine reads the
+    partials in split order whichever workgroup finishes last)."""
+    w = workloads.decode_case(seed=15)
+    dev, ref = make_caches(w)
+    r_out, *_ = oracle_decode(w, ref)
+    vmax = vmax_per_head(w, ref)
+    one = run_decode(w, dev, num_splits=1)
+    for splits in (2, 4):
+        out = run_decode(w, dev, num_splits=splits)
+        assert_close(to_np(out), r_out, "bf16", f"full size, splits={splits}")
+        split_invariant(out, one, vmax, f"full size splits={splits} vs 1")
+    first = run_decode(w, dev, num_splits=4).view(torch.int16).clone()
+    for i in range(10):
+        assert torch.equal(run_decode(w, dev, num_splits=4).view(torch.int16), first), f"launch {i} differs"
+
+
+def _rescaled(w, name, factor):
+    """Replace input `name` by its values times `factor` (broadcast), rounded to bf16."""
+    bits, vals = workloads.bf16_round((w[name].astype(np.float64) * factor).astype(np.float32))
+    w[name], w[name + "_bits"] = vals, bits
+
+
+def assert_close_scaled(got, ref, mag, what):
+    """The int8-KV tolerance on outputs measured in units of the values' magnitude
+    (the bounds are absolute for N(0,1) data; scaling V by c scales the output by c)."""
+    assert_close(got / mag, ref / mag, "bf16", what)
+
+
+@pytest.mark.parametrize("qmag,vmag", [(1e-6, 1.0), (1e5, 1.0), (1.0, 1e-4), (1.0, 1e5), (3e4, 3e4)])
+@pytest.mark.parametrize("splits", [1, 4])
+def test_decode_input_ranges(qmag, vmag, splits):
+    """q and V far from unit scale: q is scaled by a power of two before its f16
+    conversion and the f16 weight operand p * s_v is formed relative to the
+    largest V scale seen, so neither overflows nor loses its low bits."""
+    B, Hq, Hkv, D, W, S = 3, 8, 2, 64, 64, 32
+    w = workloads.decode_case(seed=41, B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, sink_len=[32, 10, 0])
+    w["pos"] = np.array([40, 300, 2000], np.int32)
+    _rescaled(w, "q", qmag)
+    for name in ("ring_v", "sink_v", "v_new"):
+        _rescaled(w, name, vmag)
+    say(f"decode ranges |q|~{qmag:g} |v|~{vmag:g} splits {splits}")
+    dev, ref = make_caches(w)
+    out = run_decode(w, dev, num_splits=splits)
+    r_out, *_ = oracle_decode(w, ref)
+    assert_close_scaled(to_np(out), r_out, vmag, f"|q|~{qmag:g} |v|~{vmag:g}")
+
+
+def test_decode_mixed_v_magnitudes():
+    """Rows of very different V magnitude in one walk (1e-4 .. 1e4, by row): the
+    exponent bookkeeping rescales the accumulators as larger scales arrive."""
+    B, Hq, Hkv, D, W, S = 2, 4, 1, 64, 128, 128
+    w = workloads.decode_case(seed=43, B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S)
+    w["pos"] = np.array([700, 300], np.int32)
+    rng = np.random.default_rng(44)
+    for name, rows in (("ring_v", W), ("sink_v", S)):
+        _rescaled(w, name, 10.0 ** rng.uniform(-4, 4, size=(B, Hkv, rows, 1)))
+    dev, ref = make_caches(w)
+    r_out, *_ = oracle_decode(w, ref)
+    for splits in (1, 3):
+        out = run_decode(w, dev, num_splits=splits)
+        assert_close_scaled(to_np(out), r_out, 1e4, f"mixed V magnitudes, splits={splits}")
+
+
+def test_decode_ignores_unwritten_ring_slots():
+    """Early in a sequence most ring slots were never written.  Their codes and
+    scales (here NaN and +inf scales, arbitrary codes) must not reach the output:
+    the rows padding a partial chunk carry zero weight and their scales are not
+    used."""
+    B, Hq, Hkv, D, W, S = 2, 8, 2, 64, 256, 256
+    w = workloads.decode_case(seed=45, B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, sink_len=[256, 100])
+    w["pos"] = np.array([259, 120], np.int32)          # ring holds positions 256..259 and 100..120
+    dev, ref = make_caches(w)
+    poison = torch.tensor([float("nan"), float("inf")], device="cuda")
+    for b, (p, sl) in enumerate(zip(w["pos"], w["sink_len"])):
+        live = set(x % W for x in range(max(sl, p - W + 1), p + 1))
+        dead = torch.tensor([t for t in range(W) if t not in live], device="cuda")
+        vals = poison[torch.arange(dead.numel(), device="cuda") % 2]          # NaN, +inf, NaN, ...
+        for name in ("ring_ks", "ring_vs"):
+            dev[name][b, :, dead, :] = vals[None, :, None].expand(Hkv, -1, D // 32)
+        dev["ring_k"][b, :, dead, :] = 127
+        dev["ring_v"][b, :, dead, :] = -127
+    for splits in (1, 2, 8):
+        out = run_decode(w, dev, num_splits=splits)
+        r_out, *_ = oracle_decode(w, ref)
+        assert_close(to_np(out), r_out, "bf16", f"poisoned unwritten slots, splits={splits}")
