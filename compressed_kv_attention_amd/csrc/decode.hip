@@ -8,6 +8,8 @@
 // channels) is the one the budget formula of [NW] "How the 256-Token Sliding
 // Window Works with Tools as KV Sinks in Needle", section "Effective KV
 // Window: Bounding the Cache Size", prices.
+#include <mutex>
+
 #include "swa_common.h"
 #include "swa_internal.h"
 
@@ -819,6 +821,55 @@ hipError_t launch_kv_quantize(long long N, int D, const void* x, int8_t* xq, flo
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     if (a.D == 64) return launch_decode_d<64>(a, s);
     return launch_decode_d<32>(a, s);
+}
+
+// ---- split-K state without caller memory --------------------------------
+// For callers that cannot allocate (HIP graph capture, tight serving loops):
+// the split-K counters and partials live in this file-scope device array, one
+// copy per GPU, held until the process ends.  Every call on a GPU shares it,
+// so calls that overlap in time on one GPU race.  Its counters are zero at
+// load time, are cleared once more by the first call on each device, and
+// every completed call leaves them zero again.
+namespace {
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_words_kernel(uint32_t* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_decode_noalloc(DecodeArgs a, const DecodeWorkspace& wl, hipStream_t s) {
+    if (wl.total > kNoAllocScratchBytes) return hipErrorInvalidValue;
+    char* base = nullptr;
+    if (wl.total > 0) {
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (g_scratch_ptr[dev] == nullptr) {
+            // this device's copy of the array: its address, taken once with the
+            // device current (the array's host-side name is not an address)
+            void* ptr = nullptr;
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, s, (uint32_t*)ptr,
+                               kNoAllocScratchBytes / sizeof(uint32_t));
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            g_scratch_ptr[dev] = ptr;
+        }
+        base = (char*)g_scratch_ptr[dev];
+        a.counters = (int*)(base + wl.counters);
+        a.part_ml = (float*)(base + wl.part_ml);
+        a.part_o = (float*)(base + wl.part_o);
+    }
+    return launch_decode(a, s);
 }
 
 }  // namespace swa

@@ -310,10 +310,16 @@ size_t swa_decode_workspace_size(const swa_decode_params* p) {
     return swa::decode_workspace_layout(p->B, p->Hq, p->Hkv, p->D, splits).total;
 }
 
-int swa_attn_decode(const swa_decode_params* p, const void* q, const void* k_new, const void* v_new, int8_t* ring_k,
-                    int8_t* ring_v, float* ring_ks, float* ring_vs, const int8_t* sink_k, const int8_t* sink_v,
-                    const float* sink_ks, const float* sink_vs, const int32_t* pos, const int32_t* sink_len,
-                    void* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Validation shared by both decode entry points; fills the argument block and
+// the split-K workspace layout (the caller decides where that memory is).
+int check_decode(const swa_decode_params* p, const void* q, const void* k_new, const void* v_new, int8_t* ring_k,
+                 int8_t* ring_v, float* ring_ks, float* ring_vs, const int8_t* sink_k, const int8_t* sink_v,
+                 const float* sink_ks, const float* sink_vs, const int32_t* pos, const int32_t* sink_len, void* out,
+                 swa::DecodeArgs& a, swa::DecodeWorkspace& wl, bool& empty) {
+    empty = false;
     REQUIRE(p != nullptr, "params must not be NULL");
     REQUIRE(p->B >= 0, "B must be >= 0");
     REQUIRE(p->Hq > 0 && p->Hkv > 0 && p->Hq % p->Hkv == 0, "Hq (%d) must be a positive multiple of Hkv (%d)", p->Hq,
@@ -325,16 +331,12 @@ int swa_attn_decode(const swa_decode_params* p, const void* q, const void* k_new
             swa::kMaxDecodeSplits, p->num_splits);
     if (p->D != 32 && p->D != 64) return fail(SWA_ERR_UNSUPPORTED, "head dim D=%d is not built (32 or 64)", p->D);
     REQUIRE((k_new == nullptr) == (v_new == nullptr), "k_new and v_new must both be given or both be NULL");
-    if (p->B == 0) return ok();
-    const int splits = resolve_splits(p);
-    const swa::DecodeWorkspace wl = swa::decode_workspace_layout(p->B, p->Hq, p->Hkv, p->D, splits);
-    if (wl.total > 0) {
-        REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 255u) == 0,
-                "workspace must be a 256-byte aligned buffer of swa_decode_workspace_size() bytes (%d splits)",
-                splits);
-        REQUIRE(workspace_bytes >= wl.total, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
-                wl.total);
+    if (p->B == 0) {
+        empty = true;
+        return SWA_OK;
     }
+    const int splits = resolve_splits(p);
+    wl = swa::decode_workspace_layout(p->B, p->Hq, p->Hkv, p->D, splits);
     REQUIRE_PTR(q);
     REQUIRE_PTR(ring_k);
     REQUIRE_PTR(ring_v);
@@ -351,7 +353,7 @@ int swa_attn_decode(const swa_decode_params* p, const void* q, const void* k_new
         REQUIRE_PTR(sink_ks);
         REQUIRE_PTR(sink_vs);
     }
-    swa::DecodeArgs a{};
+    a = swa::DecodeArgs{};
     a.q = q;
     a.k_new = k_new;
     a.v_new = v_new;
@@ -373,14 +375,55 @@ int swa_attn_decode(const swa_decode_params* p, const void* q, const void* k_new
     a.W = p->W;
     a.S = p->S;
     a.num_splits = splits;
+    a.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->D);
+    return SWA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int swa_attn_decode(const swa_decode_params* p, const void* q, const void* k_new, const void* v_new, int8_t* ring_k,
+                    int8_t* ring_v, float* ring_ks, float* ring_vs, const int8_t* sink_k, const int8_t* sink_v,
+                    const float* sink_ks, const float* sink_vs, const int32_t* pos, const int32_t* sink_len,
+                    void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    swa::DecodeArgs a;
+    swa::DecodeWorkspace wl;
+    bool empty;
+    const int rc = check_decode(p, q, k_new, v_new, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks,
+                                sink_vs, pos, sink_len, out, a, wl, empty);
+    if (rc != SWA_OK) return rc;
+    if (empty) return ok();
     if (wl.total > 0) {
+        REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 255u) == 0,
+                "workspace must be a 256-byte aligned buffer of swa_decode_workspace_size() bytes (%d splits)",
+                a.num_splits);
+        REQUIRE(workspace_bytes >= wl.total, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                wl.total);
         char* ws = (char*)workspace;
         a.counters = (int*)(ws + wl.counters);
         a.part_ml = (float*)(ws + wl.part_ml);
         a.part_o = (float*)(ws + wl.part_o);
     }
-    a.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->D);
     return hip_status(swa::launch_decode(a, (hipStream_t)stream), "swa_attn_decode launch");
+}
+
+int swa_attn_decode_noalloc(const swa_decode_params* p, const void* q, const void* k_new, const void* v_new,
+                            int8_t* ring_k, int8_t* ring_v, float* ring_ks, float* ring_vs, const int8_t* sink_k,
+                            const int8_t* sink_v, const float* sink_ks, const float* sink_vs, const int32_t* pos,
+                            const int32_t* sink_len, void* out, void* stream) {
+    swa::DecodeArgs a;
+    swa::DecodeWorkspace wl;
+    bool empty;
+    const int rc = check_decode(p, q, k_new, v_new, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks,
+                                sink_vs, pos, sink_len, out, a, wl, empty);
+    if (rc != SWA_OK) return rc;
+    if (empty) return ok();
+    if (wl.total > swa::kNoAllocScratchBytes)
+        return fail(SWA_ERR_UNSUPPORTED,
+                    "split-K state of %zu bytes (%d splits) exceeds the %zu bytes swa_attn_decode_noalloc holds; "
+                    "use fewer splits or swa_attn_decode with a workspace",
+                    wl.total, a.num_splits, swa::kNoAllocScratchBytes);
+    return hip_status(swa::launch_decode_noalloc(a, wl, (hipStream_t)stream), "swa_attn_decode_noalloc launch");
 }
 
 long long swa_kv_budget_window(long long d_model, long long attn_dim, long long num_heads, long long num_kv_heads,

@@ -161,5 +161,11 @@ inline int decode_auto_splits(int B, int Hq, int Hkv, int W, int S) {
 }
 constexpr int kMaxDecodeSplits = 256;
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Largest split-K state swa_attn_decode_noalloc holds (its device array).
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+// The decode launch with the split-K state in the library's device array
+// instead of caller memory; fails with hipErrorInvalidValue when wl.total
+// exceeds kNoAllocScratchBytes.
+hipError_t launch_decode_noalloc(DecodeArgs a, const DecodeWorkspace& wl, hipStream_t s);
 
 }  // namespace swa

@@ -22,6 +22,7 @@ SWA_F32, SWA_BF16 = 0, 1
 EXPORTS = ("swa_last_error", "swa_version", "swa_prefill_workspace_size", "swa_attn_prefill", "swa_debug_visibility", "swa_rope_table",
            "swa_rope_table_host",
            "kv_pool_compress_rope", "swa_kv_quantize", "swa_decode_workspace_size", "swa_attn_decode",
+           "swa_attn_decode_noalloc",
            "swa_kv_budget_window", "swa_effective_kv_window")
 
 
@@ -75,6 +76,8 @@ def lib():
     L.swa_decode_workspace_size.restype = Z
     L.swa_attn_decode.argtypes = [ctypes.POINTER(DecodeParams)] + [P] * 14 + [P, Z, P]
     L.swa_attn_decode.restype = I
+    L.swa_attn_decode_noalloc.argtypes = [ctypes.POINTER(DecodeParams)] + [P] * 14 + [P]
+    L.swa_attn_decode_noalloc.restype = I
     L.swa_kv_budget_window.argtypes = [LL] * 7
     L.swa_kv_budget_window.restype = LL
     L.swa_effective_kv_window.argtypes = [LL] * 8
@@ -349,6 +352,22 @@ def decode(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs
                                  _ptr(ring_ks), _ptr(ring_vs), _ptr(sink_k), _ptr(sink_v), _ptr(sink_ks),
                                  _ptr(sink_vs), _ptr(pos), _ptr(sink_len), _ptr(out),
                                  _ptr(workspace) if ws_len else None, ws_len, _stream(q)))
+    return out
+
+
+def decode_noalloc(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos, sink_len=None,
+                   k_new=None, v_new=None, scale=0.0, num_splits=0, out=None):
+    """decode() without a workspace: the split-K state lives in the library's own device array (for callers
+    that cannot allocate; `out` should then be passed in).  Calls overlapping in time on one GPU race."""
+    _decode_checks(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos, sink_len, k_new,
+                   v_new, out)
+    p = decode_params(q, ring_k, sink_k, scale, num_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().swa_attn_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(ring_k),
+                                         _ptr(ring_v), _ptr(ring_ks), _ptr(ring_vs), _ptr(sink_k), _ptr(sink_v),
+                                         _ptr(sink_ks), _ptr(sink_vs), _ptr(pos), _ptr(sink_len), _ptr(out),
+                                         _stream(q)))
     return out
 
 

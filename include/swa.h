@@ -151,16 +151,24 @@ int kv_pool_compress_rope(int B, int H, int T, int D, int block, int dtype,
 int swa_kv_quantize(long long N, int D, const void* x_bf16, int8_t* xq, float* xs, void* stream);
 
 typedef struct {
-    int B, Hq, Hkv, D; /* D in {32, 64}; Hq % Hkv == 0                         */
+    int B, Hq, Hkv, D; /* D in {32, 64}; Hq % Hkv == 0 (any group size)        */
     int W;             /* ring capacity = window length, >= 1                   */
     int S;             /* sink cache capacity, >= 0                             */
     float scale;       /* 0 selects 1/sqrt(D)                                   */
-    int num_splits;    /* 0 or 1: one workgroup walks all rows of a (b, kv head);
-                          larger values return SWA_ERR_UNSUPPORTED              */
+    int num_splits;    /* split-K parts per (b, kv head) walk, 0..256.  0 lets  */
+                       /* the library choose: one part when B * Hkv * ceil(G/4) */
+                       /* workgroups reach 512, else enough parts for 512, at   */
+                       /* most one per 64 rows of S + W.  Parts are whole       */
+                       /* 16-row pieces; extra parts are empty.                 */
 } swa_decode_params;
 
-/* Workspace bytes swa_attn_decode needs for these parameters (always 0:    */
-/* the decode kernel keeps its partials on chip).                            */
+/* Workspace bytes swa_attn_decode needs for these parameters: 0 with one    */
+/* split; else one int32 arrival counter per (b, kv head, group of 4 query    */
+/* heads), then per split and query head the softmax partial (m, l) and o[D] */
+/* as fp32, each part 256-byte aligned.  The workspace must be zero-filled   */
+/* before its first use; every completed call leaves the counters zero       */
+/* again, so it can be reused by later calls on the same stream.  Two calls  */
+/* that overlap in time need two workspaces.                                 */
 size_t swa_decode_workspace_size(const swa_decode_params* p);
 
 /* One decode step with the mask of [NS §"256-token 滑动窗口：源码走读"]:     */
@@ -181,6 +189,19 @@ int swa_attn_decode(const swa_decode_params* p,
                     const int32_t* sink_len,              /* [B] or NULL (= S)                 */
                     void* out,                            /* [B,Hq,D] bf16                     */
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* swa_attn_decode for callers that cannot allocate memory (code under HIP   */
+/* graph capture, tight serving loops, harnesses that forbid allocation):    */
+/* the same computation, kernels and results, with the split-K state kept in */
+/* a device array inside the library (4 MiB per GPU, held until the process  */
+/* ends) instead of a caller workspace.  Calls needing more state than that  */
+/* return SWA_ERR_UNSUPPORTED (use fewer splits).  It allocates nothing.  All */
+/* calls on one GPU share the array: calls that overlap in time on one GPU   */
+/* race.  The device current at the call must be the stream's device.       */
+int swa_attn_decode_noalloc(const swa_decode_params* p, const void* q, const void* k_new, const void* v_new,
+                            int8_t* ring_k, int8_t* ring_v, float* ring_ks, float* ring_vs, const int8_t* sink_k,
+                            const int8_t* sink_v, const float* sink_ks, const float* sink_vs, const int32_t* pos,
+                            const int32_t* sink_len, void* out, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Window sizing (HOST functions, no device work).                           */
