@@ -31,6 +31,11 @@
 //   O^T += V^T P^T   2 x 2 MFMAs; P^T comes straight from the S^T registers
 // Sub-tiles the mask hides completely are skipped, sub-tiles it shows
 // completely skip the element predicate (swa_tiles.h).
+//
+// DUMP instantiations run the same walk, sub-tile classification, lane gate
+// and masks, but write the pairs they would let through (and each row's
+// visible count) instead of computing attention: the tests check this
+// kernel's own mask bit for bit.
 #include "swa_common.h"
 #include "swa_internal.h"
 #include "swa_tiles.h"
@@ -141,7 +146,7 @@ __device__ __forceinline__ TileBases tile_bases(const PrefillArgs& a, int b, int
 // metadata, wave 0 also moves the keys' packed info and kMetaWave the two
 // sub-tile summaries.  Rows past the last key load the last key's row
 // (finite data, masked later).
-template <int D>
+template <int D, bool DUMP>
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TileBases& tb, SmemBf16<D>& sm, uint32_t koff,
                                            uint32_t voff, int buf, int kind, int tile, int wave, int lane) {
     using TL = TileLoads<D>;
@@ -153,7 +158,9 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TileBases
     const size_t toff = (size_t)k0 * D * 2;
     const char* kb = (pooled ? tb.pk : tb.k) + toff;
     const char* vb = (pooled ? tb.pv : tb.v) + toff;
-    if (k0 + BN <= nkeys) {
+    if (DUMP) {
+        // the mask alone: no K or V (the visibility dump is given no tensors)
+    } else if (k0 + BN <= nkeys) {
 #pragma unroll
         for (int i = 0; i < TL::LOADS; ++i) {
             const int ld = wave + kMfmaWaves * i;
@@ -270,8 +277,14 @@ __device__ __forceinline__ uint32_t k_lane_off(int c, int lane) {
 }
 
 
-template <int D, bool ROPE, bool COMPRESSED>
-__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_bf16_kernel(PrefillArgs a) {
+struct DumpOut {
+    uint8_t* mask;   // [B, T, Tk] visibility (zeroed by the launcher), or null
+    int32_t* count;  // [B, T] visible columns per row
+};
+
+template <int D, bool ROPE, bool COMPRESSED, bool DUMP>
+__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_bf16_kernel(
+    PrefillArgs a, DumpOut dump) {
     static_assert(D == 32 || D == 64, "head dim");
     __shared__ __align__(16) SmemBf16<D> sm;
     SWA_TRACE_DECL
@@ -325,7 +338,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     TileLoads<D> tl;
     tl.init(wave, lane);
     const TileBases tb = tile_bases<D>(a, b, hkv);
-    if (have0) issue_tile<D>(a, tb, sm, tl.koff, tl.voff, 0, kc, tc, wave, lane);
+    if (have0) issue_tile<D, DUMP>(a, tb, sm, tl.koff, tl.voff, 0, kc, tc, wave, lane);
     // one 32-row block per workgroup: the table rows go through LDS, once
     const bool tab_lds = ROPE && a.rbs == 1;
     if (tab_lds) issue_rope_rows<D>(a, sm, q0, wave, lane);
@@ -336,7 +349,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         const uint16_t* qrow = (const uint16_t*)a.q + (((size_t)b * a.Hq + my_h) * T + (row_ok ? my_q : 0)) * D;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
-            raw[c] = row_ok ? *(const uint4*)(qrow + 16 * c + 8 * h) : make_uint4(0, 0, 0, 0);
+            raw[c] = (!DUMP && row_ok) ? *(const uint4*)(qrow + 16 * c + 8 * h) : make_uint4(0, 0, 0, 0);
     }
     float4 rc[D / 32][2], rsn[D / 32][2];
     if (ROPE && !tab_lds && row_ok) {
@@ -461,6 +474,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const int fast_seg = !plain ? 1 : (rs.smin == rs.smax && rs.smin > 0 ? rs.smin : -2);
     const bool fpos_any = fpos_hi >= fpos_lo;
     const uint32_t sum_lds = lds_off(&sm.ksum[0][0][0]);
+    int cnt = 0;  // DUMP: visible columns of this lane's row (its key half)
+    const bool dump_writer = DUMP && hkv == 0 && (my_h % G) == 0 && dump.mask != nullptr;
+    const int Tk = COMPRESSED ? a.nblk + T : T;
     int cur = 0;
     bool have = have0;
     while (have) {
@@ -468,7 +484,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         const int nxt = cur ^ 1;
         int kn = 0, tn = 0;
         const bool have_next = it.next(kn, tn);
-        if (have_next) issue_tile<D>(a, tb, sm, tl.koff, tl.voff, nxt, kn, tn, wave, lane);
+        if (have_next) issue_tile<D, DUMP>(a, tb, sm, tl.koff, tl.voff, nxt, kn, tn, wave, lane);
         SWA_TRACE(1);
 
         if (wave_active) {
@@ -515,18 +531,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 gate_st[st] =
                     (pooled || cls == TILE_PARTIAL) ? row_vis : lane_gate(row_vis, plain, seg_q, ks);
 
-                u32x4 kr[D / 16];
-#pragma unroll
-                for (int c = 0; c < D / 16; ++c) kr[c] = lds_load128(k_addr[c] + st * SUB * D * 2);
                 // Element j of the score block holds key k0 + off(j) + 4h with
                 // off(j) = 8(j/4) + j%4.  The mask enters as the accumulator's
                 // initial value: 0 where the pair is visible, -inf where it is not.
                 const int kb = k0 + 4 * h;  // key of element 0
-                f32x16 sacc;
-                if (cls == TILE_FULL) {
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0], f32x16{},
-                                                                   0, 0, 0);
-                } else {
+                auto make_bias = [&]() {
                     f32x16 bias;
                     if (cls == TILE_PARTIAL_POS) {
                         // Element j is visible iff its key offset off(j) lies in
@@ -569,8 +578,35 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                             }
                         }
                     }
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0], bias, 0, 0,
-                                                                   0);
+                    return bias;
+                };
+                if constexpr (DUMP) {
+                    // the pairs this sub-tile lets through for this row: its
+                    // mask, where the lane gate lets the row take weight at all
+                    if (!gate_st[st]) continue;
+                    const f32x16 bias = cls == TILE_FULL ? f32x16{} : make_bias();
+                    uint8_t* mrow = dump_writer ? dump.mask + ((size_t)b * T + my_q) * Tk : nullptr;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = kb + 8 * (j >> 2) + (j & 3);
+                        if (bias[j] == 0.f && key < nkeys) {
+                            ++cnt;
+                            if (mrow) mrow[(COMPRESSED && !pooled ? a.nblk : 0) + key] = 1;
+                        }
+                    }
+                    continue;
+                }
+
+                u32x4 kr[D / 16];
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) kr[c] = lds_load128(k_addr[c] + st * SUB * D * 2);
+                f32x16 sacc;
+                if (cls == TILE_FULL) {
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0], f32x16{},
+                                                                   0, 0, 0);
+                } else {
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0],
+                                                                   make_bias(), 0, 0, 0);
                 }
 #pragma unroll
                 for (int c = 1; c < D / 16; ++c)
@@ -678,6 +714,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     }
 
     if (!wave_active) return;
+    if constexpr (DUMP) {
+        if (hkv == 0 && (my_h % G) == 0 && dump.count != nullptr) {
+            const int tot = cnt + __shfl_xor(cnt, 32, 64);
+            if (row_ok && h == 0) dump.count[(size_t)b * T + my_q] = tot;
+        }
+        return;
+    }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (row_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -699,9 +742,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     SWA_TRACE(5);
 }
 
-}  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs& args, hipStream_t s) {
+template <bool DUMP>
+hipError_t launch_bf16(const PrefillArgs& args, DumpOut dump, hipStream_t s) {
     PrefillArgs a = args;
     const int G = a.Hq / a.Hkv;
     const int wg_rows = 32 * a.rbs;
@@ -715,28 +758,47 @@ hipError_t launch_prefill_bf16(const PrefillArgs& args, hipStream_t s) {
     a.div_block = make_fastdiv((uint32_t)(a.block > 0 ? a.block : 1));
     dim3 grid((unsigned)nblocks);
     dim3 block(64 * kMfmaWaves);
-    const bool rope = a.rope_len > 0;
+    const bool rope = !DUMP && a.rope_len > 0;
     const bool comp = a.block > 0;
-#define SWA_LAUNCH(DD, RR, CC) hipLaunchKernelGGL((prefill_bf16_kernel<DD, RR, CC>), grid, block, 0, s, a)
+#define SWA_LAUNCH(DD, RR, CC) hipLaunchKernelGGL((prefill_bf16_kernel<DD, RR, CC, DUMP>), grid, block, 0, s, a, dump)
     if (a.D == 64) {
         if (comp) {
-            if (rope) SWA_LAUNCH(64, true, true);
+            if (rope) SWA_LAUNCH(64, !DUMP, true);
             else SWA_LAUNCH(64, false, true);
         } else {
-            if (rope) SWA_LAUNCH(64, true, false);
+            if (rope) SWA_LAUNCH(64, !DUMP, false);
             else SWA_LAUNCH(64, false, false);
         }
     } else {
         if (comp) {
-            if (rope) SWA_LAUNCH(32, true, true);
+            if (rope) SWA_LAUNCH(32, !DUMP, true);
             else SWA_LAUNCH(32, false, true);
         } else {
-            if (rope) SWA_LAUNCH(32, true, false);
+            if (rope) SWA_LAUNCH(32, !DUMP, false);
             else SWA_LAUNCH(32, false, false);
         }
     }
 #undef SWA_LAUNCH
     return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(uint8_t* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) { return launch_bf16<false>(a, DumpOut{}, s); }
+
+hipError_t launch_prefill_bf16_dump(const PrefillArgs& a, uint8_t* mask, int32_t* count, hipStream_t s) {
+    if (mask != nullptr) {  // zero the mask first (a fill kernel, not a memset)
+        const int Tk = a.block > 0 ? a.nblk + a.T : a.T;
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, s, mask, (size_t)a.B * a.T * Tk);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_bf16<true>(a, DumpOut{mask, count}, s);
 }
 
 }  // namespace swa

@@ -216,16 +216,54 @@ int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, 
 }
 
 int swa_debug_visibility(const swa_prefill_params* p, const int32_t* seg_ids, const uint8_t* prefix,
-                         uint8_t* mask_out, int32_t* count_out, void* stream) {
+                         uint8_t* mask_out, int32_t* count_out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
     swa::PrefillArgs a;
     int rc = check_prefill(p, seg_ids, prefix, a);
     if (rc != SWA_OK) return rc;
-    if (p->T > swa::kDebugMaxT)
-        return fail(SWA_ERR_UNSUPPORTED, "swa_debug_visibility supports T <= %d (got %d)", swa::kDebugMaxT, p->T);
+    if (mask_out != nullptr && p->T > swa::kDebugMaxT)
+        return fail(SWA_ERR_UNSUPPORTED, "swa_debug_visibility writes masks for T <= %d (got %d)", swa::kDebugMaxT,
+                    p->T);
     if (p->B == 0 || p->T == 0) return ok();
     REQUIRE_PTR(count_out);
-    const hipError_t e = swa::launch_debug_visibility(a, p->dtype == SWA_BF16, mask_out, count_out, (hipStream_t)stream);
-    return hip_status(e, "swa_debug_visibility launch");
+    OPTIONAL_PTR(mask_out);
+    const hipStream_t s = (hipStream_t)stream;
+    if (p->dtype != SWA_BF16) {
+        if (p->T > swa::kDebugMaxT)
+            return fail(SWA_ERR_UNSUPPORTED, "swa_debug_visibility (fp32) supports T <= %d (got %d)", swa::kDebugMaxT,
+                        p->T);
+        return hip_status(swa::launch_debug_visibility(a, false, mask_out, count_out, s), "swa_debug_visibility launch");
+    }
+    // bf16: the MFMA kernel's own walk and masks, fed by the same key-metadata
+    // pre-pass as a prefill call (rope_len is irrelevant to visibility)
+    swa_prefill_params pm = *p;
+    pm.rope_len = 0;
+    const MetaLayout meta = key_meta_layout(&pm);
+    if (meta.total > 0 && (seg_ids || prefix)) {
+        REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 255u) == 0,
+                "workspace must be a 256-byte aligned buffer of swa_prefill_workspace_size() bytes");
+        REQUIRE(workspace_bytes >= meta.total, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                meta.total);
+        char* ws = (char*)workspace;
+        swa::PrepArgs pa{};
+        pa.B = p->B;
+        pa.T = p->T;
+        pa.D = p->D;
+        pa.ntile = a.ntile;
+        pa.div_T = swa::make_fastdiv((uint32_t)p->T);
+        pa.seg = seg_ids;
+        pa.prefix = prefix;
+        pa.info = (int32_t*)(ws + meta.info);
+        pa.ksub = (int32_t*)(ws + meta.ksub);
+        pa.tsink = (int32_t*)(ws + meta.tsink);
+        a.kinfo = pa.info;
+        a.ksub = pa.ksub;
+        a.tsink = pa.tsink;
+        const hipError_t e = swa::launch_prefill_prep(pa, s);
+        if (e != hipSuccess) return hip_status(e, "swa_debug_visibility prep launch");
+    }
+    a.rope_len = 0;
+    return hip_status(swa::launch_prefill_bf16_dump(a, mask_out, count_out, s), "swa_debug_visibility launch");
 }
 
 int swa_rope_table(double theta, int rope_len, int D, float* cos_out, float* sin_out, void* stream) {

@@ -62,7 +62,7 @@ struct PrefillArgs {
 
 // Geometry the bf16 MFMA kernel uses for a given GQA group size: 4 waves per
 // workgroup, hpw heads (the largest divisor of G that is at most 4) times rbs
-// 32-row blocks (hpw * rbs = 4).  With G >= 4 every wave of a workgroup has
+// 64-row blocks (hpw * rbs = 4).  With G >= 4 every wave of a workgroup has
 // the same rows, hence the same mask and the same amount of work.
 constexpr int kMfmaWaves = 4;
 struct MfmaGeom {
@@ -77,6 +77,9 @@ inline MfmaGeom mfma_geometry(int G) {
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+// The bf16 kernel's own visibility: the same walk and masks, written out as
+// mask [B, T, Tk] (zeroed first; may be null) and count [B, T].
+hipError_t launch_prefill_bf16_dump(const PrefillArgs& a, uint8_t* mask, int32_t* count, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_debug_visibility(const PrefillArgs& a, bool mfma_geometry, uint8_t* mask, int32_t* count,
                                    hipStream_t s);

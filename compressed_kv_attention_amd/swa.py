@@ -62,7 +62,7 @@ def lib():
     L.swa_prefill_workspace_size.restype = Z
     L.swa_attn_prefill.argtypes = [ctypes.POINTER(PrefillParams)] + [P] * 11 + [P, Z, P]
     L.swa_attn_prefill.restype = I
-    L.swa_debug_visibility.argtypes = [ctypes.POINTER(PrefillParams), P, P, P, P, P]
+    L.swa_debug_visibility.argtypes = [ctypes.POINTER(PrefillParams), P, P, P, P, P, Z, P]
     L.swa_debug_visibility.restype = I
     L.swa_rope_table.argtypes = [ctypes.c_double, I, I, P, P, P]
     L.swa_rope_table.restype = I
@@ -230,8 +230,10 @@ def debug_visibility(B, Hq, Hkv, T, D, window, dtype=torch.bfloat16, seg_ids=Non
     Tk = T + (T // compress_block if compress_block else 0)
     mask = torch.empty((B, T, Tk), dtype=torch.uint8, device=device) if want_mask else None
     count = torch.empty((B, T), dtype=torch.int32, device=device)
+    ws_bytes = lib().swa_prefill_workspace_size(ctypes.byref(p))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None
     _check(lib().swa_debug_visibility(ctypes.byref(p), _ptr(seg_ids), _ptr(prefix), _ptr(mask), _ptr(count),
-                                      _stream(count)))
+                                      _ptr(ws), ws_bytes, _stream(count)))
     return mask, count
 
 

@@ -101,13 +101,18 @@ int swa_attn_prefill(const swa_prefill_params* p,
                      void* workspace, size_t workspace_bytes,    /* see swa_prefill_workspace_size */
                      void* stream);
 
-/* Visibility as the prefill kernels see it: the same tile enumeration, the  */
-/* same tile classification (skip / full / per-element) and the same element */
-/* predicate, written out.  mask_out [B,T,Tk] u8 (Tk = T, or T/b + T in       */
-/* compressed mode) may be NULL; count_out [B,T] i32 receives the number of   */
-/* visible columns per row.  Used to check masks bit-exactly.                */
+/* Visibility as the prefill kernels apply it (a test hook): for bf16, the   */
+/* MFMA kernel itself runs its walk, sub-tile classification and masks and   */
+/* writes the pairs it would let through instead of computing attention; for */
+/* fp32, a kernel with the fp32 kernel's tile enumeration and predicate does. */
+/* mask_out [B,T,Tk] u8 (Tk = T, or T/b + T in compressed mode, pooled        */
+/* columns first) may be NULL (then any T is accepted, else T <= 16384);      */
+/* count_out [B,T] i32 receives the number of visible columns per row.  bf16  */
+/* calls with seg_ids or prefix need the workspace swa_prefill_workspace_size */
+/* reports (the key-metadata pre-pass writes into it).                       */
 int swa_debug_visibility(const swa_prefill_params* p, const int32_t* seg_ids, const uint8_t* prefix,
-                         uint8_t* mask_out, int32_t* count_out, void* stream);
+                         uint8_t* mask_out, int32_t* count_out, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* RoPE tables and block pooling.                                            */

@@ -111,10 +111,15 @@ def test_empty_problems_are_ok_without_pointers():
 def test_debug_visibility_limits():
     L = swa.lib()
     p = _p(T=20000)
-    assert L.swa_debug_visibility(ctypes.byref(p), None, None, None, FAKE, None) == swa.SWA_ERR_UNSUPPORTED
+    assert L.swa_debug_visibility(ctypes.byref(p), None, None, FAKE, FAKE, None, 0, None) == swa.SWA_ERR_UNSUPPORTED
+    p = _p(T=20000, dtype=swa.SWA_F32)
+    assert L.swa_debug_visibility(ctypes.byref(p), None, None, None, FAKE, None, 0, None) == swa.SWA_ERR_UNSUPPORTED
     p = _p()
-    assert L.swa_debug_visibility(ctypes.byref(p), None, None, None, None, None) == swa.SWA_ERR_INVALID
+    assert L.swa_debug_visibility(ctypes.byref(p), None, None, None, None, None, 0, None) == swa.SWA_ERR_INVALID
     assert "count_out" in L.swa_last_error().decode()
+    # bf16 with segment ids: the key-metadata pre-pass needs the workspace
+    assert L.swa_debug_visibility(ctypes.byref(p), FAKE, None, None, FAKE, None, 0, None) == swa.SWA_ERR_INVALID
+    assert "workspace" in L.swa_last_error().decode()
 
 
 @pytest.mark.parametrize("kw,code,text", [
