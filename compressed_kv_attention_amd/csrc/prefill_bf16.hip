@@ -231,9 +231,10 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 }
 
 // Rotate-half RoPE of 8 channel pairs: x1 holds channels d..d+7 (< D/2), x2
-// holds d+D/2..d+D/2+7; c/s hold the table entries of channels d..d+7.
+// holds d+D/2..d+D/2+7; c/s hold the table entries of channels d..d+7.  The
+// rotated values are multiplied by `mul` before their one rounding to bf16.
 __device__ __forceinline__ void rotate8(uint4& x1, uint4& x2, const float4& c0, const float4& c1, const float4& s0,
-                                        const float4& s1) {
+                                        const float4& s1, float mul) {
     float a[8], bb[8];
     unpack8(x1, a);
     unpack8(x2, bb);
@@ -242,8 +243,8 @@ __device__ __forceinline__ void rotate8(uint4& x1, uint4& x2, const float4& c0, 
     float y1[8], y2[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        y1[i] = a[i] * c[i] - bb[i] * s[i];
-        y2[i] = bb[i] * c[i] + a[i] * s[i];
+        y1[i] = (a[i] * c[i] - bb[i] * s[i]) * mul;
+        y2[i] = (bb[i] * c[i] + a[i] * s[i]) * mul;
     }
     x1 = pack8(y1);
     x2 = pack8(y2);
@@ -325,6 +326,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const int my_q = r0 + lq;
     const bool row_ok = my_q < T;
     constexpr bool plain = !COMPRESSED;
+    // scale * log2 e, folded into q (one rounding of q to bf16)
+    const float c_log2 = a.scale * kLog2e;
 
     // Tile plan.  The band comes first in the walk, so the first tile's loads
     // start at once; every global load of the prologue is issued before any of
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 
     if (ROPE && !tab_lds && row_ok) {
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) rotate8(raw[c], raw[c + D / 32], rc[c][0], rc[c][1], rsn[c][0], rsn[c][1]);
+        for (int c = 0; c < D / 32; ++c) rotate8(raw[c], raw[c + D / 32], rc[c][0], rc[c][1], rsn[c][0], rsn[c][1], c_log2);
     }
 
     SWA_TRACE(7);
@@ -411,10 +414,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         }
     }
     SWA_TRACE(8);
-    const float c_log2 = a.scale * kLog2e;
-    float m_run = kNegInf;  // reference max (raw score units) used for p
-    float base_vis = 0.f;   // m_run * scale * log2 e, or 0 while m_run is -inf
+    // Reference max, in the units of the scaled scores u = s * scale * log2 e
+    // (q carries the factor): weights are exp2(u - base).  base is 0 and
+    // m_set false until a row's first visible sub-tile sets it.  nbase holds
+    // -base in all 16 places for rows that see anything (-inf for rows that
+    // see nothing): the initial accumulator of fully visible sub-tiles, so
+    // the MFMA itself leaves u - base and the exponent reads it directly.
+    float base = 0.f;
+    bool m_set = false;
     float l_run = 0.f;
+    f32x16 nbase;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) nbase[j] = row_vis ? -0.f : kNegInf;
     f32x16 o[D / 32];
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) o[n] = f32x16{};
@@ -438,12 +449,23 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         if (row_ok) {
 #pragma unroll
             for (int c = 0; c < D / 32; ++c)
-                rotate8(raw[c], raw[c + D / 32], rc[c][0], rc[c][1], rsn[c][0], rsn[c][1]);
+                rotate8(raw[c], raw[c + D / 32], rc[c][0], rc[c][1], rsn[c][0], rsn[c][1], c_log2);
         }
         // every wave has read the rows before the walk's second tile overwrites them
         lds_reads_done();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+    }
+    // without RoPE q is scaled here (with RoPE, by the rotation)
+    if (!ROPE && !DUMP) {
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            float f[8];
+            unpack8(raw[c], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] *= c_log2;
+            raw[c] = pack8(f);
+        }
     }
     // Q^T operand: lane holds row my_q, channels 16c + 8h .. +7 for each c.
     bf16x8 qf[D / 16];
@@ -513,11 +535,17 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 int cls;
                 unsigned wl = wlim;
                 const KeySum& ks = ks_cur[st];
+                // (fully visible by the fast test or as pooled blocks: then every
+                // row that sees anything sees every key, and the lane gate is the
+                // row's own visibility, already in nbase)
+                bool splat = false;
                 if (pooled) {
                     cls = classify_pooled(rs, k0, SUB, a.window, a.block, a.nblk);
+                    splat = cls == TILE_FULL;
                 } else if (fpos_any && (unsigned)(k0 - fpos_lo) <= (unsigned)(fpos_hi - fpos_lo) &&
                            (!plain || (ks.smin == ks.smax && ks.any_sink == 0 && ks.smin == fast_seg))) {
                     cls = TILE_FULL;
+                    splat = true;
                 } else {
                     cls = classify_exact(rs, ks, k0, SUB, nkeys, a.window, plain, wl);
                 }
@@ -535,23 +563,28 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 // off(j) = 8(j/4) + j%4.  The mask enters as the accumulator's
                 // initial value: 0 where the pair is visible, -inf where it is not.
                 const int kb = k0 + 4 * h;  // key of element 0
+                // The accumulator's initial value: -base where the pair is visible
+                // (and the row passes the lane gate), -inf where it is not.
+                const bool gate = gate_st[st];
                 auto make_bias = [&]() {
+                    const uint32_t nb = __float_as_uint(-base);
                     f32x16 bias;
-                    if (cls == TILE_PARTIAL_POS) {
+                    if (cls == TILE_PARTIAL_POS || cls == TILE_FULL) {
                         // Element j is visible iff its key offset off(j) lies in
-                        // [d0 - wl + 1, d0]: a mask over offsets 0..31, then one
-                        // bit extract and one AND per element.
+                        // [d0 - wl + 1, d0] (all 32 offsets for FULL): a mask over
+                        // offsets 0..31, then one bit extract and one bit select
+                        // per element.
                         const int d0 = my_q - kb;
                         // (bounds past 2^20 act as no bound: |d0| stays far below it)
-                        const int lo = max(d0 + 1 - (int)min(wl, 1u << 20), 0);
-                        const int hi = min(d0, 31);
+                        const int lo = cls == TILE_FULL ? 0 : max(d0 + 1 - (int)min(wl, 1u << 20), 0);
+                        const int hi = cls == TILE_FULL ? 31 : min(d0, 31);
                         uint32_t vis = 0u;
-                        if (hi >= lo) vis = (hi == 31 ? 0xffffffffu : (2u << hi) - 1u) & ~((1u << lo) - 1u);
-                        const uint32_t hid = ~vis;
+                        if (hi >= lo && gate) vis = (hi == 31 ? 0xffffffffu : (2u << hi) - 1u) & ~((1u << lo) - 1u);
 #pragma unroll
-                        for (int j = 0; j < 16; ++j)
-                            bias[j] = __uint_as_float(
-                                (uint32_t)__builtin_amdgcn_sbfe((int)hid, 8 * (j >> 2) + (j & 3), 1) & 0xff800000u);
+                        for (int j = 0; j < 16; ++j) {
+                            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)vis, 8 * (j >> 2) + (j & 3), 1);
+                            bias[j] = __uint_as_float((m & nb) | (~m & 0xff800000u));
+                        }
                     } else if (pooled) {
                         // pooled blocks visible to this row (recomputed here, where
                         // it is rarely needed, rather than held in a register)
@@ -561,7 +594,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                             plim < a.block ? 0 : min((int)fdiv((uint32_t)plim, a.div_block), a.nblk);
                         const int lim = row_vis ? pooled_n - kb : -1;
 #pragma unroll
-                        for (int j = 0; j < 16; ++j) bias[j] = (8 * (j >> 2) + (j & 3)) < lim ? 0.f : kNegInf;
+                        for (int j = 0; j < 16; ++j)
+                            bias[j] = (8 * (j >> 2) + (j & 3)) < lim ? __uint_as_float(nb) : kNegInf;
                     } else {
                         const int d0 = my_q - kb;
                         u32x4 inf[4];
@@ -574,7 +608,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                             for (int r = 0; r < 4; ++r) {
                                 const bool vis =
                                     row_vis & visible_full(d0 - (8 * g4 + r), wlim, (int)inf[g4][r], seg_q);
-                                bias[4 * g4 + r] = vis ? 0.f : kNegInf;
+                                bias[4 * g4 + r] = vis ? __uint_as_float(nb) : kNegInf;
                             }
                         }
                     }
@@ -584,12 +618,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                     // the pairs this sub-tile lets through for this row: its
                     // mask, where the lane gate lets the row take weight at all
                     if (!gate_st[st]) continue;
-                    const f32x16 bias = cls == TILE_FULL ? f32x16{} : make_bias();
+                    const f32x16 bias = splat ? nbase : make_bias();
                     uint8_t* mrow = dump_writer ? dump.mask + ((size_t)b * T + my_q) * Tk : nullptr;
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const int key = kb + 8 * (j >> 2) + (j & 3);
-                        if (bias[j] == 0.f && key < nkeys) {
+                        if (bias[j] != kNegInf && key < nkeys) {
                             ++cnt;
                             if (mrow) mrow[(COMPRESSED && !pooled ? a.nblk : 0) + key] = 1;
                         }
@@ -600,71 +634,64 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 u32x4 kr[D / 16];
 #pragma unroll
                 for (int c = 0; c < D / 16; ++c) kr[c] = lds_load128(k_addr[c] + st * SUB * D * 2);
-                f32x16 sacc;
-                if (cls == TILE_FULL) {
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0], f32x16{},
-                                                                   0, 0, 0);
-                } else {
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0],
-                                                                   make_bias(), 0, 0, 0);
-                }
+                // sacc = u - base (visible pairs) or -inf
+                f32x16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0],
+                                                                      splat ? nbase : make_bias(), 0, 0, 0);
 #pragma unroll
                 for (int c = 1; c < D / 16; ++c)
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc, 0, 0,
                                                                    0);
-                const bool gate = gate_st[st];
-                float sv[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) sv[j] = sacc[j];
-                // Max of the sub-tile's scores per row (both key halves); -inf
-                // for rows the lane gate excludes.
+                // Largest sacc of the row over both key halves (-inf where the row
+                // sees nothing of this sub-tile).
                 auto sub_max = [&]() {
-                    // (compiler-generated max, not inline asm: sv holds MFMA results,
-                    // and only the compiler inserts the wait a VALU read of them needs)
-                    float mx = sv[0];
+                    // (compiler-generated max: sacc holds MFMA results, and only the
+                    // compiler inserts the wait a VALU read of them needs)
+                    float mx = sacc[0];
 #pragma unroll
-                    for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, sv[j]);
+                    for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, sacc[j]);
                     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false,
                                                                      false);
-                    mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-                    return gate ? mx : kNegInf;
+                    return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
                 };
-                // Move each row's reference max up to mx (if larger), rescaling
-                // what has been accumulated against the old one.
-                auto raise_max = [&](float mx) {
-                    const float m_new = __builtin_fmaxf(m_run, mx);
-                    const float corr = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
-                    m_run = m_new;
-                    base_vis = (m_new == kNegInf) ? 0.f : m_new * c_log2;
+                // Raise each row's reference by the sub-tile's excess over it (the
+                // whole max for a row's first visible sub-tile), rescaling what has
+                // been accumulated and the sub-tile's scores against the new one.
+                auto raise_base = [&]() {
+                    const float mx = sub_max();
+                    const float up = mx == kNegInf ? 0.f : (m_set ? __builtin_fmaxf(mx, 0.f) : mx);
+                    const float corr = m_set ? __builtin_amdgcn_exp2f(-up) : 1.f;
+                    m_set = m_set || mx != kNegInf;
+                    base += up;
                     l_run *= corr;
 #pragma unroll
                     for (int n = 0; n < D / 32; ++n) o[n] *= corr;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) sacc[j] -= up;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) nbase[j] = row_vis ? -base : kNegInf;
                 };
-                // bf16 weights exp2((s - m_run) * scale * log2 e) and the sum of
-                // exactly those weights over this lane's keys; rows the gate
-                // excludes get base +inf, hence weights of exactly 0.
+                // bf16 weights exp2(u - base) and the sum of exactly those weights
+                // over this lane's keys (hidden pairs give exactly 0).
                 uint32_t pw[8];
                 auto weights = [&]() {
-                    const float base = gate ? base_vis : __builtin_inff();
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        pw[i] = cvt_pk_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c_log2, -base)),
-                                            __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c_log2, -base)));
+                        pw[i] = cvt_pk_bf16(__builtin_amdgcn_exp2f(sacc[2 * i]), __builtin_amdgcn_exp2f(sacc[2 * i + 1]));
                     float ps = 0.f;
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
                         ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]), ones2, ps, false);
                     return ps;
                 };
-                // Rows with no reference max yet take this sub-tile's max.
-                if (__builtin_amdgcn_ballot_w64(gate && m_run == kNegInf) != 0) raise_max(sub_max());
+                // Rows with no reference yet take this sub-tile's max.
+                if (__builtin_amdgcn_ballot_w64(gate && !m_set) != 0) raise_base();
                 float psum = weights();
-                // The reference max is lazy: it moves only when some row's scores
+                // The reference is lazy: it moves only when some row's scores
                 // outgrow it by more than 2^8.  Any weight above 2^8 lifts its
                 // lane's sum above 2^8, so the sum is the test; the rare case
                 // recomputes the weights against the true max.
                 if (__builtin_amdgcn_ballot_w64(psum > kRescaleSum) != 0) {
-                    raise_max(sub_max());
+                    raise_base();
                     psum = weights();
                 }
                 l_run += psum;
@@ -736,8 +763,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 *(uint2*)(orow + d) = w;
             }
         }
+        // lse = base / log2 e + ln(l) (base is in log2 units of the scaled scores)
         if (a.lse && h == 0)
-            a.lse[((size_t)b * a.Hq + my_h) * T + my_q] = l_tot > 0.f ? m_run * a.scale + __logf(l_tot) : kNegInf;
+            a.lse[((size_t)b * a.Hq + my_h) * T + my_q] = l_tot > 0.f ? base * 0.6931471805599453f + __logf(l_tot)
+                                                                      : kNegInf;
     }
     SWA_TRACE(5);
 }
