@@ -48,7 +48,9 @@ def parse():
     ap.add_argument("--reps", type=int, default=20, help="iterations per timed graph when timing one kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16")
+    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16,decode_b1,decode_b8,decode_b32")
+    ap.add_argument("--decode-splits", type=int, default=0,
+                    help="num_splits of the batch-256 decode part (0: the library's choice)")
     ap.add_argument("--eager", action="store_true",
                     help="launch kernels directly instead of replaying HIP graphs (for counter collection)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -195,8 +197,17 @@ def main():
         p.w = w
         return p
 
-    def make_decode(name, layers=12):
-        B, Hq, Hkv, D, W, S = 256, 16, 4, 64, 256, 256
+    decode_ws = {}
+
+    def make_decode(name, B=256, min_layers=12, num_splits=0):
+        """One decode launch per layer over distinct caches.  The batch-256 part is the step's 12 layers
+        (0.92 GB of cache); smaller batches use as many cache sets as it takes to exceed the 256 MB
+        Infinity Cache, so every rate is an HBM rate."""
+        Hq, Hkv, D, W, S = 16, 4, 64, 256, 256
+        cache_bytes = 2 * (B * Hkv * (W + S) * D) + 2 * (B * Hkv * (W + S) * (D // 32) * 4)
+        io_bytes = 2 * B * Hq * D * 2 + 2 * B * Hkv * D * 2 + 2 * B * Hkv * (D + (D // 32) * 4)
+        per_layer = cache_bytes + io_bytes
+        layers = max(min_layers, min(2048, -(-ROTATE_BYTES // per_layer)))
         g = torch.Generator(device=dev)
         g.manual_seed(5)
         caches = []
@@ -213,18 +224,25 @@ def main():
         rng = np.random.default_rng(5)
         pos = torch.from_numpy(rng.integers(512, 32768, size=B).astype(np.int32)).to(dev)
         sink_len = torch.full((B,), S, dtype=torch.int32, device=dev)
-        cache_bytes = 2 * (B * Hkv * (W + S) * D) + 2 * (B * Hkv * (W + S) * (D // 32) * 4)
-        io_bytes = 2 * B * Hq * D * 2 + 2 * B * Hkv * D * 2 + 2 * B * Hkv * (D + (D // 32) * 4)
-        per_layer = cache_bytes + io_bytes
+        # one zero-filled split-K workspace serves every layer: launches on one stream run one after
+        # another and each leaves its counters at zero
+        c0 = caches[0]
+        ws = swa.decode_workspace(c0["q"], c0["ring_k"], c0["sink_k"], num_splits)
+        decode_ws[name] = ws
 
         def launch(i):
             for c in caches:
                 swa.decode(c["q"], c["ring_k"], c["ring_v"], c["ring_ks"], c["ring_vs"], c["sink_k"], c["sink_v"],
-                           c["sink_ks"], c["sink_vs"], pos, sink_len, c["k_new"], c["v_new"], out=c["out"])
+                           c["sink_ks"], c["sink_vs"], pos, sink_len, c["k_new"], c["v_new"],
+                           num_splits=num_splits, out=c["out"], workspace=ws)
         p = Part(name, launch, 1, 0.0, per_layer * layers, kernel="decode_kernel")
-        p.extra = dict(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, layers=layers, bytes_per_layer=per_layer)
+        p.extra = dict(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, layers=layers, bytes_per_layer=per_layer,
+                       num_splits=num_splits or "auto",
+                       workspace_bytes=0 if ws is None else ws.numel())
         p.tokens = B
         p.launches = layers
+        # iterations per timed graph: about as many launches as 20 passes over 12 layers
+        p.reps = max(1, (args.reps * 12) // layers)
         return p
 
     t_setup = time.time()
@@ -233,7 +251,10 @@ def main():
     if "compressed4" in parts_wanted:
         parts["compressed4"] = make_compressed("compressed4", 4)
     if "decode" in parts_wanted:
-        parts["decode"] = make_decode("decode")
+        parts["decode"] = make_decode("decode", num_splits=args.decode_splits)
+    for b in (1, 8, 32):
+        if f"decode_b{b}" in parts_wanted:
+            parts[f"decode_b{b}"] = make_decode(f"decode_b{b}", B=b)
     if "packed" in parts_wanted:
         parts["packed"] = make_prefill("packed", workloads.packed())
     if "compressed16" in parts_wanted:
@@ -253,15 +274,17 @@ def main():
             for i in range(self.iters):
                 self.fn(self.offset + i)
 
-    def capture(fn, iters, offset=0):
+    def capture(fn, iters, offset=0, prewarm=True):
         if args.eager:
-            with torch.cuda.stream(stream):
-                fn(offset)
-            torch.cuda.synchronize()
+            if prewarm:
+                with torch.cuda.stream(stream):
+                    fn(offset)
+                torch.cuda.synchronize()
             return Eager(fn, iters, offset)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
-            fn(offset)  # warm the code path on the capture stream
+            if prewarm:
+                fn(offset)  # warm the code path on the capture stream
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=stream):
                 for i in range(iters):
@@ -289,7 +312,7 @@ def main():
     # ---- per-part timing (one graph of `reps` iterations each) -----------------
     results = {}
     for name, p in parts.items():
-        reps = max(p.ncopies, args.reps)
+        reps = getattr(p, "reps", max(p.ncopies, args.reps))
         g = capture(p.launch, reps)
         warm(g, args.warmup)
         ms = time_graph(g, max(1, args.steps // 4)) / (max(1, args.steps // 4) * reps)
@@ -309,17 +332,20 @@ def main():
         del g
 
     # ---- the step: needle + compressed4 + decode, K timed steps ----------------
+    # W warmup steps launched directly, then one graph of exactly K steps (input copies cycle with the
+    # step index) replayed once inside the timed region.
     step_names = [n for n in ("needle", "compressed4", "decode") if n in parts]
 
     def step(i):
         for n in step_names:
             parts[n].launch(i)
-    ncopy = max([parts[n].ncopies for n in step_names] + [1])
-    step_graph = capture(step, ncopy)
-    warm(step_graph, args.warmup)
-    replays = max(1, args.steps // ncopy)
-    steps_timed = replays * ncopy
-    ms_total = time_graph(step_graph, replays)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+    step_graph = capture(step, args.steps, offset=args.warmup, prewarm=False)
+    steps_timed = args.steps
+    ms_total = time_graph(step_graph, 1)
     ms_per_step = ms_total / steps_timed
 
     head = results.get("needle", {})
@@ -338,12 +364,24 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "needle-shaped windowed+sink GQA prefill, B8 8q/2kv D64 T2048 window 256, "
-                               "sink prefix 64..384, RoPE; step also runs compressed b=4 (B4 8/8 T4096) and a "
-                               "12-layer int8 decode step (B256 16q/4kv ring 256 + 256 sinks)",
+                               "sink prefix 64..384, RoPE (value); the step also runs compressed b=4 (B4 8/8 "
+                               "T4096) and a 12-layer int8 decode step (B256 16q/4kv ring 256 + 256 sinks); the "
+                               "largest prefill, packed multi-segment B16 16q/4kv T4096 (3-6 segments per row, "
+                               "128-token prefix), is timed on its own under packed",
                    "global_batch": 8, "seq_len": 2048, "parallelism": "none (1 GPU)"},
         "decode": {"value": round(dec.get("gbs", 0.0), 1), "unit": "GB/s",
                    "frac_hbm_peak": round(dec.get("frac_hbm_peak", 0.0), 4),
-                   "tokens_per_s": round(dec.get("tokens_per_s", 0.0), 1)},
+                   "tokens_per_s": round(dec.get("tokens_per_s", 0.0), 1),
+                   "us_per_layer": round(dec.get("ms_per_launch", 0.0) * 1e3, 2)},
+        "decode_by_batch": {str(r["B"]): {"us_per_layer": round(r["ms_per_launch"] * 1e3, 2),
+                                          "gbs": round(r["gbs"], 1), "frac_hbm_peak": round(r["frac_hbm_peak"], 4),
+                                          "tokens_per_s": round(r["tokens_per_s"], 1)}
+                            for n, r in sorted(results.items(), key=lambda kv: kv[1].get("B", 0))
+                            if n.startswith("decode")},
+        "packed": {"value": round(results.get("packed", {}).get("tflops", 0.0), 3), "unit": "TFLOP/s",
+                   "frac_mfma_peak": round(results.get("packed", {}).get("frac_mfma_peak", 0.0), 5),
+                   "us_per_call": round(results.get("packed", {}).get("ms", 0.0) * 1e3, 2),
+                   "traffic": measured_traffic("prefill_packed_call", PREFILL_SOURCES)},
         "parts": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                   for k, v in results.items()},
         # The dominant kernel of the step by GPU time is the decode kernel (12 launches per step); one
@@ -387,6 +425,16 @@ def roofline_decode(dec):
             "ms_per_launch": round(dec["ms_per_launch"], 5)}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(part, seconds):
     """Time the CPU oracle on the needle workload (visible-pair TFLOP/s).  The oracle evaluates whole
     passes over every (b, head, row) of the workload, repeated until about `seconds` have elapsed."""
@@ -404,7 +452,8 @@ def cpu_baseline(part, seconds):
     nvis = float(part.count.astype(np.float64).sum())
     flops = 4.0 * D * Hq * nvis * passes
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"{passes} full passes of the oracle over the needle workload ({B * Hq * T} query rows, "
                       f"RoPE of all keys included); {elapsed:.1f} s", "seconds": round(elapsed, 2)}
 

@@ -168,11 +168,10 @@ struct DecSmem {
 // which the walk over positions [first, pos - 1] never reads); it joins the
 // final merge as one more exact softmax partial, so the walk needs no
 // per-lane special case.
-template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(DecodeArgs a) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(DecodeArgs a) {
     constexpr int NI = D / 4;       // 4-channel instructions per row
     constexpr int GROUPS = D / 32;  // scale groups per row
-    constexpr int NW = 2;           // waves per workgroup
     constexpr int NBUF = 1;         // chunk buffers per wave (K and V parts refilled separately)
     constexpr int CH = 64;          // rows per chunk (one per lane)
     constexpr int CPR = D / 16;     // 16-byte pieces per row
@@ -732,6 +731,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     };
     // Partials of split-K, [unit][split][head] (m, l) and [unit][split][head][D] o.
     const size_t pbase = ((size_t)unit * splits) * 4;
+    auto st = [](float* p, float v) {
+        __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
     // (4 * D is a multiple of the block size; with D = 64 each iteration is one
     // head per wave and lane = channel, so the head's merge factors are uniform
     // and the lane's own v_new is the channel's)
@@ -754,10 +756,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
             if (r < nh) finish(r, d, r == 0 ? sn[0] : r == 1 ? sn[1] : r == 2 ? sn[2] : sn[3], vn, m, l, o);
         } else {
             const size_t row = pbase + (size_t)sp * 4 + r;
-            a.part_o[row * D + d] = o;
+            st(a.part_o + row * D + d, o);
             if (d == 0) {
-                a.part_ml[2 * row] = m;
-                a.part_ml[2 * row + 1] = l;
+                st(a.part_ml + 2 * row, m);
+                st(a.part_ml + 2 * row + 1, l);
             }
         }
     }
@@ -766,15 +768,21 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     // Split-K combine: the last workgroup of the unit to finish merges every
     // split's partial (in split order, so the result does not depend on which
     // workgroup is last) and sets the unit's counter back to zero.
-    __threadfence();  // this workgroup's partials are visible device-wide ...
+    // The L2 caches of the XCDs are not coherent with one another, and a
+    // device-scope fence writes back and invalidates a whole L2: done by
+    // every workgroup, that costs more than the walk itself.  So the partials
+    // travel only through device-scope atomic stores and loads, which write
+    // through and read past the L2, and the ordering is made explicit: every
+    // store of the workgroup has completed before its arrival is counted, and
+    // the last workgroup reads only after its count came back.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) {   // ... before its arrival is counted
-        const int prev = __hip_atomic_fetch_add(a.counters + unit, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        const int prev = __hip_atomic_fetch_add(a.counters + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sm.last = prev == splits - 1;
     }
     __syncthreads();
     if (!sm.last) return;
-    __threadfence();
     auto ld = [](const float* p) {
         return __uint_as_float(__hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     };
@@ -782,15 +790,32 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
         const int r = e / D, d = e % D;
         const float vn = D == 64 ? v_new : __shfl(v_new, d, 64);
         if (r >= nh) continue;
-        float m = kNegInf;
-        for (int q = 0; q < splits; ++q) m = fmaxf(m, ld(a.part_ml + 2 * (pbase + (size_t)q * 4 + r)));
-        float o = 0.f, l = 0.f;
-        if (m != kNegInf) {
-            for (int q = 0; q < splits; ++q) {
-                const size_t row = pbase + (size_t)q * 4 + r;
-                const float f = __builtin_amdgcn_exp2f(ld(a.part_ml + 2 * row) - m);
-                o += f * ld(a.part_o + row * D + d);
-                l += f * ld(a.part_ml + 2 * row + 1);
+        // the partials in batches of 8 splits whose loads are in flight
+        // together, each batch merged into the running (m, l, o)
+        float m = kNegInf, o = 0.f, l = 0.f;
+        for (int q0 = 0; q0 < splits; q0 += 8) {
+            float mq[8], lq[8], oq[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const size_t row = pbase + (size_t)min(q0 + j, splits - 1) * 4 + r;
+                mq[j] = ld(a.part_ml + 2 * row);
+                lq[j] = ld(a.part_ml + 2 * row + 1);
+                oq[j] = ld(a.part_o + row * D + d);
+            }
+            float mb = m;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mb = q0 + j < splits ? fmaxf(mb, mq[j]) : mb;
+            if (mb != kNegInf) {  // (exp2 of -inf is 0: empty partials drop out)
+                const float f = __builtin_amdgcn_exp2f(m - mb);
+                o *= f;
+                l *= f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float fj = q0 + j < splits ? __builtin_amdgcn_exp2f(mq[j] - mb) : 0.f;
+                    o += fj * oq[j];
+                    l += fj * lq[j];
+                }
+                m = mb;
             }
         }
         finish(r, d, r == 0 ? sn[0] : r == 1 ? sn[1] : r == 2 ? sn[2] : sn[3], vn, m, l, o);
@@ -804,7 +829,10 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     const int G = a.Hq / a.Hkv;
     const long long nblocks = (long long)a.B * a.Hkv * ((G + 3) / 4) * a.num_splits;
     if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_kernel<D>), dim3((unsigned)nblocks), dim3(128), 0, s, a);
+    if (decode_waves(a.B, a.Hq, a.Hkv) == 8)
+        hipLaunchKernelGGL((decode_kernel<D, 8>), dim3((unsigned)nblocks), dim3(512), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, 2>), dim3((unsigned)nblocks), dim3(128), 0, s, a);
     return hipGetLastError();
 }
 

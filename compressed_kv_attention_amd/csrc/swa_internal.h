@@ -150,16 +150,27 @@ inline DecodeWorkspace decode_workspace_layout(int B, int Hq, int Hkv, int D, in
     w.total = w.part_o + r256(units * splits * 4 * (size_t)D * sizeof(float));
     return w;
 }
-// Split count the library picks for num_splits == 0: enough workgroups for
-// two per compute unit when the batch alone does not provide them, each
-// split keeping at least one 64-row chunk of the walk.
+// Waves per decode workgroup.  A batch with at least 512 (batch row, kv head,
+// group of 4 query heads) units fills the chip with two-wave workgroups, each
+// wave walking every other 64-row chunk.  Smaller batches take eight waves
+// per workgroup, so a unit's chunks are walked side by side instead of one
+// after another and its waves merge through LDS.
+inline int decode_waves(int B, int Hq, int Hkv) {
+    const long long units = (long long)B * Hkv * ((Hq / Hkv + 3) / 4);
+    return units >= 512 ? 2 : 8;
+}
+// Split count the library picks for num_splits == 0: one, unless a unit's
+// walk would leave its eight waves more than two chunks each; then enough
+// splits for two chunks per wave, within 1024 workgroups.  (A split-K
+// combine costs about four dependent memory round trips, more than the walk
+// of two chunks.)
 inline int decode_auto_splits(int B, int Hq, int Hkv, int W, int S) {
     const long long units = (long long)B * Hkv * ((Hq / Hkv + 3) / 4);
-    const long long want = 512;  // 2 x 256 compute units
-    if (units <= 0 || units >= want) return 1;
-    long long s = (want + units - 1) / units;
-    const long long max_by_rows = ((long long)S + W + 63) / 64;
-    if (s > max_by_rows) s = max_by_rows;
+    if (units <= 0 || decode_waves(B, Hq, Hkv) != 8) return 1;
+    const long long chunks = ((long long)S + W + 63) / 64;
+    long long s = (chunks + 15) / 16;
+    const long long max_by_grid = 1024 / units;
+    if (s > max_by_grid) s = max_by_grid;
     return (int)(s < 1 ? 1 : s);
 }
 constexpr int kMaxDecodeSplits = 256;

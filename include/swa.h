@@ -161,9 +161,10 @@ typedef struct {
     int S;             /* sink cache capacity, >= 0                             */
     float scale;       /* 0 selects 1/sqrt(D)                                   */
     int num_splits;    /* split-K parts per (b, kv head) walk, 0..256.  0 lets  */
-                       /* the library choose: one part when B * Hkv * ceil(G/4) */
-                       /* workgroups reach 512, else enough parts for 512, at   */
-                       /* most one per 64 rows of S + W.  Parts are whole       */
+                       /* the library choose: one part, unless the batch has    */
+                       /* fewer than 512 (b, kv head, group of 4 query heads)   */
+                       /* units and S + W exceeds 1024 rows; then one part per  */
+                       /* 1024 rows, within 1024 workgroups.  Parts are whole   */
                        /* 16-row pieces; extra parts are empty.                 */
 } swa_decode_params;
 

@@ -152,8 +152,15 @@ def test_decode_workspace_sizes():
     r = lambda x: (x + 255) // 256 * 256
     assert size(B=1, num_splits=8) == r(units * 4) + r(units * 8 * 4 * 2 * 4) + r(units * 8 * 4 * 64 * 4)
     assert size(B=1, Hq=24, Hkv=4, num_splits=2) == r(8 * 4) + r(8 * 2 * 4 * 2 * 4) + r(8 * 2 * 4 * 64 * 4)
-    # automatic: at least 512 workgroups when the batch allows, one 64-row chunk per split at least
-    assert size(B=1) == r(units * 4) + r(units * 8 * 4 * 2 * 4) + r(units * 8 * 4 * 64 * 4)
+    # automatic: one split while the eight waves of a small batch's workgroup walk at most two 64-row chunks
+    # each (S + W <= 1024), else one split per 1024 rows, within 1024 workgroups
+    assert size(B=1) == 0
+    assert size(B=1, W=1024, S=0) == 0
+    assert size(B=1, W=1024, S=64) == r(units * 4) + r(units * 2 * 4 * 2 * 4) + r(units * 2 * 4 * 64 * 4)
+    assert size(B=1, W=8192, S=256) == r(units * 4) + r(units * 9 * 4 * 2 * 4) + r(units * 9 * 4 * 64 * 4)
+    big = 64 * 4                                          # 64 rows x 4 kv heads: 256 units, at most 4 splits
+    assert size(B=64, W=8192, S=256) == r(big * 4) + r(big * 4 * 4 * 2 * 4) + r(big * 4 * 4 * 64 * 4)
+    assert size(B=128, W=8192, S=256) == 0                 # 512 units: two-wave workgroups, one split
     dp = swa.DecodeParams(1, 16, 4, 64, 256, 256, 0.0, 8)
     args = [FAKE] * 14
     assert L.swa_attn_decode(ctypes.byref(dp), *args, None, 0, None) == swa.SWA_ERR_INVALID
