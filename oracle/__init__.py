@@ -62,6 +62,8 @@ def _load():
     lib.oracle_effective_kv_window.restype = LL
     lib.oracle_quantize.argtypes = [LL, I, P, P, P]
     lib.oracle_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, D, P, P]
+    lib.oracle_compressed_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, D, I, D, I,
+                                             P, P]
     _lib = lib
     return lib
 
@@ -244,3 +246,40 @@ def decode(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs
                       _ptr(rks), _ptr(rvs), _ptr(sk), _ptr(sv), _ptr(sks), _ptr(svs), _ptr(p),
                       _ptr(sl), float(scale), _ptr(out), _ptr(lse))
     return out, lse, rk, rv, rks, rvs
+
+
+COMPRESSED_STATE = ("ring_k", "ring_v", "pool_k", "pool_v", "front_k", "front_v")
+
+
+def compressed_decode_state(B, Hkv, D, W, P):
+    """An empty compressed decode state (fp64 row values; see compressed_decode)."""
+    return {"ring_k": np.zeros((B, Hkv, W, D)), "ring_v": np.zeros((B, Hkv, W, D)),
+            "pool_k": np.zeros((B, Hkv, P, D)), "pool_v": np.zeros((B, Hkv, P, D)),
+            "front_k": np.zeros((B, Hkv, D)), "front_v": np.zeros((B, Hkv, D))}
+
+
+def compressed_decode(q, k_new, k_pre, v_new, state, pos, block, theta=10000.0, rope_len=None, scale=None,
+                      quantize=True):
+    """O8: one compressed decode step.  q [B,Hq,D] and k_new [B,Hkv,D] rotated at pos, k_pre the same key
+    before rotation, v_new [B,Hkv,D].  state: dict of fp64 arrays ring_k/ring_v [B,Hkv,W,D], pool_k/pool_v
+    [B,Hkv,P,D], front_k/front_v [B,Hkv,D] (row values: dequantized codes, or exact values with
+    quantize=False).  Returns (out [B,Hq,D], lse [B,Hq], new state); the given state is not modified."""
+    lib = _load()
+    q = _f64(q)
+    B, Hq, Dm = q.shape
+    st = {k: np.array(state[k], dtype=np.float64, copy=True, order="C") for k in COMPRESSED_STATE}
+    Hkv, W = st["ring_k"].shape[1], st["ring_k"].shape[2]
+    P = st["pool_k"].shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dm)
+    if rope_len is None:
+        rope_len = 1 << 30
+    kn, kp, vn = _f64(k_new), _f64(k_pre), _f64(v_new)
+    p = np.ascontiguousarray(pos, dtype=np.int32)
+    out = np.empty((B, Hq, Dm), dtype=np.float64)
+    lse = np.empty((B, Hq), dtype=np.float64)
+    lib.oracle_compressed_decode(B, Hq, Hkv, Dm, W, P, int(block), _ptr(q), _ptr(kn), _ptr(kp), _ptr(vn),
+                                 _ptr(st["ring_k"]), _ptr(st["ring_v"]), _ptr(st["pool_k"]), _ptr(st["pool_v"]),
+                                 _ptr(st["front_k"]), _ptr(st["front_v"]), _ptr(p), float(theta), int(rope_len),
+                                 float(scale), int(bool(quantize)), _ptr(out), _ptr(lse))
+    return out, lse, st

@@ -33,6 +33,8 @@
 //   R-A13 int8 scheme: symmetric absmax/127 per 32 channels, round half even,
 //        clamp to +-127, zero group -> zero scale and zero codes.
 //   R-A14 decode ring: slot = position mod W; sinks live in their own cache.
+//   R-A15 compressed decode state: exact ring + pooled blocks (capacity P) +
+//        frontier sums of the block in progress (see O8).
 
 #include <cmath>
 #include <cstdint>
@@ -423,6 +425,106 @@ void oracle_decode(int B, int Hq, int Hkv, int D, int W, int S, const double* q,
         for (size_t j = 0; j < n; ++j) {
             keys[j] = kd.data() + j * D;
             vals[j] = vd.data() + j * D;
+        }
+        attend_row(q + static_cast<size_t>(bh) * D, keys, vals, D, scale,
+                   out + static_cast<size_t>(bh) * D, lse ? lse + bh : nullptr);
+    }
+}
+
+// O8: one decode step of the compressed variant.  [CA §"Two kinds of columns,
+// pooled blocks and exact recent keys"]: the columns are the pooled blocks
+// that have cleared the window, (j + 1) * b <= pos - W + 1, then the exact
+// keys of the window, positions max(0, pos - W + 1) .. pos (no sinks,
+// reading R-A9).  [CA §"Pool before rotating, not after"]: a pooled key is
+// the mean of its block's keys BEFORE rotation, rotated once at
+// min(j * b + b/2, rope_len - 1); the pooled value is the mean of the values.
+// [CA §"So what happened ?"]: blocks join one at a time as they clear the
+// window.  Reading R-A15 (the decode-side state, which the pages only name,
+// as the compressor frontier of [DS §磁盘 KV 缓存]): per (sequence, kv head)
+// the cache holds the exact ring (slot = position mod W, post-RoPE keys), the
+// pooled blocks in order of j (capacity P; a block with j >= P is dropped and
+// at most P blocks are visible), and the frontier: the running sums of the
+// pre-RoPE keys and of the values of the block in progress.  A step at
+// position pos (steps of one sequence come at consecutive positions) first
+// appends: ring slot pos % W takes (k_new, v_new); the frontier restarts at
+// pos % b == 0 and adds (k_pre, v_new); at pos % b == b - 1 the block
+// j = pos / b is complete and is pooled into slot j.  Then the query attends.
+// A block completed at pos is not visible before pos + W, so the order of
+// pooling and attending within a step does not matter.
+//   q [B,Hq,D] (rotated at pos), k_new [B,Hkv,D] (rotated at pos), k_pre
+//   [B,Hkv,D] (the same key before rotation), v_new [B,Hkv,D]: fp64 holding
+//   the values the GPU receives.  ring_k/ring_v [B,Hkv,W,D], pool_k/pool_v
+//   [B,Hkv,P,D]: row values in fp64; with quantize != 0 every stored row is
+//   the O6 quantization of its fp32-rounded value, dequantized as code * scale
+//   (the int8 cache), else the exact value.  front_k/front_v [B,Hkv,D] fp64.
+//   Every state array is UPDATED in place.  pos < 0 appends nothing and sees
+//   no column.  out [B,Hq,D], lse [B,Hq] or NULL.
+void oracle_compressed_decode(int B, int Hq, int Hkv, int D, int W, int P, int block,
+                              const double* q, const double* k_new, const double* k_pre,
+                              const double* v_new, double* ring_k, double* ring_v, double* pool_k,
+                              double* pool_v, double* front_k, double* front_v, const int32_t* pos,
+                              double theta, int rope_len, double scale, int quantize, double* out,
+                              double* lse) {
+    const int G = Hq / Hkv;
+    auto store = [&](const double* x, double* row) {
+        if (!quantize) {
+            for (int d = 0; d < D; ++d) row[d] = x[d];
+            return;
+        }
+        std::vector<float> xf(D), xs(D / 32);
+        std::vector<int8_t> xq(D);
+        for (int d = 0; d < D; ++d) xf[d] = static_cast<float>(x[d]);
+        oracle_quantize(1, D, xf.data(), xq.data(), xs.data());
+        for (int d = 0; d < D; ++d) row[d] = static_cast<double>(xq[d]) * static_cast<double>(xs[d / 32]);
+    };
+    for (int b = 0; b < B; ++b) {
+        const long long p = pos[b];
+        if (p < 0) continue;
+        for (int h = 0; h < Hkv; ++h) {
+            const size_t nk = static_cast<size_t>(b) * Hkv + h;
+            const size_t slot = nk * W + static_cast<size_t>(p % W);
+            store(k_new + nk * D, ring_k + slot * D);
+            store(v_new + nk * D, ring_v + slot * D);
+            double* fk = front_k + nk * D;
+            double* fv = front_v + nk * D;
+            for (int d = 0; d < D; ++d) {
+                fk[d] = (p % block == 0 ? 0.0 : fk[d]) + k_pre[nk * D + d];
+                fv[d] = (p % block == 0 ? 0.0 : fv[d]) + v_new[nk * D + d];
+            }
+            const long long j = p / block;
+            if (p % block == block - 1 && j < P) {
+                std::vector<double> mk(D), mv(D), rk(D);
+                for (int d = 0; d < D; ++d) {
+                    mk[d] = fk[d] / block;
+                    mv[d] = fv[d] / block;
+                }
+                long long mid = j * block + block / 2;
+                if (mid > rope_len - 1) mid = rope_len - 1;
+                if (theta > 0.0) rope_rotate(mk.data(), rk.data(), D, theta, mid);
+                else rk = mk;
+                store(rk.data(), pool_k + (nk * P + j) * D);
+                store(mv.data(), pool_v + (nk * P + j) * D);
+            }
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int bh = 0; bh < B * Hq; ++bh) {
+        const int b = bh / Hq;
+        const int hk = (bh % Hq) / G;
+        const size_t nk = static_cast<size_t>(b) * Hkv + hk;
+        const long long p = pos[b];
+        std::vector<const double*> keys, vals;
+        if (p >= 0) {
+            for (long long j = 0; j < P; ++j) {            // pooled columns first
+                if (!visible_pooled(static_cast<int>(p), static_cast<int>(j), W, block)) break;
+                keys.push_back(pool_k + (nk * P + j) * D);
+                vals.push_back(pool_v + (nk * P + j) * D);
+            }
+            for (long long t = (p - W + 1 > 0 ? p - W + 1 : 0); t <= p; ++t) {   // then the window
+                const size_t row = nk * W + static_cast<size_t>(t % W);
+                keys.push_back(ring_k + row * D);
+                vals.push_back(ring_v + row * D);
+            }
         }
         attend_row(q + static_cast<size_t>(bh) * D, keys, vals, D, scale,
                    out + static_cast<size_t>(bh) * D, lse ? lse + bh : nullptr);

@@ -527,3 +527,116 @@ def test_decode_equals_prefill_row_with_sink_prefix():
     prefix[0, :sl] = 1
     ref, _ = oracle.prefill(Q, K, V, np.ones((1, T), np.int32), prefix, W, rows=[p])
     np.testing.assert_allclose(out[0, 0], ref[0], rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# O8 compressed decode  [CA §"Two kinds of columns, pooled blocks and exact
+# recent keys", §"Pool before rotating, not after", §"So what happened ?"]
+# --------------------------------------------------------------------------
+
+def _compressed_sequence(q, k, v, W, b, P, theta, rope_len, quantize, t_end=None):
+    """Run O8 from an empty state over positions 0 .. t_end-1 of q/k/v [B,H,T,D] (pre-RoPE); q and k are
+    rotated at their position with O2 before each step.  Returns the outputs [B,Hq,T,D], lse and the state."""
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    t_end = T if t_end is None else t_end
+    st = oracle.compressed_decode_state(B, Hkv, D, W, P)
+    outs, lses = [], []
+    for t in range(t_end):
+        pos = np.full(B, t, np.int32)
+        qr = np.stack([oracle.rope(q[bb, :, t], np.full(Hq, t), theta) for bb in range(B)])
+        kr = np.stack([oracle.rope(k[bb, :, t], np.full(Hkv, t), theta) for bb in range(B)])
+        o, l, st = oracle.compressed_decode(qr, kr, k[:, :, t], v[:, :, t], st, pos, b, theta=theta,
+                                            rope_len=rope_len, quantize=quantize)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs, axis=2), np.stack(lses, axis=2), st
+
+
+@pytest.mark.parametrize("W,b,rope_len", [(5, 3, 41), (8, 4, 41), (8, 4, 20), (3, 1, 41), (50, 4, 41)])
+def test_compressed_decode_sequence_equals_compressed_prefill(W, b, rope_len):
+    # Decoding a sequence token by token from an empty cache reproduces every row
+    # of the compressed prefill over the same pre-RoPE keys: the frontier, the
+    # pooling at block completion, the midpoint rotation, the visibility and
+    # the ring slots all have to agree with the pooled-then-attend definition.
+    B, Hq, Hkv, T, D = 2, 4, 2, 41, 16
+    q, k, v = _case(B, Hq, Hkv, T, D, seed=40 + W + b)
+    P = (T + b - 1) // b
+    out, lse, _ = _compressed_sequence(q, k, v, W, b, P, 1e4, rope_len, quantize=False)
+    ref, ref_lse = oracle.compressed_prefill(q, k, v, window=W, block=b, theta=1e4, rope_len=rope_len)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-13)
+
+
+def test_compressed_decode_block1_is_full_causal_attention():
+    # b = 1: each pooled block is one key rotated at its own position, so the
+    # columns cover [0, t] once each: causal attention from the library.
+    B, H, T, D = 1, 2, 30, 8
+    q, k, v = _case(B, H, H, T, D, seed=47)
+    out, _, _ = _compressed_sequence(q, k, v, 4, 1, T, 1e4, T, quantize=False)
+    pos = np.arange(T)
+    qr = np.stack([oracle.rope(q[0, h], pos, 1e4) for h in range(H)])[None]
+    kr = np.stack([oracle.rope(k[0, h], pos, 1e4) for h in range(H)])[None]
+    np.testing.assert_allclose(out, sdpa(qr, kr, v, causal=True), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("b,pooled", [(4, 960), (16, 240)])
+def test_compressed_decode_column_count_figure(b, pooled):
+    # [CA §"So what happened ?"]: at 4K positions with a 256 window the last
+    # token reads 960 pooled blocks (block 4) + 256 exact keys = 1216 columns,
+    # 1216 / 4096 of the 4 MiB cache, about 1.2 MiB.  With q = 0 the output is
+    # the plain mean of the visible values and exp(lse) counts the columns.
+    T, W, D = 4096, 256, 4
+    rng = np.random.default_rng(48)
+    k, v = rng.standard_normal((2, 1, 1, T, D))
+    q = np.zeros((1, 1, T, D))
+    st = oracle.compressed_decode_state(1, 1, D, W, T // b)
+    for t in range(T):
+        pos = np.array([t], np.int32)
+        o, lse, st = oracle.compressed_decode(q[:, :, t], oracle.rope(k[0, :, t], [t], 1e4)[None], k[:, :, t],
+                                              v[:, :, t], st, pos, b, theta=1e4, quantize=False)
+    assert round(math.exp(lse[0, 0])) == pooled + W
+    cols = np.concatenate([v[0, 0].reshape(T // b, b, D).mean(axis=1)[:pooled], v[0, 0, T - W:]])
+    np.testing.assert_allclose(o[0, 0], cols.mean(axis=0), rtol=1e-12, atol=1e-14)
+    assert 4.0 * (pooled + W) / T == (1.1875 if b == 4 else 0.484375)
+
+
+def test_compressed_decode_quantized_state_and_edges():
+    B, Hq, Hkv, T, D, W, b = 2, 2, 1, 37, 32, 6, 4
+    q, k, v = _case(B, Hq, Hkv, T, D, seed=49)
+    P = T // b                                          # the last, partial block has no slot
+    _, _, st_exact = _compressed_sequence(q, k, v, W, b, P, 1e4, T, quantize=False)
+    out_q, _, st_q = _compressed_sequence(q, k, v, W, b, P, 1e4, T, quantize=True)
+    out_x, _, _ = _compressed_sequence(q, k, v, W, b, P, 1e4, T, quantize=False)
+    # every stored row of the int8 cache is the O6 quantization of the exact row
+    for name in ("ring_k", "ring_v", "pool_k", "pool_v"):
+        x = st_exact[name].reshape(-1, D)
+        xq, xs = oracle.quantize(x.astype(np.float32))
+        np.testing.assert_array_equal(st_q[name].reshape(-1, D), xq.astype(np.float64) * np.repeat(xs, 32, 1))
+    # the frontier holds the sum of the partial block's pre-RoPE keys and values
+    lo = (T - 1) // b * b
+    np.testing.assert_allclose(st_exact["front_k"], k[:, :, lo:T].sum(axis=2), rtol=1e-14)
+    np.testing.assert_allclose(st_exact["front_v"], v[:, :, lo:T].sum(axis=2), rtol=1e-14)
+    # int8 caches change the output by no more than the quantization noise
+    assert np.abs(out_q - out_x).max() < 0.05
+    # pos < 0: nothing appended, no column visible
+    qr = np.ones((B, Hq, D))
+    o, lse, st2 = oracle.compressed_decode(qr, k[:, :, 0], k[:, :, 0], v[:, :, 0], st_q,
+                                           np.array([-1, -5], np.int32), b, theta=1e4, quantize=True)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    for name in oracle.COMPRESSED_STATE:
+        np.testing.assert_array_equal(st2[name], st_q[name])
+
+
+def test_compressed_decode_pool_capacity_drops_later_blocks():
+    # blocks past the pooled cache's capacity P are dropped: at most P pooled columns
+    T, W, b, D, P = 60, 4, 4, 8, 5
+    rng = np.random.default_rng(50)
+    k, v = rng.standard_normal((2, 1, 1, T, D))
+    st = oracle.compressed_decode_state(1, 1, D, W, P)
+    for t in range(T):
+        o, lse, st = oracle.compressed_decode(np.zeros((1, 1, D)), k[:, :, t], k[:, :, t], v[:, :, t], st,
+                                              np.array([t], np.int32), b, theta=0.0, quantize=False)
+        n_pool = min(P, max(0, (t - W + 1) // b))
+        assert round(math.exp(lse[0, 0])) == n_pool + min(W, t + 1)
+    np.testing.assert_allclose(st["pool_v"][0, 0], v[0, 0, :P * b].reshape(P, b, D).mean(axis=1), rtol=1e-14)
