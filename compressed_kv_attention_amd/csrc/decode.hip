@@ -113,6 +113,11 @@ __device__ __forceinline__ u32x4 gload_b128_untracked(const void* p) {
     asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
     return r;
 }
+__device__ __forceinline__ uint32_t gload_b32_untracked(const void* p) {
+    uint32_t r;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
 __device__ __forceinline__ uint32_t gload_u16_untracked(const void* p) {
     uint32_t r;
     asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
@@ -168,7 +173,16 @@ struct DecSmem {
 // which the walk over positions [first, pos - 1] never reads); it joins the
 // final merge as one more exact softmax partial, so the walk needs no
 // per-lane special case.
-template <int D, int NW>
+//
+// Compressed mode (COMP): the sink cache is the cache of pooled blocks, of
+// which the first floor((pos - W + 1) / b) -- those that have cleared the
+// window -- are walked, and the ring holds the window from position
+// max(0, pos - W + 1).  The appending wave also adds the new token's pre-RoPE
+// key and its value to the frontier sums of the block in progress and, when
+// the token completes its block, stores the block's mean (the key rotated at
+// the block midpoint) quantized into the block's pooled slot; that slot is
+// not walked before position pos + W.
+template <int D, int NW, bool COMP>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(DecodeArgs a) {
     constexpr int NI = D / 4;       // 4-channel instructions per row
     constexpr int GROUPS = D / 32;  // scale groups per row
@@ -201,8 +215,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     const int W = a.W, S = a.S;
     const int pos_in = a.pos[b];
     const int pos = pos_in < 0 ? -1 : pos_in;  // a negative position appends nothing and sees only sinks
-    int sl = a.sink_len ? a.sink_len[b] : S;
-    sl = sl < 0 ? 0 : (sl > S ? S : sl);
+    int sl;
+    if constexpr (COMP) {
+        // pooled blocks that have cleared the window: (j + 1) * b <= pos - W + 1
+        const int cleared = pos - W + 1;
+        sl = cleared >= a.block ? min(cleared / a.block, S) : 0;
+    } else {
+        sl = a.sink_len ? a.sink_len[b] : S;
+        sl = sl < 0 ? 0 : (sl > S ? S : sl);
+    }
     const size_t bh = (size_t)b * a.Hkv + hkv;
     int8_t* rk = a.ring_k + bh * W * D;
     int8_t* rv = a.ring_v + bh * W * D;
@@ -216,7 +237,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
 
     // rows: sinks [0, sl), then ring positions [first, pos]; with an append
     // the last of them (position pos) is merged from registers at the end
-    const int first = max(sl, pos - W + 1);
+    const int first = COMP ? max(0, pos - W + 1) : max(sl, pos - W + 1);
     const int n_ring = pos >= first ? pos - first + 1 : 0;
     const bool has_new = append && n_ring > 0;
     const int n_ring_mem = n_ring - (has_new ? 1 : 0);  // ring rows read from the cache
@@ -279,6 +300,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     const uint16_t* kn_src = append ? (const uint16_t*)a.k_new + bh * D : (const uint16_t*)a.q;
     const uint16_t* vn_src = append ? (const uint16_t*)a.v_new + bh * D : (const uint16_t*)a.q;
     uint32_t xk = gload_u16_untracked(kn_src + lane % D), xv = gload_u16_untracked(vn_src + lane % D);
+    // compressed mode: the pre-RoPE key and the frontier sums of this lane's
+    // channel (every (batch row, kv head) has them, so the loads stay in bounds)
+    uint32_t xkp = 0, xfk = 0, xfv = 0;
+    if constexpr (COMP) {
+        xkp = gload_u16_untracked((const uint16_t*)a.k_pre + bh * D + lane % D);
+        xfk = gload_b32_untracked(a.front_k + bh * D + lane % D);
+        xfv = gload_b32_untracked(a.front_v + bh * D + lane % D);
+    }
 
     // DMA of chunk ci into buffer bi: NKI instructions each for K and V (RPI
     // rows of CPR pieces), GROUPS each for the two scale arrays.  Rows past a
@@ -340,6 +369,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     for (int j = 0; j < NI / 2; ++j) tie(qraw[j]);
     tie(xk);
     tie(xv);
+    tie(xkp);
+    tie(xfk);
+    tie(xfv);
     // q is scaled by a power of two (per head, exact) that brings its largest
     // magnitude into [2^13, 2^14): the f16 operand then neither overflows nor
     // drops the low bits of small values (bf16 carries 8 significant bits, f16
@@ -675,6 +707,44 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
             rvs[(size_t)slot * GROUPS + lane / 32] = scv;
         }
     }
+    if constexpr (COMP) {
+        if (append && hs == 0 && sp == 0 && wave == 0) {
+            const int ch = lane % D;
+            const int blk = a.block;
+            const bool restart = pos % blk == 0;
+            const float fk = (restart ? 0.f : __uint_as_float(xfk)) + bf16_bits_to_f32((uint16_t)xkp);
+            const float fv = (restart ? 0.f : __uint_as_float(xfv)) + bf16_bits_to_f32((uint16_t)xv);
+            if (lane < D) {
+                a.front_k[bh * D + ch] = fk;
+                a.front_v[bh * D + ch] = fv;
+            }
+            const int j = pos / blk;
+            if (pos % blk == blk - 1 && j < S) {
+                // the completed block: mean of its pre-RoPE keys rotated at the
+                // block midpoint (rotate-half pairing: channel ch with ch ^ D/2)
+                const float mk = fk / (float)blk, mv = fv / (float)blk;
+                const float other = __shfl_xor(mk, D / 2, 64);
+                float rk = mk;
+                if (a.rope_cos) {
+                    const int mid = min(j * blk + blk / 2, a.rope_len - 1);
+                    const int i = ch % (D / 2);
+                    const float cs = a.rope_cos[(size_t)mid * (D / 2) + i], sn = a.rope_sin[(size_t)mid * (D / 2) + i];
+                    rk = ch < D / 2 ? __builtin_fmaf(mk, cs, -other * sn) : __builtin_fmaf(mk, cs, other * sn);
+                }
+                float spk, spv;
+                const int cpk = quantize_lane(rk, spk), cpv = quantize_lane(mv, spv);
+                const size_t row = bh * S + j;
+                if (lane < D) {
+                    a.pool_k[row * D + ch] = (int8_t)cpk;
+                    a.pool_v[row * D + ch] = (int8_t)cpv;
+                    if ((lane & 31) == 0) {
+                        a.pool_ks[row * GROUPS + lane / 32] = spk;
+                        a.pool_vs[row * GROUPS + lane / 32] = spv;
+                    }
+                }
+            }
+        }
+    }
     SWA_TRACE(4);
 
     // Merge of the waves: each leaves its per-head partial in LDS, in final
@@ -829,10 +899,14 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     const int G = a.Hq / a.Hkv;
     const long long nblocks = (long long)a.B * a.Hkv * ((G + 3) / 4) * a.num_splits;
     if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (decode_waves(a.B, a.Hq, a.Hkv) == 8)
-        hipLaunchKernelGGL((decode_kernel<D, 8>), dim3((unsigned)nblocks), dim3(512), 0, s, a);
-    else
-        hipLaunchKernelGGL((decode_kernel<D, 2>), dim3((unsigned)nblocks), dim3(128), 0, s, a);
+    const bool wide = decode_waves(a.B, a.Hq, a.Hkv) == 8;
+    if (a.block > 0) {
+        if (wide) hipLaunchKernelGGL((decode_kernel<D, 8, true>), dim3((unsigned)nblocks), dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((decode_kernel<D, 2, true>), dim3((unsigned)nblocks), dim3(128), 0, s, a);
+    } else {
+        if (wide) hipLaunchKernelGGL((decode_kernel<D, 8, false>), dim3((unsigned)nblocks), dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((decode_kernel<D, 2, false>), dim3((unsigned)nblocks), dim3(128), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -464,6 +464,54 @@ int swa_attn_decode_noalloc(const swa_decode_params* p, const void* q, const voi
     return hip_status(swa::launch_decode_noalloc(a, wl, (hipStream_t)stream), "swa_attn_decode_noalloc launch");
 }
 
+int swa_attn_decode_compressed(const swa_decode_params* p, int block, const float* rope_cos, const float* rope_sin,
+                               int rope_len, const void* q, const void* k_new, const void* k_new_pre,
+                               const void* v_new, int8_t* ring_k, int8_t* ring_v, float* ring_ks, float* ring_vs,
+                               int8_t* pool_k, int8_t* pool_v, float* pool_ks, float* pool_vs, float* front_k,
+                               float* front_v, const int32_t* pos, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    REQUIRE(block >= 1, "block must be >= 1 (got %d)", block);
+    REQUIRE((rope_cos == nullptr) == (rope_sin == nullptr), "rope_cos and rope_sin must both be given or both be NULL");
+    REQUIRE(rope_cos == nullptr || rope_len >= 1, "rope_len must be >= 1 with a table (got %d)", rope_len);
+    swa::DecodeArgs a;
+    swa::DecodeWorkspace wl;
+    bool empty;
+    const int rc = check_decode(p, q, k_new, v_new, ring_k, ring_v, ring_ks, ring_vs, pool_k, pool_v, pool_ks,
+                                pool_vs, pos, nullptr, out, a, wl, empty);
+    if (rc != SWA_OK) return rc;
+    if (empty) return ok();
+    REQUIRE_PTR(k_new);
+    REQUIRE_PTR(v_new);
+    REQUIRE_PTR(k_new_pre);
+    REQUIRE_PTR(front_k);
+    REQUIRE_PTR(front_v);
+    OPTIONAL_PTR(rope_cos);
+    OPTIONAL_PTR(rope_sin);
+    a.block = block;
+    a.k_pre = k_new_pre;
+    a.front_k = front_k;
+    a.front_v = front_v;
+    a.pool_k = p->S > 0 ? pool_k : nullptr;
+    a.pool_v = p->S > 0 ? pool_v : nullptr;
+    a.pool_ks = p->S > 0 ? pool_ks : nullptr;
+    a.pool_vs = p->S > 0 ? pool_vs : nullptr;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
+    a.rope_len = rope_cos ? rope_len : 0;
+    if (wl.total > 0) {
+        REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 255u) == 0,
+                "workspace must be a 256-byte aligned buffer of swa_decode_workspace_size() bytes (%d splits)",
+                a.num_splits);
+        REQUIRE(workspace_bytes >= wl.total, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                wl.total);
+        char* ws = (char*)workspace;
+        a.counters = (int*)(ws + wl.counters);
+        a.part_ml = (float*)(ws + wl.part_ml);
+        a.part_o = (float*)(ws + wl.part_o);
+    }
+    return hip_status(swa::launch_decode(a, (hipStream_t)stream), "swa_attn_decode_compressed launch");
+}
+
 long long swa_kv_budget_window(long long d_model, long long attn_dim, long long num_heads, long long num_kv_heads,
                                long long num_layers, long long sites, long long max_seq_len) {
     if (d_model <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_layers <= 0 || sites < 0 || max_seq_len <= 0 ||

@@ -133,6 +133,23 @@ struct DecodeArgs {
     int B, Hq, Hkv, D, W, S;
     int num_splits;  // >= 1 (the entry point resolves 0 = automatic)
     float scale;
+    // Compressed mode (block > 0): the sink arrays are the pooled-block cache
+    // (capacity S rows, written through pool_* when a block completes),
+    // k_pre [B][Hkv][D] bf16 is the appended key before rotation, front_k /
+    // front_v [B][Hkv][D] fp32 hold the running sums of the block in progress,
+    // and rope_cos / rope_sin [rope_len][D/2] (or NULL: no rotation) rotate a
+    // pooled key at its block midpoint.
+    int block;
+    const void* k_pre;
+    float* front_k;
+    float* front_v;
+    int8_t* pool_k;
+    int8_t* pool_v;
+    float* pool_ks;
+    float* pool_vs;
+    const float* rope_cos;
+    const float* rope_sin;
+    int rope_len;
 };
 // Workspace of a decode with `splits` parts: [counters][partial m, l][partial o],
 // each part 256-byte aligned; 0 bytes when splits == 1.

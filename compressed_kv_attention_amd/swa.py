@@ -22,7 +22,7 @@ SWA_F32, SWA_BF16 = 0, 1
 EXPORTS = ("swa_last_error", "swa_version", "swa_prefill_workspace_size", "swa_attn_prefill", "swa_debug_visibility", "swa_rope_table",
            "swa_rope_table_host",
            "kv_pool_compress_rope", "swa_kv_quantize", "swa_decode_workspace_size", "swa_attn_decode",
-           "swa_attn_decode_noalloc",
+           "swa_attn_decode_noalloc", "swa_attn_decode_compressed",
            "swa_kv_budget_window", "swa_effective_kv_window")
 
 
@@ -78,6 +78,8 @@ def lib():
     L.swa_attn_decode.restype = I
     L.swa_attn_decode_noalloc.argtypes = [ctypes.POINTER(DecodeParams)] + [P] * 14 + [P]
     L.swa_attn_decode_noalloc.restype = I
+    L.swa_attn_decode_compressed.argtypes = [ctypes.POINTER(DecodeParams), I, P, P, I] + [P] * 16 + [P, Z, P]
+    L.swa_attn_decode_compressed.restype = I
     L.swa_kv_budget_window.argtypes = [LL] * 7
     L.swa_kv_budget_window.restype = LL
     L.swa_effective_kv_window.argtypes = [LL] * 8
@@ -370,6 +372,54 @@ def decode_noalloc(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks,
                                          _ptr(ring_v), _ptr(ring_ks), _ptr(ring_vs), _ptr(sink_k), _ptr(sink_v),
                                          _ptr(sink_ks), _ptr(sink_vs), _ptr(pos), _ptr(sink_len), _ptr(out),
                                          _stream(q)))
+    return out
+
+
+def decode_compressed(q, k_new, k_new_pre, v_new, ring_k, ring_v, ring_ks, ring_vs, pool_k, pool_v, pool_ks, pool_vs,
+                      front_k, front_v, pos, block, rope=None, scale=0.0, num_splits=0, out=None, workspace=None):
+    """One compressed decode step (swa_attn_decode_compressed).  q [B,Hq,D] and k_new [B,Hkv,D] are rotated
+    at pos, k_new_pre is the same key before rotation, v_new [B,Hkv,D]; all bf16.  ring_* as in decode();
+    pool_k/pool_v [B,Hkv,P,D] int8 and pool_ks/pool_vs [B,Hkv,P,D/32] fp32 (P may be 0: pass None);
+    front_k/front_v [B,Hkv,D] fp32.  rope: (cos, sin) from rope_table(), or None for no rotation of the
+    pooled keys.  The caches and the frontier are updated in place.  Returns out [B,Hq,D] bf16."""
+    if q.dim() != 3 or ring_k.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and ring_k [B, Hkv, W, D]")
+    B, Hq, D = q.shape
+    Hkv = ring_k.shape[1]
+    if int(block) < 1:
+        raise ValueError(f"block must be >= 1 (got {block})")
+    if k_new is None or v_new is None or k_new_pre is None:
+        raise ValueError("k_new, k_new_pre and v_new are required")
+    _shape(k_new_pre, "k_new_pre", (B, Hkv, D))
+    _shape(front_k, "front_k", (B, Hkv, D))
+    _shape(front_v, "front_v", (B, Hkv, D))
+    _decode_checks(q, ring_k, ring_v, ring_ks, ring_vs, pool_k, pool_v, pool_ks, pool_vs, pos, None, k_new, v_new,
+                   out)
+    _dev(k_new_pre, "k_new_pre", torch.bfloat16)
+    _dev(front_k, "front_k", torch.float32)
+    _dev(front_v, "front_v", torch.float32)
+    cos, sin = rope if rope is not None else (None, None)
+    rope_len = 0
+    if cos is not None:
+        _shape(cos, "rope cos", (cos.shape[0], D // 2))
+        _shape(sin, "rope sin", (cos.shape[0], D // 2))
+        _dev(cos, "rope cos", torch.float32)
+        _dev(sin, "rope sin", torch.float32)
+        rope_len = cos.shape[0]
+    _same_device(q, ("k_new_pre", k_new_pre), ("front_k", front_k), ("front_v", front_v), ("rope cos", cos),
+                 ("rope sin", sin))
+    p = decode_params(q, ring_k, pool_k, scale, num_splits)
+    ws_bytes = lib().swa_decode_workspace_size(ctypes.byref(p))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = workspace.numel() * workspace.element_size() if (ws_bytes and workspace is not None) else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().swa_attn_decode_compressed(ctypes.byref(p), int(block), _ptr(cos), _ptr(sin), int(rope_len),
+                                            _ptr(q), _ptr(k_new), _ptr(k_new_pre), _ptr(v_new), _ptr(ring_k),
+                                            _ptr(ring_v), _ptr(ring_ks), _ptr(ring_vs), _ptr(pool_k), _ptr(pool_v),
+                                            _ptr(pool_ks), _ptr(pool_vs), _ptr(front_k), _ptr(front_v), _ptr(pos),
+                                            _ptr(out), _ptr(workspace) if ws_len else None, ws_len, _stream(q)))
     return out
 
 

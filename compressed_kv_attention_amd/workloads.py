@@ -159,3 +159,39 @@ def decode_case(seed=5, B=256, Hq=16, Hkv=4, D=64, W=256, S=256, pos_lo=512, pos
         out["sink_len"] = np.ascontiguousarray(sink_len, dtype=np.int32)
     out.update(dict(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, seed=seed))
     return out
+
+
+def compressed_decode_case(seed=6, B=256, Hq=16, Hkv=4, D=64, W=256, P=1024, block=4, pos_lo=0, pos_hi=4095):
+    """One layer of compressed-decode inputs: q [B,Hq,D] and k_new [B,Hkv,D] (standing for rotated values),
+    k_pre [B,Hkv,D] (standing for the key before rotation), v_new [B,Hkv,D], the pre-quantization ring and
+    pooled caches [B,Hkv,W|P,D] (bf16 values), frontier sums front_k/front_v [B,Hkv,D] (float32, the sum of
+    pos % block standard-normal rows' worth of spread) and pos [B]."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape in (("q", (B, Hq, D)), ("k_new", (B, Hkv, D)), ("k_pre", (B, Hkv, D)), ("v_new", (B, Hkv, D)),
+                        ("ring_k", (B, Hkv, W, D)), ("ring_v", (B, Hkv, W, D)),
+                        ("pool_k", (B, Hkv, P, D)), ("pool_v", (B, Hkv, P, D))):
+        bits, vals = bf16_round(_normals(rng, shape))
+        out[name] = vals
+        out[name + "_bits"] = bits
+    pos = rng.integers(pos_lo, pos_hi + 1, size=B).astype(np.int32)
+    spread = np.sqrt(np.maximum(pos % block, 1)).astype(np.float32)[:, None, None]
+    out["front_k"] = (_normals(rng, (B, Hkv, D)) * spread).astype(np.float32)
+    out["front_v"] = (_normals(rng, (B, Hkv, D)) * spread).astype(np.float32)
+    out["pos"] = pos
+    out.update(dict(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, P=P, block=block, seed=seed))
+    return out
+
+
+def compressed_decode_sequence(seed=7, B=3, Hq=4, Hkv=2, D=64, T=150):
+    """Per-step inputs of a decode run from an empty cache: q [T,B,Hq,D], k_new/k_pre/v_new [T,B,Hkv,D]
+    (bf16 values and bits)."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape in (("q", (T, B, Hq, D)), ("k_new", (T, B, Hkv, D)), ("k_pre", (T, B, Hkv, D)),
+                        ("v_new", (T, B, Hkv, D))):
+        bits, vals = bf16_round(_normals(rng, shape))
+        out[name] = vals
+        out[name + "_bits"] = bits
+    out.update(dict(B=B, Hq=Hq, Hkv=Hkv, D=D, T=T, seed=seed))
+    return out

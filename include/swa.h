@@ -196,6 +196,44 @@ int swa_attn_decode(const swa_decode_params* p,
                     void* out,                            /* [B,Hq,D] bf16                     */
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step of the compressed variant ([CA §"Two kinds of columns,   */
+/* pooled blocks and exact recent keys", §"Pool before rotating, not after"]).*/
+/* Per (b, kv head) the cache is an exact ring (as in swa_attn_decode), a    */
+/* pooled-block cache of capacity P = p->S rows, and the frontier: fp32      */
+/* running sums of the pre-RoPE keys and of the values of the block in       */
+/* progress (the compressor frontier of [DS §磁盘 KV 缓存]).  The step at     */
+/* position pos[b] (steps of one sequence come at consecutive positions):    */
+/*  1. quantizes k_new (rotated at pos) and v_new into ring slot pos % W;    */
+/*  2. sets the frontier to (k_new_pre, v_new) when pos % block == 0, else   */
+/*     adds them;                                                            */
+/*  3. when pos % block == block - 1 the block j = pos / block is complete:  */
+/*     if j < P, its mean key, rotated at min(j*block + block/2, rope_len-1) */
+/*     with the tables of swa_rope_table (no rotation when they are NULL),   */
+/*     and its mean value are quantized into pooled row j;                   */
+/*  4. the query attends over the pooled rows j < min(P, floor((pos - W + 1) */
+/*     / block)) -- the blocks that have cleared the window -- and the ring  */
+/*     positions [max(0, pos - W + 1), pos], one softmax.                    */
+/* A block completed at pos is first read at pos + W, so no step reads a row */
+/* it writes.  pos[b] < 0 appends nothing and gives out = 0.  Blocks with   */
+/* j >= P are dropped.  Quantization is that of swa_kv_quantize.  num_splits */
+/* and the workspace are those of swa_attn_decode for the same params.       */
+int swa_attn_decode_compressed(const swa_decode_params* p,   /* S = P, the pooled capacity     */
+                               int block,                    /* b >= 1                          */
+                               const float* rope_cos, const float* rope_sin, /* [rope_len,D/2] or NULL */
+                               int rope_len,
+                               const void* q,                /* [B,Hq,D] bf16, rotated at pos   */
+                               const void* k_new,            /* [B,Hkv,D] bf16, rotated at pos  */
+                               const void* k_new_pre,        /* [B,Hkv,D] bf16, before rotation */
+                               const void* v_new,            /* [B,Hkv,D] bf16                  */
+                               int8_t* ring_k, int8_t* ring_v,   /* [B,Hkv,W,D]                 */
+                               float* ring_ks, float* ring_vs,   /* [B,Hkv,W,D/32]              */
+                               int8_t* pool_k, int8_t* pool_v,   /* [B,Hkv,P,D] (NULL if P==0)  */
+                               float* pool_ks, float* pool_vs,   /* [B,Hkv,P,D/32]              */
+                               float* front_k, float* front_v,   /* [B,Hkv,D] fp32              */
+                               const int32_t* pos,           /* [B]                             */
+                               void* out,                    /* [B,Hq,D] bf16                   */
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* swa_attn_decode for callers that cannot allocate memory (code under HIP   */
 /* graph capture, tight serving loops, harnesses that forbid allocation):    */
 /* the same computation, kernels and results, with the split-K state kept in */

@@ -365,3 +365,48 @@ def test_pool_wrapper_rejects_bad_shapes():
     with pytest.raises(ValueError, match="rope_cos"):
         swa.pool_compress_rope(_t(1, 2, 32, 64), _t(1, 2, 32, 64), 4,
                                rope=(_t(32, 16, dtype=torch.float32), _t(32, 32, dtype=torch.float32)))
+
+
+def test_compressed_decode_validation():
+    L = swa.lib()
+    dp = swa.DecodeParams(2, 4, 2, 64, 8, 16, 0.0, 0)
+    P = [FAKE] * 16          # q, k_new, k_pre, v_new, ring x4, pool x4, front x2, pos, out
+
+    def call(block=4, cos=None, sin=None, rope_len=0, ptrs=None, params=dp):
+        rc = L.swa_attn_decode_compressed(ctypes.byref(params), block, cos, sin, rope_len, *(ptrs or P), None, 0,
+                                          None)
+        return rc, L.swa_last_error().decode()
+
+    assert call(block=0) == (swa.SWA_ERR_INVALID, call(block=0)[1]) and "block" in call(block=0)[1]
+    rc, msg = call(cos=FAKE)
+    assert rc == swa.SWA_ERR_INVALID and "rope_cos and rope_sin" in msg
+    rc, msg = call(cos=FAKE, sin=FAKE, rope_len=0)
+    assert rc == swa.SWA_ERR_INVALID and "rope_len" in msg
+    for i, name in ((2, "k_new_pre"), (12, "front_k"), (13, "front_v"), (1, "k_new")):
+        ptrs = list(P)
+        ptrs[i] = None
+        rc, msg = call(ptrs=ptrs)
+        assert rc == swa.SWA_ERR_INVALID and name.split("_pre")[0] in msg, (name, msg)
+    ptrs = list(P)
+    ptrs[8] = None                                    # pooled cache missing while P > 0
+    rc, msg = call(ptrs=ptrs)
+    assert rc == swa.SWA_ERR_INVALID and "sink_k" in msg
+    rc, msg = call(params=swa.DecodeParams(2, 4, 2, 48, 8, 16, 0.0, 0))
+    assert rc == swa.SWA_ERR_UNSUPPORTED
+
+
+def test_compressed_decode_wrapper_rejects_bad_shapes():
+    import torch
+    a = _decode_args()
+    kw = dict(q=a["q"], k_new=a["k_new"], k_new_pre=_t(3, 2, 64), v_new=a["v_new"], ring_k=a["ring_k"],
+              ring_v=a["ring_v"], ring_ks=a["ring_ks"], ring_vs=a["ring_vs"], pool_k=a["sink_k"],
+              pool_v=a["sink_v"], pool_ks=a["sink_ks"], pool_vs=a["sink_vs"],
+              front_k=_t(3, 2, 64, dtype=torch.float32), front_v=_t(3, 2, 64, dtype=torch.float32), pos=a["pos"],
+              block=4)
+    for over, what in ((dict(k_new_pre=_t(3, 2, 32)), "k_new_pre"), (dict(front_v=_t(3, 1, 64)), "front_v"),
+                       (dict(pool_vs=_t(3, 2, 7, 2, dtype=torch.float32)), "sink_vs"),
+                       (dict(block=0), "block"), (dict(k_new_pre=None), "k_new_pre")):
+        with pytest.raises(ValueError, match=what):
+            swa.decode_compressed(**dict(kw, **over))
+    with pytest.raises(ValueError, match="device tensor"):
+        swa.decode_compressed(**kw)
