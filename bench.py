@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--reps", type=int, default=20, help="iterations per timed graph when timing one kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16,decode_b1,decode_b8,decode_b32")
+    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16,decode_b1,decode_b8,decode_b32,decode_c4")
     ap.add_argument("--decode-splits", type=int, default=0,
                     help="num_splits of the batch-256 decode part (0: the library's choice)")
     ap.add_argument("--eager", action="store_true",
@@ -245,6 +245,54 @@ def main():
         p.reps = max(1, (args.reps * 12) // layers)
         return p
 
+    def make_compressed_decode(name, block=4, layers=12, B=256):
+        """The compressed decode step: B256 16q/4kv D64, window 256, pooled blocks of `block` (capacity for
+        4096 positions), positions 512..4095 (the 4K context of the compressed-cache figure); 12 layers of
+        caches.  Bytes counted: the rows each query walks (visible pooled blocks + window, codes and scales),
+        q, out, the appended token, the frontier read and write, and the pooled rows written."""
+        Hq, Hkv, D, W = 16, 4, 64, 256
+        P = 4096 // block
+        g = torch.Generator(device=dev)
+        g.manual_seed(6)
+        rng = np.random.default_rng(6)
+        pos_np = rng.integers(512, 4096, size=B).astype(np.int64)
+        pos = torch.from_numpy(pos_np.astype(np.int32)).to(dev)
+        rope = swa.rope_table(10000.0, 4096, D)
+        caches = []
+        for _ in range(layers):
+            c = {}
+            for nm, rows in (("ring_k", W), ("ring_v", W), ("pool_k", P), ("pool_v", P)):
+                x = torch.randn((B, Hkv, rows, D), generator=g, device=dev).to(torch.bfloat16)
+                c[nm], c[nm + "s"] = swa.kv_quantize(x)
+            for nm, shape in (("q", (B, Hq, D)), ("k_new", (B, Hkv, D)), ("k_pre", (B, Hkv, D)),
+                              ("v_new", (B, Hkv, D))):
+                c[nm] = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+            c["front_k"] = torch.randn((B, Hkv, D), generator=g, device=dev)
+            c["front_v"] = torch.randn((B, Hkv, D), generator=g, device=dev)
+            c["out"] = torch.empty_like(c["q"])
+            caches.append(c)
+        row = D + (D // 32) * 4                                   # int8 codes + fp32 scales of one row
+        n_vis = np.maximum(pos_np - W + 1, 0) // block
+        walked = (n_vis + np.minimum(W, pos_np + 1) - 1).sum()    # cached rows (the new token is in registers)
+        done = int((pos_np % block == block - 1).sum())
+        # per (b, kv head): the walked K and V rows; k_new, k_pre, v_new read (bf16), the ring rows written,
+        # the frontier sums read and written (fp32), and the pooled K and V rows of a completed block
+        per_layer = int(Hkv * (2 * row * walked + B * (3 * 2 * D + 2 * row + 2 * 2 * D * 4) + done * 2 * row)
+                        + 2 * B * Hq * D * 2)
+
+        def launch(i):
+            for c in caches:
+                swa.decode_compressed(c["q"], c["k_new"], c["k_pre"], c["v_new"], c["ring_k"], c["ring_v"],
+                                      c["ring_ks"], c["ring_vs"], c["pool_k"], c["pool_v"], c["pool_ks"],
+                                      c["pool_vs"], c["front_k"], c["front_v"], pos, block, rope=rope,
+                                      out=c["out"])
+        p = Part(name, launch, 1, 0.0, per_layer * layers, kernel="decode_kernel<64, 2, true>")
+        p.extra = dict(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, P=P, block=block, layers=layers, bytes_per_layer=per_layer,
+                       mean_walked_rows=round(float(walked) / B, 1))
+        p.tokens = B
+        p.launches = layers
+        return p
+
     t_setup = time.time()
     if "needle" in parts_wanted:
         parts["needle"] = make_prefill("needle", workloads.needle())
@@ -255,6 +303,8 @@ def main():
     for b in (1, 8, 32):
         if f"decode_b{b}" in parts_wanted:
             parts[f"decode_b{b}"] = make_decode(f"decode_b{b}", B=b)
+    if "decode_c4" in parts_wanted:
+        parts["decode_c4"] = make_compressed_decode("decode_c4", 4)
     if "packed" in parts_wanted:
         parts["packed"] = make_prefill("packed", workloads.packed())
     if "compressed16" in parts_wanted:
@@ -377,7 +427,9 @@ def main():
                                           "gbs": round(r["gbs"], 1), "frac_hbm_peak": round(r["frac_hbm_peak"], 4),
                                           "tokens_per_s": round(r["tokens_per_s"], 1)}
                             for n, r in sorted(results.items(), key=lambda kv: kv[1].get("B", 0))
-                            if n.startswith("decode")},
+                            if n.startswith("decode") and n != "decode_c4"},
+        "compressed_decode": {k: (round(v, 5) if isinstance(v, float) else v)
+                              for k, v in results.get("decode_c4", {}).items()},
         "packed": {"value": round(results.get("packed", {}).get("tflops", 0.0), 3), "unit": "TFLOP/s",
                    "frac_mfma_peak": round(results.get("packed", {}).get("frac_mfma_peak", 0.0), 5),
                    "us_per_call": round(results.get("packed", {}).get("ms", 0.0) * 1e3, 2),
