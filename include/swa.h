@@ -184,6 +184,16 @@ size_t swa_decode_workspace_size(const swa_decode_params* p);
 /* v_new are given they are first quantized into slot pos[b] % W of the ring. */
 /* Preconditions the device cannot check cheaply: sink_len[b] <= pos[b] (else */
 /* the ring counts as empty) and sink_len[b] <= S.                           */
+/* Numerics: the dot products run on f16 matrix instructions with fp32       */
+/* accumulation.  q enters as f16 after an exact power-of-two scaling per    */
+/* head (its largest magnitude lands in [2^13, 2^14)), so any finite q is    */
+/* taken; components below 2^-27 of the head's largest lose bits.  Each P.V  */
+/* weight enters as the f16 number p * s_v / 2^e, with s_v the row's V scale */
+/* of a 32-channel group and 2^e a power of two at least as large as every   */
+/* V scale of that group seen so far in the walk (p <= 2^8): rows whose      */
+/* p * s_v is below 2^(e-14) keep fewer bits, below 2^(e-25) they add 0 --   */
+/* a V group whose scale is 2^25 times smaller than the largest one of the   */
+/* window is counted as zero.                                                */
 int swa_attn_decode(const swa_decode_params* p,
                     const void* q,                        /* [B,Hq,D] bf16, already rotated   */
                     const void* k_new, const void* v_new, /* [B,Hkv,D] bf16, or both NULL      */
