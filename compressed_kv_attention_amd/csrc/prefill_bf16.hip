@@ -426,6 +426,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     f32x16 nbase;
 #pragma unroll
     for (int j = 0; j < 16; ++j) nbase[j] = row_vis ? -0.f : kNegInf;
+    // (kept in 16 registers: the compiler would otherwise hold one value and
+    // copy it into 16 registers before every fully visible sub-tile)
+    asm volatile("" : "+v"(nbase));
     f32x16 o[D / 32];
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) o[n] = f32x16{};
@@ -669,6 +672,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                     for (int j = 0; j < 16; ++j) sacc[j] -= up;
 #pragma unroll
                     for (int j = 0; j < 16; ++j) nbase[j] = row_vis ? -base : kNegInf;
+                    asm volatile("" : "+v"(nbase));
                 };
                 // bf16 weights exp2(u - base) and the sum of exactly those weights
                 // over this lane's keys (hidden pairs give exactly 0).
