@@ -62,6 +62,7 @@ def _load():
     lib.oracle_effective_kv_window.restype = LL
     lib.oracle_quantize.argtypes = [LL, I, P, P, P]
     lib.oracle_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, D, P, P]
+    lib.oracle_chunk_prefill.argtypes = [I, I, I, I, I, I, I] + [P] * 13 + [D, P, P]
     lib.oracle_compressed_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, D, I, D, I,
                                              P, P]
     _lib = lib
@@ -283,3 +284,35 @@ def compressed_decode(q, k_new, k_pre, v_new, state, pos, block, theta=10000.0, 
                                  _ptr(st["front_k"]), _ptr(st["front_v"]), _ptr(p), float(theta), int(rope_len),
                                  float(scale), int(bool(quantize)), _ptr(out), _ptr(lse))
     return out, lse, st
+
+
+def chunk_prefill(q, k, v, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos0, sink_len=None,
+                  scale=None):
+    """O9: a chunk q [B,Hq,Tc,D], k/v [B,Hkv,Tc,D] (float32 values) at positions pos0[b] .. + Tc - 1 over the
+    sink cache, the ring and itself; then the ring takes the chunk's last W tokens.  The ring arrays are
+    copied, updated and returned: (out [B,Hq,Tc,D], lse [B,Hq,Tc], ring_k, ring_v, ring_ks, ring_vs)."""
+    lib = _load()
+    q = _f64(q)
+    B, Hq, Tc, Dm = q.shape
+    Hkv, W = ring_k.shape[1], ring_k.shape[2]
+    S = sink_k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dm)
+    rk = np.array(ring_k, dtype=np.int8, copy=True, order="C")
+    rv = np.array(ring_v, dtype=np.int8, copy=True, order="C")
+    rks = np.array(ring_ks, dtype=np.float32, copy=True, order="C")
+    rvs = np.array(ring_vs, dtype=np.float32, copy=True, order="C")
+    kk = np.ascontiguousarray(k, dtype=np.float32)
+    vv = np.ascontiguousarray(v, dtype=np.float32)
+    sk = np.ascontiguousarray(sink_k, dtype=np.int8)
+    sv = np.ascontiguousarray(sink_v, dtype=np.int8)
+    sks = np.ascontiguousarray(sink_ks, dtype=np.float32)
+    svs = np.ascontiguousarray(sink_vs, dtype=np.float32)
+    p0 = np.ascontiguousarray(pos0, dtype=np.int32)
+    sl = _opt(sink_len, np.int32)
+    out = np.empty((B, Hq, Tc, Dm), dtype=np.float64)
+    lse = np.empty((B, Hq, Tc), dtype=np.float64)
+    lib.oracle_chunk_prefill(B, Hq, Hkv, Dm, W, S, Tc, _ptr(q), _ptr(kk), _ptr(vv), _ptr(rk), _ptr(rv), _ptr(rks),
+                             _ptr(rvs), _ptr(sk), _ptr(sv), _ptr(sks), _ptr(svs), _ptr(p0), _ptr(sl), float(scale),
+                             _ptr(out), _ptr(lse))
+    return out, lse, rk, rv, rks, rvs

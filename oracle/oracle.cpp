@@ -35,6 +35,9 @@
 //   R-A14 decode ring: slot = position mod W; sinks live in their own cache.
 //   R-A15 compressed decode state: exact ring + pooled blocks (capacity P) +
 //        frontier sums of the block in progress (see O8).
+//   R-A20 chunked prefill: the chunk attends over the sinks, the ring as it
+//        was before the chunk, and its own unquantized keys; then the ring
+//        takes its last W tokens (see O9).
 
 #include <cmath>
 #include <cstdint>
@@ -529,6 +532,89 @@ void oracle_compressed_decode(int B, int Hq, int Hkv, int D, int W, int P, int b
         attend_row(q + static_cast<size_t>(bh) * D, keys, vals, D, scale,
                    out + static_cast<size_t>(bh) * D, lse ? lse + bh : nullptr);
     }
+}
+
+// O9: chunked prefill into existing caches.  Reading A20 (the pages name
+// chunked prefill -- [DS] runs long prompts in chunks of 4096 tokens,
+// "工作原理与配置方式" -- and [NW] "End-to-End Execution Flow" keeps in the
+// cache only what the mask can still show, but neither defines the step):
+// a chunk of Tc tokens at positions pos0 .. pos0 + Tc - 1 attends, with the
+// decode mask of [NS §"256-token 滑动窗口：源码走读"] (recent | sink, no
+// packing term), over the sink rows [0, sl) with sl = min(sink_len, pos0),
+// the ring positions [max(sl, t - W + 1), pos0 - 1] as the ring holds them
+// BEFORE the chunk, and the chunk's own keys [max(pos0, t - W + 1), t] as
+// given (not quantized); then the chunk's last min(W, Tc) tokens are
+// quantized (O6) into ring slots position mod W.  K/V of the caches are
+// dequantized in fp64 as code * scale.
+//   q [B,Hq,Tc,D] fp64 (rotated), k/v [B,Hkv,Tc,D] fp32 (k rotated); ring/sink
+//   caches as in O7 (the ring is UPDATED in place); pos0 [B], sink_len [B] or
+//   NULL (= S); out [B,Hq,Tc,D] fp64, lse [B,Hq,Tc] or NULL.
+void oracle_chunk_prefill(int B, int Hq, int Hkv, int D, int W, int S, int Tc, const double* q,
+                          const float* k, const float* v, int8_t* ring_k, int8_t* ring_v, float* ring_ks,
+                          float* ring_vs, const int8_t* sink_k, const int8_t* sink_v, const float* sink_ks,
+                          const float* sink_vs, const int32_t* pos0, const int32_t* sink_len, double scale,
+                          double* out, double* lse) {
+    const int G = Hq / Hkv;
+    const int groups = D / 32;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int bh = 0; bh < B * Hq; ++bh) {
+        const int b = bh / Hq;
+        const int hk = (bh % Hq) / G;
+        const size_t nk = static_cast<size_t>(b) * Hkv + hk;
+        const long long p0 = pos0[b];
+        long long sl = sink_len ? sink_len[b] : S;
+        if (sl > p0) sl = p0;
+        if (sl > S) sl = S;
+        if (sl < 0) sl = 0;
+        std::vector<double> kd, vd;  // dequantized sink and ring rows
+        std::vector<long long> kpos;  // their positions
+        auto add_row = [&](const int8_t* kc, const float* ks, const int8_t* vc, const float* vs, long long p) {
+            for (int d = 0; d < D; ++d) {
+                kd.push_back(static_cast<double>(kc[d]) * static_cast<double>(ks[d / 32]));
+                vd.push_back(static_cast<double>(vc[d]) * static_cast<double>(vs[d / 32]));
+            }
+            kpos.push_back(p);
+        };
+        for (long long s = 0; s < sl; ++s) {
+            const size_t row = nk * S + static_cast<size_t>(s);
+            add_row(sink_k + row * D, sink_ks + row * groups, sink_v + row * D, sink_vs + row * groups, -1);
+        }
+        for (long long p = (p0 - W + 1 > sl ? p0 - W + 1 : sl); p < p0; ++p) {
+            const size_t row = nk * W + static_cast<size_t>(p % W);
+            add_row(ring_k + row * D, ring_ks + row * groups, ring_v + row * D, ring_vs + row * groups, p);
+        }
+        std::vector<double> kc(static_cast<size_t>(Tc) * D), vc(static_cast<size_t>(Tc) * D);
+        for (size_t x = 0; x < kc.size(); ++x) {
+            kc[x] = k[nk * Tc * D + x];
+            vc[x] = v[nk * Tc * D + x];
+        }
+        for (int i = 0; i < Tc; ++i) {
+            const long long t = p0 + i;
+            std::vector<const double*> keys, vals;
+            for (size_t r = 0; r < kpos.size(); ++r) {
+                if (kpos[r] >= 0 && t - kpos[r] >= W) continue;   // sinks (-1) always; ring rows in the window
+                keys.push_back(kd.data() + r * D);
+                vals.push_back(vd.data() + r * D);
+            }
+            for (int j = 0; j <= i; ++j) {
+                if (t - (p0 + j) >= W) continue;
+                keys.push_back(kc.data() + static_cast<size_t>(j) * D);
+                vals.push_back(vc.data() + static_cast<size_t>(j) * D);
+            }
+            const size_t o = static_cast<size_t>(bh) * Tc + i;
+            attend_row(q + o * D, keys, vals, D, scale, out + o * D, lse ? lse + o : nullptr);
+        }
+    }
+    // the ring write: the chunk's last min(W, Tc) tokens, after every query has read the old ring
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hkv; ++h) {
+            const size_t nk = static_cast<size_t>(b) * Hkv + h;
+            for (int i = (Tc > W ? Tc - W : 0); i < Tc; ++i) {
+                const size_t slot = nk * W + static_cast<size_t>((pos0[b] + static_cast<long long>(i)) % W);
+                oracle_quantize(1, D, k + (nk * Tc + i) * D, ring_k + slot * D, ring_ks + slot * groups);
+                oracle_quantize(1, D, v + (nk * Tc + i) * D, ring_v + slot * D, ring_vs + slot * groups);
+            }
+        }
 }
 
 }  // extern "C"

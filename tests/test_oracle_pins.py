@@ -640,3 +640,86 @@ def test_compressed_decode_pool_capacity_drops_later_blocks():
         n_pool = min(P, max(0, (t - W + 1) // b))
         assert round(math.exp(lse[0, 0])) == n_pool + min(W, t + 1)
     np.testing.assert_allclose(st["pool_v"][0, 0], v[0, 0, :P * b].reshape(P, b, D).mean(axis=1), rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# O9 chunked prefill into existing caches (reading A20; decode mask of
+# [NS §"256-token 滑动窗口：源码走读"])
+# --------------------------------------------------------------------------
+
+def _dequant(codes, scales):
+    return codes.astype(np.float64) * np.repeat(scales.astype(np.float64), 32, axis=-1)
+
+
+@pytest.mark.parametrize("W,S,Tc,pos0,sink_len", [
+    (8, 5, 13, [5, 20, 40], [5, 3, 0]),      # empty ring after the sinks, a wrapped ring, no sinks
+    (8, 5, 3, [9, 30, 2], [5, 5, 5]),        # a chunk shorter than the window; sink_len > pos0 (clamped)
+    (64, 0, 20, [0, 7, 100], None),          # no sink cache; an empty cache at position 0
+])
+def test_chunk_prefill_equals_prefill_over_the_cached_sequence(W, S, Tc, pos0, sink_len):
+    # The chunk's queries see exactly what a prefill over the whole sequence
+    # would show them, given the cached rows as the keys of their positions:
+    # sinks (prefix), the ring's window rows, and the chunk itself.  Positions
+    # the ring no longer holds get random junk, which must stay invisible.
+    B, Hq, Hkv, D = 3, 4, 2, 32
+    rng = np.random.default_rng(60 + W + Tc)
+    q = rng.standard_normal((B, Hq, Tc, D))
+    k, v = rng.standard_normal((2, B, Hkv, Tc, D)).astype(np.float32)
+    caches = {}
+    for name, rows in (("ring_k", W), ("ring_v", W), ("sink_k", S), ("sink_v", S)):
+        x = rng.standard_normal((B * Hkv * rows, D)).astype(np.float32) * 2
+        c, sc = oracle.quantize(x)
+        caches[name] = c.reshape(B, Hkv, rows, D)
+        caches[name + "s"] = sc.reshape(B, Hkv, rows, D // 32)
+    out, lse, rk, rv, rks, rvs = oracle.chunk_prefill(
+        q, k, v, caches["ring_k"], caches["ring_v"], caches["ring_ks"], caches["ring_vs"], caches["sink_k"],
+        caches["sink_v"], caches["sink_ks"], caches["sink_vs"], pos0, sink_len)
+    G = Hq // Hkv
+    for b in range(B):
+        p0 = pos0[b]
+        sl = min(S if sink_len is None else sink_len[b], p0, S)
+        L = p0 + Tc
+        Kf = rng.standard_normal((1, Hkv, L, D)) * 30          # junk where the cache holds nothing
+        Vf = rng.standard_normal((1, Hkv, L, D)) * 30
+        for h in range(Hkv):
+            Kf[0, h, :sl] = _dequant(caches["sink_k"][b, h, :sl], caches["sink_ks"][b, h, :sl])
+            Vf[0, h, :sl] = _dequant(caches["sink_v"][b, h, :sl], caches["sink_vs"][b, h, :sl])
+            for p in range(max(sl, p0 - W + 1), p0):
+                Kf[0, h, p] = _dequant(caches["ring_k"][b, h, p % W], caches["ring_ks"][b, h, p % W])
+                Vf[0, h, p] = _dequant(caches["ring_v"][b, h, p % W], caches["ring_vs"][b, h, p % W])
+            Kf[0, h, p0:] = k[b, h]
+            Vf[0, h, p0:] = v[b, h]
+        Qf = np.zeros((1, Hq, L, D))
+        Qf[0, :, p0:] = q[b]
+        prefix = np.zeros((1, L), np.uint8)
+        prefix[0, :sl] = 1
+        rows = [(h * L + t) for h in range(Hq) for t in range(p0, L)]
+        ref, ref_lse = oracle.prefill(Qf, Kf, Vf, np.ones((1, L), np.int32), prefix, W, rows=rows)
+        np.testing.assert_allclose(out[b].reshape(-1, D), ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[b].reshape(-1), ref_lse, rtol=1e-12, atol=1e-12)
+        # the ring: the chunk's last min(W, Tc) tokens, quantized into their slots; other slots untouched
+        written = {(p0 + i) % W: i for i in range(max(0, Tc - W), Tc)}
+        for h in range(Hkv):
+            kq, ks = oracle.quantize(k[b, h])
+            for slot in range(W):
+                if slot in written:
+                    np.testing.assert_array_equal(rk[b, h, slot], kq[written[slot]])
+                    np.testing.assert_array_equal(rks[b, h, slot], ks[written[slot]])
+                else:
+                    np.testing.assert_array_equal(rk[b, h, slot], caches["ring_k"][b, h, slot])
+    assert G == 2
+
+
+def test_chunk_prefill_from_an_empty_cache_is_causal_window_attention():
+    # pos0 = 0, no sinks: the chunk alone, causal with window W (SDPA with a band mask)
+    B, H, Tc, D, W = 2, 2, 24, 32, 5
+    rng = np.random.default_rng(70)
+    q = rng.standard_normal((B, H, Tc, D))
+    k, v = rng.standard_normal((2, B, H, Tc, D)).astype(np.float32)
+    z8 = np.zeros((B, H, W, D), np.int8)
+    z32 = np.zeros((B, H, W, 1), np.float32)
+    s8 = np.zeros((B, H, 0, D), np.int8)
+    s32 = np.zeros((B, H, 0, 1), np.float32)
+    out, *_ = oracle.chunk_prefill(q, k, v, z8, z8, z32, z32, s8, s8, s32, s32, [0, 0])
+    np.testing.assert_allclose(out, sdpa(q, k.astype(np.float64), v.astype(np.float64), mask=band(Tc, W)),
+                               rtol=1e-12, atol=1e-12)
