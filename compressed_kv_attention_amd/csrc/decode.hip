@@ -22,18 +22,6 @@
 namespace swa {
 namespace {
 
-// Symmetric absmax/127 quantization of one 32-channel group held by 32
-// consecutive lanes (one element per lane).  Returns the code; `s` receives
-// the group scale.
-__device__ __forceinline__ int quantize_lane(float x, float& s) {
-    float amax = fabsf(x);
-    amax = wave_max_xor(amax, 1, 16);
-    s = amax / 127.0f;
-    if (s == 0.0f) return 0;
-    float r = rintf(x / s);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
-}
 
 __global__ __launch_bounds__(256) void kv_quantize_kernel(long long total, const uint16_t* x, int8_t* xq,
                                                           float* xs) {

@@ -512,6 +512,117 @@ int swa_attn_decode_compressed(const swa_decode_params* p, int block, const floa
     return hip_status(swa::launch_decode(a, (hipStream_t)stream), "swa_attn_decode_compressed launch");
 }
 
+}  // extern "C"
+
+namespace {
+// Workspace layout of a chunked prefill: staged q, k, v, out, segment ids,
+// prefix flags, then the prefill workspace of the staged sequence.
+struct ChunkLayout {
+    size_t q, k, v, out, seg, prefix, pf, pf_bytes, total;
+    swa_prefill_params pp;
+};
+bool chunk_layout(const swa_chunk_params* p, ChunkLayout& L) {
+    if (p == nullptr || p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->D <= 0 || p->W < 1 || p->S < 0 || p->Tc <= 0)
+        return false;
+    const long long Tv = (long long)p->S + p->W - 1 + p->Tc;
+    if (Tv > swa::kMaxT) return false;
+    L.pp = swa_prefill_params{p->B, p->Hq, p->Hkv, (int)Tv, p->D, p->W, 0, 0, p->scale, SWA_BF16};
+    const size_t qb = (size_t)p->B * p->Hq * Tv * p->D * 2, kb = (size_t)p->B * p->Hkv * Tv * p->D * 2;
+    L.q = 0;
+    L.k = L.q + round256(qb);
+    L.v = L.k + round256(kb);
+    L.out = L.v + round256(kb);
+    L.seg = L.out + round256(qb);
+    L.prefix = L.seg + round256((size_t)p->B * Tv * 4);
+    L.pf = L.prefix + round256((size_t)p->B * Tv);
+    L.pf_bytes = swa_prefill_workspace_size(&L.pp);
+    L.total = L.pf + round256(L.pf_bytes);
+    return true;
+}
+}  // namespace
+
+extern "C" {
+
+size_t swa_chunk_prefill_workspace_size(const swa_chunk_params* p) {
+    ChunkLayout L;
+    return chunk_layout(p, L) ? L.total : 0;
+}
+
+int swa_attn_chunk_prefill(const swa_chunk_params* p, const void* q, const void* k, const void* v, int8_t* ring_k,
+                           int8_t* ring_v, float* ring_ks, float* ring_vs, const int8_t* sink_k, const int8_t* sink_v,
+                           const float* sink_ks, const float* sink_vs, const int32_t* pos0, const int32_t* sink_len,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    REQUIRE(p != nullptr, "params must not be NULL");
+    REQUIRE(p->B >= 0 && p->Tc >= 0, "B and Tc must be >= 0 (B=%d, Tc=%d)", p->B, p->Tc);
+    REQUIRE(p->Hq > 0 && p->Hkv > 0 && p->Hq % p->Hkv == 0, "Hq (%d) must be a positive multiple of Hkv (%d)", p->Hq,
+            p->Hkv);
+    REQUIRE(p->W >= 1, "W must be >= 1 (got %d)", p->W);
+    REQUIRE(p->S >= 0, "S must be >= 0 (got %d)", p->S);
+    REQUIRE(p->scale >= 0.f && std::isfinite(p->scale), "scale must be finite and >= 0");
+    if (p->D != 32 && p->D != 64) return fail(SWA_ERR_UNSUPPORTED, "head dim D=%d is not built (32 or 64)", p->D);
+    if ((long long)p->S + p->W - 1 + p->Tc > swa::kMaxT)
+        return fail(SWA_ERR_UNSUPPORTED, "S + W - 1 + Tc = %lld exceeds the supported %d",
+                    (long long)p->S + p->W - 1 + p->Tc, swa::kMaxT);
+    if ((long long)p->B * p->Hkv > 65535)
+        return fail(SWA_ERR_UNSUPPORTED, "B * Hkv = %lld exceeds 65535", (long long)p->B * p->Hkv);
+    if (p->B == 0 || p->Tc == 0) return ok();
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(ring_k);
+    REQUIRE_PTR(ring_v);
+    REQUIRE_PTR(ring_ks);
+    REQUIRE_PTR(ring_vs);
+    REQUIRE_PTR(pos0);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(sink_len);
+    if (p->S > 0) {
+        REQUIRE_PTR(sink_k);
+        REQUIRE_PTR(sink_v);
+        REQUIRE_PTR(sink_ks);
+        REQUIRE_PTR(sink_vs);
+    }
+    ChunkLayout L;
+    if (!chunk_layout(p, L)) return fail(SWA_ERR_INVALID, "chunk parameters out of range");
+    REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 255u) == 0,
+            "workspace must be a 256-byte aligned buffer of swa_chunk_prefill_workspace_size() bytes");
+    REQUIRE(workspace_bytes >= L.total, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, L.total);
+    swa::ChunkArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.ring_k = ring_k;
+    a.ring_v = ring_v;
+    a.ring_ks = ring_ks;
+    a.ring_vs = ring_vs;
+    a.sink_k = p->S > 0 ? sink_k : nullptr;
+    a.sink_v = p->S > 0 ? sink_v : nullptr;
+    a.sink_ks = p->S > 0 ? sink_ks : nullptr;
+    a.sink_vs = p->S > 0 ? sink_vs : nullptr;
+    a.pos0 = pos0;
+    a.sink_len = sink_len;
+    a.out = out;
+    a.B = p->B;
+    a.Hq = p->Hq;
+    a.Hkv = p->Hkv;
+    a.D = p->D;
+    a.W = p->W;
+    a.S = p->S;
+    a.Tc = p->Tc;
+    a.Tv = L.pp.T;
+    char* ws = (char*)workspace;
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e = swa::launch_chunk_stage(a, ws + L.k, ws + L.v, (int32_t*)(ws + L.seg), (uint8_t*)(ws + L.prefix),
+                                           ws + L.q, s);
+    if (e != hipSuccess) return hip_status(e, "swa_attn_chunk_prefill staging launch");
+    const int rc = swa_attn_prefill(&L.pp, ws + L.q, ws + L.k, ws + L.v, nullptr, nullptr, (const int32_t*)(ws + L.seg),
+                                    (const uint8_t*)(ws + L.prefix), nullptr, nullptr, ws + L.out, nullptr,
+                                    L.pf_bytes ? ws + L.pf : nullptr, L.pf_bytes, stream);
+    if (rc != SWA_OK) return rc;
+    e = swa::launch_chunk_finish(a, ws + L.out, s);
+    return hip_status(e, "swa_attn_chunk_prefill ring write launch");
+}
+
 long long swa_kv_budget_window(long long d_model, long long attn_dim, long long num_heads, long long num_kv_heads,
                                long long num_layers, long long sites, long long max_seq_len) {
     if (d_model <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_layers <= 0 || sites < 0 || max_seq_len <= 0 ||

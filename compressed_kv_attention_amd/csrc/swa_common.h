@@ -35,6 +35,22 @@ __device__ __forceinline__ float wave_max_xor(float v, int first, int last) {
     for (int o = first; o <= last; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;
 }
+
+// Symmetric absmax/127 quantization of one 32-channel group held by 32
+// consecutive lanes (one element per lane), the int8 cache layout that the
+// budget formula of [NW] "How the 256-Token Sliding Window Works with Tools
+// as KV Sinks in Needle" ("Effective KV Window") prices: scale = amax / 127
+// in fp32, code = round-half-even(x / scale) clamped to +-127, a zero group
+// gives scale 0 and codes 0.  Returns the code; `s` receives the group scale.
+__device__ __forceinline__ int quantize_lane(float x, float& s) {
+    float amax = fabsf(x);
+    amax = wave_max_xor(amax, 1, 16);
+    s = amax / 127.0f;
+    if (s == 0.0f) return 0;
+    float r = rintf(x / s);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
 __device__ __forceinline__ int wave_imin_xor(int v, int first, int last) {
     for (int o = first; o <= last; o <<= 1) v = min(v, __shfl_xor(v, o, 64));
     return v;

@@ -191,6 +191,32 @@ inline int decode_auto_splits(int B, int Hq, int Hkv, int W, int S) {
     return (int)(s < 1 ? 1 : s);
 }
 constexpr int kMaxDecodeSplits = 256;
+
+// Chunked prefill: the caller's tensors and the staged sequence length
+// Tv = S + W - 1 + Tc (sink rows, ring rows before the chunk, the chunk).
+struct ChunkArgs {
+    const void* q;  // [B][Hq][Tc][D] bf16
+    const void* k;  // [B][Hkv][Tc][D] bf16
+    const void* v;
+    int8_t* ring_k;
+    int8_t* ring_v;
+    float* ring_ks;
+    float* ring_vs;
+    const int8_t* sink_k;
+    const int8_t* sink_v;
+    const float* sink_ks;
+    const float* sink_vs;
+    const int32_t* pos0;
+    const int32_t* sink_len;
+    void* out;  // [B][Hq][Tc][D] bf16
+    int B, Hq, Hkv, D, W, S, Tc, Tv;
+};
+// Stage K/V (sink and ring rows dequantized, the chunk copied), the segment and
+// prefix arrays of the staged sequence, and the staged queries.
+hipError_t launch_chunk_stage(const ChunkArgs& a, void* k_stage, void* v_stage, int32_t* seg, uint8_t* prefix,
+                              void* q_stage, hipStream_t s);
+// Copy the chunk's rows of the staged output out, then write the ring.
+hipError_t launch_chunk_finish(const ChunkArgs& a, const void* out_stage, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // Largest split-K state swa_attn_decode_noalloc holds (its device array).
 constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;

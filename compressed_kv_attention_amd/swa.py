@@ -22,8 +22,14 @@ SWA_F32, SWA_BF16 = 0, 1
 EXPORTS = ("swa_last_error", "swa_version", "swa_prefill_workspace_size", "swa_attn_prefill", "swa_debug_visibility", "swa_rope_table",
            "swa_rope_table_host",
            "kv_pool_compress_rope", "swa_kv_quantize", "swa_decode_workspace_size", "swa_attn_decode",
-           "swa_attn_decode_noalloc", "swa_attn_decode_compressed",
+           "swa_attn_decode_noalloc", "swa_attn_decode_compressed", "swa_chunk_prefill_workspace_size",
+           "swa_attn_chunk_prefill",
            "swa_kv_budget_window", "swa_effective_kv_window")
+
+
+class ChunkParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("D", ctypes.c_int),
+                ("W", ctypes.c_int), ("S", ctypes.c_int), ("Tc", ctypes.c_int), ("scale", ctypes.c_float)]
 
 
 class PrefillParams(ctypes.Structure):
@@ -80,6 +86,10 @@ def lib():
     L.swa_attn_decode_noalloc.restype = I
     L.swa_attn_decode_compressed.argtypes = [ctypes.POINTER(DecodeParams), I, P, P, I] + [P] * 16 + [P, Z, P]
     L.swa_attn_decode_compressed.restype = I
+    L.swa_chunk_prefill_workspace_size.argtypes = [ctypes.POINTER(ChunkParams)]
+    L.swa_chunk_prefill_workspace_size.restype = Z
+    L.swa_attn_chunk_prefill.argtypes = [ctypes.POINTER(ChunkParams)] + [P] * 14 + [P, Z, P]
+    L.swa_attn_chunk_prefill.restype = I
     L.swa_kv_budget_window.argtypes = [LL] * 7
     L.swa_kv_budget_window.restype = LL
     L.swa_effective_kv_window.argtypes = [LL] * 8
@@ -296,6 +306,36 @@ def decode_workspace(q, ring_k, sink_k, num_splits=0):
     return torch.zeros(n, dtype=torch.uint8, device=q.device) if n else None
 
 
+def _cache_shapes(B, Hkv, W, D, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos, sink_len):
+    """Shapes of the ring and sink caches and the per-row position arrays."""
+    _shape(ring_k, "ring_k", (B, Hkv, W, D))
+    _shape(ring_v, "ring_v", (B, Hkv, W, D))
+    _shape(ring_ks, "ring_ks", (B, Hkv, W, D // 32))
+    _shape(ring_vs, "ring_vs", (B, Hkv, W, D // 32))
+    if (sink_k is None) != (sink_v is None) or (sink_k is None) != (sink_ks is None) or \
+            (sink_k is None) != (sink_vs is None):
+        raise ValueError("sink_k, sink_v, sink_ks and sink_vs must all be given or all be None")
+    S = sink_k.shape[2] if sink_k is not None else 0
+    _shape(sink_k, "sink_k", (B, Hkv, S, D))
+    _shape(sink_v, "sink_v", (B, Hkv, S, D))
+    _shape(sink_ks, "sink_ks", (B, Hkv, S, D // 32))
+    _shape(sink_vs, "sink_vs", (B, Hkv, S, D // 32))
+    _shape(pos, "pos", (B,))
+    _shape(sink_len, "sink_len", (B,))
+
+
+def _cache_devices(ref, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos, sink_len):
+    for name, t, dt in (("ring_k", ring_k, torch.int8), ("ring_v", ring_v, torch.int8),
+                        ("ring_ks", ring_ks, torch.float32), ("ring_vs", ring_vs, torch.float32),
+                        ("sink_k", sink_k, torch.int8), ("sink_v", sink_v, torch.int8),
+                        ("sink_ks", sink_ks, torch.float32), ("sink_vs", sink_vs, torch.float32),
+                        ("pos", pos, torch.int32), ("sink_len", sink_len, torch.int32)):
+        _dev(t, name, dt)
+    _same_device(ref, ("ring_k", ring_k), ("ring_v", ring_v), ("ring_ks", ring_ks), ("ring_vs", ring_vs),
+                 ("sink_k", sink_k), ("sink_v", sink_v), ("sink_ks", sink_ks), ("sink_vs", sink_vs), ("pos", pos),
+                 ("sink_len", sink_len))
+
+
 def _decode_checks(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos, sink_len, k_new,
                    v_new, out):
     if q.dim() != 3 or ring_k.dim() != 4:
@@ -420,6 +460,52 @@ def decode_compressed(q, k_new, k_new_pre, v_new, ring_k, ring_v, ring_ks, ring_
                                             _ptr(ring_v), _ptr(ring_ks), _ptr(ring_vs), _ptr(pool_k), _ptr(pool_v),
                                             _ptr(pool_ks), _ptr(pool_vs), _ptr(front_k), _ptr(front_v), _ptr(pos),
                                             _ptr(out), _ptr(workspace) if ws_len else None, ws_len, _stream(q)))
+    return out
+
+
+def chunk_params(q, ring_k, sink_k, scale=0.0):
+    B, Hq, Tc, D = q.shape
+    Hkv, W = ring_k.shape[1], ring_k.shape[2]
+    S = sink_k.shape[2] if sink_k is not None else 0
+    return ChunkParams(B, Hq, Hkv, D, W, S, Tc, float(scale))
+
+
+def chunk_prefill_workspace(q, ring_k, sink_k):
+    """The workspace swa_attn_chunk_prefill needs for these shapes (None when none is needed)."""
+    n = lib().swa_chunk_prefill_workspace_size(ctypes.byref(chunk_params(q, ring_k, sink_k)))
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def chunk_prefill(q, k, v, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos0, sink_len=None,
+                  scale=0.0, out=None, workspace=None):
+    """Chunked prefill into existing caches (swa_attn_chunk_prefill).  q [B,Hq,Tc,D], k/v [B,Hkv,Tc,D] bf16
+    (q and k rotated); ring/sink caches as in decode(); pos0 [B] int32 (first position of the chunk).  The
+    ring takes the chunk's last min(W, Tc) tokens.  Returns out [B,Hq,Tc,D] bf16."""
+    if q.dim() != 4 or ring_k.dim() != 4:
+        raise ValueError("q must be [B, Hq, Tc, D] and ring_k [B, Hkv, W, D]")
+    B, Hq, Tc, D = q.shape
+    Hkv, W = ring_k.shape[1], ring_k.shape[2]
+    if D % 32:
+        raise ValueError(f"head dim {D} must be a multiple of 32")
+    _shape(k, "k", (B, Hkv, Tc, D))
+    _shape(v, "v", (B, Hkv, Tc, D))
+    _shape(out, "out", (B, Hq, Tc, D))
+    _cache_shapes(B, Hkv, W, D, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos0, sink_len)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _dev(t, name, torch.bfloat16)
+    _same_device(q, ("k", k), ("v", v), ("out", out))
+    _cache_devices(q, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sink_ks, sink_vs, pos0, sink_len)
+    p = chunk_params(q, ring_k, sink_k, scale)
+    ws_bytes = lib().swa_chunk_prefill_workspace_size(ctypes.byref(p))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = workspace.numel() * workspace.element_size() if (ws_bytes and workspace is not None) else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().swa_attn_chunk_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(ring_k), _ptr(ring_v),
+                                        _ptr(ring_ks), _ptr(ring_vs), _ptr(sink_k), _ptr(sink_v), _ptr(sink_ks),
+                                        _ptr(sink_vs), _ptr(pos0), _ptr(sink_len), _ptr(out),
+                                        _ptr(workspace) if ws_len else None, ws_len, _stream(q)))
     return out
 
 

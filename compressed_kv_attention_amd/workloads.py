@@ -195,3 +195,21 @@ def compressed_decode_sequence(seed=7, B=3, Hq=4, Hkv=2, D=64, T=150):
         out[name + "_bits"] = bits
     out.update(dict(B=B, Hq=Hq, Hkv=Hkv, D=D, T=T, seed=seed))
     return out
+
+
+def chunk_case(seed=8, B=8, Hq=16, Hkv=4, D=64, W=256, S=256, Tc=4096, pos_lo=256, pos_hi=32767, sink_len=None):
+    """Inputs of one chunked-prefill call: q [B,Hq,Tc,D], k/v [B,Hkv,Tc,D] (standing for rotated q and k), the
+    pre-quantization ring and sink caches [B,Hkv,W|S,D] (bf16 values), pos0 [B] and sink_len [B]."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape in (("q", (B, Hq, Tc, D)), ("k", (B, Hkv, Tc, D)), ("v", (B, Hkv, Tc, D)),
+                        ("ring_k", (B, Hkv, W, D)), ("ring_v", (B, Hkv, W, D)),
+                        ("sink_k", (B, Hkv, S, D)), ("sink_v", (B, Hkv, S, D))):
+        bits, vals = bf16_round(_normals(rng, shape))
+        out[name] = vals
+        out[name + "_bits"] = bits
+    out["pos0"] = rng.integers(pos_lo, pos_hi + 1, size=B).astype(np.int32)
+    out["sink_len"] = (np.full(B, S, dtype=np.int32) if sink_len is None
+                       else np.ascontiguousarray(sink_len, dtype=np.int32))
+    out.update(dict(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, Tc=Tc, seed=seed))
+    return out

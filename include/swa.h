@@ -244,6 +244,43 @@ int swa_attn_decode_compressed(const swa_decode_params* p,   /* S = P, the poole
                                void* out,                    /* [B,Hq,D] bf16                   */
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Chunked prefill into existing caches (the long-prompt path of [DS]       */
+/* "工作原理与配置方式", which prefills in chunks of 4096 tokens; mask of [NS] */
+/* "256-token 滑动窗口：源码走读").  A chunk of Tc tokens at positions         */
+/* pos0[b] .. pos0[b] + Tc - 1 attends, for token t, over the sink rows      */
+/* [0, sl) with sl = min(sink_len[b], pos0[b], S), the ring positions        */
+/* [max(sl, t - W + 1), pos0[b] - 1] as the ring holds them before the call, */
+/* and the chunk's own keys [max(pos0[b], t - W + 1), t] (unquantized); one  */
+/* softmax.  Then the chunk's last min(W, Tc) tokens are quantized (as by    */
+/* swa_kv_quantize) into ring slots position % W.  Precondition: the ring    */
+/* holds positions pos0[b] - W .. pos0[b] - 1 (those >= sl), as after a      */
+/* decode or a chunk that ended at pos0[b] - 1.  Negative pos0 counts as 0.  */
+/* Cached rows are dequantized and rounded to bf16 for the MFMA attention.   */
+typedef struct {
+    int B, Hq, Hkv, D; /* D in {32, 64}; Hq % Hkv == 0; B * Hkv <= 65535      */
+    int W;             /* ring capacity = window length, >= 1                   */
+    int S;             /* sink cache capacity, >= 0                             */
+    int Tc;            /* chunk length, >= 0; S + W - 1 + Tc <= 131072          */
+    float scale;       /* 0 selects 1/sqrt(D)                                   */
+} swa_chunk_params;
+
+/* Bytes of workspace swa_attn_chunk_prefill needs (staged queries, keys,   */
+/* values and outputs of S + W - 1 + Tc rows, their segment and prefix      */
+/* arrays, and the prefill workspace of that sequence).                     */
+size_t swa_chunk_prefill_workspace_size(const swa_chunk_params* p);
+
+int swa_attn_chunk_prefill(const swa_chunk_params* p,
+                           const void* q,                       /* [B,Hq,Tc,D] bf16, rotated     */
+                           const void* k, const void* v,        /* [B,Hkv,Tc,D] bf16, k rotated  */
+                           int8_t* ring_k, int8_t* ring_v,      /* [B,Hkv,W,D], updated          */
+                           float* ring_ks, float* ring_vs,      /* [B,Hkv,W,D/32], updated       */
+                           const int8_t* sink_k, const int8_t* sink_v, /* [B,Hkv,S,D] (NULL if S==0) */
+                           const float* sink_ks, const float* sink_vs, /* [B,Hkv,S,D/32]         */
+                           const int32_t* pos0,                 /* [B] first position of the chunk */
+                           const int32_t* sink_len,             /* [B] or NULL (= S)             */
+                           void* out,                           /* [B,Hq,Tc,D] bf16              */
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* swa_attn_decode for callers that cannot allocate memory (code under HIP   */
 /* graph capture, tight serving loops, harnesses that forbid allocation):    */
 /* the same computation, kernels and results, with the split-K state kept in */

@@ -410,3 +410,44 @@ def test_compressed_decode_wrapper_rejects_bad_shapes():
             swa.decode_compressed(**dict(kw, **over))
     with pytest.raises(ValueError, match="device tensor"):
         swa.decode_compressed(**kw)
+
+
+def test_chunk_prefill_validation_and_workspace():
+    L = swa.lib()
+    size = lambda **kw: L.swa_chunk_prefill_workspace_size(ctypes.byref(swa.ChunkParams(**dict(
+        dict(B=2, Hq=4, Hkv=2, D=64, W=8, S=5, Tc=13, scale=0.0), **kw))))
+    Tv = 5 + 8 - 1 + 13
+    r = lambda x: (x + 255) // 256 * 256
+    pf = L.swa_prefill_workspace_size(ctypes.byref(swa.PrefillParams(2, 4, 2, Tv, 64, 8, 0, 0, 0.0, swa.SWA_BF16)))
+    assert size() == 2 * r(2 * 4 * Tv * 64 * 2) + 2 * r(2 * 2 * Tv * 64 * 2) + r(2 * Tv * 4) + r(2 * Tv) + r(pf)
+    assert size(Tc=0) == 0 and size(W=0) == 0
+    args = [FAKE] * 14        # q, k, v, ring x4, sink x4, pos0, sink_len, out
+    p = swa.ChunkParams(2, 4, 2, 64, 8, 5, 13, 0.0)
+    assert L.swa_attn_chunk_prefill(ctypes.byref(p), *args, None, 0, None) == swa.SWA_ERR_INVALID
+    assert "workspace" in L.swa_last_error().decode()
+    for i, name in ((0, "q"), (3, "ring_k"), (11, "pos0"), (7, "sink_k")):
+        a2 = list(args)
+        a2[i] = None
+        assert L.swa_attn_chunk_prefill(ctypes.byref(p), *a2, FAKE, size(), None) == swa.SWA_ERR_INVALID
+        assert name in L.swa_last_error().decode()
+    bad = swa.ChunkParams(2, 4, 2, 64, 0, 5, 13, 0.0)
+    assert L.swa_attn_chunk_prefill(ctypes.byref(bad), *args, FAKE, 1 << 30, None) == swa.SWA_ERR_INVALID
+    big = swa.ChunkParams(2, 4, 2, 64, 8, 5, 131072, 0.0)
+    assert L.swa_attn_chunk_prefill(ctypes.byref(big), *args, FAKE, 1 << 30, None) == swa.SWA_ERR_UNSUPPORTED
+    empty = swa.ChunkParams(2, 4, 2, 64, 8, 5, 0, 0.0)
+    assert L.swa_attn_chunk_prefill(ctypes.byref(empty), *([None] * 14), None, 0, None) == swa.SWA_OK
+
+
+def test_chunk_prefill_wrapper_rejects_bad_shapes():
+    import torch
+    a = _decode_args()
+    kw = dict(q=_t(3, 8, 10, 64), k=_t(3, 2, 10, 64), v=_t(3, 2, 10, 64), ring_k=a["ring_k"], ring_v=a["ring_v"],
+              ring_ks=a["ring_ks"], ring_vs=a["ring_vs"], sink_k=a["sink_k"], sink_v=a["sink_v"],
+              sink_ks=a["sink_ks"], sink_vs=a["sink_vs"], pos0=a["pos"], sink_len=a["sink_len"])
+    for over, what in ((dict(k=_t(3, 2, 9, 64)), "k must"), (dict(v=_t(3, 1, 10, 64)), "v must"),
+                       (dict(ring_vs=_t(3, 2, 16, 1, dtype=torch.float32)), "ring_vs"),
+                       (dict(pos0=_t(2, dtype=torch.int32)), "pos"), (dict(out=_t(3, 8, 10, 32)), "out")):
+        with pytest.raises(ValueError, match=what):
+            swa.chunk_prefill(**dict(kw, **over))
+    with pytest.raises(ValueError, match="device tensor"):
+        swa.chunk_prefill(**kw)
