@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--reps", type=int, default=20, help="iterations per timed graph when timing one kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16,decode_b1,decode_b8,decode_b32,decode_c4")
+    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16,decode_b1,decode_b8,decode_b32,decode_c4,chunk")
     ap.add_argument("--decode-splits", type=int, default=0,
                     help="num_splits of the batch-256 decode part (0: the library's choice)")
     ap.add_argument("--eager", action="store_true",
@@ -293,6 +293,47 @@ def main():
         p.launches = layers
         return p
 
+    def make_chunk(name, B=8, Tc=4096):
+        """Chunked prefill into the decode caches: B8, 16q/4kv D64, ring 256 + 256 sinks, a 4096-token chunk
+        at positions 256..32767.  FLOPs are counted on visible (query, key) pairs: sinks + the ring rows in
+        the window + the chunk's own causal window."""
+        Hq, Hkv, D, W, S = 16, 4, 64, 256, 256
+        g = torch.Generator(device=dev)
+        g.manual_seed(8)
+        rng = np.random.default_rng(8)
+        pos0_np = rng.integers(256, 32768 - Tc, size=B).astype(np.int64)
+        pos0 = torch.from_numpy(pos0_np.astype(np.int32)).to(dev)
+        sink_len = torch.full((B,), S, dtype=torch.int32, device=dev)
+        c = {}
+        for nm, rows in (("ring_k", W), ("ring_v", W), ("sink_k", S), ("sink_v", S)):
+            x = torch.randn((B, Hkv, rows, D), generator=g, device=dev).to(torch.bfloat16)
+            c[nm], c[nm + "s"] = swa.kv_quantize(x)
+        per_copy = (B * Hq * Tc * D * 2) * 2 + (B * Hkv * Tc * D * 2) * 2
+        n = max(2, min(8, ROTATE_BYTES // per_copy + 1))
+        bufs = []
+        for _ in range(n):
+            q = torch.randn((B, Hq, Tc, D), generator=g, device=dev).to(torch.bfloat16)
+            k = torch.randn((B, Hkv, Tc, D), generator=g, device=dev).to(torch.bfloat16)
+            v = torch.randn((B, Hkv, Tc, D), generator=g, device=dev).to(torch.bfloat16)
+            bufs.append((q, k, v, torch.empty_like(q)))
+        ws = swa.chunk_prefill_workspace(bufs[0][0], c["ring_k"], c["sink_k"])
+        i = np.arange(Tc)
+        vis = 0
+        for p0 in pos0_np:
+            t = p0 + i
+            ring = np.maximum(0, p0 - np.maximum(S, t - W + 1))
+            vis += int((S + ring + np.minimum(i + 1, W)).sum())
+        flops = 4.0 * D * Hq * vis
+        bytes_ = per_copy + 2 * (B * Hkv * (W + S) * (D + (D // 32) * 4))
+
+        def launch(it):
+            q, k, v, o = bufs[it % n]
+            swa.chunk_prefill(q, k, v, c["ring_k"], c["ring_v"], c["ring_ks"], c["ring_vs"], c["sink_k"],
+                              c["sink_v"], c["sink_ks"], c["sink_vs"], pos0, sink_len, out=o, workspace=ws)
+        p = Part(name, launch, n, flops, bytes_, kernel="prefill_bf16_kernel")
+        p.extra = dict(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, Tc=Tc, visible_pairs_per_head=vis)
+        return p
+
     t_setup = time.time()
     if "needle" in parts_wanted:
         parts["needle"] = make_prefill("needle", workloads.needle())
@@ -303,6 +344,8 @@ def main():
     for b in (1, 8, 32):
         if f"decode_b{b}" in parts_wanted:
             parts[f"decode_b{b}"] = make_decode(f"decode_b{b}", B=b)
+    if "chunk" in parts_wanted:
+        parts["chunk"] = make_chunk("chunk")
     if "decode_c4" in parts_wanted:
         parts["decode_c4"] = make_compressed_decode("decode_c4", 4)
     if "packed" in parts_wanted:
@@ -430,6 +473,9 @@ def main():
                             if n.startswith("decode") and n != "decode_c4"},
         "compressed_decode": {k: (round(v, 5) if isinstance(v, float) else v)
                               for k, v in results.get("decode_c4", {}).items()},
+        "chunked_prefill": {"value": round(results.get("chunk", {}).get("tflops", 0.0), 3), "unit": "TFLOP/s",
+                            "frac_mfma_peak": round(results.get("chunk", {}).get("frac_mfma_peak", 0.0), 5),
+                            "us_per_call": round(results.get("chunk", {}).get("ms", 0.0) * 1e3, 2)},
         "packed": {"value": round(results.get("packed", {}).get("tflops", 0.0), 3), "unit": "TFLOP/s",
                    "frac_mfma_peak": round(results.get("packed", {}).get("frac_mfma_peak", 0.0), 5),
                    "us_per_call": round(results.get("packed", {}).get("ms", 0.0) * 1e3, 2),
