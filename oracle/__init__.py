@@ -62,6 +62,7 @@ def _load():
     lib.oracle_effective_kv_window.restype = LL
     lib.oracle_quantize.argtypes = [LL, I, P, P, P]
     lib.oracle_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, D, P, P]
+    lib.oracle_prefill_backward.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I, D, D, P, P, P]
     lib.oracle_chunk_prefill.argtypes = [I, I, I, I, I, I, I] + [P] * 13 + [D, P, P]
     lib.oracle_compressed_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, D, I, D, I,
                                              P, P]
@@ -316,3 +317,22 @@ def chunk_prefill(q, k, v, ring_k, ring_v, ring_ks, ring_vs, sink_k, sink_v, sin
                              _ptr(rvs), _ptr(sk), _ptr(sv), _ptr(sks), _ptr(svs), _ptr(p0), _ptr(sl), float(scale),
                              _ptr(out), _ptr(lse))
     return out, lse, rk, rv, rks, rvs
+
+
+def prefill_backward(q, k, v, dout, seg_ids=None, prefix=None, window=0, scale=None, theta=0.0):
+    """O10: gradients (dq, dk, dv) of the O1-O3 prefill for the output gradient dout [B,Hq,T,D].  With theta > 0
+    q and k are the values before rotation and so are their gradients."""
+    lib = _load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Hq, T, Dm = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dm)
+    seg = _opt(seg_ids, np.int32)
+    pre = _opt(prefix, np.uint8)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    lib.oracle_prefill_backward(B, Hq, Hkv, T, Dm, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(seg), _ptr(pre),
+                                int(window), float(scale), float(theta), _ptr(dq), _ptr(dk), _ptr(dv))
+    return dq, dk, dv

@@ -38,6 +38,7 @@
 //   R-A20 chunked prefill: the chunk attends over the sinks, the ring as it
 //        was before the chunk, and its own unquantized keys; then the ring
 //        takes its last W tokens (see O9).
+//   R-A21 backward: the plain derivative of the forward definition (O10).
 
 #include <cmath>
 #include <cstdint>
@@ -615,6 +616,101 @@ void oracle_chunk_prefill(int B, int Hq, int Hkv, int D, int W, int S, int Tc, c
                 oracle_quantize(1, D, v + (nk * Tc + i) * D, ring_v + slot * D, ring_vs + slot * groups);
             }
         }
+}
+
+// O10: backward of the windowed+sink prefill (O1 + O2 + O3).  [NS §"KV sink
+// 如何「钉住」工具"] and [NW §"KV Sinks for Tools"]: the packing mask is the
+// training-side mask, so its gradients are part of the method; the pages give
+// no backward, and this is the plain derivative of the forward definition
+// (reading A21).  Per visible column j of row t (exact two-pass softmax):
+//   p_j = softmax_j(scale <q_t, k_j>),  dP_j = <dO_t, v_j>,
+//   Delta_t = sum_j p_j dP_j,  dS_j = p_j (dP_j - Delta_t),
+//   dq_t = scale sum_j dS_j k_j,  dk_j += scale dS_j q_t,  dv_j += p_j dO_t.
+// With theta > 0 q and k are rotated at their row index first (O2), and the
+// gradients are taken back through the rotation (rotating by the negative
+// angle, the transpose of the rotation).  GQA: a kv head's dk/dv sum over its
+// query heads.  q [B,Hq,T,D], k/v [B,Hkv,T,D], dout [B,Hq,T,D]; seg/prefix as
+// in O1; dq [B,Hq,T,D], dk/dv [B,Hkv,T,D] fp64 (written, not accumulated into).
+void oracle_prefill_backward(int B, int Hq, int Hkv, int T, int D, const double* q, const double* k,
+                             const double* v, const double* dout, const int32_t* seg,
+                             const uint8_t* prefix, int window, double scale, double theta,
+                             double* dq, double* dk, double* dv) {
+    const int G = Hq / Hkv;
+    const long long NKV = static_cast<long long>(B) * Hkv;
+    std::vector<double> kr;
+    const double* kk = k;
+    if (theta > 0.0) {
+        kr = rotate_rows(k, NKV, T, D, theta);
+        kk = kr.data();
+    }
+    const size_t nkv = static_cast<size_t>(NKV) * T * D;
+    std::vector<double> dk_rot(nkv, 0.0), dv_acc(nkv, 0.0);
+    // rows of one (batch row, kv head) group are handled by one thread so the
+    // dk/dv sums need no synchronisation
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long nk = 0; nk < NKV; ++nk) {
+        const int b = static_cast<int>(nk / Hkv);
+        const int hk = static_cast<int>(nk % Hkv);
+        const int32_t* seg_row = seg ? seg + static_cast<size_t>(b) * T : nullptr;
+        const uint8_t* pre_row = prefix ? prefix + static_cast<size_t>(b) * T : nullptr;
+        std::vector<double> qrow(D), dqr(D), s, dp;
+        std::vector<int> cols;
+        for (int h = hk * G; h < (hk + 1) * G; ++h) {
+            for (int t = 0; t < T; ++t) {
+                const size_t qo = ((static_cast<size_t>(b) * Hq + h) * T + t) * D;
+                if (theta > 0.0) rope_rotate(q + qo, qrow.data(), D, theta, t);
+                else for (int d = 0; d < D; ++d) qrow[d] = q[qo + d];
+                cols.clear();
+                for (int j = 0; j < T; ++j)
+                    if (visible_prefill(seg_row, pre_row, t, j, window)) cols.push_back(j);
+                for (int d = 0; d < D; ++d) dqr[d] = 0.0;
+                if (!cols.empty()) {
+                    const size_t n = cols.size();
+                    s.assign(n, 0.0);
+                    dp.assign(n, 0.0);
+                    double m = -std::numeric_limits<double>::infinity();
+                    for (size_t c = 0; c < n; ++c) {
+                        const double* kj = kk + (static_cast<size_t>(nk) * T + cols[c]) * D;
+                        double dot = 0.0;
+                        for (int d = 0; d < D; ++d) dot += qrow[d] * kj[d];
+                        s[c] = scale * dot;
+                        if (s[c] > m) m = s[c];
+                    }
+                    double l = 0.0;
+                    for (size_t c = 0; c < n; ++c) {
+                        s[c] = std::exp(s[c] - m);
+                        l += s[c];
+                    }
+                    double delta = 0.0;
+                    for (size_t c = 0; c < n; ++c) {
+                        s[c] /= l;  // p_j
+                        const double* vj = v + (static_cast<size_t>(nk) * T + cols[c]) * D;
+                        double x = 0.0;
+                        for (int d = 0; d < D; ++d) x += dout[qo + d] * vj[d];
+                        dp[c] = x;
+                        delta += s[c] * x;
+                    }
+                    for (size_t c = 0; c < n; ++c) {
+                        const double ds = s[c] * (dp[c] - delta);
+                        const size_t ko = (static_cast<size_t>(nk) * T + cols[c]) * D;
+                        for (int d = 0; d < D; ++d) {
+                            dqr[d] += scale * ds * kk[ko + d];
+                            dk_rot[ko + d] += scale * ds * qrow[d];
+                            dv_acc[ko + d] += s[c] * dout[qo + d];
+                        }
+                    }
+                }
+                if (theta > 0.0) rope_rotate(dqr.data(), dq + qo, D, theta, -static_cast<long long>(t));
+                else for (int d = 0; d < D; ++d) dq[qo + d] = dqr[d];
+            }
+        }
+        for (int j = 0; j < T; ++j) {
+            const size_t ko = (static_cast<size_t>(nk) * T + j) * D;
+            if (theta > 0.0) rope_rotate(dk_rot.data() + ko, dk + ko, D, theta, -static_cast<long long>(j));
+            else for (int d = 0; d < D; ++d) dk[ko + d] = dk_rot[ko + d];
+            for (int d = 0; d < D; ++d) dv[ko + d] = dv_acc[ko + d];
+        }
+    }
 }
 
 }  // extern "C"

@@ -723,3 +723,102 @@ def test_chunk_prefill_from_an_empty_cache_is_causal_window_attention():
     out, *_ = oracle.chunk_prefill(q, k, v, z8, z8, z32, z32, s8, s8, s32, s32, [0, 0])
     np.testing.assert_allclose(out, sdpa(q, k.astype(np.float64), v.astype(np.float64), mask=band(Tc, W)),
                                rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# O10 backward of the prefill  (the training-side mask of [NS §"KV sink 如何
+# 「钉住」工具"] and [NW §"KV Sinks for Tools"]; reading A21)
+# --------------------------------------------------------------------------
+
+def _autograd_reference(q, k, v, dout, mask, scale):
+    """dq, dk, dv of torch SDPA (fp64, CPU) under an explicit boolean mask [B, T, T]; GQA by repeated heads."""
+    G = q.shape[1] // k.shape[1]
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    m = torch.from_numpy(np.asarray(mask, dtype=bool))[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt.repeat_interleave(G, 1), vt.repeat_interleave(G, 1),
+                                                         attn_mask=m, scale=scale)
+    o.backward(torch.from_numpy(np.ascontiguousarray(dout, dtype=np.float64)))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("case", ["causal", "window_sinks", "segments", "gqa"])
+def test_prefill_backward_matches_autograd(case):
+    rng = np.random.default_rng({"causal": 80, "window_sinks": 81, "segments": 82, "gqa": 83}[case])
+    B, T, D = 2, 40, 16
+    Hq, Hkv = (4, 2) if case == "gqa" else (2, 2)
+    seg = np.ones((B, T), np.int32)
+    prefix = None
+    W = 0
+    if case == "window_sinks":
+        W = 6
+        prefix = np.zeros((B, T), np.uint8)
+        prefix[:, :5] = 1
+        seg[:, :5] = 1
+    if case in ("segments", "gqa"):
+        W = 9
+        seg[0, 13:] = 2
+        seg[0, 30:] = 3
+        seg[1, 20:] = 2
+        prefix = np.zeros((B, T), np.uint8)
+        prefix[0, 13:16] = 1
+        prefix[1, 0:4] = 1
+    q = rng.standard_normal((B, Hq, T, D))
+    k, v = rng.standard_normal((2, B, Hkv, T, D))
+    dout = rng.standard_normal((B, Hq, T, D))
+    scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = oracle.prefill_backward(q, k, v, dout, seg, prefix, W)
+    mask = oracle.mask(seg, prefix, W).astype(bool)
+    rq, rk, rv = _autograd_reference(q, k, v, dout, mask, scale)
+    np.testing.assert_allclose(dq, rq, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, rk, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, rv, rtol=1e-10, atol=1e-12)
+
+
+def test_prefill_backward_rope_is_the_rotated_problem_rotated_back():
+    # with RoPE the gradients w.r.t. the unrotated q, k are those of the rotated
+    # problem rotated back (the rotation at -pos is the transpose of the one at pos)
+    rng = np.random.default_rng(84)
+    B, H, T, D = 1, 2, 30, 16
+    q, k, v, dout = rng.standard_normal((4, B, H, T, D))
+    pos = np.arange(T)
+    qr = np.stack([oracle.rope(q[0, h], pos, 1e4) for h in range(H)])[None]
+    kr = np.stack([oracle.rope(k[0, h], pos, 1e4) for h in range(H)])[None]
+    dq, dk, dv = oracle.prefill_backward(q, k, v, dout, None, None, 7, theta=1e4)
+    dq0, dk0, dv0 = oracle.prefill_backward(qr, kr, v, dout, None, None, 7)
+    np.testing.assert_allclose(dq[0], np.stack([oracle.rope(dq0[0, h], -pos, 1e4) for h in range(H)]),
+                               rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk[0], np.stack([oracle.rope(dk0[0, h], -pos, 1e4) for h in range(H)]),
+                               rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, dv0, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_backward_finite_differences_and_padding():
+    # central differences of L = <dout, out> on a tiny problem with sinks, a
+    # window and a padding row (segment 0: no output, no gradient, no effect)
+    rng = np.random.default_rng(85)
+    B, Hq, Hkv, T, D, W = 1, 2, 1, 9, 4, 3
+    seg = np.array([[1, 1, 1, 1, 2, 2, 2, 2, 0]], np.int32)
+    prefix = np.array([[1, 0, 0, 0, 1, 0, 0, 0, 0]], np.uint8)
+    q = rng.standard_normal((B, Hq, T, D))
+    k, v = rng.standard_normal((2, B, Hkv, T, D))
+    dout = rng.standard_normal((B, Hq, T, D))
+    dq, dk, dv = oracle.prefill_backward(q, k, v, dout, seg, prefix, W, theta=1e4)
+
+    def loss(qq, kk, vv):
+        out, _ = oracle.prefill(qq, kk, vv, seg, prefix, W, theta=1e4)
+        return float((out * dout).sum())
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": (q, k, v), "k": (q, k, v), "v": (q, k, v)}[name]
+            a_p = [xp if n == name else a for n, a in zip("qkv", args)]
+            a_m = [xm if n == name else a for n, a in zip("qkv", args)]
+            num[idx] = (loss(*a_p) - loss(*a_m)) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-7, err_msg=name)
+    assert np.all(dq[:, :, 8] == 0) and np.all(dk[:, :, 8] == 0) and np.all(dv[:, :, 8] == 0)
