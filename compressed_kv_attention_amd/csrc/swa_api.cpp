@@ -515,6 +515,89 @@ int swa_attn_decode_compressed(const swa_decode_params* p, int block, const floa
 }  // extern "C"
 
 namespace {
+// Workspace of a backward call: fp32 q, dO, k, v and Delta, 256-byte aligned parts.
+struct BwdLayout {
+    size_t q32, do32, k32, v32, delta, total;
+};
+BwdLayout bwd_layout(const swa_prefill_params* p) {
+    BwdLayout L{0, 0, 0, 0, 0, 0};
+    const size_t nq = (size_t)p->B * p->Hq * p->T * p->D * 4, nk = (size_t)p->B * p->Hkv * p->T * p->D * 4;
+    L.do32 = round256(nq);
+    L.k32 = L.do32 + round256(nq);
+    L.v32 = L.k32 + round256(nk);
+    L.delta = L.v32 + round256(nk);
+    L.total = L.delta + round256((size_t)p->B * p->Hq * p->T * 4);
+    return L;
+}
+}  // namespace
+
+extern "C" {
+
+size_t swa_prefill_backward_workspace_size(const swa_prefill_params* p) {
+    if (p == nullptr || p->B <= 0 || p->T <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->D <= 0) return 0;
+    return bwd_layout(p).total;
+}
+
+int swa_attn_prefill_backward(const swa_prefill_params* p, const void* q, const void* k, const void* v,
+                              const void* out, const float* lse, const void* dout, const int32_t* seg_ids,
+                              const uint8_t* prefix, const float* rope_cos, const float* rope_sin, float* dq,
+                              float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+    swa::PrefillArgs pa;
+    int rc = check_prefill(p, seg_ids, prefix, pa);
+    if (rc != SWA_OK) return rc;
+    if (p->compress_block != 0)
+        return fail(SWA_ERR_UNSUPPORTED, "the backward is built for plain mode (compress_block 0)");
+    if (p->T > 65535 * 32) return fail(SWA_ERR_UNSUPPORTED, "T=%d too long for the backward grid", p->T);
+    if (p->B > 65535 || p->Hq > 65535) return fail(SWA_ERR_UNSUPPORTED, "B and Hq must be <= 65535");
+    if (p->B == 0 || p->T == 0) return ok();
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(lse);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(dq);
+    REQUIRE_PTR(dk);
+    REQUIRE_PTR(dv);
+    if (p->rope_len > 0) {
+        REQUIRE_PTR(rope_cos);
+        REQUIRE_PTR(rope_sin);
+    }
+    const BwdLayout L = bwd_layout(p);
+    REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 255u) == 0,
+            "workspace must be a 256-byte aligned buffer of swa_prefill_backward_workspace_size() bytes");
+    REQUIRE(workspace_bytes >= L.total, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, L.total);
+    swa::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.dout = dout;
+    a.lse = lse;
+    a.seg = seg_ids;
+    a.prefix = prefix;
+    a.rope_cos = p->rope_len > 0 ? rope_cos : nullptr;
+    a.rope_sin = p->rope_len > 0 ? rope_sin : nullptr;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.B = p->B;
+    a.Hq = p->Hq;
+    a.Hkv = p->Hkv;
+    a.T = p->T;
+    a.D = p->D;
+    a.window = p->window;
+    a.dtype = p->dtype == SWA_BF16 ? 1 : 0;
+    a.scale = pa.scale;
+    char* ws = (char*)workspace;
+    const swa::BwdWorkspace w{(float*)(ws + L.q32), (float*)(ws + L.k32), (float*)(ws + L.v32),
+                              (float*)(ws + L.do32), (float*)(ws + L.delta)};
+    return hip_status(swa::launch_prefill_backward(a, w, (hipStream_t)stream), "swa_attn_prefill_backward launch");
+}
+
+}  // extern "C"
+
+namespace {
 // Workspace layout of a chunked prefill: staged q, k, v, out, segment ids,
 // prefix flags, then the prefill workspace of the staged sequence.
 struct ChunkLayout {

@@ -192,6 +192,35 @@ inline int decode_auto_splits(int B, int Hq, int Hkv, int W, int S) {
 }
 constexpr int kMaxDecodeSplits = 256;
 
+// Backward of the plain-mode prefill: the caller's tensors and the fp32
+// staging (q and k rotated when a table is given, dO, and Delta = rowsum(dO o)).
+struct BwdArgs {
+    const void* q;     // [B][Hq][T][D], dtype
+    const void* k;     // [B][Hkv][T][D], dtype
+    const void* v;
+    const void* out;   // [B][Hq][T][D], dtype (the forward's output)
+    const void* dout;  // [B][Hq][T][D], dtype
+    const float* lse;  // [B][Hq][T] (the forward's row log-sum-exp)
+    const int32_t* seg;
+    const uint8_t* prefix;
+    const float* rope_cos;  // [T][D/2] or NULL
+    const float* rope_sin;
+    float* dq;  // [B][Hq][T][D]
+    float* dk;  // [B][Hkv][T][D]
+    float* dv;
+    int B, Hq, Hkv, T, D, window;
+    int dtype;  // 0 fp32, 1 bf16
+    float scale;
+};
+struct BwdWorkspace {
+    float* q32;
+    float* k32;
+    float* v32;
+    float* do32;
+    float* delta;
+};
+hipError_t launch_prefill_backward(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
+
 // Chunked prefill: the caller's tensors and the staged sequence length
 // Tv = S + W - 1 + Tc (sink rows, ring rows before the chunk, the chunk).
 struct ChunkArgs {

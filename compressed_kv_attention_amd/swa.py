@@ -23,7 +23,7 @@ EXPORTS = ("swa_last_error", "swa_version", "swa_prefill_workspace_size", "swa_a
            "swa_rope_table_host",
            "kv_pool_compress_rope", "swa_kv_quantize", "swa_decode_workspace_size", "swa_attn_decode",
            "swa_attn_decode_noalloc", "swa_attn_decode_compressed", "swa_chunk_prefill_workspace_size",
-           "swa_attn_chunk_prefill",
+           "swa_attn_chunk_prefill", "swa_prefill_backward_workspace_size", "swa_attn_prefill_backward",
            "swa_kv_budget_window", "swa_effective_kv_window")
 
 
@@ -86,6 +86,10 @@ def lib():
     L.swa_attn_decode_noalloc.restype = I
     L.swa_attn_decode_compressed.argtypes = [ctypes.POINTER(DecodeParams), I, P, P, I] + [P] * 16 + [P, Z, P]
     L.swa_attn_decode_compressed.restype = I
+    L.swa_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
+    L.swa_prefill_backward_workspace_size.restype = Z
+    L.swa_attn_prefill_backward.argtypes = [ctypes.POINTER(PrefillParams)] + [P] * 13 + [P, Z, P]
+    L.swa_attn_prefill_backward.restype = I
     L.swa_chunk_prefill_workspace_size.argtypes = [ctypes.POINTER(ChunkParams)]
     L.swa_chunk_prefill_workspace_size.restype = Z
     L.swa_attn_chunk_prefill.argtypes = [ctypes.POINTER(ChunkParams)] + [P] * 14 + [P, Z, P]
@@ -461,6 +465,49 @@ def decode_compressed(q, k_new, k_new_pre, v_new, ring_k, ring_v, ring_ks, ring_
                                             _ptr(pool_ks), _ptr(pool_vs), _ptr(front_k), _ptr(front_v), _ptr(pos),
                                             _ptr(out), _ptr(workspace) if ws_len else None, ws_len, _stream(q)))
     return out
+
+
+def prefill_backward(q, k, v, out, lse, dout, seg_ids=None, prefix=None, window=0, rope=None, scale=0.0,
+                     workspace=None):
+    """Gradients (dq, dk, dv) of prefill() in plain mode, fp32, from the forward's out and lse (prefill(...,
+    return_lse=True)).  q, k, v, out, dout share the forward's dtype; with rope (the forward's table) q and k
+    are the unrotated inputs and so are dq and dk."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, T, D] and k [B, Hkv, T, D]")
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    _shape(k, "k", (B, Hkv, T, D))
+    _shape(v, "v", (B, Hkv, T, D))
+    _shape(out, "out", (B, Hq, T, D))
+    _shape(dout, "dout", (B, Hq, T, D))
+    _shape(lse, "lse", (B, Hq, T))
+    _shape(seg_ids, "seg_ids", (B, T))
+    _shape(prefix, "prefix", (B, T))
+    cos, sin = rope if rope is not None else (None, None)
+    if cos is not None:
+        _shape(cos, "rope cos", (cos.shape[0], D // 2))
+        _shape(sin, "rope sin", (cos.shape[0], D // 2))
+    _dev(q, "q")
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _dev(t, name, q.dtype)
+    _dev(lse, "lse", torch.float32)
+    _dev(seg_ids, "seg_ids", torch.int32)
+    _dev(prefix, "prefix", torch.uint8)
+    _dev(cos, "rope cos", torch.float32)
+    _dev(sin, "rope sin", torch.float32)
+    _same_device(q, ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse), ("seg_ids", seg_ids),
+                 ("prefix", prefix), ("rope cos", cos), ("rope sin", sin))
+    p = prefill_params(q, k, window, 0, cos.shape[0] if cos is not None else 0, scale)
+    n = lib().swa_prefill_backward_workspace_size(ctypes.byref(p))
+    if n and (workspace is None or workspace.numel() * workspace.element_size() < n):
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    _check(lib().swa_attn_prefill_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                           _ptr(dout), _ptr(seg_ids), _ptr(prefix), _ptr(cos), _ptr(sin), _ptr(dq),
+                                           _ptr(dk), _ptr(dv), _ptr(workspace) if n else None, n, _stream(q)))
+    return dq, dk, dv
 
 
 def chunk_params(q, ring_k, sink_k, scale=0.0):

@@ -244,6 +244,27 @@ int swa_attn_decode_compressed(const swa_decode_params* p,   /* S = P, the poole
                                void* out,                    /* [B,Hq,D] bf16                   */
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Gradients of swa_attn_prefill in plain mode (compress_block == 0): the    */
+/* training-side use of the packing & causal & (recent | sink) mask ([NS]    */
+/* "KV sink 如何「钉住」工具"; [NW] "KV Sinks for Tools").  The pages give no  */
+/* backward; this is the derivative of the forward: with P = exp(scale q k^T */
+/* - lse) over the visible pairs, dP = dO v^T, Delta = rowsum(dO * out),     */
+/* dS = P (dP - Delta): dq = scale dS k, dk = scale dS^T q, dv = P^T dO,     */
+/* summed over each kv head's query heads.  out and lse are the forward's    */
+/* (lse: [B,Hq,T] fp32, natural log).  With rope_len > 0, q and k are the    */
+/* unrotated inputs (as for the forward) and so are dq and dk.  All         */
+/* arithmetic is fp32; dq/dk/dv are fp32, written (not accumulated into).   */
+/* Rows that see nothing (segment 0, lse = -inf) get dq = 0 and give nothing.*/
+size_t swa_prefill_backward_workspace_size(const swa_prefill_params* p);
+int swa_attn_prefill_backward(const swa_prefill_params* p,
+                              const void* q, const void* k, const void* v, /* as for swa_attn_prefill   */
+                              const void* out, const float* lse,           /* the forward's out and lse  */
+                              const void* dout,                            /* [B,Hq,T,D], p->dtype       */
+                              const int32_t* seg_ids, const uint8_t* prefix,
+                              const float* rope_cos, const float* rope_sin,
+                              float* dq, float* dk, float* dv,             /* [B,Hq|Hkv,T,D] fp32        */
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Chunked prefill into existing caches (the long-prompt path of [DS]       */
 /* "工作原理与配置方式", which prefills in chunks of 4096 tokens; mask of [NS] */
 /* "256-token 滑动窗口：源码走读").  A chunk of Tc tokens at positions         */

@@ -451,3 +451,22 @@ def test_chunk_prefill_wrapper_rejects_bad_shapes():
             swa.chunk_prefill(**dict(kw, **over))
     with pytest.raises(ValueError, match="device tensor"):
         swa.chunk_prefill(**kw)
+
+
+def test_prefill_backward_validation():
+    L = swa.lib()
+    p = _p(T=64, D=64, window=16)
+    n = L.swa_prefill_backward_workspace_size(ctypes.byref(p))
+    r = lambda x: (x + 255) // 256 * 256
+    nq, nk = 1 * 4 * 64 * 64 * 4, 1 * 2 * 64 * 64 * 4
+    assert n == 2 * r(nq) + 2 * r(nk) + r(1 * 4 * 64 * 4)
+    ptrs = [FAKE] * 13       # q, k, v, out, lse, dout, seg, prefix, cos, sin, dq, dk, dv
+    call = lambda pp, pt, ws=FAKE, nb=n: L.swa_attn_prefill_backward(ctypes.byref(pp), *pt, ws, nb, None)
+    assert call(_p(T=64, compress_block=4), ptrs) == swa.SWA_ERR_UNSUPPORTED
+    assert call(p, ptrs, None, 0) == swa.SWA_ERR_INVALID and "workspace" in L.swa_last_error().decode()
+    for i, name in ((0, "q"), (4, "lse"), (5, "dout"), (12, "dv")):
+        pt = list(ptrs)
+        pt[i] = None
+        assert call(p, pt) == swa.SWA_ERR_INVALID and name in L.swa_last_error().decode()
+    assert call(_p(T=64, D=48), ptrs) == swa.SWA_ERR_UNSUPPORTED
+    assert call(_p(T=0), [None] * 13, None, 0) == swa.SWA_OK
