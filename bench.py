@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3          # vector fp32 (the backward's arithmetic)
 ROTATE_BYTES = 600 << 20          # > 2 x the 256 MB MALL
 
 
@@ -48,7 +49,7 @@ def parse():
     ap.add_argument("--reps", type=int, default=20, help="iterations per timed graph when timing one kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16,decode_b1,decode_b8,decode_b32,decode_c4,chunk")
+    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16,decode_b1,decode_b8,decode_b32,decode_c4,chunk,backward")
     ap.add_argument("--decode-splits", type=int, default=0,
                     help="num_splits of the batch-256 decode part (0: the library's choice)")
     ap.add_argument("--eager", action="store_true",
@@ -334,6 +335,35 @@ def main():
         p.extra = dict(B=B, Hq=Hq, Hkv=Hkv, D=D, W=W, S=S, Tc=Tc, visible_pairs_per_head=vis)
         return p
 
+    def make_backward(name):
+        """The backward of the needle prefill (bf16 inputs, fp32 gradients): the forward's out and lse are made
+        once; a call is the whole backward (preparation, dq pass, dk/dv pass).  FLOPs counted as 2.5x the
+        forward's visible-pair FLOPs (five products per visible pair instead of two)."""
+        w = workloads.needle()
+        q, k, v = bf16(w["q_bits"]), bf16(w["k_bits"]), bf16(w["v_bits"])
+        seg = torch.from_numpy(w["seg_ids"]).to(dev)
+        pre = torch.from_numpy(w["prefix"]).to(dev)
+        rope = swa.rope_table(w["rope_theta"], w["T"], w["D"])
+        out, lse = swa.prefill(q, k, v, seg, pre, w["window"], rope=rope, return_lse=True)
+        dout = torch.randn(out.shape, device=dev).to(torch.bfloat16)
+        _, count = swa.debug_visibility(w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["window"], torch.bfloat16,
+                                        seg, pre, want_mask=False)
+        nvis = int(count.to(torch.int64).sum().item())
+        flops = 2.5 * 4.0 * w["D"] * w["Hq"] * nvis
+        ws = [None]
+
+        def launch(i):
+            swa.prefill_backward(q, k, v, out, lse, dout, seg, pre, w["window"], rope=rope, workspace=ws[0])
+        # the workspace, allocated once outside the timed graphs
+        p_ = swa.prefill_params(q, k, w["window"], 0, w["T"], 0.0)
+        import ctypes as _ct
+        ws[0] = torch.empty(swa.lib().swa_prefill_backward_workspace_size(_ct.byref(p_)), dtype=torch.uint8,
+                            device=dev)
+        p = Part(name, launch, 1, flops, 0.0, kernel="bwd_dq_kernel + bwd_dkv_kernel")
+        p.extra = dict(B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], T=w["T"], D=w["D"], window=w["window"],
+                       visible_pairs_per_head=nvis)
+        return p
+
     t_setup = time.time()
     if "needle" in parts_wanted:
         parts["needle"] = make_prefill("needle", workloads.needle())
@@ -344,6 +374,8 @@ def main():
     for b in (1, 8, 32):
         if f"decode_b{b}" in parts_wanted:
             parts[f"decode_b{b}"] = make_decode(f"decode_b{b}", B=b)
+    if "backward" in parts_wanted:
+        parts["backward"] = make_backward("backward")
     if "chunk" in parts_wanted:
         parts["chunk"] = make_chunk("chunk")
     if "decode_c4" in parts_wanted:
@@ -473,6 +505,10 @@ def main():
                             if n.startswith("decode") and n != "decode_c4"},
         "compressed_decode": {k: (round(v, 5) if isinstance(v, float) else v)
                               for k, v in results.get("decode_c4", {}).items()},
+        "backward": {"value": round(results.get("backward", {}).get("tflops", 0.0), 3), "unit": "TFLOP/s",
+                     "frac_fp32_peak": round(results.get("backward", {}).get("tflops", 0.0) / FP32_PEAK_TFLOPS, 5),
+                     "us_per_call": round(results.get("backward", {}).get("ms", 0.0) * 1e3, 2),
+                     "config": "needle prefill backward, bf16 inputs, fp32 vector arithmetic"},
         "chunked_prefill": {"value": round(results.get("chunk", {}).get("tflops", 0.0), 3), "unit": "TFLOP/s",
                             "frac_mfma_peak": round(results.get("chunk", {}).get("frac_mfma_peak", 0.0), 5),
                             "us_per_call": round(results.get("chunk", {}).get("ms", 0.0) * 1e3, 2)},

@@ -12,7 +12,7 @@
 // (rotating q and k when a RoPE table is given) and forms Delta; a
 // query-major pass walks each query row's visible keys (the forward's tile
 // enumeration) for dq; a key-major pass walks each key's visible queries for
-// dk and dv, summing over the query heads of its GQA group.  With RoPE, dq and
+// dk and dv, one query head per wave, and the heads of a GQA group are summed.  With RoPE, dq and
 // dk are rotated back (by the negative angle) before they are stored.
 //
 // Both passes use lane pairs: lanes l and l + 32 of a wave hold the two channel
@@ -99,8 +99,8 @@ __device__ __forceinline__ void unrotate_half(float (&g)[H], int half, const Bwd
 
 template <int D>
 struct SmemDq {
-    float ks[BT][D + 1];
-    float vs[BT][D + 1];
+    float ks[BT][D];  // (rows 16-byte aligned: every lane of a half reads the same row)
+    float vs[BT][D];
     int kinfo[BT];
     int ksum[4];
     uint32_t sink_bits[(kMaxT / BT + 31) / 32];
@@ -194,27 +194,30 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdArgs a, const float* q32,
 
 template <int D>
 struct SmemDkv {
-    float qs[BT][D + 1];
-    float gs[BT][D + 1];
+    float qs[BT][D];
+    float gs[BT][D];
     float lse[BT];
     float dlt[BT];
     int seg[BT];
 };
 
-// dk, dv: one wave per 32 keys of one kv head; lane pair (r, half).  The
+// dk, dv: one wave per 32 keys and one query head; lane pair (r, half).  The
 // queries that can see a key of the block: the rows from the block's first
 // key to its last key + W - 1 (every row after it without a window), and,
-// when the block holds sink keys, every later row of their segments.
+// when the block holds sink keys, every later row of their segments.  With
+// GQA groups of G > 1 heads each head's share goes to the per-head buffers
+// pk/pv ([B][Hq][T][D]) and bwd_sum_heads_kernel adds them in head order.
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dkv_kernel(BwdArgs a, const float* q32, const float* k32, const float* v32,
-                                                     const float* do32, const float* delta) {
+                                                     const float* do32, const float* delta, float* pk, float* pv) {
     constexpr int H = D / 2;
     __shared__ SmemDkv<D> sm;
     const int lane = threadIdx.x;
     const int r = lane & 31, half = lane >> 5;
     const int T = a.T;
-    const int b = blockIdx.z, hkv = blockIdx.y;
+    const int b = blockIdx.z, hq = blockIdx.y;
     const int G = a.Hq / a.Hkv;
+    const int hkv = hq / G;
     const int s0 = blockIdx.x * BT;
     const int my_k = s0 + r;
     const bool key_ok = my_k < T;
@@ -249,8 +252,8 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(BwdArgs a, const float* q32
             const int sq = tq < T ? (a.seg ? a.seg[(size_t)b * T + tq] : 1) : 0;
             if (__ballot(sq >= sk_lo && sq <= sk_hi) == 0) continue;
         }
-        for (int h = hkv * G; h < (hkv + 1) * G; ++h) {
-            const size_t qhead = ((size_t)b * a.Hq + h) * (size_t)T;
+        {
+            const size_t qhead = ((size_t)b * a.Hq + hq) * (size_t)T;
             __syncthreads();
             for (int e = lane; e < BT * D; e += 64) {
                 const int qi = e / D, d = e % D, tq = t0 + qi;
@@ -291,10 +294,30 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(BwdArgs a, const float* q32
     }
     if (a.rope_cos) unrotate_half<H>(dk, half, a, key_ok ? my_k : 0);
     if (!key_ok) return;
+    float* ok = G == 1 ? a.dk + krow * D : pk + (((size_t)b * a.Hq + hq) * T + my_k) * D;
+    float* ov = G == 1 ? a.dv + krow * D : pv + (((size_t)b * a.Hq + hq) * T + my_k) * D;
 #pragma unroll
     for (int i = 0; i < H; ++i) {
-        a.dk[krow * D + half * H + i] = dk[i];
-        a.dv[krow * D + half * H + i] = dv[i];
+        ok[half * H + i] = dk[i];
+        ov[half * H + i] = dv[i];
+    }
+}
+
+// dk, dv of a kv head = the sum of its G query heads' shares, in head order.
+__global__ void bwd_sum_heads_kernel(BwdArgs a, const float* pk, const float* pv) {
+    const int G = a.Hq / a.Hkv;
+    const long long n = (long long)a.B * a.Hkv * a.T * a.D;
+    const long long per_head = (long long)a.T * a.D;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
+        const long long bh = i / per_head, e = i % per_head;  // bh = b * Hkv + hkv
+        const long long src = (bh * G) * per_head + e;         // first query head of the group
+        float sk = 0.f, sv = 0.f;
+        for (int g = 0; g < G; ++g) {
+            sk += pk[src + g * per_head];
+            sv += pv[src + g * per_head];
+        }
+        a.dk[i] = sk;
+        a.dv[i] = sv;
     }
 }
 
@@ -314,8 +337,9 @@ hipError_t launch_bwd_d(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) 
     const unsigned nt = (unsigned)((a.T + BT - 1) / BT);
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(nt, (unsigned)a.Hq, (unsigned)a.B), blk, 0, s, a, w.q32, w.k32, w.v32,
                        w.do32, w.delta);
-    hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3(nt, (unsigned)a.Hkv, (unsigned)a.B), blk, 0, s, a, w.q32, w.k32,
-                       w.v32, w.do32, w.delta);
+    hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3(nt, (unsigned)a.Hq, (unsigned)a.B), blk, 0, s, a, w.q32, w.k32,
+                       w.v32, w.do32, w.delta, w.pk, w.pv);
+    if (a.Hq != a.Hkv) hipLaunchKernelGGL(bwd_sum_heads_kernel, dim3(2048), dim3(256), 0, s, a, w.pk, w.pv);
     return hipGetLastError();
 }
 

@@ -517,16 +517,19 @@ int swa_attn_decode_compressed(const swa_decode_params* p, int block, const floa
 namespace {
 // Workspace of a backward call: fp32 q, dO, k, v and Delta, 256-byte aligned parts.
 struct BwdLayout {
-    size_t q32, do32, k32, v32, delta, total;
+    size_t q32, do32, k32, v32, delta, pk, pv, total;
 };
 BwdLayout bwd_layout(const swa_prefill_params* p) {
-    BwdLayout L{0, 0, 0, 0, 0, 0};
+    BwdLayout L{0, 0, 0, 0, 0, 0, 0, 0};
     const size_t nq = (size_t)p->B * p->Hq * p->T * p->D * 4, nk = (size_t)p->B * p->Hkv * p->T * p->D * 4;
     L.do32 = round256(nq);
     L.k32 = L.do32 + round256(nq);
     L.v32 = L.k32 + round256(nk);
     L.delta = L.v32 + round256(nk);
-    L.total = L.delta + round256((size_t)p->B * p->Hq * p->T * 4);
+    L.pk = L.delta + round256((size_t)p->B * p->Hq * p->T * 4);
+    const size_t part = p->Hq != p->Hkv ? round256(nq) : 0;  // per-head dk/dv shares
+    L.pv = L.pk + part;
+    L.total = L.pv + part;
     return L;
 }
 }  // namespace
@@ -591,7 +594,8 @@ int swa_attn_prefill_backward(const swa_prefill_params* p, const void* q, const 
     a.scale = pa.scale;
     char* ws = (char*)workspace;
     const swa::BwdWorkspace w{(float*)(ws + L.q32), (float*)(ws + L.k32), (float*)(ws + L.v32),
-                              (float*)(ws + L.do32), (float*)(ws + L.delta)};
+                              (float*)(ws + L.do32), (float*)(ws + L.delta), (float*)(ws + L.pk),
+                              (float*)(ws + L.pv)};
     return hip_status(swa::launch_prefill_backward(a, w, (hipStream_t)stream), "swa_attn_prefill_backward launch");
 }
 

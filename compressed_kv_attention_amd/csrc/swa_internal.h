@@ -218,6 +218,8 @@ struct BwdWorkspace {
     float* v32;
     float* do32;
     float* delta;
+    float* pk;  // per-query-head dk / dv shares [B][Hq][T][D] (GQA groups of more than one head)
+    float* pv;
 };
 hipError_t launch_prefill_backward(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
 

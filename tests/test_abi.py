@@ -459,7 +459,7 @@ def test_prefill_backward_validation():
     n = L.swa_prefill_backward_workspace_size(ctypes.byref(p))
     r = lambda x: (x + 255) // 256 * 256
     nq, nk = 1 * 4 * 64 * 64 * 4, 1 * 2 * 64 * 64 * 4
-    assert n == 2 * r(nq) + 2 * r(nk) + r(1 * 4 * 64 * 4)
+    assert n == 2 * r(nq) + 2 * r(nk) + r(1 * 4 * 64 * 4) + 2 * r(nq)   # GQA 2: per-head dk/dv shares
     ptrs = [FAKE] * 13       # q, k, v, out, lse, dout, seg, prefix, cos, sin, dq, dk, dv
     call = lambda pp, pt, ws=FAKE, nb=n: L.swa_attn_prefill_backward(ctypes.byref(pp), *pt, ws, nb, None)
     assert call(_p(T=64, compress_block=4), ptrs) == swa.SWA_ERR_UNSUPPORTED
