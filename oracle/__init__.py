@@ -62,6 +62,7 @@ def _load():
     lib.oracle_effective_kv_window.restype = LL
     lib.oracle_quantize.argtypes = [LL, I, P, P, P]
     lib.oracle_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, D, P, P]
+    lib.oracle_nsa_select.argtypes = [I, I, I, I, I, P, P, P, I, I, I, D, D, I, P, P, P, P]
     lib.oracle_prefill_backward.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I, D, D, P, P, P]
     lib.oracle_chunk_prefill.argtypes = [I, I, I, I, I, I, I] + [P] * 13 + [D, P, P]
     lib.oracle_compressed_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, D, I, D, I,
@@ -336,3 +337,24 @@ def prefill_backward(q, k, v, dout, seg_ids=None, prefix=None, window=0, scale=N
     lib.oracle_prefill_backward(B, Hq, Hkv, T, Dm, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(seg), _ptr(pre),
                                 int(window), float(scale), float(theta), _ptr(dq), _ptr(dk), _ptr(dv))
     return dq, dk, dv
+
+
+def nsa_select(q, k_pre, v, window, block, n_select, scale=None, theta=10000.0, rope_len=None, sel=None):
+    """O11: the NSA selection branch (no gate).  q/k_pre/v [B,Hq|Hkv,T,D] before RoPE.  Returns (out [B,Hq,T,D],
+    lse [B,Hq,T], sel [B,Hq,T,n_select] int32 in score order, -1 = none).  `sel` replaces the selection."""
+    lib = _load()
+    q, k_pre, v = _f64(q), _f64(k_pre), _f64(v)
+    B, Hq, T, Dm = q.shape
+    Hkv = k_pre.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dm)
+    if rope_len is None:
+        rope_len = T
+    sel_in = _opt(sel, np.int32)
+    sel_out = np.empty((B, Hq, T, n_select), dtype=np.int32)
+    out = np.empty((B, Hq, T, Dm), dtype=np.float64)
+    lse = np.empty((B, Hq, T), dtype=np.float64)
+    lib.oracle_nsa_select(B, Hq, Hkv, T, Dm, _ptr(q), _ptr(k_pre), _ptr(v), int(window), int(block), int(n_select),
+                          float(scale), float(theta), int(rope_len), _ptr(sel_in), _ptr(sel_out), _ptr(out),
+                          _ptr(lse))
+    return out, lse, sel_out

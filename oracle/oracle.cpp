@@ -39,7 +39,10 @@
 //        was before the chunk, and its own unquantized keys; then the ring
 //        takes its last W tokens (see O9).
 //   R-A21 backward: the plain derivative of the forward definition (O10).
+//   R-A22 NSA selection branch: top-k pooled blocks among those that cleared
+//        the window, by compressed score; attention over their exact tokens.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -710,6 +713,74 @@ void oracle_prefill_backward(int B, int Hq, int Hkv, int T, int D, const double*
             else for (int d = 0; d < D; ++d) dk[ko + d] = dk_rot[ko + d];
             for (int d = 0; d < D; ++d) dv[ko + d] = dv_acc[ko + d];
         }
+    }
+}
+
+// O11: the selection branch of NSA without its gate.  [CA §"Two kinds of
+// columns, pooled blocks and exact recent keys"] names NSA's three branches
+// -- compressed, selected (the top-k blocks by their compressed scores) and
+// the window -- mixed by a learned gate; [CA §"What we didn't build, and
+// why"] left selection and the gate out.  Reading A22: for row t the
+// candidates are the pooled blocks the compressed variant shows,
+// (j + 1) * b <= t - W + 1 (so no selected token is in the window); block
+// j's score is scale <q_t, pk_j> with q rotated at t and pk_j the O4 pooled
+// key (mean before RoPE, rotated at the block midpoint); the branch takes the
+// n_select best blocks (higher score first, the lower j on ties; all when
+// fewer) and attends with one softmax over the exact keys, rotated at their
+// positions, of every token in them.  No candidate: output 0, lse -inf.
+// sel_in (optional, [B,Hq,T,n_select], -1 = none) replaces the selection;
+// sel_out (optional) receives it, in score order.
+//   q/k/v [B,Hq|Hkv,T,D] (pre-RoPE), out [B,Hq,T,D], lse [B,Hq,T] or NULL.
+void oracle_nsa_select(int B, int Hq, int Hkv, int T, int D, const double* q, const double* k_pre,
+                       const double* v, int window, int block, int n_select, double scale, double theta,
+                       int rope_len, const int32_t* sel_in, int32_t* sel_out, double* out, double* lse) {
+    const int G = Hq / Hkv;
+    const int nblk = T / block;
+    const long long NKV = static_cast<long long>(B) * Hkv;
+    std::vector<double> pk(static_cast<size_t>(NKV) * nblk * D), pv(static_cast<size_t>(NKV) * nblk * D);
+    oracle_pool_rope(NKV, T, D, block, theta, rope_len, k_pre, v, pk.data(), pv.data());
+    std::vector<double> k_rot;
+    const double* kk = k_pre;
+    if (theta > 0.0) {
+        k_rot = rotate_rows(k_pre, NKV, T, D, theta);
+        kk = k_rot.data();
+    }
+    const long long rows = static_cast<long long>(B) * Hq * T;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long long r = 0; r < rows; ++r) {
+        const int t = static_cast<int>(r % T);
+        const int h = static_cast<int>((r / T) % Hq);
+        const int b = static_cast<int>(r / (static_cast<long long>(T) * Hq));
+        const size_t nk = static_cast<size_t>(b) * Hkv + h / G;
+        std::vector<double> qrow(D);
+        if (theta > 0.0) rope_rotate(q + r * D, qrow.data(), D, theta, t);
+        else for (int d = 0; d < D; ++d) qrow[d] = q[r * D + d];
+        std::vector<int> chosen;
+        if (sel_in) {
+            for (int i = 0; i < n_select; ++i)
+                if (sel_in[r * n_select + i] >= 0) chosen.push_back(sel_in[r * n_select + i]);
+        } else {
+            std::vector<std::pair<double, int>> cand;  // (-score, j): ascending = best first, lower j on ties
+            for (int j = 0; j < nblk; ++j) {
+                if (!visible_pooled(t, j, window, block)) continue;
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d) dot += qrow[d] * pk[(nk * nblk + j) * D + d];
+                cand.push_back({-scale * dot, j});
+            }
+            std::sort(cand.begin(), cand.end());
+            for (size_t i = 0; i < cand.size() && static_cast<int>(i) < n_select; ++i) chosen.push_back(cand[i].second);
+        }
+        if (sel_out)
+            for (int i = 0; i < n_select; ++i)
+                sel_out[r * n_select + i] = i < static_cast<int>(chosen.size()) ? chosen[i] : -1;
+        std::vector<const double*> keys, vals;
+        for (int j : chosen)
+            for (int u = 0; u < block; ++u) {
+                const size_t row = nk * T + static_cast<size_t>(j) * block + u;
+                keys.push_back(kk + row * D);
+                vals.push_back(v + row * D);
+            }
+        attend_row(qrow.data(), keys, vals, D, scale, out + r * D, lse ? lse + r : nullptr);
     }
 }
 

@@ -822,3 +822,60 @@ def test_prefill_backward_finite_differences_and_padding():
             num[idx] = (loss(*a_p) - loss(*a_m)) / (2 * eps)
         np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-7, err_msg=name)
     assert np.all(dq[:, :, 8] == 0) and np.all(dk[:, :, 8] == 0) and np.all(dv[:, :, 8] == 0)
+
+
+# --------------------------------------------------------------------------
+# O11 NSA selection branch without the gate  ([CA §"Two kinds of columns,
+# pooled blocks and exact recent keys", §"What we didn't build, and why"];
+# reading A22)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("W,b,n_sel,Hq,Hkv", [(8, 4, 3, 2, 2), (5, 3, 5, 4, 2), (16, 8, 2, 2, 1)])
+def test_nsa_select_is_top_k_of_numpy_scores_then_sdpa(W, b, n_sel, Hq, Hkv):
+    # the selection is the stable argsort of the compressed scores (numpy
+    # matmul of the O2-rotated q and the O4 pooled keys) over the visible
+    # blocks; the output is SDPA over the chosen blocks' rotated exact keys
+    B, T, D = 2, 64, 16
+    q, k, v = _case(B, Hq, Hkv, T, D, seed=90 + W + b)
+    out, lse, sel = oracle.nsa_select(q, k, v, W, b, n_sel, theta=1e4)
+    pk, _ = oracle.pool_rope(k, v, b, theta=1e4, rope_len=T)
+    pos = np.arange(T)
+    scale = 1.0 / math.sqrt(D)
+    G = Hq // Hkv
+    for bb in range(B):
+        for h in range(Hq):
+            qr = oracle.rope(q[bb, h], pos, 1e4)
+            kr = oracle.rope(k[bb, h // G], pos, 1e4)
+            scores = scale * qr @ pk[bb, h // G].T
+            for t in range(T):
+                nv = max(0, (t - W + 1) // b)
+                order = np.argsort(-scores[t, :nv], kind="stable")[:n_sel]
+                want = np.full(n_sel, -1)
+                want[:len(order)] = order
+                np.testing.assert_array_equal(sel[bb, h, t], want)
+                if len(order) == 0:
+                    assert np.all(out[bb, h, t] == 0) and np.isneginf(lse[bb, h, t])
+                    continue
+                cols = np.concatenate([np.arange(j * b, (j + 1) * b) for j in order])
+                ref = sdpa(qr[t][None], kr[cols], v[bb, h // G][cols])
+                np.testing.assert_allclose(out[bb, h, t], ref[0], rtol=1e-12, atol=1e-12)
+
+
+def test_nsa_select_all_blocks_is_attention_over_every_cleared_block():
+    # n_select >= the number of candidates: every token of every block that
+    # cleared the window, i.e. positions [0, floor((t - W + 1) / b) * b)
+    B, H, T, D, W, b = 1, 2, 50, 8, 6, 4
+    q, k, v = _case(B, H, H, T, D, seed=95)
+    out, lse, sel = oracle.nsa_select(q, k, v, W, b, T, theta=1e4)
+    pos = np.arange(T)
+    qr = np.stack([oracle.rope(q[0, h], pos, 1e4) for h in range(H)])[None]
+    kr = np.stack([oracle.rope(k[0, h], pos, 1e4) for h in range(H)])[None]
+    nv = np.maximum(0, (pos - W + 1) // b)
+    mask = np.arange(T)[None, :] < (nv * b)[:, None]
+    ok = nv > 0
+    ref = sdpa(qr[:, :, ok], kr, v, mask=mask[ok])
+    np.testing.assert_allclose(out[:, :, ok], ref, rtol=1e-12, atol=1e-12)
+    assert np.all(out[:, :, ~ok] == 0) and np.all(sel[:, :, ~ok] == -1)
+    # the override replaces the selection
+    out2, _, sel2 = oracle.nsa_select(q, k, v, W, b, T, theta=1e4, sel=sel)
+    np.testing.assert_array_equal(out2, out)
