@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libswa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["swa_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "debug_visibility.hip", "pool_rope.hip", "chunk.hip", "backward.hip",
+SOURCES = ["swa_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "debug_visibility.hip", "pool_rope.hip", "chunk.hip", "backward.hip", "nsa.hip",
            "decode.hip"]
 ARCH = os.environ.get("SWA_OFFLOAD_ARCH", "gfx950")
 

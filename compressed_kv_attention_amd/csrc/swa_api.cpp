@@ -512,6 +512,65 @@ int swa_attn_decode_compressed(const swa_decode_params* p, int block, const floa
     return hip_status(swa::launch_decode(a, (hipStream_t)stream), "swa_attn_decode_compressed launch");
 }
 
+size_t swa_nsa_select_workspace_size(const swa_prefill_params* p) {
+    if (p == nullptr || p->B <= 0 || p->T <= 0 || p->Hkv <= 0 || p->D <= 0 || p->compress_block <= 0) return 0;
+    const size_t nk = (size_t)p->B * p->Hkv * p->T * p->D * 4;
+    const size_t np = (size_t)p->B * p->Hkv * (p->T / p->compress_block) * p->D * 4;
+    return 2 * round256(nk) + round256(np);
+}
+
+int swa_nsa_select_attn(const swa_prefill_params* p, int n_select, const void* q, const void* k, const void* v,
+                        const float* rope_cos, const float* rope_sin, void* out, float* lse, int32_t* sel,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    swa::PrefillArgs pa;
+    int rc = check_prefill(p, nullptr, nullptr, pa);
+    if (rc != SWA_OK) return rc;
+    REQUIRE(p->compress_block >= 1, "compress_block (the block size) must be >= 1 (got %d)", p->compress_block);
+    REQUIRE(n_select >= 1 && n_select <= 32, "n_select must be in [1, 32] (got %d)", n_select);
+    if (p->B > 65535 || p->Hq > 65535) return fail(SWA_ERR_UNSUPPORTED, "B and Hq must be <= 65535");
+    if (p->B == 0 || p->T == 0) return ok();
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(lse);
+    OPTIONAL_PTR(sel);
+    if (p->rope_len > 0) {
+        REQUIRE_PTR(rope_cos);
+        REQUIRE_PTR(rope_sin);
+    }
+    const size_t need = swa_nsa_select_workspace_size(p);
+    REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 255u) == 0,
+            "workspace must be a 256-byte aligned buffer of swa_nsa_select_workspace_size() bytes");
+    REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+    swa::NsaArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.rope_cos = p->rope_len > 0 ? rope_cos : nullptr;
+    a.rope_sin = p->rope_len > 0 ? rope_sin : nullptr;
+    a.out = out;
+    a.lse = lse;
+    a.sel = sel;
+    a.B = p->B;
+    a.Hq = p->Hq;
+    a.Hkv = p->Hkv;
+    a.T = p->T;
+    a.D = p->D;
+    a.window = p->window;
+    a.block = p->compress_block;
+    a.nblk = p->T / p->compress_block;
+    a.n_select = n_select;
+    a.rope_len = p->rope_len;
+    a.dtype = p->dtype == SWA_BF16 ? 1 : 0;
+    a.scale = pa.scale;
+    const size_t nk = round256((size_t)p->B * p->Hkv * p->T * p->D * 4);
+    char* ws = (char*)workspace;
+    return hip_status(swa::launch_nsa_select(a, (float*)ws, (float*)(ws + nk), (float*)(ws + 2 * nk),
+                                             (hipStream_t)stream),
+                      "swa_nsa_select_attn launch");
+}
+
 }  // extern "C"
 
 namespace {

@@ -223,6 +223,24 @@ struct BwdWorkspace {
 };
 hipError_t launch_prefill_backward(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
 
+// NSA selection branch: the caller's tensors (q, k, v before RoPE).
+struct NsaArgs {
+    const void* q;  // [B][Hq][T][D], dtype
+    const void* k;  // [B][Hkv][T][D], dtype
+    const void* v;
+    const float* rope_cos;  // [rope_len][D/2] or NULL
+    const float* rope_sin;
+    void* out;       // [B][Hq][T][D], dtype
+    float* lse;      // [B][Hq][T] or NULL
+    int32_t* sel;    // [B][Hq][T][n_select] or NULL
+    int B, Hq, Hkv, T, D, window, block, nblk, n_select, rope_len;
+    int dtype;  // 0 fp32, 1 bf16
+    float scale;
+};
+// Preparation (fp32 rotated exact keys and values, fp32 pooled keys) and the
+// selection kernel; k32/v32 [B][Hkv][T][D], pk32 [B][Hkv][nblk][D].
+hipError_t launch_nsa_select(const NsaArgs& a, float* k32, float* v32, float* pk32, hipStream_t s);
+
 // Chunked prefill: the caller's tensors and the staged sequence length
 // Tv = S + W - 1 + Tc (sink rows, ring rows before the chunk, the chunk).
 struct ChunkArgs {

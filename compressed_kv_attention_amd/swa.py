@@ -24,6 +24,7 @@ EXPORTS = ("swa_last_error", "swa_version", "swa_prefill_workspace_size", "swa_a
            "kv_pool_compress_rope", "swa_kv_quantize", "swa_decode_workspace_size", "swa_attn_decode",
            "swa_attn_decode_noalloc", "swa_attn_decode_compressed", "swa_chunk_prefill_workspace_size",
            "swa_attn_chunk_prefill", "swa_prefill_backward_workspace_size", "swa_attn_prefill_backward",
+           "swa_nsa_select_workspace_size", "swa_nsa_select_attn",
            "swa_kv_budget_window", "swa_effective_kv_window")
 
 
@@ -86,6 +87,10 @@ def lib():
     L.swa_attn_decode_noalloc.restype = I
     L.swa_attn_decode_compressed.argtypes = [ctypes.POINTER(DecodeParams), I, P, P, I] + [P] * 16 + [P, Z, P]
     L.swa_attn_decode_compressed.restype = I
+    L.swa_nsa_select_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
+    L.swa_nsa_select_workspace_size.restype = Z
+    L.swa_nsa_select_attn.argtypes = [ctypes.POINTER(PrefillParams), I] + [P] * 8 + [P, Z, P]
+    L.swa_nsa_select_attn.restype = I
     L.swa_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
     L.swa_prefill_backward_workspace_size.restype = Z
     L.swa_attn_prefill_backward.argtypes = [ctypes.POINTER(PrefillParams)] + [P] * 13 + [P, Z, P]
@@ -508,6 +513,42 @@ def prefill_backward(q, k, v, out, lse, dout, seg_ids=None, prefix=None, window=
                                            _ptr(dout), _ptr(seg_ids), _ptr(prefix), _ptr(cos), _ptr(sin), _ptr(dq),
                                            _ptr(dk), _ptr(dv), _ptr(workspace) if n else None, n, _stream(q)))
     return dq, dk, dv
+
+
+def nsa_select(q, k, v, window, block, n_select, rope=None, scale=0.0, workspace=None):
+    """The NSA selection branch without its gate (swa_nsa_select_attn).  q [B,Hq,T,D], k/v [B,Hkv,T,D] before
+    RoPE (fp32 or bf16); rope: (cos, sin) from rope_table() or None.  Returns (out [B,Hq,T,D] in q's dtype,
+    lse [B,Hq,T] fp32, sel [B,Hq,T,n_select] int32: the chosen blocks in score order, -1 after the last)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, T, D] and k [B, Hkv, T, D]")
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    _shape(k, "k", (B, Hkv, T, D))
+    _shape(v, "v", (B, Hkv, T, D))
+    if not 1 <= int(n_select) <= 32:
+        raise ValueError(f"n_select must be in [1, 32] (got {n_select})")
+    if int(block) < 1 or int(window) < 1:
+        raise ValueError("block and window must be >= 1")
+    cos, sin = rope if rope is not None else (None, None)
+    if cos is not None:
+        _shape(cos, "rope cos", (cos.shape[0], D // 2))
+        _shape(sin, "rope sin", (cos.shape[0], D // 2))
+    _dev(q, "q")
+    _dev(k, "k", q.dtype)
+    _dev(v, "v", q.dtype)
+    _dev(cos, "rope cos", torch.float32)
+    _dev(sin, "rope sin", torch.float32)
+    _same_device(q, ("k", k), ("v", v), ("rope cos", cos), ("rope sin", sin))
+    p = prefill_params(q, k, window, block, cos.shape[0] if cos is not None else 0, scale)
+    n = lib().swa_nsa_select_workspace_size(ctypes.byref(p))
+    if n and (workspace is None or workspace.numel() * workspace.element_size() < n):
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    sel = torch.empty((B, Hq, T, int(n_select)), dtype=torch.int32, device=q.device)
+    _check(lib().swa_nsa_select_attn(ctypes.byref(p), int(n_select), _ptr(q), _ptr(k), _ptr(v), _ptr(cos), _ptr(sin),
+                                     _ptr(out), _ptr(lse), _ptr(sel), _ptr(workspace) if n else None, n, _stream(q)))
+    return out, lse, sel
 
 
 def chunk_params(q, ring_k, sink_k, scale=0.0):

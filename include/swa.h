@@ -265,6 +265,27 @@ int swa_attn_prefill_backward(const swa_prefill_params* p,
                               float* dq, float* dk, float* dv,             /* [B,Hq|Hkv,T,D] fp32        */
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* The selection branch of NSA, without its learned gate ([CA] "Two kinds of */
+/* columns, pooled blocks and exact recent keys": the top-k blocks by their  */
+/* compressed scores; "What we didn't build, and why").  For row t the        */
+/* candidates are the pooled blocks that have cleared the window,            */
+/* (j + 1) * b <= t - W + 1 with b = p->compress_block and W = p->window;    */
+/* block j's score is scale <q_t, pk_j>, pk_j the mean of the block's keys   */
+/* before RoPE rotated at min(j b + b/2, rope_len - 1) ([CA] "Pool before    */
+/* rotating, not after"); the n_select best blocks (the lower j on ties; all */
+/* when fewer) are chosen, and one softmax runs over the exact keys, rotated */
+/* at their positions, of all their tokens.  out [B,Hq,T,D] (p->dtype), lse  */
+/* [B,Hq,T] fp32 or NULL, sel [B,Hq,T,n_select] int32 (the chosen blocks in  */
+/* score order, -1 after the last) or NULL.  A row with no candidate gets    */
+/* out = 0, lse = -inf.  Arithmetic is fp32.  1 <= n_select <= 32; W >= 1;   */
+/* q, k, v as for swa_attn_prefill (rope_len 0: no rotation).               */
+size_t swa_nsa_select_workspace_size(const swa_prefill_params* p);
+int swa_nsa_select_attn(const swa_prefill_params* p, int n_select,
+                        const void* q, const void* k, const void* v, /* [B,Hq|Hkv,T,D], before RoPE */
+                        const float* rope_cos, const float* rope_sin,
+                        void* out, float* lse, int32_t* sel,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Chunked prefill into existing caches (the long-prompt path of [DS]       */
 /* "工作原理与配置方式", which prefills in chunks of 4096 tokens; mask of [NS] */
 /* "256-token 滑动窗口：源码走读").  A chunk of Tc tokens at positions         */

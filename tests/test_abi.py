@@ -470,3 +470,22 @@ def test_prefill_backward_validation():
         assert call(p, pt) == swa.SWA_ERR_INVALID and name in L.swa_last_error().decode()
     assert call(_p(T=64, D=48), ptrs) == swa.SWA_ERR_UNSUPPORTED
     assert call(_p(T=0), [None] * 13, None, 0) == swa.SWA_OK
+
+
+def test_nsa_select_validation():
+    L = swa.lib()
+    p = _p(T=64, D=64, window=16, compress_block=4)
+    n = L.swa_nsa_select_workspace_size(ctypes.byref(p))
+    r = lambda x: (x + 255) // 256 * 256
+    assert n == 2 * r(1 * 2 * 64 * 64 * 4) + r(1 * 2 * 16 * 64 * 4)
+    assert L.swa_nsa_select_workspace_size(ctypes.byref(_p(T=64, compress_block=0))) == 0
+    ptrs = [FAKE] * 8           # q, k, v, cos, sin, out, lse, sel
+    call = lambda pp, ns, pt, ws=FAKE, nb=n: L.swa_nsa_select_attn(ctypes.byref(pp), ns, *pt, ws, nb, None)
+    assert call(p, 0, ptrs) == swa.SWA_ERR_INVALID and "n_select" in L.swa_last_error().decode()
+    assert call(p, 33, ptrs) == swa.SWA_ERR_INVALID
+    assert call(_p(T=64, compress_block=0), 4, ptrs) == swa.SWA_ERR_INVALID
+    assert call(_p(T=64, window=0, compress_block=4), 4, ptrs) == swa.SWA_ERR_INVALID
+    assert call(p, 4, ptrs, None, 0) == swa.SWA_ERR_INVALID and "workspace" in L.swa_last_error().decode()
+    pt = list(ptrs)
+    pt[1] = None
+    assert call(p, 4, pt) == swa.SWA_ERR_INVALID and "k" in L.swa_last_error().decode()
