@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--reps", type=int, default=20, help="iterations per timed graph when timing one kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16,decode_b1,decode_b8,decode_b32,decode_c4,chunk,backward")
+    ap.add_argument("--parts", default="needle,compressed4,decode,packed,compressed16,decode_b1,decode_b8,decode_b32,decode_c4,chunk,backward,nsa")
     ap.add_argument("--decode-splits", type=int, default=0,
                     help="num_splits of the batch-256 decode part (0: the library's choice)")
     ap.add_argument("--eager", action="store_true",
@@ -364,6 +364,27 @@ def main():
                        visible_pairs_per_head=nvis)
         return p
 
+    def make_nsa(name, block=4, n_select=16):
+        """The NSA selection branch on the compressed config (B4, 8/8 heads, D64, T4096, window 256, bf16
+        inputs), 16 blocks of 4 per row.  FLOPs: the compressed scores of every candidate block (2 D each) and
+        attention over the chosen tokens (4 D per token)."""
+        w = workloads.compressed(block=block, dtype="bf16")
+        q, k, v = bf16(w["q_bits"]), bf16(w["k_bits"]), bf16(w["v_bits"])
+        rope = swa.rope_table(w["rope_theta"], w["T"], w["D"])
+        T, W, D = w["T"], w["window"], w["D"]
+        nv = np.minimum(np.maximum(0, (np.arange(T) - W + 1) // block), T // block)
+        per_row = 2.0 * D * nv + 4.0 * D * block * np.minimum(nv, n_select)
+        flops = float(per_row.sum()) * w["B"] * w["Hq"]
+        p_ = swa.prefill_params(q, k, W, block, T, 0.0)
+        import ctypes as _ct
+        ws = torch.empty(swa.lib().swa_nsa_select_workspace_size(_ct.byref(p_)), dtype=torch.uint8, device=dev)
+
+        def launch(i):
+            swa.nsa_select(q, k, v, W, block, n_select, rope=rope, workspace=ws)
+        p = Part(name, launch, 1, flops, 0.0, kernel="nsa_select_kernel")
+        p.extra = dict(B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], T=T, D=D, window=W, block=block, n_select=n_select)
+        return p
+
     t_setup = time.time()
     if "needle" in parts_wanted:
         parts["needle"] = make_prefill("needle", workloads.needle())
@@ -374,6 +395,8 @@ def main():
     for b in (1, 8, 32):
         if f"decode_b{b}" in parts_wanted:
             parts[f"decode_b{b}"] = make_decode(f"decode_b{b}", B=b)
+    if "nsa" in parts_wanted:
+        parts["nsa"] = make_nsa("nsa")
     if "backward" in parts_wanted:
         parts["backward"] = make_backward("backward")
     if "chunk" in parts_wanted:
@@ -509,6 +532,10 @@ def main():
                      "frac_fp32_peak": round(results.get("backward", {}).get("tflops", 0.0) / FP32_PEAK_TFLOPS, 5),
                      "us_per_call": round(results.get("backward", {}).get("ms", 0.0) * 1e3, 2),
                      "config": "needle prefill backward, bf16 inputs, fp32 vector arithmetic"},
+        "nsa_selection": {"value": round(results.get("nsa", {}).get("tflops", 0.0), 3), "unit": "TFLOP/s",
+                          "frac_fp32_peak": round(results.get("nsa", {}).get("tflops", 0.0) / FP32_PEAK_TFLOPS, 5),
+                          "us_per_call": round(results.get("nsa", {}).get("ms", 0.0) * 1e3, 2),
+                          "config": "compressed config, b=4, 16 selected blocks, fp32 vector arithmetic"},
         "chunked_prefill": {"value": round(results.get("chunk", {}).get("tflops", 0.0), 3), "unit": "TFLOP/s",
                             "frac_mfma_peak": round(results.get("chunk", {}).get("frac_mfma_peak", 0.0), 5),
                             "us_per_call": round(results.get("chunk", {}).get("ms", 0.0) * 1e3, 2)},

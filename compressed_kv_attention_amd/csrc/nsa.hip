@@ -15,7 +15,7 @@
 //
 // Everything is fp32.  A preparation pass rotates the exact keys and forms the
 // pooled keys; the main kernel gives each query row a lane: the row's rotated
-// q in registers, a streaming top-32 of the scores of the candidate blocks
+// q in registers, a streaming top-k (8, 16 or 32 kept) of the scores of the candidate blocks
 // (staged through LDS 32 blocks at a time), then attention over the chosen
 // blocks' tokens, read straight from the fp32 key and value rows.
 #include "swa_common.h"
@@ -24,7 +24,6 @@
 namespace swa {
 namespace {
 
-constexpr int kTopK = 32;  // kept candidates per row (n_select <= kTopK)
 constexpr int NT = 32;     // pooled keys per staged tile
 
 template <class X>
@@ -76,7 +75,8 @@ __global__ __launch_bounds__(64) void nsa_prep_pooled_kernel(NsaArgs a, float* p
     if (lane < D) pk32[(((size_t)b * a.Hkv + h) * a.nblk + j) * D + d] = x;
 }
 
-template <class X, int D>
+// kTopK candidates are kept per row: 8, 16 or 32, the smallest that holds n_select.
+template <class X, int D, int kTopK>
 __global__ __launch_bounds__(64) void nsa_select_kernel(NsaArgs a, const float* k32, const float* v32,
                                                         const float* pk32) {
     __shared__ float tile[NT][D];
@@ -215,8 +215,17 @@ hipError_t launch_nsa_t(const NsaArgs& a, float* k32, float* v32, float* pk32, h
         hipLaunchKernelGGL(nsa_prep_pooled_kernel<X>, dim3((unsigned)a.nblk, (unsigned)a.Hkv, (unsigned)a.B), blk, 0,
                            s, a, pk32);
     const dim3 grid((unsigned)((a.T + 63) / 64), (unsigned)a.Hq, (unsigned)a.B);
-    if (a.D == 64) hipLaunchKernelGGL((nsa_select_kernel<X, 64>), grid, blk, 0, s, a, k32, v32, pk32);
-    else hipLaunchKernelGGL((nsa_select_kernel<X, 32>), grid, blk, 0, s, a, k32, v32, pk32);
+#define SWA_NSA(DD, KK) hipLaunchKernelGGL((nsa_select_kernel<X, DD, KK>), grid, blk, 0, s, a, k32, v32, pk32)
+    if (a.D == 64) {
+        if (a.n_select <= 8) SWA_NSA(64, 8);
+        else if (a.n_select <= 16) SWA_NSA(64, 16);
+        else SWA_NSA(64, 32);
+    } else {
+        if (a.n_select <= 8) SWA_NSA(32, 8);
+        else if (a.n_select <= 16) SWA_NSA(32, 16);
+        else SWA_NSA(32, 32);
+    }
+#undef SWA_NSA
     return hipGetLastError();
 }
 
