@@ -543,6 +543,10 @@ def main():
                    "frac_mfma_peak": round(results.get("packed", {}).get("frac_mfma_peak", 0.0), 5),
                    "us_per_call": round(results.get("packed", {}).get("ms", 0.0) * 1e3, 2),
                    "traffic": measured_traffic("prefill_packed_call", PREFILL_SOURCES)},
+        "compressed4": {"value": round(results.get("compressed4", {}).get("tflops", 0.0), 3), "unit": "TFLOP/s",
+                        "frac_mfma_peak": round(results.get("compressed4", {}).get("frac_mfma_peak", 0.0), 5),
+                        "us_per_call": round(results.get("compressed4", {}).get("ms", 0.0) * 1e3, 2),
+                        "traffic": measured_traffic("prefill_compressed4_call", PREFILL_SOURCES)},
         "parts": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                   for k, v in results.items()},
         # The dominant kernel of the step by GPU time is the decode kernel (12 launches per step); one
