@@ -638,8 +638,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
                 for (int c = 0; c < D / 16; ++c) kr[c] = lds_load128(k_addr[c] + st * SUB * D * 2);
                 // sacc = u - base (visible pairs) or -inf
-                f32x16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0],
-                                                                      splat ? nbase : make_bias(), 0, 0, 0);
+                f32x16 sacc;
+                if (splat)
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0], nbase, 0, 0,
+                                                                   0);
+                else
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[0]), qf[0], make_bias(),
+                                                                   0, 0, 0);
 #pragma unroll
                 for (int c = 1; c < D / 16; ++c)
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc, 0, 0,
