@@ -206,6 +206,15 @@ __device__ __forceinline__ void issue_rope_rows(const PrefillArgs& a, SmemBf16<D
     }
 }
 
+__device__ __forceinline__ void lds_store64(uint32_t addr, u32x2 v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    *__builtin_bit_cast(__attribute__((address_space(3))) u32x2*, addr) = v;
+#else
+    (void)addr;
+    (void)v;
+#endif
+}
+
 __device__ __forceinline__ void unpack8(const uint4& x, float* f) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -758,20 +767,39 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         return;
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    if (row_ok) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* orow = (uint16_t*)a.out + (((size_t)b * a.Hq + my_h) * T + my_q) * D;
+    // The output block of the wave (32 rows x D) goes through LDS (the wave's
+    // own 64 D bytes of the K buffers, free after the walk) so that it reaches
+    // global memory in whole rows: each store instruction then writes
+    // 64 x 16 contiguous bytes (1024 / 2D rows) instead of 16 bytes of each of
+    // 32 rows.  In LDS, rows are row-major with their 16-byte chunks XOR-swizzled
+    // by the row, so both the writes (a lane per row) and the reads (a row per
+    // group of D / 8 lanes) spread over the banks.
+    {
+        constexpr int CPR = D / 8;  // 16-byte chunks per row
+        const float inv = (row_ok && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+        const uint32_t ob = lds_off(&sm.k[0][0]) + (uint32_t)wave * 32u * D * 2u;
 #pragma unroll
         for (int n = 0; n < D / 32; ++n) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int d = 32 * n + 8 * i + 4 * h;
-                uint2 w;
-                w.x = cvt_pk_bf16(o[n][4 * i] * inv, o[n][4 * i + 1] * inv);
-                w.y = cvt_pk_bf16(o[n][4 * i + 2] * inv, o[n][4 * i + 3] * inv);
-                *(uint2*)(orow + d) = w;
+                const int c = 4 * n + i;  // chunk of channels 32n + 8i .. +7; this lane has +4h .. +3
+                u32x2 w;
+                w[0] = cvt_pk_bf16(o[n][4 * i] * inv, o[n][4 * i + 1] * inv);
+                w[1] = cvt_pk_bf16(o[n][4 * i + 2] * inv, o[n][4 * i + 3] * inv);
+                lds_store64(ob + (uint32_t)(lq * CPR + (c ^ (lq % CPR))) * 16u + 8u * h, w);
             }
         }
+        lds_reads_done();  // (also the writes: the LDS wait covers both)
+        constexpr int RPI = 64 / CPR;  // rows per store instruction
+        uint16_t* ohead = (uint16_t*)a.out + ((size_t)b * a.Hq + my_h) * T * D;
+#pragma unroll
+        for (int j = 0; j < 32 / RPI; ++j) {
+            const int r = j * RPI + lane / CPR, c = lane % CPR;
+            const u32x4 x = lds_load128(ob + (uint32_t)(r * CPR + (c ^ (r % CPR))) * 16u);
+            if (r0 + r < T) *(u32x4*)(ohead + (size_t)(r0 + r) * D + 8 * c) = x;
+        }
+    }
+    if (row_ok) {
         // lse = base / log2 e + ln(l) (base is in log2 units of the scaled scores)
         if (a.lse && h == 0)
             a.lse[((size_t)b * a.Hq + my_h) * T + my_q] = l_tot > 0.f ? base * 0.6931471805599453f + __logf(l_tot)
