@@ -356,8 +356,30 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     if (tab_lds) issue_rope_rows<D>(a, sm, q0, wave, lane);
     SWA_TRACE(6);
 
+    // q.  Without the table rows in LDS, the wave's 32 rows come by direct
+    // loads into its quarter of K/V buffer 1 (free until the walk's second
+    // tile): whole rows per instruction, the 16-byte chunks of row r stored
+    // XOR-swizzled by r so that the operand reads below (a row per lane) spread
+    // over the banks.  With the table rows there, each lane reads its own.
+    constexpr int QCPR = D / 8;       // 16-byte chunks per q row
+    constexpr int QRPI = 64 / QCPR;   // q rows per direct-load instruction
+    const bool q_lds = !DUMP && !tab_lds;
+    const uint32_t q_lds_base =
+        lds_off(wave < 2 ? &sm.k[1][0] : &sm.v[1][0]) + (uint32_t)(wave & 1) * 32u * D * 2u;
     uint4 raw[D / 16];
-    {
+    if (q_lds) {
+        if (wave_active) {
+            const void* qbase = (const uint16_t*)a.q + (((size_t)b * a.Hq + my_h) * T + r0) * D;
+#pragma unroll
+            for (int i = 0; i < 32 / QRPI; ++i) {
+                const int r = i * QRPI + lane / QCPR, pc = lane % QCPR;
+                const int rr = min(r, T - 1 - r0);  // rows past the end repeat the last row
+                dma16(qbase, (uint32_t)(rr * D * 2 + (pc ^ (r % QCPR)) * 16), q_lds_base + 1024u * i);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) raw[c] = make_uint4(0, 0, 0, 0);
+    } else {
         const uint16_t* qrow = (const uint16_t*)a.q + (((size_t)b * a.Hq + my_h) * T + (row_ok ? my_q : 0)) * D;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
@@ -392,10 +414,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         if (lane < n_sink_tiles) tsk = *(const int2*)(a.tsink + ((size_t)b * a.ntile + lane) * 2);
     }
 
-    if (ROPE && !tab_lds && row_ok) {
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) rotate8(raw[c], raw[c + D / 32], rc[c][0], rc[c][1], rsn[c][0], rsn[c][1], c_log2);
-    }
 
     SWA_TRACE(7);
     const bool row_vis = row_ok && (!plain || seg_q > 0);  // padding rows see nothing
@@ -446,6 +464,24 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 
     // tile 0 (and the staged table rows) must have landed
     wait_all_barrier();
+    if (q_lds) {
+        // the wave's q rows (row lq, chunks 2c + h), then the K/V buffer 1 is
+        // free again once every wave has read its rows
+        if (wave_active && row_ok) {
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c)
+                raw[c] = __builtin_bit_cast(
+                    uint4, lds_load128(q_lds_base + (uint32_t)(lq * QCPR + ((2 * c + h) ^ (lq % QCPR))) * 16u));
+            if (ROPE) {
+#pragma unroll
+                for (int c = 0; c < D / 32; ++c)
+                    rotate8(raw[c], raw[c + D / 32], rc[c][0], rc[c][1], rsn[c][0], rsn[c][1], c_log2);
+            }
+        }
+        lds_reads_done();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
     if (tab_lds) {
         const uint32_t tab = lds_off(&sm.v[1][0]);
 #pragma unroll
