@@ -206,6 +206,14 @@ __device__ __forceinline__ void issue_rope_rows(const PrefillArgs& a, SmemBf16<D
     }
 }
 
+__device__ __forceinline__ int lds_load32(uint32_t addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return *__builtin_bit_cast(__attribute__((address_space(3))) const int*, addr);
+#else
+    (void)addr;
+    return 0;
+#endif
+}
 __device__ __forceinline__ void lds_store64(uint32_t addr, u32x2 v) {
 #if defined(__HIP_DEVICE_COMPILE__)
     *__builtin_bit_cast(__attribute__((address_space(3))) u32x2*, addr) = v;
@@ -423,6 +431,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     rs.r1 = min(r0 + 31, T - 1);
     rs.smin = __builtin_amdgcn_readfirstlane(wave_min_i32(row_ok ? seg_q : 0x7fffffff));
     rs.smax = __builtin_amdgcn_readfirstlane(wave_max_i32(row_ok ? seg_q : (int)0x80000000));
+    // every row of the wave lies in segment rs.smin or rs.smax (or is padding)
+    const bool two_seg =
+        __builtin_amdgcn_ballot_w64(row_ok && seg_q > 0 && seg_q != rs.smin && seg_q != rs.smax) == 0;
 
     if (scan) {
         const int lo = max(1, wave_min_i32(min(rseg0, rseg1)));
@@ -535,10 +546,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     int buf_step = (int)kTileBytes;
     const uint32_t info_lds = lds_off(&sm.kinfo[0][0]);
     // Fast classification of exact sub-tiles: a sub-tile starting at key k0
-    // is FULL for this wave when fpos_lo <= k0 <= fpos_hi (every pair causal
-    // and inside the window) and its keys are sink-free and all in the
-    // segment every row of the wave belongs to (fast_seg; -2 when the rows
-    // are not all in one real segment).
+    // is FULL for this wave when its keys all lie in the segment every row of
+    // the wave belongs to (fast_seg; -2 when the rows are not all in one real
+    // segment) and either fpos_lo <= k0 <= fpos_hi (every pair causal and
+    // inside the window) or every key is a sink and k0 <= fpos_hi (every pair
+    // causal; sinks stay visible at any distance).
     const int fpos_lo = a.window != 0 ? max(rs.r1 - a.window + 1, 0) : 0;
     const int fpos_hi = rs.r0 - (SUB - 1);
     const int fast_seg = !plain ? 1 : (rs.smin == rs.smax && rs.smin > 0 ? rs.smin : -2);
@@ -590,8 +602,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 if (pooled) {
                     cls = classify_pooled(rs, k0, SUB, a.window, a.block, a.nblk);
                     splat = cls == TILE_FULL;
-                } else if (fpos_any && (unsigned)(k0 - fpos_lo) <= (unsigned)(fpos_hi - fpos_lo) &&
-                           (!plain || (ks.smin == ks.smax && ks.any_sink == 0 && ks.smin == fast_seg))) {
+                } else if ((!plain || (ks.smin == ks.smax && ks.smin == fast_seg)) &&
+                           ((fpos_any && (unsigned)(k0 - fpos_lo) <= (unsigned)(fpos_hi - fpos_lo)) ||
+                            (plain && ks.all_sink != 0 && k0 <= fpos_hi))) {
                     cls = TILE_FULL;
                     splat = true;
                 } else {
@@ -644,6 +657,37 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
                         for (int j = 0; j < 16; ++j)
                             bias[j] = (8 * (j >> 2) + (j & 3)) < lim ? __uint_as_float(nb) : kNegInf;
+                    } else if (!plain) {
+                        // (unreachable: exact keys of the compressed variant are
+                        // never PARTIAL, having neither segments nor sinks)
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) bias[j] = kNegInf;
+                    } else if (two_seg) {
+                        // The wave's rows lie in at most two segments (rs.smin,
+                        // rs.smax): a ballot over the sub-tile's 32 key infos
+                        // gives the keys of each segment and the sink keys as
+                        // bit masks over key offsets; the row then takes
+                        // (its segment) & ((causal & in window) | (causal & sink)).
+                        const int kinf = lds_load32(info_lds + (uint32_t)(cur * BN + st * SUB + lq) * 4u);
+                        const int kseg = kinf & 0x7fffffff;
+                        const uint32_t m_lo = (uint32_t)__builtin_amdgcn_ballot_w64(kseg == rs.smin);
+                        const uint32_t m_hi = (uint32_t)__builtin_amdgcn_ballot_w64(kseg == rs.smax);
+                        const uint32_t m_sink = (uint32_t)__builtin_amdgcn_ballot_w64(kinf < 0);
+                        const uint32_t m_seg = seg_q == rs.smin ? m_lo : m_hi;
+                        // offsets relative to kb = k0 + 4h; causal: off <= d0,
+                        // window: off >= d0 + 1 - wlim (bounds past 2^20 act as none)
+                        const int d0 = my_q - kb;
+                        const int hi = min(d0, 31);
+                        const int lo = max(d0 + 1 - (int)min(wlim, 1u << 20), 0);
+                        const uint32_t causal = hi < 0 ? 0u : (hi == 31 ? 0xffffffffu : (2u << hi) - 1u);
+                        const uint32_t recent = lo > 31 ? 0u : causal & ~((1u << lo) - 1u);
+                        uint32_t vis = (m_seg >> (4 * h)) & (recent | ((m_sink >> (4 * h)) & causal));
+                        vis = row_vis ? vis : 0u;
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)vis, 8 * (j >> 2) + (j & 3), 1);
+                            bias[j] = __uint_as_float((m & nb) | (~m & 0xff800000u));
+                        }
                     } else {
                         const int d0 = my_q - kb;
                         u32x4 inf[4];
@@ -665,8 +709,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 if constexpr (DUMP) {
                     // the pairs this sub-tile lets through for this row: its
                     // mask, where the lane gate lets the row take weight at all
-                    if (!gate_st[st]) continue;
+                    // (the mask is formed by every lane: it may take ballots)
                     const f32x16 bias = splat ? nbase : make_bias();
+                    if (!gate_st[st]) continue;
                     uint8_t* mrow = dump_writer ? dump.mask + ((size_t)b * T + my_q) * Tk : nullptr;
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
