@@ -602,11 +602,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 if (pooled) {
                     cls = classify_pooled(rs, k0, SUB, a.window, a.block, a.nblk);
                     splat = cls == TILE_FULL;
-                } else if ((!plain || (ks.smin == ks.smax && ks.smin == fast_seg)) &&
+                } else if ((!plain || (ks.smin == ks.smax && ks.smin > 0 &&
+                                       (ks.smin == fast_seg || (two_seg && (ks.smin == rs.smin || ks.smin == rs.smax))))) &&
                            ((fpos_any && (unsigned)(k0 - fpos_lo) <= (unsigned)(fpos_hi - fpos_lo)) ||
                             (plain && ks.all_sink != 0 && k0 <= fpos_hi))) {
+                    // (rows of a two-segment wave that are not in the keys'
+                    // segment are left out by the lane gate)
                     cls = TILE_FULL;
-                    splat = true;
+                    splat = !plain || ks.smin == fast_seg;
                 } else {
                     cls = classify_exact(rs, ks, k0, SUB, nkeys, a.window, plain, wl);
                 }
@@ -630,15 +633,19 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 auto make_bias = [&]() {
                     const uint32_t nb = __float_as_uint(-base);
                     f32x16 bias;
-                    if (cls == TILE_PARTIAL_POS || cls == TILE_FULL) {
+                    if (cls == TILE_FULL) {
+                        // every pair of the sub-tile, for the rows the lane gate lets through
+                        const float v = gate ? __uint_as_float(nb) : kNegInf;
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) bias[j] = v;
+                    } else if (cls == TILE_PARTIAL_POS) {
                         // Element j is visible iff its key offset off(j) lies in
-                        // [d0 - wl + 1, d0] (all 32 offsets for FULL): a mask over
-                        // offsets 0..31, then one bit extract and one bit select
-                        // per element.
+                        // [d0 - wl + 1, d0]: a mask over offsets 0..31, then one
+                        // bit extract and one bit select per element.
                         const int d0 = my_q - kb;
                         // (bounds past 2^20 act as no bound: |d0| stays far below it)
-                        const int lo = cls == TILE_FULL ? 0 : max(d0 + 1 - (int)min(wl, 1u << 20), 0);
-                        const int hi = cls == TILE_FULL ? 31 : min(d0, 31);
+                        const int lo = max(d0 + 1 - (int)min(wl, 1u << 20), 0);
+                        const int hi = min(d0, 31);
                         uint32_t vis = 0u;
                         if (hi >= lo && gate) vis = (hi == 31 ? 0xffffffffu : (2u << hi) - 1u) & ~((1u << lo) - 1u);
 #pragma unroll
