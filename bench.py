@@ -175,9 +175,7 @@ def main():
         n = max(2, min(16, ROTATE_BYTES // per_copy + 1))
         bufs = []
         for _ in range(n):
-            kk, vv = k.clone(), v.clone()
-            pk, pv = swa.pool_compress_rope(kk, vv, block, rope)
-            bufs.append((q.clone(), kk, vv, torch.empty_like(q), pk, pv))
+            bufs.append((q.clone(), k.clone(), v.clone(), torch.empty_like(q)))
         ws = swa.prefill_workspace(q, k, w["window"], rope, block)
         _, count = swa.debug_visibility(w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["window"], torch.bfloat16,
                                         compress_block=block, want_mask=False)
@@ -186,12 +184,11 @@ def main():
         nb = w["T"] // block
         bytes_ = q.numel() * 2 * 2 + k.numel() * 2 * 2 + 2 * (w["B"] * w["Hkv"] * nb * w["D"] * 2) * 2
 
-        # pooled_k/pooled_v of the step are produced inside the step (pool then attend)
+        # the step pools k and v and attends: one call, given no pooled inputs (its pre-pass rotates the exact
+        # keys and forms the rotated pooled keys and the pooled values in one read of k and v)
         def launch_step(i):
-            qq, kk, vv, oo, pk, pv = bufs[i % n]
-            swa.pool_compress_rope(kk, vv, block, rope, out=(pk, pv))
-            swa.prefill(qq, kk, vv, window=w["window"], rope=rope, pooled_k=pk, pooled_v=pv, compress_block=block,
-                        out=oo, workspace=ws)
+            qq, kk, vv, oo = bufs[i % n]
+            swa.prefill(qq, kk, vv, window=w["window"], rope=rope, compress_block=block, out=oo, workspace=ws)
         p = Part(name, launch_step, n, flops, bytes_, kernel="prefill_bf16_kernel")
         p.extra = dict(B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], T=w["T"], D=w["D"], window=w["window"], block=block,
                        visible_pairs_per_head=nvis)

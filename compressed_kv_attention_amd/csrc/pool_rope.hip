@@ -310,6 +310,101 @@ __device__ __forceinline__ void rope_chunk_bf16(long long row, int t, int i0, in
     *(uint4*)(y + base + half + i0) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
 }
 
+// Fused pre-pass of a compressed bf16 prefill with RoPE: one read of the
+// exact keys and values.  A workgroup takes a span of whole blocks of one
+// (batch row, kv head); each thread rotates one 8-pair chunk of one key row
+// into the rotated-key buffer (the arithmetic of rope_chunk_bf16) and leaves
+// that row's pre-RoPE key and value chunks in LDS as loaded; the block means
+// are then summed in fp32 from LDS row by row in order (the arithmetic of
+// pool_rope_vec_kernel), and each key mean is rotated at its block midpoint.
+template <int D>
+__global__ __launch_bounds__(256) void pool_rotate_bf16_kernel(PoolRotArgs p) {
+    constexpr int P = D / 16;    // 8-pair chunks per row
+    constexpr int R = 256 / P;   // rows a workgroup can hold
+    constexpr int LD = D + 8;    // LDS row stride in bf16 (padded against bank conflicts)
+    constexpr int half = D / 2;
+    __shared__ __align__(16) uint16_t sk[R * LD];  // pre-RoPE keys and values, as loaded
+    __shared__ __align__(16) uint16_t sv[R * LD];
+    const int n = blockIdx.y;  // (batch row, kv head)
+    const int r0 = blockIdx.x * p.span;
+    const int tid = threadIdx.x, rl = tid / P, i0 = 8 * (tid % P);
+    const int row = r0 + rl;
+    if (rl < p.span && row < p.T) {
+        const size_t base = ((size_t)n * p.T + row) * D + i0;
+        const uint4 k1 = *(const uint4*)(p.k + base), k2 = *(const uint4*)(p.k + base + half);
+        const uint4 v1 = *(const uint4*)(p.v + base), v2 = *(const uint4*)(p.v + base + half);
+        const float4 c0 = *(const float4*)(p.cs + (size_t)row * half + i0);
+        const float4 c1 = *(const float4*)(p.cs + (size_t)row * half + i0 + 4);
+        const float4 s0 = *(const float4*)(p.sn + (size_t)row * half + i0);
+        const float4 s1 = *(const float4*)(p.sn + (size_t)row * half + i0 + 4);
+        *(uint4*)(sk + rl * LD + i0) = k1;
+        *(uint4*)(sk + rl * LD + half + i0) = k2;
+        *(uint4*)(sv + rl * LD + i0) = v1;
+        *(uint4*)(sv + rl * LD + half + i0) = v2;
+        const uint32_t a[4] = {k1.x, k1.y, k1.z, k1.w}, bb[4] = {k2.x, k2.y, k2.z, k2.w};
+        const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        uint32_t o1[4], o2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x1l = __uint_as_float(a[i] << 16), x1h = __uint_as_float(a[i] & 0xffff0000u);
+            const float x2l = __uint_as_float(bb[i] << 16), x2h = __uint_as_float(bb[i] & 0xffff0000u);
+            const float cl = c[2 * i], ch = c[2 * i + 1], sl = sn[2 * i], sh = sn[2 * i + 1];
+            o1[i] = f32_to_bf16_bits(x1l * cl - x2l * sl) | (f32_to_bf16_bits(x1h * ch - x2h * sh) << 16);
+            o2[i] = f32_to_bf16_bits(x2l * cl + x1l * sl) | (f32_to_bf16_bits(x2h * ch + x1h * sh) << 16);
+        }
+        *(uint4*)(p.kr + base) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+        *(uint4*)(p.kr + base + half) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+    }
+    __syncthreads();
+    // the span's blocks: one item per (block, tensor, chunk)
+    const int nb = p.span / p.block;
+    const int j0 = r0 / p.block;
+    for (int item = tid; item < nb * 2 * P; item += 256) {
+        const int jl = item / (2 * P), rest = item - jl * 2 * P;
+        const bool is_v = rest >= P;
+        const int q0 = 8 * (rest - (is_v ? P : 0));
+        const int j = j0 + jl;
+        if (j >= p.nblk) continue;
+        const uint16_t* src = (is_v ? sv : sk) + jl * p.block * LD;
+        float x1[8], x2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x1[e] = x2[e] = 0.f;
+        for (int rr = 0; rr < p.block; ++rr) {
+            const uint4 u1 = *(const uint4*)(src + rr * LD + q0), u2 = *(const uint4*)(src + rr * LD + half + q0);
+            const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w}, w2[4] = {u2.x, u2.y, u2.z, u2.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x1[2 * i] += __uint_as_float(w1[i] << 16);
+                x1[2 * i + 1] += __uint_as_float(w1[i] & 0xffff0000u);
+                x2[2 * i] += __uint_as_float(w2[i] << 16);
+                x2[2 * i + 1] += __uint_as_float(w2[i] & 0xffff0000u);
+            }
+        }
+        scale_by_block(x1, 8, p.block, p.inv_b);
+        scale_by_block(x2, 8, p.block, p.inv_b);
+        if (!is_v) {
+            int mid = j * p.block + p.block / 2;
+            if (mid > p.rope_len - 1) mid = p.rope_len - 1;
+            const float* cr = p.cs + (size_t)mid * half + q0;
+            const float* sr = p.sn + (size_t)mid * half + q0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float cc = cr[e], ss = sr[e];
+                const float y1 = x1[e] * cc - x2[e] * ss;
+                const float y2 = x2[e] * cc + x1[e] * ss;
+                x1[e] = y1;
+                x2[e] = y2;
+            }
+        }
+        uint16_t* dst = (is_v ? p.pv : p.pk) + ((size_t)n * p.nblk + j) * D + q0;
+        *(uint4*)dst = make_uint4(pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]), pack_bf16x2(x1[4], x1[5]),
+                                  pack_bf16x2(x1[6], x1[7]));
+        *(uint4*)(dst + half) = make_uint4(pack_bf16x2(x2[0], x2[1]), pack_bf16x2(x2[2], x2[3]),
+                                          pack_bf16x2(x2[4], x2[5]), pack_bf16x2(x2[6], x2[7]));
+    }
+}
+
 // One launch for everything a bf16 prefill prepares before attention:
 //   the first blocks: key metadata, one wave per key tile of 64 keys --
 //     info[b][t]     packed segment | sink << 31 of every key
@@ -381,6 +476,18 @@ hipError_t launch_prefill_prep(const PrepArgs& p, hipStream_t s) {
     const long long blocks = p.rope_blocks + meta_blocks;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(prefill_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+bool pool_rotate_fits(int D, int block) { return (D == 32 || D == 64) && block >= 1 && block <= 256 / (D / 16); }
+
+hipError_t launch_pool_rotate_bf16(PoolRotArgs p, hipStream_t s) {
+    const int R = 256 / (p.D / 16);
+    p.span = p.block * (R / p.block);
+    p.inv_b = pow2_reciprocal(p.block);
+    const dim3 grid((unsigned)((p.T + p.span - 1) / p.span), (unsigned)p.N);
+    if (p.D == 64) hipLaunchKernelGGL(pool_rotate_bf16_kernel<64>, grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(pool_rotate_bf16_kernel<32>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -124,6 +124,13 @@ size_t rotated_key_bytes(const swa_prefill_params* p) {
     const size_t elem = p->dtype == SWA_BF16 ? 2 : 4;
     return round256((size_t)p->B * p->Hkv * p->T * p->D * elem);
 }
+// Compressed mode: room for one pooled tensor (keys or values), used when the
+// caller passes no pooled_k / pooled_v and the call pools them itself.
+size_t pooled_bytes(const swa_prefill_params* p) {
+    if (p->compress_block <= 0) return 0;
+    const size_t elem = p->dtype == SWA_BF16 ? 2 : 4;
+    return round256((size_t)p->B * p->Hkv * (size_t)(p->T / p->compress_block) * p->D * elem);
+}
 
 }  // namespace
 
@@ -135,7 +142,7 @@ int swa_version(void) { return 100; }
 
 size_t swa_prefill_workspace_size(const swa_prefill_params* p) {
     if (p == nullptr || p->B <= 0 || p->T <= 0 || p->Hkv <= 0 || p->D <= 0) return 0;
-    return key_meta_layout(p).total + rotated_key_bytes(p);
+    return key_meta_layout(p).total + rotated_key_bytes(p) + 2 * pooled_bytes(p);
 }
 
 int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, const void* v, const void* pooled_k,
@@ -151,7 +158,9 @@ int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, 
     REQUIRE_PTR(v);
     REQUIRE_PTR(out);
     OPTIONAL_PTR(lse);
-    if (p->compress_block > 0 && a.nblk > 0) {
+    // compressed mode without pooled inputs: the call pools k and v itself
+    const bool pool_here = p->compress_block > 0 && a.nblk > 0 && pooled_k == nullptr && pooled_v == nullptr;
+    if (p->compress_block > 0 && a.nblk > 0 && !pool_here) {
         REQUIRE_PTR(pooled_k);
         REQUIRE_PTR(pooled_v);
     }
@@ -178,6 +187,39 @@ int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, 
     char* ws = (char*)workspace;
     const MetaLayout meta = key_meta_layout(p);
     void* kr = p->rope_len > 0 ? ws + meta.total : nullptr;  // rotated keys
+    bool rotated = false;  // the exact keys are already in kr
+    if (pool_here) {
+        char* pk = ws + meta.total + rotated_key_bytes(p);
+        char* pv = pk + pooled_bytes(p);
+        a.pk = pk;
+        a.pv = pv;
+        hipError_t e;
+        if (p->dtype == SWA_BF16 && kr != nullptr && swa::pool_rotate_fits(p->D, p->compress_block) &&
+            (long long)p->B * p->Hkv <= 65535) {
+            // one pass: rotated exact keys and the pooled keys and values
+            swa::PoolRotArgs pr{};
+            pr.N = p->B * p->Hkv;
+            pr.T = p->T;
+            pr.D = p->D;
+            pr.block = p->compress_block;
+            pr.nblk = a.nblk;
+            pr.rope_len = p->rope_len;
+            pr.k = (const uint16_t*)k;
+            pr.v = (const uint16_t*)v;
+            pr.cs = rope_cos;
+            pr.sn = rope_sin;
+            pr.kr = (uint16_t*)kr;
+            pr.pk = (uint16_t*)pk;
+            pr.pv = (uint16_t*)pv;
+            e = swa::launch_pool_rotate_bf16(pr, s);
+            rotated = true;
+        } else {
+            e = swa::launch_pool_rope(p->B, p->Hkv, p->T, p->D, p->compress_block, p->dtype, k, v,
+                                      p->rope_len > 0 ? rope_cos : nullptr, p->rope_len > 0 ? rope_sin : nullptr,
+                                      p->rope_len, pk, pv, s);
+        }
+        if (e != hipSuccess) return hip_status(e, "swa_attn_prefill pooling launch");
+    }
     if (p->dtype == SWA_BF16) {
         swa::PrepArgs pa{};
         pa.B = p->B;
@@ -185,7 +227,7 @@ int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, 
         pa.D = p->D;
         pa.ntile = a.ntile;
         pa.div_T = swa::make_fastdiv((uint32_t)p->T);
-        if (kr) {  // rotate the exact keys once, into the workspace
+        if (kr && !rotated) {  // rotate the exact keys once, into the workspace
             pa.rope_rows = (long long)p->B * p->Hkv * p->T;
             pa.rope_blocks = (pa.rope_rows * (p->D / 16) + 255) / 256;
             pa.x = (const uint16_t*)k;
@@ -203,8 +245,10 @@ int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, 
             a.ksub = pa.ksub;
             a.tsink = pa.tsink;
         }
-        const hipError_t e = swa::launch_prefill_prep(pa, s);
-        if (e != hipSuccess) return hip_status(e, "swa_attn_prefill prep launch");
+        if (pa.rope_blocks > 0 || pa.info != nullptr) {
+            const hipError_t e = swa::launch_prefill_prep(pa, s);
+            if (e != hipSuccess) return hip_status(e, "swa_attn_prefill prep launch");
+        }
     } else if (kr) {
         const hipError_t e = swa::launch_rope_rows_f32((long long)p->B * p->Hkv * p->T, p->T, p->D, (const float*)k,
                                                        rope_cos, rope_sin, (float*)kr, s);

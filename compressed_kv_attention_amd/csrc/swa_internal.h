@@ -87,6 +87,23 @@ hipError_t launch_rope_table(double theta, int rope_len, int D, float* c, float*
 hipError_t launch_pool_rope(int B, int H, int T, int D, int block, int dtype, const void* k_pre,
                             const void* v, const float* c, const float* sn, int rope_len, void* pk,
                             void* pv, hipStream_t s);
+// The fused pre-pass of a compressed bf16 prefill with RoPE: rotated exact
+// keys and the pooled keys (rotated at their block midpoints) and values from
+// one read of k and v.  Blocks of up to 256 / (D / 16) rows (pool_rotate_fits).
+struct PoolRotArgs {
+    int N, T, D, block, nblk, rope_len;
+    int span;     // rows per workgroup (whole blocks; set by the launcher)
+    float inv_b;  // 1 / block when a power of two, else 0 (set by the launcher)
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* cs;
+    const float* sn;
+    uint16_t* kr;  // rotated keys [N, T, D]
+    uint16_t* pk;  // [N, nblk, D]
+    uint16_t* pv;
+};
+bool pool_rotate_fits(int D, int block);
+hipError_t launch_pool_rotate_bf16(PoolRotArgs p, hipStream_t s);
 // Arguments of the bf16 prep pass (key rotation and key metadata in one
 // launch); either part may be empty (rope_blocks == 0, or info == NULL).
 struct PrepArgs {

@@ -60,7 +60,10 @@ int swa_version(void);
 /* row t iff (j + 1) * b <= t - window + 1 and exact key s iff s <= t and     */
 /* t - s < window.  One softmax runs over both column sets.  pooled_k must   */
 /* already be rotated (kv_pool_compress_rope does that); seg_ids and prefix   */
-/* must be NULL and window >= 1.                                             */
+/* must be NULL and window >= 1.  With pooled_k and pooled_v both NULL the    */
+/* call pools k and v itself (the arithmetic of kv_pool_compress_rope, into   */
+/* the workspace): for bf16 with RoPE and b <= 256 / (D / 16), in the same    */
+/* pass over k that rotates the exact keys.                                  */
 /*                                                                           */
 /* RoPE: with rope_len > 0, q and the exact k are rotated at their row index */
 /* t with the tables from swa_rope_table (rotate-half pairing (i, i + D/2)):  */
@@ -73,10 +76,13 @@ int swa_version(void);
 /*                                                                           */
 /* Workspace (swa_prefill_workspace_size bytes, 256-byte aligned; required */
 /* whenever that size is > 0): pre-passes write into it (a) for bf16 plain   */
-/* mode, seg_ids and prefix packed to one int32 per key, B*T*4 bytes, and     */
-/* (b) with RoPE, the rotated keys, B*Hkv*T*D*sizeof(dtype) bytes; each part  */
-/* is rounded up to 256 bytes.  Its contents are scratch between calls; two  */
-/* calls that overlap in time need two workspaces.                           */
+/* mode, the key metadata: seg_ids and prefix packed to one int32 per key     */
+/* (B*T*4 bytes) and summaries of every 32-key sub-tile and 64-key tile       */
+/* (B*ceil(T/64)*40 bytes); (b) with RoPE, the rotated keys,                  */
+/* B*Hkv*T*D*sizeof(dtype) bytes; (c) in compressed mode, room for pooled     */
+/* keys and values, 2*B*Hkv*(T/b)*D*sizeof(dtype) bytes (used when the call   */
+/* pools); each part is rounded up to 256 bytes.  Its contents are scratch   */
+/* between calls; two calls that overlap in time need two workspaces.        */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     int B, Hq, Hkv, T, D; /* q, out: [B,Hq,T,D]; k, v: [B,Hkv,T,D]; Hq % Hkv == 0; D in {32, 64} */
@@ -92,7 +98,7 @@ size_t swa_prefill_workspace_size(const swa_prefill_params* p);
 
 int swa_attn_prefill(const swa_prefill_params* p,
                      const void* q, const void* k, const void* v,
-                     const void* pooled_k, const void* pooled_v, /* NULL unless compress_block > 0 */
+                     const void* pooled_k, const void* pooled_v, /* compressed mode; both NULL: pooled here */
                      const int32_t* seg_ids,                     /* [B,T] or NULL (all segment 1)  */
                      const uint8_t* prefix,                      /* [B,T] sink flags or NULL       */
                      const float* rope_cos, const float* rope_sin, /* [rope_len, D/2] or NULL      */

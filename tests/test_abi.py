@@ -73,8 +73,12 @@ def test_prefill_rejects_null_and_misaligned_pointers():
     assert rc == swa.SWA_ERR_INVALID and "must not be NULL" in msg
     rc, msg = _prefill(_p(), ptrs=FAKE + 2)
     assert rc == swa.SWA_ERR_INVALID and "aligned" in msg
-    rc, msg = _prefill(_p(compress_block=4), ptrs=FAKE)           # pooled tensors missing
+    rc, msg = _prefill(_p(compress_block=4), ptrs=FAKE, pk=FAKE)  # one pooled tensor only
+    assert rc == swa.SWA_ERR_INVALID and "pooled_v" in msg
+    rc, msg = _prefill(_p(compress_block=4), ptrs=FAKE, pv=FAKE)
     assert rc == swa.SWA_ERR_INVALID and "pooled_k" in msg
+    rc, msg = _prefill(_p(compress_block=4), ptrs=FAKE)           # none: pooled in the call, into the workspace
+    assert rc == swa.SWA_ERR_INVALID and "workspace" in msg
     rc, msg = _prefill(_p(compress_block=4), ptrs=FAKE, seg=FAKE)
     assert rc == swa.SWA_ERR_UNSUPPORTED and "seg_ids" in msg
     rc, msg = _prefill(_p(rope_len=64), ptrs=FAKE)                # tables missing
@@ -91,8 +95,12 @@ def test_prefill_rejects_null_and_misaligned_pointers():
     assert size(_p()) == 3 * 256                               # bf16 plain: key metadata only
     assert size(_p(T=65)) == 512 + 256 + 256
     assert size(_p(dtype=swa.SWA_F32)) == 0                    # the fp32 kernel reads seg/prefix itself
-    assert size(_p(compress_block=4)) == 0                     # no segments in compressed mode
-    assert size(_p(compress_block=4, rope_len=64)) == 1 * 2 * 64 * 64 * 2
+    # compressed mode: no key metadata; room for pooled keys and values [B,Hkv,T/b,D]
+    pooled = 2 * 1 * 2 * (64 // 4) * 64 * 2
+    assert size(_p(compress_block=4)) == pooled
+    assert size(_p(compress_block=4, rope_len=64)) == 1 * 2 * 64 * 64 * 2 + pooled
+    assert size(_p(compress_block=4, dtype=swa.SWA_F32)) == 2 * 1 * 2 * 16 * 64 * 4
+    assert size(_p(compress_block=100)) == 0                   # T/b = 0 pooled rows
     rc, msg = _prefill(_p(), ptrs=FAKE)                        # bf16 plain without workspace
     assert rc == swa.SWA_ERR_INVALID and "workspace" in msg
 

@@ -27,6 +27,16 @@ def run_compressed(w, q_override=None):
     return out, lse, pk, pv
 
 
+def run_pool_in_call(w):
+    """The compressed prefill with no pooled inputs: the call pools k and v itself."""
+    q, k, v = dev_input(w, "q"), dev_input(w, "k"), dev_input(w, "v")
+    rope = swa.rope_table(w["rope_theta"], w["T"], w["D"]) if w["rope_theta"] else None
+    out, lse = swa.prefill(q, k, v, window=w["window"], rope=rope, compress_block=w["compress_block"],
+                           return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
 def oracle_compressed(w, rows=None):
     return oracle.compressed_prefill(w["q"], w["k"], w["v"], w["window"], w["compress_block"],
                                      theta=w["rope_theta"], rope_len=w["T"], rows=rows)
@@ -121,6 +131,37 @@ def test_compressed_random_small(dtype, B, H, Hkv, T, W, b, seed, D=64):
     assert_lse_close(to_np(lse), ref_lse, dtype, "out")
 
 
+# dtype, B, Hq, Hkv, T, W, b, D: blocks that fit the fused pool-and-rotate pass
+# (b <= 64 at D = 64, b <= 128 at D = 32) and blocks that do not (separate
+# pooling pass), no RoPE, remainders T mod b, fp32 (separate passes).
+POOL_IN_CALL = [("bf16", 1, 4, 2, 300, 32, 4, 64, True), ("bf16", 2, 2, 2, 150, 16, 3, 64, True),
+                ("bf16", 1, 4, 2, 300, 32, 16, 64, True), ("bf16", 1, 2, 2, 257, 64, 1, 64, True),
+                ("bf16", 1, 2, 1, 333, 40, 7, 32, True), ("bf16", 1, 2, 2, 500, 64, 64, 64, True),
+                ("bf16", 1, 2, 2, 500, 64, 80, 64, True), ("bf16", 1, 2, 2, 600, 64, 128, 32, True),
+                ("bf16", 1, 2, 2, 203, 30, 5, 64, False), ("f32", 1, 2, 2, 150, 16, 4, 64, True),
+                ("bf16", 2, 8, 8, 1000, 256, 4, 64, True)]
+
+
+@pytest.mark.parametrize("dtype,B,H,Hkv,T,W,b,D,rope", POOL_IN_CALL,
+                         ids=[f"{c[0]}-T{c[4]}-b{c[6]}-D{c[7]}{'' if c[8] else '-norope'}" for c in POOL_IN_CALL])
+def test_compressed_pools_in_call(dtype, B, H, Hkv, T, W, b, D, rope):
+    """pooled_k = pooled_v = NULL: the call pools k and v itself.  Against the
+    oracle, and against the call with pooled inputs from kv_pool_compress_rope:
+    the same bits wherever both pool with the same summation order (fp32, or
+    blocks below 8, whose pooling kernel adds rows one after another like the
+    fused pass; blocks too long for the fused pass use that very kernel)."""
+    w = workloads.prefill_case(B, H, Hkv, T, D, W, dtype, seed=900 + b, rope_theta=10000.0 if rope else 0.0,
+                               compress_block=b)
+    out, lse = run_pool_in_call(w)
+    ref, ref_lse = oracle_compressed(w)
+    assert_close(to_np(out), ref, dtype, "out (pooled in the call)")
+    assert_lse_close(to_np(lse), ref_lse, dtype, "lse (pooled in the call)")
+    out2, lse2, _, _ = run_compressed(w)
+    fused = dtype == "bf16" and rope and b <= 256 // (D // 16)
+    if dtype == "f32" or not fused or b < 8:
+        assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
 @pytest.mark.parametrize("T,W,b", [(200, 16, 4), (333, 64, 16), (129, 8, 3), (4096, 256, 4), (4096, 256, 16)])
 def test_compressed_visibility_bit_exact(T, W, b):
     """Both kernels' masks bit for bit against the oracle's compressed mask; the
@@ -145,6 +186,10 @@ def test_compressed_full_size(dtype, block):
     ref, ref_lse = oracle_compressed(w)
     assert_close(to_np(out), ref, dtype, f"b={block}, every row")
     assert_lse_close(lse.cpu().numpy(), ref_lse, dtype, f"b={block}, every row")
+    # the same call pooling k and v itself (the fused pre-pass for bf16)
+    out_h, lse_h = run_pool_in_call(w)
+    assert_close(to_np(out_h), ref, dtype, f"b={block}, pooled in the call, every row")
+    assert_lse_close(lse_h.cpu().numpy(), ref_lse, dtype, f"b={block}, pooled in the call, every row")
     # the last row reads the pooled blocks that cleared the window plus W exact keys
     q0 = torch.zeros_like(dev_input(w, "q"))
     _, lse0, _, _ = run_compressed(w, q_override=q0)
