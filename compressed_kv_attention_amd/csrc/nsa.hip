@@ -24,7 +24,6 @@
 namespace swa {
 namespace {
 
-constexpr int NT = 32;     // pooled keys per staged tile
 
 template <class X>
 __device__ __forceinline__ float ld_f(const X* p, size_t i);
@@ -33,25 +32,69 @@ __device__ __forceinline__ float ld_f<float>(const float* p, size_t i) { return 
 template <>
 __device__ __forceinline__ float ld_f<uint16_t>(const uint16_t* p, size_t i) { return bf16_bits_to_f32(p[i]); }
 
-// Exact keys (rotated at their position) and values in fp32: one row per
-// 64-lane block, lane d < D holds channel d.
+__device__ __forceinline__ void lds_store64(uint32_t addr, u32x2 v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    *__builtin_bit_cast(__attribute__((address_space(3))) u32x2*, addr) = v;
+#else
+    (void)addr;
+    (void)v;
+#endif
+}
+
 template <class X>
-__global__ __launch_bounds__(64) void nsa_prep_rows_kernel(NsaArgs a, float* k32, float* v32) {
-    const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x, D = a.D, d = lane % D;
-    const size_t row = ((size_t)b * a.Hkv + h) * a.T + t;
-    float x = ld_f((const X*)a.k, row * D + d);
-    const float vv = ld_f((const X*)a.v, row * D + d);
-    if (a.rope_cos) {
-        const float other = __shfl_xor(x, D / 2, 64);
-        const int i = d % (D / 2);
-        const int p = min(t, a.rope_len - 1);
-        const float c = a.rope_cos[(size_t)p * (D / 2) + i], s = a.rope_sin[(size_t)p * (D / 2) + i];
-        x = d < D / 2 ? x * c - other * s : x * c + other * s;
+__device__ __forceinline__ void st_x(X* p, float v);
+template <>
+__device__ __forceinline__ void st_x<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void st_x<uint16_t>(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
+
+// Exact keys rotated at their position, in the input dtype (bf16 keys are
+// rounded once after the fp32 rotation, as the key pre-pass of a prefill
+// does): one thread per (row, 8 channel pairs).
+template <class X>
+__global__ __launch_bounds__(256) void nsa_rotate_keys_kernel(NsaArgs a, X* kr) {
+    const int D = a.D, half = D / 2, per_row = half / 8;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long rows = (long long)a.B * a.Hkv * a.T;
+    if (idx >= rows * per_row) return;
+    const long long row = idx / per_row;
+    const int i0 = (int)(idx - row * per_row) * 8;
+    const int t = (int)(row % a.T);
+    const int p = min(t, a.rope_len - 1);
+    const X* src = (const X*)a.k + row * D;
+    X* dst = kr + row * D;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x1 = ld_f(src, i0 + e), x2 = ld_f(src, half + i0 + e);
+        const float c = a.rope_cos[(size_t)p * half + i0 + e], sn = a.rope_sin[(size_t)p * half + i0 + e];
+        st_x(dst + i0 + e, x1 * c - x2 * sn);
+        st_x(dst + half + i0 + e, x2 * c + x1 * sn);
     }
-    if (lane < D) {
-        k32[row * D + d] = x;
-        v32[row * D + d] = vv;
+}
+
+// Half a row (channels [0, H) from p) in fp32.
+template <int H>
+__device__ __forceinline__ void load_half(const float* p, float (&x)[H]) {
+#pragma unroll
+    for (int i = 0; i < H / 4; ++i) {
+        const float4 v = ((const float4*)p)[i];
+        x[4 * i] = v.x;
+        x[4 * i + 1] = v.y;
+        x[4 * i + 2] = v.z;
+        x[4 * i + 3] = v.w;
+    }
+}
+template <int H>
+__device__ __forceinline__ void load_half(const uint16_t* p, float (&x)[H]) {
+#pragma unroll
+    for (int i = 0; i < H / 8; ++i) {
+        const uint4 v = ((const uint4*)p)[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[8 * i + 2 * e] = __uint_as_float(w[e] << 16);
+            x[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
     }
 }
 
@@ -75,29 +118,74 @@ __global__ __launch_bounds__(64) void nsa_prep_pooled_kernel(NsaArgs a, float* p
     if (lane < D) pk32[(((size_t)b * a.Hkv + h) * a.nblk + j) * D + d] = x;
 }
 
-// kTopK candidates are kept per row: 8, 16 or 32, the smallest that holds n_select.
+// One wave per 32 query rows of one head; lanes n and n + 32 share row n.
+// The compressed scores of 32 pooled keys at a time come from fp32 matrix
+// instructions (S^T = PK Q^T, v_mfma_f32_32x32x2_f32: lane (n, h) supplies
+// channels 2i + h of row n's rotated q and of pooled key n); lane (n, h) then
+// holds the scores of row n on keys 8r + 4h + {0..3}, r = 0..3, and keeps the
+// best kTopK of its own candidates (candidates arrive in increasing order; a
+// later one replaces only a strictly smaller score, so ties keep the lower
+// block).  The two lanes of a row merge their lists (ties to the lower block)
+// and attend together over the chosen blocks' tokens, each over half of the
+// channels.  kTopK is 8, 16 or 32, the smallest that holds n_select.
+template <class X, int D>
+__device__ __forceinline__ void load_q_rotated(const NsaArgs& a, size_t qrow, int t, bool row_ok, float (&q)[D]) {
+    constexpr int H = D / 2;
+    if (!row_ok) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) q[d] = 0.f;
+        return;
+    }
+    load_half<H>((const X*)a.q + qrow * D, *(float(*)[H])&q[0]);
+    load_half<H>((const X*)a.q + qrow * D + H, *(float(*)[H])&q[H]);
+    if (a.rope_cos) {
+        const int p = min(t, a.rope_len - 1);
+        float c[H], sn[H];
+        load_half<H>(a.rope_cos + (size_t)p * H, c);
+        load_half<H>(a.rope_sin + (size_t)p * H, sn);
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+            const float x1 = q[i], x2 = q[i + H];
+            q[i] = x1 * c[i] - x2 * sn[i];
+            q[i + H] = x2 * c[i] + x1 * sn[i];
+        }
+    }
+}
+
 template <class X, int D, int kTopK>
-__global__ __launch_bounds__(64) void nsa_select_kernel(NsaArgs a, const float* k32, const float* v32,
-                                                        const float* pk32) {
-    __shared__ float tile[NT][D];
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(64) void nsa_select_kernel(NsaArgs a, const X* krot, const float* pk32) {
+    constexpr int H = D / 2;   // channels per lane of a row pair
+    constexpr int RS = D + 4;  // LDS row stride of the staged pooled keys (floats)
+    __shared__ __align__(16) float tile[32 * RS];
+    __shared__ float sc[64 * 17];  // each lane's 16 scores of the current tile
+    const int lane = threadIdx.x, n = lane & 31, kk = lane >> 5;
     const int T = a.T;
-    const int b = blockIdx.z, hq = blockIdx.y;
+    // XCD-aware numbering: dispatch sends workgroup i to XCD i % 8; each XCD
+    // takes a contiguous range of (row block fastest, head, batch row), so the
+    // rows one head gathers stay in that XCD's L2
+    const int nrb = (T + 31) / 32;
+    const long long nwg = (long long)nrb * a.Hq * a.B;
+    long long lb = blockIdx.x;
+    if ((nwg & 7) == 0) lb = (long long)(blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int rb = (int)(lb % nrb);
+    const int hq = (int)((lb / nrb) % a.Hq);
+    const int b = (int)(lb / ((long long)nrb * a.Hq));
     const int hkv = hq / (a.Hq / a.Hkv);
-    const int t = blockIdx.x * 64 + lane;
+    const int t = rb * 32 + n;
     const bool row_ok = t < T;
     const size_t qrow = ((size_t)b * a.Hq + hq) * T + (row_ok ? t : 0);
-    float q[D];
+    // the matrix operand: channels 2i + kk of row n's rotated q
+    // and, for the attention over the chosen tokens, channels [H kk, H kk + H)
+    // (kept from here when the lists are short, else loaded again then)
+    constexpr bool kKeepQA = kTopK <= 16;
+    float qB[H], qA[H];
+    {
+        float q[D];
+        load_q_rotated<X, D>(a, qrow, t, row_ok, q);
 #pragma unroll
-    for (int d = 0; d < D; ++d) q[d] = row_ok ? ld_f((const X*)a.q, qrow * D + d) : 0.f;
-    if (a.rope_cos && row_ok) {
-        const int p = min(t, a.rope_len - 1);
-#pragma unroll
-        for (int i = 0; i < D / 2; ++i) {
-            const float c = a.rope_cos[(size_t)p * (D / 2) + i], s = a.rope_sin[(size_t)p * (D / 2) + i];
-            const float x1 = q[i], x2 = q[i + D / 2];
-            q[i] = x1 * c - x2 * s;
-            q[i + D / 2] = x2 * c + x1 * s;
+        for (int i = 0; i < H; ++i) {
+            qB[i] = kk ? q[2 * i + 1] : q[2 * i];
+            if (kKeepQA) qA[i] = kk ? q[H + i] : q[i];
         }
     }
     // candidates: the pooled blocks that have cleared the window
@@ -105,8 +193,6 @@ __global__ __launch_bounds__(64) void nsa_select_kernel(NsaArgs a, const float* 
     const int n_vis = row_ok && cleared >= a.block ? min(cleared / a.block, a.nblk) : 0;
     int n_max = n_vis;
     for (int o = 1; o < 64; o <<= 1) n_max = max(n_max, __shfl_xor(n_max, o, 64));
-    // streaming top-kTopK, best first; a later block replaces only a strictly
-    // smaller score, so equal scores keep the lower block first
     float tv[kTopK];
     int ti[kTopK];
 #pragma unroll
@@ -115,107 +201,190 @@ __global__ __launch_bounds__(64) void nsa_select_kernel(NsaArgs a, const float* 
         ti[i] = -1;
     }
     const float* pkh = pk32 + ((size_t)b * a.Hkv + hkv) * (size_t)a.nblk * D;
-    for (int j0 = 0; j0 < n_max; j0 += NT) {
-        __syncthreads();
-        for (int e = lane; e < NT * D; e += 64) {
-            const int jj = j0 + e / D;
-            tile[e / D][e % D] = jj < a.nblk ? pkh[(size_t)jj * D + e % D] : 0.f;
+    const uint32_t tl = lds_off(tile);
+    for (int j0 = 0; j0 < n_max; j0 += 32) {
+        // stage pooled keys j0 .. j0 + 31: lane (m, kk) copies channels
+        // [H kk, H kk + H) of key m, split by channel parity (row m holds the
+        // even channels, then the odd ones)
+        {
+            const int jj = j0 + n;
+            const float* src = pkh + (size_t)min(jj, a.nblk - 1) * D + H * kk;
+#pragma unroll
+            for (int c4 = 0; c4 < H / 4; ++c4) {
+                const float4 x = jj < a.nblk ? *(const float4*)(src + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+                const int c = H * kk + 4 * c4;  // even
+                lds_store64(tl + (uint32_t)(n * RS + c / 2) * 4u, u32x2{__float_as_uint(x.x), __float_as_uint(x.z)});
+                lds_store64(tl + (uint32_t)(n * RS + H + c / 2) * 4u, u32x2{__float_as_uint(x.y), __float_as_uint(x.w)});
+            }
         }
-        __syncthreads();
-#pragma unroll 1
-        for (int u = 0; u < NT; ++u) {
-            const int j = j0 + u;
-            float dot = 0.f;
+        lds_reads_done();  // (LDS writes and reads of the wave complete in order; the wait also covers the writes)
+        f32x16 acc{};
 #pragma unroll
-            for (int d = 0; d < D; ++d) dot = fmaf(q[d], tile[u][d], dot);
-            float s = dot * a.scale;
-            if (j < n_vis && s > tv[kTopK - 1]) {
-                int id = j;
+        for (int i4 = 0; i4 < H / 4; ++i4) {
+            const u32x4 av = lds_load128(tl + (uint32_t)(n * RS + kk * H + 4 * i4) * 4u);
 #pragma unroll
-                for (int i = 0; i < kTopK; ++i) {
-                    if (s > tv[i]) {
-                        const float fs = tv[i];
-                        const int is = ti[i];
-                        tv[i] = s;
-                        ti[i] = id;
-                        s = fs;
-                        id = is;
+            for (int e = 0; e < 4; ++e)
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(av[e]), qB[4 * i4 + e], acc, 0, 0, 0);
+        }
+        lds_reads_done();  // the tile is reread only after these reads
+        // This lane's candidates above its current threshold, as a bit mask;
+        // their scores wait in LDS.  The lanes then insert together, each its
+        // next candidate in increasing order, as long as any lane has one:
+        // the insertion runs as often as the busiest lane needs, not once
+        // for every candidate some lane takes.
+        uint32_t want = 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float s = acc[j] * a.scale;
+            const int jj = j0 + 8 * (j >> 2) + 4 * kk + (j & 3);
+            sc[lane * 17 + j] = s;
+            if (jj < n_vis && s > tv[kTopK - 1]) want |= 1u << j;
+        }
+        while (__builtin_amdgcn_ballot_w64(want != 0u) != 0) {
+            if (want != 0u) {
+                const int j = __builtin_ctz(want);
+                want &= want - 1u;
+                float s = sc[lane * 17 + j];
+                int id = j0 + 8 * (j >> 2) + 4 * kk + (j & 3);
+                if (s > tv[kTopK - 1]) {
+#pragma unroll
+                    for (int i = 0; i < kTopK; ++i) {
+                        if (s > tv[i]) {
+                            const float fs = tv[i];
+                            const int is = ti[i];
+                            tv[i] = s;
+                            ti[i] = id;
+                            s = fs;
+                            id = is;
+                        }
                     }
                 }
             }
         }
     }
-    // attention over the chosen blocks' exact tokens (online softmax)
-    const float* kh = k32 + ((size_t)b * a.Hkv + hkv) * (size_t)T * D;
-    const float* vh = v32 + ((size_t)b * a.Hkv + hkv) * (size_t)T * D;
-    float m = kNegInf, l = 0.f, o[D];
+    // Merge the two lists of the row (both lanes compute it): the better of
+    // entry i of the kk = 0 list and entry K-1-i of the kk = 1 list, for every
+    // i, is the top K as a bitonic sequence, then sorted by a bitonic network.
+    // Better: the larger score, or the lower block on equal scores.
+    {
+        float ov[kTopK];
+        int oi[kTopK];
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] = 0.f;
+        for (int i = 0; i < kTopK; ++i) {
+            ov[i] = __shfl_xor(tv[i], 32, 64);
+            oi[i] = __shfl_xor(ti[i], 32, 64);
+        }
+        auto better = [](float va, int ia, float vb, int ib) {
+            return va > vb || (va == vb && (unsigned)ia < (unsigned)ib);
+        };
+        // (list A: the kk = 0 lane's, list B: the kk = 1 lane's; both lanes read
+        // them from copies, since the merge overwrites tv / ti)
+        float av[kTopK], bv[kTopK];
+        int ai[kTopK], bi[kTopK];
+#pragma unroll
+        for (int i = 0; i < kTopK; ++i) {
+            av[i] = kk ? ov[i] : tv[i];
+            ai[i] = kk ? oi[i] : ti[i];
+            bv[i] = kk ? tv[i] : ov[i];
+            bi[i] = kk ? ti[i] : oi[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kTopK; ++i) {
+            const bool first = better(av[i], ai[i], bv[kTopK - 1 - i], bi[kTopK - 1 - i]);
+            tv[i] = first ? av[i] : bv[kTopK - 1 - i];
+            ti[i] = first ? ai[i] : bi[kTopK - 1 - i];
+        }
+#pragma unroll
+        for (int st = kTopK / 2; st >= 1; st >>= 1) {
+#pragma unroll
+            for (int i = 0; i < kTopK; ++i) {
+                if (i & st) continue;
+                const bool keep = !better(tv[i + st], ti[i + st], tv[i], ti[i]);
+                const float va = tv[i], vb = tv[i + st];
+                const int ia = ti[i], ib = ti[i + st];
+                tv[i] = keep ? va : vb;
+                ti[i] = keep ? ia : ib;
+                tv[i + st] = keep ? vb : va;
+                ti[i + st] = keep ? ib : ia;
+            }
+        }
+    }
+    // attention over the chosen blocks' exact tokens (online softmax); lane
+    // (n, kk) holds channels [H kk, H kk + H) of row n
+    if (!kKeepQA) {
+        float q[D];
+        load_q_rotated<X, D>(a, qrow, t, row_ok, q);
+#pragma unroll
+        for (int i = 0; i < H; ++i) qA[i] = kk ? q[H + i] : q[i];
+    }
+    const X* kh = krot + ((size_t)b * a.Hkv + hkv) * (size_t)T * D + H * kk;
+    const X* vh = (const X*)a.v + ((size_t)b * a.Hkv + hkv) * (size_t)T * D + H * kk;
+    float m = kNegInf, l = 0.f, o[H];
+#pragma unroll
+    for (int d = 0; d < H; ++d) o[d] = 0.f;
 #pragma unroll
     for (int i = 0; i < kTopK; ++i) {
         if (i >= a.n_select || ti[i] < 0) continue;
         for (int u = 0; u < a.block; ++u) {
             const size_t r = (size_t)ti[i] * a.block + u;
-            const float4* kr = (const float4*)(kh + r * D);
+            float kx[H], vx[H];
+            load_half<H>(kh + r * D, kx);
+            load_half<H>(vh + r * D, vx);
             float dot = 0.f;
 #pragma unroll
-            for (int d4 = 0; d4 < D / 4; ++d4) {
-                const float4 kk = kr[d4];
-                dot = fmaf(q[4 * d4], kk.x, dot);
-                dot = fmaf(q[4 * d4 + 1], kk.y, dot);
-                dot = fmaf(q[4 * d4 + 2], kk.z, dot);
-                dot = fmaf(q[4 * d4 + 3], kk.w, dot);
-            }
-            const float s = dot * a.scale;
+            for (int d = 0; d < H; ++d) dot = fmaf(qA[d], kx[d], dot);
+            const float other = __shfl_xor(dot, 32, 64);
+            const float s = (kk ? other + dot : dot + other) * a.scale;
             if (s > m) {
                 const float corr = expf(m - s);
                 m = s;
                 l *= corr;
 #pragma unroll
-                for (int d = 0; d < D; ++d) o[d] *= corr;
+                for (int d = 0; d < H; ++d) o[d] *= corr;
             }
             const float p = expf(s - m);
             l += p;
-            const float4* vr = (const float4*)(vh + r * D);
 #pragma unroll
-            for (int d4 = 0; d4 < D / 4; ++d4) {
-                const float4 vv = vr[d4];
-                o[4 * d4] = fmaf(p, vv.x, o[4 * d4]);
-                o[4 * d4 + 1] = fmaf(p, vv.y, o[4 * d4 + 1]);
-                o[4 * d4 + 2] = fmaf(p, vv.z, o[4 * d4 + 2]);
-                o[4 * d4 + 3] = fmaf(p, vv.w, o[4 * d4 + 3]);
-            }
+            for (int d = 0; d < H; ++d) o[d] = fmaf(p, vx[d], o[d]);
         }
     }
     if (!row_ok) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (a.dtype == 1) {
-        uint16_t* orow = (uint16_t*)a.out + qrow * D;
+        uint16_t* orow = (uint16_t*)a.out + qrow * D + H * kk;
 #pragma unroll
-        for (int d = 0; d < D; ++d) orow[d] = (uint16_t)f32_to_bf16_bits(o[d] * inv);
+        for (int d = 0; d < H; ++d) orow[d] = (uint16_t)f32_to_bf16_bits(o[d] * inv);
     } else {
-        float* orow = (float*)a.out + qrow * D;
+        float* orow = (float*)a.out + qrow * D + H * kk;
 #pragma unroll
-        for (int d = 0; d < D; ++d) orow[d] = o[d] * inv;
+        for (int d = 0; d < H; ++d) orow[d] = o[d] * inv;
     }
-    if (a.lse) a.lse[qrow] = l > 0.f ? m + logf(l) : kNegInf;
-    if (a.sel) {
+    if (kk == 0) {
+        if (a.lse) a.lse[qrow] = l > 0.f ? m + logf(l) : kNegInf;
+        if (a.sel) {
 #pragma unroll
-        for (int i = 0; i < kTopK; ++i)
-            if (i < a.n_select) a.sel[qrow * a.n_select + i] = ti[i];
+            for (int i = 0; i < kTopK; ++i)
+                if (i < a.n_select) a.sel[qrow * a.n_select + i] = ti[i];
+        }
     }
 }
 
 template <class X>
-hipError_t launch_nsa_t(const NsaArgs& a, float* k32, float* v32, float* pk32, hipStream_t s) {
-    const dim3 blk(64);
-    hipLaunchKernelGGL(nsa_prep_rows_kernel<X>, dim3((unsigned)a.T, (unsigned)a.Hkv, (unsigned)a.B), blk, 0, s, a,
-                       k32, v32);
+hipError_t launch_nsa_t(const NsaArgs& a, void* krot_ws, float* pk32, hipStream_t s) {
+    const X* krot = (const X*)a.k;  // without RoPE the keys are read as given
+    if (a.rope_cos) {
+        const long long n = (long long)a.B * a.Hkv * a.T * (a.D / 16);
+        hipLaunchKernelGGL(nsa_rotate_keys_kernel<X>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
+                           (X*)krot_ws);
+        krot = (const X*)krot_ws;
+    }
     if (a.nblk > 0)
-        hipLaunchKernelGGL(nsa_prep_pooled_kernel<X>, dim3((unsigned)a.nblk, (unsigned)a.Hkv, (unsigned)a.B), blk, 0,
-                           s, a, pk32);
-    const dim3 grid((unsigned)((a.T + 63) / 64), (unsigned)a.Hq, (unsigned)a.B);
-#define SWA_NSA(DD, KK) hipLaunchKernelGGL((nsa_select_kernel<X, DD, KK>), grid, blk, 0, s, a, k32, v32, pk32)
+        hipLaunchKernelGGL(nsa_prep_pooled_kernel<X>, dim3((unsigned)a.nblk, (unsigned)a.Hkv, (unsigned)a.B), dim3(64),
+                           0, s, a, pk32);
+    const long long nwg = (long long)((a.T + 31) / 32) * a.Hq * a.B;
+    if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)nwg), blk(64);
+#define SWA_NSA(DD, KK) hipLaunchKernelGGL((nsa_select_kernel<X, DD, KK>), grid, blk, 0, s, a, krot, pk32)
     if (a.D == 64) {
         if (a.n_select <= 8) SWA_NSA(64, 8);
         else if (a.n_select <= 16) SWA_NSA(64, 16);
@@ -231,8 +400,8 @@ hipError_t launch_nsa_t(const NsaArgs& a, float* k32, float* v32, float* pk32, h
 
 }  // namespace
 
-hipError_t launch_nsa_select(const NsaArgs& a, float* k32, float* v32, float* pk32, hipStream_t s) {
-    return a.dtype == 1 ? launch_nsa_t<uint16_t>(a, k32, v32, pk32, s) : launch_nsa_t<float>(a, k32, v32, pk32, s);
+hipError_t launch_nsa_select(const NsaArgs& a, void* krot, float* pk32, hipStream_t s) {
+    return a.dtype == 1 ? launch_nsa_t<uint16_t>(a, krot, pk32, s) : launch_nsa_t<float>(a, krot, pk32, s);
 }
 
 }  // namespace swa

@@ -558,9 +558,10 @@ int swa_attn_decode_compressed(const swa_decode_params* p, int block, const floa
 
 size_t swa_nsa_select_workspace_size(const swa_prefill_params* p) {
     if (p == nullptr || p->B <= 0 || p->T <= 0 || p->Hkv <= 0 || p->D <= 0 || p->compress_block <= 0) return 0;
-    const size_t nk = (size_t)p->B * p->Hkv * p->T * p->D * 4;
-    const size_t np = (size_t)p->B * p->Hkv * (p->T / p->compress_block) * p->D * 4;
-    return 2 * round256(nk) + round256(np);
+    const size_t elem = p->dtype == SWA_BF16 ? 2 : 4;
+    const size_t nk = p->rope_len > 0 ? (size_t)p->B * p->Hkv * p->T * p->D * elem : 0;  // rotated keys
+    const size_t np = (size_t)p->B * p->Hkv * (p->T / p->compress_block) * p->D * 4;    // fp32 pooled keys
+    return round256(nk) + round256(np);
 }
 
 int swa_nsa_select_attn(const swa_prefill_params* p, int n_select, const void* q, const void* k, const void* v,
@@ -608,10 +609,10 @@ int swa_nsa_select_attn(const swa_prefill_params* p, int n_select, const void* q
     a.rope_len = p->rope_len;
     a.dtype = p->dtype == SWA_BF16 ? 1 : 0;
     a.scale = pa.scale;
-    const size_t nk = round256((size_t)p->B * p->Hkv * p->T * p->D * 4);
+    const size_t elem = p->dtype == SWA_BF16 ? 2 : 4;
+    const size_t nk = p->rope_len > 0 ? round256((size_t)p->B * p->Hkv * p->T * p->D * elem) : 0;
     char* ws = (char*)workspace;
-    return hip_status(swa::launch_nsa_select(a, (float*)ws, (float*)(ws + nk), (float*)(ws + 2 * nk),
-                                             (hipStream_t)stream),
+    return hip_status(swa::launch_nsa_select(a, ws, (float*)(ws + nk), (hipStream_t)stream),
                       "swa_nsa_select_attn launch");
 }
 

@@ -254,9 +254,10 @@ struct NsaArgs {
     int dtype;  // 0 fp32, 1 bf16
     float scale;
 };
-// Preparation (fp32 rotated exact keys and values, fp32 pooled keys) and the
-// selection kernel; k32/v32 [B][Hkv][T][D], pk32 [B][Hkv][nblk][D].
-hipError_t launch_nsa_select(const NsaArgs& a, float* k32, float* v32, float* pk32, hipStream_t s);
+// Preparation (the exact keys rotated, in the input dtype, when a table is
+// given; fp32 pooled keys) and the selection kernel; krot [B][Hkv][T][D],
+// pk32 [B][Hkv][nblk][D].
+hipError_t launch_nsa_select(const NsaArgs& a, void* krot, float* pk32, hipStream_t s);
 
 // Chunked prefill: the caller's tensors and the staged sequence length
 // Tv = S + W - 1 + Tc (sink rows, ring rows before the chunk, the chunk).

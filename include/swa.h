@@ -283,8 +283,12 @@ int swa_attn_prefill_backward(const swa_prefill_params* p,
 /* at their positions, of all their tokens.  out [B,Hq,T,D] (p->dtype), lse  */
 /* [B,Hq,T] fp32 or NULL, sel [B,Hq,T,n_select] int32 (the chosen blocks in  */
 /* score order, -1 after the last) or NULL.  A row with no candidate gets    */
-/* out = 0, lse = -inf.  Arithmetic is fp32.  1 <= n_select <= 32; W >= 1;   */
-/* q, k, v as for swa_attn_prefill (rope_len 0: no rotation).               */
+/* out = 0, lse = -inf.  Arithmetic is fp32 (with bf16 inputs the rotated   */
+/* exact keys are rounded to bf16 once, as in swa_attn_prefill).             */
+/* 1 <= n_select <= 32; W >= 1; q, k, v as for swa_attn_prefill (rope_len 0: */
+/* no rotation).  Workspace: the rotated exact keys (B*Hkv*T*D elements of   */
+/* the dtype, with RoPE only) and the fp32 pooled keys (B*Hkv*(T/b)*D*4      */
+/* bytes), each rounded up to 256 bytes.                                     */
 size_t swa_nsa_select_workspace_size(const swa_prefill_params* p);
 int swa_nsa_select_attn(const swa_prefill_params* p, int n_select,
                         const void* q, const void* k, const void* v, /* [B,Hq|Hkv,T,D], before RoPE */

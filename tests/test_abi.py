@@ -485,7 +485,11 @@ def test_nsa_select_validation():
     p = _p(T=64, D=64, window=16, compress_block=4)
     n = L.swa_nsa_select_workspace_size(ctypes.byref(p))
     r = lambda x: (x + 255) // 256 * 256
-    assert n == 2 * r(1 * 2 * 64 * 64 * 4) + r(1 * 2 * 16 * 64 * 4)
+    assert n == r(1 * 2 * 16 * 64 * 4)                            # fp32 pooled keys
+    pr = _p(T=64, D=64, window=16, compress_block=4, rope_len=64)
+    assert L.swa_nsa_select_workspace_size(ctypes.byref(pr)) == r(1 * 2 * 64 * 64 * 2) + r(1 * 2 * 16 * 64 * 4)
+    pr = _p(T=64, D=64, window=16, compress_block=4, rope_len=64, dtype=swa.SWA_F32)
+    assert L.swa_nsa_select_workspace_size(ctypes.byref(pr)) == r(1 * 2 * 64 * 64 * 4) + r(1 * 2 * 16 * 64 * 4)
     assert L.swa_nsa_select_workspace_size(ctypes.byref(_p(T=64, compress_block=0))) == 0
     ptrs = [FAKE] * 8           # q, k, v, cos, sin, out, lse, sel
     call = lambda pp, ns, pt, ws=FAKE, nb=n: L.swa_nsa_select_attn(ctypes.byref(pp), ns, *pt, ws, nb, None)
