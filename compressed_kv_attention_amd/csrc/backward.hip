@@ -321,9 +321,454 @@ __global__ void bwd_sum_heads_kernel(BwdArgs a, const float* pk, const float* pv
     }
 }
 
+// ---- bf16 inputs: the same gradients on bf16 matrix instructions ---------
+//
+// The operands are those of the forward's MFMA kernel: q rotated and scaled
+// by scale * log2 e (rounded to bf16 once), k rotated (rounded once), v and
+// dO as given; P = exp2(s' - lse log2 e) comes out in fp32 and enters the
+// gradient products rounded to bf16, as P does in the forward.  Sub-tiles are
+// 32 x 32 with the forward's operand layouts (transposed LDS reads for the
+// operands whose rows are the reduction dimension):
+//   query-major, per 32 keys:  S^T = K Q'^T,  dP^T = V dO^T,
+//                              dS^T = P^T (dP^T - Delta),  dQ^T += K^T dS^T
+//   key-major, per 32 queries: S = Q' K^T,  dP = dO V^T,  dS = P (dP - Delta),
+//                              dV^T += dO^T P,  dK^T += Q'^T dS
+// dq = scale dQ, dk = dK / log2 e (Q' carries scale log2 e), dv = dV.
+
+__device__ __forceinline__ uint32_t bwd_pk_bf16(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// q' = bf16((rotate(q) at t) * scale * log2 e) and Delta = sum dO o, one
+// thread per (row, 8 channel pairs); a row's D/16 threads are adjacent.
+__global__ __launch_bounds__(256) void bwd_prep_bf16_q_kernel(BwdArgs a, uint16_t* qs, float* delta) {
+    const int D = a.D, H = D / 2, per_row = H / 8;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long rows = (long long)a.B * a.Hq * a.T;
+    const bool ok = idx < rows * per_row;
+    const long long row = ok ? idx / per_row : 0;
+    const int i0 = (int)(idx - row * per_row) * 8;
+    const int t = (int)(row % a.T);
+    const uint16_t* q = (const uint16_t*)a.q + row * D;
+    const uint16_t* go = (const uint16_t*)a.dout + row * D;
+    const uint16_t* o = (const uint16_t*)a.out + row * D;
+    const float mul = a.scale * kLog2e;
+    float part = 0.f;
+    if (ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x1 = bf16_bits_to_f32(q[i0 + e]), x2 = bf16_bits_to_f32(q[H + i0 + e]);
+            if (a.rope_cos) {
+                const float c = a.rope_cos[(size_t)t * H + i0 + e], sn = a.rope_sin[(size_t)t * H + i0 + e];
+                const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
+                x1 = y1;
+                x2 = y2;
+            }
+            qs[row * D + i0 + e] = (uint16_t)f32_to_bf16_bits(x1 * mul);
+            qs[row * D + H + i0 + e] = (uint16_t)f32_to_bf16_bits(x2 * mul);
+            part = fmaf(bf16_bits_to_f32(go[i0 + e]), bf16_bits_to_f32(o[i0 + e]), part);
+            part = fmaf(bf16_bits_to_f32(go[H + i0 + e]), bf16_bits_to_f32(o[H + i0 + e]), part);
+        }
+    }
+    // the row's per_row (2 or 4) adjacent threads add their parts
+    for (int off = 1; off < per_row; off <<= 1) part += __shfl_xor(part, off, 64);
+    if (ok && i0 == 0) delta[row] = part;
+}
+
+// k rotated at its position, rounded to bf16 once (the forward's key pre-pass).
+__global__ __launch_bounds__(256) void bwd_prep_bf16_k_kernel(BwdArgs a, uint16_t* ks) {
+    const int D = a.D, H = D / 2, per_row = H / 8;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long rows = (long long)a.B * a.Hkv * a.T;
+    if (idx >= rows * per_row) return;
+    const long long row = idx / per_row;
+    const int i0 = (int)(idx - row * per_row) * 8;
+    const int t = (int)(row % a.T);
+    const uint16_t* k = (const uint16_t*)a.k + row * D;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x1 = bf16_bits_to_f32(k[i0 + e]), x2 = bf16_bits_to_f32(k[H + i0 + e]);
+        const float c = a.rope_cos[(size_t)t * H + i0 + e], sn = a.rope_sin[(size_t)t * H + i0 + e];
+        ks[row * D + i0 + e] = (uint16_t)f32_to_bf16_bits(x1 * c - x2 * sn);
+        ks[row * D + H + i0 + e] = (uint16_t)f32_to_bf16_bits(x2 * c + x1 * sn);
+    }
+}
+
+// LDS tiles of 32 rows, row-major with a 16-byte pad per row.
+template <int D>
+struct Bf16Tile {
+    static constexpr int RS = D + 8;  // row stride in bf16
+    uint16_t x[32 * RS];
+};
+// Copy 32 rows (src + r * D, rows >= nrows read as zero) into a tile: 16 bytes
+// per lane per step.
+template <int D>
+__device__ __forceinline__ void stage_rows(Bf16Tile<D>& t, const uint16_t* src, int nrows, int lane) {
+    constexpr int CPR = D / 8;  // 16-byte pieces per row
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+        const int piece = i * 64 + lane, r = piece / CPR, c = piece % CPR;
+        const uint4 x = r < nrows ? *(const uint4*)(src + (size_t)r * D + 8 * c) : make_uint4(0, 0, 0, 0);
+        *(uint4*)&t.x[r * Bf16Tile<D>::RS + 8 * c] = x;
+    }
+}
+// Operand of the sub-tile's rows (A operand: row l % 32, channels 16c + 8 (l / 32) ..).
+template <int D>
+__device__ __forceinline__ bf16x8 tile_row(const Bf16Tile<D>& t, int c, int lane) {
+    return __builtin_bit_cast(bf16x8, *(const uint4*)&t.x[(lane & 31) * Bf16Tile<D>::RS + 16 * c + 8 * (lane >> 5)]);
+}
+// Transposed operand (A operand of a product whose reduction runs over the
+// tile's rows): rows 16m .. 16m + 15 and channels 32n .. 32n + 31, from two
+// transposing reads per 8 rows (the forward's V^T reads on a plain layout).
+template <int D>
+__device__ __forceinline__ bf16x8 tile_tr(const Bf16Tile<D>& t, int m, int n, int lane) {
+    const int g = lane >> 4, hh = g >> 1, j = lane & 15, r = j >> 2, a4 = j & 3;
+    const int ch = 32 * n + 16 * (g & 1) + 4 * a4;
+    const uint32_t base = lds_off(&t.x[0]);
+    const u32x2 lo = lds_load_tr16(base + (uint32_t)(((16 * m + 4 * hh + r) * Bf16Tile<D>::RS + ch) * 2));
+    const u32x2 hi = lds_load_tr16(base + (uint32_t)(((16 * m + 8 + 4 * hh + r) * Bf16Tile<D>::RS + ch) * 2));
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+// B operand of a row of global memory (row r's channels 16c + 8 (l / 32) ..).
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t* row, int c, int lane) {
+    return __builtin_bit_cast(bf16x8, *(const uint4*)(row + 16 * c + 8 * (lane >> 5)));
+}
+// The 16 accumulator values of a lane as the bf16 B operands of the two
+// 16-row steps (elements 8m .. 8m + 7).
+__device__ __forceinline__ void pack_steps(const float (&x)[16], bf16x8 (&b)[2]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+        b[m] = __builtin_bit_cast(bf16x8, make_uint4(bwd_pk_bf16(x[8 * m], x[8 * m + 1]), bwd_pk_bf16(x[8 * m + 2], x[8 * m + 3]),
+                                                     bwd_pk_bf16(x[8 * m + 4], x[8 * m + 5]),
+                                                     bwd_pk_bf16(x[8 * m + 6], x[8 * m + 7])));
+}
+
+template <int D>
+struct SmemDqMfma {
+    Bf16Tile<D> k, v;
+    int kinfo[32];
+    int red[4];
+    uint32_t sink_bits[(kMaxT / BT + 31) / 32];
+};
+
+// dq: one wave per 32 query rows of one head; the forward's walk over key
+// tiles of 32 (band first, then the tiles holding visible sinks).
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(BwdArgs a, const uint16_t* qs, const uint16_t* kr,
+                                                         const float* delta) {
+    constexpr int NC = D / 16;
+    __shared__ __align__(16) SmemDqMfma<D> sm;
+    const int lane = threadIdx.x, lq = lane & 31, h = lane >> 5;
+    const int T = a.T;
+    const int b = blockIdx.z, hq = blockIdx.y;
+    const int hkv = hq / (a.Hq / a.Hkv);
+    const int q0 = blockIdx.x * BT;
+    const int q1 = min(q0 + BT - 1, T - 1);
+    const int my_q = q0 + lq;
+    const bool row_ok = my_q < T;
+    const size_t qrow = ((size_t)b * a.Hq + hq) * T + (row_ok ? my_q : q0);
+    bf16x8 qf[NC], gf[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        qf[c] = row_operand(qs + qrow * D, c, lane);
+        gf[c] = row_operand((const uint16_t*)a.dout + qrow * D, c, lane);
+    }
+    const float lse = row_ok ? a.lse[qrow] : kNegInf;
+    const float dlt = row_ok ? delta[qrow] : 0.f;
+    int seg_q = 0;
+    if (row_ok) seg_q = a.seg ? a.seg[(size_t)b * T + my_q] : 1;
+    const bool row_vis = row_ok && seg_q > 0 && lse != kNegInf;
+    const float nl = row_vis ? -lse * kLog2e : kNegInf;
+    const unsigned wlim = window_limit(a.window);
+
+    const TilePlan plan = plan_tiles(q0, q1, a.window, 0, 0, a.prefix != nullptr, BT);
+    plan_sink_tiles(plan, a.seg ? a.seg + (size_t)b * T : nullptr, a.prefix ? a.prefix + (size_t)b * T : nullptr, T,
+                    q0, q1, BT, sm.red, sm.sink_bits, lane, 64);
+    TileIter it;
+    it.init(plan, sm.sink_bits, BT);
+    const uint16_t* khead = kr + ((size_t)b * a.Hkv + hkv) * (size_t)T * D;
+    const uint16_t* vhead = (const uint16_t*)a.v + ((size_t)b * a.Hkv + hkv) * (size_t)T * D;
+    f32x16 dqa[D / 32];
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) dqa[n] = f32x16{};
+    int kind = 0, tile = 0;
+    while (it.next(kind, tile)) {
+        const int k0 = tile * BT;
+        __syncthreads();
+        stage_rows<D>(sm.k, khead + (size_t)k0 * D, T - k0, lane);
+        stage_rows<D>(sm.v, vhead + (size_t)k0 * D, T - k0, lane);
+        if (lane < BT) {
+            const int gk = k0 + lane;
+            int info = 0;
+            if (gk < T) {
+                const int sg = a.seg ? a.seg[(size_t)b * T + gk] : 1;
+                const bool sk = a.prefix ? (a.prefix[(size_t)b * T + gk] != 0) : false;
+                info = pack_key_info(sg, sk);
+            }
+            sm.kinfo[lane] = info;
+        }
+        __syncthreads();
+        // S^T = K Q'^T, started from the mask: -lse log2 e where visible, -inf elsewhere
+        f32x16 sacc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int kk = 8 * (j >> 2) + (j & 3) + 4 * h;  // key of element j within the tile
+            const bool vis = row_vis && k0 + kk < T && visible_full(my_q - (k0 + kk), wlim, sm.kinfo[kk], seg_q);
+            sacc[j] = vis ? nl : kNegInf;
+        }
+        f32x16 dpa = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sm.k, c, lane), qf[c], sacc, 0, 0, 0);
+            dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sm.v, c, lane), gf[c], dpa, 0, 0, 0);
+        }
+        float ds[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ds[j] = __builtin_amdgcn_exp2f(sacc[j]) * (dpa[j] - dlt);
+        bf16x8 db[2];
+        pack_steps(ds, db);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int n = 0; n < D / 32; ++n)
+                dqa[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(sm.k, m, n, lane), db[m], dqa[n], 0, 0, 0);
+    }
+    // lane holds query my_q, channels 32n + 8i + 4h + r (element 4i + r of block n)
+    // (each lane holds D/2 of the row's channels: blocks n of 16 values)
+    float g[D / 2];
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) g[16 * n + e] = dqa[n][e] * a.scale;
+    if (!row_ok) return;
+    // channel of value e: 32 (e / 16) + 8 ((e % 16) / 4) + 4 h + e % 4
+    auto chan = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * h + (e & 3); };
+    if (a.rope_cos) {
+        // back by the negative angle: channel d < D/2 pairs with d + D/2, held by
+        // this lane too (D = 64: the other 32-channel block; D = 32: i + 2)
+        constexpr int HALF = D / 2;
+#pragma unroll
+        for (int e = 0; e < D / 2; ++e) {
+            const int d = chan(e);
+            if (d >= HALF) continue;
+            const int e2 = D == 64 ? e + 16 : e + 8;
+            const float c = a.rope_cos[(size_t)my_q * HALF + d], sn = a.rope_sin[(size_t)my_q * HALF + d];
+            const float x1 = g[e], x2 = g[e2];
+            g[e] = x1 * c + x2 * sn;
+            g[e2] = x2 * c - x1 * sn;
+        }
+    }
+    float* out = a.dq + qrow * D;
+#pragma unroll
+    for (int e = 0; e < D / 2; e += 4) *(float4*)(out + chan(e)) = make_float4(g[e], g[e + 1], g[e + 2], g[e + 3]);
+}
+
+template <int D>
+struct SmemDkvMfma {
+    struct Wave {
+        Bf16Tile<D> q, go;
+        float lse2[32];  // lse * log2 e of the tile's queries (-inf: none)
+        float dlt[32];
+        int seg[32];
+    } w[4];
+};
+
+// dk, dv: a workgroup of four waves per 32 keys of one kv head; wave w walks
+// the query tiles that can see the keys for the query heads w, w + 4, ... of
+// the group (each wave stages its own tiles), and the four waves' sums are
+// added in head order at the end.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkv_mfma_kernel(BwdArgs a, const uint16_t* qs, const uint16_t* kr,
+                                                           const float* delta) {
+    constexpr int NC = D / 16;
+    __shared__ __align__(16) SmemDkvMfma<D> sm;
+    const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    typename SmemDkvMfma<D>::Wave& ws = sm.w[wave];
+    const int T = a.T;
+    const int b = blockIdx.z, hkv = blockIdx.y;
+    const int G = a.Hq / a.Hkv;
+    const int s0 = blockIdx.x * BT;
+    const int my_k = s0 + lq;
+    const bool key_ok = my_k < T;
+    const size_t krow = ((size_t)b * a.Hkv + hkv) * T + (key_ok ? my_k : s0);
+    bf16x8 kf[NC], vf[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        kf[c] = row_operand(kr + krow * D, c, lane);
+        vf[c] = row_operand((const uint16_t*)a.v + krow * D, c, lane);
+    }
+    int seg_k = 0;
+    bool sink_k = false;
+    if (key_ok) {
+        seg_k = a.seg ? a.seg[(size_t)b * T + my_k] : 1;
+        sink_k = a.prefix ? a.prefix[(size_t)b * T + my_k] != 0 : false;
+    }
+    const int info_k = pack_key_info(seg_k, sink_k);
+    const unsigned wlim = window_limit(a.window);
+    // rows to walk: the band, and with sinks in the block every later row of their segments
+    const int s1 = min(s0 + BT - 1, T - 1);
+    const int band_end = a.window != 0 ? min(T - 1, s1 + a.window - 1) : T - 1;
+    const bool has_sink = a.window != 0 && __ballot(key_ok && sink_k && seg_k > 0) != 0;
+    const int sk_lo = wave_imin_xor(key_ok && sink_k && seg_k > 0 ? seg_k : 0x7fffffff, 1, 32);
+    const int sk_hi = wave_imax_xor(key_ok && sink_k && seg_k > 0 ? seg_k : (int)0x80000000, 1, 32);
+    const int last = has_sink ? T - 1 : band_end;
+    f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+        dka[n] = f32x16{};
+        dva[n] = f32x16{};
+    }
+    for (int g = wave; g < G; g += 4) {
+        const int hq = hkv * G + g;
+        const size_t qhead = ((size_t)b * a.Hq + hq) * (size_t)T;
+        for (int t0 = (s0 / BT) * BT; t0 <= last; t0 += BT) {
+            // a tile past the band matters only if one of its rows is in a sink segment of the block
+            if (t0 > band_end) {
+                const int tq = t0 + lq;
+                const int sq = tq < T ? (a.seg ? a.seg[(size_t)b * T + tq] : 1) : 0;
+                if (__ballot(sq >= sk_lo && sq <= sk_hi) == 0) continue;
+            }
+            // this wave's tiles (its own LDS; its reads of the previous tile are done,
+            // LDS accesses of a wave complete in order)
+            stage_rows<D>(ws.q, qs + (qhead + t0) * D, T - t0, lane);
+            stage_rows<D>(ws.go, (const uint16_t*)a.dout + (qhead + t0) * D, T - t0, lane);
+            if (lane < BT) {
+                const int tq = t0 + lane;
+                const float l = tq < T ? a.lse[qhead + tq] : kNegInf;
+                ws.lse2[lane] = l == kNegInf ? kNegInf : l * kLog2e;
+                ws.dlt[lane] = tq < T ? delta[qhead + tq] : 0.f;
+                ws.seg[lane] = tq < T ? (a.seg ? a.seg[(size_t)b * T + tq] : 1) : 0;
+            }
+            lds_reads_done();
+            // S = Q' K^T from the mask (element j: query 8 (j / 4) + j % 4 + 4h of the tile)
+            f32x16 sacc;
+            float dl[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int qi = 8 * (j >> 2) + (j & 3) + 4 * h;
+                const int tq = t0 + qi;
+                const int sq = ws.seg[qi];
+                const float l2 = ws.lse2[qi];
+                dl[j] = ws.dlt[qi];
+                const bool vis = key_ok && tq < T && sq > 0 && l2 != kNegInf &&
+                                 visible_full(tq - my_k, wlim, info_k, sq);
+                sacc[j] = vis ? -l2 : kNegInf;
+            }
+            f32x16 dpa = f32x16{};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(ws.q, c, lane), kf[c], sacc, 0, 0, 0);
+                dpa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(ws.go, c, lane), vf[c], dpa, 0, 0, 0);
+            }
+            float p[16], ds[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                p[j] = __builtin_amdgcn_exp2f(sacc[j]);
+                ds[j] = p[j] * (dpa[j] - dl[j]);
+            }
+            bf16x8 pb[2], db[2];
+            pack_steps(p, pb);
+            pack_steps(ds, db);
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int n = 0; n < D / 32; ++n) {
+                    dva[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(ws.go, m, n, lane), pb[m], dva[n], 0, 0, 0);
+                    dka[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(ws.q, m, n, lane), db[m], dka[n], 0, 0, 0);
+                }
+        }
+    }
+    // the four waves' sums, added in head order through LDS (the tile space,
+    // free once every wave is past its walk): dk first, then dv
+    auto chan = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * h + (e & 3); };
+    float* red = (float*)&sm;  // [4 waves][32 keys][D] fp32 (4 * 32 * D * 4 bytes fit the tiles)
+    static_assert(sizeof(SmemDkvMfma<D>) >= 4 * 32 * D * 4, "reduction space");
+    float gk[D / 2], gv[D / 2];  // this lane's half of the key's channels
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) {
+                const f32x16& acc = pass == 0 ? dka[n] : dva[n];
+                *(float4*)&red[(wave * 32 + lq) * D + chan(16 * n + e)] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+            }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int e = 0; e < D / 2; e += 4) {
+                float4 sum = *(const float4*)&red[lq * D + chan(e)];
+#pragma unroll
+                for (int w = 1; w < 4; ++w) {
+                    const float4 x = *(const float4*)&red[(w * 32 + lq) * D + chan(e)];
+                    sum.x += x.x;
+                    sum.y += x.y;
+                    sum.z += x.z;
+                    sum.w += x.w;
+                }
+                float* dst = pass == 0 ? gk : gv;
+                dst[e] = sum.x;
+                dst[e + 1] = sum.y;
+                dst[e + 2] = sum.z;
+                dst[e + 3] = sum.w;
+            }
+        }
+    }
+    if (wave != 0 || !key_ok) return;
+#pragma unroll
+    for (int e = 0; e < D / 2; ++e) gk[e] *= 0.6931471805599453f;  // dk = dK / log2 e
+    if (a.rope_cos) {
+        constexpr int HALF = D / 2;
+#pragma unroll
+        for (int e = 0; e < D / 2; ++e) {
+            const int d = chan(e);
+            if (d >= HALF) continue;
+            const int e2 = D == 64 ? e + 16 : e + 8;
+            const float c = a.rope_cos[(size_t)my_k * HALF + d], sn = a.rope_sin[(size_t)my_k * HALF + d];
+            const float x1 = gk[e], x2 = gk[e2];
+            gk[e] = x1 * c + x2 * sn;
+            gk[e2] = x2 * c - x1 * sn;
+        }
+    }
+    float* ok = a.dk + krow * D;
+    float* ov = a.dv + krow * D;
+#pragma unroll
+    for (int e = 0; e < D / 2; e += 4) {
+        *(float4*)(ok + chan(e)) = make_float4(gk[e], gk[e + 1], gk[e + 2], gk[e + 3]);
+        *(float4*)(ov + chan(e)) = make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
+    }
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
     const dim3 blk(64);
+    if (a.dtype == 1) {
+        // bf16 operands in the fp32 buffers of the workspace: q' in q32, rotated k in k32
+        uint16_t* qs = (uint16_t*)w.q32;
+        const uint16_t* kr = (const uint16_t*)a.k;
+        const long long nq = (long long)a.B * a.Hq * a.T * (a.D / 16);
+        hipLaunchKernelGGL(bwd_prep_bf16_q_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, a, qs, w.delta);
+        if (a.rope_cos) {
+            const long long nk = (long long)a.B * a.Hkv * a.T * (a.D / 16);
+            hipLaunchKernelGGL(bwd_prep_bf16_k_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, s, a,
+                               (uint16_t*)w.k32);
+            kr = (const uint16_t*)w.k32;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const unsigned nt = (unsigned)((a.T + BT - 1) / BT);
+        hipLaunchKernelGGL(bwd_dq_mfma_kernel<D>, dim3(nt, (unsigned)a.Hq, (unsigned)a.B), blk, 0, s, a, qs, kr,
+                           w.delta);
+        hipLaunchKernelGGL(bwd_dkv_mfma_kernel<D>, dim3(nt, (unsigned)a.Hkv, (unsigned)a.B), dim3(256), 0, s, a, qs, kr,
+                           w.delta);
+        return hipGetLastError();
+    }
     const dim3 grid_q((unsigned)a.T, (unsigned)a.Hq, (unsigned)a.B), grid_k((unsigned)a.T, (unsigned)a.Hkv, (unsigned)a.B);
     if (a.dtype == 1) {
         hipLaunchKernelGGL(bwd_prep_q_kernel<uint16_t>, grid_q, blk, 0, s, a, w.q32, w.do32, w.delta);
