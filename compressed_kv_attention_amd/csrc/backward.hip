@@ -344,7 +344,16 @@ __device__ __forceinline__ uint32_t bwd_pk_bf16(float lo, float hi) {
 }
 
 // q' = bf16((rotate(q) at t) * scale * log2 e) and Delta = sum dO o, one
-// thread per (row, 8 channel pairs); a row's D/16 threads are adjacent.
+// thread per (row, 8 channel pairs: channels i0 .. i0+7 and their partners
+// i0 + D/2 ..); a row's D/16 threads are adjacent.  16-byte accesses.
+__device__ __forceinline__ void unpack8_bf16(const uint4& x, float* f) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
 __global__ __launch_bounds__(256) void bwd_prep_bf16_q_kernel(BwdArgs a, uint16_t* qs, float* delta) {
     const int D = a.D, H = D / 2, per_row = H / 8;
     const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -353,25 +362,43 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16_q_kernel(BwdArgs a, uint16_
     const long long row = ok ? idx / per_row : 0;
     const int i0 = (int)(idx - row * per_row) * 8;
     const int t = (int)(row % a.T);
-    const uint16_t* q = (const uint16_t*)a.q + row * D;
-    const uint16_t* go = (const uint16_t*)a.dout + row * D;
-    const uint16_t* o = (const uint16_t*)a.out + row * D;
+    const size_t base = (size_t)row * D + i0;
     const float mul = a.scale * kLog2e;
     float part = 0.f;
     if (ok) {
+        float x1[8], x2[8], g1[8], g2[8], o1[8], o2[8];
+        unpack8_bf16(*(const uint4*)((const uint16_t*)a.q + base), x1);
+        unpack8_bf16(*(const uint4*)((const uint16_t*)a.q + base + H), x2);
+        unpack8_bf16(*(const uint4*)((const uint16_t*)a.dout + base), g1);
+        unpack8_bf16(*(const uint4*)((const uint16_t*)a.dout + base + H), g2);
+        unpack8_bf16(*(const uint4*)((const uint16_t*)a.out + base), o1);
+        unpack8_bf16(*(const uint4*)((const uint16_t*)a.out + base + H), o2);
+        if (a.rope_cos) {
+            const float4 c0 = *(const float4*)(a.rope_cos + (size_t)t * H + i0);
+            const float4 c1 = *(const float4*)(a.rope_cos + (size_t)t * H + i0 + 4);
+            const float4 s0 = *(const float4*)(a.rope_sin + (size_t)t * H + i0);
+            const float4 s1 = *(const float4*)(a.rope_sin + (size_t)t * H + i0 + 4);
+            const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float y1 = x1[e] * c[e] - x2[e] * sn[e], y2 = x2[e] * c[e] + x1[e] * sn[e];
+                x1[e] = y1;
+                x2[e] = y2;
+            }
+        }
+        uint32_t w1[4], w2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w1[i] = bwd_pk_bf16(x1[2 * i] * mul, x1[2 * i + 1] * mul);
+            w2[i] = bwd_pk_bf16(x2[2 * i] * mul, x2[2 * i + 1] * mul);
+        }
+        *(uint4*)(qs + base) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        *(uint4*)(qs + base + H) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float x1 = bf16_bits_to_f32(q[i0 + e]), x2 = bf16_bits_to_f32(q[H + i0 + e]);
-            if (a.rope_cos) {
-                const float c = a.rope_cos[(size_t)t * H + i0 + e], sn = a.rope_sin[(size_t)t * H + i0 + e];
-                const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
-                x1 = y1;
-                x2 = y2;
-            }
-            qs[row * D + i0 + e] = (uint16_t)f32_to_bf16_bits(x1 * mul);
-            qs[row * D + H + i0 + e] = (uint16_t)f32_to_bf16_bits(x2 * mul);
-            part = fmaf(bf16_bits_to_f32(go[i0 + e]), bf16_bits_to_f32(o[i0 + e]), part);
-            part = fmaf(bf16_bits_to_f32(go[H + i0 + e]), bf16_bits_to_f32(o[H + i0 + e]), part);
+            part = fmaf(g1[e], o1[e], part);
+            part = fmaf(g2[e], o2[e], part);
         }
     }
     // the row's per_row (2 or 4) adjacent threads add their parts
@@ -404,14 +431,13 @@ struct Bf16Tile {
     static constexpr int RS = D + 8;  // row stride in bf16
     uint16_t x[32 * RS];
 };
-// Copy 32 rows (src + r * D, rows >= nrows read as zero) into a tile: 16 bytes
-// per lane per step.
+// Copy 32 rows (src + r * D, rows >= nrows read as zero) into a tile, 16
+// bytes per thread per step, by threads tid of nthreads (a multiple of 64).
 template <int D>
-__device__ __forceinline__ void stage_rows(Bf16Tile<D>& t, const uint16_t* src, int nrows, int lane) {
+__device__ __forceinline__ void stage_rows(Bf16Tile<D>& t, const uint16_t* src, int nrows, int tid, int nthreads) {
     constexpr int CPR = D / 8;  // 16-byte pieces per row
-#pragma unroll
-    for (int i = 0; i < 32 * CPR / 64; ++i) {
-        const int piece = i * 64 + lane, r = piece / CPR, c = piece % CPR;
+    for (int piece = tid; piece < 32 * CPR; piece += nthreads) {
+        const int r = piece / CPR, c = piece % CPR;
         const uint4 x = r < nrows ? *(const uint4*)(src + (size_t)r * D + 8 * c) : make_uint4(0, 0, 0, 0);
         *(uint4*)&t.x[r * Bf16Tile<D>::RS + 8 * c] = x;
     }
@@ -455,17 +481,23 @@ struct SmemDqMfma {
     uint32_t sink_bits[(kMaxT / BT + 31) / 32];
 };
 
-// dq: one wave per 32 query rows of one head; the forward's walk over key
-// tiles of 32 (band first, then the tiles holding visible sinks).
+// dq: a workgroup of four waves per 32 query rows and four query heads of one
+// GQA group (one head per wave; they share every staged K/V tile); the
+// forward's walk over key tiles of 32 (band first, then the tiles holding
+// visible sinks).
 template <int D>
-__global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(BwdArgs a, const uint16_t* qs, const uint16_t* kr,
-                                                         const float* delta) {
+__global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(BwdArgs a, const uint16_t* qs, const uint16_t* kr,
+                                                          const float* delta) {
     constexpr int NC = D / 16;
     __shared__ __align__(16) SmemDqMfma<D> sm;
-    const int lane = threadIdx.x, lq = lane & 31, h = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = a.T;
-    const int b = blockIdx.z, hq = blockIdx.y;
-    const int hkv = hq / (a.Hq / a.Hkv);
+    const int G = a.Hq / a.Hkv, ngs = (G + 3) / 4;
+    const int b = blockIdx.z, hkv = blockIdx.y / ngs;
+    const int gh = (blockIdx.y - hkv * ngs) * 4 + wave;  // head within the group
+    const bool wave_on = gh < G;  // (waves past the group's last head only stage tiles)
+    const int hq = hkv * G + min(gh, G - 1);
     const int q0 = blockIdx.x * BT;
     const int q1 = min(q0 + BT - 1, T - 1);
     const int my_q = q0 + lq;
@@ -487,7 +519,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(BwdArgs a, const uint16
 
     const TilePlan plan = plan_tiles(q0, q1, a.window, 0, 0, a.prefix != nullptr, BT);
     plan_sink_tiles(plan, a.seg ? a.seg + (size_t)b * T : nullptr, a.prefix ? a.prefix + (size_t)b * T : nullptr, T,
-                    q0, q1, BT, sm.red, sm.sink_bits, lane, 64);
+                    q0, q1, BT, sm.red, sm.sink_bits, tid, 256);
     TileIter it;
     it.init(plan, sm.sink_bits, BT);
     const uint16_t* khead = kr + ((size_t)b * a.Hkv + hkv) * (size_t)T * D;
@@ -499,19 +531,20 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(BwdArgs a, const uint16
     while (it.next(kind, tile)) {
         const int k0 = tile * BT;
         __syncthreads();
-        stage_rows<D>(sm.k, khead + (size_t)k0 * D, T - k0, lane);
-        stage_rows<D>(sm.v, vhead + (size_t)k0 * D, T - k0, lane);
-        if (lane < BT) {
-            const int gk = k0 + lane;
+        stage_rows<D>(sm.k, khead + (size_t)k0 * D, T - k0, tid, 256);
+        stage_rows<D>(sm.v, vhead + (size_t)k0 * D, T - k0, tid, 256);
+        if (tid < BT) {
+            const int gk = k0 + tid;
             int info = 0;
             if (gk < T) {
                 const int sg = a.seg ? a.seg[(size_t)b * T + gk] : 1;
                 const bool sk = a.prefix ? (a.prefix[(size_t)b * T + gk] != 0) : false;
                 info = pack_key_info(sg, sk);
             }
-            sm.kinfo[lane] = info;
+            sm.kinfo[tid] = info;
         }
         __syncthreads();
+        if (!wave_on) continue;
         // S^T = K Q'^T, started from the mask: -lse log2 e where visible, -inf elsewhere
         f32x16 sacc;
 #pragma unroll
@@ -544,7 +577,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(BwdArgs a, const uint16
     for (int n = 0; n < D / 32; ++n)
 #pragma unroll
         for (int e = 0; e < 16; ++e) g[16 * n + e] = dqa[n][e] * a.scale;
-    if (!row_ok) return;
+    if (!row_ok || !wave_on) return;
     // channel of value e: 32 (e / 16) + 8 ((e % 16) / 4) + 4 h + e % 4
     auto chan = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * h + (e & 3); };
     if (a.rope_cos) {
@@ -635,8 +668,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_mfma_kernel(BwdArgs a, const uint
             }
             // this wave's tiles (its own LDS; its reads of the previous tile are done,
             // LDS accesses of a wave complete in order)
-            stage_rows<D>(ws.q, qs + (qhead + t0) * D, T - t0, lane);
-            stage_rows<D>(ws.go, (const uint16_t*)a.dout + (qhead + t0) * D, T - t0, lane);
+            stage_rows<D>(ws.q, qs + (qhead + t0) * D, T - t0, lane, 64);
+            stage_rows<D>(ws.go, (const uint16_t*)a.dout + (qhead + t0) * D, T - t0, lane, 64);
             if (lane < BT) {
                 const int tq = t0 + lane;
                 const float l = tq < T ? a.lse[qhead + tq] : kNegInf;
@@ -763,8 +796,9 @@ hipError_t launch_bwd_d(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const unsigned nt = (unsigned)((a.T + BT - 1) / BT);
-        hipLaunchKernelGGL(bwd_dq_mfma_kernel<D>, dim3(nt, (unsigned)a.Hq, (unsigned)a.B), blk, 0, s, a, qs, kr,
-                           w.delta);
+        const unsigned ngs = (unsigned)((a.Hq / a.Hkv + 3) / 4);
+        hipLaunchKernelGGL(bwd_dq_mfma_kernel<D>, dim3(nt, (unsigned)a.Hkv * ngs, (unsigned)a.B), dim3(256), 0, s, a,
+                           qs, kr, w.delta);
         hipLaunchKernelGGL(bwd_dkv_mfma_kernel<D>, dim3(nt, (unsigned)a.Hkv, (unsigned)a.B), dim3(256), 0, s, a, qs, kr,
                            w.delta);
         return hipGetLastError();
