@@ -476,7 +476,7 @@ __device__ __forceinline__ void pack_steps(const float (&x)[16], bf16x8 (&b)[2])
 template <int D>
 struct SmemDqMfma {
     Bf16Tile<D> k, v;
-    int kinfo[32];
+    __attribute__((aligned(16))) int kinfo[32];
     int red[4];
     uint32_t sink_bits[(kMaxT / BT + 31) / 32];
 };
@@ -527,31 +527,58 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(BwdArgs a, const uint1
     f32x16 dqa[D / 32];
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) dqa[n] = f32x16{};
-    int kind = 0, tile = 0;
-    while (it.next(kind, tile)) {
-        const int k0 = tile * BT;
-        __syncthreads();
-        stage_rows<D>(sm.k, khead + (size_t)k0 * D, T - k0, tid, 256);
-        stage_rows<D>(sm.v, vhead + (size_t)k0 * D, T - k0, tid, 256);
-        if (tid < BT) {
-            const int gk = k0 + tid;
-            int info = 0;
-            if (gk < T) {
-                const int sg = a.seg ? a.seg[(size_t)b * T + gk] : 1;
-                const bool sk = a.prefix ? (a.prefix[(size_t)b * T + gk] != 0) : false;
-                info = pack_key_info(sg, sk);
-            }
-            sm.kinfo[tid] = info;
+    // Staging: thread tid moves piece tid (16 bytes) of the tile's K and V rows
+    // and, below 32, key tid's info; the next tile's pieces are loaded into
+    // registers while the current tile is computed.
+    constexpr int CPR = D / 8;
+    const int pr = tid / CPR, pc = tid % CPR;
+    const bool mover = tid < 32 * CPR;
+    auto fetch = [&](int k0, uint4& xk, uint4& xv, int& info) {
+        xk = xv = make_uint4(0, 0, 0, 0);
+        if (mover && pr < T - k0) {
+            xk = *(const uint4*)(khead + (size_t)(k0 + pr) * D + 8 * pc);
+            xv = *(const uint4*)(vhead + (size_t)(k0 + pr) * D + 8 * pc);
         }
+        info = 0;
+        if (tid < BT && k0 + tid < T) {
+            const int gk = k0 + tid;
+            const int sg = a.seg ? a.seg[(size_t)b * T + gk] : 1;
+            const bool sk = a.prefix ? (a.prefix[(size_t)b * T + gk] != 0) : false;
+            info = pack_key_info(sg, sk);
+        }
+    };
+    int kind = 0, tile = 0;
+    bool have = it.next(kind, tile);
+    uint4 ck = make_uint4(0, 0, 0, 0), cv = ck;
+    int cinfo = 0;
+    if (have) fetch(tile * BT, ck, cv, cinfo);
+    while (have) {
+        const int k0 = tile * BT;
+        int kn = 0, tn = 0;
+        const bool have_next = it.next(kn, tn);
+        __syncthreads();  // every wave is done with the previous tile
+        if (mover) {
+            *(uint4*)&sm.k.x[pr * Bf16Tile<D>::RS + 8 * pc] = ck;
+            *(uint4*)&sm.v.x[pr * Bf16Tile<D>::RS + 8 * pc] = cv;
+        }
+        if (tid < BT) sm.kinfo[tid] = cinfo;
         __syncthreads();
+        if (have_next) fetch(tn * BT, ck, cv, cinfo);
+        tile = tn;
+        have = have_next;
         if (!wave_on) continue;
         // S^T = K Q'^T, started from the mask: -lse log2 e where visible, -inf elsewhere
         f32x16 sacc;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int kk = 8 * (j >> 2) + (j & 3) + 4 * h;  // key of element j within the tile
-            const bool vis = row_vis && k0 + kk < T && visible_full(my_q - (k0 + kk), wlim, sm.kinfo[kk], seg_q);
-            sacc[j] = vis ? nl : kNegInf;
+        for (int i = 0; i < 4; ++i) {
+            // keys 8i + 4h + r of the tile (r = 0..3: elements 4i + r), their infos in one read
+            const u32x4 inf = lds_load128(lds_off(&sm.kinfo[8 * i + 4 * h]));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kk = 8 * i + 4 * h + r;
+                const bool vis = row_vis && k0 + kk < T && visible_full(my_q - (k0 + kk), wlim, (int)inf[r], seg_q);
+                sacc[4 * i + r] = vis ? nl : kNegInf;
+            }
         }
         f32x16 dpa = f32x16{};
 #pragma unroll
@@ -604,9 +631,9 @@ template <int D>
 struct SmemDkvMfma {
     struct Wave {
         Bf16Tile<D> q, go;
-        float lse2[32];  // lse * log2 e of the tile's queries (-inf: none)
-        float dlt[32];
-        int seg[32];
+        __attribute__((aligned(16))) float lse2[32];  // lse * log2 e of the tile's queries (-inf: none)
+        __attribute__((aligned(16))) float dlt[32];
+        __attribute__((aligned(16))) int seg[32];
     } w[4];
 };
 
@@ -682,15 +709,22 @@ __global__ __launch_bounds__(256) void bwd_dkv_mfma_kernel(BwdArgs a, const uint
             f32x16 sacc;
             float dl[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int qi = 8 * (j >> 2) + (j & 3) + 4 * h;
-                const int tq = t0 + qi;
-                const int sq = ws.seg[qi];
-                const float l2 = ws.lse2[qi];
-                dl[j] = ws.dlt[qi];
-                const bool vis = key_ok && tq < T && sq > 0 && l2 != kNegInf &&
-                                 visible_full(tq - my_k, wlim, info_k, sq);
-                sacc[j] = vis ? -l2 : kNegInf;
+            for (int i = 0; i < 4; ++i) {
+                // queries 8i + 4h + r of the tile (elements 4i + r): one read per array
+                const u32x4 sg4 = lds_load128(lds_off(&ws.seg[8 * i + 4 * h]));
+                const u32x4 l24 = lds_load128(lds_off(&ws.lse2[8 * i + 4 * h]));
+                const u32x4 dl4 = lds_load128(lds_off(&ws.dlt[8 * i + 4 * h]));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qi = 8 * i + 4 * h + r;
+                    const int tq = t0 + qi;
+                    const int sq = (int)sg4[r];
+                    const float l2 = __uint_as_float(l24[r]);
+                    dl[4 * i + r] = __uint_as_float(dl4[r]);
+                    const bool vis = key_ok && tq < T && sq > 0 && l2 != kNegInf &&
+                                     visible_full(tq - my_k, wlim, info_k, sq);
+                    sacc[4 * i + r] = vis ? -l2 : kNegInf;
+                }
             }
             f32x16 dpa = f32x16{};
 #pragma unroll
