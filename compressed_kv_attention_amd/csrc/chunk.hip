@@ -9,29 +9,33 @@
 // chunks of 4096 tokens) without defining the step; this is its plainest
 // reading.
 //
-// The attention itself is the bf16 prefill kernel, run over a staged key
-// sequence of Tv = S + W - 1 + Tc rows per (batch row, kv head):
+// The attention itself is the bf16 prefill kernel over a key sequence of
+// Tv = C + Tc rows per (batch row, kv head), C = S + W - 1 rounded up to 64:
 //   rows [0, S)            sink rows (prefix, segment 1) up to sink_len,
 //                          padding (segment 0) after it;
-//   rows [S, S + W - 1)    ring positions pos0 - W + 1 .. pos0 - 1, in order,
+//   rows [S, C - W + 1)    padding (at most 63 rows);
+//   rows [C - W + 1, C)    ring positions pos0 - W + 1 .. pos0 - 1, in order,
 //                          padding where the ring holds no such position;
-//   rows [S + W - 1, Tv)   the chunk.
+//   rows [C, Tv)           the chunk.
 // Ring and chunk rows are contiguous in position, so the kernel's window test
 // on row indices is the test on positions; the sinks are visible as prefix
-// keys; padding rows are in no segment.  Cached rows are dequantized (code x
-// scale in fp32, then rounded to bf16) as they are staged.  The staged query
-// rows before the chunk are zero and their outputs are not copied out.
+// keys; padding rows are in no segment.  Only the C cached rows are staged
+// (dequantized: code x scale in fp32, then rounded to bf16); the kernel reads
+// the chunk's keys and values, and its queries, where the caller keeps them,
+// and writes the output in place (its query rows start at C, its keys switch
+// source at C).
+#include <algorithm>
+
 #include "swa_common.h"
 #include "swa_internal.h"
 
 namespace swa {
 namespace {
 
-// One (row j of the staged sequence, batch row b, kv head) per 64-lane block:
-// lane d < D moves channel d of K and V.
-__global__ __launch_bounds__(64) void chunk_stage_kv_kernel(ChunkArgs a, uint16_t* ks, uint16_t* vs, int32_t* seg,
-                                                            uint8_t* prefix) {
-    const int j = blockIdx.x;
+// One (cached row j, batch row b, kv head) per 64-lane block: lane d < D
+// moves channel d of K and V.
+__global__ __launch_bounds__(64) void chunk_stage_kv_kernel(ChunkArgs a, uint16_t* ks, uint16_t* vs) {
+    const int j = blockIdx.x;   // < C
     const int bh = blockIdx.y;  // b * Hkv + hkv
     const int b = bh / a.Hkv;
     const int d = threadIdx.x;
@@ -39,28 +43,24 @@ __global__ __launch_bounds__(64) void chunk_stage_kv_kernel(ChunkArgs a, uint16_
     const int p0 = a.pos0[b] > 0 ? a.pos0[b] : 0;
     int sl = a.sink_len ? a.sink_len[b] : S;
     sl = max(0, min(min(sl, S), p0));
-    const int ring0 = S, chunk0 = S + W - 1;
-    int kind = 0;  // 0 padding, 1 sink, 2 ring, 3 chunk
+    const int ring0 = a.C - (W - 1);
+    int kind = 0;  // 0 padding, 1 sink, 2 ring
     long long src = 0;
-    if (j < ring0) {
+    if (j < S) {
         if (j < sl) {
             kind = 1;
             src = (long long)bh * S + j;
         }
-    } else if (j < chunk0) {
+    } else if (j >= ring0) {
         const int p = p0 - (W - 1) + (j - ring0);
         if (p >= sl && p >= 0) {
             kind = 2;
             src = (long long)bh * W + (p % W);
         }
-    } else {
-        kind = 3;
-        src = (long long)bh * a.Tc + (j - chunk0);
     }
-    const size_t dst = ((size_t)bh * a.Tv + j) * D;
     if (d < D) {
         uint16_t kb = 0, vb = 0;
-        if (kind == 1 || kind == 2) {
+        if (kind != 0) {
             const int8_t* kc = kind == 1 ? a.sink_k : a.ring_k;
             const int8_t* vc = kind == 1 ? a.sink_v : a.ring_v;
             const float* kss = kind == 1 ? a.sink_ks : a.ring_ks;
@@ -69,49 +69,37 @@ __global__ __launch_bounds__(64) void chunk_stage_kv_kernel(ChunkArgs a, uint16_
             const float vf = (float)vc[src * D + d] * vss[src * (D / 32) + d / 32];
             kb = (uint16_t)f32_to_bf16_bits(kf);
             vb = (uint16_t)f32_to_bf16_bits(vf);
-        } else if (kind == 3) {
-            kb = ((const uint16_t*)a.k)[src * D + d];
-            vb = ((const uint16_t*)a.v)[src * D + d];
         }
+        const size_t dst = ((size_t)bh * a.C + j) * D;
         ks[dst + d] = kb;
         vs[dst + d] = vb;
     }
-    if (bh % a.Hkv == 0 && d == 0) {
-        seg[(size_t)b * a.Tv + j] = kind != 0 ? 1 : 0;
-        prefix[(size_t)b * a.Tv + j] = kind == 1 ? 1 : 0;
-    }
 }
 
-// The staged queries: zero before the chunk, the chunk's rows after it.  One
-// thread per 16 bytes.
-__global__ void chunk_stage_q_kernel(ChunkArgs a, uint4* qs) {
-    const int per_row = a.D / 8;  // 16-byte pieces per row
-    const long long total = (long long)a.B * a.Hq * a.Tv * per_row;
-    const int chunk0 = a.S + a.W - 1;
+// Segment ids and prefix flags of the key sequence, one thread per (b, row):
+// sinks up to sink_len and held ring positions in segment 1 (sinks flagged),
+// the chunk in segment 1, padding in segment 0.
+__global__ void chunk_stage_meta_kernel(ChunkArgs a, int32_t* seg, uint8_t* prefix) {
+    const long long total = (long long)a.B * a.Tv;
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (long long)gridDim.x * blockDim.x) {
-        const int c = (int)(i % per_row);
-        const long long row = i / per_row;  // (b * Hq + h) * Tv + j
-        const int j = (int)(row % a.Tv);
-        const long long bh = row / a.Tv;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (j >= chunk0) x = ((const uint4*)a.q)[(bh * a.Tc + (j - chunk0)) * per_row + c];
-        qs[i] = x;
-    }
-}
-
-// The chunk's rows of the staged output into `out`.
-__global__ void chunk_copy_out_kernel(ChunkArgs a, const uint4* os) {
-    const int per_row = a.D / 8;
-    const long long total = (long long)a.B * a.Hq * a.Tc * per_row;
-    const int chunk0 = a.S + a.W - 1;
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (long long)gridDim.x * blockDim.x) {
-        const int c = (int)(i % per_row);
-        const long long row = i / per_row;  // (b * Hq + h) * Tc + t
-        const long long bh = row / a.Tc;
-        const int t = (int)(row % a.Tc);
-        ((uint4*)a.out)[i] = os[(bh * a.Tv + chunk0 + t) * per_row + c];
+        const int b = (int)(i / a.Tv);
+        const int j = (int)(i - (long long)b * a.Tv);
+        const int p0 = a.pos0[b] > 0 ? a.pos0[b] : 0;
+        int sl = a.sink_len ? a.sink_len[b] : a.S;
+        sl = max(0, min(min(sl, a.S), p0));
+        const int ring0 = a.C - (a.W - 1);
+        int kind = 0;
+        if (j >= a.C) {
+            kind = 3;
+        } else if (j < a.S) {
+            kind = j < sl ? 1 : 0;
+        } else if (j >= ring0) {
+            const int p = p0 - (a.W - 1) + (j - ring0);
+            kind = (p >= sl && p >= 0) ? 2 : 0;
+        }
+        seg[i] = kind != 0 ? 1 : 0;
+        prefix[i] = kind == 1 ? 1 : 0;
     }
 }
 
@@ -144,26 +132,27 @@ __global__ __launch_bounds__(64) void chunk_ring_write_kernel(ChunkArgs a, int f
 }  // namespace
 
 hipError_t launch_chunk_stage(const ChunkArgs& a, void* k_stage, void* v_stage, int32_t* seg, uint8_t* prefix,
-                              void* q_stage, hipStream_t s) {
-    hipLaunchKernelGGL(chunk_stage_kv_kernel, dim3((unsigned)a.Tv, (unsigned)(a.B * a.Hkv)), dim3(64), 0, s, a,
-                       (uint16_t*)k_stage, (uint16_t*)v_stage, seg, prefix);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_stage_q_kernel, dim3(2048), dim3(256), 0, s, a, (uint4*)q_stage);
+                              hipStream_t s) {
+    if (a.C > 0) {
+        hipLaunchKernelGGL(chunk_stage_kv_kernel, dim3((unsigned)a.C, (unsigned)(a.B * a.Hkv)), dim3(64), 0, s, a,
+                           (uint16_t*)k_stage, (uint16_t*)v_stage);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const long long n = (long long)a.B * a.Tv;
+    const unsigned blocks = (unsigned)std::min<long long>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(chunk_stage_meta_kernel, dim3(blocks), dim3(256), 0, s, a, seg, prefix);
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_finish(const ChunkArgs& a, const void* out_stage, hipStream_t s) {
-    hipLaunchKernelGGL(chunk_copy_out_kernel, dim3(2048), dim3(256), 0, s, a, (const uint4*)out_stage);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t launch_chunk_finish(const ChunkArgs& a, hipStream_t s) {
     const int first = a.Tc > a.W ? a.Tc - a.W : 0;
     if (a.Tc - first > 0) {
         hipLaunchKernelGGL(chunk_ring_write_kernel, dim3((unsigned)(a.Tc - first), (unsigned)(a.B * a.Hkv)), dim3(64),
                            0, s, a, first);
-        e = hipGetLastError();
+        return hipGetLastError();
     }
-    return e;
+    return hipSuccess;
 }
 
 }  // namespace swa

@@ -123,17 +123,23 @@ constexpr int kMetaWave = 1 % kMfmaWaves;
 struct TileBases {
     const char* k;      // exact keys: row 0 of this head
     const char* v;
+    const char* k2;     // split keys: row kv_split of this head (or null)
+    const char* v2;
     const char* pk;     // pooled keys (compressed mode)
     const char* pv;
     const char* info;   // packed key info of this batch row (or null)
     const char* ksub;   // sub-tile summaries of this batch row
 };
-template <int D>
+template <int D, bool SPLIT>
 __device__ __forceinline__ TileBases tile_bases(const PrefillArgs& a, int b, int hkv) {
     TileBases t;
     const size_t head = (size_t)b * a.Hkv + hkv;
-    t.k = (const char*)((const uint16_t*)a.k + head * (size_t)a.T * D);
-    t.v = (const char*)((const uint16_t*)a.v + head * (size_t)a.T * D);
+    const size_t t1 = (size_t)(SPLIT ? a.kv_split : a.T);  // rows per head of the first source
+    t.k = (const char*)((const uint16_t*)a.k + head * t1 * D);
+    t.v = (const char*)((const uint16_t*)a.v + head * t1 * D);
+    const size_t t2 = (size_t)(a.T - a.kv_split);
+    t.k2 = SPLIT ? (const char*)((const uint16_t*)a.k2 + head * t2 * D) : nullptr;
+    t.v2 = SPLIT ? (const char*)((const uint16_t*)a.v2 + head * t2 * D) : nullptr;
     t.pk = a.pk ? (const char*)((const uint16_t*)a.pk + head * (size_t)a.nblk * D) : nullptr;
     t.pv = a.pv ? (const char*)((const uint16_t*)a.pv + head * (size_t)a.nblk * D) : nullptr;
     t.info = a.kinfo ? (const char*)(a.kinfo + (size_t)b * a.T) : nullptr;
@@ -146,7 +152,7 @@ __device__ __forceinline__ TileBases tile_bases(const PrefillArgs& a, int b, int
 // metadata, wave 0 also moves the keys' packed info and kMetaWave the two
 // sub-tile summaries.  Rows past the last key load the last key's row
 // (finite data, masked later).
-template <int D, bool DUMP>
+template <int D, bool DUMP, bool SPLIT>
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TileBases& tb, SmemBf16<D>& sm, uint32_t koff,
                                            uint32_t voff, int buf, int kind, int tile, int wave, int lane) {
     using TL = TileLoads<D>;
@@ -158,6 +164,11 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TileBases
     const size_t toff = (size_t)k0 * D * 2;
     const char* kb = (pooled ? tb.pk : tb.k) + toff;
     const char* vb = (pooled ? tb.pv : tb.v) + toff;
+    if (SPLIT && !pooled && k0 >= a.kv_split) {  // a tile of the second source (kv_split is a multiple of BN)
+        const size_t off2 = (size_t)(k0 - a.kv_split) * D * 2;
+        kb = tb.k2 + off2;
+        vb = tb.v2 + off2;
+    }
     if (DUMP) {
         // the mask alone: no K or V (the visibility dump is given no tensors)
     } else if (k0 + BN <= nkeys) {
@@ -300,7 +311,7 @@ struct DumpOut {
     int32_t* count;  // [B, T] visible columns per row
 };
 
-template <int D, bool ROPE, bool COMPRESSED, bool DUMP>
+template <int D, bool ROPE, bool COMPRESSED, bool DUMP, bool SPLIT>
 __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_bf16_kernel(
     PrefillArgs a, DumpOut dump) {
     static_assert(D == 32 || D == 64, "head dim");
@@ -334,7 +345,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const int hg = bh - b * (int)a.div_hg.d;
     const int hkv = (int)fdiv((uint32_t)hg, a.div_groups);
     const int hsub = hg - hkv * (int)a.div_groups.d;
-    const int q0 = qb * wg_rows;
+    const int q_first = SPLIT ? a.q_first : 0;
+    const int q0 = q_first + qb * wg_rows;
     const int q1 = min(q0 + wg_rows - 1, T - 1);
     const int wrb = (int)fdiv((uint32_t)wave, a.div_hpw);  // row block of this wave
     const int my_h = hkv * G + hsub * a.hpw + (wave - wrb * a.hpw);
@@ -342,6 +354,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const bool wave_active = wave < a.hpw * a.rbs && r0 < T;
     const int my_q = r0 + lq;
     const bool row_ok = my_q < T;
+    // q, out and lse hold rows q_first .. T - 1 of each head
+    const int Tq = T - q_first;
+    const size_t qhead = ((size_t)b * a.Hq + my_h) * Tq;
     constexpr bool plain = !COMPRESSED;
     // scale * log2 e, folded into q (one rounding of q to bf16)
     const float c_log2 = a.scale * kLog2e;
@@ -357,8 +372,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     SWA_TRACE(11);
     TileLoads<D> tl;
     tl.init(wave, lane);
-    const TileBases tb = tile_bases<D>(a, b, hkv);
-    if (have0) issue_tile<D, DUMP>(a, tb, sm, tl.koff, tl.voff, 0, kc, tc, wave, lane);
+    const TileBases tb = tile_bases<D, SPLIT>(a, b, hkv);
+    if (have0) issue_tile<D, DUMP, SPLIT>(a, tb, sm, tl.koff, tl.voff, 0, kc, tc, wave, lane);
     // one 32-row block per workgroup: the table rows go through LDS, once
     const bool tab_lds = ROPE && a.rbs == 1;
     if (tab_lds) issue_rope_rows<D>(a, sm, q0, wave, lane);
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     uint4 raw[D / 16];
     if (q_lds) {
         if (wave_active) {
-            const void* qbase = (const uint16_t*)a.q + (((size_t)b * a.Hq + my_h) * T + r0) * D;
+            const void* qbase = (const uint16_t*)a.q + (qhead + (r0 - q_first)) * D;
 #pragma unroll
             for (int i = 0; i < 32 / QRPI; ++i) {
                 const int r = i * QRPI + lane / QCPR, pc = lane % QCPR;
@@ -388,7 +403,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) raw[c] = make_uint4(0, 0, 0, 0);
     } else {
-        const uint16_t* qrow = (const uint16_t*)a.q + (((size_t)b * a.Hq + my_h) * T + (row_ok ? my_q : 0)) * D;
+        const uint16_t* qrow = (const uint16_t*)a.q + (qhead + (row_ok ? my_q - q_first : 0)) * D;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
             raw[c] = (!DUMP && row_ok) ? *(const uint4*)(qrow + 16 * c + 8 * h) : make_uint4(0, 0, 0, 0);
@@ -566,7 +581,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         const int nxt = cur ^ 1;
         int kn = 0, tn = 0;
         const bool have_next = it.next(kn, tn);
-        if (have_next) issue_tile<D, DUMP>(a, tb, sm, tl.koff, tl.voff, nxt, kn, tn, wave, lane);
+        if (have_next) issue_tile<D, DUMP, SPLIT>(a, tb, sm, tl.koff, tl.voff, nxt, kn, tn, wave, lane);
         SWA_TRACE(1);
 
         if (wave_active) {
@@ -879,18 +894,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         }
         lds_reads_done();  // (also the writes: the LDS wait covers both)
         constexpr int RPI = 64 / CPR;  // rows per store instruction
-        uint16_t* ohead = (uint16_t*)a.out + ((size_t)b * a.Hq + my_h) * T * D;
+        uint16_t* ohead = (uint16_t*)a.out + qhead * D;
 #pragma unroll
         for (int j = 0; j < 32 / RPI; ++j) {
             const int r = j * RPI + lane / CPR, c = lane % CPR;
             const u32x4 x = lds_load128(ob + (uint32_t)(r * CPR + (c ^ (r % CPR))) * 16u);
-            if (r0 + r < T) *(u32x4*)(ohead + (size_t)(r0 + r) * D + 8 * c) = x;
+            if (r0 + r < T) *(u32x4*)(ohead + (size_t)(r0 + r - q_first) * D + 8 * c) = x;
         }
     }
     if (row_ok) {
         // lse = base / log2 e + ln(l) (base is in log2 units of the scaled scores)
         if (a.lse && h == 0)
-            a.lse[((size_t)b * a.Hq + my_h) * T + my_q] = l_tot > 0.f ? base * 0.6931471805599453f + __logf(l_tot)
+            a.lse[qhead + (my_q - q_first)] = l_tot > 0.f ? base * 0.6931471805599453f + __logf(l_tot)
                                                                       : kNegInf;
     }
     SWA_TRACE(5);
@@ -902,7 +917,7 @@ hipError_t launch_bf16(const PrefillArgs& args, DumpOut dump, hipStream_t s) {
     PrefillArgs a = args;
     const int G = a.Hq / a.Hkv;
     const int wg_rows = 32 * a.rbs;
-    const int nqb = (a.T + wg_rows - 1) / wg_rows;
+    const int nqb = (a.T - a.q_first + wg_rows - 1) / wg_rows;
     const long long nblocks = (long long)nqb * a.Hkv * (G / a.hpw) * a.B;
     if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     a.div_nqb = make_fastdiv((uint32_t)nqb);
@@ -914,8 +929,14 @@ hipError_t launch_bf16(const PrefillArgs& args, DumpOut dump, hipStream_t s) {
     dim3 block(64 * kMfmaWaves);
     const bool rope = !DUMP && a.rope_len > 0;
     const bool comp = a.block > 0;
-#define SWA_LAUNCH(DD, RR, CC) hipLaunchKernelGGL((prefill_bf16_kernel<DD, RR, CC, DUMP>), grid, block, 0, s, a, dump)
-    if (a.D == 64) {
+#define SWA_LAUNCH(DD, RR, CC) \
+    hipLaunchKernelGGL((prefill_bf16_kernel<DD, RR, CC, DUMP, false>), grid, block, 0, s, a, dump)
+    if (!DUMP && a.k2 != nullptr) {  // split sources: plain mode, no rotation
+        if (a.D == 64)
+            hipLaunchKernelGGL((prefill_bf16_kernel<64, false, false, false, true>), grid, block, 0, s, a, dump);
+        else
+            hipLaunchKernelGGL((prefill_bf16_kernel<32, false, false, false, true>), grid, block, 0, s, a, dump);
+    } else if (a.D == 64) {
         if (comp) {
             if (rope) SWA_LAUNCH(64, !DUMP, true);
             else SWA_LAUNCH(64, false, true);

@@ -145,13 +145,35 @@ size_t swa_prefill_workspace_size(const swa_prefill_params* p) {
     return key_meta_layout(p).total + rotated_key_bytes(p) + 2 * pooled_bytes(p);
 }
 
-int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, const void* v, const void* pooled_k,
-                     const void* pooled_v, const int32_t* seg_ids, const uint8_t* prefix, const float* rope_cos,
-                     const float* rope_sin, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+// Sources of a prefill whose queries and keys are not one [T] sequence each:
+// the queries (and outputs) hold rows q_first .. T - 1; keys before kv_split
+// come from the call's k / v (kv_split rows per head), the rest from k2 / v2.
+struct SplitSources {
+    int q_first, kv_split;
+    const void* k2;
+    const void* v2;
+};
+
+int prefill_run(const swa_prefill_params* p, const void* q, const void* k, const void* v, const void* pooled_k,
+                const void* pooled_v, const int32_t* seg_ids, const uint8_t* prefix, const float* rope_cos,
+                const float* rope_sin, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                const SplitSources* split) {
     swa::PrefillArgs a;
     int rc = check_prefill(p, seg_ids, prefix, a);
     if (rc != SWA_OK) return rc;
+    if (split != nullptr) {
+        REQUIRE(p->dtype == SWA_BF16 && p->rope_len == 0 && p->compress_block == 0 && split->q_first % 64 == 0 &&
+                    split->kv_split % 64 == 0 && split->q_first <= p->T && split->kv_split <= p->T &&
+                    split->k2 != nullptr && split->v2 != nullptr,
+                "split prefill sources out of range");
+        a.q_first = split->q_first;
+        a.kv_split = split->kv_split;
+        a.k2 = split->k2;
+        a.v2 = split->v2;
+    }
     if (p->B == 0 || p->T == 0) return ok();
     REQUIRE_PTR(q);
     REQUIRE_PTR(k);
@@ -257,6 +279,17 @@ int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, 
     if (kr) a.k = kr;
     const hipError_t e = p->dtype == SWA_BF16 ? swa::launch_prefill_bf16(a, s) : swa::launch_prefill_f32(a, s);
     return hip_status(e, "swa_attn_prefill launch");
+}
+}  // namespace
+
+extern "C" {
+
+int swa_attn_prefill(const swa_prefill_params* p, const void* q, const void* k, const void* v, const void* pooled_k,
+                     const void* pooled_v, const int32_t* seg_ids, const uint8_t* prefix, const float* rope_cos,
+                     const float* rope_sin, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    return prefill_run(p, q, k, v, pooled_k, pooled_v, seg_ids, prefix, rope_cos, rope_sin, out, lse, workspace,
+                       workspace_bytes, stream, nullptr);
 }
 
 int swa_debug_visibility(const swa_prefill_params* p, const int32_t* seg_ids, const uint8_t* prefix,
@@ -706,24 +739,26 @@ int swa_attn_prefill_backward(const swa_prefill_params* p, const void* q, const 
 }  // extern "C"
 
 namespace {
-// Workspace layout of a chunked prefill: staged q, k, v, out, segment ids,
-// prefix flags, then the prefill workspace of the staged sequence.
+// Workspace layout of a chunked prefill: the staged cached rows of k and v
+// (C = S + W - 1 rounded up to 64 per kv head), segment ids and prefix flags
+// of the C + Tc keys, then the prefill workspace of that key sequence.
 struct ChunkLayout {
-    size_t q, k, v, out, seg, prefix, pf, pf_bytes, total;
+    size_t k, v, seg, prefix, pf, pf_bytes, total;
+    int C;
     swa_prefill_params pp;
 };
 bool chunk_layout(const swa_chunk_params* p, ChunkLayout& L) {
     if (p == nullptr || p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->D <= 0 || p->W < 1 || p->S < 0 || p->Tc <= 0)
         return false;
-    const long long Tv = (long long)p->S + p->W - 1 + p->Tc;
+    const long long C = ((long long)p->S + p->W - 1 + 63) / 64 * 64;
+    const long long Tv = C + p->Tc;
     if (Tv > swa::kMaxT) return false;
+    L.C = (int)C;
     L.pp = swa_prefill_params{p->B, p->Hq, p->Hkv, (int)Tv, p->D, p->W, 0, 0, p->scale, SWA_BF16};
-    const size_t qb = (size_t)p->B * p->Hq * Tv * p->D * 2, kb = (size_t)p->B * p->Hkv * Tv * p->D * 2;
-    L.q = 0;
-    L.k = L.q + round256(qb);
+    const size_t kb = (size_t)p->B * p->Hkv * C * p->D * 2;
+    L.k = 0;
     L.v = L.k + round256(kb);
-    L.out = L.v + round256(kb);
-    L.seg = L.out + round256(qb);
+    L.seg = L.v + round256(kb);
     L.prefix = L.seg + round256((size_t)p->B * Tv * 4);
     L.pf = L.prefix + round256((size_t)p->B * Tv);
     L.pf_bytes = swa_prefill_workspace_size(&L.pp);
@@ -751,9 +786,10 @@ int swa_attn_chunk_prefill(const swa_chunk_params* p, const void* q, const void*
     REQUIRE(p->S >= 0, "S must be >= 0 (got %d)", p->S);
     REQUIRE(p->scale >= 0.f && std::isfinite(p->scale), "scale must be finite and >= 0");
     if (p->D != 32 && p->D != 64) return fail(SWA_ERR_UNSUPPORTED, "head dim D=%d is not built (32 or 64)", p->D);
-    if ((long long)p->S + p->W - 1 + p->Tc > swa::kMaxT)
-        return fail(SWA_ERR_UNSUPPORTED, "S + W - 1 + Tc = %lld exceeds the supported %d",
-                    (long long)p->S + p->W - 1 + p->Tc, swa::kMaxT);
+    const long long cached = ((long long)p->S + p->W - 1 + 63) / 64 * 64;
+    if (cached + p->Tc > swa::kMaxT)
+        return fail(SWA_ERR_UNSUPPORTED, "S + W - 1 (rounded up to 64) + Tc = %lld exceeds the supported %d",
+                    cached + p->Tc, swa::kMaxT);
     if ((long long)p->B * p->Hkv > 65535)
         return fail(SWA_ERR_UNSUPPORTED, "B * Hkv = %lld exceeds 65535", (long long)p->B * p->Hkv);
     if (p->B == 0 || p->Tc == 0) return ok();
@@ -800,17 +836,20 @@ int swa_attn_chunk_prefill(const swa_chunk_params* p, const void* q, const void*
     a.W = p->W;
     a.S = p->S;
     a.Tc = p->Tc;
+    a.C = L.C;
     a.Tv = L.pp.T;
     char* ws = (char*)workspace;
     const hipStream_t s = (hipStream_t)stream;
-    hipError_t e = swa::launch_chunk_stage(a, ws + L.k, ws + L.v, (int32_t*)(ws + L.seg), (uint8_t*)(ws + L.prefix),
-                                           ws + L.q, s);
+    hipError_t e = swa::launch_chunk_stage(a, ws + L.k, ws + L.v, (int32_t*)(ws + L.seg), (uint8_t*)(ws + L.prefix), s);
     if (e != hipSuccess) return hip_status(e, "swa_attn_chunk_prefill staging launch");
-    const int rc = swa_attn_prefill(&L.pp, ws + L.q, ws + L.k, ws + L.v, nullptr, nullptr, (const int32_t*)(ws + L.seg),
-                                    (const uint8_t*)(ws + L.prefix), nullptr, nullptr, ws + L.out, nullptr,
-                                    L.pf_bytes ? ws + L.pf : nullptr, L.pf_bytes, stream);
+    // queries and outputs in place (rows C .. Tv - 1 of the key sequence); keys
+    // switch from the staged cached rows to the caller's chunk at row C
+    const SplitSources split{L.C, L.C, k, v};
+    const int rc = prefill_run(&L.pp, q, ws + L.k, ws + L.v, nullptr, nullptr, (const int32_t*)(ws + L.seg),
+                               (const uint8_t*)(ws + L.prefix), nullptr, nullptr, out, nullptr,
+                               L.pf_bytes ? ws + L.pf : nullptr, L.pf_bytes, stream, &split);
     if (rc != SWA_OK) return rc;
-    e = swa::launch_chunk_finish(a, ws + L.out, s);
+    e = swa::launch_chunk_finish(a, s);
     return hip_status(e, "swa_attn_chunk_prefill ring write launch");
 }
 

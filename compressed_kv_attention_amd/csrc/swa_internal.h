@@ -58,6 +58,15 @@ struct PrefillArgs {
     // query blocks, head groups per batch row (Hkv * G / hpw), head groups per
     // kv head (G / hpw), hpw, and the compress block
     FastDiv div_nqb, div_hg, div_groups, div_hpw, div_block;
+    // Split sources (bf16 kernel only; zero and null otherwise): the query
+    // rows start at q_first, so q, out and lse hold rows q_first .. T - 1 of
+    // each head; with k2 set, key rows from kv_split on come from k2 / v2,
+    // which hold rows kv_split .. T - 1 of each kv head.  Both are multiples
+    // of 64.
+    int q_first = 0;
+    int kv_split = 0;
+    const void* k2 = nullptr;
+    const void* v2 = nullptr;
 };
 
 // Geometry the bf16 MFMA kernel uses for a given GQA group size: 4 waves per
@@ -276,14 +285,16 @@ struct ChunkArgs {
     const int32_t* pos0;
     const int32_t* sink_len;
     void* out;  // [B][Hq][Tc][D] bf16
-    int B, Hq, Hkv, D, W, S, Tc, Tv;
+    int B, Hq, Hkv, D, W, S, Tc;
+    int C;   // cached rows of the key sequence: S + W - 1 rounded up to 64
+    int Tv;  // C + Tc
 };
-// Stage K/V (sink and ring rows dequantized, the chunk copied), the segment and
-// prefix arrays of the staged sequence, and the staged queries.
+// Stage the cached rows of K/V (sink and ring rows dequantized, padding zero)
+// and the segment and prefix arrays of the whole key sequence.
 hipError_t launch_chunk_stage(const ChunkArgs& a, void* k_stage, void* v_stage, int32_t* seg, uint8_t* prefix,
-                              void* q_stage, hipStream_t s);
-// Copy the chunk's rows of the staged output out, then write the ring.
-hipError_t launch_chunk_finish(const ChunkArgs& a, const void* out_stage, hipStream_t s);
+                              hipStream_t s);
+// Quantize the chunk's last min(W, Tc) tokens into the ring.
+hipError_t launch_chunk_finish(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // Largest split-K state swa_attn_decode_noalloc holds (its device array).
 constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;

@@ -307,18 +307,20 @@ int swa_nsa_select_attn(const swa_prefill_params* p, int n_select,
 /* swa_kv_quantize) into ring slots position % W.  Precondition: the ring    */
 /* holds positions pos0[b] - W .. pos0[b] - 1 (those >= sl), as after a      */
 /* decode or a chunk that ended at pos0[b] - 1.  Negative pos0 counts as 0.  */
-/* Cached rows are dequantized and rounded to bf16 for the MFMA attention.   */
+/* Cached rows are dequantized and rounded to bf16 for the MFMA attention;   */
+/* q, k, v are read and out written in place.                              */
 typedef struct {
     int B, Hq, Hkv, D; /* D in {32, 64}; Hq % Hkv == 0; B * Hkv <= 65535      */
     int W;             /* ring capacity = window length, >= 1                   */
     int S;             /* sink cache capacity, >= 0                             */
-    int Tc;            /* chunk length, >= 0; S + W - 1 + Tc <= 131072          */
+    int Tc;            /* chunk length, >= 0; C + Tc <= 131072 with C =        */
+                       /* S + W - 1 rounded up to a multiple of 64             */
     float scale;       /* 0 selects 1/sqrt(D)                                   */
 } swa_chunk_params;
 
-/* Bytes of workspace swa_attn_chunk_prefill needs (staged queries, keys,   */
-/* values and outputs of S + W - 1 + Tc rows, their segment and prefix      */
-/* arrays, and the prefill workspace of that sequence).                     */
+/* Bytes of workspace swa_attn_chunk_prefill needs (the C cached rows of   */
+/* keys and values per kv head, dequantized to bf16; segment ids and prefix */
+/* flags of the C + Tc keys; the prefill workspace of that key sequence).   */
 size_t swa_chunk_prefill_workspace_size(const swa_chunk_params* p);
 
 int swa_attn_chunk_prefill(const swa_chunk_params* p,

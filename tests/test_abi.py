@@ -424,10 +424,12 @@ def test_chunk_prefill_validation_and_workspace():
     L = swa.lib()
     size = lambda **kw: L.swa_chunk_prefill_workspace_size(ctypes.byref(swa.ChunkParams(**dict(
         dict(B=2, Hq=4, Hkv=2, D=64, W=8, S=5, Tc=13, scale=0.0), **kw))))
-    Tv = 5 + 8 - 1 + 13
+    C = 64                     # S + W - 1 = 12 cached rows, rounded up to 64
+    Tv = C + 13
     r = lambda x: (x + 255) // 256 * 256
     pf = L.swa_prefill_workspace_size(ctypes.byref(swa.PrefillParams(2, 4, 2, Tv, 64, 8, 0, 0, 0.0, swa.SWA_BF16)))
-    assert size() == 2 * r(2 * 4 * Tv * 64 * 2) + 2 * r(2 * 2 * Tv * 64 * 2) + r(2 * Tv * 4) + r(2 * Tv) + r(pf)
+    assert size() == 2 * r(2 * 2 * C * 64 * 2) + r(2 * Tv * 4) + r(2 * Tv) + r(pf)
+    assert size(S=52, W=13) == size(S=64, W=1) < size(S=65, W=1)   # C = 64, 64, 128
     assert size(Tc=0) == 0 and size(W=0) == 0
     args = [FAKE] * 14        # q, k, v, ring x4, sink x4, pos0, sink_len, out
     p = swa.ChunkParams(2, 4, 2, 64, 8, 5, 13, 0.0)

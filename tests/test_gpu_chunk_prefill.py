@@ -73,6 +73,9 @@ def check(w, what):
     (64, 1, 4, 40, [4, 50, 77], [4, 2, 4]),        # window 1: every token sees sinks and itself
     (32, 37, 11, 129, [11, 300, 48], [11, 11, 6]), # odd sizes, several 64-key tiles, ragged tail
     (64, 256, 256, 1, [256, 5000, 40000], [256, 100, 256]),  # one token
+    (64, 1, 0, 70, [0, 5, 130], [0, 0, 0]),        # no cached rows at all: the chunk alone
+    (32, 65, 0, 100, [0, 64, 1000], [0, 0, 0]),    # cached part exactly 64 rows (no padding)
+    (64, 33, 32, 65, [32, 40, 700], [32, 17, 32]), # sinks + ring exactly 64 rows
 ])
 def test_chunk_prefill_small(D, W, S, Tc, pos0, sink_len):
     w = workloads.chunk_case(seed=D + W + Tc, B=3, Hq=4, Hkv=2, D=D, W=W, S=S, Tc=Tc, sink_len=sink_len)
