@@ -404,6 +404,8 @@ def main():
         parts["packed"] = make_prefill("packed", workloads.packed())
     if "compressed16" in parts_wanted:
         parts["compressed16"] = make_compressed("compressed16", 16)
+    if "causal" in parts_wanted:  # (not in the default set) plain causal B4 16q/4kv T4096, no window
+        parts["causal"] = make_prefill("causal", workloads.causal())
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s")
 

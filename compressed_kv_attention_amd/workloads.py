@@ -128,6 +128,16 @@ def packed(seed=3, B=16, Hq=16, Hkv=4, T=4096, D=64, window=256):
     return w
 
 
+def causal(seed=8, B=4, Hq=16, Hkv=4, T=4096, D=64, window=0):
+    """Plain causal GQA prefill (one segment, no sinks, no RoPE; window 0 = none): the kernel on long
+    fully visible spans, for measurement beside the windowed workloads."""
+    rng = np.random.default_rng(seed)
+    w = _qkv(rng, B, Hq, Hkv, T, D, "bf16")
+    w.update(dict(B=B, Hq=Hq, Hkv=Hkv, T=T, D=D, window=window, dtype="bf16", seg_ids=None,
+                  prefix=None, rope_theta=0.0, compress_block=0, seed=seed))
+    return w
+
+
 def compressed(block=4, dtype="bf16", seed=4, B=4, H=8, T=4096, D=64, window=256):
     rng = np.random.default_rng(seed)
     w = _qkv(rng, B, H, H, T, D, dtype)
