@@ -431,17 +431,29 @@ struct Bf16Tile {
     static constexpr int RS = D + 8;  // row stride in bf16
     uint16_t x[32 * RS];
 };
-// Copy 32 rows (src + r * D, rows >= nrows read as zero) into a tile, 16
-// bytes per thread per step, by threads tid of nthreads (a multiple of 64).
+// The 32 rows (src + r * D, rows >= nrows read as zero) of a tile, 16 bytes
+// per lane per piece, as one wave loads them: every load is issued before any
+// of the stores below, so staging a tile costs one memory round trip.
 template <int D>
-__device__ __forceinline__ void stage_rows(Bf16Tile<D>& t, const uint16_t* src, int nrows, int tid, int nthreads) {
-    constexpr int CPR = D / 8;  // 16-byte pieces per row
-    for (int piece = tid; piece < 32 * CPR; piece += nthreads) {
-        const int r = piece / CPR, c = piece % CPR;
-        const uint4 x = r < nrows ? *(const uint4*)(src + (size_t)r * D + 8 * c) : make_uint4(0, 0, 0, 0);
-        *(uint4*)&t.x[r * Bf16Tile<D>::RS + 8 * c] = x;
+struct TileRows {
+    static constexpr int CPR = D / 8;           // 16-byte pieces per row
+    static constexpr int PER = 32 * CPR / 64;   // pieces per lane
+    uint4 x[PER];
+    __device__ __forceinline__ void load(const uint16_t* src, int nrows, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int piece = lane + 64 * i, r = piece / CPR, c = piece % CPR;
+            x[i] = r < nrows ? *(const uint4*)(src + (size_t)r * D + 8 * c) : make_uint4(0, 0, 0, 0);
+        }
     }
-}
+    __device__ __forceinline__ void store(Bf16Tile<D>& t, int lane) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int piece = lane + 64 * i, r = piece / CPR, c = piece % CPR;
+            *(uint4*)&t.x[r * Bf16Tile<D>::RS + 8 * c] = x[i];
+        }
+    }
+};
 // Operand of the sub-tile's rows (A operand: row l % 32, channels 16c + 8 (l / 32) ..).
 template <int D>
 __device__ __forceinline__ bf16x8 tile_row(const Bf16Tile<D>& t, int c, int lane) {
@@ -635,6 +647,8 @@ struct SmemDkvMfma {
         __attribute__((aligned(16))) float dlt[32];
         __attribute__((aligned(16))) int seg[32];
     } w[4];
+    // query tiles past the band holding rows of the block's sink segments
+    uint32_t qbits[(kMaxT / BT + 31) / 32];
 };
 
 // dk, dv: a workgroup of four waves per 32 keys of one kv head; wave w walks
@@ -676,7 +690,44 @@ __global__ __launch_bounds__(256) void bwd_dkv_mfma_kernel(BwdArgs a, const uint
     const bool has_sink = a.window != 0 && __ballot(key_ok && sink_k && seg_k > 0) != 0;
     const int sk_lo = wave_imin_xor(key_ok && sink_k && seg_k > 0 ? seg_k : 0x7fffffff, 1, 32);
     const int sk_hi = wave_imax_xor(key_ok && sink_k && seg_k > 0 ? seg_k : (int)0x80000000, 1, 32);
-    const int last = has_sink ? T - 1 : band_end;
+    // Query tiles past the band matter only where one of their rows is in a
+    // sink segment of the block: one scan of the rows' segment ids by the
+    // whole workgroup (every wave has the same keys, so the same has_sink)
+    // marks those tiles in a bit set, eight independent loads per thread at a
+    // time.
+    const int ntiles = (T + BT - 1) / BT;
+    const int tile_end = band_end / BT;  // the band's last tile
+    if (has_sink) {
+        for (int i = tid; i < (ntiles + 31) / 32; i += 256) sm.qbits[i] = 0u;
+        __syncthreads();
+        for (int r0 = (tile_end + 1) * BT; r0 < T; r0 += 256 * 8) {
+            int sq[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = r0 + 256 * u + tid;
+                sq[u] = r < T ? (a.seg ? a.seg[(size_t)b * T + r] : 1) : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = r0 + 256 * u + tid;
+                if (r < T && sq[u] >= sk_lo && sq[u] <= sk_hi)
+                    atomicOr(&sm.qbits[(r / BT) >> 5], 1u << ((r / BT) & 31));
+            }
+        }
+        __syncthreads();
+    }
+    // the tile after t0: the next band tile, then the marked tiles in order; -1 at the end
+    auto next_tile = [&](int t) -> int {
+        if (t + BT <= band_end) return t + BT;
+        if (!has_sink) return -1;
+        int k = max(t / BT + 1, tile_end + 1);
+        while (k < ntiles) {
+            const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.qbits[k >> 5]) >> (k & 31);
+            if (m != 0u) return (k + __builtin_ctz(m)) * BT;
+            k = ((k >> 5) + 1) << 5;
+        }
+        return -1;
+    };
     f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) {
@@ -686,23 +737,22 @@ __global__ __launch_bounds__(256) void bwd_dkv_mfma_kernel(BwdArgs a, const uint
     for (int g = wave; g < G; g += 4) {
         const int hq = hkv * G + g;
         const size_t qhead = ((size_t)b * a.Hq + hq) * (size_t)T;
-        for (int t0 = (s0 / BT) * BT; t0 <= last; t0 += BT) {
-            // a tile past the band matters only if one of its rows is in a sink segment of the block
-            if (t0 > band_end) {
-                const int tq = t0 + lq;
-                const int sq = tq < T ? (a.seg ? a.seg[(size_t)b * T + tq] : 1) : 0;
-                if (__ballot(sq >= sk_lo && sq <= sk_hi) == 0) continue;
-            }
+        for (int t0 = s0; t0 >= 0; t0 = next_tile(t0)) {
             // this wave's tiles (its own LDS; its reads of the previous tile are done,
-            // LDS accesses of a wave complete in order)
-            stage_rows<D>(ws.q, qs + (qhead + t0) * D, T - t0, lane, 64);
-            stage_rows<D>(ws.go, (const uint16_t*)a.dout + (qhead + t0) * D, T - t0, lane, 64);
+            // LDS accesses of a wave complete in order): all loads, then all stores
+            TileRows<D> rq, ro;
+            rq.load(qs + (qhead + t0) * D, T - t0, lane);
+            ro.load((const uint16_t*)a.dout + (qhead + t0) * D, T - t0, lane);
+            const int tq = t0 + (lane & 31);
+            const float l = tq < T ? a.lse[qhead + tq] : kNegInf;
+            const float dlt = tq < T ? delta[qhead + tq] : 0.f;
+            const int sgq = tq < T ? (a.seg ? a.seg[(size_t)b * T + tq] : 1) : 0;
+            rq.store(ws.q, lane);
+            ro.store(ws.go, lane);
             if (lane < BT) {
-                const int tq = t0 + lane;
-                const float l = tq < T ? a.lse[qhead + tq] : kNegInf;
                 ws.lse2[lane] = l == kNegInf ? kNegInf : l * kLog2e;
-                ws.dlt[lane] = tq < T ? delta[qhead + tq] : 0.f;
-                ws.seg[lane] = tq < T ? (a.seg ? a.seg[(size_t)b * T + tq] : 1) : 0;
+                ws.dlt[lane] = dlt;
+                ws.seg[lane] = sgq;
             }
             lds_reads_done();
             // S = Q' K^T from the mask (element j: query 8 (j / 4) + j % 4 + 4h of the tile)
