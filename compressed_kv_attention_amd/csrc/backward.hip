@@ -656,7 +656,7 @@ struct SmemDkvMfma {
 // the group (each wave stages its own tiles), and the four waves' sums are
 // added in head order at the end.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkv_mfma_kernel(BwdArgs a, const uint16_t* qs, const uint16_t* kr,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_mfma_kernel(BwdArgs a, const uint16_t* qs, const uint16_t* kr,
                                                            const float* delta) {
     constexpr int NC = D / 16;
     __shared__ __align__(16) SmemDkvMfma<D> sm;
@@ -737,16 +737,24 @@ __global__ __launch_bounds__(256) void bwd_dkv_mfma_kernel(BwdArgs a, const uint
     for (int g = wave; g < G; g += 4) {
         const int hq = hkv * G + g;
         const size_t qhead = ((size_t)b * a.Hq + hq) * (size_t)T;
-        for (int t0 = s0; t0 >= 0; t0 = next_tile(t0)) {
+        // A tile's rows, lse, delta and segment ids are loaded into registers
+        // one tile ahead: the next tile's loads are issued as soon as the
+        // current tile is in LDS, and land while it is computed.
+        TileRows<D> rq, ro;
+        float l = 0.f, dlt = 0.f;
+        int sgq = 0;
+        auto fetch = [&](int t) {
+            rq.load(qs + (qhead + t) * D, T - t, lane);
+            ro.load((const uint16_t*)a.dout + (qhead + t) * D, T - t, lane);
+            const int tq = t + (lane & 31);
+            l = tq < T ? a.lse[qhead + tq] : kNegInf;
+            dlt = tq < T ? delta[qhead + tq] : 0.f;
+            sgq = tq < T ? (a.seg ? a.seg[(size_t)b * T + tq] : 1) : 0;
+        };
+        fetch(s0);
+        for (int t0 = s0; t0 >= 0;) {
             // this wave's tiles (its own LDS; its reads of the previous tile are done,
-            // LDS accesses of a wave complete in order): all loads, then all stores
-            TileRows<D> rq, ro;
-            rq.load(qs + (qhead + t0) * D, T - t0, lane);
-            ro.load((const uint16_t*)a.dout + (qhead + t0) * D, T - t0, lane);
-            const int tq = t0 + (lane & 31);
-            const float l = tq < T ? a.lse[qhead + tq] : kNegInf;
-            const float dlt = tq < T ? delta[qhead + tq] : 0.f;
-            const int sgq = tq < T ? (a.seg ? a.seg[(size_t)b * T + tq] : 1) : 0;
+            // LDS accesses of a wave complete in order)
             rq.store(ws.q, lane);
             ro.store(ws.go, lane);
             if (lane < BT) {
@@ -754,6 +762,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_mfma_kernel(BwdArgs a, const uint
                 ws.dlt[lane] = dlt;
                 ws.seg[lane] = sgq;
             }
+            const int tn = next_tile(t0);
+            if (tn >= 0) fetch(tn);
             lds_reads_done();
             // S = Q' K^T from the mask (element j: query 8 (j / 4) + j % 4 + 4h of the tile)
             f32x16 sacc;
@@ -798,6 +808,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_mfma_kernel(BwdArgs a, const uint
                     dva[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(ws.go, m, n, lane), pb[m], dva[n], 0, 0, 0);
                     dka[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(ws.q, m, n, lane), db[m], dka[n], 0, 0, 0);
                 }
+            t0 = tn;
         }
     }
     // the four waves' sums, added in head order through LDS (the tile space,
