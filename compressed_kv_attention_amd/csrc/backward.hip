@@ -498,7 +498,9 @@ struct SmemDqMfma {
 // forward's walk over key tiles of 32 (band first, then the tiles holding
 // visible sinks).
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(BwdArgs a, const uint16_t* qs, const uint16_t* kr,
+// (four waves per SIMD: a launch of the needle's size then fits in one round,
+// at the cost of a few registers kept in scratch)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void bwd_dq_mfma_kernel(BwdArgs a, const uint16_t* qs, const uint16_t* kr,
                                                           const float* delta) {
     constexpr int NC = D / 16;
     __shared__ __align__(16) SmemDqMfma<D> sm;
@@ -656,6 +658,8 @@ struct SmemDkvMfma {
 // the group (each wave stages its own tiles), and the four waves' sums are
 // added in head order at the end.
 template <int D>
+// (two waves per SIMD: the compiler keeps every value, the next tile's rows
+// included, in registers)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_mfma_kernel(BwdArgs a, const uint16_t* qs, const uint16_t* kr,
                                                            const float* delta) {
     constexpr int NC = D / 16;
