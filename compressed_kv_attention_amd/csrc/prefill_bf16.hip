@@ -370,6 +370,30 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     int kc = 0, tc = 0;  // tile being computed
     const bool have0 = it.next(kc, tc);
     SWA_TRACE(11);
+    // The rows' segment ids and the sink-tile summaries first (the first
+    // values the prologue waits for), then the tile, table and q loads.  The
+    // loads are unconditional, from clamped addresses, with the values
+    // selected afterwards: a load under a divergent branch is waited for where
+    // the branch ends.  (Sink tiles before the band: tiles whose sinks belong
+    // to a segment of the workgroup's rows; the prep pass gives each tile's
+    // sink segment range, and every wave loads the rows' segment ids, at most
+    // 128 rows, itself.)
+    // (each branch only loads into a variable given its default before it, so
+    // that no value is waited for until it is used)
+    const int32_t* seg_row = a.seg ? a.seg + (size_t)b * T : nullptr;
+    int seg_ld = 1;
+    if (seg_row) seg_ld = seg_row[min(my_q, T - 1)];
+    const int n_sink_tiles = plan.sink_keys / BN;
+    const bool scan = n_sink_tiles > 0;
+    int s0v = 1, s1v = 1;
+    int2 tv = make_int2(0x7fffffff, (int)0x80000000);
+    if (scan) {
+        if (seg_row) {
+            s0v = seg_row[min(q0 + lane, q1)];
+            s1v = seg_row[min(q0 + 64 + lane, q1)];
+        }
+        tv = *(const int2*)(a.tsink + ((size_t)b * a.ntile + min(lane, n_sink_tiles - 1)) * 2);
+    }
     TileLoads<D> tl;
     tl.init(wave, lane);
     const TileBases tb = tile_bases<D, SPLIT>(a, b, hkv);
@@ -421,21 +445,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
             rsn[c][1] = *(const float4*)(sn + 4);
         }
     }
-    int seg_q = 0;
-    if (row_ok) seg_q = a.seg ? a.seg[(size_t)b * T + my_q] : 1;
-    // Sink tiles before the band: tiles whose sinks belong to a segment of the
-    // workgroup's rows (the prep pass gives each tile's sink segment range).
-    // Every wave loads the rows' segment ids (at most 128 rows) itself.
-    const int n_sink_tiles = plan.sink_keys / BN;
-    const bool scan = n_sink_tiles > 0;
-    int rseg0 = 0x7fffffff, rseg1 = 0x7fffffff;
-    int2 tsk = make_int2(0x7fffffff, (int)0x80000000);
-    if (scan) {
-        const int32_t* seg_row = a.seg ? a.seg + (size_t)b * T : nullptr;
-        if (q0 + lane <= q1) rseg0 = seg_row ? seg_row[q0 + lane] : 1;
-        if (q0 + 64 + lane <= q1) rseg1 = seg_row ? seg_row[q0 + 64 + lane] : 1;
-        if (lane < n_sink_tiles) tsk = *(const int2*)(a.tsink + ((size_t)b * a.ntile + lane) * 2);
-    }
+    const int seg_q = row_ok ? seg_ld : 0;
 
 
     SWA_TRACE(7);
@@ -451,6 +461,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         __builtin_amdgcn_ballot_w64(row_ok && seg_q > 0 && seg_q != rs.smin && seg_q != rs.smax) == 0;
 
     if (scan) {
+        const int rseg0 = q0 + lane <= q1 ? s0v : 0x7fffffff;
+        const int rseg1 = q0 + 64 + lane <= q1 ? s1v : 0x7fffffff;
+        int2 tsk = lane < n_sink_tiles ? tv : make_int2(0x7fffffff, (int)0x80000000);
         const int lo = max(1, wave_min_i32(min(rseg0, rseg1)));
         const int hi = wave_max_i32(max(rseg0 == 0x7fffffff ? (int)0x80000000 : rseg0,
                                          rseg1 == 0x7fffffff ? (int)0x80000000 : rseg1));
