@@ -443,12 +443,20 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs p) {
     const int b = (int)(gt / p.ntile), j = (int)(gt % p.ntile);
     const int t = 64 * j + lane;
     const bool valid = t < p.T;
-    int info = 0;
-    if (valid) {
-        const size_t i = (size_t)b * p.T + t;
-        info = pack_key_info(p.seg ? p.seg[i] : 1, p.prefix ? p.prefix[i] != 0 : false);
-        p.info[i] = info;
+    // both loads unconditional (clamped key index) and issued together; the
+    // values are selected afterwards
+    const size_t ic = (size_t)b * p.T + min(t, p.T - 1);
+    int sgv = 1, pfv = 0;
+    if (p.seg && p.prefix) {
+        sgv = p.seg[ic];
+        pfv = p.prefix[ic];
+    } else if (p.seg) {
+        sgv = p.seg[ic];
+    } else {
+        pfv = p.prefix[ic];
     }
+    const int info = valid ? pack_key_info(sgv, pfv != 0) : 0;
+    if (valid) p.info[(size_t)b * p.T + t] = info;
     const int sg = info & 0x7fffffff;
     const bool sk = info < 0;
     const int half = lane >> 5;
