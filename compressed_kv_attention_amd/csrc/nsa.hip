@@ -202,21 +202,31 @@ __global__ __launch_bounds__(64) void nsa_select_kernel(NsaArgs a, const X* krot
     }
     const float* pkh = pk32 + ((size_t)b * a.Hkv + hkv) * (size_t)a.nblk * D;
     const uint32_t tl = lds_off(tile);
+    // Pooled keys j0 .. j0 + 31, lane (m, kk) loading channels [H kk, H kk + H)
+    // of key m: every load from a clamped address, the values selected when
+    // stored; the next tile's loads are issued as soon as the current tile is
+    // in LDS, and land while it is scored and inserted.
+    float4 xs[H / 4];
+    auto fetch = [&](int j) {
+        const float* src = pkh + (size_t)min(j + n, a.nblk - 1) * D + H * kk;
+#pragma unroll
+        for (int c4 = 0; c4 < H / 4; ++c4) xs[c4] = *(const float4*)(src + 4 * c4);
+    };
+    if (n_max > 0) fetch(0);
     for (int j0 = 0; j0 < n_max; j0 += 32) {
-        // stage pooled keys j0 .. j0 + 31: lane (m, kk) copies channels
-        // [H kk, H kk + H) of key m, split by channel parity (row m holds the
-        // even channels, then the odd ones)
+        // stage pooled keys j0 .. j0 + 31, split by channel parity (row m
+        // holds the even channels, then the odd ones)
         {
             const int jj = j0 + n;
-            const float* src = pkh + (size_t)min(jj, a.nblk - 1) * D + H * kk;
 #pragma unroll
             for (int c4 = 0; c4 < H / 4; ++c4) {
-                const float4 x = jj < a.nblk ? *(const float4*)(src + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float4 x = jj < a.nblk ? xs[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
                 const int c = H * kk + 4 * c4;  // even
                 lds_store64(tl + (uint32_t)(n * RS + c / 2) * 4u, u32x2{__float_as_uint(x.x), __float_as_uint(x.z)});
                 lds_store64(tl + (uint32_t)(n * RS + H + c / 2) * 4u, u32x2{__float_as_uint(x.y), __float_as_uint(x.w)});
             }
         }
+        if (j0 + 32 < n_max) fetch(j0 + 32);
         lds_reads_done();  // (LDS writes and reads of the wave complete in order; the wait also covers the writes)
         f32x16 acc{};
 #pragma unroll
