@@ -98,6 +98,46 @@ __device__ __forceinline__ void load_half(const uint16_t* p, float (&x)[H]) {
     }
 }
 
+// Half a row as loaded (16-byte pieces), converted to fp32 where it is used.
+template <class X, int H>
+struct HalfRow;
+template <int H>
+struct HalfRow<float, H> {
+    float4 v[H / 4];
+    __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+        for (int i = 0; i < H / 4; ++i) v[i] = ((const float4*)p)[i];
+    }
+    __device__ __forceinline__ void to(float (&x)[H]) const {
+#pragma unroll
+        for (int i = 0; i < H / 4; ++i) {
+            x[4 * i] = v[i].x;
+            x[4 * i + 1] = v[i].y;
+            x[4 * i + 2] = v[i].z;
+            x[4 * i + 3] = v[i].w;
+        }
+    }
+};
+template <int H>
+struct HalfRow<uint16_t, H> {
+    uint4 v[H / 8];
+    __device__ __forceinline__ void load(const uint16_t* p) {
+#pragma unroll
+        for (int i = 0; i < H / 8; ++i) v[i] = ((const uint4*)p)[i];
+    }
+    __device__ __forceinline__ void to(float (&x)[H]) const {
+#pragma unroll
+        for (int i = 0; i < H / 8; ++i) {
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[8 * i + 2 * e] = __uint_as_float(w[e] << 16);
+                x[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            }
+        }
+    }
+};
+
 // Pooled keys: the mean of block j's keys before RoPE (rows added in order),
 // rotated at min(j b + b/2, rope_len - 1).
 template <class X>
@@ -332,19 +372,37 @@ __global__ __launch_bounds__(64) void nsa_select_kernel(NsaArgs a, const X* krot
     float m = kNegInf, l = 0.f, o[H];
 #pragma unroll
     for (int d = 0; d < H; ++d) o[d] = 0.f;
+    // The chosen tokens in list order, each token's K and V half rows loaded
+    // while the previous token is used.  Every lane walks the list to the
+    // longest one in the wave (an entry a lane does not have reads a valid row
+    // and weighs nothing), so no load sits under a divergent branch.
+    const int nsel = min(a.n_select, kTopK);
+    HalfRow<X, H> nk, nv;
+    {
+        const size_t r0 = (size_t)(nsel > 0 && ti[0] >= 0 ? ti[0] : 0) * a.block;
+        nk.load(kh + r0 * D);
+        nv.load(vh + r0 * D);
+    }
 #pragma unroll
     for (int i = 0; i < kTopK; ++i) {
-        if (i >= a.n_select || ti[i] < 0) continue;
+        // (lists hold their valid entries first)
+        if (i >= nsel || __builtin_amdgcn_ballot_w64(ti[i] >= 0) == 0) break;
+        const bool vi = ti[i] >= 0;
+        const int bi = vi ? ti[i] : 0;
+        const int bn = (i + 1 < kTopK && i + 1 < nsel && ti[i + 1 < kTopK ? i + 1 : i] >= 0) ? ti[i + 1 < kTopK ? i + 1 : i] : 0;
         for (int u = 0; u < a.block; ++u) {
-            const size_t r = (size_t)ti[i] * a.block + u;
+            const HalfRow<X, H> ck = nk, cv = nv;
+            const size_t rn = u + 1 < a.block ? (size_t)bi * a.block + u + 1 : (size_t)bn * a.block;
+            nk.load(kh + rn * D);
+            nv.load(vh + rn * D);
             float kx[H], vx[H];
-            load_half<H>(kh + r * D, kx);
-            load_half<H>(vh + r * D, vx);
+            ck.to(kx);
+            cv.to(vx);
             float dot = 0.f;
 #pragma unroll
             for (int d = 0; d < H; ++d) dot = fmaf(qA[d], kx[d], dot);
             const float other = __shfl_xor(dot, 32, 64);
-            const float s = (kk ? other + dot : dot + other) * a.scale;
+            const float s = vi ? (kk ? other + dot : dot + other) * a.scale : kNegInf;
             if (s > m) {
                 const float corr = expf(m - s);
                 m = s;
@@ -352,7 +410,7 @@ __global__ __launch_bounds__(64) void nsa_select_kernel(NsaArgs a, const X* krot
 #pragma unroll
                 for (int d = 0; d < H; ++d) o[d] *= corr;
             }
-            const float p = expf(s - m);
+            const float p = vi ? expf(s - m) : 0.f;
             l += p;
 #pragma unroll
             for (int d = 0; d < H; ++d) o[d] = fmaf(p, vx[d], o[d]);
