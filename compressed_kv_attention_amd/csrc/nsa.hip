@@ -48,6 +48,32 @@ __device__ __forceinline__ void st_x<float>(float* p, float v) { *p = v; }
 template <>
 __device__ __forceinline__ void st_x<uint16_t>(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
 
+// Eight consecutive elements (16-byte aligned) in fp32, and back in the
+// element type (bf16 rounded to nearest even, as st_x does).
+__device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
+    const float4 u = ((const float4*)p)[0], v = ((const float4*)p)[1];
+    x[0] = u.x, x[1] = u.y, x[2] = u.z, x[3] = u.w, x[4] = v.x, x[5] = v.y, x[6] = v.z, x[7] = v.w;
+}
+__device__ __forceinline__ void ld8(const uint16_t* p, float (&x)[8]) {
+    const uint4 v = *(const uint4*)p;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(w[e] << 16);
+        x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void st8(float* p, const float (&x)[8]) {
+    ((float4*)p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    ((float4*)p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void st8(uint16_t* p, const float (&x)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = f32_to_bf16_bits(x[2 * e]) | (f32_to_bf16_bits(x[2 * e + 1]) << 16);
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Exact keys rotated at their position, in the input dtype (bf16 keys are
 // rounded once after the fp32 rotation, as the key pre-pass of a prefill
 // does): one thread per (row, 8 channel pairs).
@@ -63,13 +89,20 @@ __global__ __launch_bounds__(256) void nsa_rotate_keys_kernel(NsaArgs a, X* kr) 
     const int p = min(t, a.rope_len - 1);
     const X* src = (const X*)a.k + row * D;
     X* dst = kr + row * D;
+    // 16-byte accesses: the 8 channels of each half and their table entries
+    float x1[8], x2[8], c[8], sn[8];
+    ld8(src + i0, x1);
+    ld8(src + half + i0, x2);
+    ld8(a.rope_cos + (size_t)p * half + i0, c);
+    ld8(a.rope_sin + (size_t)p * half + i0, sn);
+    float y1[8], y2[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float x1 = ld_f(src, i0 + e), x2 = ld_f(src, half + i0 + e);
-        const float c = a.rope_cos[(size_t)p * half + i0 + e], sn = a.rope_sin[(size_t)p * half + i0 + e];
-        st_x(dst + i0 + e, x1 * c - x2 * sn);
-        st_x(dst + half + i0 + e, x2 * c + x1 * sn);
+        y1[e] = x1[e] * c[e] - x2[e] * sn[e];
+        y2[e] = x2[e] * c[e] + x1[e] * sn[e];
     }
+    st8(dst + i0, y1);
+    st8(dst + half + i0, y2);
 }
 
 // Half a row (channels [0, H) from p) in fp32.
@@ -141,21 +174,53 @@ struct HalfRow<uint16_t, H> {
 // Pooled keys: the mean of block j's keys before RoPE (rows added in order),
 // rotated at min(j b + b/2, rope_len - 1).
 template <class X>
-__global__ __launch_bounds__(64) void nsa_prep_pooled_kernel(NsaArgs a, float* pk32) {
-    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x, D = a.D, d = lane % D;
-    const size_t head = ((size_t)b * a.Hkv + h) * a.T;
-    float sum = 0.f;
-    for (int u = 0; u < a.block; ++u) sum += ld_f((const X*)a.k, (head + (size_t)j * a.block + u) * D + d);
-    float x = sum / (float)a.block;
-    if (a.rope_cos) {
-        const float other = __shfl_xor(x, D / 2, 64);
-        const int i = d % (D / 2);
-        const int p = min(j * a.block + a.block / 2, a.rope_len - 1);
-        const float c = a.rope_cos[(size_t)p * (D / 2) + i], s = a.rope_sin[(size_t)p * (D / 2) + i];
-        x = d < D / 2 ? x * c - other * s : x * c + other * s;
+__global__ __launch_bounds__(256) void nsa_prep_pooled_kernel(NsaArgs a, float* pk32) {
+    // one thread per (pooled key, 8 channel pairs): channels i0 .. i0 + 7 and
+    // their rotate-half partners, 16 bytes per access
+    const int D = a.D, half = D / 2, per = half / 8;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total = (long long)a.B * a.Hkv * a.nblk * per;
+    if (idx >= total) return;
+    const long long key = idx / per;  // ((b * Hkv + h) * nblk + j)
+    const int i0 = (int)(idx - key * per) * 8;
+    const long long n = key / a.nblk;
+    const int j = (int)(key - n * a.nblk);
+    const X* src = (const X*)a.k + ((size_t)n * a.T + (size_t)j * a.block) * D;
+    float s1[8], s2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s1[e] = s2[e] = 0.f;
+#pragma unroll 4
+    for (int u = 0; u < a.block; ++u) {  // rows added in order
+        float x1[8], x2[8];
+        ld8(src + (size_t)u * D + i0, x1);
+        ld8(src + (size_t)u * D + half + i0, x2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s1[e] += x1[e];
+            s2[e] += x2[e];
+        }
     }
-    if (lane < D) pk32[(((size_t)b * a.Hkv + h) * a.nblk + j) * D + d] = x;
+    float y1[8], y2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        y1[e] = s1[e] / (float)a.block;
+        y2[e] = s2[e] / (float)a.block;
+    }
+    if (a.rope_cos) {
+        const int p = min(j * a.block + a.block / 2, a.rope_len - 1);
+        float c[8], sn[8];
+        ld8(a.rope_cos + (size_t)p * half + i0, c);
+        ld8(a.rope_sin + (size_t)p * half + i0, sn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float r1 = y1[e] * c[e] - y2[e] * sn[e];
+            const float r2 = y2[e] * c[e] + y1[e] * sn[e];
+            y1[e] = r1;
+            y2[e] = r2;
+        }
+    }
+    st8(pk32 + key * D + i0, y1);
+    st8(pk32 + key * D + half + i0, y2);
 }
 
 // One wave per 32 query rows of one head; lanes n and n + 32 share row n.
@@ -446,9 +511,10 @@ hipError_t launch_nsa_t(const NsaArgs& a, void* krot_ws, float* pk32, hipStream_
                            (X*)krot_ws);
         krot = (const X*)krot_ws;
     }
-    if (a.nblk > 0)
-        hipLaunchKernelGGL(nsa_prep_pooled_kernel<X>, dim3((unsigned)a.nblk, (unsigned)a.Hkv, (unsigned)a.B), dim3(64),
-                           0, s, a, pk32);
+    if (a.nblk > 0) {
+        const long long n = (long long)a.B * a.Hkv * a.nblk * (a.D / 16);
+        hipLaunchKernelGGL(nsa_prep_pooled_kernel<X>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, pk32);
+    }
     const long long nwg = (long long)((a.T + 31) / 32) * a.Hq * a.B;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)nwg), blk(64);
