@@ -24,83 +24,89 @@
 // the chunk's keys and values, and its queries, where the caller keeps them,
 // and writes the output in place (its query rows start at C, its keys switch
 // source at C).
-#include <algorithm>
-
 #include "swa_common.h"
 #include "swa_internal.h"
 
 namespace swa {
 namespace {
 
-// One (cached row j, batch row b, kv head) per 64-lane block: lane d < D
-// moves channel d of K and V.
-__global__ __launch_bounds__(64) void chunk_stage_kv_kernel(ChunkArgs a, uint16_t* ks, uint16_t* vs) {
-    const int j = blockIdx.x;   // < C
-    const int bh = blockIdx.y;  // b * Hkv + hkv
+// Where cached row j of batch row b comes from: kind 0 padding, 1 sink row
+// src of the sink cache, 2 ring slot src; src counts rows of the (batch row,
+// kv head) bh's cache.
+struct CachedRow {
+    int kind;
+    long long src;
+};
+__device__ __forceinline__ CachedRow cached_row(const ChunkArgs& a, int j, int bh) {
     const int b = bh / a.Hkv;
-    const int d = threadIdx.x;
-    const int D = a.D, W = a.W, S = a.S;
     const int p0 = a.pos0[b] > 0 ? a.pos0[b] : 0;
-    int sl = a.sink_len ? a.sink_len[b] : S;
-    sl = max(0, min(min(sl, S), p0));
-    const int ring0 = a.C - (W - 1);
-    int kind = 0;  // 0 padding, 1 sink, 2 ring
-    long long src = 0;
-    if (j < S) {
-        if (j < sl) {
-            kind = 1;
-            src = (long long)bh * S + j;
-        }
+    int sl = a.sink_len ? a.sink_len[b] : a.S;
+    sl = max(0, min(min(sl, a.S), p0));
+    const int ring0 = a.C - (a.W - 1);
+    CachedRow r{0, 0};
+    if (j < a.S) {
+        if (j < sl) r = CachedRow{1, (long long)bh * a.S + j};
     } else if (j >= ring0) {
-        const int p = p0 - (W - 1) + (j - ring0);
-        if (p >= sl && p >= 0) {
-            kind = 2;
-            src = (long long)bh * W + (p % W);
-        }
+        const int p = p0 - (a.W - 1) + (j - ring0);
+        if (p >= sl && p >= 0) r = CachedRow{2, (long long)bh * a.W + (p % a.W)};
     }
-    if (d < D) {
-        uint16_t kb = 0, vb = 0;
-        if (kind != 0) {
-            const int8_t* kc = kind == 1 ? a.sink_k : a.ring_k;
-            const int8_t* vc = kind == 1 ? a.sink_v : a.ring_v;
-            const float* kss = kind == 1 ? a.sink_ks : a.ring_ks;
-            const float* vss = kind == 1 ? a.sink_vs : a.ring_vs;
-            const float kf = (float)kc[src * D + d] * kss[src * (D / 32) + d / 32];
-            const float vf = (float)vc[src * D + d] * vss[src * (D / 32) + d / 32];
-            kb = (uint16_t)f32_to_bf16_bits(kf);
-            vb = (uint16_t)f32_to_bf16_bits(vf);
-        }
-        const size_t dst = ((size_t)bh * a.C + j) * D;
-        ks[dst + d] = kb;
-        vs[dst + d] = vb;
-    }
+    return r;
 }
 
-// Segment ids and prefix flags of the key sequence, one thread per (b, row):
-// sinks up to sink_len and held ring positions in segment 1 (sinks flagged),
-// the chunk in segment 1, padding in segment 0.
-__global__ void chunk_stage_meta_kernel(ChunkArgs a, int32_t* seg, uint8_t* prefix) {
-    const long long total = (long long)a.B * a.Tv;
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (long long)gridDim.x * blockDim.x) {
-        const int b = (int)(i / a.Tv);
-        const int j = (int)(i - (long long)b * a.Tv);
-        const int p0 = a.pos0[b] > 0 ? a.pos0[b] : 0;
-        int sl = a.sink_len ? a.sink_len[b] : a.S;
-        sl = max(0, min(min(sl, a.S), p0));
-        const int ring0 = a.C - (a.W - 1);
-        int kind = 0;
-        if (j >= a.C) {
-            kind = 3;
-        } else if (j < a.S) {
-            kind = j < sl ? 1 : 0;
-        } else if (j >= ring0) {
-            const int p = p0 - (a.W - 1) + (j - ring0);
-            kind = (p >= sl && p >= 0) ? 2 : 0;
+// One launch stages everything.  Blocks below kv_blocks: one thread per
+// (batch row, kv head, cached row j, 16 channels) dequantizes K and V (code x
+// scale in fp32, rounded to bf16), 16-byte accesses; padding rows are zero.
+// The other blocks: one thread per (batch row, key) writes the segment id
+// and prefix flag -- sinks up to sink_len and held ring positions in segment
+// 1 (sinks flagged), the chunk in segment 1, padding in segment 0.
+__global__ __launch_bounds__(256) void chunk_stage_kernel(ChunkArgs a, uint16_t* ks, uint16_t* vs, int32_t* seg,
+                                                          uint8_t* prefix, int kv_blocks) {
+    if ((int)blockIdx.x < kv_blocks) {
+        const int D = a.D, per = D / 16;
+        const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+        if (idx >= (long long)a.B * a.Hkv * a.C * per) return;
+        const int d0 = 16 * (int)(idx % per);
+        const long long rowid = idx / per;  // bh * C + j
+        const int j = (int)(rowid % a.C);
+        const int bh = (int)(rowid / a.C);
+        const CachedRow r = cached_row(a, j, bh);
+        uint32_t kw[8] = {0, 0, 0, 0, 0, 0, 0, 0}, vw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (r.kind != 0) {
+            const int8_t* kc = r.kind == 1 ? a.sink_k : a.ring_k;
+            const int8_t* vc = r.kind == 1 ? a.sink_v : a.ring_v;
+            const float* kss = r.kind == 1 ? a.sink_ks : a.ring_ks;
+            const float* vss = r.kind == 1 ? a.sink_vs : a.ring_vs;
+            const uint4 kq = *(const uint4*)(kc + r.src * D + d0);
+            const uint4 vq = *(const uint4*)(vc + r.src * D + d0);
+            const float sk = kss[r.src * (D / 32) + d0 / 32], sv = vss[r.src * (D / 32) + d0 / 32];
+            const uint32_t kq4[4] = {kq.x, kq.y, kq.z, kq.w}, vq4[4] = {vq.x, vq.y, vq.z, vq.w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    // codes of channels 4w + 2h and 4w + 2h + 1 (bytes 2h, 2h + 1), sign-extended
+                    const int k0 = (int)(kq4[w] << (24 - 16 * h)) >> 24, k1 = (int)(kq4[w] << (16 - 16 * h)) >> 24;
+                    const int v0 = (int)(vq4[w] << (24 - 16 * h)) >> 24, v1 = (int)(vq4[w] << (16 - 16 * h)) >> 24;
+                    kw[2 * w + h] = f32_to_bf16_bits((float)k0 * sk) | (f32_to_bf16_bits((float)k1 * sk) << 16);
+                    vw[2 * w + h] = f32_to_bf16_bits((float)v0 * sv) | (f32_to_bf16_bits((float)v1 * sv) << 16);
+                }
+            }
         }
-        seg[i] = kind != 0 ? 1 : 0;
-        prefix[i] = kind == 1 ? 1 : 0;
+        const size_t dst = ((size_t)bh * a.C + j) * D + d0;
+        *(uint4*)(ks + dst) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+        *(uint4*)(ks + dst + 8) = make_uint4(kw[4], kw[5], kw[6], kw[7]);
+        *(uint4*)(vs + dst) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+        *(uint4*)(vs + dst + 8) = make_uint4(vw[4], vw[5], vw[6], vw[7]);
+        return;
     }
+    const long long i = (long long)(blockIdx.x - kv_blocks) * 256 + threadIdx.x;
+    if (i >= (long long)a.B * a.Tv) return;
+    const int b = (int)(i / a.Tv);
+    const int j = (int)(i - (long long)b * a.Tv);
+    int kind = 3;  // the chunk
+    if (j < a.C) kind = cached_row(a, j, b * a.Hkv).kind;
+    seg[i] = kind != 0 ? 1 : 0;
+    prefix[i] = kind == 1 ? 1 : 0;
 }
 
 // The ring write: token i of the chunk (one of its last min(W, Tc)) goes to
@@ -133,15 +139,12 @@ __global__ __launch_bounds__(64) void chunk_ring_write_kernel(ChunkArgs a, int f
 
 hipError_t launch_chunk_stage(const ChunkArgs& a, void* k_stage, void* v_stage, int32_t* seg, uint8_t* prefix,
                               hipStream_t s) {
-    if (a.C > 0) {
-        hipLaunchKernelGGL(chunk_stage_kv_kernel, dim3((unsigned)a.C, (unsigned)(a.B * a.Hkv)), dim3(64), 0, s, a,
-                           (uint16_t*)k_stage, (uint16_t*)v_stage);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    const long long n = (long long)a.B * a.Tv;
-    const unsigned blocks = (unsigned)std::min<long long>((n + 255) / 256, 1024);
-    hipLaunchKernelGGL(chunk_stage_meta_kernel, dim3(blocks), dim3(256), 0, s, a, seg, prefix);
+    const long long kv = (long long)a.B * a.Hkv * a.C * (a.D / 16);
+    const long long meta = (long long)a.B * a.Tv;
+    const long long kv_blocks = (kv + 255) / 256, blocks = kv_blocks + (meta + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(chunk_stage_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, (uint16_t*)k_stage,
+                       (uint16_t*)v_stage, seg, prefix, (int)kv_blocks);
     return hipGetLastError();
 }
 
