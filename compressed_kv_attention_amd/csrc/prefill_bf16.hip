@@ -460,6 +460,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const bool two_seg =
         __builtin_amdgcn_ballot_w64(row_ok && seg_q > 0 && seg_q != rs.smin && seg_q != rs.smax) == 0;
 
+    int n_sink_sel = 0;  // sink tiles the walk visits
     if (scan) {
         const int rseg0 = q0 + lane <= q1 ? s0v : 0x7fffffff;
         const int rseg1 = q0 + 64 + lane <= q1 ? s1v : 0x7fffffff;
@@ -473,6 +474,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                 if (t0 + lane < n_sink_tiles) tsk = *(const int2*)(a.tsink + ((size_t)b * a.ntile + t0 + lane) * 2);
             }
             const uint64_t hit = __ballot(tsk.x <= hi && tsk.y >= lo);
+            n_sink_sel += __builtin_popcountll(hit);
             if (wave == 0 && lane == 0) {
                 sm.sink_bits[t0 / 32] = (uint32_t)hit;
                 if (t0 / 32 + 1 < kSinkWords) sm.sink_bits[t0 / 32 + 1] = (uint32_t)(hit >> 32);
@@ -501,6 +503,19 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 
+    // Workgroups with more tiles to walk than a plain window band issue first
+    // on their SIMDs: when every workgroup is resident at once, the call
+    // ends with its longest walks (query blocks that see a sink prefix or
+    // many pooled blocks), and the lighter ones beside them can wait.
+    {
+        const int n_band = plan.band_hi >= plan.band_lo ? plan.band_hi - plan.band_lo + 1 : 0;
+        const int n_walk = n_band + plan.n_pooled + n_sink_sel;
+        const int n_typ = a.window > 0 ? (wg_rows + a.window - 1 + BN - 1) / BN + 1 : 0;
+        const int extra = a.window > 0 ? n_walk - n_typ : 0;
+        if (extra >= 3) __builtin_amdgcn_s_setprio(3);
+        else if (extra == 2) __builtin_amdgcn_s_setprio(2);
+        else if (extra == 1) __builtin_amdgcn_s_setprio(1);
+    }
     // tile 0 (and the staged table rows) must have landed
     wait_all_barrier();
     if (q_lds) {
