@@ -26,6 +26,7 @@
 // source at C).
 #include "swa_common.h"
 #include "swa_internal.h"
+#include "swa_tiles.h"
 
 namespace swa {
 namespace {
@@ -56,9 +57,11 @@ __device__ __forceinline__ CachedRow cached_row(const ChunkArgs& a, int j, int b
 // One launch stages everything.  Blocks below kv_blocks: one thread per
 // (batch row, kv head, cached row j, 16 channels) dequantizes K and V (code x
 // scale in fp32, rounded to bf16), 16-byte accesses; padding rows are zero.
-// The other blocks: one thread per (batch row, key) writes the segment id
-// and prefix flag -- sinks up to sink_len and held ring positions in segment
-// 1 (sinks flagged), the chunk in segment 1, padding in segment 0.
+// The other blocks: one wave per (batch row, 64-key tile) writes the keys'
+// segment ids and prefix flags -- sinks up to sink_len and held ring
+// positions in segment 1 (sinks flagged), the chunk in segment 1, padding in
+// segment 0 -- and the prefill's key metadata of the tile, so that the
+// prefill needs no pre-pass.
 __global__ __launch_bounds__(256) void chunk_stage_kernel(ChunkArgs a, uint16_t* ks, uint16_t* vs, int32_t* seg,
                                                           uint8_t* prefix, int kv_blocks) {
     if ((int)blockIdx.x < kv_blocks) {
@@ -99,14 +102,21 @@ __global__ __launch_bounds__(256) void chunk_stage_kernel(ChunkArgs a, uint16_t*
         *(uint4*)(vs + dst + 8) = make_uint4(vw[4], vw[5], vw[6], vw[7]);
         return;
     }
-    const long long i = (long long)(blockIdx.x - kv_blocks) * 256 + threadIdx.x;
-    if (i >= (long long)a.B * a.Tv) return;
-    const int b = (int)(i / a.Tv);
-    const int j = (int)(i - (long long)b * a.Tv);
+    const long long gt = (long long)(blockIdx.x - kv_blocks) * 4 + (threadIdx.x >> 6);
+    if (gt >= (long long)a.B * a.ntile) return;
+    const int lane = threadIdx.x & 63;
+    const int b = (int)(gt / a.ntile), jt = (int)(gt % a.ntile);
+    const int j = 64 * jt + lane;
+    const bool valid = j < a.Tv;
     int kind = 3;  // the chunk
-    if (j < a.C) kind = cached_row(a, j, b * a.Hkv).kind;
-    seg[i] = kind != 0 ? 1 : 0;
-    prefix[i] = kind == 1 ? 1 : 0;
+    if (valid && j < a.C) kind = cached_row(a, j, b * a.Hkv).kind;
+    const int sg = kind != 0 ? 1 : 0;
+    const bool sk = kind == 1;
+    if (valid) {
+        seg[(size_t)b * a.Tv + j] = sg;
+        prefix[(size_t)b * a.Tv + j] = sk ? 1 : 0;
+    }
+    write_key_tile_meta(b, jt, lane, a.Tv, a.ntile, valid, sg, sk, a.info, a.ksub, a.tsink);
 }
 
 // The ring write: token i of the chunk (one of its last min(W, Tc)) goes to
@@ -140,8 +150,8 @@ __global__ __launch_bounds__(64) void chunk_ring_write_kernel(ChunkArgs a, int f
 hipError_t launch_chunk_stage(const ChunkArgs& a, void* k_stage, void* v_stage, int32_t* seg, uint8_t* prefix,
                               hipStream_t s) {
     const long long kv = (long long)a.B * a.Hkv * a.C * (a.D / 16);
-    const long long meta = (long long)a.B * a.Tv;
-    const long long kv_blocks = (kv + 255) / 256, blocks = kv_blocks + (meta + 255) / 256;
+    const long long meta = (long long)a.B * a.ntile;  // one wave per 64-key tile
+    const long long kv_blocks = (kv + 255) / 256, blocks = kv_blocks + (meta + 3) / 4;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(chunk_stage_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, (uint16_t*)k_stage,
                        (uint16_t*)v_stage, seg, prefix, (int)kv_blocks);

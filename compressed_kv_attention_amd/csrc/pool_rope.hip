@@ -455,26 +455,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs p) {
     } else {
         pfv = p.prefix[ic];
     }
-    const int info = valid ? pack_key_info(sgv, pfv != 0) : 0;
-    if (valid) p.info[(size_t)b * p.T + t] = info;
-    const int sg = info & 0x7fffffff;
-    const bool sk = info < 0;
-    const int half = lane >> 5;
-    const int s_first = half ? __builtin_amdgcn_readlane(sg, 32) : __builtin_amdgcn_readlane(sg, 0);
-    const uint64_t eq_b = __ballot(!valid || sg == s_first);
-    const uint64_t any_b = __ballot(valid && sk);
-    const uint64_t all_b = __ballot(!valid || sk);
-    const int smn = wave_min_i32(valid && sk ? sg : 0x7fffffff);
-    const int smx = wave_max_i32(valid && sk ? sg : (int)0x80000000);
-    if ((lane & 31) == 0) {
-        const uint32_t eq_h = (uint32_t)(eq_b >> (32 * half));
-        const uint32_t any_h = (uint32_t)(any_b >> (32 * half));
-        const uint32_t all_h = (uint32_t)(all_b >> (32 * half));
-        const KeySum ks = make_key_sum(eq_h == 0xffffffffu, s_first, any_h != 0u, all_h == 0xffffffffu);
-        *(int4*)(p.ksub + ((size_t)b * 2 * p.ntile + 2 * j + half) * 4) = make_int4(ks.smin, ks.smax, ks.any_sink,
-                                                                                      ks.all_sink);
-    }
-    if (lane == 0) *(int2*)(p.tsink + ((size_t)b * p.ntile + j) * 2) = make_int2(smn, smx);
+    write_key_tile_meta(b, j, lane, p.T, p.ntile, valid, sgv, pfv != 0, p.info, p.ksub, p.tsink);
 }
 
 }  // namespace

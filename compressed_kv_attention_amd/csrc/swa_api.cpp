@@ -155,6 +155,7 @@ struct SplitSources {
     int q_first, kv_split;
     const void* k2;
     const void* v2;
+    bool meta_ready;  // the key metadata is already in the workspace (no pre-pass)
 };
 
 int prefill_run(const swa_prefill_params* p, const void* q, const void* k, const void* v, const void* pooled_k,
@@ -257,7 +258,11 @@ int prefill_run(const swa_prefill_params* p, const void* q, const void* k, const
             pa.sn = rope_sin;
             pa.y = (uint16_t*)kr;
         }
-        if (meta.total > 0 && (a.seg || a.prefix)) {  // key metadata once per prefill
+        if (meta.total > 0 && (a.seg || a.prefix) && split != nullptr && split->meta_ready) {
+            a.kinfo = (const int32_t*)(ws + meta.info);
+            a.ksub = (const int32_t*)(ws + meta.ksub);
+            a.tsink = (const int32_t*)(ws + meta.tsink);
+        } else if (meta.total > 0 && (a.seg || a.prefix)) {  // key metadata once per prefill
             pa.seg = a.seg;
             pa.prefix = a.prefix;
             pa.info = (int32_t*)(ws + meta.info);
@@ -839,12 +844,19 @@ int swa_attn_chunk_prefill(const swa_chunk_params* p, const void* q, const void*
     a.C = L.C;
     a.Tv = L.pp.T;
     char* ws = (char*)workspace;
+    // the prefill's key metadata, written by the staging into the prefill's
+    // workspace where its pre-pass would have put it
+    const MetaLayout meta = key_meta_layout(&L.pp);
+    a.info = (int32_t*)(ws + L.pf + meta.info);
+    a.ksub = (int32_t*)(ws + L.pf + meta.ksub);
+    a.tsink = (int32_t*)(ws + L.pf + meta.tsink);
+    a.ntile = (L.pp.T + 63) / 64;
     const hipStream_t s = (hipStream_t)stream;
     hipError_t e = swa::launch_chunk_stage(a, ws + L.k, ws + L.v, (int32_t*)(ws + L.seg), (uint8_t*)(ws + L.prefix), s);
     if (e != hipSuccess) return hip_status(e, "swa_attn_chunk_prefill staging launch");
     // queries and outputs in place (rows C .. Tv - 1 of the key sequence); keys
     // switch from the staged cached rows to the caller's chunk at row C
-    const SplitSources split{L.C, L.C, k, v};
+    const SplitSources split{L.C, L.C, k, v, true};
     const int rc = prefill_run(&L.pp, q, ws + L.k, ws + L.v, nullptr, nullptr, (const int32_t*)(ws + L.seg),
                                (const uint8_t*)(ws + L.prefix), nullptr, nullptr, out, nullptr,
                                L.pf_bytes ? ws + L.pf : nullptr, L.pf_bytes, stream, &split);

@@ -288,9 +288,15 @@ struct ChunkArgs {
     int B, Hq, Hkv, D, W, S, Tc;
     int C;   // cached rows of the key sequence: S + W - 1 rounded up to 64
     int Tv;  // C + Tc
+    // the prefill's key metadata of the Tv keys (as its pre-pass writes it)
+    int32_t* info;
+    int32_t* ksub;
+    int32_t* tsink;
+    int ntile;  // ceil(Tv / 64)
 };
-// Stage the cached rows of K/V (sink and ring rows dequantized, padding zero)
-// and the segment and prefix arrays of the whole key sequence.
+// Stage the cached rows of K/V (sink and ring rows dequantized, padding zero),
+// the segment and prefix arrays of the whole key sequence and the prefill's
+// key metadata of it.
 hipError_t launch_chunk_stage(const ChunkArgs& a, void* k_stage, void* v_stage, int32_t* seg, uint8_t* prefix,
                               hipStream_t s);
 // Quantize the chunk's last min(W, Tc) tokens into the ring.

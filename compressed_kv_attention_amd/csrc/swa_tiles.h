@@ -84,6 +84,36 @@ __device__ __forceinline__ KeySum make_key_sum(bool uniform, int seg, bool any_s
     return k;
 }
 
+// The key metadata of one 64-key tile j of batch row b, written by one wave
+// (lane l: key 64 j + l, valid below T, with segment sg and sink flag sk):
+//   info[b][t]     packed segment | sink << 31 of every valid key
+//   ksub[b][2j+h]  KeySum of keys [64j + 32h, 64j + 32h + 32) ∩ [0, T)
+//   tsink[b][j]    (min, max) segment of the tile's sink keys,
+//                  (INT_MAX, INT_MIN) when it holds none
+__device__ __forceinline__ void write_key_tile_meta(int b, int j, int lane, int T, int ntile, bool valid, int sg,
+                                                    bool sk, int32_t* info, int32_t* ksub, int32_t* tsink) {
+    const int inf = valid ? pack_key_info(sg, sk) : 0;
+    if (valid) info[(size_t)b * T + 64 * j + lane] = inf;
+    const int seg = inf & 0x7fffffff;
+    const bool sink = inf < 0;
+    const int half = lane >> 5;
+    const int s_first = half ? __builtin_amdgcn_readlane(seg, 32) : __builtin_amdgcn_readlane(seg, 0);
+    const uint64_t eq_b = __ballot(!valid || seg == s_first);
+    const uint64_t any_b = __ballot(valid && sink);
+    const uint64_t all_b = __ballot(!valid || sink);
+    const int smn = wave_min_i32(valid && sink ? seg : 0x7fffffff);
+    const int smx = wave_max_i32(valid && sink ? seg : (int)0x80000000);
+    if ((lane & 31) == 0) {
+        const uint32_t eq_h = (uint32_t)(eq_b >> (32 * half));
+        const uint32_t any_h = (uint32_t)(any_b >> (32 * half));
+        const uint32_t all_h = (uint32_t)(all_b >> (32 * half));
+        const KeySum ks = make_key_sum(eq_h == 0xffffffffu, s_first, any_h != 0u, all_h == 0xffffffffu);
+        *(int4*)(ksub + ((size_t)b * 2 * ntile + 2 * j + half) * 4) = make_int4(ks.smin, ks.smax, ks.any_sink,
+                                                                              ks.all_sink);
+    }
+    if (lane == 0) *(int2*)(tsink + ((size_t)b * ntile + j) * 2) = make_int2(smn, smx);
+}
+
 // Classify a (row group, key sub-tile [k0, k0 + sub)) pair of plain mode, or
 // of the exact columns of compressed mode (plain == false: no segments, no
 // sinks).  SKIP: no pair is visible.  For FULL and PARTIAL_POS, wlim_eff is
