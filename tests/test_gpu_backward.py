@@ -115,3 +115,22 @@ def test_backward_needle_full_size():
     """The needle configuration (B8, 8q/2kv, D64, T2048, window 256, sink prefixes 64..384, RoPE), bf16."""
     w = workloads.needle()
     run_case(w, theta=w["rope_theta"], what="needle full size")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_sinks_in_later_segments(dtype):
+    """Sinks at the start of three segments of a 2500-token row (79 key tiles, a ragged tail of padding) and a
+    short window: a key tile of sinks is seen by every later row of its segment, far past the band, so the dk/dv
+    pass walks query tiles marked across several words of its tile set."""
+    B, Hq, Hkv, T, D, W = 2, 4, 1, 2500, 64, 64
+    seg = np.zeros((B, T), np.int32)
+    pre = np.zeros((B, T), np.uint8)
+    for b in range(B):
+        seg[b, :800] = 1
+        seg[b, 800:1900] = 2
+        seg[b, 1900:T - 7 - b] = 3
+        pre[b, :41] = 1
+        pre[b, 800:831 + 3 * b] = 1
+        pre[b, 1900:1906] = 1
+    w = workloads.prefill_case(B, Hq, Hkv, T, D, W, dtype=dtype, seed=777, seg_ids=seg, prefix=pre)
+    run_case(w, what="sinks in later segments")
