@@ -87,6 +87,8 @@ def test_nsa_select_compressed_config(block, dtype):
     (1, 6, 2, 257, 64, 1, 1, 32, "f32", 0.0),
     (3, 2, 2, 130, 64, 64, 8, 1, "bf16", 10000.0),
     (1, 2, 1, 100, 64, 200, 4, 8, "f32", 10000.0),   # window past T: no candidate anywhere
+    (2, 4, 2, 400, 32, 48, 16, 8, "bf16", 10000.0),  # bf16 at D = 32, long blocks
+    (1, 8, 4, 333, 64, 30, 3, 16, "bf16", 0.0),      # bf16, a block of 3, no RoPE
 ])
 def test_nsa_select_small(B, Hq, Hkv, T, D, W, b, n, dtype, theta):
     w = workloads.prefill_case(B, Hq, Hkv, T, D, W, dtype=dtype, seed=B * 7 + T, compress_block=b)
