@@ -258,7 +258,7 @@ __device__ __forceinline__ void load_q_rotated(const NsaArgs& a, size_t qrow, in
 }
 
 template <class X, int D, int kTopK>
-__global__ __launch_bounds__(64) void nsa_select_kernel(NsaArgs a, const X* krot, const float* pk32) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void nsa_select_kernel(NsaArgs a, const X* krot, const float* pk32) {
     constexpr int H = D / 2;   // channels per lane of a row pair
     constexpr int RS = D + 4;  // LDS row stride of the staged pooled keys (floats)
     __shared__ __align__(16) float tile[32 * RS];
@@ -342,38 +342,106 @@ __global__ __launch_bounds__(64) void nsa_select_kernel(NsaArgs a, const X* krot
                 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(av[e]), qB[4 * i4 + e], acc, 0, 0, 0);
         }
         lds_reads_done();  // the tile is reread only after these reads
+        if (j0 == 0) {
+            // The first tile: the list is empty, so it is this lane's 16
+            // candidates sorted (best first: larger score, or lower block on
+            // equal scores) by a bitonic network, cut to k.
+            float cv[16];
+            int ci[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int jj = 8 * (j >> 2) + 4 * kk + (j & 3);
+                const bool ok = jj < n_vis;
+                cv[j] = ok ? acc[j] * a.scale : kNegInf;
+                ci[j] = ok ? jj : -1;
+            }
+            auto better = [](float va, int ia, float vb, int ib) {
+                return va > vb || (va == vb && (unsigned)ia < (unsigned)ib);
+            };
+#pragma unroll
+            for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+                for (int st = k >> 1; st > 0; st >>= 1)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int l = i ^ st;
+                        if (l <= i) continue;
+                        // best first within blocks of k whose bit k is clear, worst first otherwise
+                        const bool sw = (i & k) == 0 ? better(cv[l], ci[l], cv[i], ci[i])
+                                                     : better(cv[i], ci[i], cv[l], ci[l]);
+                        const float fv = cv[i];
+                        const int fi = ci[i];
+                        cv[i] = sw ? cv[l] : fv;
+                        ci[i] = sw ? ci[l] : fi;
+                        cv[l] = sw ? fv : cv[l];
+                        ci[l] = sw ? fi : ci[l];
+                    }
+#pragma unroll
+            for (int i = 0; i < (kTopK < 16 ? kTopK : 16); ++i) {
+                tv[i] = cv[i];
+                ti[i] = ci[i];
+            }
+            continue;
+        }
         // This lane's candidates above its current threshold, as a bit mask;
         // their scores wait in LDS.  The lanes then insert together, each its
         // next candidate in increasing order, as long as any lane has one:
         // the insertion runs as often as the busiest lane needs, not once
         // for every candidate some lane takes.
+        // The row's k-th best score is at least this lane's and its partner's
+        // k-th best, and at least the smaller of their (k/2)-th best (together
+        // they hold k scores at or above it): a candidate below that bound is
+        // not among the row's k best and is not inserted (equal ones are).
+        const float own_k = tv[kTopK - 1], own_h = tv[kTopK / 2 - 1];
+        const float par_k = __shfl_xor(own_k, 32, 64), par_h = __shfl_xor(own_h, 32, 64);
+        const float bound = fmaxf(fmaxf(own_k, par_k), fminf(own_h, par_h));
         uint32_t want = 0u;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const float s = acc[j] * a.scale;
             const int jj = j0 + 8 * (j >> 2) + 4 * kk + (j & 3);
             sc[lane * 17 + j] = s;
-            if (jj < n_vis && s > tv[kTopK - 1]) want |= 1u << j;
+            if (jj < n_vis && s > own_k && s >= bound) want |= 1u << j;
         }
+        // Two candidates per pass, in increasing order: the second moves one
+        // list place behind the first, which is the same as inserting them one
+        // after the other (the second's step at place i follows the first's
+        // step there and no later one of the first touches place i), with
+        // half the passes and two independent chains of compare-and-swap.
         while (__builtin_amdgcn_ballot_w64(want != 0u) != 0) {
+            float s1 = kNegInf, s2 = kNegInf;
+            int id1 = -1, id2 = -1;
             if (want != 0u) {
                 const int j = __builtin_ctz(want);
                 want &= want - 1u;
-                float s = sc[lane * 17 + j];
-                int id = j0 + 8 * (j >> 2) + 4 * kk + (j & 3);
-                if (s > tv[kTopK - 1]) {
+                s1 = sc[lane * 17 + j];
+                id1 = j0 + 8 * (j >> 2) + 4 * kk + (j & 3);
+            }
+            if (want != 0u) {
+                const int j = __builtin_ctz(want);
+                want &= want - 1u;
+                s2 = sc[lane * 17 + j];
+                id2 = j0 + 8 * (j >> 2) + 4 * kk + (j & 3);
+            }
+            // (no lane's pair reaches its list: the pass is skipped)
+            if (__builtin_amdgcn_ballot_w64(s1 > tv[kTopK - 1] || s2 > tv[kTopK - 1]) == 0) continue;
+            // (compare-and-swap by selects: no branch per place)
 #pragma unroll
-                    for (int i = 0; i < kTopK; ++i) {
-                        if (s > tv[i]) {
-                            const float fs = tv[i];
-                            const int is = ti[i];
-                            tv[i] = s;
-                            ti[i] = id;
-                            s = fs;
-                            id = is;
-                        }
-                    }
-                }
+            for (int i = 0; i < kTopK; ++i) {
+                const bool g1 = s1 > tv[i];
+                const float v1 = tv[i];
+                const int i1 = ti[i];
+                tv[i] = g1 ? s1 : v1;
+                ti[i] = g1 ? id1 : i1;
+                s1 = g1 ? v1 : s1;
+                id1 = g1 ? i1 : id1;
+                const bool g2 = s2 > tv[i];
+                const float v2 = tv[i];
+                const int i2 = ti[i];
+                tv[i] = g2 ? s2 : v2;
+                ti[i] = g2 ? id2 : i2;
+                s2 = g2 ? v2 : s2;
+                id2 = g2 ? i2 : id2;
             }
         }
     }
