@@ -438,19 +438,22 @@ template <int D>
 struct TileRows {
     static constexpr int CPR = D / 8;           // 16-byte pieces per row
     static constexpr int PER = 32 * CPR / 64;   // pieces per lane
-    uint4 x[PER];
+    u32x4 x[PER];  // a plain vector type: copies of an aggregate would go through memory
+    // Every lane loads, rows past the end (nrows >= 1) from the last row, so that
+    // no load sits under a branch.  Those copies are finite data whose products
+    // the mask sends to zero: their rows are invisible to every key.
     __device__ __forceinline__ void load(const uint16_t* src, int nrows, int lane) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int piece = lane + 64 * i, r = piece / CPR, c = piece % CPR;
-            x[i] = r < nrows ? *(const uint4*)(src + (size_t)r * D + 8 * c) : make_uint4(0, 0, 0, 0);
+            x[i] = *(const u32x4*)(src + (size_t)(r < nrows ? r : nrows - 1) * D + 8 * c);
         }
     }
     __device__ __forceinline__ void store(Bf16Tile<D>& t, int lane) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int piece = lane + 64 * i, r = piece / CPR, c = piece % CPR;
-            *(uint4*)&t.x[r * Bf16Tile<D>::RS + 8 * c] = x[i];
+            *(u32x4*)&t.x[r * Bf16Tile<D>::RS + 8 * c] = x[i];
         }
     }
 };
@@ -547,37 +550,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
     constexpr int CPR = D / 8;
     const int pr = tid / CPR, pc = tid % CPR;
     const bool mover = tid < 32 * CPR;
-    auto fetch = [&](int k0, uint4& xk, uint4& xv, int& info) {
-        xk = xv = make_uint4(0, 0, 0, 0);
-        if (mover && pr < T - k0) {
-            xk = *(const uint4*)(khead + (size_t)(k0 + pr) * D + 8 * pc);
-            xv = *(const uint4*)(vhead + (size_t)(k0 + pr) * D + 8 * pc);
-        }
-        info = 0;
-        if (tid < BT && k0 + tid < T) {
-            const int gk = k0 + tid;
-            const int sg = a.seg ? a.seg[(size_t)b * T + gk] : 1;
-            const bool sk = a.prefix ? (a.prefix[(size_t)b * T + gk] != 0) : false;
-            info = pack_key_info(sg, sk);
-        }
+    // Unconditional loads from clamped rows, so that no load sits under a
+    // branch.  Rows past the end hold copies of the last key, invisible to every
+    // query (the mask tests the key index), and their infos are cleared when
+    // stored, where the loaded values are needed anyway.
+    struct Staged {
+        uint4 k, v;
+        int sg, sk;
+    };
+    auto fetch = [&](int k0, Staged& x) {
+        const int last = T - k0 - 1;
+        const int rr = min(min(pr, BT - 1), last);
+        x.k = *(const uint4*)(khead + (size_t)(k0 + rr) * D + 8 * pc);
+        x.v = *(const uint4*)(vhead + (size_t)(k0 + rr) * D + 8 * pc);
+        const int gk = k0 + min(tid & (BT - 1), last);
+        x.sg = a.seg ? a.seg[(size_t)b * T + gk] : 1;
+        x.sk = a.prefix ? a.prefix[(size_t)b * T + gk] : 0;
     };
     int kind = 0, tile = 0;
     bool have = it.next(kind, tile);
-    uint4 ck = make_uint4(0, 0, 0, 0), cv = ck;
-    int cinfo = 0;
-    if (have) fetch(tile * BT, ck, cv, cinfo);
+    Staged cur{make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), 0, 0};
+    if (have) fetch(tile * BT, cur);
     while (have) {
         const int k0 = tile * BT;
         int kn = 0, tn = 0;
         const bool have_next = it.next(kn, tn);
         __syncthreads();  // every wave is done with the previous tile
         if (mover) {
-            *(uint4*)&sm.k.x[pr * Bf16Tile<D>::RS + 8 * pc] = ck;
-            *(uint4*)&sm.v.x[pr * Bf16Tile<D>::RS + 8 * pc] = cv;
+            *(uint4*)&sm.k.x[pr * Bf16Tile<D>::RS + 8 * pc] = cur.k;
+            *(uint4*)&sm.v.x[pr * Bf16Tile<D>::RS + 8 * pc] = cur.v;
         }
-        if (tid < BT) sm.kinfo[tid] = cinfo;
+        if (tid < BT) sm.kinfo[tid] = k0 + tid < T ? pack_key_info(cur.sg, cur.sk != 0) : 0;
         __syncthreads();
-        if (have_next) fetch(tn * BT, ck, cv, cinfo);
+        if (have_next) fetch(tn * BT, cur);
         tile = tn;
         have = have_next;
         if (!wave_on) continue;
@@ -590,7 +595,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int kk = 8 * i + 4 * h + r;
-                const bool vis = row_vis && k0 + kk < T && visible_full(my_q - (k0 + kk), wlim, (int)inf[r], seg_q);
+                const bool vis = row_vis & (k0 + kk < T) & visible_full(my_q - (k0 + kk), wlim, (int)inf[r], seg_q);
                 sacc[4 * i + r] = vis ? nl : kNegInf;
             }
         }
@@ -750,10 +755,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         auto fetch = [&](int t) {
             rq.load(qs + (qhead + t) * D, T - t, lane);
             ro.load((const uint16_t*)a.dout + (qhead + t) * D, T - t, lane);
-            const int tq = t + (lane & 31);
-            l = tq < T ? a.lse[qhead + tq] : kNegInf;
-            dlt = tq < T ? delta[qhead + tq] : 0.f;
-            sgq = tq < T ? (a.seg ? a.seg[(size_t)b * T + tq] : 1) : 0;
+            // clamped row (the tile's rows past the end are cleared when stored)
+            const int tq = min(t + (lane & 31), T - 1);
+            l = a.lse[qhead + tq];
+            dlt = delta[qhead + tq];
+            sgq = a.seg ? a.seg[(size_t)b * T + tq] : 1;
         };
         fetch(s0);
         for (int t0 = s0; t0 >= 0;) {
@@ -762,9 +768,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
             rq.store(ws.q, lane);
             ro.store(ws.go, lane);
             if (lane < BT) {
-                ws.lse2[lane] = l == kNegInf ? kNegInf : l * kLog2e;
-                ws.dlt[lane] = dlt;
-                ws.seg[lane] = sgq;
+                const bool in = t0 + lane < T;
+                ws.lse2[lane] = !in || l == kNegInf ? kNegInf : l * kLog2e;
+                ws.dlt[lane] = in ? dlt : 0.f;
+                ws.seg[lane] = in ? sgq : 0;
             }
             const int tn = next_tile(t0);
             if (tn >= 0) fetch(tn);
@@ -785,7 +792,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                     const int sq = (int)sg4[r];
                     const float l2 = __uint_as_float(l24[r]);
                     dl[4 * i + r] = __uint_as_float(dl4[r]);
-                    const bool vis = key_ok && tq < T && sq > 0 && l2 != kNegInf &&
+                    const bool vis = key_ok & (tq < T) & (sq > 0) & (l2 != kNegInf) &
                                      visible_full(tq - my_k, wlim, info_k, sq);
                     sacc[4 * i + r] = vis ? -l2 : kNegInf;
                 }
