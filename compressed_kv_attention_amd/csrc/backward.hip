@@ -773,28 +773,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                 ws.dlt[lane] = in ? dlt : 0.f;
                 ws.seg[lane] = in ? sgq : 0;
             }
+            // the tile's rows all exist, are visible to some key and share one
+            // segment: tseg is that segment, else 0
+            const int sq0 = __builtin_amdgcn_readfirstlane(sgq);
+            const int tseg =
+                __ballot(lane < BT && (t0 + lane >= T || sgq != sq0 || l == kNegInf)) == 0 && sq0 > 0 ? sq0 : 0;
             const int tn = next_tile(t0);
             if (tn >= 0) fetch(tn);
             lds_reads_done();
             // S = Q' K^T from the mask (element j: query 8 (j / 4) + j % 4 + 4h of the tile)
             f32x16 sacc;
             float dl[16];
+            // Whole tile visible to every valid key of the wave (the rows share
+            // the key's segment and the key lies inside every row's window).
+            const bool full =
+                tseg > 0 && __ballot(key_ok && !((info_k & 0x7fffffff) == tseg && t0 >= my_k &&
+                                                 (unsigned)(t0 + BT - 1 - my_k) < wlim)) == 0;
+            if (full) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // queries 8i + 4h + r of the tile (elements 4i + r): one read per array
-                const u32x4 sg4 = lds_load128(lds_off(&ws.seg[8 * i + 4 * h]));
-                const u32x4 l24 = lds_load128(lds_off(&ws.lse2[8 * i + 4 * h]));
-                const u32x4 dl4 = lds_load128(lds_off(&ws.dlt[8 * i + 4 * h]));
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 l24 = lds_load128(lds_off(&ws.lse2[8 * i + 4 * h]));
+                    const u32x4 dl4 = lds_load128(lds_off(&ws.dlt[8 * i + 4 * h]));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int qi = 8 * i + 4 * h + r;
-                    const int tq = t0 + qi;
-                    const int sq = (int)sg4[r];
-                    const float l2 = __uint_as_float(l24[r]);
-                    dl[4 * i + r] = __uint_as_float(dl4[r]);
-                    const bool vis = key_ok & (tq < T) & (sq > 0) & (l2 != kNegInf) &
-                                     visible_full(tq - my_k, wlim, info_k, sq);
-                    sacc[4 * i + r] = vis ? -l2 : kNegInf;
+                    for (int r = 0; r < 4; ++r) {
+                        dl[4 * i + r] = __uint_as_float(dl4[r]);
+                        sacc[4 * i + r] = key_ok ? -__uint_as_float(l24[r]) : kNegInf;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // queries 8i + 4h + r of the tile (elements 4i + r): one read per array
+                    const u32x4 sg4 = lds_load128(lds_off(&ws.seg[8 * i + 4 * h]));
+                    const u32x4 l24 = lds_load128(lds_off(&ws.lse2[8 * i + 4 * h]));
+                    const u32x4 dl4 = lds_load128(lds_off(&ws.dlt[8 * i + 4 * h]));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int qi = 8 * i + 4 * h + r;
+                        const int tq = t0 + qi;
+                        const int sq = (int)sg4[r];
+                        const float l2 = __uint_as_float(l24[r]);
+                        dl[4 * i + r] = __uint_as_float(dl4[r]);
+                        const bool vis = key_ok & (tq < T) & (sq > 0) & (l2 != kNegInf) &
+                                         visible_full(tq - my_k, wlim, info_k, sq);
+                        sacc[4 * i + r] = vis ? -l2 : kNegInf;
+                    }
                 }
             }
             f32x16 dpa = f32x16{};
