@@ -643,7 +643,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
     }
     float* out = a.dq + qrow * D;
 #pragma unroll
-    for (int e = 0; e < D / 2; e += 4) *(float4*)(out + chan(e)) = make_float4(g[e], g[e + 1], g[e + 2], g[e + 3]);
+    for (int e = 0; e < D / 2; e += 4)
+        __builtin_nontemporal_store(f32x4{g[e], g[e + 1], g[e + 2], g[e + 3]}, (f32x4*)(out + chan(e)));
 }
 
 template <int D>
@@ -902,8 +903,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     float* ov = a.dv + krow * D;
 #pragma unroll
     for (int e = 0; e < D / 2; e += 4) {
-        *(float4*)(ok + chan(e)) = make_float4(gk[e], gk[e + 1], gk[e + 2], gk[e + 3]);
-        *(float4*)(ov + chan(e)) = make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
+        __builtin_nontemporal_store(f32x4{gk[e], gk[e + 1], gk[e + 2], gk[e + 3]}, (f32x4*)(ok + chan(e)));
+        __builtin_nontemporal_store(f32x4{gv[e], gv[e + 1], gv[e + 2], gv[e + 3]}, (f32x4*)(ov + chan(e)));
     }
 }
 

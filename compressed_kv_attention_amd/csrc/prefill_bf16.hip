@@ -927,7 +927,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         for (int j = 0; j < 32 / RPI; ++j) {
             const int r = j * RPI + lane / CPR, c = lane % CPR;
             const u32x4 x = lds_load128(ob + (uint32_t)(r * CPR + (c ^ (r % CPR))) * 16u);
-            if (r0 + r < T) *(u32x4*)(ohead + (size_t)(r0 + r - q_first) * D + 8 * c) = x;
+            // non-temporal: nothing in this launch reads the output back, and the
+            // cache lines it would occupy hold K/V tiles other workgroups reuse
+            if (r0 + r < T) __builtin_nontemporal_store(x, (u32x4*)(ohead + (size_t)(r0 + r - q_first) * D + 8 * c));
         }
     }
     if (row_ok) {
