@@ -329,11 +329,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
                 const int pc = lane % CPR;
                 if (t == 0) {
                     const int lc = pc ^ ((rr >> 1) & (CPR - 1));  // logical piece stored at slot pc
-                    dma16(kb, (uint32_t)row_of(rr) * D + 16 * lc, lds_off(&B.k[j * 1024]));
+                    dma16_nt(kb, (uint32_t)row_of(rr) * D + 16 * lc, lds_off(&B.k[j * 1024]));
                 } else {
                     // (V stays row-major for D = 64: it is read with transposing reads)
                     const int lv = D == 64 ? pc : pc ^ ((rr >> 1) & (CPR - 1));
-                    dma16(vb, (uint32_t)row_of(rr) * D + 16 * lv, lds_off(&B.v[j * 1024]));
+                    dma16_nt(vb, (uint32_t)row_of(rr) * D + 16 * lv, lds_off(&B.v[j * 1024]));
                 }
             }
 #pragma unroll

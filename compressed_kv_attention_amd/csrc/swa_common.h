@@ -155,6 +155,13 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                  "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory", "m0");
 }
+// The same with the non-temporal hint, for data that one launch reads once
+// (a decode step's cache rows): they need not displace reused lines.
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(uniform_ptr(base)),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(base)),
                  "s"(__builtin_amdgcn_readfirstlane(lds))
