@@ -421,7 +421,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
             for (int i = 0; i < 32 / QRPI; ++i) {
                 const int r = i * QRPI + lane / QCPR, pc = lane % QCPR;
                 const int rr = min(r, T - 1 - r0);  // rows past the end repeat the last row
-                dma16(qbase, (uint32_t)(rr * D * 2 + (pc ^ (r % QCPR)) * 16), q_lds_base + 1024u * i);
+                // (non-temporal: each q row is read by this workgroup alone)
+                dma16_nt(qbase, (uint32_t)(rr * D * 2 + (pc ^ (r % QCPR)) * 16), q_lds_base + 1024u * i);
             }
         }
 #pragma unroll
