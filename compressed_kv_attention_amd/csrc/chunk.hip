@@ -79,8 +79,9 @@ __global__ __launch_bounds__(256) void chunk_stage_kernel(ChunkArgs a, uint16_t*
             const int8_t* vc = r.kind == 1 ? a.sink_v : a.ring_v;
             const float* kss = r.kind == 1 ? a.sink_ks : a.ring_ks;
             const float* vss = r.kind == 1 ? a.sink_vs : a.ring_vs;
-            const uint4 kq = *(const uint4*)(kc + r.src * D + d0);
-            const uint4 vq = *(const uint4*)(vc + r.src * D + d0);
+            // (non-temporal: every cached row is read once per call)
+            const uint4 kq = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(kc + r.src * D + d0)));
+            const uint4 vq = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(vc + r.src * D + d0)));
             const float sk = kss[r.src * (D / 32) + d0 / 32], sv = vss[r.src * (D / 32) + d0 / 32];
             const uint32_t kq4[4] = {kq.x, kq.y, kq.z, kq.w}, vq4[4] = {vq.x, vq.y, vq.z, vq.w};
 #pragma unroll
