@@ -120,7 +120,7 @@ class Part:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)

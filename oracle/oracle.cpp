@@ -17,7 +17,7 @@
 //   [NS] "256-token滑动窗口+KV sink：Needle 2工具钉住机制源码分析" (cf-1.com)
 //   [CA] "Compressed attention and the copy probe" (octlm.ramaa.tech)
 //
-// Readings taken where the pages are silent (each listed in the design doc):
+// Readings taken where the pages are silent:
 //   R-A1 prefill mask = packing & causal & (recent | sink), literally as the
 //        make_causal_packing_mask code composes it, so sinks do not cross
 //        segments in prefill; the decode mask has no packing term.
